@@ -1,0 +1,152 @@
+"""fp64 CPU oracle for DAR attention (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It is independent of the HIP path:
+it shares no code with ``distance_adaptive_dual_amd`` and never imports it.
+
+The arithmetic lives in ``dar_oracle.c`` (plain loops from the DAR paper,
+"Dual Dimensionality for Local and Global Attention", Eqs. 1-4); this module
+only marshals numpy float64 arrays to it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dar_oracle.c")
+_LIB = os.path.join(_HERE, "libdar_oracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int)
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        lib.dar_oracle_threads.restype = ctypes.c_int
+        lib.dar_oracle_project.restype = ctypes.c_int
+        lib.dar_oracle_project.argtypes = [_D] * 6 + [ctypes.c_int] * 6 + [
+            ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [_D] * 7
+        lib.dar_oracle_attend.restype = ctypes.c_int
+        lib.dar_oracle_attend.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [ctypes.c_long] + [_D] * 2
+        lib.dar_oracle_attend_rows.restype = ctypes.c_int
+        lib.dar_oracle_attend_rows.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [
+            ctypes.c_long, ctypes.c_int, _I, _I, _I, _D, _D]
+        lib.dar_oracle_decode.restype = ctypes.c_int
+        lib.dar_oracle_decode.argtypes = [_D] * 7 + [ctypes.c_int, ctypes.c_long, ctypes.c_long] + [
+            ctypes.c_int] * 4 + [ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_int, _D]
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(_D)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def threads() -> int:
+    return _load().dar_oracle_threads()
+
+
+def project(h, W_down, W_up, W_Q, W_K, W_V, H, d_k, pos0=0, base=10000.0, n_tok=None,
+            heads=None):
+    """Eqs. 1-3 projections.  Returns dict hD, hp, Q, KL, VL, KG, VG (float64).
+
+    h [B,N,d]; Q/KL/VL/KG/VG [B,H,N,d_k]; only tokens < n_tok and heads in the
+    ``heads`` range (lo, hi) are computed (the rest stay zero).
+    """
+    h, W_down, W_up, W_Q, W_K, W_V = map(_f64, (h, W_down, W_up, W_Q, W_K, W_V))
+    B, N, d = h.shape
+    d_down = W_down.shape[1]
+    assert W_down.shape == (d, d_down) and W_up.shape == (d_down, d)
+    assert W_Q.shape == W_K.shape == W_V.shape == (d, H * d_k)
+    n_tok = N if n_tok is None else int(n_tok)
+    lo, hi = (0, H) if heads is None else heads
+    out = dict(hD=np.zeros((B, N, d_down)), hp=np.zeros((B, N, d)))
+    for k in ("Q", "KL", "VL", "KG", "VG"):
+        out[k] = np.zeros((B, H, N, d_k))
+    rc = _load().dar_oracle_project(
+        _p(h), _p(W_down), _p(W_up), _p(W_Q), _p(W_K), _p(W_V), B, N, d, d_down, H, d_k,
+        int(pos0), float(base), n_tok, lo, hi, _p(out["hD"]), _p(out["hp"]), _p(out["Q"]),
+        _p(out["KL"]), _p(out["VL"]), _p(out["KG"]), _p(out["VG"]))
+    if rc != 0:
+        raise ValueError("dar_oracle_project rejected its arguments")
+    return out
+
+
+def attend(P, w):
+    """Eq. 3 selection + Eq. 4 for every row.  Returns (o [B,N,H*d_k], rowsum [B,H,N])."""
+    Q, KL, VL, KG, VG = (_f64(P[k]) for k in ("Q", "KL", "VL", "KG", "VG"))
+    B, H, N, d_k = Q.shape
+    o = np.zeros((B, N, H * d_k))
+    rs = np.zeros((B, H, N))
+    rc = _load().dar_oracle_attend(_p(Q), _p(KL), _p(VL), _p(KG), _p(VG), B, N, H, d_k,
+                                   int(w), _p(o), _p(rs))
+    if rc != 0:
+        raise ValueError("dar_oracle_attend rejected its arguments")
+    return o, rs
+
+
+def attend_rows(P, w, rows):
+    """Selected rows [(b, head, i), ...].  Returns (o_rows [n, d_k], rowsum [n])."""
+    Q, KL, VL, KG, VG = (_f64(P[k]) for k in ("Q", "KL", "VL", "KG", "VG"))
+    B, H, N, d_k = Q.shape
+    rows = np.asarray(rows, dtype=np.int32).reshape(-1, 3)
+    rb, rh, ri = (np.ascontiguousarray(rows[:, c]) for c in range(3))
+    o = np.zeros((len(rows), d_k))
+    rs = np.zeros(len(rows))
+    I = lambda a: a.ctypes.data_as(_I)  # noqa: E731
+    rc = _load().dar_oracle_attend_rows(_p(Q), _p(KL), _p(VL), _p(KG), _p(VG), B, N, H, d_k,
+                                        int(w), len(rows), I(rb), I(rh), I(ri), _p(o), _p(rs))
+    if rc != 0:
+        raise ValueError("dar_oracle_attend_rows rejected its arguments")
+    return o, rs
+
+
+def prefill(inp, H, d_k, w, pos0=0, base=10000.0):
+    """Whole forward pass: projections then attention.  Returns (o, rowsum, projections)."""
+    P = project(inp["h"], inp["W_down"], inp["W_up"], inp["W_Q"], inp["W_K"], inp["W_V"],
+                H, d_k, pos0=pos0, base=base)
+    o, rs = attend(P, w)
+    return o, rs, P
+
+
+def decode(q, K_win, V_win, hD, W_up, W_K, W_V, ctx, w, base=10000.0, heads=None):
+    """Mixed-cache decode at position ctx-1.  q [B,H,d_k]; K_win/V_win [B,H,w,d_k];
+    hD [B,cap,d_down].  Returns o [B, H*d_k] (heads outside ``heads`` are zero)."""
+    q, hD, W_up, W_K, W_V = map(_f64, (q, hD, W_up, W_K, W_V))
+    B, H, d_k = q.shape
+    cap, d_down = hD.shape[1], hD.shape[2]
+    d = W_up.shape[1]
+    if w > 0:
+        K_win, V_win = _f64(K_win), _f64(V_win)
+        assert K_win.shape == V_win.shape == (B, H, w, d_k)
+    else:
+        K_win = V_win = np.zeros(1)
+    lo, hi = (0, H) if heads is None else heads
+    o = np.zeros((B, H * d_k))
+    rc = _load().dar_oracle_decode(_p(q), _p(K_win), _p(V_win), _p(hD), _p(W_up), _p(W_K),
+                                   _p(W_V), B, int(ctx), cap, H, d_k, d_down, d, int(w),
+                                   float(base), lo, hi, _p(o))
+    if rc != 0:
+        raise ValueError("dar_oracle_decode rejected its arguments (rc=%d)" % rc)
+    return o
