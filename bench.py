@@ -1,0 +1,255 @@
+"""Benchmark of the DAR attention forward pass on one MI355X.
+
+A step is one prefill pass of the layer (dar_project + dar_attn_prefill, the
+folded weights prepared once beforehand) over one batch of synthetic input
+already resident in HBM.  Default workload: the Pythia-70M-shaped layer
+(batch 8, N 2048, d 512, 8 heads of 64, w 128, d_down 128, bf16).  The same
+run also times the long-context decode step (batch 16, context 32768, d 2048,
+16 heads of 128, w 512, d_down 256) and the d_down sweep, and times the fp64
+oracle on a bounded sample on the host cores (a reported baseline).
+
+Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, N, d, d_down):
+    """Algorithmic FLOPs of one prefill pass on the minimal route: the fused
+    projection h [W_Q|W_K|W_V|W_down], the folded global projection
+    h^D [W_upK|W_upV] and causal attention (each pair once)."""
+    proj = 2.0 * B * N * (3 * d * d + 3 * d * d_down)
+    attn = 2.0 * B * d * N * (N + 1)
+    return proj, attn
+
+
+def prefill_bytes(B, N, d, d_down, H, d_k):
+    """Algorithmic HBM bytes (bf16): read h and the weights, write o."""
+    return 2.0 * (B * N * d + d * (3 * d + d_down) + 2 * d_down * d + B * N * H * d_k)
+
+
+def decode_work(B, ctx, d, d_down, w, H):
+    """Per-step decode bytes (latents + window K/V + folded weights + q + o) and
+    FLOPs: per latent token the key rebuild (2 d d_down), the scores (2 d) and
+    the latent-space value sum (2 H d_down); per window token 4 d; per
+    sequence one lift by W_upV (2 d_down d)."""
+    n_lat = ctx - w
+    byts = 2.0 * (B * n_lat * d_down + B * w * 2 * d + 2 * d_down * d + 2 * B * d)
+    flops = (B * n_lat * (2.0 * d * d_down + 2.0 * d + 2.0 * H * d_down)
+             + B * w * 4.0 * d + B * 2.0 * d_down * d)
+    return byts, flops
+
+
+def make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed):
+    inp = di.prefill_inputs(B, N, d, H, d_k, d_down, dtype="bf16", seed0=seed)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(
+            torch.bfloat16).cuda()
+
+    W = {k: dev(inp[k].T) for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    h = dev(inp["h"])
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    kw = dict(dtype=torch.bfloat16, device="cuda")
+    out = dict(Q=torch.empty((B, H, N, d_k), **kw), K_loc=torch.empty((B, H, N, d_k), **kw),
+               V_loc=torch.empty((B, H, d_k, N), **kw), h_D=torch.empty((B, N, d_down), **kw),
+               K_glob=torch.empty((B, H, N, d_k), **kw), V_glob=torch.empty((B, H, d_k, N), **kw))
+    o = torch.empty((B, N, H * d_k), **kw)
+    ws = torch.empty(max(dar.project_workspace_bytes(B, N, d, d_down, H, d_k), 256),
+                     dtype=torch.uint8, device="cuda")
+    return inp, dict(h=h, W=W, Wk=Wk, Wv=Wv, out=out, o=o, ws=ws)
+
+
+def prefill_step(dar, s, H, d_k, w, ev=None):
+    W = s["W"]
+    if ev is not None:
+        ev[0].record()
+    dar.dar_project(s["h"], W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                    W_upK=s["Wk"], W_upV=s["Wv"], out=s["out"], workspace=s["ws"])
+    if ev is not None:
+        ev[1].record()
+    out = s["out"]
+    dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"], out["V_glob"], w,
+                         o=s["o"])
+    if ev is not None:
+        ev[2].record()
+
+
+def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
+    for _ in range(warmup):
+        prefill_step(dar, s, H, d_k, w)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        prefill_step(dar, s, H, d_k, w, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    proj_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    return wall / steps * 1e3, proj_ms, attn_ms
+
+
+def cpu_baseline(oracle, inp, H, d_k, w, d_down):
+    """The fp64 oracle on one sequence of the same workload (all heads)."""
+    one = {k: (v[:1] if k == "h" else v) for k, v in inp.items()}
+    B1, N, d = one["h"].shape
+    t0 = time.perf_counter()
+    oracle.prefill(one, H, d_k, w)
+    dt = time.perf_counter() - t0
+    proj, attn = prefill_flops(1, N, d, d_down)
+    return {"value": (proj + attn) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": "one of the 8 sequences (N %d, all %d heads), projections + attention, "
+                      "fp64, same algorithmic FLOP count as the GPU metric" % (N, H)}
+
+
+def time_decode(torch, dar, di, steps, warmup, cfg):
+    B, ctx, d, H, d_k, d_down, w = cfg
+    inp = di.decode_inputs(B, ctx, d, H, d_k, d_down, w, dtype="bf16", seed0=5000)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(
+            torch.bfloat16).cuda()
+
+    W_up, W_K, W_V = (dev(inp[k].T) for k in ("W_up", "W_K", "W_V"))
+    Wk, Wv = dar.dar_fold(W_up, W_K, W_V, H, d_k)
+    q, K_win, V_win, h_D = (dev(inp[k]) for k in ("q", "K_win", "V_win", "h_D"))
+    del inp
+    o = torch.empty((B, H * d_k), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dar.decode_workspace_bytes(B, ctx, ctx, H, d_k, d_down, w),
+                     dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # > Infinity Cache
+    for _ in range(warmup):
+        dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    byts, flops = decode_work(B, ctx, d, d_down, w, H)
+    return {"workload": "decode B%d ctx%d d%d H%d dk%d w%d d_down%d" % (B, ctx, d, H, d_k, w, d_down),
+            "ms": ms, "GB/s": byts / ms / 1e6, "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBS,
+            "TFLOP/s": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "bytes": byts, "flops": flops}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dar_inputs as di
+    import distance_adaptive_dual_amd as dar
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dar.lib()
+
+    res = {"metric": "DAR prefill TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
+           "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+
+    B, N, d, H, d_k, w, d_down = 8, 2048, 512, 8, 64, 128, 128
+    if args.only in ("all", "prefill"):
+        log("prefill: building inputs")
+        inp, s = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=2000 + d_down)
+        ms, proj_ms, attn_ms = time_prefill(torch, dar, s, H, d_k, w, args.steps, args.warmup)
+        proj_f, attn_f = prefill_flops(B, N, d, d_down)
+        tflops = (proj_f + attn_f) / ms / 1e9
+        log("prefill: %.3f ms/step, %.1f TFLOP/s (proj %.3f ms, attn %.3f ms)"
+            % (ms, tflops, proj_ms, attn_ms))
+        res.update(value=tflops, ms_per_step=ms)
+        res["config"] = {"workload": "pythia70m-layer prefill B%d N%d d%d H%d dk%d w%d d_down%d"
+                         % (B, N, d, H, d_k, w, d_down), "global_batch": B, "seq_len": N,
+                         "parallelism": "none (1 GPU)"}
+        res["mfma_frac"] = tflops / PEAK_BF16_TFLOPS
+        res["kernels"] = {"dar_project_ms": proj_ms, "dar_project_TFLOP/s": proj_f / proj_ms / 1e9,
+                          "dar_attn_prefill_ms": attn_ms,
+                          "dar_attn_prefill_TFLOP/s": attn_f / attn_ms / 1e9}
+        dom_attn = attn_ms >= proj_ms
+        dom_flops, dom_ms = (attn_f, attn_ms) if dom_attn else (proj_f, proj_ms)
+        achieved = dom_flops / dom_ms / 1e9
+        res["roofline"] = {"kernel": "attn_prefill_bf16<64>" if dom_attn else "project GEMMs",
+                           "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": None}
+        if not args.no_cpu:
+            import oracle
+            log("cpu baseline: oracle on one sequence")
+            res["cpu_baseline"] = cpu_baseline(oracle, inp, H, d_k, w, d_down)
+        del s, inp
+        if not args.no_sweep:
+            sweep = {}
+            for dd in (256, 64):
+                _, s2 = make_prefill(torch, dar, di, B, N, d, H, d_k, dd, seed=2000 + dd)
+                ms2, p2, a2 = time_prefill(torch, dar, s2, H, d_k, w, args.steps, args.warmup)
+                pf, af = prefill_flops(B, N, d, dd)
+                sweep["d_down%d" % dd] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9}
+                del s2
+            for name, cfg in (("pythia410m B8 N2048 d1024 H16 dk64 w128 d_down256",
+                               (8, 2048, 1024, 16, 64, 128, 256)),
+                              ("1b B4 N8192 d2048 H16 dk128 w512 d_down512",
+                               (4, 8192, 2048, 16, 128, 512, 512))):
+                b_, n_, d_, h_, k_, w_, dd_ = cfg
+                _, s3 = make_prefill(torch, dar, di, b_, n_, d_, h_, k_, dd_, seed=3000)
+                ms3, p3, a3 = time_prefill(torch, dar, s3, h_, k_, w_, max(3, args.steps // 4),
+                                           2)
+                pf, af = prefill_flops(b_, n_, d_, dd_)
+                sweep[name] = {"ms": ms3, "TFLOP/s": (pf + af) / ms3 / 1e9,
+                               "proj_ms": p3, "attn_ms": a3,
+                               "attn_TFLOP/s": af / a3 / 1e9, "proj_TFLOP/s": pf / p3 / 1e9}
+                log("%s: %.3f ms, %.1f TFLOP/s" % (name, ms3, (pf + af) / ms3 / 1e9))
+                del s3
+            res["sweep"] = sweep
+        torch.cuda.empty_cache()
+    if args.only in ("all", "decode"):
+        log("decode: building the 32k-context cache")
+        dec = time_decode(torch, dar, di, max(3, args.steps // 2), 2,
+                          (16, 32768, 2048, 16, 128, 256, 512))
+        log("decode: %.3f ms, %.0f GB/s, %.1f TFLOP/s" % (dec["ms"], dec["GB/s"], dec["TFLOP/s"]))
+        res["decode"] = dec
+        if res["value"] is None:
+            res.update(value=dec["GB/s"], unit="GB/s", ms_per_step=dec["ms"])
+            res["config"] = {"workload": dec["workload"], "global_batch": 16, "seq_len": 32768,
+                             "parallelism": "none (1 GPU)"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+"""DAR (Distance-Adaptive Representation) attention forward pass on MI355X.
+
+Thin ctypes binding over ``libdar.so`` (C ABI in ``include/dar.h``).  The
+functions below only marshal arguments: torch tensors provide device memory
+and the current HIP stream; every step of the computation runs in the HIP
+kernels of the library.  There is no fallback: if the library is missing or
+a call fails, an exception is raised.
+
+Method: "Dual Dimensionality for Local and Global Attention", Eqs. (1)-(4).
+Weights are column-major (pass a [out, in] tensor, the nn.Linear layout: the
+equations' W in R^{in x out} transposed and made contiguous).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdar.so")
+
+DAR_FP32, DAR_BF16 = 0, 1
+STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
+          3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
+# Every entry point include/dar.h declares.
+EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
+           "dar_attn_prefill", "dar_attn_decode")
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.POINTER(ctypes.c_size_t)
+
+
+class DarError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s returned %s" % (fn, STATUS.get(status, str(status))))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdar.so (built by ``distance_adaptive_dual_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libdar.so is not built; run python -m distance_adaptive_dual_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.dar_abi_version.restype = _I
+        L.dar_status_string.restype = ctypes.c_char_p
+        L.dar_status_string.argtypes = [_I]
+        L.dar_fold.restype = _I
+        L.dar_fold.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]
+        L.dar_project.restype = _I
+        L.dar_project.argtypes = [_P] * 8 + [_I] * 7 + [ctypes.c_float, _I] + [_P] * 7 + [_SZ, _P]
+        L.dar_attn_prefill.restype = _I
+        L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P]
+        L.dar_attn_decode.restype = _I
+        L.dar_attn_decode.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P, _SZ, _P]
+        _lib = L
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DAR_BF16
+    if t.dtype == torch.float32:
+        return DAR_FP32
+    raise TypeError("DAR tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("DAR tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("DAR tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DarError(fn, status)
+
+
+def _workspace(nbytes: int, like):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
+def dar_fold(W_up, W_K, W_V, heads: int, d_k: int, W_upK=None, W_upV=None, stream=None):
+    """W_upK = W_up W_K, W_upV = W_up W_V (column-major, [heads*d_k, d_down] tensors)."""
+    torch = _torch()
+    d_down, d = W_up.shape[1], W_up.shape[0]  # W_up given as [d, d_down] (column-major)
+    hd = heads * d_k
+    if W_upK is None:
+        W_upK = torch.empty((hd, d_down), dtype=W_up.dtype, device=W_up.device)
+    if W_upV is None:
+        W_upV = torch.empty((hd, d_down), dtype=W_up.dtype, device=W_up.device)
+    st = lib().dar_fold(_ptr(W_up), _ptr(W_K), _ptr(W_V), d, d_down, heads, d_k,
+                        _dtype_code(W_up), _ptr(W_upK), _ptr(W_upV), _stream(stream))
+    _check("dar_fold", st)
+    return W_upK, W_upV
+
+
+def _fake(i: int) -> int:
+    """Distinct, aligned, never-dereferenced addresses for size queries (the
+    library only compares them when workspace is NULL)."""
+    return (1 << 44) + (i << 38)
+
+
+def project_workspace_bytes(B, N, d, d_down, heads, d_k, pos0=0, folded=True, dtype=DAR_BF16):
+    n = ctypes.c_size_t(0)
+    f = [_fake(i) for i in range(14)]
+    st = lib().dar_project(f[0], f[1], f[2], f[3], f[4], f[5],
+                           f[6] if folded else None, f[7] if folded else None,
+                           B, N, d, d_down, heads, d_k, pos0, 10000.0, dtype,
+                           f[8], f[9], f[10], f[11], f[12], f[13], None, ctypes.byref(n), None)
+    _check("dar_project", st)
+    return n.value
+
+
+def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None, W_upV=None,
+                pos0: int = 0, rope_base: float = 10000.0, out=None, workspace=None,
+                stream=None):
+    """Eqs. (1)-(3) projections.  Returns dict Q, K_loc, V_loc, h_D, K_glob, V_glob.
+
+    h [B, N, d]; weights column-major ([out, in] tensors).  V_loc / V_glob come
+    back as [B, heads, d_k, N] (token innermost)."""
+    torch = _torch()
+    B, N, d = h.shape
+    d_down = W_down.shape[0]
+    dt = _dtype_code(h)
+    if out is None:
+        kw = dict(dtype=h.dtype, device=h.device)
+        out = dict(Q=torch.empty((B, heads, N, d_k), **kw),
+                   K_loc=torch.empty((B, heads, N, d_k), **kw),
+                   V_loc=torch.empty((B, heads, d_k, N), **kw),
+                   h_D=torch.empty((B, N, d_down), **kw),
+                   K_glob=torch.empty((B, heads, N, d_k), **kw),
+                   V_glob=torch.empty((B, heads, d_k, N), **kw))
+    L = lib()
+    n = ctypes.c_size_t(0)
+    args_in = [_ptr(h), _ptr(W_down), _ptr(W_up), _ptr(W_Q), _ptr(W_K), _ptr(W_V),
+               _ptr(W_upK), _ptr(W_upV), B, N, d, d_down, heads, d_k, pos0,
+               float(rope_base), dt]
+    outs = [_ptr(out[k]) for k in ("Q", "K_loc", "V_loc", "h_D", "K_glob", "V_glob")]
+    st = L.dar_project(*args_in, *outs, None, ctypes.byref(n), None)
+    _check("dar_project", st)
+    if workspace is None or workspace.numel() < n.value:
+        workspace = _workspace(n.value, h)
+    n = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
+    st = L.dar_project(*args_in, *outs, _ptr(workspace), ctypes.byref(n), _stream(stream))
+    _check("dar_project", st)
+    return out
+
+
+def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=None):
+    """Eq. (4) with the Eq. (3) selection.  Returns o [B, N, heads*d_k]."""
+    torch = _torch()
+    B, H, N, d_k = Q.shape
+    if o is None:
+        o = torch.empty((B, N, H * d_k), dtype=Q.dtype, device=Q.device)
+    st = lib().dar_attn_prefill(_ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(K_glob), _ptr(V_glob),
+                                B, N, H, d_k, int(w), _dtype_code(Q), _ptr(o), _stream(stream))
+    _check("dar_attn_prefill", st)
+    return o
+
+
+def decode_workspace_bytes(B, ctx_len, cap, heads, d_k, d_down, w, dtype=DAR_BF16):
+    n = ctypes.c_size_t(0)
+    f = [_fake(i) for i in range(7)]
+    st = lib().dar_attn_decode(f[0], f[1], f[2], f[3], f[4], f[5], B, ctx_len, cap, heads, d_k,
+                               d_down, w, 10000.0, dtype, f[6], None, ctypes.byref(n), None)
+    _check("dar_attn_decode", st)
+    return n.value
+
+
+def dar_attn_decode(q, K_win, V_win, h_D, W_upK, W_upV, ctx_len: int, w: int,
+                    rope_base: float = 10000.0, o=None, workspace=None, stream=None):
+    """One query per sequence at position ctx_len-1 over the mixed cache.  Returns o [B, heads*d_k]."""
+    torch = _torch()
+    B, H, d_k = q.shape
+    cap, d_down = h_D.shape[1], h_D.shape[2]
+    if o is None:
+        o = torch.empty((B, H * d_k), dtype=q.dtype, device=q.device)
+    L = lib()
+    n = ctypes.c_size_t(0)
+    head = [_ptr(q), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D),
+            _ptr(W_upK), _ptr(W_upV), B, int(ctx_len), cap, H, d_k, d_down, int(w),
+            float(rope_base), _dtype_code(q), _ptr(o)]
+    st = L.dar_attn_decode(*head, None, ctypes.byref(n), None)
+    _check("dar_attn_decode", st)
+    if workspace is None or workspace.numel() < n.value:
+        workspace = _workspace(n.value, q)
+    n = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
+    st = L.dar_attn_decode(*head, _ptr(workspace), ctypes.byref(n), _stream(stream))
+    _check("dar_attn_decode", st)
+    return o

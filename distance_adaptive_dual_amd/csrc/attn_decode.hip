@@ -1,0 +1,474 @@
+// Decode over the mixed cache.
+//
+// "Dual Dimensionality for Local and Global Attention": at inference every
+// past token contributes through exactly one path (the remark after Eq. (5)),
+// so the cache keeps full keys/values only for the w most recent positions and
+// the d_down-wide latent h^D_j (Eq. 1) for every older position j.  For the
+// query at position p:
+//   j >  p - w : k_j, v_j read from the window ring (slot j mod w)
+//   j <= p - w : k_j = RoPE_j(h^D_j W_upK), v_j = h^D_j W_upV   (Eqs. 2-3,
+//                W_upK = W_up W_K and W_upV = W_up W_V folded once)
+// and o = softmax(q K^T / sqrt(d_k)) V (Eq. 4).
+//
+// Keys of distant tokens must be rebuilt: RoPE at position j sits between
+// W_upK and q, so W_upK cannot be absorbed into the query.  Values can: no
+// rotation acts on them, so sum_j p_j h^D_j W_upV = (sum_j p_j h^D_j) W_upV
+// and the latent kernel accumulates sum_j p_j h^D_j in d_down-space only.
+//
+// Three launches:
+//  latent  -- one workgroup per (batch, head group, context chunk), 8 waves.
+//             Each wave keeps 64 rows of W_upK^T in registers: 32 rotary
+//             frequencies t of one head and their rotate-half partners
+//             t + d_k/2, so a rebuilt key's two rotated components meet in one
+//             lane.  32-token latent blocks stream through LDS (double
+//             buffered); K'^T = W^T L^T on 32x32x16 MFMAs; RoPE + q.k per lane;
+//             an online softmax per head; sum_j p_j h^D_j on 16x16x32 MFMAs.
+//             Writes (max, sum, latent accumulator) per chunk.
+//  window  -- one workgroup per (batch, head): the w full keys/values.
+//  combine -- log-sum-exp merge of all partials, then one lift by W_upV.
+// Scores are kept in base 2 (log2(e)/sqrt(d_k) folded into q).
+#include <math.h>
+
+#include "dar_common.hpp"
+
+namespace dar {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int TB = 32;        // tokens per latent block
+constexpr int NWAVE = 8;      // waves per latent workgroup
+constexpr int TARGET_WG = 1024;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct DecodeGeom {
+  int n_glob;      // latent positions 0 .. n_glob-1
+  int n_chunks;    // context chunks per (batch, head group)
+  int chunk_len;   // tokens per chunk (multiple of TB)
+  int heads_per_wg;
+  int n_hg;        // head groups
+  int pairs;       // B * n_chunks, padded to a multiple of kNumXcd
+  size_t part_lat_floats;  // per (b, head, chunk): 2 + d_down
+};
+
+DecodeGeom geom(const DecodeProblem& p) {
+  DecodeGeom g{};
+  const long pp = (long)p.ctx - 1;
+  g.n_glob = (int)(pp - p.w + 1 > 0 ? pp - p.w + 1 : 0);
+  g.heads_per_wg = NWAVE * 64 / p.d_k;
+  g.n_hg = (p.H + g.heads_per_wg - 1) / g.heads_per_wg;
+  const int blocks = (g.n_glob + TB - 1) / TB;
+  int want = TARGET_WG / (p.B * g.n_hg);
+  if (want < 1) want = 1;
+  if (want > blocks) want = blocks > 0 ? blocks : 1;
+  const int bpc = (blocks + want - 1) / want > 0 ? (blocks + want - 1) / want : 1;
+  g.chunk_len = bpc * TB;
+  g.n_chunks = g.n_glob > 0 ? (g.n_glob + g.chunk_len - 1) / g.chunk_len : 1;
+  g.pairs = (p.B * g.n_chunks + kNumXcd - 1) / kNumXcd * kNumXcd;
+  g.part_lat_floats = 2 + (size_t)p.d_down;
+  return g;
+}
+
+// --------------------------------------------------------------------------
+template <int D, int KS>
+struct LatentSmem {
+  static constexpr int DD = KS * 16;   // d_down
+  static constexpr int LP = DD + 8;    // bf16 per latent row (16 B pad)
+  static constexpr int HPW = NWAVE * 64 / D;
+  bf16 lat[2][TB * LP];                // latent blocks
+  float2 lo[64 * (D / 2)];             // fine RoPE table
+  float2 hi[2][D / 2];                 // coarse RoPE row of the current block
+  float sc[NWAVE][TB];                 // per-wave partial scores
+  bf16 pm[16][TB + 8];                 // probabilities, rows = heads of the group
+  float alpha[16];
+};
+
+template <int D, int KS>
+__global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeGeom g) {
+  using S = LatentSmem<D, KS>;
+  constexpr int DD = S::DD, LP = S::LP, HPW = S::HPW, WPH = D / 64, HALF = D / 2;
+  __shared__ S sm;
+
+  // XCD-aware order: the head groups of one (batch, chunk) run on one XCD so
+  // its latent block is fetched from HBM once and served to the rest by L2.
+  const int bid = blockIdx.x;
+  const int x = bid % kNumXcd, k = bid / kNumXcd;
+  const int pair = x + kNumXcd * (k / g.n_hg), hg = k % g.n_hg;
+  if (pair >= p.B * g.n_chunks) return;
+  const int b = pair / g.n_chunks, chunk = pair % g.n_chunks;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int hl = wave / WPH, tb = wave % WPH;
+  const int head = hg * HPW + hl;
+  const bool head_ok = head < p.H;
+
+  const int j_begin = chunk * g.chunk_len;
+  const int j_end = min(g.n_glob, j_begin + g.chunk_len);
+  const int nblk = j_end > j_begin ? (j_end - j_begin + TB - 1) / TB : 0;
+
+  // fine RoPE table -> LDS
+  for (int e = tid; e < 64 * HALF; e += 512) sm.lo[e] = p.rope.lo[e];
+
+  // This wave's rows of W_upK^T: t = 32 tb + rho and its partner t + D/2.
+  const bf16* Wk = (const bf16*)p.W_upK;
+  bf16x8 wf[2][KS];
+  {
+    const int hrow = (head_ok ? head : 0) * D + 32 * tb + lr;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        wf[mb][ks] = *(const bf16x8*)(Wk + (size_t)(hrow + mb * HALF) * DD + 16 * ks + 8 * lg);
+  }
+  // q components of this lane's 16 frequencies, scaled into base-2 logits
+  float q1[16], q2[16];
+  {
+    const bf16* qp = (const bf16*)p.q + ((size_t)b * p.H + (head_ok ? head : 0)) * D;
+    const float sc = kLog2e / sqrtf((float)D);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * tb + 8 * (r >> 2) + 4 * lg + (r & 3);
+      q1[r] = (float)qp[t] * sc;
+      q2[r] = (float)qp[t + HALF] * sc;
+    }
+  }
+
+  const bf16* Lb = (const bf16*)p.h_D + (size_t)b * p.cap * DD;
+  // staging: TB*DD bf16 = TB*DD/8 chunks of 16 B
+  constexpr int NCH = TB * DD / 8;
+  constexpr int CPT = (NCH + 511) / 512;
+  u32x4 stg[CPT];
+  auto load_blk = [&](int blk) {
+    const int j0 = j_begin + blk * TB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 512 * i;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (c < NCH) {
+        const int row = c / (DD / 8), col = (c % (DD / 8)) * 8;
+        if (j0 + row < j_end) v = *(const u32x4*)(Lb + (size_t)(j0 + row) * DD + col);
+      }
+      stg[i] = v;
+    }
+  };
+  auto store_blk = [&](int buf, int blk) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 512 * i;
+      if (c < NCH) {
+        const int row = c / (DD / 8), col = (c % (DD / 8)) * 8;
+        *(u32x4*)(&sm.lat[buf][row * LP + col]) = stg[i];
+      }
+    }
+    const int j0 = j_begin + blk * TB;
+    for (int e = tid; e < HALF; e += 512) sm.hi[buf][e] = p.rope.hi[(size_t)(j0 >> 6) * HALF + e];
+  };
+
+  // softmax state (kept by lanes of wave hl for head hl, hl < HPW)
+  float m_run = -INFINITY, l_run = 0.f;
+  // latent accumulator: 16x16 tiles over d_down, rows = heads of the group
+  constexpr int NB = DD / 16;                     // n-blocks of 16 latent dims
+  constexpr int NB_PER_WAVE = (NB + NWAVE - 1) / NWAVE;
+  f32x4 acc[NB_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < NB_PER_WAVE; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) {
+    load_blk(0);
+    store_blk(0, 0);
+  }
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    const int j0 = j_begin + blk * TB;
+    if (blk + 1 < nblk) load_blk(blk + 1);
+
+    // rebuild 64 key components x 32 tokens: K'^T = W^T L^T
+    const bf16* lrow = &sm.lat[buf][lr * LP + 8 * lg];
+    f32x16 kc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) kc[mb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 lf = *(const bf16x8*)(lrow + 16 * ks);
+      kc[0] = mfma32x32x16(wf[0][ks], lf, kc[0]);
+      kc[1] = mfma32x32x16(wf[1][ks], lf, kc[1]);
+    }
+    // RoPE at position j, then this lane's share of q . k
+    const int pos = j0 + lr;
+    const float2* lo_row = &sm.lo[(pos & 63) * HALF];
+    float sp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * tb + 8 * (r >> 2) + 4 * lg + (r & 3);
+      const float2 a = sm.hi[buf][t], c = lo_row[t];
+      const float cs = a.x * c.x - a.y * c.y, sn = a.x * c.y + a.y * c.x;
+      const float k1 = kc[0][r], k2 = kc[1][r];
+      sp += k1 * (q1[r] * cs + q2[r] * sn) + k2 * (q2[r] * cs - q1[r] * sn);
+    }
+    sp += __shfl_xor(sp, 32);
+    if (lg == 0) sm.sc[wave][lr] = sp;
+    __syncthreads();
+
+    // online softmax per head: wave hl, lanes 0..31 (one token each)
+    if (wave < HPW) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < WPH; ++i) s += sm.sc[wave * WPH + i][lr];
+      const bool ok = (hg * HPW + wave < p.H) && (j0 + lr < j_end);
+      s = ok ? s : -INFINITY;
+      float mt = s;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+      const float m_new = fmaxf(m_run, mt);
+      const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      const float e = (m_new == -INFINITY) ? 0.f : exp2f(s - m_new);
+      float es = e;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) es += __shfl_xor(es, off);
+      l_run = l_run * al + es;
+      m_run = m_new;
+      if (lg == 0) sm.pm[wave][lr] = (bf16)e;
+      if (lane == 0) sm.alpha[wave] = al;
+    }
+    __syncthreads();
+
+    // acc[head, dims] = alpha * acc + P L  (16x16x32 MFMA, K = the 32 tokens)
+#pragma unroll
+    for (int i = 0; i < NB_PER_WAVE; ++i) {
+      const int nb = wave + NWAVE * i;
+      if (nb < NB) {
+        const int row = lane & 15, kg = lane >> 4;
+        bf16x8 af;
+        if (row < HPW) {
+          af = *(const bf16x8*)(&sm.pm[row][8 * kg]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) af[c] = (bf16)0.f;
+        }
+        bf16x8 bfr;
+        const int n = nb * 16 + row;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bfr[c] = sm.lat[buf][(8 * kg + c) * LP + n];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hrow = 4 * kg + r;
+          acc[i][r] *= (hrow < HPW) ? sm.alpha[hrow] : 1.f;
+        }
+        acc[i] = mfma16x16x32(af, bfr, acc[i]);
+      }
+    }
+    if (blk + 1 < nblk) store_blk(buf ^ 1, blk + 1);
+    __syncthreads();
+  }
+
+  // partials: part[((b*H + head)*n_chunks + chunk)] = {m, l, acc[d_down]}
+  float* part = (float*)p.ws;
+  if (wave < HPW && lane == 0) {
+    const int hh = hg * HPW + wave;
+    if (hh < p.H) {
+      float* dst = part + (((size_t)b * p.H + hh) * g.n_chunks + chunk) * g.part_lat_floats;
+      dst[0] = m_run;
+      dst[1] = l_run;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NB_PER_WAVE; ++i) {
+    const int nb = wave + NWAVE * i;
+    if (nb < NB) {
+      const int col = nb * 16 + (lane & 15), kg = lane >> 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hrow = 4 * kg + r, hh = hg * HPW + hrow;
+        if (hrow < HPW && hh < p.H) {
+          float* dst = part + (((size_t)b * p.H + hh) * g.n_chunks + chunk) * g.part_lat_floats;
+          dst[2 + col] = acc[i][r];
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Window part: keys/values of positions max(0, p-w+1) .. p from the ring.
+template <int D>
+__global__ __launch_bounds__(256) void decode_window(DecodeProblem p, float* part_win) {
+  __shared__ float qs[D];
+  __shared__ float ps[256];
+  __shared__ float red[256];
+  __shared__ float accs[256 / D][D];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const long pp = (long)p.ctx - 1;
+  const long first = pp - p.w + 1 > 0 ? pp - p.w + 1 : 0;
+  const int nw = (int)(pp - first + 1 < p.w ? pp - first + 1 : p.w);
+  const float sc = kLog2e / sqrtf((float)D);
+  const bf16* qp = (const bf16*)p.q + (size_t)bh * D;
+  for (int d = tid; d < D; d += 256) qs[d] = (float)qp[d] * sc;
+  __syncthreads();
+  const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
+  const bf16* Vw = (const bf16*)p.V_win + (size_t)bh * p.w * D;
+  float m_run = -INFINITY, l_run = 0.f;
+  constexpr int KPB = 256 / D;  // key lanes in the value phase
+  const int vd = tid % D, vk = tid / D;
+  float acc = 0.f;
+  for (int c0 = 0; c0 < nw; c0 += 256) {
+    const int kk = c0 + tid;
+    float s = -INFINITY;
+    if (kk < nw) {
+      const long pos = first + kk;
+      const bf16* kr = Kw + (size_t)(pos % p.w) * D;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot += qs[d] * (float)kr[d];
+      s = dot;
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
+      __syncthreads();
+    }
+    const float m_new = fmaxf(m_run, red[0]);
+    __syncthreads();
+    const float al = exp2f(m_run - m_new);
+    const float e = (kk < nw) ? exp2f(s - m_new) : 0.f;
+    ps[tid] = e;
+    red[tid] = e;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if (tid < st) red[tid] += red[tid + st];
+      __syncthreads();
+    }
+    l_run = l_run * al + red[0];
+    m_run = m_new;
+    acc *= al;
+    const int lim = min(256, nw - c0);
+    for (int i = vk; i < lim; i += KPB) {
+      const long pos = first + c0 + i;
+      acc += ps[i] * (float)Vw[(size_t)(pos % p.w) * D + vd];
+    }
+    __syncthreads();
+  }
+  accs[vk][vd] = acc;
+  __syncthreads();
+  float* dst = part_win + (size_t)bh * (2 + D);
+  if (tid < D) {
+    float a = 0.f;
+    for (int i = 0; i < KPB; ++i) a += accs[i][tid];
+    dst[2 + tid] = a;
+  }
+  if (tid == 0) {
+    dst[0] = m_run;
+    dst[1] = l_run;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Merge: o_h = (acc_lat W_upV_h + acc_win) / l with every partial rescaled to
+// the common maximum.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeom g,
+                                                      const float* part_lat,
+                                                      const float* part_win) {
+  __shared__ float lat[1024];
+  __shared__ float wsc[1024];
+  __shared__ float red[2];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int DD = p.d_down, nc = g.n_chunks;
+  const float* pl = part_lat + (size_t)bh * nc * g.part_lat_floats;
+  const float* pw = part_win + (size_t)bh * (2 + D);
+  if (tid == 0) {
+    float M = pw[1] > 0.f ? pw[0] : -INFINITY;
+    for (int c = 0; c < nc; ++c)
+      if (pl[(size_t)c * g.part_lat_floats + 1] > 0.f)
+        M = fmaxf(M, pl[(size_t)c * g.part_lat_floats]);
+    float L = 0.f;
+    for (int c = 0; c < nc; ++c) {
+      const float* e = pl + (size_t)c * g.part_lat_floats;
+      const float f = (e[1] > 0.f) ? exp2f(e[0] - M) : 0.f;
+      wsc[c] = f;
+      L += f * e[1];
+    }
+    const float fw = (pw[1] > 0.f) ? exp2f(pw[0] - M) : 0.f;
+    L += fw * pw[1];
+    red[0] = fw;
+    red[1] = L;
+  }
+  __syncthreads();
+  for (int kk = tid; kk < DD; kk += 256) {
+    float a = 0.f;
+    for (int c = 0; c < nc; ++c) a += wsc[c] * pl[(size_t)c * g.part_lat_floats + 2 + kk];
+    lat[kk] = a;
+  }
+  __syncthreads();
+  const int h = bh % p.H;
+  const bf16* Wv = (const bf16*)p.W_upV + (size_t)h * D * DD;
+  const float inv = 1.f / red[1];
+  for (int t = tid; t < D; t += 256) {
+    const bf16* wr = Wv + (size_t)t * DD;
+    float a = 0.f;
+    for (int kk = 0; kk < DD; ++kk) a += lat[kk] * (float)wr[kk];
+    a += red[0] * pw[2 + t];
+    ((bf16*)p.o)[(size_t)bh * D + t] = (bf16)(a * inv);
+  }
+}
+
+template <int D, int KS>
+hipError_t launch_latent(const DecodeProblem& p, const DecodeGeom& g, hipStream_t s) {
+  const int grid = g.pairs * g.n_hg;
+  hipLaunchKernelGGL((decode_latent<D, KS>), dim3(grid), dim3(512), 0, s, p, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(const DecodeProblem& p) {
+  const DecodeGeom g = geom(p);
+  const size_t lat = sizeof(float) * (size_t)p.B * p.H * g.n_chunks * g.part_lat_floats;
+  const size_t win = sizeof(float) * (size_t)p.B * p.H * (2 + p.d_k);
+  return ((lat + 255) & ~(size_t)255) + ((win + 255) & ~(size_t)255);
+}
+
+hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
+  const DecodeGeom g = geom(p);
+  float* part_lat = (float*)p.ws;
+  const size_t lat = sizeof(float) * (size_t)p.B * p.H * g.n_chunks * g.part_lat_floats;
+  float* part_win = (float*)((char*)p.ws + ((lat + 255) & ~(size_t)255));
+  hipError_t e = hipSuccess;
+  const int KS = p.d_down / 16;
+#define DAR_LAT(DV, KV) \
+  if (p.d_k == DV && KS == KV) e = launch_latent<DV, KV>(p, g, s);
+  DAR_LAT(64, 2)
+  DAR_LAT(64, 4)
+  DAR_LAT(64, 8)
+  DAR_LAT(64, 16)
+  DAR_LAT(128, 2)
+  DAR_LAT(128, 4)
+  DAR_LAT(128, 8)
+  DAR_LAT(128, 16)
+#undef DAR_LAT
+  if (e != hipSuccess) return e;
+  if (p.d_k == 64) {
+    hipLaunchKernelGGL(decode_window<64>, dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+    hipLaunchKernelGGL(decode_combine<64>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
+                       part_win);
+  } else {
+    hipLaunchKernelGGL(decode_window<128>, dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+    hipLaunchKernelGGL(decode_combine<128>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
+                       part_win);
+  }
+  return hipGetLastError();
+}
+
+bool decode_supported(int d_k, int d_down) {
+  const int KS = d_down / 16;
+  return (d_k == 64 || d_k == 128) && d_down % 16 == 0 && (KS == 2 || KS == 4 || KS == 8 || KS == 16);
+}
+
+}  // namespace dar

@@ -1,0 +1,269 @@
+// C ABI of the DAR attention library: argument validation, workspace sizing
+// and launches on the caller's stream.  No allocation, no state, no host
+// synchronisation.  The kernels live in rope.hip, gemm.hip, attn_prefill.hip
+// and attn_decode.hip.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "dar_common.hpp"
+
+using namespace dar;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+size_t elem_size(dar_dtype dt) { return dt == DAR_BF16 ? 2 : 4; }
+bool dtype_ok(dar_dtype dt) { return dt == DAR_BF16 || dt == DAR_FP32; }
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every input and every other output.
+bool disjoint(const Span* outs, int nout, const Span* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return false;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return false;
+  }
+  return true;
+}
+
+// Limits of the kernels (DAR_ERR_UNSUPPORTED beyond them).
+bool head_supported(int d_k) { return d_k == 64 || d_k == 128; }
+
+dar_status hip_status(hipError_t e) { return e == hipSuccess ? DAR_OK : DAR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dar_abi_version(void) { return kAbiVersion; }
+
+const char* dar_status_string(dar_status s) {
+  switch (s) {
+    case DAR_OK: return "DAR_OK";
+    case DAR_ERR_INVALID_ARG: return "DAR_ERR_INVALID_ARG";
+    case DAR_ERR_UNSUPPORTED: return "DAR_ERR_UNSUPPORTED";
+    case DAR_ERR_WORKSPACE: return "DAR_ERR_WORKSPACE";
+    case DAR_ERR_HIP: return "DAR_ERR_HIP";
+  }
+  return "DAR_ERR_UNKNOWN";
+}
+
+dar_status dar_fold(const void* W_up, const void* W_K, const void* W_V, int d, int d_down,
+                    int heads, int d_k, dar_dtype dtype, void* W_upK, void* W_upV,
+                    hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1)) return DAR_ERR_INVALID_ARG;
+  if (!aligned16(W_up) || !aligned16(W_K) || !aligned16(W_V) || !aligned16(W_upK) ||
+      !aligned16(W_upV))
+    return DAR_ERR_INVALID_ARG;
+  const int hd = heads * d_k;
+  const size_t es = elem_size(dtype);
+  const Span ins[3] = {{W_up, es * d_down * d}, {W_K, es * d * hd}, {W_V, es * d * hd}};
+  const Span outs[2] = {{W_upK, es * d_down * hd}, {W_upV, es * d_down * hd}};
+  if (!disjoint(outs, 2, ins, 3)) return DAR_ERR_INVALID_ARG;
+  if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
+    return DAR_ERR_UNSUPPORTED;
+  hipError_t e = launch_fold(W_up, W_K, W_upK, d, d_down, hd, dtype, stream);
+  if (e == hipSuccess) e = launch_fold(W_up, W_V, W_upV, d, d_down, hd, dtype, stream);
+  return hip_status(e);
+}
+
+dar_status dar_project(const void* h, const void* W_down, const void* W_up, const void* W_Q,
+                       const void* W_K, const void* W_V, const void* W_upK, const void* W_upV,
+                       int B, int N, int d, int d_down, int heads, int d_k, int pos0,
+                       float rope_base, dar_dtype dtype, void* Q, void* K_loc, void* V_loc,
+                       void* h_D, void* K_glob, void* V_glob, void* workspace,
+                       size_t* workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || pos0 < 0)
+    return DAR_ERR_INVALID_ARG;
+  if (!(rope_base > 1.0f)) return DAR_ERR_INVALID_ARG;
+  if ((long)pos0 + N - 1 > 0x7fffffffL) return DAR_ERR_INVALID_ARG;
+  const bool have_fold = (W_upK != nullptr) || (W_upV != nullptr);
+  if (have_fold && (!aligned16(W_upK) || !aligned16(W_upV))) return DAR_ERR_INVALID_ARG;
+  if (!have_fold && !aligned16(W_up)) return DAR_ERR_INVALID_ARG;
+  const void* need[] = {h, W_down, W_Q, W_K, W_V, Q, K_loc, V_loc, h_D, K_glob, V_glob};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  const int hd = heads * d_k;
+  const size_t es = elem_size(dtype);
+  const size_t M = (size_t)B * N;
+  const Span ins[8] = {{h, es * M * d},           {W_down, es * d * d_down},
+                       {W_Q, es * d * hd},        {W_K, es * d * hd},
+                       {W_V, es * d * hd},        {have_fold ? nullptr : W_up, es * d_down * d},
+                       {W_upK, es * d_down * hd}, {W_upV, es * d_down * hd}};
+  const Span outs[6] = {{Q, es * M * hd},    {K_loc, es * M * hd}, {V_loc, es * M * hd},
+                        {h_D, es * M * d_down}, {K_glob, es * M * hd}, {V_glob, es * M * hd}};
+  if (!disjoint(outs, 6, ins, 8)) return DAR_ERR_INVALID_ARG;
+  if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
+    return DAR_ERR_UNSUPPORTED;
+
+  const long max_pos = (long)pos0 + N - 1;
+  const size_t rope_bytes = rope_table_bytes(d_k, max_pos);
+  const size_t fold_bytes = have_fold ? 0 : 2 * round256(es * d_down * hd);
+  const size_t need_bytes = rope_bytes + fold_bytes;
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& s : ins)
+      if (overlap(ws, s)) return DAR_ERR_INVALID_ARG;
+    for (const Span& s : outs)
+      if (overlap(ws, s)) return DAR_ERR_INVALID_ARG;
+  }
+
+  char* wsp = (char*)workspace;
+  float2* lo = (float2*)wsp;
+  float2* hi = lo + 64 * (d_k / 2);
+  hipError_t e = launch_rope_tables(lo, hi, d_k, max_pos, rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  const void* fK = W_upK;
+  const void* fV = W_upV;
+  if (!have_fold) {
+    void* k_out = wsp + rope_bytes;
+    void* v_out = wsp + rope_bytes + round256(es * d_down * hd);
+    e = launch_fold(W_up, W_K, k_out, d, d_down, hd, dtype, stream);
+    if (e == hipSuccess) e = launch_fold(W_up, W_V, v_out, d, d_down, hd, dtype, stream);
+    if (e != hipSuccess) return DAR_ERR_HIP;
+    fK = k_out;
+    fV = v_out;
+  }
+  const RopeTab rope{lo, hi, d_k / 2};
+
+  GemmProblem g1{};
+  g1.A = h;
+  g1.M = (int)M;
+  g1.K = d;
+  g1.nseg = 4;
+  g1.seg[0] = GemmSeg{W_Q, Q, hd, kHead, 1};
+  g1.seg[1] = GemmSeg{W_K, K_loc, hd, kHead, 1};
+  g1.seg[2] = GemmSeg{W_V, V_loc, hd, kHeadT, 0};
+  g1.seg[3] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0};
+  g1.n_seq = N;
+  g1.heads = heads;
+  g1.d_k = d_k;
+  g1.pos0 = pos0;
+  g1.rope = rope;
+  e = launch_project_gemm(g1, dtype, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+
+  GemmProblem g2 = g1;
+  g2.A = h_D;
+  g2.K = d_down;
+  g2.nseg = 2;
+  g2.seg[0] = GemmSeg{fK, K_glob, hd, kHead, 1};
+  g2.seg[1] = GemmSeg{fV, V_glob, hd, kHeadT, 0};
+  e = launch_project_gemm(g2, dtype, stream);
+  return hip_status(e);
+}
+
+dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
+                            const void* K_glob, const void* V_glob, int B, int N, int heads,
+                            int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || w < 0) return DAR_ERR_INVALID_ARG;
+  const void* need[] = {Q, K_loc, V_loc, K_glob, V_glob, o};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  const size_t sz = es * (size_t)B * N * heads * d_k;
+  const Span ins[5] = {{Q, sz}, {K_loc, sz}, {V_loc, sz}, {K_glob, sz}, {V_glob, sz}};
+  const Span outs[1] = {{o, sz}};
+  if (!disjoint(outs, 1, ins, 5)) return DAR_ERR_INVALID_ARG;
+  if (!head_supported(d_k)) return DAR_ERR_UNSUPPORTED;
+  if ((size_t)B * heads * N * d_k > 0x7fffffffffffL) return DAR_ERR_UNSUPPORTED;
+  PrefillProblem p{Q, K_loc, V_loc, K_glob, V_glob, o, B, N, heads, d_k, w};
+  return hip_status(launch_attn_prefill(p, dtype, stream));
+}
+
+dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
+                           const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
+                           int heads, int d_k, int d_down, int w, float rope_base,
+                           dar_dtype dtype, void* o, void* workspace, size_t* workspace_bytes,
+                           hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || ctx_len < 1 || cap < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_down < 1 ||
+      w < 0)
+    return DAR_ERR_INVALID_ARG;
+  if (!(rope_base > 1.0f)) return DAR_ERR_INVALID_ARG;
+  const long p_pos = (long)ctx_len - 1;
+  const long n_glob = std::max(0L, p_pos - w + 1);
+  if (n_glob > cap) return DAR_ERR_INVALID_ARG;
+  const void* need[] = {q, h_D, W_upK, W_upV, o};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
+  const int hd = heads * d_k;
+  const size_t es = elem_size(dtype);
+  const Span ins[6] = {{q, es * B * hd},
+                       {K_win, w > 0 ? es * B * hd * (size_t)w : 0},
+                       {V_win, w > 0 ? es * B * hd * (size_t)w : 0},
+                       {h_D, es * B * (size_t)cap * d_down},
+                       {W_upK, es * d_down * hd},
+                       {W_upV, es * d_down * hd}};
+  const Span outs[1] = {{o, es * B * hd}};
+  if (!disjoint(outs, 1, ins, 6)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!decode_supported(d_k, d_down) || hd % 64) return DAR_ERR_UNSUPPORTED;
+
+  DecodeProblem p{};
+  p.q = q;
+  p.K_win = K_win;
+  p.V_win = V_win;
+  p.h_D = h_D;
+  p.W_upK = W_upK;
+  p.W_upV = W_upV;
+  p.o = o;
+  p.B = B;
+  p.ctx = ctx_len;
+  p.cap = cap;
+  p.H = heads;
+  p.d_k = d_k;
+  p.d_down = d_down;
+  p.w = w;
+  const size_t rope_bytes = rope_table_bytes(d_k, std::max(0L, n_glob - 1));
+  const size_t need_bytes = rope_bytes + decode_workspace_bytes(p);
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& s : ins)
+      if (overlap(ws, s)) return DAR_ERR_INVALID_ARG;
+    if (overlap(ws, outs[0])) return DAR_ERR_INVALID_ARG;
+  }
+  char* wsp = (char*)workspace;
+  float2* lo = (float2*)wsp;
+  float2* hi = lo + 64 * (d_k / 2);
+  hipError_t e = launch_rope_tables(lo, hi, d_k, std::max(0L, n_glob - 1), rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  p.rope = RopeTab{lo, hi, d_k / 2};
+  p.ws = wsp + rope_bytes;
+  return hip_status(launch_attn_decode(p, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Shared device helpers for the DAR attention kernels (gfx950 / CDNA4 only).
+//
+// Everything here is plumbing: vector types for the MFMA operands, bf16
+// conversion, the RoPE cos/sin lookup and the internal launch declarations.
+// The method's arithmetic lives in the kernels that include this header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dar.h"
+
+namespace dar {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workgroups are handed to the 8 XCDs of an MI355X round-robin by linear id.
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+  return (bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+}
+
+// Two fp32 values -> one dword of two bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout (wave64):
+// lane l supplies row/column (l % 32) and contraction elements
+// [8*(l/32), 8*(l/32)+8) of the 16-wide step.  Result register r of lane l
+// holds row 8*(r/4) + 4*(l/32) + (r%4), column (l % 32).
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
+                                               const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// RoPE angle lookup.  cos/sin(p * theta_t) is the complex product of a
+// coarse entry (p >> 6) and a fine entry (p & 63); both tables are computed
+// in fp64 and stored as fp32 (cos, sin) pairs, row length d_k/2.
+struct RopeTab {
+  const float2* lo;  // [64][half]
+  const float2* hi;  // [n_hi][half]
+  int half;
+};
+
+__device__ __forceinline__ float2 rope_cs(const RopeTab& t, int pos, int k) {
+  const float2 a = t.hi[(size_t)(pos >> 6) * t.half + k];
+  const float2 b = t.lo[(size_t)(pos & 63) * t.half + k];
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+// ----------------------------------------------------------------------------
+// Internal launchers (defined in the .hip files, called by the C ABI layer).
+// All return hipSuccess or the launch error.
+
+// RoPE tables for positions [0, max_pos], written into lo / hi.
+size_t rope_table_bytes(int d_k, long max_pos);
+hipError_t launch_rope_tables(float2* lo, float2* hi, int d_k, long max_pos, float base,
+                              hipStream_t s);
+
+// Output kinds of the projection GEMM epilogue.
+enum OutKind : int {
+  kRowMajor = 0,  // out[row, col]                     (h^D, folded weights)
+  kHead = 1,      // out[b, head, n, t]                (Q, K_loc, K_glob)
+  kHeadT = 2      // out[b, head, t, n]                (V_loc, V_glob)
+};
+
+struct GemmSeg {
+  const void* Bt;  // operand, [width, K] row-major (column-major weight)
+  void* out;
+  int width;       // number of output columns in this segment
+  int kind;        // OutKind
+  int rope;        // rotate (kind == kHead only)
+};
+
+struct GemmProblem {
+  const void* A;  // [M, K] row-major
+  int M, K;
+  int nseg;
+  GemmSeg seg[4];
+  int n_seq;  // rows per sequence (row -> (b, n))
+  int heads, d_k, pos0;
+  RopeTab rope;
+};
+
+hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s);
+
+// W_upK^T = W_K^T W_up^T etc. (the fold), fp32 accumulate.
+hipError_t launch_fold(const void* W_up, const void* W_KV, void* out, int d, int d_down, int hd,
+                       dar_dtype dt, hipStream_t s);
+
+struct PrefillProblem {
+  const void *Q, *K_loc, *V_loc, *K_glob, *V_glob;
+  void* o;
+  int B, N, H, d_k, w;
+};
+hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s);
+
+struct DecodeProblem {
+  const void *q, *K_win, *V_win, *h_D, *W_upK, *W_upV;
+  void* o;
+  int B, ctx, cap, H, d_k, d_down, w;
+  RopeTab rope;
+  void* ws;  // workspace after the rope tables
+};
+size_t decode_workspace_bytes(const DecodeProblem& p);
+bool decode_supported(int d_k, int d_down);  // d_k in {64,128}, d_down in {32,64,128,256}
+hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s);
+
+}  // namespace dar

@@ -1,0 +1,154 @@
+/*
+ * dar.h -- C ABI of the DAR (Distance-Adaptive Representation) attention
+ * forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Dual Dimensionality for Local and Global Attention".
+ *   Eq. (1)  h^D_j = h_j W_down                     (W_down in R^{d x d_down})
+ *   Eq. (2)  h'_j  = h^D_j W_up                     (W_up   in R^{d_down x d})
+ *   Eq. (3)  k_j = RoPE(h_j W_K), v_j = h_j W_V     if i - j <  w   (local path)
+ *            k_j = RoPE(h'_j W_K), v_j = h'_j W_V   otherwise       (global path)
+ *   Eq. (4)  o_i = softmax(q_i K_i^T / sqrt(d_k)) V_i, q_i = h_i W_Q, causal j <= i
+ * Multi-head attention replicates the construction per head (the paragraph
+ * after Eq. (1)); one W_down / W_up is shared by all heads.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers are DEVICE pointers, owned by the caller.  The library
+ *    never allocates, keeps no state between calls and is re-entrant.
+ *  - Work is enqueued on `stream` (NULL = the default stream); calls return
+ *    after enqueue.  Device faults surface at the caller's next sync.
+ *  - Activations are row-major with the innermost index contiguous.
+ *  - WEIGHTS ARE COLUMN-MAJOR: a matrix W in R^{r x c} of the equations is
+ *    stored with element (row k, column n) at offset n*r + k, i.e. each
+ *    output column is contiguous.  These are the same bytes as a row-major
+ *    [c, r] array (the layout of a torch.nn.Linear weight).  The MFMA GEMMs
+ *    read both operands along the contraction index, so no transpose runs.
+ *  - dtype DAR_BF16: every float tensor is bfloat16; arithmetic is MFMA with
+ *    fp32 accumulation, softmax in fp32.  DAR_FP32: every float tensor is
+ *    float32 and every step is computed in fp32 (no bf16 rounding anywhere).
+ *  - Positions are 0-based: token n of a prefill sits at position pos0 + n.
+ *    RoPE uses rotate-half pairs (t, t + d_k/2) over the full head width with
+ *    theta_t = rope_base^(-2t/d_k), applied to queries and keys alike.
+ *  - Workspace protocol: if `workspace` is NULL the call writes the bytes it
+ *    needs to *workspace_bytes and returns DAR_OK without touching the
+ *    device.  Otherwise *workspace_bytes must be at least that size
+ *    (DAR_ERR_WORKSPACE if not).  Workspace must be 256-byte aligned.
+ *  - Validation happens before any device work; on an error nothing is
+ *    launched and no output is written.  DAR_ERR_INVALID_ARG: null or
+ *    misaligned (16 B) pointer, a size < 1 (w < 0, pos0 < 0), an odd d_k.
+ *    DAR_ERR_UNSUPPORTED: outside the kernels' limits (d_k in {64, 128};
+ *    d % 64 == 0; d_down % 32 == 0, d_down <= 1024; heads*d_k % 64 == 0).
+ *    DAR_ERR_HIP: a launch reported an error.
+ */
+#ifndef DAR_H
+#define DAR_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DAR_OK = 0,
+  DAR_ERR_INVALID_ARG = 1,
+  DAR_ERR_UNSUPPORTED = 2,
+  DAR_ERR_WORKSPACE = 3,
+  DAR_ERR_HIP = 4
+} dar_status;
+
+typedef enum { DAR_FP32 = 0, DAR_BF16 = 1 } dar_dtype;
+
+/* Version of this ABI (bumped on any signature or layout change). */
+int dar_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dar_status_string(dar_status s);
+
+/*
+ * dar_fold -- fold the up-projection into the shared key/value weights.
+ *
+ * Eqs. (2)-(3): the global path applies W_K and W_V to h'_j = h^D_j W_up, so
+ * h'_j W_K = h^D_j (W_up W_K).  This computes
+ *     W_upK = W_up W_K,   W_upV = W_up W_V      (both d_down x heads*d_k)
+ * in fp32 and stores them in `dtype`, column-major like every weight (i.e.
+ * as row-major [heads*d_k, d_down]).  Run once per weight set.
+ *   W_up [d_down x d], W_K, W_V [d x heads*d_k]      (column-major, dtype)
+ * No workspace is needed; pass workspace = NULL only to query (writes 0).
+ */
+dar_status dar_fold(const void* W_up, const void* W_K, const void* W_V, int d, int d_down,
+                    int heads, int d_k, dar_dtype dtype, void* W_upK, void* W_upV,
+                    hipStream_t stream);
+
+/*
+ * dar_project -- the projections of Eqs. (1)-(3) and q_i = h_i W_Q (Eq. 4).
+ *
+ *   h      [B, N, d]                       hidden states, token n at pos0+n
+ *   W_down [d x d_down], W_Q, W_K, W_V [d x heads*d_k]      (column-major)
+ *   W_up   [d_down x d]                    used only when W_upK/W_upV are NULL
+ *   W_upK, W_upV [d_down x heads*d_k]      folded weights from dar_fold, or
+ *                                          both NULL: the call folds them into
+ *                                          its workspace first
+ * Outputs (each written in full):
+ *   Q      [B, heads, N, d_k]   RoPE(h W_Q) at the token's position
+ *   K_loc  [B, heads, N, d_k]   RoPE(h W_K)                 (Eq. 3, local)
+ *   V_loc  [B, heads, d_k, N]   h W_V, TRANSPOSED per head (token innermost)
+ *   h_D    [B, N, d_down]       h W_down                    (Eq. 1)
+ *   K_glob [B, heads, N, d_k]   RoPE(h^D W_upK) = RoPE(h' W_K)  (Eq. 3, global)
+ *   V_glob [B, heads, d_k, N]   h^D W_upV = h' W_V, transposed like V_loc
+ * In bf16 mode h^D is rounded to bf16 before the global GEMM (it is the
+ * stored latent).  Outputs must not alias inputs or each other.
+ */
+dar_status dar_project(const void* h, const void* W_down, const void* W_up, const void* W_Q,
+                       const void* W_K, const void* W_V, const void* W_upK, const void* W_upV,
+                       int B, int N, int d, int d_down, int heads, int d_k, int pos0,
+                       float rope_base, dar_dtype dtype, void* Q, void* K_loc, void* V_loc,
+                       void* h_D, void* K_glob, void* V_glob, void* workspace,
+                       size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * dar_attn_prefill -- Eq. (4) with the Eq. (3) distance selection, causal.
+ *
+ * For query i and key j <= i of the same sequence and head, the key/value
+ * pair comes from (K_loc, V_loc) when i - j < w and from (K_glob, V_glob)
+ * otherwise; w = 0 sends every pair (j = i included) to the global path,
+ * w >= N every pair to the local path.
+ *   Q, K_loc, K_glob   [B, heads, N, d_k]
+ *   V_loc, V_glob      [B, heads, d_k, N]   (token innermost, as dar_project writes)
+ *   o                  [B, N, heads*d_k]    heads concatenated, before W_O
+ * No workspace is used (query returns 0).
+ */
+dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
+                            const void* K_glob, const void* V_glob, int B, int N, int heads,
+                            int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream);
+
+/*
+ * dar_attn_decode -- one new query per sequence over the mixed cache.
+ *
+ * The inference remarks of the paper note that each past token contributes
+ * through exactly one path, so a decode cache only needs full keys/values for
+ * the w most recent positions and the d_down-wide latent h^D beyond them.
+ * The query sits at position p = ctx_len - 1 (its own key/value already in
+ * the window).
+ *   q      [B, heads, d_k]          RoPE'd at p
+ *   K_win  [B, heads, w, d_k]       RoPE'd keys of positions max(0,p-w+1)..p,
+ *   V_win  [B, heads, w, d_k]       values; position j lives in slot j mod w
+ *   h_D    [B, cap, d_down]         latents; rows 0 .. p-w are read (cap >= p-w+1)
+ *   W_upK, W_upV [d_down x heads*d_k]   folded weights (dar_fold), column-major
+ *   o      [B, heads*d_k]
+ * Global keys are rebuilt as RoPE_j(h^D_j W_upK); values are accumulated in
+ * latent space and lifted once: sum_j p_j h^D_j W_upV = (sum_j p_j h^D_j) W_upV.
+ * bf16 only (fp32 returns DAR_ERR_UNSUPPORTED).
+ */
+dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
+                           const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
+                           int heads, int d_k, int d_down, int w, float rope_base,
+                           dar_dtype dtype, void* o, void* workspace, size_t* workspace_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAR_H */

@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/dar.h declares, and rejects bad arguments before
+any device work.  Only size queries and rejected calls are made here, with
+fake, never-dereferenced addresses."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import distance_adaptive_dual_amd as dar
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dar.h")
+OK, INVALID, UNSUP, WS = 0, 1, 2, 3
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dar_status|int|const char\*)\s+(dar_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_exports_match_header():
+    names = declared()
+    assert set(names) == set(dar.EXPORTS)
+    L = dar.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = dar.lib()
+    assert L.dar_abi_version() == 1
+    for code, name in dar.STATUS.items():
+        assert L.dar_status_string(code).decode() == name
+
+
+F = dar._fake
+
+
+def project(**kw):
+    a = dict(h=F(0), W_down=F(1), W_up=F(2), W_Q=F(3), W_K=F(4), W_V=F(5), W_upK=F(6),
+             W_upV=F(7), B=2, N=128, d=256, d_down=64, heads=4, d_k=64, pos0=0, base=10000.0,
+             dtype=1, Q=F(8), K_loc=F(9), V_loc=F(10), h_D=F(11), K_glob=F(12), V_glob=F(13),
+             ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    st = dar.lib().dar_project(a["h"], a["W_down"], a["W_up"], a["W_Q"], a["W_K"], a["W_V"],
+                               a["W_upK"], a["W_upV"], a["B"], a["N"], a["d"], a["d_down"],
+                               a["heads"], a["d_k"], a["pos0"], a["base"], a["dtype"], a["Q"],
+                               a["K_loc"], a["V_loc"], a["h_D"], a["K_glob"], a["V_glob"],
+                               a["ws"], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_project_size_query():
+    st, n = project()
+    assert st == OK and n > 0
+    st2, n2 = project(W_upK=None, W_upV=None)  # fold into the workspace
+    assert st2 == OK and n2 > n
+    st3, n3 = project(N=4096)                  # longer RoPE table
+    assert st3 == OK and n3 > n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(N=0), INVALID), (dict(d_k=63), INVALID), (dict(pos0=-1), INVALID),
+    (dict(h=None), INVALID), (dict(Q=F(8) + 2), INVALID), (dict(dtype=7), INVALID),
+    (dict(base=0.5), INVALID),
+    (dict(K_glob=F(0)), INVALID),              # output aliases an input
+    (dict(V_glob=F(8)), INVALID),              # two outputs alias
+    (dict(W_upK=None, W_upV=None, W_up=None), INVALID),
+    (dict(d_k=96), UNSUP), (dict(d=200), UNSUP), (dict(d_down=48), UNSUP),
+])
+def test_project_rejects(kw, code):
+    assert project(**kw)[0] == code
+
+
+def test_project_small_workspace():
+    st, n = project()
+    assert project(ws=F(20), wsb=n - 1)[0] == WS
+    assert project(ws=F(20) + 16, wsb=n)[0] == INVALID  # workspace must be 256-B aligned
+
+
+def attn(**kw):
+    a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), B=1, N=64, heads=2,
+             d_k=64, w=8, dtype=1, o=F(5))
+    a.update(kw)
+    return dar.lib().dar_attn_prefill(a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"],
+                                      a["B"], a["N"], a["heads"], a["d_k"], a["w"], a["dtype"],
+                                      a["o"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=-1), INVALID), (dict(N=0), INVALID), (dict(o=F(0)), INVALID), (dict(Q=None), INVALID),
+    (dict(d_k=32), UNSUP),
+])
+def test_prefill_rejects(kw, code):
+    assert attn(**kw) == code
+
+
+def decode(**kw):
+    a = dict(q=F(0), K_win=F(1), V_win=F(2), h_D=F(3), W_upK=F(4), W_upV=F(5), B=2, ctx=1000,
+             cap=1000, heads=4, d_k=128, d_down=256, w=128, base=10000.0, dtype=1, o=F(6),
+             ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    st = dar.lib().dar_attn_decode(a["q"], a["K_win"], a["V_win"], a["h_D"], a["W_upK"],
+                                   a["W_upV"], a["B"], a["ctx"], a["cap"], a["heads"], a["d_k"],
+                                   a["d_down"], a["w"], a["base"], a["dtype"], a["o"], a["ws"],
+                                   ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_decode_size_query_and_rejects():
+    st, n = decode()
+    assert st == OK and n > 0
+    assert decode(cap=800)[0] == INVALID        # cache shorter than the latent range
+    assert decode(cap=873)[0] == OK             # exactly p - w + 1 rows
+    assert decode(w=-1)[0] == INVALID
+    assert decode(dtype=0)[0] == UNSUP          # fp32 decode is not provided
+    assert decode(d_down=96)[0] == UNSUP
+    assert decode(w=0, K_win=None, V_win=None)[0] == OK
+    assert decode(ws=F(20), wsb=n - 1)[0] == WS
+
+
+def test_fold_rejects():
+    L = dar.lib()
+    assert L.dar_fold(F(0), F(1), F(2), 256, 64, 4, 64, 1, F(3), F(0), None) == INVALID
+    assert L.dar_fold(F(0), F(1), F(2), 256, 64, 4, 48, 1, F(3), F(4), None) == UNSUP
+    assert L.dar_fold(None, F(1), F(2), 256, 64, 4, 64, 1, F(3), F(4), None) == INVALID

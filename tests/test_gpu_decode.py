@@ -1,0 +1,101 @@
+"""GPU parity of the mixed-cache decode step (dar_attn_decode) against the
+fp64 oracle, through the C ABI.  bf16 I/O, max-abs 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import dar_inputs as di
+import distance_adaptive_dual_amd as dar
+import oracle
+from gpu_helpers import TOL, dev, dev_w, host, log, max_err, prefill_case
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(inp, ctx, w, H, d_k):
+    W_up, W_K, W_V = (dev_w(inp[k], "bf16") for k in ("W_up", "W_K", "W_V"))
+    Wk, Wv = dar.dar_fold(W_up, W_K, W_V, H, d_k)
+    q = dev(inp["q"], "bf16")
+    K_win = dev(inp["K_win"], "bf16")
+    V_win = dev(inp["V_win"], "bf16")
+    h_D = dev(inp["h_D"], "bf16")
+    o = dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w)
+    torch.cuda.synchronize()
+    return host(o)
+
+
+@pytest.mark.parametrize("B,ctx,d,H,d_k,dd,w", [
+    (2, 1000, 512, 4, 128, 256, 128),
+    (3, 4097, 256, 4, 64, 64, 512),     # ragged context, many chunks
+    (2, 300, 256, 2, 128, 128, 0),      # w = 0: every key rebuilt from the latent
+    (2, 300, 256, 4, 64, 32, 1),        # w = 1: only the query's own key is full
+    (1, 200, 256, 2, 128, 128, 500),    # w >= ctx: no latent reads at all
+    (2, 1, 128, 2, 64, 64, 4),          # first token
+    (1, 65, 512, 8, 64, 256, 64),       # exactly one latent token
+    (2, 2000, 512, 16, 128, 256, 100),  # 16 heads (several head groups)
+])
+def test_decode_small(B, ctx, d, H, d_k, dd, w):
+    inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=10 * ctx + w)
+    log("decode B%d ctx%d d%d H%d dk%d dd%d w%d" % (B, ctx, d, H, d_k, dd, w))
+    got = run_decode(inp, ctx, w, H, d_k)
+    ref = oracle.decode(inp["q"], inp["K_win"], inp["V_win"], inp["h_D"], inp["W_up"],
+                        inp["W_K"], inp["W_V"], ctx, w)
+    err = max_err(got, ref)
+    log("  max err %.3g" % err)
+    assert err <= TOL["bf16"]
+
+
+def test_decode_cap_larger_than_context():
+    """The latent cache may hold more rows than the context uses."""
+    B, ctx, d, H, d_k, dd, w = 2, 700, 256, 4, 64, 128, 64
+    inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, cap=1024, seed0=4242)
+    got = run_decode(inp, ctx, w, H, d_k)
+    ref = oracle.decode(inp["q"], inp["K_win"], inp["V_win"], inp["h_D"], inp["W_up"],
+                        inp["W_K"], inp["W_V"], ctx, w)
+    assert max_err(got, ref) <= TOL["bf16"]
+
+
+def test_decode_matches_prefill_row():
+    """The decode step at position p reproduces row p of the full prefill
+    (oracle), with the cache filled from the oracle's own projections."""
+    B, N, d, H, d_k, dd, w = 2, 600, 256, 4, 64, 128, 100
+    inp = prefill_case(B, N, d, H, d_k, dd, "bf16", seed=606)
+    o_ref, _, P = oracle.prefill(inp, H, d_k, w)
+    p = N - 1
+    r = di.round_bf16
+    K_win = np.zeros((B, H, w, d_k))
+    V_win = np.zeros((B, H, w, d_k))
+    for j in range(p - w + 1, p + 1):
+        K_win[:, :, j % w] = P["KL"][:, :, j]
+        V_win[:, :, j % w] = P["VL"][:, :, j]
+    cache = dict(q=r(P["Q"][:, :, p]), K_win=r(K_win), V_win=r(V_win), h_D=r(P["hD"]),
+                 W_up=inp["W_up"], W_K=inp["W_K"], W_V=inp["W_V"])
+    got = run_decode(cache, N, w, H, d_k)
+    err = max_err(got, o_ref[:, p])
+    log("  decode vs prefill row err %.3g" % err)
+    assert err <= TOL["bf16"]
+
+
+def test_long_context_decode_sampled():
+    """B16, ctx 32768, d2048, 16 heads of 128, w512, d_down 256: the full-size
+    launch, checked for two (batch, head) pairs (the oracle rebuilds every
+    global key of that batch and head in fp64)."""
+    B, ctx, d, H, d_k, dd, w = 16, 32768, 2048, 16, 128, 256, 512
+    inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=5000)
+    got = run_decode(inp, ctx, w, H, d_k)
+    for b, hh in [(0, 0), (13, 11)]:
+        ref = oracle.decode(inp["q"][b:b + 1], inp["K_win"][b:b + 1], inp["V_win"][b:b + 1],
+                            inp["h_D"][b:b + 1], inp["W_up"], inp["W_K"], inp["W_V"], ctx, w,
+                            heads=(hh, hh + 1))
+        sl = slice(hh * d_k, (hh + 1) * d_k)
+        err = max_err(got[b, sl], ref[0, sl])
+        log("  long decode b%d h%d max err %.3g" % (b, hh, err))
+        assert err <= TOL["bf16"]
+
+
+def test_decode_deterministic():
+    B, ctx, d, H, d_k, dd, w = 2, 3000, 256, 4, 128, 128, 256
+    inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=77)
+    a = run_decode(inp, ctx, w, H, d_k)
+    b = run_decode(inp, ctx, w, H, d_k)
+    assert np.array_equal(a, b)
