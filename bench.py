@@ -67,11 +67,11 @@ def make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed):
     W = {k: dev(inp[k].T) for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
     h = dev(inp["h"])
     Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
-    kw = dict(dtype=torch.bfloat16, device="cuda")
+    kw = dict(dtype=torch.float16, device="cuda")  # the fp16 intermediates of bf16 mode
     out = dict(Q=torch.empty((B, H, N, d_k), **kw), K_loc=torch.empty((B, H, N, d_k), **kw),
                V_loc=torch.empty((B, H, d_k, N), **kw), h_D=torch.empty((B, N, d_down), **kw),
                K_glob=torch.empty((B, H, N, d_k), **kw), V_glob=torch.empty((B, H, d_k, N), **kw))
-    o = torch.empty((B, N, H * d_k), **kw)
+    o = torch.empty((B, N, H * d_k), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(max(dar.project_workspace_bytes(B, N, d, d_down, H, d_k), 256),
                      dtype=torch.uint8, device="cuda")
     return inp, dict(h=h, W=W, Wk=Wk, Wv=Wv, out=out, o=o, ws=ws)

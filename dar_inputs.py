@@ -52,9 +52,16 @@ def round_f32(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
+def round_f16(x) -> np.ndarray:
+    """Round float64 values to the nearest IEEE half (ties to even), as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
 def round_to(x, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16(x)
+    if dtype == "f16":
+        return round_f16(x)
     if dtype == "f32":
         return round_f32(x)
     raise ValueError(dtype)

@@ -7,6 +7,8 @@ kernels of the library.  There is no fallback: if the library is missing or
 a call fails, an exception is raised.
 
 Method: "Dual Dimensionality for Local and Global Attention", Eqs. (1)-(4).
+In bf16 mode the projections handed from dar_project to dar_attn_prefill are
+float16 tensors (see include/dar.h); h, the weights and o are bfloat16.
 Weights are column-major (pass a [out, in] tensor, the nn.Linear layout: the
 equations' W in R^{in x out} transposed and made contiguous).
 """
@@ -65,8 +67,10 @@ def _torch():
 
 
 def _dtype_code(t) -> int:
+    """Library mode of a tensor: bf16 I/O (bfloat16 tensors, or the float16
+    intermediates of that mode) or fp32."""
     torch = _torch()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return DAR_BF16
     if t.dtype == torch.float32:
         return DAR_FP32
@@ -145,7 +149,7 @@ def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None
     d_down = W_down.shape[0]
     dt = _dtype_code(h)
     if out is None:
-        kw = dict(dtype=h.dtype, device=h.device)
+        kw = dict(dtype=torch.float16 if dt == DAR_BF16 else torch.float32, device=h.device)
         out = dict(Q=torch.empty((B, heads, N, d_k), **kw),
                    K_loc=torch.empty((B, heads, N, d_k), **kw),
                    V_loc=torch.empty((B, heads, d_k, N), **kw),
@@ -172,10 +176,12 @@ def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=Non
     """Eq. (4) with the Eq. (3) selection.  Returns o [B, N, heads*d_k]."""
     torch = _torch()
     B, H, N, d_k = Q.shape
+    dt = _dtype_code(Q)
     if o is None:
-        o = torch.empty((B, N, H * d_k), dtype=Q.dtype, device=Q.device)
+        o = torch.empty((B, N, H * d_k), dtype=torch.bfloat16 if dt == DAR_BF16 else torch.float32,
+                        device=Q.device)
     st = lib().dar_attn_prefill(_ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(K_glob), _ptr(V_glob),
-                                B, N, H, d_k, int(w), _dtype_code(Q), _ptr(o), _stream(stream))
+                                B, N, H, d_k, int(w), dt, _ptr(o), _stream(stream))
     _check("dar_attn_prefill", st)
     return o
 

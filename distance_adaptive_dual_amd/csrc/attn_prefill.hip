@@ -5,7 +5,9 @@
 // (K_loc, V_loc) when i - j < w and the bottleneck key/value (K_glob, V_glob)
 // otherwise; o_i = softmax(q_i K_i^T / sqrt(d_k)) V_i.
 //
-// bf16 kernel (gfx950): one workgroup = 128 queries of one (batch, head), four
+// bf16 mode (gfx950).  The layer's I/O is bf16; Q, K and V arrive as IEEE fp16
+// (written so by the projection) and P is rounded to fp16, so both products
+// run on fp16 MFMAs with fp32 accumulation.  One workgroup = 128 queries of one (batch, head), four
 // waves of 32 queries.  Keys stream in tiles of 64.  Every (query-wave, key
 // tile) pair is classified from its distance range [dmin, dmax]:
 //   dmax < 0             skipped (causally in the future)
@@ -34,87 +36,155 @@ namespace dar {
 
 namespace {
 
-constexpr int QT = 128;  // queries per workgroup
-constexpr int KT = 64;   // keys per tile
+constexpr int QT = 128;      // queries per workgroup
+constexpr int KT = 64;       // keys per tile
+constexpr float kTau = 8.f;  // rescale only when a row max grows by > 2^8 (log2 units)
+constexpr float kNegBig = -1e30f;
 
 __device__ __forceinline__ int key_perm(int r) {  // swap bits 2 and 3
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Offset of score register (kb, r) from the lane's first key j0 + 8*lg.
+__device__ __forceinline__ constexpr int key_off(int kb, int r) {
+  return 32 * kb + 16 * (r >> 3) + (r & 7);
+}
+
 template <int D>
-struct PrefillSmem {
-  static constexpr int KP = D + 8;   // bf16 per K row (16 B pad: 4-bank shift per row)
-  static constexpr int VP = KT + 8;  // bf16 per V^T row
-  bf16 k[2][KT * KP];                // [source][key][d]
-  bf16 v[2][D * VP];                 // [source][d][key]
+struct PassSmem {
+  static constexpr int KP = D + 8;   // fp16 per K row (16 B pad: 4-bank shift per row)
+  static constexpr int VP = KT + 8;  // fp16 per V^T row
+  f16 k[2][KT * KP];                 // [buffer][key][d]
+  f16 v[2][D * VP];                  // [buffer][d][key]
 };
 
-// Stage one source's K tile [KT x D] and V^T tile [D x KT] into LDS.
+// Register staging of one pass: a key tile of one source (K [KT x D] and
+// V^T [D x KT]), 16-byte chunks spread over the 256 threads.
 template <int D>
-__device__ __forceinline__ void stage_tile(bf16* sk, bf16* sv, const bf16* K, const bf16* Vt,
-                                           int N, int j0, bool vec_ok) {
-  constexpr int KP = PrefillSmem<D>::KP, VP = PrefillSmem<D>::VP;
+struct Stage {
+  static constexpr int NCH = KT * D / 8 / 256;
+  u32x4 k[NCH], v[NCH];
+};
+
+template <int D>
+__device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16* Vt, int N, int j0,
+                                          bool vec_ok) {
   const int tid = threadIdx.x;
-  constexpr int KCH = KT * D / 8;  // 16-byte chunks of the K tile
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int c = tid; c < KCH; c += 256) {
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int c = tid + 256 * i;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    const int j = j0 + row;
-    const u32x4 val = (j < N) ? *(const u32x4*)(K + (size_t)j * D + col) : z;
-    *(u32x4*)(sk + row * KP + col) = val;
-  }
-  constexpr int VCH = D * KT / 8;
-  if (vec_ok) {
+    st.k[i] = (j0 + row < N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
+    const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
+    if (vec_ok) {
+      st.v[i] = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
+    } else {  // ragged tail, or N not a multiple of 8
+      const uint16_t* src = (const uint16_t*)Vt + (size_t)d * N;
+      uint32_t w4[4];
 #pragma unroll
-    for (int c = tid; c < VCH; c += 256) {
-      const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
-      *(u32x4*)(sv + d * VP + kc) = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
-    }
-  } else {  // ragged tail or N not a multiple of 8: element-wise with bounds
-    const uint16_t* src = (const uint16_t*)Vt;
-    uint16_t* dst = (uint16_t*)sv;
-    for (int e = tid; e < D * KT; e += 256) {
-      const int d = e / KT, kk = e % KT, j = j0 + kk;
-      dst[d * VP + kk] = (j < N) ? src[(size_t)d * N + j] : (uint16_t)0;
+      for (int e = 0; e < 4; ++e) {
+        const int ja = j0 + kc + 2 * e, jb = ja + 1;
+        const uint32_t a = ja < N ? src[ja] : 0u, b = jb < N ? src[jb] : 0u;
+        w4[e] = a | (b << 16);
+      }
+      st.v[i] = u32x4{w4[0], w4[1], w4[2], w4[3]};
     }
   }
 }
 
-// S^T for one 64-key tile: s[kb][r] is key j0 + 32kb + 16(r/8) + 8lg + (r%8).
 template <int D>
-__device__ __forceinline__ void tile_scores(f32x16 (&s)[2], const bf16* sk, const bf16x8 (&qf)[D / 16],
-                                            int lr, int lg) {
-  constexpr int KP = PrefillSmem<D>::KP;
+__device__ __forceinline__ void store_pass(const Stage<D>& st, f16* sk, f16* sv) {
+  constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    *(u32x4*)(sk + row * KP + col) = st.k[i];
+    const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
+    *(u32x4*)(sv + d * VP + kc) = st.v[i];
+  }
+}
+
+// One pass of one wave: scores against the staged tile, the Eq. (3) keep mask,
+// online softmax, and O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f16x8 (&qf)[D / 16],
+                                          f32x16 (&o)[D / 32], float& m_ref, float& l_run,
+                                          bool masked, int keep_lo, int keep_hi, float sc,
+                                          int lr, int lg) {
+  constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
+  // S^T = K Q^T: s[kb][r] is key j0 + 8 lg + key_off(kb, r) of this lane's query.
+  f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const bf16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
+    const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
-      acc = mfma32x32x16(*(const bf16x8*)(base + 16 * st), qf[st], acc);
+      acc = mfma32x32x16(*(const f16x8*)(base + 16 * st), qf[st], acc);
     s[kb] = acc;
   }
-}
-
-// O^T += V^T P^T over one 64-key tile.  pf[u] holds keys j0 + 16u + 8lg + c.
-template <int D>
-__device__ __forceinline__ void tile_pv(f32x16 (&o)[D / 32], const bf16* sv, const bf16x8 (&pf)[4],
-                                        int lr, int lg) {
-  constexpr int VP = PrefillSmem<D>::VP;
+  // keep iff keep_lo < key_off <= keep_hi (distance window, causality, length)
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = key_off(kb, r);
+        if (!(off > keep_lo && off <= keep_hi)) s[kb][r] = -INFINITY;
+      }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32)) * sc;
+  // Softmax is invariant to the reference maximum, so it is only moved (and O,
+  // l rescaled) when some row's maximum exceeds it by more than 2^kTau.
+  if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
+    const float m_new = fmaxf(m_ref, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  }
+  // p = 2^(s*sc - m_ref), rounded to fp16 for the MFMA; l sums the same fp16 p
+  f16x8 pf[4];
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one2 = {(f16)1.f, (f16)1.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + c], sc, -m_ref));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + c + 1], sc, -m_ref));
+      const uint32_t pk = pack_f16x2(e0, e1);
+      const h2 ph = __builtin_bit_cast(h2, pk);
+      l_run = __builtin_amdgcn_fdot2(ph, one2, l_run, false);
+      pf[u][c] = ph[0];
+      pf[u][c + 1] = ph[1];
+    }
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    const bf16* base = sv + (32 * db + lr) * VP + 8 * lg;
+    const f16* base = sv + (32 * db + lr) * VP + 8 * lg;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o[db] = mfma32x32x16(*(const bf16x8*)(base + 16 * u), pf[u], o[db]);
+    for (int u = 0; u < 4; ++u)
+      o[db] = mfma32x32x16(*(const f16x8*)(base + 16 * u), pf[u], o[db]);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_prefill_bf16(PrefillProblem p, int nQT, int remap) {
-  __shared__ PrefillSmem<D> sm;
+__global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int nQT, int remap) {
+  __shared__ PassSmem<D> sm;
   const int N = p.N, H = p.H, BH = p.B * p.H, w = p.w;
   // Longest query tiles first; with remap, all tiles of one (batch, head) stay
   // on one XCD so its K/V prefix is shared through that XCD's L2.
@@ -122,11 +192,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_bf16(PrefillProblem p, in
   {
     const int bid = blockIdx.x;
     if (remap) {
-      const int x = bid % kNumXcd, k = bid / kNumXcd, per = BH / kNumXcd;
-      const int bl = k / nQT;
+      const int x = bid % kNumXcd, k = bid / kNumXcd;
       qt = nQT - 1 - (k % nQT);
-      bh = bl * kNumXcd + x;
-      (void)per;
+      bh = (k / nQT) * kNumXcd + x;
     } else {
       qt = nQT - 1 - bid / BH;
       bh = bid % BH;
@@ -134,11 +202,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_bf16(PrefillProblem p, in
   }
   const int b = bh / H, h = bh % H;
   const size_t kv_off = (size_t)bh * N * D;
-  const bf16* Qp = (const bf16*)p.Q + kv_off;
-  const bf16* Kl = (const bf16*)p.K_loc + kv_off;
-  const bf16* Kg = (const bf16*)p.K_glob + kv_off;
-  const bf16* Vl = (const bf16*)p.V_loc + kv_off;
-  const bf16* Vg = (const bf16*)p.V_glob + kv_off;
+  const f16* Qp = (const f16*)p.Q + kv_off;
+  const f16* Ks[2] = {(const f16*)p.K_glob + kv_off, (const f16*)p.K_loc + kv_off};
+  const f16* Vs[2] = {(const f16*)p.V_glob + kv_off, (const f16*)p.V_loc + kv_off};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
@@ -147,13 +213,13 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_bf16(PrefillProblem p, in
   const int i_last = min(i0 + QT - 1, N - 1);
   const int wi_last = min(qw0 + 31, N - 1);
 
-  bf16x8 qf[D / 16];
+  f16x8 qf[D / 16];
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
       u32x4 v = (qi < N) ? *(const u32x4*)(Qp + (size_t)qi * D + 16 * st + 8 * lg) : z;
-      qf[st] = __builtin_bit_cast(bf16x8, v);
+      qf[st] = __builtin_bit_cast(f16x8, v);
     }
   }
   f32x16 o[D / 32];
@@ -161,97 +227,55 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_bf16(PrefillProblem p, in
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = kNegBig, l_run = 0.f;
   const float sc = kLog2e / sqrtf((float)D);
   const bool nvec = (N % 8) == 0;
 
+  // Passes: for each key tile, the global source (if any pair of the
+  // workgroup is at distance >= w) then the local source (if any is < w).
   const int j_end = min(N, i0 + QT);
-  for (int j0 = 0; j0 < j_end; j0 += KT) {
-    const int dmin = i0 - (j0 + KT - 1), dmax = i_last - j0;
-    const bool need_loc = (w > 0) && (max(dmin, 0) < w);
-    const bool need_glob = dmax >= w;
-    const bool vec_ok = nvec && (j0 + KT <= N);
-    __syncthreads();
-    if (need_loc) stage_tile<D>(sm.k[0], sm.v[0], Kl, Vl, N, j0, vec_ok);
-    if (need_glob) stage_tile<D>(sm.k[1], sm.v[1], Kg, Vg, N, j0, vec_ok);
-    __syncthreads();
+  auto need_glob = [&](int j0) { return i_last - j0 >= w; };
+  auto need_loc = [&](int j0) { return w > 0 && max(i0 - (j0 + KT - 1), 0) < w; };
+  int j0 = 0, src = need_glob(0) ? 0 : 1;  // src 0 = global, 1 = local
+  Stage<D> stg;
+  load_pass<D>(stg, Ks[src], Vs[src], N, j0, nvec && (j0 + KT <= N));
+  store_pass<D>(stg, sm.k[0], sm.v[0]);
+  __syncthreads();
+  int buf = 0;
+  while (true) {
+    int nj0 = j0, nsrc;
+    if (src == 0 && need_loc(j0)) {
+      nsrc = 1;
+    } else {
+      nj0 = j0 + KT;
+      nsrc = need_glob(nj0) ? 0 : 1;
+    }
+    const bool has_next = nj0 < j_end;
+    if (has_next) load_pass<D>(stg, Ks[nsrc], Vs[nsrc], N, nj0, nvec && (nj0 + KT <= N));
 
     const int wdmax = wi_last - j0, wdmin = qw0 - (j0 + KT - 1);
-    if (qw0 >= N || wdmax < 0) continue;
-    const bool wl = (w > 0) && (max(wdmin, 0) < w);
-    const bool wgl = wdmax >= w;
-    const bool masked = (wdmin < 0) || (j0 + KT > N);
-
-    f32x16 s[2];
-    if (wl && wgl) {
-      f32x16 sg[2];
-      tile_scores<D>(s, sm.k[0], qf, lr, lg);
-      tile_scores<D>(sg, sm.k[1], qf, lr, lg);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * kb + 16 * (r >> 3) + 8 * lg + (r & 7);
-          if (qi - j >= w) s[kb][r] = sg[kb][r];
-        }
-    } else {
-      tile_scores<D>(s, wl ? sm.k[0] : sm.k[1], qf, lr, lg);
-    }
-
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * sc;
-        if (masked) {
-          const int j = j0 + 32 * kb + 16 * (r >> 3) + 8 * lg + (r & 7);
-          if (j > qi || j >= N) v = -INFINITY;
-        }
-        s[kb][r] = v;
-        mt = fmaxf(mt, v);
+    if (qw0 < N && wdmax >= 0) {
+      // keep pairs with distance in [lo, hi) for this source, j <= i, j < N
+      const bool glob = src == 0;
+      const bool part = glob ? (wdmax >= w) : (w > 0 && max(wdmin, 0) < w);
+      if (part) {
+        const bool masked =
+            (glob ? (wdmin < w) : (wdmin < 0 || wdmax >= w)) || (j0 + KT > N);
+        const int base = qi - j0 - 8 * lg;  // distance of key offset 0
+        const int lo = glob ? w : 0;
+        // keep iff base - hi < off <= min(base - lo, N - 1 - j0 - 8 lg)
+        const int keep_lo = glob ? -1 : base - w;
+        const int keep_hi = min(base - lo, N - 1 - j0 - 8 * lg);
+        wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, masked, keep_lo, keep_hi, sc,
+                     lr, lg);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[kb][r] - m_new);
-        s[kb][r] = e;
-        ls += e;
-      }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-    if (wl && wgl) {
-      bf16x8 pl[4], pg[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int j = j0 + 16 * u + 8 * lg + c;
-          const float e = s[u >> 1][8 * (u & 1) + c];
-          const bool loc = (qi - j) < w;
-          pl[u][c] = (bf16)(loc ? e : 0.f);
-          pg[u][c] = (bf16)(loc ? 0.f : e);
-        }
-      tile_pv<D>(o, sm.v[0], pl, lr, lg);
-      tile_pv<D>(o, sm.v[1], pg, lr, lg);
-    } else {
-      bf16x8 pf[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) pf[u][c] = (bf16)s[u >> 1][8 * (u & 1) + c];
-      tile_pv<D>(o, wl ? sm.v[0] : sm.v[1], pf, lr, lg);
     }
+    if (!has_next) break;
+    store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
+    __syncthreads();
+    buf ^= 1;
+    j0 = nj0;
+    src = nsrc;
   }
 
   if (qi >= N) return;
@@ -339,16 +363,20 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(PrefillProblem p) {
 
 }  // namespace
 
-hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s) {
+hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStream_t s) {
+  // Distances never exceed N - 1, so any w >= N selects the local path for
+  // every pair; clamping keeps the kernels' distance arithmetic in range.
+  PrefillProblem p = p_in;
+  if (p.w > p.N) p.w = p.N;
   const int BH = p.B * p.H;
   if (dt == DAR_BF16) {
     const int nQT = (p.N + QT - 1) / QT;
     const int remap = (BH % kNumXcd) == 0 ? 1 : 0;
     const dim3 grid(nQT * BH);
     if (p.d_k == 64)
-      hipLaunchKernelGGL(attn_prefill_bf16<64>, grid, dim3(256), 0, s, p, nQT, remap);
+      hipLaunchKernelGGL(attn_prefill_f16<64>, grid, dim3(256), 0, s, p, nQT, remap);
     else
-      hipLaunchKernelGGL(attn_prefill_bf16<128>, grid, dim3(256), 0, s, p, nQT, remap);
+      hipLaunchKernelGGL(attn_prefill_f16<128>, grid, dim3(256), 0, s, p, nQT, remap);
   } else {
     const dim3 grid((p.N + FQ - 1) / FQ, p.H, p.B);
     if (p.d_k == 64)

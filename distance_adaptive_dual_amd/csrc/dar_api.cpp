@@ -152,9 +152,13 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   const RopeTab rope{lo, hi, d_k / 2};
 
   GemmProblem g1{};
+  const bool bf = dtype == DAR_BF16;
   g1.A = h;
   g1.M = (int)M;
   g1.K = d;
+  g1.a_type = bf ? kBF16 : kF32;
+  g1.b_type = bf ? kBF16 : kF32;
+  g1.out_type = bf ? kF16 : kF32;
   g1.nseg = 4;
   g1.seg[0] = GemmSeg{W_Q, Q, hd, kHead, 1};
   g1.seg[1] = GemmSeg{W_K, K_loc, hd, kHead, 1};
@@ -171,6 +175,7 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   GemmProblem g2 = g1;
   g2.A = h_D;
   g2.K = d_down;
+  g2.a_type = bf ? kF16 : kF32;
   g2.nseg = 2;
   g2.seg[0] = GemmSeg{fK, K_glob, hd, kHead, 1};
   g2.seg[1] = GemmSeg{fV, V_glob, hd, kHeadT, 0};

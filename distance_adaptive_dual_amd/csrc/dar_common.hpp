@@ -13,7 +13,9 @@
 namespace dar {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -41,6 +43,23 @@ template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
   return (bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 }
+template <>
+__device__ __forceinline__ f16 from_f32<f16>(float x) {
+  return (f16)x;  // round to nearest even
+}
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+
+// 8-wide MFMA operand of element type T.
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  typedef bf16x8 type;
+};
+template <>
+struct Vec8<f16> {
+  typedef f16x8 type;
+};
 
 // Two fp32 values -> one dword of two bf16 (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -58,6 +77,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
                                                const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Same shape and lane layout with IEEE fp16 operands.
+__device__ __forceinline__ f32x16 mfma32x32x16(const f16x8& a, const f16x8& b,
+                                               const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 values -> one dword of two fp16 (low half = a).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v;
+  v[0] = (f16)a;
+  v[1] = (f16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight bf16 (as 4 dwords) -> eight fp16 (as 4 dwords).  Exact for every bf16
+// value inside the fp16 normal range.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+    r[i] = pack_f16x2(lo, hi);
+  }
+  return r;
 }
 
 // RoPE angle lookup.  cos/sin(p * theta_t) is the complex product of a
@@ -99,9 +144,13 @@ struct GemmSeg {
   int rope;        // rotate (kind == kHead only)
 };
 
+// Element types of GEMM operands and outputs.
+enum ElemType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
 struct GemmProblem {
   const void* A;  // [M, K] row-major
   int M, K;
+  int a_type, b_type, out_type;  // ElemType of A, of every segment's B, of the outputs
   int nseg;
   GemmSeg seg[4];
   int n_seq;  // rows per sequence (row -> (b, n))

@@ -11,9 +11,12 @@
 // tensor and layout; the epilogue applies RoPE and scatters into the
 // head-major layouts the attention kernels read.
 //
-// bf16 path: 128x128x64 tiles, 4 waves of 64x64 built from 32x32x16 MFMAs,
+// bf16 mode: 128x128x64 tiles, 4 waves of 64x64 built from 32x32x16 MFMAs,
 // double-buffered LDS, fp32 accumulate, epilogue staged through LDS so the
 // rotate-half partners (t, t + d_k/2) meet in one thread and stores coalesce.
+// The projections are written as IEEE fp16 (3 more mantissa bits than bf16 at
+// the same size and MFMA rate); the second GEMM therefore runs on fp16 MFMAs,
+// converting the bf16 folded weights to fp16 as they are staged into LDS.
 // fp32 path: an LDS-tiled VALU GEMM with the same epilogue (no bf16 anywhere).
 #include "dar_common.hpp"
 
@@ -35,85 +38,128 @@ __device__ __forceinline__ int find_seg(const SegTiles& st, int nseg, int ct) {
   return s;
 }
 
-// Writes a [rows x BN] fp32 tile held in LDS (pitch EPI_P) to segment `seg`.
-// Tile row r is GEMM row row0 + r; tile column c is segment column col0 + c.
-template <typename OutT>
-__device__ void epilogue_store(const float* tile, int rows, int row0, int col0,
-                               const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int M = p.M, width = seg.width;
-  OutT* out = (OutT*)seg.out;
-  if (seg.kind == kRowMajor) {
-    for (int it = tid; it < rows * (BN / 4); it += nthr) {
-      const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
-      const int grow = row0 + r, gcol = col0 + c;
-      if (grow >= M || gcol >= width) continue;
-      const float* src = tile + r * EPI_P + c;
-      OutT* dst = out + (size_t)grow * width + gcol;
+// Stores n consecutive fp32 values as OutT with the widest aligned stores.
+template <typename OutT, int NV>
+__device__ __forceinline__ void store_run(OutT* dst, const float* v) {
+  if constexpr (sizeof(OutT) == 2) {
+    static_assert(NV % 8 == 0, "fp16 runs are stored 8 at a time");
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = from_f32<OutT>(src[e]);
+    for (int i = 0; i < NV; i += 8) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = __is_same(OutT, f16) ? pack_f16x2(v[i + 2 * e], v[i + 2 * e + 1])
+                                    : pack_bf16x2(v[i + 2 * e], v[i + 2 * e + 1]);
+      *(u32x4*)(dst + i) = w;
     }
-    return;
-  }
-  const int D = p.d_k, H = p.heads, Nq = p.n_seq;
-  if (seg.kind == kHead) {
-    if (seg.rope) {
-      const int half = D / 2;
-      // one item = 4 columns t..t+3 of the first half of a head and their partners
-      const int per_row = BN / 8;
-      for (int it = tid; it < rows * per_row; it += nthr) {
-        const int r = it / per_row, q = it % per_row;
-        const int hl = (q * 4) / half;          // head within the tile
-        const int t = (q * 4) % half;           // first-half column within the head
-        const int c = hl * D + t;               // tile column of x
-        const int grow = row0 + r, gcol = col0 + c;
-        if (grow >= M || gcol >= width) continue;
-        const int b = grow / Nq, n = grow % Nq, head = gcol / D;
-        const int pos = p.pos0 + n;
-        const float* x = tile + r * EPI_P + c;
-        const float* y = x + half;
-        OutT* dst = out + (((size_t)b * H + head) * Nq + n) * D + t;
+  } else {
+    static_assert(NV % 4 == 0, "fp32 runs are stored 4 at a time");
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 cs = rope_cs(p.rope, pos, t + e);
-          dst[e] = from_f32<OutT>(x[e] * cs.x - y[e] * cs.y);
-          dst[e + half] = from_f32<OutT>(x[e] * cs.y + y[e] * cs.x);
-        }
-      }
-    } else {
-      for (int it = tid; it < rows * (BN / 4); it += nthr) {
-        const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
-        const int grow = row0 + r, gcol = col0 + c;
-        if (grow >= M || gcol >= width) continue;
-        const int b = grow / Nq, n = grow % Nq, head = gcol / D, t = gcol % D;
-        const float* src = tile + r * EPI_P + c;
-        OutT* dst = out + (((size_t)b * H + head) * Nq + n) * D + t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = from_f32<OutT>(src[e]);
-      }
-    }
-    return;
-  }
-  // kHeadT: out[b, head, t, n]; consecutive threads take consecutive rows n so
-  // every scalar store of a wave is contiguous.
-  for (int it = tid; it < rows * (BN / 4); it += nthr) {
-    const int r = it % rows, c = (it / rows) * 4;
-    const int grow = row0 + r, gcol = col0 + c;
-    if (grow >= M || gcol >= width) continue;
-    const int b = grow / Nq, n = grow % Nq;
-    const float* src = tile + r * EPI_P + c;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int head = (gcol + e) / D, t = (gcol + e) % D;
-      out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<OutT>(src[e]);
-    }
+    for (int i = 0; i < NV; i += 4) *(float4*)(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
   }
 }
 
+// Writes a [ROWS x BN] fp32 tile held in LDS (pitch EPI_P) to segment `seg`.
+// Tile row r is GEMM row row0 + r, i.e. token (b, n) = divmod(row0 + r, n_seq);
+// tile column c is segment column col0 + c.  Each thread owns one row and a
+// contiguous run of columns (kHeadT: one column and a run of rows), so the
+// (b, n) division happens once per thread and stores are 8-16 bytes wide.
+template <typename OutT, int D, int ROWS>
+__device__ void epilogue_store(const float* tile, int row0, int col0, const GemmSeg& seg,
+                               const GemmProblem& p) {
+  constexpr int TPR = 256 / ROWS;  // threads per tile row
+  constexpr int CPT = BN / TPR;    // columns per thread
+  const int tid = threadIdx.x;
+  const int M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  OutT* out = (OutT*)seg.out;
+  if (seg.kind == kHeadT) {
+    // out[b, head, t, n]: thread = (column c, run of ROWS/2 rows)
+    constexpr int RPT = ROWS / 2;
+    const int c = tid % BN, r0 = (tid / BN) * RPT;
+    const int gcol = col0 + c;
+    if (gcol >= width) return;
+    const int head = gcol / D, t = gcol % D;
+    const int grow0 = row0 + r0;
+    const int b0 = grow0 / Nq, n0 = grow0 % Nq;
+    float v[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) v[i] = tile[(r0 + i) * EPI_P + c];
+    const bool fast = (grow0 + RPT <= M) && (n0 + RPT <= Nq) && ((n0 & 7) == 0) && ((Nq & 7) == 0);
+    if (fast) {
+      store_run<OutT, RPT>(out + (((size_t)b0 * H + head) * D + t) * Nq + n0, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int grow = grow0 + i;
+        if (grow >= M) break;
+        const int b = grow / Nq, n = grow % Nq;
+        out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<OutT>(v[i]);
+      }
+    }
+    return;
+  }
+  const int r = tid / TPR, part = tid % TPR;
+  const int grow = row0 + r;
+  if (grow >= M) return;
+  const int b = grow / Nq, n = grow % Nq;
+  const float* trow = tile + r * EPI_P;
+  if (seg.kind == kRowMajor) {
+    // width is a multiple of 32: the run is stored in chunks of 8 columns,
+    // each either wholly inside the segment or wholly past its end
+    const int c = part * CPT;
+    OutT* dst = out + (size_t)grow * width + col0 + c;
+#pragma unroll
+    for (int i = 0; i < CPT; i += 8) {
+      if (col0 + c + i >= width) break;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = trow[c + i + e];
+      store_run<OutT, 8>(dst + i, v);
+    }
+    return;
+  }
+  // kHead: out[b, head, n, t]
+  if (!seg.rope) {
+    const int c = part * CPT;
+    const int gcol = col0 + c;
+    if (gcol >= width) return;
+    const int head = gcol / D, t = gcol % D;  // CPT divides D: the run stays in one head
+    float v[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) v[i] = trow[c + i];
+    store_run<OutT, CPT>(out + (((size_t)b * H + head) * Nq + n) * D + t, v);
+    return;
+  }
+  // RoPE at position pos0 + n on rotate-half pairs (t, t + D/2): the thread
+  // takes CPT/2 consecutive pairs of one head.
+  constexpr int HALF = D / 2, PPT = CPT / 2;
+  const int q0 = part * PPT;              // first pair of this thread within the tile
+  const int hl = q0 / HALF, t0 = q0 % HALF;
+  const int gcol = col0 + hl * D;
+  if (gcol >= width) return;
+  const int head = gcol / D;
+  const int pos = p.pos0 + n;
+  const float* x = trow + hl * D + t0;
+  const float* y = x + HALF;
+  float a[PPT], bb[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const float2 cs = rope_cs(p.rope, pos, t0 + i);
+    a[i] = x[i] * cs.x - y[i] * cs.y;
+    bb[i] = x[i] * cs.y + y[i] * cs.x;
+  }
+  OutT* dst = out + (((size_t)b * H + head) * Nq + n) * D + t0;
+  store_run<OutT, PPT>(dst, a);
+  store_run<OutT, PPT>(dst + HALF, bb);
+}
+
 // --------------------------------------------------------------------------
-// bf16 MFMA GEMM.
-__global__ __launch_bounds__(256, 2) void project_gemm_bf16(GemmProblem p, SegTiles st, int nM,
+// MFMA GEMM: A and the MFMA operands of type TM (bf16 or fp16), B stored as TB
+// (converted to TM while staged), outputs of type TO.
+template <typename TM, typename TB, typename TO, int D>
+__global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTiles st, int nM,
                                                            int nC, int nCp) {
+  typedef typename Vec8<TM>::type TMx8;
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * BM * LDA_S * 2];
   // XCD-aware order: XCD x owns a contiguous group of column tiles (its slice
   // of the weights stays in that XCD's L2) and walks the row tiles in order,
@@ -127,11 +173,11 @@ __global__ __launch_bounds__(256, 2) void project_gemm_bf16(GemmProblem p, SegTi
   const int col0 = (ct - st.tile0[s]) * BN;  // first segment column of the tile
   const int row0 = mt * BM;
   const int K = p.K, M = p.M;
-  const bf16* A = (const bf16*)p.A;
-  const bf16* Bt = (const bf16*)seg.Bt;
+  const TM* A = (const TM*)p.A;
+  const TB* Bt = (const TB*)seg.Bt;
 
-  // LDS: [buf][A tile | B tile], each BM x LDA_S bf16
-  bf16* const lds = (bf16*)smem;
+  // LDS: [buf][A tile | B tile], each BM x LDA_S elements of TM
+  TM* const lds = (TM*)smem;
   auto sA = [&](int buf) { return lds + (2 * buf) * BM * LDA_S; };
   auto sB = [&](int buf) { return lds + (2 * buf + 1) * BM * LDA_S; };
 
@@ -156,7 +202,10 @@ __global__ __launch_bounds__(256, 2) void project_gemm_bf16(GemmProblem p, SegTi
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 32 * i, kc = (tid & 7) * 8;
       *(u32x4*)(sA(buf) + r * LDA_S + kc) = ra[i];
-      *(u32x4*)(sB(buf) + r * LDA_S + kc) = rb[i];
+      if constexpr (__is_same(TM, TB))
+        *(u32x4*)(sB(buf) + r * LDA_S + kc) = rb[i];
+      else
+        *(u32x4*)(sB(buf) + r * LDA_S + kc) = bf16x8_to_f16x8(rb[i]);
     }
   };
 
@@ -175,15 +224,15 @@ __global__ __launch_bounds__(256, 2) void project_gemm_bf16(GemmProblem p, SegTi
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_regs((kt + 1) * BK);
-    const bf16* a_s = sA(cur) + (wm * 64 + lr) * LDA_S + 8 * lg;
-    const bf16* b_s = sB(cur) + (wn * 64 + lr) * LDA_S + 8 * lg;
+    const TM* a_s = sA(cur) + (wm * 64 + lr) * LDA_S + 8 * lg;
+    const TM* b_s = sB(cur) + (wn * 64 + lr) * LDA_S + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 a[2], b[2];
+      TMx8 a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8*)(a_s + 32 * i * LDA_S + 16 * ks);
+      for (int i = 0; i < 2; ++i) a[i] = *(const TMx8*)(a_s + 32 * i * LDA_S + 16 * ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)(b_s + 32 * j * LDA_S + 16 * ks);
+      for (int j = 0; j < 2; ++j) b[j] = *(const TMx8*)(b_s + 32 * j * LDA_S + 16 * ks);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -206,14 +255,14 @@ __global__ __launch_bounds__(256, 2) void project_gemm_bf16(GemmProblem p, SegTi
         tile[row * EPI_P + col] = acc[i][j][r];
       }
   __syncthreads();
-  epilogue_store<bf16>(tile, BM, row0, col0, seg, p);
+  epilogue_store<TO, D, BM>(tile, row0, col0, seg, p);
 }
 
 // --------------------------------------------------------------------------
 // fp32 VALU GEMM (fp32 mode and the weight fold).  B(k, n) = Bp[k*sbk + n*sbn].
 constexpr int SM = 64, SK = 16;
 
-template <typename InT, typename OutT>
+template <typename InT, typename OutT, int D>
 __global__ __launch_bounds__(256) void gemm_simt(GemmProblem p, SegTiles st, long sbk, long sbn) {
   __shared__ float sAs[SK][SM + 4];
   __shared__ float sBs[SK][BN + 4];
@@ -274,7 +323,7 @@ __global__ __launch_bounds__(256) void gemm_simt(GemmProblem p, SegTiles st, lon
 #pragma unroll
     for (int j = 0; j < 8; ++j) tile[(4 * ty + i) * EPI_P + tx + 16 * j] = acc[i][j];
   __syncthreads();
-  epilogue_store<OutT>(tile, SM, row0, col0, seg, p);
+  epilogue_store<OutT, D, SM>(tile, row0, col0, seg, p);
 }
 
 SegTiles seg_tiles(const GemmProblem& p) {
@@ -296,11 +345,27 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
   if (dt == DAR_BF16) {
     const int nM = (p.M + BM - 1) / BM;
     const int nCp = (nC + kNumXcd - 1) / kNumXcd * kNumXcd;
-    hipLaunchKernelGGL(project_gemm_bf16, dim3(nM * nCp), dim3(256), 0, s, p, st, nM, nC, nCp);
+    const dim3 grid(nM * nCp);
+#define DAR_G(TA, D)                                                                          \
+  hipLaunchKernelGGL((project_gemm_mfma<TA, bf16, f16, D>), grid, dim3(256), 0, s, p, st, nM, \
+                     nC, nCp)
+    if (p.b_type != kBF16 || p.out_type != kF16) return hipErrorInvalidValue;
+    if (p.a_type == kBF16) {
+      if (p.d_k == 64) DAR_G(bf16, 64); else DAR_G(bf16, 128);
+    } else if (p.a_type == kF16) {
+      if (p.d_k == 64) DAR_G(f16, 64); else DAR_G(f16, 128);
+    } else {
+      return hipErrorInvalidValue;
+    }
+#undef DAR_G
   } else {
     const int nM = (p.M + SM - 1) / SM;
-    hipLaunchKernelGGL((gemm_simt<float, float>), dim3(nC, nM), dim3(256), 0, s, p, st, 1L,
-                       (long)p.K);
+    if (p.d_k == 64)
+      hipLaunchKernelGGL((gemm_simt<float, float, 64>), dim3(nC, nM), dim3(256), 0, s, p, st, 1L,
+                         (long)p.K);
+    else
+      hipLaunchKernelGGL((gemm_simt<float, float, 128>), dim3(nC, nM), dim3(256), 0, s, p, st,
+                         1L, (long)p.K);
   }
   return hipGetLastError();
 }
@@ -318,14 +383,14 @@ hipError_t launch_fold(const void* W_up, const void* W_KV, void* out, int d, int
   p.seg[0] = GemmSeg{W_up, out, d_down, kRowMajor, 0};
   p.n_seq = hd;
   p.heads = 1;
-  p.d_k = 2;
+  p.d_k = 64;  // unused by the row-major epilogue
   const SegTiles st = seg_tiles(p);
   const int nC = st.tile0[1], nM = (hd + SM - 1) / SM;
   if (dt == DAR_BF16)
-    hipLaunchKernelGGL((gemm_simt<bf16, bf16>), dim3(nC, nM), dim3(256), 0, s, p, st,
+    hipLaunchKernelGGL((gemm_simt<bf16, bf16, 64>), dim3(nC, nM), dim3(256), 0, s, p, st,
                        (long)d_down, 1L);
   else
-    hipLaunchKernelGGL((gemm_simt<float, float>), dim3(nC, nM), dim3(256), 0, s, p, st,
+    hipLaunchKernelGGL((gemm_simt<float, float, 64>), dim3(nC, nM), dim3(256), 0, s, p, st,
                        (long)d_down, 1L);
   return hipGetLastError();
 }

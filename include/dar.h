@@ -23,9 +23,15 @@
  *    output column is contiguous.  These are the same bytes as a row-major
  *    [c, r] array (the layout of a torch.nn.Linear weight).  The MFMA GEMMs
  *    read both operands along the contraction index, so no transpose runs.
- *  - dtype DAR_BF16: every float tensor is bfloat16; arithmetic is MFMA with
- *    fp32 accumulation, softmax in fp32.  DAR_FP32: every float tensor is
- *    float32 and every step is computed in fp32 (no bf16 rounding anywhere).
+ *  - dtype DAR_BF16: the layer's inputs and outputs (h, the weights, the
+ *    folded weights, o, and the decode cache q / K_win / V_win / h_D) are
+ *    bfloat16.  The six prefill intermediates that dar_project hands to
+ *    dar_attn_prefill (Q, K_loc, V_loc, h_D, K_glob, V_glob) are IEEE fp16:
+ *    same size and MFMA rate, 3 more mantissa bits, which keeps the
+ *    end-to-end error several times inside 2e-2; their magnitude must stay
+ *    below 65504 (not checked).  Arithmetic is MFMA with fp32 accumulation,
+ *    softmax in fp32.  DAR_FP32: every float tensor is float32 and every
+ *    step is computed in fp32 (no 16-bit rounding anywhere).
  *  - Positions are 0-based: token n of a prefill sits at position pos0 + n.
  *    RoPE uses rotate-half pairs (t, t + d_k/2) over the full head width with
  *    theta_t = rope_base^(-2t/d_k), applied to queries and keys alike.
@@ -90,14 +96,14 @@ dar_status dar_fold(const void* W_up, const void* W_K, const void* W_V, int d, i
  *   W_upK, W_upV [d_down x heads*d_k]      folded weights from dar_fold, or
  *                                          both NULL: the call folds them into
  *                                          its workspace first
- * Outputs (each written in full):
+ * Outputs (each written in full; fp16 in DAR_BF16 mode, fp32 in DAR_FP32):
  *   Q      [B, heads, N, d_k]   RoPE(h W_Q) at the token's position
  *   K_loc  [B, heads, N, d_k]   RoPE(h W_K)                 (Eq. 3, local)
  *   V_loc  [B, heads, d_k, N]   h W_V, TRANSPOSED per head (token innermost)
  *   h_D    [B, N, d_down]       h W_down                    (Eq. 1)
  *   K_glob [B, heads, N, d_k]   RoPE(h^D W_upK) = RoPE(h' W_K)  (Eq. 3, global)
  *   V_glob [B, heads, d_k, N]   h^D W_upV = h' W_V, transposed like V_loc
- * In bf16 mode h^D is rounded to bf16 before the global GEMM (it is the
+ * In bf16 mode h^D is rounded to fp16 before the global GEMM (it is the
  * stored latent).  Outputs must not alias inputs or each other.
  */
 dar_status dar_project(const void* h, const void* W_down, const void* W_up, const void* W_Q,
@@ -114,9 +120,10 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
  * pair comes from (K_loc, V_loc) when i - j < w and from (K_glob, V_glob)
  * otherwise; w = 0 sends every pair (j = i included) to the global path,
  * w >= N every pair to the local path.
- *   Q, K_loc, K_glob   [B, heads, N, d_k]
+ *   Q, K_loc, K_glob   [B, heads, N, d_k]   (fp16 in DAR_BF16 mode)
  *   V_loc, V_glob      [B, heads, d_k, N]   (token innermost, as dar_project writes)
  *   o                  [B, N, heads*d_k]    heads concatenated, before W_O
+ *                                           (bf16 in DAR_BF16 mode)
  * No workspace is used (query returns 0).
  */
 dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,

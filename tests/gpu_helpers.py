@@ -12,7 +12,7 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
 def tdtype(dtype: str):
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
 def dev(x, dtype: str):
