@@ -13,8 +13,10 @@ Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +31,35 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "distance_adaptive_dual_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_key, files):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE runs
+    (profiles/*.md, line 'traffic <key> <bytes> sha <hash>'), or None when the
+    kernel's sources changed since the counters were taken."""
+    sha = source_sha(files)
+    if not os.path.isdir(PROFILES):
+        return None
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        for line in open(os.path.join(PROFILES, name)):
+            m = re.match(r"^traffic (\S+) (\d+) sha (\w+)", line.strip())
+            if m and m.group(1) == kernel_key and m.group(3) == sha:
+                return int(m.group(2))
+    return None
 
 
 def prefill_flops(B, N, d, d_down):
@@ -165,6 +196,8 @@ def main():
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="one 256 MiB device-to-device copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -179,6 +212,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dar.lib()
+    if args.calib_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     res = {"metric": "DAR prefill TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
            "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -202,13 +242,15 @@ def main():
         res["kernels"] = {"dar_project_ms": proj_ms, "dar_project_TFLOP/s": proj_f / proj_ms / 1e9,
                           "dar_attn_prefill_ms": attn_ms,
                           "dar_attn_prefill_TFLOP/s": attn_f / attn_ms / 1e9}
-        dom_attn = attn_ms >= proj_ms
-        dom_flops, dom_ms = (attn_f, attn_ms) if dom_attn else (proj_f, proj_ms)
-        achieved = dom_flops / dom_ms / 1e9
-        res["roofline"] = {"kernel": "attn_prefill_bf16<64>" if dom_attn else "project GEMMs",
-                           "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                           "traffic": None}
+        # The fused attention kernel is the only launch of dar_attn_prefill, so
+        # the events around that call time exactly one kernel.
+        achieved = attn_f / attn_ms / 1e9
+        res["roofline"] = {"kernel": "attn_prefill_f16<64>", "bound": "mfma",
+                           "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": recorded_traffic("attn_prefill_f16<64>@pythia70m",
+                                                       ["attn_prefill.hip", "dar_common.hpp"]),
+                           "flops_per_launch": attn_f, "launch_ms": attn_ms}
         if not args.no_cpu:
             import oracle
             log("cpu baseline: oracle on one sequence")
