@@ -25,7 +25,7 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
-           "dar_attn_prefill", "dar_attn_decode")
+           "dar_attn_prefill", "dar_decode_append", "dar_attn_decode")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.dar_project.argtypes = [_P] * 8 + [_I] * 7 + [ctypes.c_float, _I] + [_P] * 7 + [_SZ, _P]
         L.dar_attn_prefill.restype = _I
         L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P]
+        L.dar_decode_append.restype = _I
+        L.dar_decode_append.argtypes = [_P] * 5 + [_I] * 8 + [ctypes.c_float, _I] + [_P] * 5 + [
+            _SZ, _P]
         L.dar_attn_decode.restype = _I
         L.dar_attn_decode.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P, _SZ, _P]
         _lib = L
@@ -184,6 +187,30 @@ def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=Non
                                 B, N, H, d_k, int(w), dt, _ptr(o), _stream(stream))
     _check("dar_attn_prefill", st)
     return o
+
+
+def dar_decode_append(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos: int, q, K_win, V_win,
+                      h_D, rope_base: float = 10000.0, workspace=None, stream=None):
+    """Project the token at position `pos` of every sequence into the cache:
+    q [B, heads, d_k] (RoPE'd), ring slot pos mod w of K_win / V_win, row pos
+    of h_D.  h [B, d]; weights column-major.  Returns q."""
+    B, d = h.shape
+    d_down = W_down.shape[0]
+    w = K_win.shape[2] if K_win is not None else 0
+    cap = h_D.shape[1]
+    L = lib()
+    n = ctypes.c_size_t(0)
+    args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), B, d, d_down, heads, d_k,
+            int(pos), int(w), cap, float(rope_base), _dtype_code(h), _ptr(q),
+            _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D)]
+    st = L.dar_decode_append(*args, None, ctypes.byref(n), None)
+    _check("dar_decode_append", st)
+    if workspace is None or workspace.numel() < n.value:
+        workspace = _workspace(n.value, h)
+    n = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
+    st = L.dar_decode_append(*args, _ptr(workspace), ctypes.byref(n), _stream(stream))
+    _check("dar_decode_append", st)
+    return q
 
 
 def decode_workspace_bytes(B, ctx_len, cap, heads, d_k, d_down, w, dtype=DAR_BF16):

@@ -202,6 +202,76 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
   return hip_status(launch_attn_prefill(p, dtype, stream));
 }
 
+dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q, const void* W_K,
+                             const void* W_V, int B, int d, int d_down, int heads, int d_k,
+                             int pos, int w, int cap, float rope_base, dar_dtype dtype, void* q,
+                             void* K_win, void* V_win, void* h_D, void* workspace,
+                             size_t* workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || pos < 0 || w < 0 ||
+      cap < 1)
+    return DAR_ERR_INVALID_ARG;
+  if (pos >= cap || !(rope_base > 1.0f)) return DAR_ERR_INVALID_ARG;
+  const void* need[] = {h, W_down, W_Q, W_K, W_V, q, h_D};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
+  const int hd = heads * d_k;
+  const size_t es = elem_size(dtype);
+  const Span ins[5] = {{h, es * B * (size_t)d}, {W_down, es * d * (size_t)d_down},
+                       {W_Q, es * d * (size_t)hd}, {W_K, es * d * (size_t)hd},
+                       {W_V, es * d * (size_t)hd}};
+  const Span outs[4] = {{q, es * B * (size_t)hd},
+                        {K_win, w > 0 ? es * B * (size_t)hd * w : 0},
+                        {V_win, w > 0 ? es * B * (size_t)hd * w : 0},
+                        {h_D, es * B * (size_t)cap * d_down}};
+  if (!disjoint(outs, 4, ins, 5)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
+    return DAR_ERR_UNSUPPORTED;
+  const size_t need_bytes = rope_table_bytes(d_k, pos);
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& sp : ins)
+      if (overlap(ws, sp)) return DAR_ERR_INVALID_ARG;
+    for (const Span& sp : outs)
+      if (overlap(ws, sp)) return DAR_ERR_INVALID_ARG;
+  }
+  float2* lo = (float2*)workspace;
+  float2* hi = lo + 64 * (d_k / 2);
+  hipError_t e = launch_rope_tables(lo, hi, d_k, pos, rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  // One GEMM over the B new tokens (one per sequence, all at position pos):
+  // q at [b, head, 0, t]; k, v into ring slot pos mod w; h^D into row pos.
+  GemmProblem g{};
+  g.A = h;
+  g.M = B;
+  g.K = d;
+  g.a_type = kBF16;
+  g.b_type = kBF16;
+  g.out_type = kBF16;
+  g.n_seq = 1;
+  g.heads = heads;
+  g.d_k = d_k;
+  g.pos0 = pos;
+  g.rope = RopeTab{lo, hi, d_k / 2};
+  int ns = 0;
+  g.seg[ns++] = GemmSeg{W_Q, q, hd, kHead, 1, 1, 0};
+  if (w > 0) {
+    g.seg[ns++] = GemmSeg{W_K, K_win, hd, kHead, 1, w, pos % w};
+    g.seg[ns++] = GemmSeg{W_V, V_win, hd, kHead, 0, w, pos % w};
+  }
+  g.seg[ns++] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos};
+  g.nseg = ns;
+  return hip_status(launch_project_gemm(g, dtype, stream));
+}
+
 dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
                            const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
                            int heads, int d_k, int d_down, int w, float rope_base,

@@ -142,6 +142,11 @@ struct GemmSeg {
   int width;       // number of output columns in this segment
   int kind;        // OutKind
   int rope;        // rotate (kind == kHead only)
+  // Output sequence addressing for kRowMajor / kHead: token (b, n) of the GEMM
+  // lands at sequence index n + seq_off of a sequence of length ld_seq
+  // (ld_seq = 0 means the GEMM's own n_seq and seq_off = 0).  This lets the
+  // decode append write one token into a ring slot or a latent-cache row.
+  int ld_seq = 0, seq_off = 0;
 };
 
 // Element types of GEMM operands and outputs.

@@ -59,6 +59,19 @@ __device__ __forceinline__ void store_run(OutT* dst, const float* v) {
   }
 }
 
+// Four consecutive fp32 values as OutT (8 or 16 bytes).
+template <typename OutT>
+__device__ __forceinline__ void store_run4(OutT* dst, const float* v) {
+  if constexpr (sizeof(OutT) == 2) {
+    u32x2 w;
+    w[0] = __is_same(OutT, f16) ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+    w[1] = __is_same(OutT, f16) ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
+    *(u32x2*)dst = w;
+  } else {
+    *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 // Writes a [ROWS x BN] fp32 tile held in LDS (pitch EPI_P) to segment `seg`.
 // Tile row r is GEMM row row0 + r, i.e. token (b, n) = divmod(row0 + r, n_seq);
 // tile column c is segment column col0 + c.  Each thread owns one row and a
@@ -102,12 +115,14 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
   const int grow = row0 + r;
   if (grow >= M) return;
   const int b = grow / Nq, n = grow % Nq;
+  const int ld = seg.ld_seq ? seg.ld_seq : Nq;  // output sequence stride
+  const int no = n + seg.seq_off;                // output sequence index
   const float* trow = tile + r * EPI_P;
   if (seg.kind == kRowMajor) {
     // width is a multiple of 32: the run is stored in chunks of 8 columns,
     // each either wholly inside the segment or wholly past its end
     const int c = part * CPT;
-    OutT* dst = out + (size_t)grow * width + col0 + c;
+    OutT* dst = out + ((size_t)b * ld + no) * width + col0 + c;
 #pragma unroll
     for (int i = 0; i < CPT; i += 8) {
       if (col0 + c + i >= width) break;
@@ -127,7 +142,7 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
     float v[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) v[i] = trow[c + i];
-    store_run<OutT, CPT>(out + (((size_t)b * H + head) * Nq + n) * D + t, v);
+    store_run<OutT, CPT>(out + (((size_t)b * H + head) * ld + no) * D + t, v);
     return;
   }
   // RoPE at position pos0 + n on rotate-half pairs (t, t + D/2): the thread
@@ -148,7 +163,7 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
     a[i] = x[i] * cs.x - y[i] * cs.y;
     bb[i] = x[i] * cs.y + y[i] * cs.x;
   }
-  OutT* dst = out + (((size_t)b * H + head) * Nq + n) * D + t0;
+  OutT* dst = out + (((size_t)b * H + head) * ld + no) * D + t0;
   store_run<OutT, PPT>(dst, a);
   store_run<OutT, PPT>(dst + HALF, bb);
 }
@@ -156,17 +171,33 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
 // --------------------------------------------------------------------------
 // MFMA GEMM: A and the MFMA operands of type TM (bf16 or fp16), B stored as TB
 // (converted to TM while staged), outputs of type TO.
+//
+// The MFMA computes the transposed tile C^T = B^T A^T: the weight rows (output
+// columns) are the first operand and the token rows the second, so a lane's
+// accumulators hold one token and runs of 4 consecutive output columns, which
+// go to an LDS staging tile as 16-byte writes ([token][column] for Q, K and h^D,
+// [column][token] for the transposed V layout [b, head, t, n]).
 template <typename TM, typename TB, typename TO, int D>
 __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTiles st, int nM,
-                                                           int nC, int nCp) {
+                                                           int nC, int nCp, int order) {
   typedef typename Vec8<TM>::type TMx8;
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * BM * LDA_S * 2];
-  // XCD-aware order: XCD x owns a contiguous group of column tiles (its slice
-  // of the weights stays in that XCD's L2) and walks the row tiles in order,
-  // so the row tile of h is read once per XCD.
+  // XCD-aware order.  order 0 (large weights): XCD x owns a contiguous group of
+  // column tiles, whose slice of the weights stays in its L2, and walks the row
+  // tiles in order.  order 1 (weights that fit in one L2): XCD x owns the row
+  // tiles congruent to x and walks every column tile of one row tile before
+  // the next, so each tile of activations is fetched once overall.
   const int bid = blockIdx.x;
-  const int x = bid % kNumXcd, k = bid / kNumXcd, g = nCp / kNumXcd;
-  const int mt = k / g, ct = x * g + (k % g);
+  const int x = bid % kNumXcd, k = bid / kNumXcd;
+  int mt, ct;
+  if (order == 0) {
+    const int g = nCp / kNumXcd;
+    mt = k / g;
+    ct = x * g + (k % g);
+  } else {
+    mt = (k / nC) * kNumXcd + x;
+    ct = k % nC;
+  }
   if (ct >= nC || mt >= nM) return;
   const int s = find_seg(st, p.nseg, ct);
   const GemmSeg seg = p.seg[s];
@@ -176,16 +207,18 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   const TM* A = (const TM*)p.A;
   const TB* Bt = (const TB*)seg.Bt;
 
-  // LDS: [buf][A tile | B tile], each BM x LDA_S elements of TM
+  // LDS: [buf][token tile | weight tile], each 128 x LDA_S elements of TM
   TM* const lds = (TM*)smem;
   auto sA = [&](int buf) { return lds + (2 * buf) * BM * LDA_S; };
   auto sB = [&](int buf) { return lds + (2 * buf + 1) * BM * LDA_S; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
+  // wave -> (partner pair of 32-column blocks, 64-token half)
+  const int wp = wave & 1, wt = wave >> 1;
+  const int cb0 = (D == 128) ? wp : 2 * wp;             // first column block (of 4)
+  const int cb1 = (D == 128) ? wp + 2 : 2 * wp + 1;     // its rotate-half partner
 
-  // global -> register staging: 4 x 16 B of A and of B per thread
   u32x4 ra[4], rb[4];
   auto load_regs = [&](int k0) {
 #pragma unroll
@@ -209,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
     }
   };
 
+  // acc[i][j]: column block (cb0, cb1)[i] x token block j of this wave
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -224,35 +258,85 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_regs((kt + 1) * BK);
-    const TM* a_s = sA(cur) + (wm * 64 + lr) * LDA_S + 8 * lg;
-    const TM* b_s = sB(cur) + (wn * 64 + lr) * LDA_S + 8 * lg;
+    const TM* w0 = sB(cur) + (32 * cb0 + lr) * LDA_S + 8 * lg;
+    const TM* w1 = sB(cur) + (32 * cb1 + lr) * LDA_S + 8 * lg;
+    const TM* h0 = sA(cur) + (64 * wt + lr) * LDA_S + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      TMx8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *(const TMx8*)(a_s + 32 * i * LDA_S + 16 * ks);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const TMx8*)(b_s + 32 * j * LDA_S + 16 * ks);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      const TMx8 a0 = *(const TMx8*)(w0 + 16 * ks), a1 = *(const TMx8*)(w1 + 16 * ks);
+      const TMx8 b0 = *(const TMx8*)(h0 + 16 * ks), b1 = *(const TMx8*)(h0 + 32 * LDA_S + 16 * ks);
+      acc[0][0] = mfma32x32x16(a0, b0, acc[0][0]);
+      acc[0][1] = mfma32x32x16(a0, b1, acc[0][1]);
+      acc[1][0] = mfma32x32x16(a1, b0, acc[1][0]);
+      acc[1][1] = mfma32x32x16(a1, b1, acc[1][1]);
     }
     if (kt + 1 < nk) store_lds(cur ^ 1);
     __syncthreads();
   }
 
-  // accumulators -> LDS tile (row-major fp32), then the layout-specific store
+  // Epilogue.  Register r of acc[i][j] is column 32*cb_i + 8*(r/4) + 4*lg + r%4
+  // of the tile, token 64*wt + 32*j + lr.
+  if (seg.kind == kHeadT) {
+    const int H = p.heads, Nq = p.n_seq, width = seg.width;
+    TO* out = (TO*)seg.out;
+    // out[b, head, t, n] through an LDS tile [column][token]
+    float* tile = (float*)smem;
+    constexpr int TP = BM + 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * (i ? cb1 : cb0) + 8 * (r >> 2) + 4 * lg + (r & 3);
+          tile[c * TP + 64 * wt + 32 * j + lr] = acc[i][j][r];
+        }
+    __syncthreads();
+    // thread = (column, run of 64 tokens)
+    const int c = tid % BN, r0 = (tid / BN) * 64;
+    const int gcol = col0 + c;
+    if (gcol >= width) return;
+    const int head = gcol / D, t = gcol % D;
+    const int grow0 = row0 + r0;
+    const int b0 = grow0 / Nq, n0 = grow0 % Nq;
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const float4 q4 = *(const float4*)(tile + c * TP + r0 + i);
+      v[i] = q4.x;
+      v[i + 1] = q4.y;
+      v[i + 2] = q4.z;
+      v[i + 3] = q4.w;
+    }
+    const bool fast = (grow0 + 64 <= M) && (n0 + 64 <= Nq) && ((n0 & 7) == 0) && ((Nq & 7) == 0);
+    if (fast) {
+      store_run<TO, 64>(out + (((size_t)b0 * H + head) * D + t) * Nq + n0, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const int grow = grow0 + i;
+        if (grow >= M) break;
+        const int b = grow / Nq, n = grow % Nq;
+        out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<TO>(v[i]);
+      }
+    }
+    return;
+  }
+  // Q, K, h^D: LDS tile [token][column] written as float4 runs, then the
+  // row-wise epilogue (one (b, n) per thread, contiguous RoPE table reads,
+  // 16-byte stores).
   float* tile = (float*)smem;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-        const int col = wn * 64 + 32 * j + lr;
-        tile[row * EPI_P + col] = acc[i][j][r];
+      for (int a = 0; a < 4; ++a) {
+        const int c = 32 * (i ? cb1 : cb0) + 8 * a + 4 * lg;
+        const int tok = 64 * wt + 32 * j + lr;
+        *(float4*)(tile + tok * EPI_P + c) =
+            make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2],
+                        acc[i][j][4 * a + 3]);
       }
   __syncthreads();
   epilogue_store<TO, D, BM>(tile, row0, col0, seg, p);
@@ -345,15 +429,22 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
   if (dt == DAR_BF16) {
     const int nM = (p.M + BM - 1) / BM;
     const int nCp = (nC + kNumXcd - 1) / kNumXcd * kNumXcd;
-    const dim3 grid(nM * nCp);
-#define DAR_G(TA, D)                                                                          \
-  hipLaunchKernelGGL((project_gemm_mfma<TA, bf16, f16, D>), grid, dim3(256), 0, s, p, st, nM, \
-                     nC, nCp)
-    if (p.b_type != kBF16 || p.out_type != kF16) return hipErrorInvalidValue;
-    if (p.a_type == kBF16) {
-      if (p.d_k == 64) DAR_G(bf16, 64); else DAR_G(bf16, 128);
-    } else if (p.a_type == kF16) {
-      if (p.d_k == 64) DAR_G(f16, 64); else DAR_G(f16, 128);
+    const int nMp = (nM + kNumXcd - 1) / kNumXcd * kNumXcd;
+    // weights of every segment, in bytes: small enough for one XCD's L2 (4 MB)?
+    size_t wbytes = 0;
+    for (int i = 0; i < p.nseg; ++i) wbytes += (size_t)p.seg[i].width * p.K * 2;
+    const int order = wbytes <= (size_t)(2 << 20) ? 1 : 0;
+    const dim3 grid(order == 1 ? nMp * nC : nM * nCp);
+#define DAR_G(TA, TO, D)                                                                    \
+  hipLaunchKernelGGL((project_gemm_mfma<TA, bf16, TO, D>), grid, dim3(256), 0, s, p, st, nM, \
+                     nC, nCp, order)
+    if (p.b_type != kBF16) return hipErrorInvalidValue;
+    if (p.a_type == kBF16 && p.out_type == kF16) {
+      if (p.d_k == 64) DAR_G(bf16, f16, 64); else DAR_G(bf16, f16, 128);
+    } else if (p.a_type == kF16 && p.out_type == kF16) {
+      if (p.d_k == 64) DAR_G(f16, f16, 64); else DAR_G(f16, f16, 128);
+    } else if (p.a_type == kBF16 && p.out_type == kBF16) {
+      if (p.d_k == 64) DAR_G(bf16, bf16, 64); else DAR_G(bf16, bf16, 128);
     } else {
       return hipErrorInvalidValue;
     }

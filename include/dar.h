@@ -131,6 +131,27 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
                             int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream);
 
 /*
+ * dar_decode_append -- project one new token per sequence into the mixed cache.
+ *
+ * The inference remark after Eq. (5) (each past token is used through exactly
+ * one path) and the O(T d_down + w d) cache of the efficiency analysis: for
+ * the new token at position `pos` of every sequence (all sequences share pos)
+ *   q   [B, heads, d_k]       <- RoPE_pos(h W_Q)             (Eq. 4 text)
+ *   K_win[b, :, pos mod w, :] <- RoPE_pos(h W_K)             (Eq. 3, local)
+ *   V_win[b, :, pos mod w, :] <- h W_V
+ *   h_D [b, pos, :]           <- h W_down                    (Eq. 1)
+ * leaving every other slot and row untouched.  h [B, d]; weights column-major;
+ * K_win, V_win [B, heads, w, d_k] (ignored when w = 0); h_D [B, cap, d_down]
+ * with pos < cap.  bf16 only; workspace holds the RoPE tables (query with
+ * workspace = NULL).  Then dar_attn_decode(ctx_len = pos + 1) attends.
+ */
+dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q, const void* W_K,
+                             const void* W_V, int B, int d, int d_down, int heads, int d_k,
+                             int pos, int w, int cap, float rope_base, dar_dtype dtype, void* q,
+                             void* K_win, void* V_win, void* h_D, void* workspace,
+                             size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * dar_attn_decode -- one new query per sequence over the mixed cache.
  *
  * The inference remarks of the paper note that each past token contributes

@@ -129,3 +129,29 @@ def test_fold_rejects():
     assert L.dar_fold(F(0), F(1), F(2), 256, 64, 4, 64, 1, F(3), F(0), None) == INVALID
     assert L.dar_fold(F(0), F(1), F(2), 256, 64, 4, 48, 1, F(3), F(4), None) == UNSUP
     assert L.dar_fold(None, F(1), F(2), 256, 64, 4, 64, 1, F(3), F(4), None) == INVALID
+
+
+def append(**kw):
+    a = dict(h=F(0), W_down=F(1), W_Q=F(2), W_K=F(3), W_V=F(4), B=2, d=256, d_down=64,
+             heads=4, d_k=64, pos=100, w=16, cap=200, base=10000.0, dtype=1, q=F(5),
+             K_win=F(6), V_win=F(7), h_D=F(8), ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    st = dar.lib().dar_decode_append(a["h"], a["W_down"], a["W_Q"], a["W_K"], a["W_V"], a["B"],
+                                     a["d"], a["d_down"], a["heads"], a["d_k"], a["pos"], a["w"],
+                                     a["cap"], a["base"], a["dtype"], a["q"], a["K_win"],
+                                     a["V_win"], a["h_D"], a["ws"], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_append_size_query_and_rejects():
+    st, n = append()
+    assert st == OK and n > 0
+    assert append(pos=200)[0] == INVALID        # position beyond the latent cache
+    assert append(pos=-1)[0] == INVALID
+    assert append(w=-1)[0] == INVALID
+    assert append(q=F(0))[0] == INVALID         # output aliases an input
+    assert append(dtype=0)[0] == UNSUP
+    assert append(d_k=96)[0] == UNSUP
+    assert append(w=0, K_win=None, V_win=None)[0] == OK
+    assert append(ws=F(20), wsb=n - 1)[0] == WS

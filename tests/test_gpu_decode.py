@@ -99,3 +99,71 @@ def test_decode_deterministic():
     a = run_decode(inp, ctx, w, H, d_k)
     b = run_decode(inp, ctx, w, H, d_k)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("B,d,H,d_k,dd,w,pos,cap", [
+    (2, 256, 4, 64, 64, 16, 100, 200),
+    (3, 512, 4, 128, 128, 512, 5000, 5001),
+    (2, 256, 2, 128, 32, 0, 7, 8),
+])
+def test_decode_append(B, d, H, d_k, dd, w, pos, cap):
+    """dar_decode_append writes q, ring slot pos mod w of K/V and latent row
+    pos (oracle projections of the token at position pos) and nothing else."""
+    inp = prefill_case(B, 1, d, H, d_k, dd, "bf16", seed=900 + pos)
+    Wd = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_Q", "W_K", "W_V")}
+    h = dev(inp["h"][:, 0], "bf16")
+    g = np.random.Generator(np.random.PCG64(pos))
+    K0 = di.round_bf16(g.standard_normal((B, H, w, d_k)))
+    V0 = di.round_bf16(g.standard_normal((B, H, w, d_k)))
+    L0 = di.round_bf16(g.standard_normal((B, cap, dd)))
+    K_win, V_win, h_D = dev(K0, "bf16"), dev(V0, "bf16"), dev(L0, "bf16")
+    q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
+    dar.dar_decode_append(h, Wd["W_down"], Wd["W_Q"], Wd["W_K"], Wd["W_V"], H, d_k, pos, q,
+                          K_win if w else None, V_win if w else None, h_D)
+    torch.cuda.synchronize()
+    P = oracle.project(inp["h"], inp["W_down"], inp["W_up"], inp["W_Q"], inp["W_K"], inp["W_V"],
+                       H, d_k, pos0=pos)
+    assert max_err(host(q), P["Q"][:, :, 0]) <= TOL["bf16"]
+    Lg = host(h_D)
+    assert max_err(Lg[:, pos], P["hD"][:, 0]) <= TOL["bf16"]
+    mask = np.ones(cap, bool)
+    mask[pos] = False
+    assert np.array_equal(Lg[:, mask], L0[:, mask])
+    if w:
+        s = pos % w
+        Kg, Vg = host(K_win), host(V_win)
+        assert max_err(Kg[:, :, s], P["KL"][:, :, 0]) <= TOL["bf16"]
+        assert max_err(Vg[:, :, s], P["VL"][:, :, 0]) <= TOL["bf16"]
+        m2 = np.ones(w, bool)
+        m2[s] = False
+        assert np.array_equal(Kg[:, :, m2], K0[:, :, m2])
+        assert np.array_equal(Vg[:, :, m2], V0[:, :, m2])
+
+
+def test_append_then_decode_matches_prefill_row():
+    """Cache for positions < p from the oracle's projections (bf16), the token
+    at p appended on the GPU, then the GPU decode step: equals row p of the
+    oracle's full prefill."""
+    B, N, d, H, d_k, dd, w = 2, 500, 256, 4, 128, 64, 64
+    inp = prefill_case(B, N, d, H, d_k, dd, "bf16", seed=707)
+    o_ref, _, P = oracle.prefill(inp, H, d_k, w)
+    p = N - 1
+    r = di.round_bf16
+    K_win = np.zeros((B, H, w, d_k))
+    V_win = np.zeros((B, H, w, d_k))
+    for j in range(p - w + 1, p):
+        K_win[:, :, j % w] = P["KL"][:, :, j]
+        V_win[:, :, j % w] = P["VL"][:, :, j]
+    hD = r(P["hD"])
+    hD[:, p] = 0.0
+    Kd, Vd, Ld = dev(r(K_win), "bf16"), dev(r(V_win), "bf16"), dev(hD, "bf16")
+    Wd = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
+    dar.dar_decode_append(dev(inp["h"][:, p], "bf16"), Wd["W_down"], Wd["W_Q"], Wd["W_K"],
+                          Wd["W_V"], H, d_k, p, q, Kd, Vd, Ld)
+    Wk, Wv = dar.dar_fold(Wd["W_up"], Wd["W_K"], Wd["W_V"], H, d_k)
+    o = dar.dar_attn_decode(q, Kd, Vd, Ld, Wk, Wv, N, w)
+    torch.cuda.synchronize()
+    err = max_err(host(o), o_ref[:, p])
+    log("  append+decode vs prefill row err %.3g" % err)
+    assert err <= TOL["bf16"]
