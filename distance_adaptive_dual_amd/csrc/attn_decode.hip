@@ -74,23 +74,35 @@ DecodeGeom geom(const DecodeProblem& p) {
 }
 
 // --------------------------------------------------------------------------
+constexpr float kTau = 8.f;        // move the reference max only past 2^8 growth
+constexpr float kNegBig = -1e30f;
+
 template <int D, int KS>
 struct LatentSmem {
   static constexpr int DD = KS * 16;   // d_down
   static constexpr int LP = DD + 8;    // bf16 per latent row (16 B pad)
-  static constexpr int HPW = NWAVE * 64 / D;
-  bf16 lat[2][TB * LP];                // latent blocks
-  float2 lo[64 * (D / 2)];             // fine RoPE table
-  float2 hi[2][D / 2];                 // coarse RoPE row of the current block
-  float sc[NWAVE][TB];                 // per-wave partial scores
-  bf16 pm[16][TB + 8];                 // probabilities, rows = heads of the group
-  float alpha[16];
+  bf16 lat[2][TB * LP];                // latent blocks (double buffer)
+  float2 step[D / 2];                  // (cos, sin)(32 theta_t): one block forward
+  float sc[2][NWAVE][TB];              // per-wave partial scores
+  bf16 pm[2][16][TB + 8];              // probabilities, rows = heads of the group
+  float alpha[2][16];                  // per-head rescale of this block
 };
 
+// Per (batch, head group, context chunk); 8 waves of 64 rows each.
+//
+// A wave keeps, for one head h and 32 rotary frequencies t, the rows W_t and
+// W_{t+d_k/2} of W_upK^T in registers and folds the (pre-rotated) query into
+// them once:  alpha_t = q_t W_t + q_{t+h} W_{t+h},  beta_t = q_{t+h} W_t - q_t W_{t+h}.
+// For a latent h^D_j the rotated key k_j = RoPE_j(h^D_j W_upK) then satisfies
+//   q . k_j = sum_t cos(j theta_t) (h^D_j . alpha_t) + sin(j theta_t) (h^D_j . beta_t)
+// (expand the rotate-half rotation), so one 32x32x16 MFMA chain over d_down
+// gives h^D . alpha and h^D . beta for 32 tokens and the score needs two FMAs
+// per frequency.  cos/sin(j theta_t) advance by one complex multiply per
+// 32-token block (the fine table's row 32), starting from the fp64 tables.
 template <int D, int KS>
 __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeGeom g) {
   using S = LatentSmem<D, KS>;
-  constexpr int DD = S::DD, LP = S::LP, HPW = S::HPW, WPH = D / 64, HALF = D / 2;
+  constexpr int DD = S::DD, LP = S::LP, HPW = NWAVE * 64 / D, WPH = D / 64, HALF = D / 2;
   __shared__ S sm;
 
   // XCD-aware order: the head groups of one (batch, chunk) run on one XCD so
@@ -111,35 +123,46 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   const int j_end = min(g.n_glob, j_begin + g.chunk_len);
   const int nblk = j_end > j_begin ? (j_end - j_begin + TB - 1) / TB : 0;
 
-  // fine RoPE table -> LDS
-  for (int e = tid; e < 64 * HALF; e += 512) sm.lo[e] = p.rope.lo[e];
+  for (int e = tid; e < HALF; e += 512) sm.step[e] = p.rope.lo[32 * HALF + e];
 
-  // This wave's rows of W_upK^T: t = 32 tb + rho and its partner t + D/2.
-  const bf16* Wk = (const bf16*)p.W_upK;
-  bf16x8 wf[2][KS];
+  // Query-folded weight rows (MFMA A operand): row t = 32 tb + lr of this
+  // lane and its partner t + D/2; scores come out in base-2 logits.
+  bf16x8 gf[2][KS];
   {
-    const int hrow = (head_ok ? head : 0) * D + 32 * tb + lr;
+    const bf16* Wk = (const bf16*)p.W_upK;
+    const int hh = head_ok ? head : 0;
+    const int t = 32 * tb + lr;
+    const bf16* qp = (const bf16*)p.q + ((size_t)b * p.H + hh) * D;
+    const float scl = kLog2e / sqrtf((float)D);
+    const float qa = (float)qp[t] * scl, qb = (float)qp[t + HALF] * scl;
+    const bf16* r0 = Wk + (size_t)(hh * D + t) * DD + 8 * lg;
+    const bf16* r1 = r0 + (size_t)HALF * DD;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 w0 = *(const bf16x8*)(r0 + 16 * ks), w1 = *(const bf16x8*)(r1 + 16 * ks);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        wf[mb][ks] = *(const bf16x8*)(Wk + (size_t)(hrow + mb * HALF) * DD + 16 * ks + 8 * lg);
+      for (int e = 0; e < 8; ++e) {
+        const float a = (float)w0[e], c = (float)w1[e];
+        gf[0][ks][e] = (bf16)(a * qa + c * qb);
+        gf[1][ks][e] = (bf16)(a * qb - c * qa);
+      }
+    }
   }
-  // q components of this lane's 16 frequencies, scaled into base-2 logits
-  float q1[16], q2[16];
+  // cos/sin(pos theta_t') of this lane's token for its 16 output frequencies
+  // t' = 32 tb + 8 (r/4) + 4 lg + r%4
+  float cs_c[16], cs_s[16];
   {
-    const bf16* qp = (const bf16*)p.q + ((size_t)b * p.H + (head_ok ? head : 0)) * D;
-    const float sc = kLog2e / sqrtf((float)D);
+    const int pos = j_begin + lr;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * tb + 8 * (r >> 2) + 4 * lg + (r & 3);
-      q1[r] = (float)qp[t] * sc;
-      q2[r] = (float)qp[t + HALF] * sc;
+      const float2 v = rope_cs(p.rope, pos, t);
+      cs_c[r] = v.x;
+      cs_s[r] = v.y;
     }
   }
 
   const bf16* Lb = (const bf16*)p.h_D + (size_t)b * p.cap * DD;
-  // staging: TB*DD bf16 = TB*DD/8 chunks of 16 B
   constexpr int NCH = TB * DD / 8;
   constexpr int CPT = (NCH + 511) / 512;
   u32x4 stg[CPT];
@@ -156,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       stg[i] = v;
     }
   };
-  auto store_blk = [&](int buf, int blk) {
+  auto store_blk = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 512 * i;
@@ -165,14 +188,11 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         *(u32x4*)(&sm.lat[buf][row * LP + col]) = stg[i];
       }
     }
-    const int j0 = j_begin + blk * TB;
-    for (int e = tid; e < HALF; e += 512) sm.hi[buf][e] = p.rope.hi[(size_t)(j0 >> 6) * HALF + e];
   };
 
-  // softmax state (kept by lanes of wave hl for head hl, hl < HPW)
-  float m_run = -INFINITY, l_run = 0.f;
-  // latent accumulator: 16x16 tiles over d_down, rows = heads of the group
-  constexpr int NB = DD / 16;                     // n-blocks of 16 latent dims
+  // softmax state, kept by the tb == 0 wave of each head (lanes 0..31 own tokens)
+  float m_ref = kNegBig, l_lane = 0.f;
+  constexpr int NB = DD / 16;
   constexpr int NB_PER_WAVE = (NB + NWAVE - 1) / NWAVE;
   f32x4 acc[NB_PER_WAVE];
 #pragma unroll
@@ -180,7 +200,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 
   if (nblk > 0) {
     load_blk(0);
-    store_blk(0, 0);
+    store_blk(0);
   }
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
@@ -188,7 +208,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     const int j0 = j_begin + blk * TB;
     if (blk + 1 < nblk) load_blk(blk + 1);
 
-    // rebuild 64 key components x 32 tokens: K'^T = W^T L^T
+    // h^D . [alpha | beta] for 32 tokens (lane column lr)
     const bf16* lrow = &sm.lat[buf][lr * LP + 8 * lg];
     f32x16 kc[2];
 #pragma unroll
@@ -198,47 +218,52 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 lf = *(const bf16x8*)(lrow + 16 * ks);
-      kc[0] = mfma32x32x16(wf[0][ks], lf, kc[0]);
-      kc[1] = mfma32x32x16(wf[1][ks], lf, kc[1]);
+      kc[0] = mfma32x32x16(gf[0][ks], lf, kc[0]);
+      kc[1] = mfma32x32x16(gf[1][ks], lf, kc[1]);
     }
-    // RoPE at position j, then this lane's share of q . k
-    const int pos = j0 + lr;
-    const float2* lo_row = &sm.lo[(pos & 63) * HALF];
     float sp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sp = fmaf(cs_c[r], kc[0][r], fmaf(cs_s[r], kc[1][r], sp));
+    sp += __shfl_xor(sp, 32);
+    if (lg == 0) sm.sc[buf][wave][lr] = sp;
+    // advance cos/sin by 32 positions
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * tb + 8 * (r >> 2) + 4 * lg + (r & 3);
-      const float2 a = sm.hi[buf][t], c = lo_row[t];
-      const float cs = a.x * c.x - a.y * c.y, sn = a.x * c.y + a.y * c.x;
-      const float k1 = kc[0][r], k2 = kc[1][r];
-      sp += k1 * (q1[r] * cs + q2[r] * sn) + k2 * (q2[r] * cs - q1[r] * sn);
+      const float2 st = sm.step[t];
+      const float c = cs_c[r] * st.x - cs_s[r] * st.y;
+      cs_s[r] = cs_c[r] * st.y + cs_s[r] * st.x;
+      cs_c[r] = c;
     }
-    sp += __shfl_xor(sp, 32);
-    if (lg == 0) sm.sc[wave][lr] = sp;
-    __syncthreads();
+    __syncthreads();  // B1: partial scores visible; lat[buf ^ 1] free
 
-    // online softmax per head: wave hl, lanes 0..31 (one token each)
-    if (wave < HPW) {
+    if (blk + 1 < nblk) store_blk(buf ^ 1);
+    if (tb == 0 && wave < NWAVE) {
+      // score of token j0 + lr for head hl (both lane halves hold it)
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < WPH; ++i) s += sm.sc[wave * WPH + i][lr];
-      const bool ok = (hg * HPW + wave < p.H) && (j0 + lr < j_end);
+      for (int i = 0; i < WPH; ++i) s += sm.sc[buf][wave + i][lr];
+      const bool ok = head_ok && (j0 + lr < j_end);
       s = ok ? s : -INFINITY;
-      float mt = s;
+      float al = 1.f;
+      if (__builtin_amdgcn_ballot_w64(s > m_ref + kTau) != 0) {
+        float mt = s;
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-      const float m_new = fmaxf(m_run, mt);
-      const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-      const float e = (m_new == -INFINITY) ? 0.f : exp2f(s - m_new);
-      float es = e;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) es += __shfl_xor(es, off);
-      l_run = l_run * al + es;
-      m_run = m_new;
-      if (lg == 0) sm.pm[wave][lr] = (bf16)e;
-      if (lane == 0) sm.alpha[wave] = al;
+        for (int off = 16; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+        const float m_new = fmaxf(m_ref, mt);
+        al = __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_lane *= al;
+      }
+      const float e = __builtin_amdgcn_exp2f(s - m_ref);
+      const bf16 eb = (bf16)e;
+      if (lg == 0) {
+        l_lane += (float)eb;  // the sum of exactly the probabilities used below
+        sm.pm[buf][hl][lr] = eb;
+      }
+      if (lane == 0) sm.alpha[buf][hl] = al;
     }
-    __syncthreads();
+    __syncthreads();  // B2: probabilities, rescale factors and lat[buf ^ 1] visible
 
     // acc[head, dims] = alpha * acc + P L  (16x16x32 MFMA, K = the 32 tokens)
 #pragma unroll
@@ -248,7 +273,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         const int row = lane & 15, kg = lane >> 4;
         bf16x8 af;
         if (row < HPW) {
-          af = *(const bf16x8*)(&sm.pm[row][8 * kg]);
+          af = *(const bf16x8*)(&sm.pm[buf][row][8 * kg]);
         } else {
 #pragma unroll
           for (int c = 0; c < 8; ++c) af[c] = (bf16)0.f;
@@ -260,23 +285,23 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int hrow = 4 * kg + r;
-          acc[i][r] *= (hrow < HPW) ? sm.alpha[hrow] : 1.f;
+          acc[i][r] *= (hrow < HPW) ? sm.alpha[buf][hrow] : 1.f;
         }
         acc[i] = mfma16x16x32(af, bfr, acc[i]);
       }
     }
-    if (blk + 1 < nblk) store_blk(buf ^ 1, blk + 1);
-    __syncthreads();
   }
 
   // partials: part[((b*H + head)*n_chunks + chunk)] = {m, l, acc[d_down]}
   float* part = (float*)p.ws;
-  if (wave < HPW && lane == 0) {
-    const int hh = hg * HPW + wave;
-    if (hh < p.H) {
-      float* dst = part + (((size_t)b * p.H + hh) * g.n_chunks + chunk) * g.part_lat_floats;
-      dst[0] = m_run;
-      dst[1] = l_run;
+  if (tb == 0) {
+    float l = l_lane;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0 && head_ok) {
+      float* dst = part + (((size_t)b * p.H + head) * g.n_chunks + chunk) * g.part_lat_floats;
+      dst[0] = m_ref;
+      dst[1] = l;
     }
   }
 #pragma unroll
@@ -297,74 +322,79 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 }
 
 // --------------------------------------------------------------------------
-// Window part: keys/values of positions max(0, p-w+1) .. p from the ring.
+// Window part: the min(w, ctx) ring slots that hold positions p-w+1 .. p (the
+// set of valid slots is always 0 .. nw-1; its order does not matter to a
+// softmax).  One workgroup per (batch, head); 64-key chunks staged in LDS with
+// 16-byte loads; four lanes per key for the scores, online softmax.
 template <int D>
 __global__ __launch_bounds__(256) void decode_window(DecodeProblem p, float* part_win) {
-  __shared__ float qs[D];
-  __shared__ float ps[256];
-  __shared__ float red[256];
+  constexpr int CK = 64, KP = D + 8;
+  __shared__ bf16 ks[CK * KP];
+  __shared__ bf16 vs[CK * KP];
+  __shared__ float sc[CK];
   __shared__ float accs[256 / D][D];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const long pp = (long)p.ctx - 1;
-  const long first = pp - p.w + 1 > 0 ? pp - p.w + 1 : 0;
-  const int nw = (int)(pp - first + 1 < p.w ? pp - first + 1 : p.w);
-  const float sc = kLog2e / sqrtf((float)D);
+  const int nw = (int)(pp + 1 < p.w ? pp + 1 : p.w);
+  const float scl = kLog2e / sqrtf((float)D);
   const bf16* qp = (const bf16*)p.q + (size_t)bh * D;
-  for (int d = tid; d < D; d += 256) qs[d] = (float)qp[d] * sc;
-  __syncthreads();
   const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
   const bf16* Vw = (const bf16*)p.V_win + (size_t)bh * p.w * D;
-  float m_run = -INFINITY, l_run = 0.f;
-  constexpr int KPB = 256 / D;  // key lanes in the value phase
+  // score lanes: key kq = tid / 4, dims pt + 4 e
+  const int kq = tid >> 2, pt = tid & 3;
+  float qv[D / 4];
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) qv[e] = (float)qp[pt + 4 * e] * scl;
+  // value lanes: dim vd, keys vk, vk + 256/D, ...
+  constexpr int KPB = 256 / D;
   const int vd = tid % D, vk = tid / D;
-  float acc = 0.f;
-  for (int c0 = 0; c0 < nw; c0 += 256) {
-    const int kk = c0 + tid;
-    float s = -INFINITY;
-    if (kk < nw) {
-      const long pos = first + kk;
-      const bf16* kr = Kw + (size_t)(pos % p.w) * D;
-      float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot += qs[d] * (float)kr[d];
-      s = dot;
-    }
-    red[tid] = s;
+  float m_run = kNegBig, l_run = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < nw; c0 += CK) {
+    const int nk = min(CK, nw - c0);
     __syncthreads();
-    for (int st = 128; st > 0; st >>= 1) {
-      if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
-      __syncthreads();
+    for (int c = tid; c < CK * D / 8; c += 256) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (r < nk) {
+        kv = *(const u32x4*)(Kw + (size_t)(c0 + r) * D + col);
+        vv = *(const u32x4*)(Vw + (size_t)(c0 + r) * D + col);
+      }
+      *(u32x4*)(ks + r * KP + col) = kv;
+      *(u32x4*)(vs + r * KP + col) = vv;
     }
-    const float m_new = fmaxf(m_run, red[0]);
     __syncthreads();
-    const float al = exp2f(m_run - m_new);
-    const float e = (kk < nw) ? exp2f(s - m_new) : 0.f;
-    ps[tid] = e;
-    red[tid] = e;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) dot = fmaf(qv[e], (float)ks[kq * KP + pt + 4 * e], dot);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    if (pt == 0) sc[kq] = kq < nk ? dot : -INFINITY;
     __syncthreads();
-    for (int st = 128; st > 0; st >>= 1) {
-      if (tid < st) red[tid] += red[tid + st];
-      __syncthreads();
-    }
-    l_run = l_run * al + red[0];
+    float mt = -INFINITY;
+    for (int i = 0; i < CK; ++i) mt = fmaxf(mt, sc[i]);
+    const float m_new = fmaxf(m_run, mt);
+    const float al = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
+    float ls = 0.f;
     acc *= al;
-    const int lim = min(256, nw - c0);
-    for (int i = vk; i < lim; i += KPB) {
-      const long pos = first + c0 + i;
-      acc += ps[i] * (float)Vw[(size_t)(pos % p.w) * D + vd];
+    for (int i = 0; i < CK; ++i) {
+      const float e = __builtin_amdgcn_exp2f(sc[i] - m_new);
+      ls += e;
+      if ((i % KPB) == vk) acc = fmaf(e, (float)vs[i * KP + vd], acc);
     }
-    __syncthreads();
+    l_run = l_run * al + ls;
   }
   accs[vk][vd] = acc;
   __syncthreads();
   float* dst = part_win + (size_t)bh * (2 + D);
   if (tid < D) {
     float a = 0.f;
+#pragma unroll
     for (int i = 0; i < KPB; ++i) a += accs[i][tid];
     dst[2 + tid] = a;
   }
   if (tid == 0) {
-    dst[0] = m_run;
+    dst[0] = nw > 0 ? m_run : -INFINITY;
     dst[1] = l_run;
   }
 }
