@@ -183,115 +183,131 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int nQT, int remap) {
+__global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int nQT, int nPair,
+                                                          int remap) {
   __shared__ PassSmem<D> sm;
   const int N = p.N, H = p.H, BH = p.B * p.H, w = p.w;
-  // Longest query tiles first; with remap, all tiles of one (batch, head) stay
-  // on one XCD so its K/V prefix is shared through that XCD's L2.
-  int qt, bh;
+  // Causal balance: a workgroup takes query tile nQT-1-pr and then tile pr,
+  // so every workgroup streams about the same number of key tiles.  With
+  // remap, all tiles of one (batch, head) stay on one XCD so its K/V prefix
+  // is shared through that XCD's L2.
+  int pr, bh;
   {
     const int bid = blockIdx.x;
     if (remap) {
       const int x = bid % kNumXcd, k = bid / kNumXcd;
-      qt = nQT - 1 - (k % nQT);
-      bh = (k / nQT) * kNumXcd + x;
+      pr = k % nPair;
+      bh = (k / nPair) * kNumXcd + x;
     } else {
-      qt = nQT - 1 - bid / BH;
+      pr = bid / BH;
       bh = bid % BH;
     }
   }
   const int b = bh / H, h = bh % H;
   const size_t kv_off = (size_t)bh * N * D;
   const f16* Qp = (const f16*)p.Q + kv_off;
-  const f16* Ks[2] = {(const f16*)p.K_glob + kv_off, (const f16*)p.K_loc + kv_off};
-  const f16* Vs[2] = {(const f16*)p.V_glob + kv_off, (const f16*)p.V_loc + kv_off};
+  const f16* Kg = (const f16*)p.K_glob + kv_off;
+  const f16* Kl = (const f16*)p.K_loc + kv_off;
+  const f16* Vg = (const f16*)p.V_glob + kv_off;
+  const f16* Vl = (const f16*)p.V_loc + kv_off;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int i0 = qt * QT, qw0 = i0 + 32 * wave;
-  const int qi = qw0 + lr;  // this lane's query
-  const int i_last = min(i0 + QT - 1, N - 1);
-  const int wi_last = min(qw0 + 31, N - 1);
-
-  f16x8 qf[D / 16];
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      u32x4 v = (qi < N) ? *(const u32x4*)(Qp + (size_t)qi * D + 16 * st + 8 * lg) : z;
-      qf[st] = __builtin_bit_cast(f16x8, v);
-    }
-  }
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_ref = kNegBig, l_run = 0.f;
   const float sc = kLog2e / sqrtf((float)D);
   const bool nvec = (N % 8) == 0;
+  const int q_hi = nQT - 1 - pr;
+  const int nq = (q_hi == pr) ? 1 : 2;
 
-  // Passes: for each key tile, the global source (if any pair of the
-  // workgroup is at distance >= w) then the local source (if any is < w).
-  const int j_end = min(N, i0 + QT);
-  auto need_glob = [&](int j0) { return i_last - j0 >= w; };
-  auto need_loc = [&](int j0) { return w > 0 && max(i0 - (j0 + KT - 1), 0) < w; };
-  int j0 = 0, src = need_glob(0) ? 0 : 1;  // src 0 = global, 1 = local
-  Stage<D> stg;
-  load_pass<D>(stg, Ks[src], Vs[src], N, j0, nvec && (j0 + KT <= N));
-  store_pass<D>(stg, sm.k[0], sm.v[0]);
-  __syncthreads();
-  int buf = 0;
-  while (true) {
-    int nj0 = j0, nsrc;
-    if (src == 0 && need_loc(j0)) {
-      nsrc = 1;
-    } else {
-      nj0 = j0 + KT;
-      nsrc = need_glob(nj0) ? 0 : 1;
-    }
-    const bool has_next = nj0 < j_end;
-    if (has_next) load_pass<D>(stg, Ks[nsrc], Vs[nsrc], N, nj0, nvec && (nj0 + KT <= N));
+  for (int qn = 0; qn < nq; ++qn) {
+    const int qt = qn == 0 ? q_hi : pr;
+    if (qn > 0) __syncthreads();  // the LDS buffers are reused
+    const int i0 = qt * QT, qw0 = i0 + 32 * wave;
+    const int qi = qw0 + lr;  // this lane's query
+    const int i_last = min(i0 + QT - 1, N - 1);
+    const int wi_last = min(qw0 + 31, N - 1);
 
-    const int wdmax = wi_last - j0, wdmin = qw0 - (j0 + KT - 1);
-    if (qw0 < N && wdmax >= 0) {
-      // keep pairs with distance in [lo, hi) for this source, j <= i, j < N
-      const bool glob = src == 0;
-      const bool part = glob ? (wdmax >= w) : (w > 0 && max(wdmin, 0) < w);
-      if (part) {
-        const bool masked =
-            (glob ? (wdmin < w) : (wdmin < 0 || wdmax >= w)) || (j0 + KT > N);
-        const int base = qi - j0 - 8 * lg;  // distance of key offset 0
-        const int lo = glob ? w : 0;
-        // keep iff base - hi < off <= min(base - lo, N - 1 - j0 - 8 lg)
-        const int keep_lo = glob ? -1 : base - w;
-        const int keep_hi = min(base - lo, N - 1 - j0 - 8 * lg);
-        wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, masked, keep_lo, keep_hi, sc,
-                     lr, lg);
+    f16x8 qf[D / 16];
+    {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        u32x4 v = (qi < N) ? *(const u32x4*)(Qp + (size_t)qi * D + 16 * st + 8 * lg) : z;
+        qf[st] = __builtin_bit_cast(f16x8, v);
       }
     }
-    if (!has_next) break;
-    store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
-    __syncthreads();
-    buf ^= 1;
-    j0 = nj0;
-    src = nsrc;
-  }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_ref = kNegBig, l_run = 0.f;
 
-  if (qi >= N) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-  bf16* out = (bf16*)p.o + ((size_t)b * N + qi) * (size_t)(H * D) + (size_t)h * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d = 32 * db + 8 * rq + 4 * lg;
-      u32x2 v;
-      v[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
-      v[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-      *(u32x2*)(out + d) = v;
+    // Passes: for each key tile, the global source (if any pair of the
+    // workgroup is at distance >= w) then the local source (if any is < w).
+    const int j_end = min(N, i0 + QT);
+    auto need_glob = [&](int j0) { return i_last - j0 >= w; };
+    auto need_loc = [&](int j0) { return w > 0 && max(i0 - (j0 + KT - 1), 0) < w; };
+    int j0 = 0, src = need_glob(0) ? 0 : 1;  // src 0 = global, 1 = local
+    Stage<D> stg;
+    load_pass<D>(stg, src ? Kl : Kg, src ? Vl : Vg, N, j0, nvec && (j0 + KT <= N));
+    store_pass<D>(stg, sm.k[0], sm.v[0]);
+    __syncthreads();
+    int buf = 0;
+    while (true) {
+      int nj0 = j0, nsrc;
+      if (src == 0 && need_loc(j0)) {
+        nsrc = 1;
+      } else {
+        nj0 = j0 + KT;
+        nsrc = need_glob(nj0) ? 0 : 1;
+      }
+      const bool has_next = nj0 < j_end;
+      if (has_next)
+        load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
+
+      const int wdmax = wi_last - j0, wdmin = qw0 - (j0 + KT - 1);
+      if (qw0 < N && wdmax >= 0) {
+        // keep pairs with distance in [lo, hi) for this source, j <= i, j < N
+        const bool glob = src == 0;
+        const bool part = glob ? (wdmax >= w) : (w > 0 && max(wdmin, 0) < w);
+        if (part) {
+          const bool masked =
+              (glob ? (wdmin < w) : (wdmin < 0 || wdmax >= w)) || (j0 + KT > N);
+          const int base = qi - j0 - 8 * lg;  // distance of key offset 0
+          const int lo = glob ? w : 0;
+          // keep iff base - hi < off <= min(base - lo, N - 1 - j0 - 8 lg)
+          const int keep_lo = glob ? -1 : base - w;
+          const int keep_hi = min(base - lo, N - 1 - j0 - 8 * lg);
+          wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, masked, keep_lo, keep_hi, sc,
+                       lr, lg);
+        }
+      }
+      if (!has_next) break;
+      store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
+      __syncthreads();
+      buf ^= 1;
+      j0 = nj0;
+      src = nsrc;
     }
+
+    if (qi < N) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const float inv = 1.f / l_tot;
+      bf16* out = (bf16*)p.o + ((size_t)b * N + qi) * (size_t)(H * D) + (size_t)h * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * db + 8 * rq + 4 * lg;
+          u32x2 v;
+          v[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
+          v[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+          *(u32x2*)(out + d) = v;
+        }
+    } else {
+      (void)__shfl_xor(l_run, 32);  // keep the exchange wave-uniform
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -371,12 +387,13 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
   const int BH = p.B * p.H;
   if (dt == DAR_BF16) {
     const int nQT = (p.N + QT - 1) / QT;
+    const int nPair = (nQT + 1) / 2;
     const int remap = (BH % kNumXcd) == 0 ? 1 : 0;
-    const dim3 grid(nQT * BH);
+    const dim3 grid(nPair * BH);
     if (p.d_k == 64)
-      hipLaunchKernelGGL(attn_prefill_f16<64>, grid, dim3(256), 0, s, p, nQT, remap);
+      hipLaunchKernelGGL(attn_prefill_f16<64>, grid, dim3(256), 0, s, p, nQT, nPair, remap);
     else
-      hipLaunchKernelGGL(attn_prefill_f16<128>, grid, dim3(256), 0, s, p, nQT, remap);
+      hipLaunchKernelGGL(attn_prefill_f16<128>, grid, dim3(256), 0, s, p, nQT, nPair, remap);
   } else {
     const dim3 grid((p.N + FQ - 1) / FQ, p.H, p.B);
     if (p.d_k == 64)

@@ -181,7 +181,17 @@ template <typename TM, typename TB, typename TO, int D>
 __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTiles st, int nM,
                                                            int nC, int nCp, int order) {
   typedef typename Vec8<TM>::type TMx8;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * BM * LDA_S * 2];
+  typedef typename Vec8<TB>::type TBx8;
+  // Main loop: k-tiles of GBK = 32 in a 3-stage LDS ring filled by direct
+  // buffer loads (global -> LDS, no staging registers; lanes past the matrix
+  // edge read zeros), prefetching two k-tiles ahead, one barrier per k-tile.
+  // Rows of a k-tile are 64 B = 4 chunks of 16 B; chunk c of row r sits in
+  // slot c ^ ((r >> 1) & 3), which makes the 16-byte MFMA fragment reads of 32
+  // consecutive rows conflict-free.
+  constexpr int GBK = 32, NST = 3;
+  constexpr int STAGE = 2 * BM * GBK;  // elements per stage: token rows, then weight rows
+  constexpr int MAIN_BYTES = NST * STAGE * 2, EPI_BYTES = BM * EPI_P * 4;
+  __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
   // XCD-aware order.  order 0 (large weights): XCD x owns a contiguous group of
   // column tiles, whose slice of the weights stays in its L2, and walks the row
   // tiles in order.  order 1 (weights that fit in one L2): XCD x owns the row
@@ -204,43 +214,51 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   const int col0 = (ct - st.tile0[s]) * BN;  // first segment column of the tile
   const int row0 = mt * BM;
   const int K = p.K, M = p.M;
-  const TM* A = (const TM*)p.A;
-  const TB* Bt = (const TB*)seg.Bt;
-
-  // LDS: [buf][token tile | weight tile], each 128 x LDA_S elements of TM
-  TM* const lds = (TM*)smem;
-  auto sA = [&](int buf) { return lds + (2 * buf) * BM * LDA_S; };
-  auto sB = [&](int buf) { return lds + (2 * buf + 1) * BM * LDA_S; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   // wave -> (partner pair of 32-column blocks, 64-token half)
   const int wp = wave & 1, wt = wave >> 1;
-  const int cb0 = (D == 128) ? wp : 2 * wp;             // first column block (of 4)
-  const int cb1 = (D == 128) ? wp + 2 : 2 * wp + 1;     // its rotate-half partner
+  const int cb0 = (D == 128) ? wp : 2 * wp;          // first column block (of 4)
+  const int cb1 = (D == 128) ? wp + 2 : 2 * wp + 1;  // its rotate-half partner
 
-  u32x4 ra[4], rb[4];
-  auto load_regs = [&](int k0) {
+  // Buffer resources over this tile's rows (byte extents; invalid lanes use an
+  // offset past the extent and read zeros).
+  const size_t a_ext = (size_t)(M - row0) * K * sizeof(TM);
+  const size_t b_ext = (size_t)(seg.width - col0) * K * sizeof(TB);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const TM*)p.A + (size_t)row0 * K), (short)0,
+      (int)(a_ext < 0x7ffffff0u ? a_ext : 0x7ffffff0u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const TB*)seg.Bt + (size_t)col0 * K), (short)0,
+      (int)(b_ext < 0x7ffffff0u ? b_ext : 0x7ffffff0u), 0x00020000);
+  // This lane's two 16-byte chunks per operand and k-tile.
+  int lrow[2], lcol[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i, kc = (tid & 7) * 8;
-      const int ar = row0 + r, bc = col0 + r, kk = k0 + kc;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      ra[i] = (ar < M && kk < K) ? *(const u32x4*)(A + (size_t)ar * K + kk) : z;
-      rb[i] = (bc < seg.width && kk < K) ? *(const u32x4*)(Bt + (size_t)bc * K + kk) : z;
+  for (int i = 0; i < 2; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane;  // 16-byte slot in the k-tile
+    const int r = P >> 2, slot = P & 3;
+    lrow[i] = r;
+    lcol[i] = 8 * (slot ^ ((r >> 1) & 3));
+  }
+  TM* const lds = (TM*)smem;
+  auto issue = [&](int kt, int stg) {
+    const int k0 = kt * GBK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = lrow[i], kk = k0 + lcol[i];
+      const unsigned oa = (row0 + r < M && kk < K) ? (unsigned)((r * K + kk) * sizeof(TM)) : 0x80000000u;
+      const unsigned ob = (col0 + r < seg.width && kk < K) ? (unsigned)((r * K + kk) * sizeof(TB))
+                                                          : 0x80000000u;
+      TM* dst_a = lds + stg * STAGE + (i * 4 + wave) * 512;
+      TM* dst_b = lds + stg * STAGE + BM * GBK + (i * 4 + wave) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst_a,
+                                               16, oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)dst_b,
+                                               16, ob, 0, 0, 0);
     }
   };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i, kc = (tid & 7) * 8;
-      *(u32x4*)(sA(buf) + r * LDA_S + kc) = ra[i];
-      if constexpr (__is_same(TM, TB))
-        *(u32x4*)(sB(buf) + r * LDA_S + kc) = rb[i];
-      else
-        *(u32x4*)(sB(buf) + r * LDA_S + kc) = bf16x8_to_f16x8(rb[i]);
-    }
-  };
+  auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ ((row >> 1) & 3)); };
 
   // acc[i][j]: column block (cb0, cb1)[i] x token block j of this wave
   f32x16 acc[2][2];
@@ -251,28 +269,41 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
+  const int nk = (K + GBK - 1) / GBK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_regs((kt + 1) * BK);
-    const TM* w0 = sB(cur) + (32 * cb0 + lr) * LDA_S + 8 * lg;
-    const TM* w1 = sB(cur) + (32 * cb1 + lr) * LDA_S + 8 * lg;
-    const TM* h0 = sA(cur) + (64 * wt + lr) * LDA_S + 8 * lg;
+    // this lane's loads of k-tile kt are done once at most those of kt+1 (4) remain
+    if (kt + 1 < nk)
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();  // k-tile kt is in LDS; everyone is done with k-tile kt-1
+    if (kt + 2 < nk) issue(kt + 2, (kt + 2) % NST);
+    const TM* sa = lds + (kt % NST) * STAGE;
+    const TB* sb = (const TB*)(lds + (kt % NST) * STAGE + BM * GBK);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const TMx8 a0 = *(const TMx8*)(w0 + 16 * ks), a1 = *(const TMx8*)(w1 + 16 * ks);
-      const TMx8 b0 = *(const TMx8*)(h0 + 16 * ks), b1 = *(const TMx8*)(h0 + 32 * LDA_S + 16 * ks);
-      acc[0][0] = mfma32x32x16(a0, b0, acc[0][0]);
-      acc[0][1] = mfma32x32x16(a0, b1, acc[0][1]);
-      acc[1][0] = mfma32x32x16(a1, b0, acc[1][0]);
-      acc[1][1] = mfma32x32x16(a1, b1, acc[1][1]);
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      const int ch = 2 * ks + lg;
+      TMx8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 32 * (i ? cb1 : cb0) + lr;
+        const TBx8 w = *(const TBx8*)(sb + frag_off(row, ch));
+        if constexpr (__is_same(TM, TB))
+          a[i] = w;
+        else
+          a[i] = __builtin_bit_cast(TMx8, bf16x8_to_f16x8(__builtin_bit_cast(u32x4, w)));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const TMx8*)(sa + frag_off(64 * wt + 32 * j + lr, ch));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // LDS is reused by the epilogue
 
   // Epilogue.  Register r of acc[i][j] is column 32*cb_i + 8*(r/4) + 4*lg + r%4
   // of the tile, token 64*wt + 32*j + lr.
