@@ -15,7 +15,7 @@
 // rotation acts on them, so sum_j p_j h^D_j W_upV = (sum_j p_j h^D_j) W_upV
 // and the latent kernel accumulates sum_j p_j h^D_j in d_down-space only.
 //
-// Three launches:
+// Two launches:
 //  latent  -- one workgroup per (batch, head group, context chunk), 8 waves.
 //             Each wave keeps 64 rows of W_upK^T in registers: 32 rotary
 //             frequencies t of one head and their rotate-half partners
@@ -24,7 +24,8 @@
 //             buffered); K'^T = W^T L^T on 32x32x16 MFMAs; RoPE + q.k per lane;
 //             an online softmax per head; sum_j p_j h^D_j on 16x16x32 MFMAs.
 //             Writes (max, sum, latent accumulator) per chunk.
-//  window  -- one workgroup per (batch, head): the w full keys/values.
+//  window  -- extra workgroups of the same launch, one per (batch, head):
+//             the w full keys/values.
 //  combine -- log-sum-exp merge of all partials, then one lift by W_upV.
 // Scores are kept in base 2 (log2(e)/sqrt(d_k) folded into q).
 #include <math.h>
@@ -52,6 +53,7 @@ struct DecodeGeom {
   int heads_per_wg;
   int n_hg;        // head groups
   int pairs;       // B * n_chunks, padded to a multiple of kNumXcd
+  int n_win_pad;   // window workgroups (B * H), padded to a multiple of kNumXcd
   size_t part_lat_floats;  // per (b, head, chunk): 2 + d_down
 };
 
@@ -70,6 +72,7 @@ DecodeGeom geom(const DecodeProblem& p) {
   g.n_chunks = g.n_glob > 0 ? (g.n_glob + g.chunk_len - 1) / g.chunk_len : 1;
   g.pairs = (p.B * g.n_chunks + kNumXcd - 1) / kNumXcd * kNumXcd;
   g.part_lat_floats = 2 + (size_t)p.d_down;
+  g.n_win_pad = (p.B * p.H + kNumXcd - 1) / kNumXcd * kNumXcd;
   return g;
 }
 
@@ -99,15 +102,112 @@ struct LatentSmem {
 // gives h^D . alpha and h^D . beta for 32 tokens and the score needs two FMAs
 // per frequency.  cos/sin(j theta_t) advance by one complex multiply per
 // 32-token block (the fine table's row 32), starting from the fp64 tables.
+// --------------------------------------------------------------------------
+// Window part: the min(w, ctx) ring slots that hold positions p-w+1 .. p (the
+// set of valid slots is always 0 .. nw-1; its order does not matter to a
+// softmax).  Run by extra workgroups of the latent launch, one per (batch,
+// head): 64-key chunks staged in LDS with 16-byte loads, eight lanes per key
+// for the scores, online softmax.
+template <int D>
+struct WindowSmem {
+  static constexpr int CK = 64, KP = D + 8;
+  bf16 ks[CK * KP];
+  bf16 vs[CK * KP];
+  float sc[CK];
+  float accs[512 / D][D];
+};
+
+template <int D>
+__device__ void window_part(const DecodeProblem& p, float* part_win, int bh, WindowSmem<D>& sm) {
+  constexpr int CK = WindowSmem<D>::CK, KP = WindowSmem<D>::KP, NT = 512;
+  const int tid = threadIdx.x;
+  const long pp = (long)p.ctx - 1;
+  const int nw = (int)(pp + 1 < p.w ? pp + 1 : p.w);
+  const float scl = kLog2e / sqrtf((float)D);
+  const bf16* qp = (const bf16*)p.q + (size_t)bh * D;
+  const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
+  const bf16* Vw = (const bf16*)p.V_win + (size_t)bh * p.w * D;
+  // score lanes: key kq = tid / 8, dims pt + 8 e
+  const int kq = tid >> 3, pt = tid & 7;
+  float qv[D / 8];
+#pragma unroll
+  for (int e = 0; e < D / 8; ++e) qv[e] = (float)qp[pt + 8 * e] * scl;
+  // value lanes: dim vd, keys vk, vk + NT/D, ...
+  constexpr int KPB = NT / D;
+  const int vd = tid % D, vk = tid / D;
+  float m_run = kNegBig, l_run = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < nw; c0 += CK) {
+    const int nk = min(CK, nw - c0);
+    __syncthreads();
+    for (int c = tid; c < CK * D / 8; c += NT) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (r < nk) {
+        kv = *(const u32x4*)(Kw + (size_t)(c0 + r) * D + col);
+        vv = *(const u32x4*)(Vw + (size_t)(c0 + r) * D + col);
+      }
+      *(u32x4*)(sm.ks + r * KP + col) = kv;
+      *(u32x4*)(sm.vs + r * KP + col) = vv;
+    }
+    __syncthreads();
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 8; ++e) dot = fmaf(qv[e], (float)sm.ks[kq * KP + pt + 8 * e], dot);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    if (pt == 0) sm.sc[kq] = kq < nk ? dot : -INFINITY;
+    __syncthreads();
+    float mt = -INFINITY;
+    for (int i = 0; i < CK; ++i) mt = fmaxf(mt, sm.sc[i]);
+    const float m_new = fmaxf(m_run, mt);
+    const float al = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float ls = 0.f;
+    acc *= al;
+    for (int i = 0; i < CK; ++i) {
+      const float e = __builtin_amdgcn_exp2f(sm.sc[i] - m_new);
+      ls += e;
+      if ((i % KPB) == vk) acc = fmaf(e, (float)sm.vs[i * KP + vd], acc);
+    }
+    l_run = l_run * al + ls;
+  }
+  sm.accs[vk][vd] = acc;
+  __syncthreads();
+  float* dst = part_win + (size_t)bh * (2 + D);
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < KPB; ++i) a += sm.accs[i][tid];
+    dst[2 + tid] = a;
+  }
+  if (tid == 0) {
+    dst[0] = nw > 0 ? m_run : -INFINITY;
+    dst[1] = l_run;
+  }
+}
+
 template <int D, int KS>
-__global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeGeom g) {
+__global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeGeom g,
+                                                    float* part_win) {
   using S = LatentSmem<D, KS>;
   constexpr int DD = S::DD, LP = S::LP, HPW = NWAVE * 64 / D, WPH = D / 64, HALF = D / 2;
-  __shared__ S sm;
+  union Smem {
+    S lat;
+    WindowSmem<D> win;
+  };
+  __shared__ Smem smu;
+  S& sm = smu.lat;
 
+  // The first n_win_pad workgroups do the window part (one per (batch,
+  // head)); they start first and overlap the latent stream.
+  if ((int)blockIdx.x < g.n_win_pad) {
+    if ((int)blockIdx.x < p.B * p.H) window_part<D>(p, part_win, blockIdx.x, smu.win);
+    return;
+  }
   // XCD-aware order: the head groups of one (batch, chunk) run on one XCD so
   // its latent block is fetched from HBM once and served to the rest by L2.
-  const int bid = blockIdx.x;
+  const int bid = blockIdx.x - g.n_win_pad;
   const int x = bid % kNumXcd, k = bid / kNumXcd;
   const int pair = x + kNumXcd * (k / g.n_hg), hg = k % g.n_hg;
   if (pair >= p.B * g.n_chunks) return;
@@ -265,7 +365,10 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     }
     __syncthreads();  // B2: probabilities, rescale factors and lat[buf ^ 1] visible
 
-    // acc[head, dims] = alpha * acc + P L  (16x16x32 MFMA, K = the 32 tokens)
+    // acc[head, dims] = alpha * acc + P L  (16x16x32 MFMA, K = the 32 tokens).
+    // Contraction slot c of lane group kg is token 8*(c/2) + 2*kg + c%2: both
+    // operands use that order, and the four groups then read latent rows two
+    // apart, which fall in disjoint LDS banks.
 #pragma unroll
     for (int i = 0; i < NB_PER_WAVE; ++i) {
       const int nb = wave + NWAVE * i;
@@ -273,7 +376,12 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         const int row = lane & 15, kg = lane >> 4;
         bf16x8 af;
         if (row < HPW) {
-          af = *(const bf16x8*)(&sm.pm[buf][row][8 * kg]);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t two = *(const uint32_t*)(&sm.pm[buf][row][8 * m + 2 * kg]);
+            af[2 * m] = __builtin_bit_cast(bf16, (uint16_t)(two & 0xffffu));
+            af[2 * m + 1] = __builtin_bit_cast(bf16, (uint16_t)(two >> 16));
+          }
         } else {
 #pragma unroll
           for (int c = 0; c < 8; ++c) af[c] = (bf16)0.f;
@@ -281,7 +389,8 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         bf16x8 bfr;
         const int n = nb * 16 + row;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) bfr[c] = sm.lat[buf][(8 * kg + c) * LP + n];
+        for (int c = 0; c < 8; ++c)
+          bfr[c] = sm.lat[buf][(8 * (c >> 1) + 2 * kg + (c & 1)) * LP + n];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int hrow = 4 * kg + r;
@@ -318,84 +427,6 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         }
       }
     }
-  }
-}
-
-// --------------------------------------------------------------------------
-// Window part: the min(w, ctx) ring slots that hold positions p-w+1 .. p (the
-// set of valid slots is always 0 .. nw-1; its order does not matter to a
-// softmax).  One workgroup per (batch, head); 64-key chunks staged in LDS with
-// 16-byte loads; four lanes per key for the scores, online softmax.
-template <int D>
-__global__ __launch_bounds__(256) void decode_window(DecodeProblem p, float* part_win) {
-  constexpr int CK = 64, KP = D + 8;
-  __shared__ bf16 ks[CK * KP];
-  __shared__ bf16 vs[CK * KP];
-  __shared__ float sc[CK];
-  __shared__ float accs[256 / D][D];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const long pp = (long)p.ctx - 1;
-  const int nw = (int)(pp + 1 < p.w ? pp + 1 : p.w);
-  const float scl = kLog2e / sqrtf((float)D);
-  const bf16* qp = (const bf16*)p.q + (size_t)bh * D;
-  const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
-  const bf16* Vw = (const bf16*)p.V_win + (size_t)bh * p.w * D;
-  // score lanes: key kq = tid / 4, dims pt + 4 e
-  const int kq = tid >> 2, pt = tid & 3;
-  float qv[D / 4];
-#pragma unroll
-  for (int e = 0; e < D / 4; ++e) qv[e] = (float)qp[pt + 4 * e] * scl;
-  // value lanes: dim vd, keys vk, vk + 256/D, ...
-  constexpr int KPB = 256 / D;
-  const int vd = tid % D, vk = tid / D;
-  float m_run = kNegBig, l_run = 0.f, acc = 0.f;
-  for (int c0 = 0; c0 < nw; c0 += CK) {
-    const int nk = min(CK, nw - c0);
-    __syncthreads();
-    for (int c = tid; c < CK * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (r < nk) {
-        kv = *(const u32x4*)(Kw + (size_t)(c0 + r) * D + col);
-        vv = *(const u32x4*)(Vw + (size_t)(c0 + r) * D + col);
-      }
-      *(u32x4*)(ks + r * KP + col) = kv;
-      *(u32x4*)(vs + r * KP + col) = vv;
-    }
-    __syncthreads();
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) dot = fmaf(qv[e], (float)ks[kq * KP + pt + 4 * e], dot);
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    if (pt == 0) sc[kq] = kq < nk ? dot : -INFINITY;
-    __syncthreads();
-    float mt = -INFINITY;
-    for (int i = 0; i < CK; ++i) mt = fmaxf(mt, sc[i]);
-    const float m_new = fmaxf(m_run, mt);
-    const float al = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
-    acc *= al;
-    for (int i = 0; i < CK; ++i) {
-      const float e = __builtin_amdgcn_exp2f(sc[i] - m_new);
-      ls += e;
-      if ((i % KPB) == vk) acc = fmaf(e, (float)vs[i * KP + vd], acc);
-    }
-    l_run = l_run * al + ls;
-  }
-  accs[vk][vd] = acc;
-  __syncthreads();
-  float* dst = part_win + (size_t)bh * (2 + D);
-  if (tid < D) {
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < KPB; ++i) a += accs[i][tid];
-    dst[2 + tid] = a;
-  }
-  if (tid == 0) {
-    dst[0] = nw > 0 ? m_run : -INFINITY;
-    dst[1] = l_run;
   }
 }
 
@@ -450,9 +481,10 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeo
 }
 
 template <int D, int KS>
-hipError_t launch_latent(const DecodeProblem& p, const DecodeGeom& g, hipStream_t s) {
-  const int grid = g.pairs * g.n_hg;
-  hipLaunchKernelGGL((decode_latent<D, KS>), dim3(grid), dim3(512), 0, s, p, g);
+hipError_t launch_latent(const DecodeProblem& p, const DecodeGeom& g, float* part_win,
+                         hipStream_t s) {
+  const int grid = g.n_win_pad + g.pairs * g.n_hg;
+  hipLaunchKernelGGL((decode_latent<D, KS>), dim3(grid), dim3(512), 0, s, p, g, part_win);
   return hipGetLastError();
 }
 
@@ -473,7 +505,7 @@ hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
   hipError_t e = hipSuccess;
   const int KS = p.d_down / 16;
 #define DAR_LAT(DV, KV) \
-  if (p.d_k == DV && KS == KV) e = launch_latent<DV, KV>(p, g, s);
+  if (p.d_k == DV && KS == KV) e = launch_latent<DV, KV>(p, g, part_win, s);
   DAR_LAT(64, 2)
   DAR_LAT(64, 4)
   DAR_LAT(64, 8)
@@ -484,15 +516,12 @@ hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
   DAR_LAT(128, 16)
 #undef DAR_LAT
   if (e != hipSuccess) return e;
-  if (p.d_k == 64) {
-    hipLaunchKernelGGL(decode_window<64>, dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+  if (p.d_k == 64)
     hipLaunchKernelGGL(decode_combine<64>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
                        part_win);
-  } else {
-    hipLaunchKernelGGL(decode_window<128>, dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+  else
     hipLaunchKernelGGL(decode_combine<128>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
                        part_win);
-  }
   return hipGetLastError();
 }
 

@@ -116,16 +116,19 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
                                           int lr, int lg) {
   constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
   // S^T = K Q^T: s[kb][r] is key j0 + 8 lg + key_off(kb, r) of this lane's query.
+  // All K fragments of a 32-key block are read before its MFMAs.
   f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
+    f16x8 kf[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      acc = mfma32x32x16(*(const f16x8*)(base + 16 * st), qf[st], acc);
+    for (int st = 0; st < D / 16; ++st) acc = mfma32x32x16(kf[st], qf[st], acc);
     s[kb] = acc;
   }
   // keep iff keep_lo < key_off <= keep_hi (distance window, causality, length)
@@ -156,6 +159,16 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
+  // V^T fragments of the first column blocks are requested now and arrive
+  // while the softmax below runs.
+  constexpr int VPRE = (D == 64) ? 2 : 2;  // column blocks of 32 preloaded
+  f16x8 vf[VPRE][4];
+#pragma unroll
+  for (int db = 0; db < VPRE; ++db) {
+    const f16* vb = sv + (32 * db + lr) * VP + 8 * lg;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vf[db][u] = *(const f16x8*)(vb + 16 * u);
+  }
   // p = 2^(s*sc - m_ref), rounded to fp16 for the MFMA; l sums the same fp16 p
   f16x8 pf[4];
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -175,10 +188,17 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
   }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    const f16* base = sv + (32 * db + lr) * VP + 8 * lg;
+    if (db < VPRE) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      o[db] = mfma32x32x16(*(const f16x8*)(base + 16 * u), pf[u], o[db]);
+      for (int u = 0; u < 4; ++u) o[db] = mfma32x32x16(vf[db][u], pf[u], o[db]);
+    } else {
+      const f16* vb = sv + (32 * db + lr) * VP + 8 * lg;
+      f16x8 vx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vx[u] = *(const f16x8*)(vb + 16 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[db] = mfma32x32x16(vx[u], pf[u], o[db]);
+    }
   }
 }
 
