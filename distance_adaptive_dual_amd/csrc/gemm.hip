@@ -182,14 +182,18 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
                                                            int nC, int nCp, int order) {
   typedef typename Vec8<TM>::type TMx8;
   typedef typename Vec8<TB>::type TBx8;
+  // Workgroup tile: 256 tokens x 128 output columns; wave tile 128 tokens x 64
+  // columns (two 32-column blocks that are rotate-half partners), so each
+  // 16-wide k-step reads 6 fragments from LDS for 8 MFMAs.
   // Main loop: k-tiles of GBK = 32 in a 3-stage LDS ring filled by direct
   // buffer loads (global -> LDS, no staging registers; lanes past the matrix
   // edge read zeros), prefetching two k-tiles ahead, one barrier per k-tile.
   // Rows of a k-tile are 64 B = 4 chunks of 16 B; chunk c of row r sits in
   // slot c ^ ((r >> 1) & 3), which makes the 16-byte MFMA fragment reads of 32
   // consecutive rows conflict-free.
+  constexpr int TBM = 2 * BM;  // tokens per workgroup tile
   constexpr int GBK = 32, NST = 3;
-  constexpr int STAGE = 2 * BM * GBK;  // elements per stage: token rows, then weight rows
+  constexpr int TOK = TBM * GBK, STAGE = TOK + BN * GBK;  // elements per stage
   constexpr int MAIN_BYTES = NST * STAGE * 2, EPI_BYTES = BM * EPI_P * 4;
   __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
   // XCD-aware order.  order 0 (large weights): XCD x owns a contiguous group of
@@ -212,12 +216,12 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   const int s = find_seg(st, p.nseg, ct);
   const GemmSeg seg = p.seg[s];
   const int col0 = (ct - st.tile0[s]) * BN;  // first segment column of the tile
-  const int row0 = mt * BM;
+  const int row0 = mt * TBM;
   const int K = p.K, M = p.M;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  // wave -> (partner pair of 32-column blocks, 64-token half)
+  // wave -> (partner pair of 32-column blocks, 128-token half)
   const int wp = wave & 1, wt = wave >> 1;
   const int cb0 = (D == 128) ? wp : 2 * wp;          // first column block (of 4)
   const int cb1 = (D == 128) ? wp + 2 : 2 * wp + 1;  // its rotate-half partner
@@ -232,40 +236,41 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const TB*)seg.Bt + (size_t)col0 * K), (short)0,
       (int)(b_ext < 0x7ffffff0u ? b_ext : 0x7ffffff0u), 0x00020000);
-  // This lane's two 16-byte chunks per operand and k-tile.
-  int lrow[2], lcol[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int P = (i * 4 + wave) * 64 + lane;  // 16-byte slot in the k-tile
-    const int r = P >> 2, slot = P & 3;
-    lrow[i] = r;
-    lcol[i] = 8 * (slot ^ ((r >> 1) & 3));
-  }
   TM* const lds = (TM*)smem;
+  // One 16-byte chunk per lane per load: slot P of the k-tile holds chunk
+  // (P & 3) ^ ((row >> 1) & 3) of row P >> 2.
   auto issue = [&](int kt, int stg) {
     const int k0 = kt * GBK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = lrow[i], kk = k0 + lcol[i];
-      const unsigned oa = (row0 + r < M && kk < K) ? (unsigned)((r * K + kk) * sizeof(TM)) : 0x80000000u;
-      const unsigned ob = (col0 + r < seg.width && kk < K) ? (unsigned)((r * K + kk) * sizeof(TB))
-                                                          : 0x80000000u;
-      TM* dst_a = lds + stg * STAGE + (i * 4 + wave) * 512;
-      TM* dst_b = lds + stg * STAGE + BM * GBK + (i * 4 + wave) * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst_a,
-                                               16, oa, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)dst_b,
-                                               16, ob, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {  // token rows: 1024 chunks
+      const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
+      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 1) & 3));
+      const unsigned oa =
+          (row0 + r < M && kk < K) ? (unsigned)((r * K + kk) * sizeof(TM)) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(lds + stg * STAGE + (i * 4 + wave) * 512),
+          16, oa, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // weight rows: 512 chunks
+      const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
+      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 1) & 3));
+      const unsigned ob =
+          (col0 + r < seg.width && kk < K) ? (unsigned)((r * K + kk) * sizeof(TB)) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb,
+          (__attribute__((address_space(3))) void*)(lds + stg * STAGE + TOK + (i * 4 + wave) * 512),
+          16, ob, 0, 0, 0);
     }
   };
   auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ ((row >> 1) & 3)); };
 
   // acc[i][j]: column block (cb0, cb1)[i] x token block j of this wave
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -273,19 +278,19 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   issue(0, 0);
   if (nk > 1) issue(1, 1);
   for (int kt = 0; kt < nk; ++kt) {
-    // this lane's loads of k-tile kt are done once at most those of kt+1 (4) remain
+    // this lane's loads of k-tile kt are done once at most those of kt+1 (6) remain
     if (kt + 1 < nk)
-      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();  // k-tile kt is in LDS; everyone is done with k-tile kt-1
     if (kt + 2 < nk) issue(kt + 2, (kt + 2) % NST);
     const TM* sa = lds + (kt % NST) * STAGE;
-    const TB* sb = (const TB*)(lds + (kt % NST) * STAGE + BM * GBK);
+    const TB* sb = (const TB*)(lds + (kt % NST) * STAGE + TOK);
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       const int ch = 2 * ks + lg;
-      TMx8 a[2], b[2];
+      TMx8 a[2], b[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = 32 * (i ? cb1 : cb0) + lr;
@@ -296,44 +301,70 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
           a[i] = __builtin_bit_cast(TMx8, bf16x8_to_f16x8(__builtin_bit_cast(u32x4, w)));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const TMx8*)(sa + frag_off(64 * wt + 32 * j + lr, ch));
+      for (int j = 0; j < 4; ++j) b[j] = *(const TMx8*)(sa + frag_off(128 * wt + 32 * j + lr, ch));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
     }
   }
-  __syncthreads();  // LDS is reused by the epilogue
 
-  // Epilogue.  Register r of acc[i][j] is column 32*cb_i + 8*(r/4) + 4*lg + r%4
-  // of the tile, token 64*wt + 32*j + lr.
-  if (seg.kind == kHeadT) {
-    const int H = p.heads, Nq = p.n_seq, width = seg.width;
-    TO* out = (TO*)seg.out;
-    // out[b, head, t, n] through an LDS tile [column][token]
-    float* tile = (float*)smem;
-    constexpr int TP = BM + 4;
+  // Epilogue in two passes through an LDS tile of 128 tokens.  Pass hf takes
+  // token blocks j = 2hf, 2hf+1 of both wave halves, i.e. the two runs of 64
+  // tokens starting at 64hf and 128 + 64hf; it frees half the accumulators.
+  // Register r of acc[i][j] is column 32*cb_i + 8*(r/4) + 4*lg + r%4, token
+  // 128*wt + 32*j + lr of the workgroup tile.
+  float* tile = (float*)smem;
+  const int H = p.heads, Nq = p.n_seq, width = seg.width;
+  TO* out = (TO*)seg.out;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int hf = 0; hf < 2; ++hf) {
+    __syncthreads();  // LDS free (main loop, or the previous pass's stores)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * hf + jj;
+      const int trow = 64 * wt + 32 * jj + lr;  // tile row of this lane's token
+      if (seg.kind == kHeadT) {  // tile [column][token]
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 32 * (i ? cb1 : cb0) + 8 * (r >> 2) + 4 * lg + (r & 3);
-          tile[c * TP + 64 * wt + 32 * j + lr] = acc[i][j][r];
-        }
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * (i ? cb1 : cb0) + 8 * (r >> 2) + 4 * lg + (r & 3);
+            tile[c * (BM + 4) + trow] = acc[i][j][r];
+          }
+      } else {  // tile [token][column], float4 runs
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int c = 32 * (i ? cb1 : cb0) + 8 * a + 4 * lg;
+            *(float4*)(tile + trow * EPI_P + c) =
+                make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2],
+                            acc[i][j][4 * a + 3]);
+          }
+      }
+    }
     __syncthreads();
-    // thread = (column, run of 64 tokens)
-    const int c = tid % BN, r0 = (tid / BN) * 64;
+    if (seg.kind != kHeadT) {
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        const int grow0 = row0 + 128 * run + 64 * hf;
+        if (grow0 < M) epilogue_store<TO, D, 64>(tile + 64 * run * EPI_P, grow0, col0, seg, p);
+      }
+      continue;
+    }
+    // out[b, head, t, n]: thread = (column, run of 64 tokens)
+    constexpr int TP = BM + 4;
+    const int c = tid % BN, run = tid / BN;
     const int gcol = col0 + c;
-    if (gcol >= width) return;
+    const int grow0 = row0 + 128 * run + 64 * hf;
+    if (gcol >= width || grow0 >= M) continue;
     const int head = gcol / D, t = gcol % D;
-    const int grow0 = row0 + r0;
     const int b0 = grow0 / Nq, n0 = grow0 % Nq;
     float v[64];
 #pragma unroll
     for (int i = 0; i < 64; i += 4) {
-      const float4 q4 = *(const float4*)(tile + c * TP + r0 + i);
+      const float4 q4 = *(const float4*)(tile + c * TP + 64 * run + i);
       v[i] = q4.x;
       v[i + 1] = q4.y;
       v[i + 2] = q4.z;
@@ -351,26 +382,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
         out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<TO>(v[i]);
       }
     }
-    return;
   }
-  // Q, K, h^D: LDS tile [token][column] written as float4 runs, then the
-  // row-wise epilogue (one (b, n) per thread, contiguous RoPE table reads,
-  // 16-byte stores).
-  float* tile = (float*)smem;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int c = 32 * (i ? cb1 : cb0) + 8 * a + 4 * lg;
-        const int tok = 64 * wt + 32 * j + lr;
-        *(float4*)(tile + tok * EPI_P + c) =
-            make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2],
-                        acc[i][j][4 * a + 3]);
-      }
-  __syncthreads();
-  epilogue_store<TO, D, BM>(tile, row0, col0, seg, p);
 }
 
 // --------------------------------------------------------------------------
@@ -458,7 +470,7 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
   const SegTiles st = seg_tiles(p);
   const int nC = st.tile0[p.nseg];
   if (dt == DAR_BF16) {
-    const int nM = (p.M + BM - 1) / BM;
+    const int nM = (p.M + 2 * BM - 1) / (2 * BM);  // 256-token workgroup tiles
     const int nCp = (nC + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int nMp = (nM + kNumXcd - 1) / kNumXcd * kNumXcd;
     // weights of every segment, in bytes: small enough for one XCD's L2 (4 MB)?
