@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   // buffer loads (global -> LDS, no staging registers; lanes past the matrix
   // edge read zeros), prefetching two k-tiles ahead, one barrier per k-tile.
   // Rows of a k-tile are 64 B = 4 chunks of 16 B; chunk c of row r sits in
-  // slot c ^ ((r >> 1) & 3), which makes the 16-byte MFMA fragment reads of 32
+  // slot c ^ ((r >> 2) & 3), which makes the 16-byte MFMA fragment reads of 32
   // consecutive rows conflict-free.
   constexpr int TBM = 2 * BM;  // tokens per workgroup tile
   constexpr int GBK = 32, NST = 3;
@@ -238,13 +238,13 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
       (int)(b_ext < 0x7ffffff0u ? b_ext : 0x7ffffff0u), 0x00020000);
   TM* const lds = (TM*)smem;
   // One 16-byte chunk per lane per load: slot P of the k-tile holds chunk
-  // (P & 3) ^ ((row >> 1) & 3) of row P >> 2.
+  // (P & 3) ^ ((row >> 2) & 3) of row P >> 2.
   auto issue = [&](int kt, int stg) {
     const int k0 = kt * GBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // token rows: 1024 chunks
       const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
-      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 1) & 3));
+      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 2) & 3));
       const unsigned oa =
           (row0 + r < M && kk < K) ? (unsigned)((r * K + kk) * sizeof(TM)) : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
 #pragma unroll
     for (int i = 0; i < 2; ++i) {  // weight rows: 512 chunks
       const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
-      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 1) & 3));
+      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 2) & 3));
       const unsigned ob =
           (col0 + r < seg.width && kk < K) ? (unsigned)((r * K + kk) * sizeof(TB)) : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
           16, ob, 0, 0, 0);
     }
   };
-  auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ ((row >> 1) & 3)); };
+  auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ ((row >> 2) & 3)); };
 
   // acc[i][j]: column block (cb0, cb1)[i] x token block j of this wave
   f32x16 acc[2][4];
