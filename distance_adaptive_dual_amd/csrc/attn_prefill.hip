@@ -116,20 +116,36 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
                                           int lr, int lg) {
   constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
   // S^T = K Q^T: s[kb][r] is key j0 + 8 lg + key_off(kb, r) of this lane's query.
-  // All K fragments of a 32-key block are read before its MFMAs.
+  // The K fragments are read before the MFMAs; for d_k = 64 the two 32-key
+  // blocks' accumulation chains are interleaved so that no MFMA waits on the
+  // result of the one just issued.
   f32x16 s[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
-    f16x8 kf[D / 16];
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
-    f32x16 acc;
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  if constexpr (D == 64) {
+    f16x8 kf[2][D / 16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int kb = 0; kb < 2; ++kb) {
+      const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) acc = mfma32x32x16(kf[st], qf[st], acc);
-    s[kb] = acc;
+      for (int st = 0; st < D / 16; ++st) kf[kb][st] = *(const f16x8*)(base + 16 * st);
+    }
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][st], qf[st], s[kb]);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
+      f16x8 kf[D / 16];
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) s[kb] = mfma32x32x16(kf[st], qf[st], s[kb]);
+    }
   }
   // keep iff keep_lo < key_off <= keep_hi (distance window, causality, length)
   if (masked) {
@@ -186,19 +202,24 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
       pf[u][c + 1] = ph[1];
     }
   }
+  // O^T += V^T P^T, column blocks interleaved in each 16-key step
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    if (db < VPRE) {
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o[db] = mfma32x32x16(vf[db][u], pf[u], o[db]);
-    } else {
+    for (int db = 0; db < VPRE; ++db) o[db] = mfma32x32x16(vf[db][u], pf[u], o[db]);
+  if constexpr (D / 32 > VPRE) {
+    f16x8 vx[D / 32 - VPRE][4];
+#pragma unroll
+    for (int db = VPRE; db < D / 32; ++db) {
       const f16* vb = sv + (32 * db + lr) * VP + 8 * lg;
-      f16x8 vx[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vx[u] = *(const f16x8*)(vb + 16 * u);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) o[db] = mfma32x32x16(vx[u], pf[u], o[db]);
+      for (int u = 0; u < 4; ++u) vx[db - VPRE][u] = *(const f16x8*)(vb + 16 * u);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = VPRE; db < D / 32; ++db)
+        o[db] = mfma32x32x16(vx[db - VPRE][u], pf[u], o[db]);
   }
 }
 
