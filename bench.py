@@ -108,48 +108,97 @@ def make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed):
     return inp, dict(h=h, W=W, Wk=Wk, Wv=Wv, out=out, o=o, ws=ws)
 
 
-def prefill_step(dar, s, H, d_k, w, ev=None):
+def prefill_step(dar, s, H, d_k, w):
     W = s["W"]
-    if ev is not None:
-        ev[0].record()
     dar.dar_project(s["h"], W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
                     W_upK=s["Wk"], W_upV=s["Wv"], out=s["out"], workspace=s["ws"])
-    if ev is not None:
-        ev[1].record()
     out = s["out"]
     dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"], out["V_glob"], w,
                          o=s["o"])
-    if ev is not None:
-        ev[2].record()
+
+
+def capture(torch, fn, copies=1):
+    """HIP graph of `copies` back-to-back calls of fn (the library never
+    allocates and records no memset, so its launches capture as plain kernel
+    nodes).  One eager call on the capture stream first finishes any lazy
+    set-up."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(copies):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_launch_ms(torch, fn, copies=10, reps=3):
+    """Average duration of one call of fn: a graph of `copies` back-to-back
+    calls, replayed `reps` times between HIP events on the launch stream."""
+    g = capture(torch, fn, copies)
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (copies * reps)
+    del g
+    return ms
 
 
 def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
+    """Whole step as one HIP graph (two library calls, four kernels), replayed:
+    W untimed replays, then K timed ones between synchronizations.  Returns
+    (ms per step by the wall clock, by HIP events, dar_project ms, dar_attn_prefill ms)."""
+    step = lambda: prefill_step(dar, s, H, d_k, w)
+    g = capture(torch, step)
     for _ in range(warmup):
-        prefill_step(dar, s, H, d_k, w)
+        g.replay()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        prefill_step(dar, s, H, d_k, w, evs[i])
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    proj_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    return wall / steps * 1e3, proj_ms, attn_ms
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ev = e0.elapsed_time(e1) / steps
+    del g
+    W = s["W"]
+    out = s["out"]
+    proj = lambda: dar.dar_project(s["h"], W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"],
+                                   H, d_k, W_upK=s["Wk"], W_upV=s["Wv"], out=out,
+                                   workspace=s["ws"])
+    attn = lambda: dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"],
+                                        out["V_glob"], w, o=s["o"])
+    return wall, ev, graph_launch_ms(torch, proj), graph_launch_ms(torch, attn)
 
 
-def cpu_baseline(oracle, inp, H, d_k, w, d_down):
-    """The fp64 oracle on one sequence of the same workload (all heads)."""
-    one = {k: (v[:1] if k == "h" else v) for k, v in inp.items()}
-    B1, N, d = one["h"].shape
-    t0 = time.perf_counter()
-    oracle.prefill(one, H, d_k, w)
-    dt = time.perf_counter() - t0
-    proj, attn = prefill_flops(1, N, d, d_down)
-    return {"value": (proj + attn) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle", "seconds": dt,
-            "sample": "one of the 8 sequences (N %d, all %d heads), projections + attention, "
-                      "fp64, same algorithmic FLOP count as the GPU metric" % (N, H)}
+def cpu_baseline(oracle, inp, H, d_k, w, d_down, budget_s=10.0):
+    """The fp64 oracle on the step's own input (all sequences, all heads),
+    repeated until about budget_s seconds of host time have passed."""
+    B, N, d = inp["h"].shape
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(inp, H, d_k, w)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            break
+    proj, attn = prefill_flops(B, N, d, d_down)
+    return {"value": reps * (proj + attn) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle", "seconds": dt,
+            "sample": "the whole step (%d sequences of N %d, %d heads, projections + "
+                      "attention) in fp64, %d times; same algorithmic FLOP count as the GPU "
+                      "metric" % (B, N, H, reps)}
 
 
 def time_decode(torch, dar, di, steps, warmup, cfg):
@@ -168,18 +217,21 @@ def time_decode(torch, dar, di, steps, warmup, cfg):
     ws = torch.empty(dar.decode_workspace_bytes(B, ctx, ctx, H, d_k, d_down, w),
                      dtype=torch.uint8, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # > Infinity Cache
+    g = capture(torch, lambda: dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o,
+                                                   workspace=ws))
     for _ in range(warmup):
-        dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o, workspace=ws)
+        g.replay()
     torch.cuda.synchronize()
     times = []
     for _ in range(steps):
         flush.zero_()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o, workspace=ws)
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
+    del g
     ms = float(np.median(times))
     byts, flops = decode_work(B, ctx, d, d_down, w, H)
     return {"workload": "decode B%d ctx%d d%d H%d dk%d w%d d_down%d" % (B, ctx, d, H, d_k, w, d_down),
@@ -229,12 +281,14 @@ def main():
     if args.only in ("all", "prefill"):
         log("prefill: building inputs")
         inp, s = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=2000 + d_down)
-        ms, proj_ms, attn_ms = time_prefill(torch, dar, s, H, d_k, w, args.steps, args.warmup)
+        ms, ev_ms, proj_ms, attn_ms = time_prefill(torch, dar, s, H, d_k, w, args.steps,
+                                                   args.warmup)
         proj_f, attn_f = prefill_flops(B, N, d, d_down)
         tflops = (proj_f + attn_f) / ms / 1e9
         log("prefill: %.3f ms/step, %.1f TFLOP/s (proj %.3f ms, attn %.3f ms)"
             % (ms, tflops, proj_ms, attn_ms))
         res.update(value=tflops, ms_per_step=ms)
+        res["gpu_ms_per_step"] = ev_ms
         res["config"] = {"workload": "pythia70m-layer prefill B%d N%d d%d H%d dk%d w%d d_down%d"
                          % (B, N, d, H, d_k, w, d_down), "global_batch": B, "seq_len": N,
                          "parallelism": "none (1 GPU)"}
@@ -242,8 +296,8 @@ def main():
         res["kernels"] = {"dar_project_ms": proj_ms, "dar_project_TFLOP/s": proj_f / proj_ms / 1e9,
                           "dar_attn_prefill_ms": attn_ms,
                           "dar_attn_prefill_TFLOP/s": attn_f / attn_ms / 1e9}
-        # The fused attention kernel is the only launch of dar_attn_prefill, so
-        # the events around that call time exactly one kernel.
+        # The fused attention kernel is the only launch of dar_attn_prefill:
+        # events around a graph of back-to-back calls time that kernel.
         achieved = attn_f / attn_ms / 1e9
         res["roofline"] = {"kernel": "attn_prefill_f16<64>", "bound": "mfma",
                            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -260,7 +314,8 @@ def main():
             sweep = {}
             for dd in (256, 64):
                 _, s2 = make_prefill(torch, dar, di, B, N, d, H, d_k, dd, seed=2000 + dd)
-                ms2, p2, a2 = time_prefill(torch, dar, s2, H, d_k, w, args.steps, args.warmup)
+                ms2, _, p2, a2 = time_prefill(torch, dar, s2, H, d_k, w, args.steps,
+                                              args.warmup)
                 pf, af = prefill_flops(B, N, d, dd)
                 sweep["d_down%d" % dd] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9}
                 del s2
@@ -270,8 +325,8 @@ def main():
                                (4, 8192, 2048, 16, 128, 512, 512))):
                 b_, n_, d_, h_, k_, w_, dd_ = cfg
                 _, s3 = make_prefill(torch, dar, di, b_, n_, d_, h_, k_, dd_, seed=3000)
-                ms3, p3, a3 = time_prefill(torch, dar, s3, h_, k_, w_, max(3, args.steps // 4),
-                                           2)
+                ms3, _, p3, a3 = time_prefill(torch, dar, s3, h_, k_, w_,
+                                              max(3, args.steps // 4), 2)
                 pf, af = prefill_flops(b_, n_, d_, dd_)
                 sweep[name] = {"ms": ms3, "TFLOP/s": (pf + af) / ms3 / 1e9,
                                "proj_ms": p3, "attn_ms": a3,

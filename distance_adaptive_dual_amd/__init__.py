@@ -101,11 +101,30 @@ def _check(fn: str, status: int):
         raise DarError(fn, status)
 
 
+def _call_ws(fn: str, f, args, workspace, like, stream):
+    """Calls entry point f with a workspace.  A caller-supplied workspace is
+    tried first; when none is given (or it is too small) the size is queried
+    and a fresh buffer allocated."""
+    if workspace is not None:
+        n = ctypes.c_size_t(workspace.numel())
+        st = f(*args, _ptr(workspace), ctypes.byref(n), _stream(stream))
+        if st != 3:  # DAR_ERR_WORKSPACE
+            _check(fn, st)
+            return
+    n = ctypes.c_size_t(0)
+    _check(fn, f(*args, None, ctypes.byref(n), None))
+    workspace = _workspace(n.value, like)
+    n = ctypes.c_size_t(n.value)
+    _check(fn, f(*args, _ptr(workspace), ctypes.byref(n), _stream(stream)))
+
+
+def torch_uint8():
+    return _torch().uint8
+
+
 def _workspace(nbytes: int, like):
-    torch = _torch()
-    if nbytes == 0:
-        return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    # never NULL: a NULL workspace asks the library for its size instead
+    return _torch().empty(max(nbytes, 256), dtype=torch_uint8(), device=like.device)
 
 
 def dar_fold(W_up, W_K, W_V, heads: int, d_k: int, W_upK=None, W_upV=None, stream=None):
@@ -159,19 +178,10 @@ def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None
                    h_D=torch.empty((B, N, d_down), **kw),
                    K_glob=torch.empty((B, heads, N, d_k), **kw),
                    V_glob=torch.empty((B, heads, d_k, N), **kw))
-    L = lib()
-    n = ctypes.c_size_t(0)
-    args_in = [_ptr(h), _ptr(W_down), _ptr(W_up), _ptr(W_Q), _ptr(W_K), _ptr(W_V),
-               _ptr(W_upK), _ptr(W_upV), B, N, d, d_down, heads, d_k, pos0,
-               float(rope_base), dt]
-    outs = [_ptr(out[k]) for k in ("Q", "K_loc", "V_loc", "h_D", "K_glob", "V_glob")]
-    st = L.dar_project(*args_in, *outs, None, ctypes.byref(n), None)
-    _check("dar_project", st)
-    if workspace is None or workspace.numel() < n.value:
-        workspace = _workspace(n.value, h)
-    n = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
-    st = L.dar_project(*args_in, *outs, _ptr(workspace), ctypes.byref(n), _stream(stream))
-    _check("dar_project", st)
+    args = [_ptr(h), _ptr(W_down), _ptr(W_up), _ptr(W_Q), _ptr(W_K), _ptr(W_V),
+            _ptr(W_upK), _ptr(W_upV), B, N, d, d_down, heads, d_k, pos0, float(rope_base), dt]
+    args += [_ptr(out[k]) for k in ("Q", "K_loc", "V_loc", "h_D", "K_glob", "V_glob")]
+    _call_ws("dar_project", lib().dar_project, args, workspace, h, stream)
     return out
 
 
@@ -198,18 +208,10 @@ def dar_decode_append(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos: int, 
     d_down = W_down.shape[0]
     w = K_win.shape[2] if K_win is not None else 0
     cap = h_D.shape[1]
-    L = lib()
-    n = ctypes.c_size_t(0)
     args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), B, d, d_down, heads, d_k,
             int(pos), int(w), cap, float(rope_base), _dtype_code(h), _ptr(q),
             _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D)]
-    st = L.dar_decode_append(*args, None, ctypes.byref(n), None)
-    _check("dar_decode_append", st)
-    if workspace is None or workspace.numel() < n.value:
-        workspace = _workspace(n.value, h)
-    n = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
-    st = L.dar_decode_append(*args, _ptr(workspace), ctypes.byref(n), _stream(stream))
-    _check("dar_decode_append", st)
+    _call_ws("dar_decode_append", lib().dar_decode_append, args, workspace, h, stream)
     return q
 
 
@@ -230,16 +232,8 @@ def dar_attn_decode(q, K_win, V_win, h_D, W_upK, W_upV, ctx_len: int, w: int,
     cap, d_down = h_D.shape[1], h_D.shape[2]
     if o is None:
         o = torch.empty((B, H * d_k), dtype=q.dtype, device=q.device)
-    L = lib()
-    n = ctypes.c_size_t(0)
-    head = [_ptr(q), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D),
+    args = [_ptr(q), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D),
             _ptr(W_upK), _ptr(W_upV), B, int(ctx_len), cap, H, d_k, d_down, int(w),
             float(rope_base), _dtype_code(q), _ptr(o)]
-    st = L.dar_attn_decode(*head, None, ctypes.byref(n), None)
-    _check("dar_attn_decode", st)
-    if workspace is None or workspace.numel() < n.value:
-        workspace = _workspace(n.value, q)
-    n = ctypes.c_size_t(workspace.numel() if workspace is not None else 0)
-    st = L.dar_attn_decode(*head, _ptr(workspace), ctypes.byref(n), _stream(stream))
-    _check("dar_attn_decode", st)
+    _call_ws("dar_attn_decode", lib().dar_attn_decode, args, workspace, q, stream)
     return o

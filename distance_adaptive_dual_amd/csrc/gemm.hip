@@ -11,9 +11,11 @@
 // tensor and layout; the epilogue applies RoPE and scatters into the
 // head-major layouts the attention kernels read.
 //
-// bf16 mode: 128x128x64 tiles, 4 waves of 64x64 built from 32x32x16 MFMAs,
-// double-buffered LDS, fp32 accumulate, epilogue staged through LDS so the
-// rotate-half partners (t, t + d_k/2) meet in one thread and stores coalesce.
+// bf16 mode: workgroup tiles of 256 tokens x 128 columns, 4 waves of 128x64
+// built from 32x32x16 MFMAs, k-tiles of 32 in a 3-stage LDS ring filled by
+// direct global-to-LDS buffer loads, fp32 accumulate, epilogue staged through
+// LDS so the rotate-half partners (t, t + d_k/2) meet in one thread and stores
+// coalesce.
 // The projections are written as IEEE fp16 (3 more mantissa bits than bf16 at
 // the same size and MFMA rate); the second GEMM therefore runs on fp16 MFMAs,
 // converting the bf16 folded weights to fp16 as they are staged into LDS.

@@ -1,0 +1,95 @@
+"""The library's calls captured into a HIP graph (torch.cuda.CUDAGraph) give,
+on every replay, exactly the bytes of the eager calls.  Replays are separated
+by eager work of the program (other library calls into other buffers, torch
+ops) and synchronizations, and each replay's output is checked."""
+import pytest
+import torch
+
+import dar_inputs as di
+import distance_adaptive_dual_amd as dar
+from gpu_helpers import dev, dev_w, log, prefill_case
+
+pytestmark = pytest.mark.gpu
+
+
+def capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_prefill_graph_replays_match_eager():
+    B, N, d, H, d_k, dd, w = 2, 700, 256, 4, 64, 64, 100
+    inp = prefill_case(B, N, d, H, d_k, dd, "bf16", seed=31)
+    W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    h = dev(inp["h"], "bf16")
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    ws = torch.empty(dar.project_workspace_bytes(B, N, d, dd, H, d_k), dtype=torch.uint8,
+                     device="cuda")
+    out = dar.dar_project(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                          W_upK=Wk, W_upV=Wv, workspace=ws)
+    o = dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"], out["V_glob"], w)
+    torch.cuda.synchronize()
+    ref_o = o.clone()
+    ref_out = {k: v.clone() for k, v in out.items()}
+
+    def step():
+        dar.dar_project(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                        W_upK=Wk, W_upV=Wv, out=out, workspace=ws)
+        dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"], out["V_glob"],
+                             w, o=o)
+
+    g = capture(step)
+    other = dev(di.prefill_inputs(B, N, d, H, d_k, dd, seed0=77)["h"], "bf16")
+    for rep in range(4):
+        o.zero_()
+        for v in out.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log("prefill graph replay %d" % rep)
+        assert torch.equal(o, ref_o)
+        for k in ref_out:
+            assert torch.equal(out[k], ref_out[k]), k
+        # eager work between replays: the same library calls on another input
+        p2 = dar.dar_project(other, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                             W_upK=Wk, W_upV=Wv)
+        o2 = dar.dar_attn_prefill(p2["Q"], p2["K_loc"], p2["V_loc"], p2["K_glob"], p2["V_glob"], w)
+        torch.cuda.synchronize()
+        assert not torch.equal(o2, ref_o)
+        del o2, p2
+
+
+def test_decode_graph_replays_match_eager():
+    B, ctx, d, H, d_k, dd, w = 2, 3000, 512, 4, 128, 128, 256
+    inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=88)
+    W_up, W_K, W_V = (dev_w(inp[k], "bf16") for k in ("W_up", "W_K", "W_V"))
+    Wk, Wv = dar.dar_fold(W_up, W_K, W_V, H, d_k)
+    q, K_win, V_win, h_D = (dev(inp[k], "bf16") for k in ("q", "K_win", "V_win", "h_D"))
+    ws = torch.empty(dar.decode_workspace_bytes(B, ctx, ctx, H, d_k, dd, w), dtype=torch.uint8,
+                     device="cuda")
+    o = dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, workspace=ws)
+    torch.cuda.synchronize()
+    ref = o.clone()
+    g = capture(lambda: dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o,
+                                            workspace=ws))
+    for rep in range(4):
+        o.zero_()
+        ws.fill_(0x7F)  # the partials must be rewritten by every replay
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log("decode graph replay %d" % rep)
+        assert torch.equal(o, ref)
+        o2 = dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx - 7, w)
+        torch.cuda.synchronize()
+        assert not torch.equal(o2, ref)
