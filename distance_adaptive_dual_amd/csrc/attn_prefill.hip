@@ -107,47 +107,43 @@ __device__ __forceinline__ void store_pass(const Stage<D>& st, f16* sk, f16* sv)
   }
 }
 
-// One pass of one wave: scores against the staged tile, the Eq. (3) keep mask,
-// online softmax, and O^T += V^T P^T.
+// K fragments of a staged key tile for S^T = K Q^T: kf[kb][st] holds rows
+// 32 kb + key_perm(lr) (keys j0 + ...) and dims 16 st + 8 lg .. +8.
 template <int D>
-__device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f16x8 (&qf)[D / 16],
-                                          f32x16 (&o)[D / 32], float& m_ref, float& l_run,
-                                          bool masked, int keep_lo, int keep_hi, float sc,
-                                          int lr, int lg) {
-  constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
-  // S^T = K Q^T: s[kb][r] is key j0 + 8 lg + key_off(kb, r) of this lane's query.
-  // The K fragments are read before the MFMAs; for d_k = 64 the two 32-key
-  // blocks' accumulation chains are interleaved so that no MFMA waits on the
-  // result of the one just issued.
-  f32x16 s[2];
+__device__ __forceinline__ void read_kfrags(const f16* sk, f16x8 (&kf)[2][D / 16], int lr, int lg) {
+  constexpr int KP = PassSmem<D>::KP;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) kf[kb][st] = *(const f16x8*)(base + 16 * st);
+  }
+}
+
+// S^T = K Q^T: s[kb][r] is key j0 + 8 lg + key_off(kb, r) of this lane's
+// query.  The two 32-key blocks' accumulation chains are interleaved so that
+// no MFMA waits on the result of the one just issued.
+template <int D>
+__device__ __forceinline__ void mfma_scores(const f16x8 (&kf)[2][D / 16], const f16x8 (&qf)[D / 16],
+                                            f32x16 (&s)[2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-  if constexpr (D == 64) {
-    f16x8 kf[2][D / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
+  for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) kf[kb][st] = *(const f16x8*)(base + 16 * st);
-    }
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][st], qf[st], s[kb]);
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
-      f16x8 kf[D / 16];
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) s[kb] = mfma32x32x16(kf[st], qf[st], s[kb]);
-    }
-  }
-  // keep iff keep_lo < key_off <= keep_hi (distance window, causality, length)
+    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][st], qf[st], s[kb]);
+}
+
+// Keep mask of Eq. (3) and causality, then the running reference maximum:
+// keep iff keep_lo < key_off <= keep_hi.  Softmax is invariant to the
+// reference maximum, so it is only moved (and O, l rescaled) when some row's
+// maximum exceeds it by more than 2^kTau.
+template <int D>
+__device__ __forceinline__ void mask_and_max(f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m_ref,
+                                             float& l_run, bool masked, int keep_lo, int keep_hi,
+                                             float sc) {
   if (masked) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -162,9 +158,10 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32)) * sc;
-  // Softmax is invariant to the reference maximum, so it is only moved (and O,
-  // l rescaled) when some row's maximum exceeds it by more than 2^kTau.
+  // the two lane halves hold the two halves of the query's keys
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                   false, false);
+  mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
   if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
     const float m_new = fmaxf(m_ref, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -175,9 +172,18 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   }
-  // V^T fragments of the first column blocks are requested now and arrive
-  // while the softmax below runs.
-  constexpr int VPRE = (D == 64) ? 2 : 2;  // column blocks of 32 preloaded
+}
+
+// p = 2^(s*sc - m_ref) rounded to fp16 (the P operand), l += the same fp16
+// p, and O^T += V^T P^T with the column blocks interleaved per 16-key step.
+template <int D>
+__device__ __forceinline__ void exp_and_pv(const f16* sv, const f32x16 (&s)[2],
+                                           f32x16 (&o)[D / 32], float m_ref, float& l_run,
+                                           float sc, int lr, int lg) {
+  constexpr int VP = PassSmem<D>::VP;
+  // V^T fragments of the first column blocks are requested first and arrive
+  // while the exponentials run.
+  constexpr int VPRE = 2;  // column blocks of 32 preloaded
   f16x8 vf[VPRE][4];
 #pragma unroll
   for (int db = 0; db < VPRE; ++db) {
@@ -185,7 +191,6 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
 #pragma unroll
     for (int u = 0; u < 4; ++u) vf[db][u] = *(const f16x8*)(vb + 16 * u);
   }
-  // p = 2^(s*sc - m_ref), rounded to fp16 for the MFMA; l sums the same fp16 p
   f16x8 pf[4];
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const h2 one2 = {(f16)1.f, (f16)1.f};
@@ -202,7 +207,6 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
       pf[u][c + 1] = ph[1];
     }
   }
-  // O^T += V^T P^T, column blocks interleaved in each 16-key step
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -221,6 +225,45 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
       for (int db = VPRE; db < D / 32; ++db)
         o[db] = mfma32x32x16(vx[db - VPRE][u], pf[u], o[db]);
   }
+}
+
+// One whole pass of one wave: scores against the staged tile, the keep mask,
+// online softmax, and O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f16x8 (&qf)[D / 16],
+                                          f32x16 (&o)[D / 32], float& m_ref, float& l_run,
+                                          bool masked, int keep_lo, int keep_hi, float sc,
+                                          int lr, int lg) {
+  f16x8 kf[2][D / 16];
+  read_kfrags<D>(sk, kf, lr, lg);
+  f32x16 s[2];
+  mfma_scores<D>(kf, qf, s);
+  mask_and_max<D>(s, o, m_ref, l_run, masked, keep_lo, keep_hi, sc);
+  exp_and_pv<D>(sv, s, o, m_ref, l_run, sc, lr, lg);
+}
+
+// What one wave does with one pass (a key tile of one source): whether it has
+// any kept pair there, whether the keep mask is needed, and the mask bounds
+// relative to the lane's first key j0 + 8 lg.
+struct WavePass {
+  bool part, masked;
+  int keep_lo, keep_hi;
+};
+
+__device__ __forceinline__ WavePass wave_pass_info(int j0, int src, int qw0, int wi_last, int qi,
+                                                   int lg, int N, int w) {
+  WavePass r{false, false, 0, 0};
+  const int wdmax = wi_last - j0, wdmin = qw0 - (j0 + KT - 1);
+  if (qw0 < N && wdmax >= 0) {
+    const bool glob = src == 0;
+    r.part = glob ? (wdmax >= w) : (w > 0 && max(wdmin, 0) < w);
+    r.masked = (glob ? (wdmin < w) : (wdmin < 0 || wdmax >= w)) || (j0 + KT > N);
+    const int base = qi - j0 - 8 * lg;  // distance of key offset 0
+    const int lo = glob ? w : 0;
+    r.keep_lo = glob ? -1 : base - w;
+    r.keep_hi = min(base - lo, N - 1 - j0 - 8 * lg);
+  }
+  return r;
 }
 
 template <int D>
@@ -306,23 +349,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int
       if (has_next)
         load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
 
-      const int wdmax = wi_last - j0, wdmin = qw0 - (j0 + KT - 1);
-      if (qw0 < N && wdmax >= 0) {
-        // keep pairs with distance in [lo, hi) for this source, j <= i, j < N
-        const bool glob = src == 0;
-        const bool part = glob ? (wdmax >= w) : (w > 0 && max(wdmin, 0) < w);
-        if (part) {
-          const bool masked =
-              (glob ? (wdmin < w) : (wdmin < 0 || wdmax >= w)) || (j0 + KT > N);
-          const int base = qi - j0 - 8 * lg;  // distance of key offset 0
-          const int lo = glob ? w : 0;
-          // keep iff base - hi < off <= min(base - lo, N - 1 - j0 - 8 lg)
-          const int keep_lo = glob ? -1 : base - w;
-          const int keep_hi = min(base - lo, N - 1 - j0 - 8 * lg);
-          wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, masked, keep_lo, keep_hi, sc,
-                       lr, lg);
-        }
-      }
+      const WavePass wp = wave_pass_info(j0, src, qw0, wi_last, qi, lg, N, w);
+      if (wp.part)
+        wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo, wp.keep_hi,
+                     sc, lr, lg);
       if (!has_next) break;
       store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
       __syncthreads();

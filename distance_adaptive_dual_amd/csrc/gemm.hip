@@ -171,6 +171,167 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
 }
 
 // --------------------------------------------------------------------------
+// Stores of the MFMA GEMM epilogue.  One epilogue pass holds 128 tokens of the
+// workgroup tile in LDS: tile row r is GEMM row epi_row(row0, hf, r) (the two
+// 64-token runs starting at 64 hf and 128 + 64 hf).  Work is cut into 16-byte
+// output chunks (8 values) so that eight consecutive lanes write 128
+// contiguous bytes, and the lane order keeps the LDS reads conflict-free.
+__device__ __forceinline__ int epi_row(int row0, int hf, int r) {
+  return row0 + 128 * (r >> 6) + 64 * hf + (r & 63);
+}
+
+__device__ __forceinline__ void read8(const float* src, float (&v)[8]) {
+  const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// cos/sin(pos * theta_t) for t = t0 .. t0+7 from the two-level tables.
+__device__ __forceinline__ void rope_cs8(const RopeTab& t, int pos, int t0, float2 (&cs)[8]) {
+  const float4* hi = (const float4*)(t.hi + (size_t)(pos >> 6) * t.half + t0);
+  const float4* lo = (const float4*)(t.lo + (size_t)(pos & 63) * t.half + t0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 a = hi[i], b = lo[i];
+    cs[2 * i] = make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+    cs[2 * i + 1] = make_float2(a.z * b.z - a.w * b.w, a.z * b.w + a.w * b.z);
+  }
+}
+
+// Tile [128 tokens][EPI_P] -> kRowMajor, or kHead without rotation.
+template <typename OutT, int D>
+__device__ __forceinline__ void store_rows_plain(const float* tile, int row0, int hf, int col0,
+                                                 const GemmSeg& seg, const GemmProblem& p) {
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int ld = seg.ld_seq ? seg.ld_seq : Nq;
+  OutT* out = (OutT*)seg.out;
+  // chunk q = tid + 256 k: column chunk (q & 7) + 8 (q >> 10), tile row (q >> 3) & 127;
+  // chunks k and k + 4 share the row
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = ((tid >> 3) + 32 * k) & 127;
+    const int grow = epi_row(row0, hf, r);
+    if (grow >= M) continue;
+    const int b = grow / Nq, no = grow % Nq + seg.seq_off;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int c = 8 * ((tid & 7) + 8 * h2);
+      const int gcol = col0 + c;  // width is a multiple of 32: chunks are whole
+      if (gcol >= width) continue;
+      float v[8];
+      read8(tile + r * EPI_P + c, v);
+      OutT* dst;
+      if (seg.kind == kRowMajor) {
+        dst = out + ((size_t)b * ld + no) * width + gcol;
+      } else {
+        const int head = gcol / D, t = gcol % D;
+        dst = out + (((size_t)b * H + head) * ld + no) * D + t;
+      }
+      store_run<OutT, 8>(dst, v);
+    }
+  }
+}
+
+// Tile [128 tokens][EPI_P] -> kHead with RoPE at position pos0 + n on the
+// rotate-half pairs (t, t + D/2).  A lane takes 8 consecutive pairs of one head
+// for 4 consecutive tokens: the angles of the first token come from the
+// tables, the next ones by one complex multiplication with (cos, sin)(theta_t)
+// each (the table row for position 1).
+template <typename OutT, int D>
+__device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int hf, int col0,
+                                                const GemmSeg& seg, const GemmProblem& p) {
+  constexpr int HALF = D / 2, PCH = D / 16;  // pair chunks of 8 per head
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int ld = seg.ld_seq ? seg.ld_seq : Nq;
+  OutT* out = (OutT*)seg.out;
+  const int w8 = tid & 7, r0 = 4 * (tid >> 3);
+  const int hl = w8 / PCH, t0 = 8 * (w8 % PCH);
+  const int c = hl * D + t0;  // tile column of x; y sits HALF further
+  const int gcol = col0 + hl * D;
+  const int grow0 = epi_row(row0, hf, r0);
+  if (gcol >= width || grow0 >= M) return;
+  const int head = gcol / D;
+  const int b0 = grow0 / Nq, n0 = grow0 % Nq;
+  const bool consec = grow0 + 3 < M && n0 + 3 < Nq;  // one sequence, consecutive positions
+  float2 cs[8], step[8];
+  rope_cs8(p.rope, p.pos0 + n0, t0, cs);
+  if (consec) {
+    const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = st[i];
+      step[2 * i] = make_float2(a.x, a.y);
+      step[2 * i + 1] = make_float2(a.z, a.w);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    int b = b0, n = n0 + kk;
+    if (kk > 0) {
+      if (consec) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          cs[i] = make_float2(cs[i].x * step[i].x - cs[i].y * step[i].y,
+                              cs[i].x * step[i].y + cs[i].y * step[i].x);
+      } else {
+        const int grow = grow0 + kk;
+        if (grow >= M) break;
+        b = grow / Nq;
+        n = grow % Nq;
+        rope_cs8(p.rope, p.pos0 + n, t0, cs);
+      }
+    }
+    float x[8], y[8], a[8], bb[8];
+    read8(tile + (r0 + kk) * EPI_P + c, x);
+    read8(tile + (r0 + kk) * EPI_P + c + HALF, y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = x[i] * cs[i].x - y[i] * cs[i].y;
+      bb[i] = x[i] * cs[i].y + y[i] * cs[i].x;
+    }
+    OutT* dst = out + (((size_t)b * H + head) * ld + n + seg.seq_off) * D + t0;
+    store_run<OutT, 8>(dst, a);
+    store_run<OutT, 8>(dst + HALF, bb);
+  }
+}
+
+// Tile [128 columns][TP] (token innermost) -> kHeadT, out[b, head, t, n].
+template <typename OutT, int D, int TP>
+__device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, int col0,
+                                           const GemmSeg& seg, const GemmProblem& p) {
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  OutT* out = (OutT*)seg.out;
+  const int tc = tid & 7;  // chunk of 8 tokens within the 64-token run
+#pragma unroll
+  for (int run = 0; run < 2; ++run) {
+    const int grow0 = row0 + 128 * run + 64 * hf + 8 * tc;
+    if (grow0 >= M) continue;
+    const int b0 = grow0 / Nq, n0 = grow0 % Nq;
+    const bool fast = (grow0 + 8 <= M) && (n0 + 8 <= Nq) && ((n0 & 7) == 0) && ((Nq & 7) == 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = (tid >> 3) + 32 * k;
+      const int gcol = col0 + c;
+      if (gcol >= width) continue;
+      const int head = gcol / D, t = gcol % D;
+      float v[8];
+      read8(tile + c * TP + 64 * run + 8 * tc, v);
+      if (fast) {
+        store_run<OutT, 8>(out + (((size_t)b0 * H + head) * D + t) * Nq + n0, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int grow = grow0 + i;
+          if (grow >= M) break;
+          const int b = grow / Nq, n = grow % Nq;
+          out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<OutT>(v[i]);
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // MFMA GEMM: A and the MFMA operands of type TM (bf16 or fp16), B stored as TB
 // (converted to TM while staged), outputs of type TO.
 //
@@ -317,8 +478,6 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   // Register r of acc[i][j] is column 32*cb_i + 8*(r/4) + 4*lg + r%4, token
   // 128*wt + 32*j + lr of the workgroup tile.
   float* tile = (float*)smem;
-  const int H = p.heads, Nq = p.n_seq, width = seg.width;
-  TO* out = (TO*)seg.out;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     __syncthreads();  // LDS free (main loop, or the previous pass's stores)
@@ -347,43 +506,12 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
       }
     }
     __syncthreads();
-    if (seg.kind != kHeadT) {
-#pragma unroll
-      for (int run = 0; run < 2; ++run) {
-        const int grow0 = row0 + 128 * run + 64 * hf;
-        if (grow0 < M) epilogue_store<TO, D, 64>(tile + 64 * run * EPI_P, grow0, col0, seg, p);
-      }
-      continue;
-    }
-    // out[b, head, t, n]: thread = (column, run of 64 tokens)
-    constexpr int TP = BM + 4;
-    const int c = tid % BN, run = tid / BN;
-    const int gcol = col0 + c;
-    const int grow0 = row0 + 128 * run + 64 * hf;
-    if (gcol >= width || grow0 >= M) continue;
-    const int head = gcol / D, t = gcol % D;
-    const int b0 = grow0 / Nq, n0 = grow0 % Nq;
-    float v[64];
-#pragma unroll
-    for (int i = 0; i < 64; i += 4) {
-      const float4 q4 = *(const float4*)(tile + c * TP + 64 * run + i);
-      v[i] = q4.x;
-      v[i + 1] = q4.y;
-      v[i + 2] = q4.z;
-      v[i + 3] = q4.w;
-    }
-    const bool fast = (grow0 + 64 <= M) && (n0 + 64 <= Nq) && ((n0 & 7) == 0) && ((Nq & 7) == 0);
-    if (fast) {
-      store_run<TO, 64>(out + (((size_t)b0 * H + head) * D + t) * Nq + n0, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const int grow = grow0 + i;
-        if (grow >= M) break;
-        const int b = grow / Nq, n = grow % Nq;
-        out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<TO>(v[i]);
-      }
-    }
+    if (seg.kind == kHeadT)
+      store_cols<TO, D, BM + 4>(tile, row0, hf, col0, seg, p);
+    else if (seg.kind == kHead && seg.rope)
+      store_rows_rope<TO, D>(tile, row0, hf, col0, seg, p);
+    else
+      store_rows_plain<TO, D>(tile, row0, hf, col0, seg, p);
   }
 }
 
