@@ -154,24 +154,25 @@ def graph_launch_ms(torch, fn, copies=10, reps=3):
 
 
 def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
-    """Whole step as one HIP graph (two library calls, four kernels), replayed:
-    W untimed replays, then K timed ones between synchronizations.  Returns
+    """The K timed steps (two library calls, four kernels each) are captured as
+    one HIP graph, as a model's forward pass would hold its layers, and
+    replayed once between synchronizations after W untimed steps.  Returns
     (ms per step by the wall clock, by HIP events, dar_project ms, dar_attn_prefill ms)."""
     step = lambda: prefill_step(dar, s, H, d_k, w)
-    g = capture(torch, step)
-    for _ in range(warmup):
-        g.replay()
+    warm = capture(torch, step, max(warmup, 1))
+    timed = capture(torch, step, steps)
+    if warmup > 0:
+        warm.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(steps):
-        g.replay()
+    timed.replay()
     e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e3
     ev = e0.elapsed_time(e1) / steps
-    del g
+    del warm, timed
     W = s["W"]
     out = s["out"]
     proj = lambda: dar.dar_project(s["h"], W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"],

@@ -10,7 +10,7 @@
  * the 1/sqrt(d_k) scale.  Multi-head attention replicates the single-head
  * construction (same section of the paper, the paragraph after Eq. (1)).
  *
- * Readings taken where the paper is silent (each is listed in the design doc):
+ * Readings taken where the paper is silent:
  *  - RoPE rotates both q_i (position i) and k_j (position j); rotate-half
  *    pairing (t, t + d_k/2) over the full head width, theta_t =
  *    base^(-2t/d_k), positions p = pos0 + n counted from 0.
