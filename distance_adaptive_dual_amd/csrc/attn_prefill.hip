@@ -93,6 +93,68 @@ __device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16*
   }
 }
 
+// The two halves of load_pass / store_pass, for staging K and V at different
+// times of a pass.
+template <int D>
+__device__ __forceinline__ void load_k(u32x4 (&k)[Stage<D>::NCH], const f16* K, int N, int j0) {
+  const int tid = threadIdx.x;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    k[i] = (j0 + row < N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(u32x4 (&v)[Stage<D>::NCH], const f16* Vt, int N, int j0,
+                                       bool vec_ok) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int c = tid + 256 * i;
+    const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
+    if (vec_ok) {
+      v[i] = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
+    } else {  // ragged tail, or N not a multiple of 8
+      const uint16_t* src = (const uint16_t*)Vt + (size_t)d * N;
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ja = j0 + kc + 2 * e, jb = ja + 1;
+        const uint32_t a = ja < N ? src[ja] : 0u, b = jb < N ? src[jb] : 0u;
+        w4[e] = a | (b << 16);
+      }
+      v[i] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const u32x4 (&k)[Stage<D>::NCH], f16* sk) {
+  constexpr int KP = PassSmem<D>::KP;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int c = tid + 256 * i;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    *(u32x4*)(sk + row * KP + col) = k[i];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(const u32x4 (&v)[Stage<D>::NCH], f16* sv) {
+  constexpr int VP = PassSmem<D>::VP;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int c = tid + 256 * i;
+    const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
+    *(u32x4*)(sv + d * VP + kc) = v[i];
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void store_pass(const Stage<D>& st, f16* sk, f16* sv) {
   constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
@@ -242,6 +304,83 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
   exp_and_pv<D>(sv, s, o, m_ref, l_run, sc, lr, lg);
 }
 
+// Half kb of a pass (d_k = 64): scores, mask, maximum, exponentials and P.V
+// of keys 32 kb .. 32 kb + 31 of the staged tile.  A pass run as two halves
+// keeps only half the score, K and V fragment registers live at a time, which
+// fits four waves per SIMD; the reference maximum may move between the halves
+// (same rule as a whole pass).
+template <int D>
+__device__ __forceinline__ void wave_half(int kb, const f16* sk, const f16* sv,
+                                          const f16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+                                          float& m_ref, float& l_run, bool masked, int keep_lo,
+                                          int keep_hi, float sc, int lr, int lg) {
+  constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one2 = {(f16)1.f, (f16)1.f};
+  {
+    f16x8 kf[D / 16];
+    {
+      const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
+    }
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) s = mfma32x32x16(kf[st], qf[st], s);
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = key_off(kb, r);
+        if (!(off > keep_lo && off <= keep_hi)) s[r] = -INFINITY;
+      }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                     false, false);
+    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    // V^T fragments of this half's 32 keys (two 16-key steps u)
+    f16x8 vf[D / 32][2];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const f16* vb = sv + (32 * db + lr) * VP + 32 * kb + 8 * lg;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) vf[db][u] = *(const f16x8*)(vb + 16 * u);
+    }
+    f16x8 pf[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int c = 0; c < 8; c += 2) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[8 * u + c], sc, -m_ref));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[8 * u + c + 1], sc, -m_ref));
+        const uint32_t pk = pack_f16x2(e0, e1);
+        const h2 ph = __builtin_bit_cast(h2, pk);
+        l_run = __builtin_amdgcn_fdot2(ph, one2, l_run, false);
+        pf[u][c] = ph[0];
+        pf[u][c + 1] = ph[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] = mfma32x32x16(vf[db][u], pf[u], o[db]);
+  }
+}
+
 // What one wave does with one pass (a key tile of one source): whether it has
 // any kept pair there, whether the keep mask is needed, and the mask bounds
 // relative to the lane's first key j0 + 8 lg.
@@ -267,21 +406,27 @@ __device__ __forceinline__ WavePass wave_pass_info(int j0, int src, int qw0, int
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int nQT, int nPair,
-                                                          int remap) {
+__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(PrefillProblem p, int nQT, int nPair,
+                                                          int remap, int paired) {
   __shared__ PassSmem<D> sm;
   const int N = p.N, H = p.H, BH = p.B * p.H, w = p.w;
-  // Causal balance: a workgroup takes query tile nQT-1-pr and then tile pr,
-  // so every workgroup streams about the same number of key tiles.  With
-  // remap, all tiles of one (batch, head) stay on one XCD so its K/V prefix
-  // is shared through that XCD's L2.
+  // paired: a workgroup takes query tile nQT-1-pr and then tile pr, so every
+  // workgroup streams about the same number of key tiles.  Unpaired: one
+  // tile per workgroup, longest first (nPair = nQT).  With remap, all tiles
+  // of one (batch, head) stay on one XCD so its K/V prefix is shared through
+  // that XCD's L2.
   int pr, bh;
   {
     const int bid = blockIdx.x;
     if (remap) {
-      const int x = bid % kNumXcd, k = bid / kNumXcd;
-      pr = k % nPair;
-      bh = (k / nPair) * kNumXcd + x;
+      const int x = bid % kNumXcd, k = bid / kNumXcd, G = BH / kNumXcd;
+      if (paired) {
+        pr = k % nPair;
+        bh = (k / nPair) * kNumXcd + x;
+      } else {
+        pr = k / G;
+        bh = (k % G) * kNumXcd + x;
+      }
     } else {
       pr = bid / BH;
       bh = bid % BH;
@@ -300,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int
   const float sc = kLog2e / sqrtf((float)D);
   const bool nvec = (N % 8) == 0;
   const int q_hi = nQT - 1 - pr;
-  const int nq = (q_hi == pr) ? 1 : 2;
+  const int nq = (!paired || q_hi == pr) ? 1 : 2;
 
   for (int qn = 0; qn < nq; ++qn) {
     const int qt = qn == 0 ? q_hi : pr;
@@ -346,15 +491,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_f16(PrefillProblem p, int
         nsrc = need_glob(nj0) ? 0 : 1;
       }
       const bool has_next = nj0 < j_end;
-      if (has_next)
-        load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
+      if constexpr (D == 64) {
+        // V of the next pass is fetched now and stored after the first half;
+        // K is fetched then and stored at the end (its LDS buffer is free
+        // for the whole pass), so only one of the two is held in registers.
+        if (has_next) load_v<D>(stg.v, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
+      } else {
+        if (has_next)
+          load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
+      }
 
       const WavePass wp = wave_pass_info(j0, src, qw0, wi_last, qi, lg, N, w);
-      if (wp.part)
-        wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo, wp.keep_hi,
-                     sc, lr, lg);
-      if (!has_next) break;
-      store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
+      if constexpr (D == 64) {
+        if (wp.part)
+          wave_half<D>(0, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
+                       wp.keep_hi, sc, lr, lg);
+        if (has_next) {
+          store_v<D>(stg.v, sm.v[buf ^ 1]);
+          load_k<D>(stg.k, nsrc ? Kl : Kg, N, nj0);
+        }
+        if (wp.part)
+          wave_half<D>(1, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
+                       wp.keep_hi, sc, lr, lg);
+        if (!has_next) break;
+        store_k<D>(stg.k, sm.k[buf ^ 1]);
+      } else {
+        if (wp.part)
+          wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
+                       wp.keep_hi, sc, lr, lg);
+        if (!has_next) break;
+        store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
+      }
       __syncthreads();
       buf ^= 1;
       j0 = nj0;
@@ -458,13 +625,18 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
   const int BH = p.B * p.H;
   if (dt == DAR_BF16) {
     const int nQT = (p.N + QT - 1) / QT;
-    const int nPair = (nQT + 1) / 2;
+    // d_k = 64 fits three waves per SIMD, so one tile per workgroup (longest
+    // first) keeps more of them resident; at d_k = 128 (two per SIMD) pairing
+    // balances the workgroups instead.
+    const int paired = p.d_k == 128 ? 1 : 0;
+    const int nPair = paired ? (nQT + 1) / 2 : nQT;
     const int remap = (BH % kNumXcd) == 0 ? 1 : 0;
     const dim3 grid(nPair * BH);
     if (p.d_k == 64)
-      hipLaunchKernelGGL(attn_prefill_f16<64>, grid, dim3(256), 0, s, p, nQT, nPair, remap);
+      hipLaunchKernelGGL(attn_prefill_f16<64>, grid, dim3(256), 0, s, p, nQT, nPair, remap, paired);
     else
-      hipLaunchKernelGGL(attn_prefill_f16<128>, grid, dim3(256), 0, s, p, nQT, nPair, remap);
+      hipLaunchKernelGGL(attn_prefill_f16<128>, grid, dim3(256), 0, s, p, nQT, nPair, remap,
+                         paired);
   } else {
     const dim3 grid((p.N + FQ - 1) / FQ, p.H, p.B);
     if (p.d_k == 64)
