@@ -304,6 +304,27 @@ __device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f1
   exp_and_pv<D>(sv, s, o, m_ref, l_run, sc, lr, lg);
 }
 
+// p = 2^(s*sc - m) for the 16 scores of a lane, rounded to fp16 (the P
+// operand of two 16-key steps), and their sum in fp32.
+__device__ __forceinline__ void exp_half(const f32x16& s, float sc, float m, f16x8 (&pf)[2],
+                                         float& ls) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one2 = {(f16)1.f, (f16)1.f};
+  ls = 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[8 * u + c], sc, -m));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[8 * u + c + 1], sc, -m));
+      const h2 ph = __builtin_bit_cast(h2, pack_f16x2(e0, e1));
+      ls = __builtin_amdgcn_fdot2(ph, one2, ls, false);
+      pf[u][c] = ph[0];
+      pf[u][c + 1] = ph[1];
+    }
+  }
+}
+
 // Half kb of a pass (d_k = 64): scores, mask, maximum, exponentials and P.V
 // of keys 32 kb .. 32 kb + 31 of the staged tile.  A pass run as two halves
 // keeps only half the score, K and V fragment registers live at a time, which
@@ -315,8 +336,6 @@ __device__ __forceinline__ void wave_half(int kb, const f16* sk, const f16* sv,
                                           float& m_ref, float& l_run, bool masked, int keep_lo,
                                           int keep_hi, float sc, int lr, int lg) {
   constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 one2 = {(f16)1.f, (f16)1.f};
   {
     f16x8 kf[D / 16];
     {
@@ -336,13 +355,20 @@ __device__ __forceinline__ void wave_half(int kb, const f16* sk, const f16* sv,
         if (!(off > keep_lo && off <= keep_hi)) s[r] = -INFINITY;
       }
     }
-    float mt = -INFINITY;
+    // p against the current reference maximum; the half's fp16 sum below
+    // 2^15 proves every p is far inside fp16 range.  Otherwise (the maximum
+    // grew, or the reference is still the initial -1e30) the true maximum is
+    // taken, O and l are rescaled and p is recomputed.
+    f16x8 pf[2];
+    float ls;
+    exp_half(s, sc, m_ref, pf, ls);
+    if (__builtin_amdgcn_ballot_w64(!(ls < 32768.f)) != 0) {
+      float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
-                                                     false, false);
-    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
-    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                       false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sc;
       const float m_new = fmaxf(m_ref, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       m_ref = m_new;
@@ -351,7 +377,9 @@ __device__ __forceinline__ void wave_half(int kb, const f16* sk, const f16* sv,
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      exp_half(s, sc, m_ref, pf, ls);
     }
+    l_run += ls;
     // V^T fragments of this half's 32 keys (two 16-key steps u)
     f16x8 vf[D / 32][2];
 #pragma unroll
@@ -359,20 +387,6 @@ __device__ __forceinline__ void wave_half(int kb, const f16* sk, const f16* sv,
       const f16* vb = sv + (32 * db + lr) * VP + 32 * kb + 8 * lg;
 #pragma unroll
       for (int u = 0; u < 2; ++u) vf[db][u] = *(const f16x8*)(vb + 16 * u);
-    }
-    f16x8 pf[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int c = 0; c < 8; c += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[8 * u + c], sc, -m_ref));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[8 * u + c + 1], sc, -m_ref));
-        const uint32_t pk = pack_f16x2(e0, e1);
-        const h2 ph = __builtin_bit_cast(h2, pk);
-        l_run = __builtin_amdgcn_fdot2(ph, one2, l_run, false);
-        pf[u][c] = ph[0];
-        pf[u][c + 1] = ph[1];
-      }
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
