@@ -241,6 +241,61 @@ def time_decode(torch, dar, di, steps, warmup, cfg):
             "bytes": byts, "flops": flops}
 
 
+def calibrate(torch):
+    """Measured peaks on this device: dense fp16 MFMA rate and HBM copy
+    bandwidth (libdar_calib.so), to read the kernels' rates against."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "distance_adaptive_dual_amd", "libdar_calib.so"))
+    L.dar_calib_mfma_flops.restype = ctypes.c_double
+    L.dar_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.dar_calib_mfma.restype = ctypes.c_int
+    L.dar_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.dar_calib_copy.restype = ctypes.c_int
+    L.dar_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    wgs, iters = 2048, 2000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rates = {}
+    for shape, name in ((0, "32x32x16"), (1, "16x16x32")):
+        def mfma():
+            if L.dar_calib_mfma(sink.data_ptr(), wgs, iters, shape, stream) != 0:
+                raise RuntimeError("dar_calib_mfma failed")
+
+        rates[name] = L.dar_calib_mfma_flops(wgs, iters, shape) / timed(mfma) / 1e9
+    tflops = max(rates.values())
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def copy():
+        if L.dar_calib_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream) != 0:
+            raise RuntimeError("dar_calib_copy failed")
+
+    ms_c = timed(copy)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"mfma_f16_tflops": tflops, "mfma_f16_tflops_by_shape": rates,
+            "hbm_copy_gbs": 2 * nbytes / ms_c / 1e6,
+            "vendor_mfma_tflops": PEAK_BF16_TFLOPS, "vendor_hbm_gbs": PEAK_HBM_GBS,
+            "how": "fp16 MFMA loops from registers (the faster of 32x32x16 and 16x16x32), "
+                   "2048 workgroups; 1 GiB device copy with 16-byte loads/stores (read + "
+                   "write bytes)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +328,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    log("calibration: measured MFMA and copy peaks")
+    cal = calibrate(torch)
     res = {"metric": "DAR prefill TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)",
            "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
@@ -305,7 +362,9 @@ def main():
                            "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": recorded_traffic("attn_prefill_f16<64>@pythia70m",
                                                        ["attn_prefill.hip", "dar_common.hpp"]),
-                           "flops_per_launch": attn_f, "launch_ms": attn_ms}
+                           "flops_per_launch": attn_f, "launch_ms": attn_ms,
+                           "peak_measured": cal["mfma_f16_tflops"],
+                           "frac_measured": achieved / cal["mfma_f16_tflops"]}
         if not args.no_cpu:
             import oracle
             log("cpu baseline: oracle on one sequence")
@@ -341,11 +400,14 @@ def main():
         dec = time_decode(torch, dar, di, max(3, args.steps // 2), 2,
                           (16, 32768, 2048, 16, 128, 256, 512))
         log("decode: %.3f ms, %.0f GB/s, %.1f TFLOP/s" % (dec["ms"], dec["GB/s"], dec["TFLOP/s"]))
+        dec["hbm_frac_measured"] = dec["GB/s"] / cal["hbm_copy_gbs"]
+        dec["mfma_frac_measured"] = dec["TFLOP/s"] / cal["mfma_f16_tflops"]
         res["decode"] = dec
         if res["value"] is None:
             res.update(value=dec["GB/s"], unit="GB/s", ms_per_step=dec["ms"])
             res["config"] = {"workload": dec["workload"], "global_batch": 16, "seq_len": 32768,
                              "parallelism": "none (1 GPU)"}
+    res["calibration"] = cal
     print(json.dumps(res), flush=True)
 
 

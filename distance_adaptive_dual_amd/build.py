@@ -1,4 +1,5 @@
-"""Compile the DAR HIP library (``libdar.so``) for gfx950 with hipcc.
+"""Compile the DAR HIP library (``libdar.so``) and the benchmark's calibration
+library (``libdar_calib.so``) for gfx950 with hipcc.
 
 The library is built in-tree, next to this file, so it travels with the
 source tree.  ``python -m distance_adaptive_dual_amd.build`` rebuilds it.
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdar.so")
 SOURCES = ["dar_api.cpp", "rope.hip", "gemm.hip", "attn_prefill.hip", "attn_decode.hip"]
+CALIB_LIB = os.path.join(HERE, "libdar_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 HEADERS = ["dar_common.hpp"]
 ARCH = "gfx950"
 
@@ -33,10 +36,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libdar.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _compile(sources, lib, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + srcs + [
         "-o", tmp]
     if verbose:
@@ -50,8 +52,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libdar.so and libdar_calib.so (always recompiles)."""
+    _compile(CALIB_SOURCES, CALIB_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,104 @@
+// Calibration kernels for the benchmark (libdar_calib.so, not part of the DAR
+// ABI): the dense fp16 MFMA rate and the HBM copy bandwidth this device
+// actually reaches, so measured kernel rates can be read against measured
+// peaks as well as the vendor figures.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Each wave keeps four independent fp16 MFMA accumulation chains busy for
+// `iters` rounds (shape 0: 32x32x16, shape 1: 16x16x32); operands come from
+// registers only.
+__global__ __launch_bounds__(256) void mfma_peak_kernel(float* sink, int iters, int shape) {
+  const int lane = threadIdx.x & 63;
+  f16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (_Float16)(1e-3f * (float)(lane + e));
+    b[e] = (_Float16)(1e-3f * (float)(lane - e));
+  }
+  float s = 0.f;
+  if (shape == 0) {
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, b, c3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  } else {
+    f32x4 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, b, c3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  }
+  if (s == 1234.5f) sink[blockIdx.x * blockDim.x + threadIdx.x] = s;  // keeps the work live
+}
+
+// Grid-stride copy, four 16-byte chunks in flight per thread.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride],
+                v3 = src[i + 3 * stride];
+    dst[i] = v0;
+    dst[i + stride] = v1;
+    dst[i + 2 * stride] = v2;
+    dst[i + 3 * stride] = v3;
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// FLOP of one dar_calib_mfma call with these arguments (a 16x16x32 MFMA does
+// half the work of a 32x32x16 one).
+double dar_calib_mfma_flops(int workgroups, int iters, int shape) {
+  const double per = shape == 0 ? 32768.0 : 16384.0;
+  return (double)workgroups * 4.0 /*waves*/ * (double)iters * 4.0 /*chains*/ * per;
+}
+
+// Launches `workgroups` workgroups of 4 waves, each wave issuing 4*iters
+// dense fp16 MFMAs (shape 0: 32x32x16, 1: 16x16x32).  sink: device buffer of
+// workgroups*256 floats (written only in an impossible case).  Returns the
+// hipError_t of the launch.
+int dar_calib_mfma(float* sink, int workgroups, int iters, int shape, hipStream_t stream) {
+  if (workgroups < 1 || iters < 1 || sink == nullptr || (shape != 0 && shape != 1))
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(workgroups), dim3(256), 0, stream, sink, iters,
+                     shape);
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16, both pointers 16-byte aligned) from src to
+// dst on the device.  Returns the hipError_t of the launch.
+int dar_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || (bytes & 15) || ((uintptr_t)src & 15) ||
+      ((uintptr_t)dst & 15))
+    return (int)hipErrorInvalidValue;
+  const size_t n16 = bytes / 16;
+  hipLaunchKernelGGL(copy_kernel, dim3(8192), dim3(256), 0, stream, (const u32x4*)src,
+                     (u32x4*)dst, n16);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

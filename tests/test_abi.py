@@ -155,3 +155,30 @@ def test_append_size_query_and_rejects():
     assert append(d_k=96)[0] == UNSUP
     assert append(w=0, K_win=None, V_win=None)[0] == OK
     assert append(ws=F(20), wsb=n - 1)[0] == WS
+
+
+CALIB_HEADER = os.path.join(ROOT, "include", "dar_calib.h")
+
+
+def test_calib_library_exports_and_rejects():
+    """libdar_calib.so (the benchmark's calibration kernels) exports what
+    include/dar_calib.h declares and rejects bad arguments before launching."""
+    text = open(CALIB_HEADER).read()
+    names = set(re.findall(r"^\s*(?:int|double)\s+(dar_\w+)\s*\(", text, re.M))
+    assert names == {"dar_calib_mfma_flops", "dar_calib_mfma", "dar_calib_copy"}
+    L = ctypes.CDLL(os.path.join(ROOT, "distance_adaptive_dual_amd", "libdar_calib.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    L.dar_calib_mfma_flops.restype = ctypes.c_double
+    L.dar_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    assert L.dar_calib_mfma_flops(2, 3, 0) == 2 * 4 * 3 * 4 * 32768
+    assert L.dar_calib_mfma_flops(2, 3, 1) == 2 * 4 * 3 * 4 * 16384
+    L.dar_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.dar_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
+    assert L.dar_calib_mfma(F(0), 0, 10, 0, None) != 0       # no workgroups
+    assert L.dar_calib_mfma(None, 4, 10, 0, None) != 0       # no sink
+    assert L.dar_calib_mfma(F(0), 4, 10, 2, None) != 0       # unknown shape
+    assert L.dar_calib_copy(F(0), F(1), 100, None) != 0      # not a multiple of 16
+    assert L.dar_calib_copy(F(0) + 8, F(1), 64, None) != 0   # misaligned source
