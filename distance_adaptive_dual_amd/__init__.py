@@ -25,7 +25,7 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
-           "dar_attn_prefill", "dar_decode_append", "dar_attn_decode")
+           "dar_attn_prefill", "dar_decode_append", "dar_cache_from_prefill", "dar_attn_decode")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.dar_decode_append.restype = _I
         L.dar_decode_append.argtypes = [_P] * 5 + [_I] * 8 + [ctypes.c_float, _I] + [_P] * 5 + [
             _SZ, _P]
+        L.dar_cache_from_prefill.restype = _I
+        L.dar_cache_from_prefill.argtypes = [_P] * 3 + [_I] * 7 + [_I] + [_P] * 4
         L.dar_attn_decode.restype = _I
         L.dar_attn_decode.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P, _SZ, _P]
         _lib = L
@@ -213,6 +215,32 @@ def dar_decode_append(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos: int, 
             _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D)]
     _call_ws("dar_decode_append", lib().dar_decode_append, args, workspace, h, stream)
     return q
+
+
+def dar_cache_from_prefill(h_D, K_loc, V_loc, w: int, cap: int = None, h_D_cache=None,
+                           K_win=None, V_win=None, stream=None):
+    """Decode cache of a prefilled prompt from dar_project's outputs (fp16):
+    latent rows 0..N-1 and the ring slots of positions max(0, N-w)..N-1, in
+    bf16.  Returns (h_D_cache [B, cap, d_down], K_win, V_win [B, heads, w, d_k]);
+    K_win / V_win are None when w = 0."""
+    torch = _torch()
+    B, N, d_down = h_D.shape
+    _, H, _, d_k = K_loc.shape
+    cap = N if cap is None else cap
+    kw = dict(dtype=torch.bfloat16, device=h_D.device)
+    if h_D_cache is None:
+        h_D_cache = torch.zeros((B, cap, d_down), **kw)
+    if w > 0 and K_win is None:
+        K_win = torch.zeros((B, H, w, d_k), **kw)
+    if w > 0 and V_win is None:
+        V_win = torch.zeros((B, H, w, d_k), **kw)
+    st = lib().dar_cache_from_prefill(_ptr(h_D), _ptr(K_loc) if w > 0 else None,
+                                      _ptr(V_loc) if w > 0 else None, B, N, H, d_k, d_down,
+                                      int(w), int(h_D_cache.shape[1]), _dtype_code(h_D),
+                                      _ptr(h_D_cache), _ptr(K_win) if w > 0 else None,
+                                      _ptr(V_win) if w > 0 else None, _stream(stream))
+    _check("dar_cache_from_prefill", st)
+    return h_D_cache, K_win, V_win
 
 
 def decode_workspace_bytes(B, ctx_len, cap, heads, d_k, d_down, w, dtype=DAR_BF16):

@@ -1,0 +1,112 @@
+// Decode cache from a prefill.
+//
+// "Dual Dimensionality for Local and Global Attention": after a prompt is
+// prefilled, generation continues with each past token used through exactly
+// one path (the remark after Eq. (5)): the latent h^D_j of every position
+// (Eq. 1) and the full keys/values of the w most recent positions only.  The
+// prefill hands its projections over in the attention kernel's formats (fp16;
+// V transposed per head); the decode cache is bf16, latents [B, cap, d_down]
+// and a ring [B, heads, w, d_k] indexed by position mod w.  Two kernels copy
+// and convert: one for the latent rows, one for the ring (V through an LDS
+// transpose).
+#include "dar_common.hpp"
+
+namespace dar {
+
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ u32x4 f16x8_to_bf16x8(const u32x4& v) {
+  const h8 x = __builtin_bit_cast(h8, v);
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2((float)x[2 * e], (float)x[2 * e + 1]);
+  return r;
+}
+
+// h_D_cache[b, n, :] = bf16(h_D[b, n, :]) for n < N; 8 values per thread.
+__global__ __launch_bounds__(256) void latent_cast_kernel(const f16* __restrict__ hD,
+                                                          bf16* __restrict__ cache, int B, int N,
+                                                          int d_down, int cap) {
+  const int cpr = d_down / 8;  // 16-byte chunks per row
+  const size_t total = (size_t)B * N * cpr;
+  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += (size_t)gridDim.x * blockDim.x) {
+    const size_t row = c / cpr;
+    const int col = (int)(c % cpr) * 8;
+    const size_t b = row / N, n = row % N;
+    const u32x4 v = *(const u32x4*)(hD + row * d_down + col);
+    *(u32x4*)(cache + (b * cap + n) * d_down + col) = f16x8_to_bf16x8(v);
+  }
+}
+
+// Ring slots of positions j0 .. j0+63 (clipped to [j_lo, N)) of one (b, head):
+// K_win[b, h, j mod w, :] = bf16(K_loc[b, h, j, :]) and
+// V_win[b, h, j mod w, :] = bf16(V_loc[b, h, :, j]).
+template <int D>
+__global__ __launch_bounds__(256) void ring_fill_kernel(const f16* __restrict__ Kl,
+                                                        const f16* __restrict__ Vl,
+                                                        bf16* __restrict__ Kw,
+                                                        bf16* __restrict__ Vw, int N, int w,
+                                                        int j_lo) {
+  constexpr int TJ = 64, TP = TJ + 2;  // positions per tile; LDS pitch (f16)
+  __shared__ f16 vt[D * TP];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int j0 = j_lo + TJ * blockIdx.y;
+  const int nj = min(TJ, N - j0);
+  const f16* K = Kl + (size_t)bh * N * D;
+  const f16* V = Vl + (size_t)bh * D * N;
+  bf16* KW = Kw + (size_t)bh * w * D;
+  bf16* VW = Vw + (size_t)bh * w * D;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  for (int c = tid; c < nj * CPR; c += 256) {
+    const int r = c / CPR, col = (c % CPR) * 8;
+    const int j = j0 + r;
+    const u32x4 v = *(const u32x4*)(K + (size_t)j * D + col);
+    *(u32x4*)(KW + (size_t)(j % w) * D + col) = f16x8_to_bf16x8(v);
+  }
+  // V^T tile: row t holds positions j0 .. j0+nj-1 (element reads: the rows of
+  // V_loc need not be 16-byte aligned at j0)
+  for (int e = tid; e < D * TJ; e += 256) {
+    const int t = e / TJ, r = e % TJ;
+    vt[t * TP + r] = r < nj ? V[(size_t)t * N + j0 + r] : (f16)0.f;
+  }
+  __syncthreads();
+  for (int c = tid; c < nj * CPR; c += 256) {
+    const int r = c / CPR, t0 = (c % CPR) * 8;
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      out[e] = pack_bf16x2((float)vt[(t0 + 2 * e) * TP + r], (float)vt[(t0 + 2 * e + 1) * TP + r]);
+    *(u32x4*)(VW + (size_t)((j0 + r) % w) * D + t0) = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc,
+                                     int B, int N, int heads, int d_k, int d_down, int w,
+                                     int cap, void* h_D_cache, void* K_win, void* V_win,
+                                     hipStream_t s) {
+  {
+    const size_t chunks = (size_t)B * N * (d_down / 8);
+    size_t blocks = (chunks + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(latent_cast_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const f16*)h_D, (bf16*)h_D_cache, B, N, d_down, cap);
+  }
+  if (w > 0) {
+    const int j_lo = N > w ? N - w : 0;
+    const dim3 grid(B * heads, (N - j_lo + 63) / 64);
+    if (d_k == 64)
+      hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, (const f16*)K_loc,
+                         (const f16*)V_loc, (bf16*)K_win, (bf16*)V_win, N, w, j_lo);
+    else
+      hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, (const f16*)K_loc,
+                         (const f16*)V_loc, (bf16*)K_win, (bf16*)V_win, N, w, j_lo);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dar

@@ -1,7 +1,7 @@
 // C ABI of the DAR attention library: argument validation, workspace sizing
 // and launches on the caller's stream.  No allocation, no state, no host
-// synchronisation.  The kernels live in rope.hip, gemm.hip, attn_prefill.hip
-// and attn_decode.hip.
+// synchronisation.  The kernels live in rope.hip, gemm.hip, attn_prefill.hip,
+// attn_decode.hip and cache.hip.
 #include <stdint.h>
 #include <string.h>
 
@@ -270,6 +270,30 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
   g.seg[ns++] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos};
   g.nseg = ns;
   return hip_status(launch_project_gemm(g, dtype, stream));
+}
+
+dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc, int B,
+                                  int N, int heads, int d_k, int d_down, int w, int cap,
+                                  dar_dtype dtype, void* h_D_cache, void* K_win, void* V_win,
+                                  hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_down < 1 || w < 0 || cap < N)
+    return DAR_ERR_INVALID_ARG;
+  if (!aligned16(h_D) || !aligned16(h_D_cache)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_loc) || !aligned16(V_loc) || !aligned16(K_win) || !aligned16(V_win)))
+    return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k;
+  const Span ins[3] = {{h_D, 2 * (size_t)B * N * d_down},
+                       {w > 0 ? K_loc : nullptr, 2 * (size_t)B * N * hd},
+                       {w > 0 ? V_loc : nullptr, 2 * (size_t)B * N * hd}};
+  const Span outs[3] = {{h_D_cache, 2 * (size_t)B * cap * d_down},
+                        {w > 0 ? K_win : nullptr, 2 * (size_t)B * w * hd},
+                        {w > 0 ? V_win : nullptr, 2 * (size_t)B * w * hd}};
+  if (!disjoint(outs, 3, ins, 3)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!head_supported(d_k) || d_down % 8) return DAR_ERR_UNSUPPORTED;
+  return hip_status(launch_cache_from_prefill(h_D, K_loc, V_loc, B, N, heads, d_k, d_down, w,
+                                              cap, h_D_cache, K_win, V_win, stream));
 }
 
 dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,

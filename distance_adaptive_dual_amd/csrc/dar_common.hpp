@@ -184,6 +184,11 @@ struct DecodeProblem {
   void* ws;  // workspace after the rope tables
 };
 size_t decode_workspace_bytes(const DecodeProblem& p);
+// Decode cache from prefill outputs (fp16 h_D, K_loc, V_loc^T -> bf16 cache).
+hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc,
+                                     int B, int N, int heads, int d_k, int d_down, int w,
+                                     int cap, void* h_D_cache, void* K_win, void* V_win,
+                                     hipStream_t s);
 bool decode_supported(int d_k, int d_down);  // d_k in {64,128}, d_down in {32,64,128,256}
 hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s);
 

@@ -152,6 +152,30 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
                              size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * dar_cache_from_prefill -- the decode cache of a prefilled prompt.
+ *
+ * After a prompt of N tokens is prefilled, generation keeps the latent h^D of
+ * every position (Eq. 1) and full keys/values for the w most recent positions
+ * only (the inference remark after Eq. (5)).  This converts dar_project's
+ * outputs into the cache dar_decode_append / dar_attn_decode use:
+ *   h_D_cache[b, n, :]       <- h_D[b, n, :]          for n < N
+ *   K_win[b, :, j mod w, :]  <- K_loc[b, :, j, :]     for max(0, N-w) <= j < N
+ *   V_win[b, :, j mod w, :]  <- V_loc[b, :, :, j]     (V_loc is token-innermost)
+ * leaving every other row and slot untouched.
+ *   h_D [B, N, d_down], K_loc [B, heads, N, d_k], V_loc [B, heads, d_k, N]
+ *                                   (fp16: dar_project's DAR_BF16 outputs)
+ *   h_D_cache [B, cap, d_down] with cap >= N; K_win, V_win [B, heads, w, d_k]
+ *                                   (bf16; ignored, may be NULL, when w = 0)
+ * Values are rounded fp16 -> bf16 (nearest even).  The next token sits at
+ * position N: dar_decode_append(pos = N), then dar_attn_decode(ctx_len = N+1).
+ * DAR_BF16 only; d_down must be a multiple of 8.  No workspace.
+ */
+dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc, int B,
+                                  int N, int heads, int d_k, int d_down, int w, int cap,
+                                  dar_dtype dtype, void* h_D_cache, void* K_win, void* V_win,
+                                  hipStream_t stream);
+
+/*
  * dar_attn_decode -- one new query per sequence over the mixed cache.
  *
  * The inference remarks of the paper note that each past token contributes

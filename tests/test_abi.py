@@ -182,3 +182,26 @@ def test_calib_library_exports_and_rejects():
     assert L.dar_calib_mfma(F(0), 4, 10, 2, None) != 0       # unknown shape
     assert L.dar_calib_copy(F(0), F(1), 100, None) != 0      # not a multiple of 16
     assert L.dar_calib_copy(F(0) + 8, F(1), 64, None) != 0   # misaligned source
+
+
+def cache(**kw):
+    a = dict(h_D=F(0), K_loc=F(1), V_loc=F(2), B=2, N=100, heads=4, d_k=64, d_down=64, w=16,
+             cap=128, dtype=1, h_D_cache=F(3), K_win=F(4), V_win=F(5))
+    a.update(kw)
+    return dar.lib().dar_cache_from_prefill(a["h_D"], a["K_loc"], a["V_loc"], a["B"], a["N"],
+                                            a["heads"], a["d_k"], a["d_down"], a["w"], a["cap"],
+                                            a["dtype"], a["h_D_cache"], a["K_win"], a["V_win"],
+                                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cap=99), INVALID),                    # the cache must hold the N prompt rows
+    (dict(N=0), INVALID), (dict(w=-1), INVALID), (dict(B=0), INVALID),
+    (dict(h_D_cache=F(0)), INVALID),            # output aliases an input
+    (dict(K_win=F(3)), INVALID),                # two outputs alias
+    (dict(V_win=None), INVALID),                # w > 0 needs the ring
+    (dict(h_D=F(0) + 8), INVALID),              # misaligned
+    (dict(dtype=0), UNSUP), (dict(d_k=96), UNSUP), (dict(d_down=60), UNSUP),
+])
+def test_cache_from_prefill_rejects(kw, code):
+    assert cache(**kw) == code

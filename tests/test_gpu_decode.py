@@ -167,3 +167,63 @@ def test_append_then_decode_matches_prefill_row():
     err = max_err(host(o), o_ref[:, p])
     log("  append+decode vs prefill row err %.3g" % err)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,N,H,d_k,dd,w,cap", [
+    (2, 100, 4, 64, 64, 16, 128),
+    (2, 77, 2, 128, 128, 32, 80),    # ragged N (not a multiple of 8)
+    (1, 10, 2, 64, 32, 32, 16),      # prompt shorter than the window
+    (2, 40, 2, 64, 64, 0, 40),       # no window
+])
+def test_cache_from_prefill_exact(B, N, H, d_k, dd, w, cap):
+    """Latent rows 0..N-1 and ring slots of positions max(0, N-w)..N-1 are the
+    prefill values rounded fp16 -> bf16; every other row and slot is left as
+    it was."""
+    g = np.random.Generator(np.random.PCG64(1000 + N))
+    hD = di.round_f16(g.standard_normal((B, N, dd)))
+    KL = di.round_f16(g.standard_normal((B, H, N, d_k)))
+    VL = di.round_f16(g.standard_normal((B, H, d_k, N)))
+    L0 = di.round_bf16(g.standard_normal((B, cap, dd)))
+    K0 = di.round_bf16(g.standard_normal((B, H, max(w, 1), d_k)))
+    V0 = di.round_bf16(g.standard_normal((B, H, max(w, 1), d_k)))
+    Lc = dev(L0, "bf16")
+    Kw = dev(K0, "bf16") if w else None
+    Vw = dev(V0, "bf16") if w else None
+    dar.dar_cache_from_prefill(dev(hD, "f16"), dev(KL, "f16"), dev(VL, "f16"), w, cap=cap,
+                               h_D_cache=Lc, K_win=Kw, V_win=Vw)
+    torch.cuda.synchronize()
+    Lg = host(Lc)
+    assert np.array_equal(Lg[:, :N], di.round_bf16(hD))
+    assert np.array_equal(Lg[:, N:], L0[:, N:])
+    if w:
+        Kg, Vg = host(Kw), host(Vw)
+        K_exp, V_exp = K0.copy(), V0.copy()
+        for j in range(max(0, N - w), N):
+            K_exp[:, :, j % w] = di.round_bf16(KL[:, :, j])
+            V_exp[:, :, j % w] = di.round_bf16(VL[:, :, :, j])
+        assert np.array_equal(Kg, K_exp)
+        assert np.array_equal(Vg, V_exp)
+
+
+@pytest.mark.parametrize("N,w,d_k,dd", [(700, 100, 64, 128), (333, 512, 128, 64)])
+def test_prefill_cache_append_decode_matches_prefill_row(N, w, d_k, dd):
+    """The inference loop on the GPU: prefill a prompt of N tokens, build the
+    decode cache from it, append token N and decode it; the output equals row
+    N of the oracle's prefill over all N+1 tokens."""
+    B, d, H = 2, 256, 4
+    inp = prefill_case(B, N + 1, d, H, d_k, dd, "bf16", seed=808 + N)
+    W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    h = dev(inp["h"], "bf16")
+    out = dar.dar_project(h[:, :N].contiguous(), W["W_down"], W["W_up"], W["W_Q"], W["W_K"],
+                          W["W_V"], H, d_k, W_upK=Wk, W_upV=Wv)
+    Lc, Kw, Vw = dar.dar_cache_from_prefill(out["h_D"], out["K_loc"], out["V_loc"], w, cap=N + 1)
+    q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
+    dar.dar_decode_append(h[:, N].contiguous(), W["W_down"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                          N, q, Kw, Vw, Lc)
+    o = dar.dar_attn_decode(q, Kw, Vw, Lc, Wk, Wv, N + 1, w)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.prefill(inp, H, d_k, w)
+    err = max_err(host(o), ref[:, N])
+    log("  prefill -> cache -> append -> decode vs prefill row %d: err %.3g" % (N, err))
+    assert err <= TOL["bf16"]
