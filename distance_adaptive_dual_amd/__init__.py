@@ -25,7 +25,8 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
-           "dar_attn_prefill", "dar_decode_append", "dar_cache_from_prefill", "dar_attn_decode")
+           "dar_attn_prefill", "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
+           "dar_attn_decode")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
             _SZ, _P]
         L.dar_cache_from_prefill.restype = _I
         L.dar_cache_from_prefill.argtypes = [_P] * 3 + [_I] * 7 + [_I] + [_P] * 4
+        L.dar_prefill_chunk.restype = _I
+        L.dar_prefill_chunk.argtypes = [_P] * 7 + [_I] * 9 + [ctypes.c_float, _I] + [_P] * 5 + [
+            _SZ, _P]
         L.dar_attn_decode.restype = _I
         L.dar_attn_decode.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P, _SZ, _P]
         _lib = L
@@ -241,6 +245,36 @@ def dar_cache_from_prefill(h_D, K_loc, V_loc, w: int, cap: int = None, h_D_cache
                                       _ptr(V_win) if w > 0 else None, _stream(stream))
     _check("dar_cache_from_prefill", st)
     return h_D_cache, K_win, V_win
+
+
+def chunk_workspace_bytes(B, C, d, d_down, heads, d_k, p0, w, cap):
+    n = ctypes.c_size_t(0)
+    f = [_fake(i) for i in range(12)]
+    st = lib().dar_prefill_chunk(*f[:7], B, C, d, d_down, heads, d_k, p0, w, cap, 10000.0,
+                                 DAR_BF16, f[7], f[8] if w > 0 else None, f[9] if w > 0 else None,
+                                 f[10], None, ctypes.byref(n), None)
+    _check("dar_prefill_chunk", st)
+    return n.value
+
+
+def dar_prefill_chunk(h, W_down, W_Q, W_K, W_V, W_upK, W_upV, heads: int, d_k: int, p0: int,
+                      h_D_cache, K_win, V_win, w: int, o=None, rope_base: float = 10000.0,
+                      workspace=None, stream=None):
+    """Prefill the chunk h [B, C, d] at positions p0 .. p0+C-1 over the cache
+    (h_D_cache [B, cap, d_down], ring K_win / V_win [B, heads, w, d_k], bf16;
+    updated in place).  Returns o [B, C, heads*d_k]."""
+    torch = _torch()
+    B, C, d = h.shape
+    d_down = W_down.shape[0]
+    cap = h_D_cache.shape[1]
+    if o is None:
+        o = torch.empty((B, C, heads * d_k), dtype=torch.bfloat16, device=h.device)
+    args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_upK), _ptr(W_upV),
+            B, C, d, d_down, heads, d_k, int(p0), int(w), cap, float(rope_base), _dtype_code(h),
+            _ptr(h_D_cache), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None,
+            _ptr(o)]
+    _call_ws("dar_prefill_chunk", lib().dar_prefill_chunk, args, workspace, h, stream)
+    return o
 
 
 def decode_workspace_bytes(B, ctx_len, cap, heads, d_k, d_down, w, dtype=DAR_BF16):

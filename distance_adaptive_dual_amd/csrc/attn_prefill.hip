@@ -66,6 +66,9 @@ struct Stage {
   u32x4 k[NCH], v[NCH];
 };
 
+// K and Vt hold positions base .. base+N-1 of one (batch, head) (K [N x D],
+// Vt [D x N]); j0 = first position of the tile - base, which may be negative
+// for the local arrays of a chunk: rows outside [0, N) read as zeros.
 template <int D>
 __device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16* Vt, int N, int j0,
                                           bool vec_ok) {
@@ -75,17 +78,18 @@ __device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16*
   for (int i = 0; i < Stage<D>::NCH; ++i) {
     const int c = tid + 256 * i;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    st.k[i] = (j0 + row < N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
+    st.k[i] = ((unsigned)(j0 + row) < (unsigned)N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
     const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
     if (vec_ok) {
       st.v[i] = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
-    } else {  // ragged tail, or N not a multiple of 8
+    } else {  // ragged tail, rows outside [0, N), or N not a multiple of 8
       const uint16_t* src = (const uint16_t*)Vt + (size_t)d * N;
       uint32_t w4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ja = j0 + kc + 2 * e, jb = ja + 1;
-        const uint32_t a = ja < N ? src[ja] : 0u, b = jb < N ? src[jb] : 0u;
+        const uint32_t a = (unsigned)ja < (unsigned)N ? src[ja] : 0u;
+        const uint32_t b = (unsigned)jb < (unsigned)N ? src[jb] : 0u;
         w4[e] = a | (b << 16);
       }
       st.v[i] = u32x4{w4[0], w4[1], w4[2], w4[3]};
@@ -103,7 +107,7 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[Stage<D>::NCH], const f16* K, 
   for (int i = 0; i < Stage<D>::NCH; ++i) {
     const int c = tid + 256 * i;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    k[i] = (j0 + row < N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
+    k[i] = ((unsigned)(j0 + row) < (unsigned)N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
   }
 }
 
@@ -117,13 +121,14 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[Stage<D>::NCH], const f16* Vt,
     const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
     if (vec_ok) {
       v[i] = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
-    } else {  // ragged tail, or N not a multiple of 8
+    } else {  // ragged tail, rows outside [0, N), or N not a multiple of 8
       const uint16_t* src = (const uint16_t*)Vt + (size_t)d * N;
       uint32_t w4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ja = j0 + kc + 2 * e, jb = ja + 1;
-        const uint32_t a = ja < N ? src[ja] : 0u, b = jb < N ? src[jb] : 0u;
+        const uint32_t a = (unsigned)ja < (unsigned)N ? src[ja] : 0u;
+        const uint32_t b = (unsigned)jb < (unsigned)N ? src[jb] : 0u;
         w4[e] = a | (b << 16);
       }
       v[i] = u32x4{w4[0], w4[1], w4[2], w4[3]};
@@ -447,24 +452,32 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     }
   }
   const int b = bh / H, h = bh % H;
-  const size_t kv_off = (size_t)bh * N * D;
-  const f16* Qp = (const f16*)p.Q + kv_off;
-  const f16* Kg = (const f16*)p.K_glob + kv_off;
-  const f16* Kl = (const f16*)p.K_loc + kv_off;
-  const f16* Vg = (const f16*)p.V_glob + kv_off;
-  const f16* Vl = (const f16*)p.V_loc + kv_off;
+  // Positions: queries q0 .. N-1 (Q and o hold those rows only), keys 0 .. N-1
+  // in the global arrays, keys loc0 .. N-1 in the local arrays.
+  const int q0 = p.q0, loc0 = p.loc0, nqr = N - q0, nloc = N - loc0;
+  const f16* Qp = (const f16*)p.Q + (size_t)bh * nqr * D;
+  const f16* Kg = (const f16*)p.K_glob + (size_t)bh * N * D;
+  const f16* Kl = (const f16*)p.K_loc + (size_t)bh * nloc * D;
+  const f16* Vg = (const f16*)p.V_glob + (size_t)bh * N * D;
+  const f16* Vl = (const f16*)p.V_loc + (size_t)bh * nloc * D;
+  // array, length, relative tile start and 16-byte V loads for source s at j0
+  auto src_len = [&](int s) { return s ? nloc : N; };
+  auto src_rel = [&](int s, int j0) { return s ? j0 - loc0 : j0; };
+  auto src_vec = [&](int s, int j0) {
+    const int len = src_len(s), jr = src_rel(s, j0);
+    return (len % 8) == 0 && (jr & 7) == 0 && jr >= 0 && jr + KT <= len;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
   const float sc = kLog2e / sqrtf((float)D);
-  const bool nvec = (N % 8) == 0;
   const int q_hi = nQT - 1 - pr;
   const int nq = (!paired || q_hi == pr) ? 1 : 2;
 
   for (int qn = 0; qn < nq; ++qn) {
     const int qt = qn == 0 ? q_hi : pr;
     if (qn > 0) __syncthreads();  // the LDS buffers are reused
-    const int i0 = qt * QT, qw0 = i0 + 32 * wave;
+    const int i0 = q0 + qt * QT, qw0 = i0 + 32 * wave;
     const int qi = qw0 + lr;  // this lane's query
     const int i_last = min(i0 + QT - 1, N - 1);
     const int wi_last = min(qw0 + 31, N - 1);
@@ -474,7 +487,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        u32x4 v = (qi < N) ? *(const u32x4*)(Qp + (size_t)qi * D + 16 * st + 8 * lg) : z;
+        u32x4 v = (qi < N) ? *(const u32x4*)(Qp + (size_t)(qi - q0) * D + 16 * st + 8 * lg) : z;
         qf[st] = __builtin_bit_cast(f16x8, v);
       }
     }
@@ -492,7 +505,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     auto need_loc = [&](int j0) { return w > 0 && max(i0 - (j0 + KT - 1), 0) < w; };
     int j0 = 0, src = need_glob(0) ? 0 : 1;  // src 0 = global, 1 = local
     Stage<D> stg;
-    load_pass<D>(stg, src ? Kl : Kg, src ? Vl : Vg, N, j0, nvec && (j0 + KT <= N));
+    load_pass<D>(stg, src ? Kl : Kg, src ? Vl : Vg, src_len(src), src_rel(src, j0),
+                 src_vec(src, j0));
     store_pass<D>(stg, sm.k[0], sm.v[0]);
     __syncthreads();
     int buf = 0;
@@ -509,10 +523,12 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
         // V of the next pass is fetched now and stored after the first half;
         // K is fetched then and stored at the end (its LDS buffer is free
         // for the whole pass), so only one of the two is held in registers.
-        if (has_next) load_v<D>(stg.v, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
+        if (has_next)
+          load_v<D>(stg.v, nsrc ? Vl : Vg, src_len(nsrc), src_rel(nsrc, nj0), src_vec(nsrc, nj0));
       } else {
         if (has_next)
-          load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, N, nj0, nvec && (nj0 + KT <= N));
+          load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, src_len(nsrc), src_rel(nsrc, nj0),
+                       src_vec(nsrc, nj0));
       }
 
       const WavePass wp = wave_pass_info(j0, src, qw0, wi_last, qi, lg, N, w);
@@ -522,7 +538,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
                        wp.keep_hi, sc, lr, lg);
         if (has_next) {
           store_v<D>(stg.v, sm.v[buf ^ 1]);
-          load_k<D>(stg.k, nsrc ? Kl : Kg, N, nj0);
+          load_k<D>(stg.k, nsrc ? Kl : Kg, src_len(nsrc), src_rel(nsrc, nj0));
         }
         if (wp.part)
           wave_half<D>(1, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
@@ -545,7 +561,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     if (qi < N) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const float inv = 1.f / l_tot;
-      bf16* out = (bf16*)p.o + ((size_t)b * N + qi) * (size_t)(H * D) + (size_t)h * D;
+      bf16* out = (bf16*)p.o + ((size_t)b * nqr + (qi - q0)) * (size_t)(H * D) + (size_t)h * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -638,7 +654,7 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
   if (p.w > p.N) p.w = p.N;
   const int BH = p.B * p.H;
   if (dt == DAR_BF16) {
-    const int nQT = (p.N + QT - 1) / QT;
+    const int nQT = (p.N - p.q0 + QT - 1) / QT;
     // d_k = 64 fits three waves per SIMD, so one tile per workgroup (longest
     // first) keeps more of them resident; at d_k = 128 (two per SIMD) pairing
     // balances the workgroups instead.

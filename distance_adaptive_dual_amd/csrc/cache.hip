@@ -25,10 +25,10 @@ __device__ __forceinline__ u32x4 f16x8_to_bf16x8(const u32x4& v) {
   return r;
 }
 
-// h_D_cache[b, n, :] = bf16(h_D[b, n, :]) for n < N; 8 values per thread.
+// h_D_cache[b, row0 + n, :] = bf16(h_D[b, n, :]) for n < N; 8 values per thread.
 __global__ __launch_bounds__(256) void latent_cast_kernel(const f16* __restrict__ hD,
                                                           bf16* __restrict__ cache, int B, int N,
-                                                          int d_down, int cap) {
+                                                          int d_down, int cap, int row0) {
   const int cpr = d_down / 8;  // 16-byte chunks per row
   const size_t total = (size_t)B * N * cpr;
   for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
@@ -37,40 +37,42 @@ __global__ __launch_bounds__(256) void latent_cast_kernel(const f16* __restrict_
     const int col = (int)(c % cpr) * 8;
     const size_t b = row / N, n = row % N;
     const u32x4 v = *(const u32x4*)(hD + row * d_down + col);
-    *(u32x4*)(cache + (b * cap + n) * d_down + col) = f16x8_to_bf16x8(v);
+    *(u32x4*)(cache + (b * cap + row0 + n) * d_down + col) = f16x8_to_bf16x8(v);
   }
 }
 
-// Ring slots of positions j0 .. j0+63 (clipped to [j_lo, N)) of one (b, head):
-// K_win[b, h, j mod w, :] = bf16(K_loc[b, h, j, :]) and
-// V_win[b, h, j mod w, :] = bf16(V_loc[b, h, :, j]).
+// Ring slots of positions j0 .. j0+63 (clipped to [j_lo, N)) of one (b, head)
+// from arrays holding positions base .. N-1 (len = N - base rows):
+// K_win[b, h, j mod w, :] = bf16(K[b, h, j - base, :]) and
+// V_win[b, h, j mod w, :] = bf16(Vt[b, h, :, j - base]).
 template <int D>
 __global__ __launch_bounds__(256) void ring_fill_kernel(const f16* __restrict__ Kl,
                                                         const f16* __restrict__ Vl,
                                                         bf16* __restrict__ Kw,
                                                         bf16* __restrict__ Vw, int N, int w,
-                                                        int j_lo) {
+                                                        int j_lo, int base) {
   constexpr int TJ = 64, TP = TJ + 2;  // positions per tile; LDS pitch (f16)
   __shared__ f16 vt[D * TP];
   const int bh = blockIdx.x, tid = threadIdx.x;
+  const int len = N - base;
   const int j0 = j_lo + TJ * blockIdx.y;
   const int nj = min(TJ, N - j0);
-  const f16* K = Kl + (size_t)bh * N * D;
-  const f16* V = Vl + (size_t)bh * D * N;
+  const f16* K = Kl + (size_t)bh * len * D;
+  const f16* V = Vl + (size_t)bh * D * len;
   bf16* KW = Kw + (size_t)bh * w * D;
   bf16* VW = Vw + (size_t)bh * w * D;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   for (int c = tid; c < nj * CPR; c += 256) {
     const int r = c / CPR, col = (c % CPR) * 8;
     const int j = j0 + r;
-    const u32x4 v = *(const u32x4*)(K + (size_t)j * D + col);
+    const u32x4 v = *(const u32x4*)(K + (size_t)(j - base) * D + col);
     *(u32x4*)(KW + (size_t)(j % w) * D + col) = f16x8_to_bf16x8(v);
   }
   // V^T tile: row t holds positions j0 .. j0+nj-1 (element reads: the rows of
-  // V_loc need not be 16-byte aligned at j0)
+  // V need not be 16-byte aligned at j0)
   for (int e = tid; e < D * TJ; e += 256) {
     const int t = e / TJ, r = e % TJ;
-    vt[t * TP + r] = r < nj ? V[(size_t)t * N + j0 + r] : (f16)0.f;
+    vt[t * TP + r] = r < nj ? V[(size_t)t * len + (j0 - base) + r] : (f16)0.f;
   }
   __syncthreads();
   for (int c = tid; c < nj * CPR; c += 256) {
@@ -83,30 +85,86 @@ __global__ __launch_bounds__(256) void ring_fill_kernel(const f16* __restrict__ 
   }
 }
 
+// The other direction, for a prefill chunk: positions j0 .. j0+63 (clipped to
+// [base, p0)) of the ring into the local arrays of positions base .. base+len-1
+// (fp16; Vt token-innermost):  K[b, h, j - base, :] = K_win[b, h, j mod w, :],
+// Vt[b, h, :, j - base] = V_win[b, h, j mod w, :].
+template <int D>
+__global__ __launch_bounds__(256) void ring_to_local_kernel(const bf16* __restrict__ Kw,
+                                                            const bf16* __restrict__ Vw,
+                                                            f16* __restrict__ Kl,
+                                                            f16* __restrict__ Vl, int w, int base,
+                                                            int p0, int len) {
+  constexpr int TJ = 64;
+  __shared__ f16 vt[TJ * (D + 2)];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int j0 = base + TJ * blockIdx.y;
+  const int nj = min(TJ, p0 - j0);
+  const bf16* KW = Kw + (size_t)bh * w * D;
+  const bf16* VW = Vw + (size_t)bh * w * D;
+  f16* K = Kl + (size_t)bh * len * D;
+  f16* V = Vl + (size_t)bh * D * len;
+  for (int e = tid; e < nj * D; e += 256) {
+    const int r = e / D, t = e % D;
+    const int j = j0 + r;
+    K[(size_t)(j - base) * D + t] = (f16)(float)KW[(size_t)(j % w) * D + t];
+    vt[r * (D + 2) + t] = (f16)(float)VW[(size_t)(j % w) * D + t];
+  }
+  __syncthreads();
+  for (int e = tid; e < nj * D; e += 256) {
+    const int t = e / nj, r = e % nj;
+    V[(size_t)t * len + (j0 - base) + r] = vt[r * (D + 2) + t];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap, int row0,
+                              void* h_D_cache, hipStream_t s) {
+  const size_t chunks = (size_t)B * N * (d_down / 8);
+  size_t blocks = (chunks + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(latent_cast_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const f16*)h_D, (bf16*)h_D_cache, B, N, d_down, cap, row0);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_fill(const void* K, const void* Vt, int B, int heads, int d_k, int N,
+                            int base, int w, void* K_win, void* V_win, hipStream_t s) {
+  const int j_lo = max(N - w, base);
+  if (w <= 0 || j_lo >= N) return hipSuccess;
+  const dim3 grid(B * heads, (N - j_lo + 63) / 64);
+  if (d_k == 64)
+    hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, (const f16*)K,
+                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base);
+  else
+    hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, (const f16*)K,
+                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_to_local(const void* K_win, const void* V_win, int B, int heads, int d_k,
+                                int w, int base, int p0, int len, void* K, void* Vt,
+                                hipStream_t s) {
+  if (w <= 0 || base >= p0) return hipSuccess;
+  const dim3 grid(B * heads, (p0 - base + 63) / 64);
+  if (d_k == 64)
+    hipLaunchKernelGGL(ring_to_local_kernel<64>, grid, dim3(256), 0, s, (const bf16*)K_win,
+                       (const bf16*)V_win, (f16*)K, (f16*)Vt, w, base, p0, len);
+  else
+    hipLaunchKernelGGL(ring_to_local_kernel<128>, grid, dim3(256), 0, s, (const bf16*)K_win,
+                       (const bf16*)V_win, (f16*)K, (f16*)Vt, w, base, p0, len);
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc,
                                      int B, int N, int heads, int d_k, int d_down, int w,
                                      int cap, void* h_D_cache, void* K_win, void* V_win,
                                      hipStream_t s) {
-  {
-    const size_t chunks = (size_t)B * N * (d_down / 8);
-    size_t blocks = (chunks + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(latent_cast_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const f16*)h_D, (bf16*)h_D_cache, B, N, d_down, cap);
-  }
-  if (w > 0) {
-    const int j_lo = N > w ? N - w : 0;
-    const dim3 grid(B * heads, (N - j_lo + 63) / 64);
-    if (d_k == 64)
-      hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, (const f16*)K_loc,
-                         (const f16*)V_loc, (bf16*)K_win, (bf16*)V_win, N, w, j_lo);
-    else
-      hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, (const f16*)K_loc,
-                         (const f16*)V_loc, (bf16*)K_win, (bf16*)V_win, N, w, j_lo);
-  }
-  return hipGetLastError();
+  hipError_t e = launch_latent_cast(h_D, B, N, d_down, cap, 0, h_D_cache, s);
+  if (e == hipSuccess)
+    e = launch_ring_fill(K_loc, V_loc, B, heads, d_k, N, 0, w, K_win, V_win, s);
+  return e;
 }
 
 }  // namespace dar

@@ -296,6 +296,167 @@ dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void
                                               cap, h_D_cache, K_win, V_win, stream));
 }
 
+dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q, const void* W_K,
+                             const void* W_V, const void* W_upK, const void* W_upV, int B, int C,
+                             int d, int d_down, int heads, int d_k, int p0, int w, int cap,
+                             float rope_base, dar_dtype dtype, void* h_D_cache, void* K_win,
+                             void* V_win, void* o, void* workspace, size_t* workspace_bytes,
+                             hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || C < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || p0 < 0 ||
+      w < 0 || cap < 1 || (long)p0 + C > cap || !(rope_base > 1.f) || workspace_bytes == nullptr)
+    return DAR_ERR_INVALID_ARG;
+  const void* need[] = {h, W_down, W_Q, W_K, W_V, W_upK, W_upV, h_D_cache, o};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k;
+  const Span ins[7] = {{h, 2 * (size_t)B * C * d},       {W_down, 2 * (size_t)d * d_down},
+                       {W_Q, 2 * (size_t)d * hd},         {W_K, 2 * (size_t)d * hd},
+                       {W_V, 2 * (size_t)d * hd},         {W_upK, 2 * (size_t)d_down * hd},
+                       {W_upV, 2 * (size_t)d_down * hd}};
+  const Span outs[4] = {{h_D_cache, 2 * (size_t)B * cap * d_down},
+                        {w > 0 ? K_win : nullptr, 2 * (size_t)B * w * hd},
+                        {w > 0 ? V_win : nullptr, 2 * (size_t)B * w * hd},
+                        {o, 2 * (size_t)B * C * hd}};
+  if (!disjoint(outs, 4, ins, 7)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
+    return DAR_ERR_UNSUPPORTED;
+
+  // Positions: the chunk is p0 .. N-1.  Global keys 0 .. N-1 are rebuilt from
+  // the latents; local keys that a chunk query can use are loc0 .. N-1
+  // (the ring's p0-w+1 .. p0-1, then the chunk's own).
+  const int N = p0 + C;
+  const int loc0 = w > 0 ? std::max(0, p0 - (w - 1)) : N;
+  const int nloc = N - loc0;
+  const size_t rope_bytes = rope_table_bytes(d_k, N - 1);
+  const size_t q_bytes = round256(2 * (size_t)B * hd * C);
+  const size_t hdc_bytes = round256(2 * (size_t)B * C * d_down);
+  const size_t glob_bytes = round256(2 * (size_t)B * hd * N);
+  const size_t loc_bytes = round256(2 * (size_t)B * hd * nloc);
+  const size_t need_bytes = rope_bytes + q_bytes + hdc_bytes + 2 * glob_bytes + 2 * loc_bytes;
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& sp : ins)
+      if (overlap(ws, sp)) return DAR_ERR_INVALID_ARG;
+    for (const Span& sp : outs)
+      if (overlap(ws, sp)) return DAR_ERR_INVALID_ARG;
+  }
+  char* wsp = (char*)workspace;
+  float2* lo = (float2*)wsp;
+  float2* hi = lo + 64 * (d_k / 2);
+  char* cur = wsp + rope_bytes;
+  void* Qc = cur;
+  cur += q_bytes;
+  void* hDc = cur;
+  cur += hdc_bytes;
+  void* Kg = cur;
+  cur += glob_bytes;
+  void* Vg = cur;
+  cur += glob_bytes;
+  void* Kl = cur;
+  cur += loc_bytes;
+  void* Vl = cur;
+  const RopeTab rope{lo, hi, d_k / 2};
+
+  hipError_t e = launch_rope_tables(lo, hi, d_k, N - 1, rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  // 1. the chunk's projections: q, local k / v (after the ring's rows of the
+  //    local arrays), h^D (fp16, then into the latent cache)
+  GemmProblem g1{};
+  g1.A = h;
+  g1.M = B * C;
+  g1.K = d;
+  g1.a_type = kBF16;
+  g1.b_type = kBF16;
+  g1.out_type = kF16;
+  g1.n_seq = C;
+  g1.heads = heads;
+  g1.d_k = d_k;
+  g1.pos0 = p0;
+  g1.rope = rope;
+  int ns = 0;
+  g1.seg[ns++] = GemmSeg{W_Q, Qc, (int)hd, kHead, 1};
+  if (w > 0) {
+    g1.seg[ns++] = GemmSeg{W_K, Kl, (int)hd, kHead, 1, nloc, p0 - loc0};
+    g1.seg[ns++] = GemmSeg{W_V, Vl, (int)hd, kHeadT, 0, nloc, p0 - loc0};
+  }
+  g1.seg[ns++] = GemmSeg{W_down, hDc, d_down, kRowMajor, 0};
+  g1.nseg = ns;
+  e = launch_project_gemm(g1, dtype, stream);
+  if (e == hipSuccess) e = launch_latent_cast(hDc, B, C, d_down, cap, p0, h_D_cache, stream);
+  // 2. the prefix's ring rows into the local arrays
+  if (e == hipSuccess)
+    e = launch_ring_to_local(K_win, V_win, B, heads, d_k, w, loc0, p0, nloc, Kl, Vl, stream);
+  // 3. global keys / values of the prefix from the latent cache (per sequence:
+  //    the cache rows are cap apart), then of the chunk from its fp16 h^D
+  for (int b = 0; b < B && p0 > 0 && e == hipSuccess; ++b) {
+    GemmProblem g2{};
+    g2.A = (const char*)h_D_cache + 2 * (size_t)b * cap * d_down;
+    g2.M = p0;
+    g2.K = d_down;
+    g2.a_type = kBF16;
+    g2.b_type = kBF16;
+    g2.out_type = kF16;
+    g2.n_seq = p0;
+    g2.heads = heads;
+    g2.d_k = d_k;
+    g2.pos0 = 0;
+    g2.rope = rope;
+    g2.nseg = 2;
+    g2.seg[0] = GemmSeg{W_upK, (char*)Kg + 2 * (size_t)b * hd * N, (int)hd, kHead, 1, N, 0};
+    g2.seg[1] = GemmSeg{W_upV, (char*)Vg + 2 * (size_t)b * hd * N, (int)hd, kHeadT, 0, N, 0};
+    e = launch_project_gemm(g2, dtype, stream);
+  }
+  if (e == hipSuccess) {
+    GemmProblem g3{};
+    g3.A = hDc;
+    g3.M = B * C;
+    g3.K = d_down;
+    g3.a_type = kF16;
+    g3.b_type = kBF16;
+    g3.out_type = kF16;
+    g3.n_seq = C;
+    g3.heads = heads;
+    g3.d_k = d_k;
+    g3.pos0 = p0;
+    g3.rope = rope;
+    g3.nseg = 2;
+    g3.seg[0] = GemmSeg{W_upK, Kg, (int)hd, kHead, 1, N, p0};
+    g3.seg[1] = GemmSeg{W_upV, Vg, (int)hd, kHeadT, 0, N, p0};
+    e = launch_project_gemm(g3, dtype, stream);
+  }
+  // 4. attention of the chunk's queries over positions 0 .. N-1
+  if (e == hipSuccess) {
+    PrefillProblem pp{};
+    pp.Q = Qc;
+    pp.K_loc = Kl;
+    pp.V_loc = Vl;
+    pp.K_glob = Kg;
+    pp.V_glob = Vg;
+    pp.o = o;
+    pp.B = B;
+    pp.N = N;
+    pp.H = heads;
+    pp.d_k = d_k;
+    pp.w = w;
+    pp.q0 = p0;
+    pp.loc0 = loc0;
+    e = launch_attn_prefill(pp, dtype, stream);
+  }
+  // 5. the ring moves on to positions N-w .. N-1
+  if (e == hipSuccess)
+    e = launch_ring_fill(Kl, Vl, B, heads, d_k, N, loc0, w, K_win, V_win, stream);
+  return hip_status(e);
+}
+
 dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
                            const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
                            int heads, int d_k, int d_down, int w, float rope_base,

@@ -142,10 +142,11 @@ struct GemmSeg {
   int width;       // number of output columns in this segment
   int kind;        // OutKind
   int rope;        // rotate (kind == kHead only)
-  // Output sequence addressing for kRowMajor / kHead: token (b, n) of the GEMM
-  // lands at sequence index n + seq_off of a sequence of length ld_seq
-  // (ld_seq = 0 means the GEMM's own n_seq and seq_off = 0).  This lets the
-  // decode append write one token into a ring slot or a latent-cache row.
+  // Output sequence addressing (every kind): token (b, n) of the GEMM lands at
+  // sequence index n + seq_off of a sequence of length ld_seq (ld_seq = 0
+  // means the GEMM's own n_seq and seq_off = 0).  This lets the decode append
+  // write one token into a ring slot or a latent-cache row, and a prefill
+  // chunk write its rows after the prefix's.
   int ld_seq = 0, seq_off = 0;
 };
 
@@ -173,6 +174,10 @@ struct PrefillProblem {
   const void *Q, *K_loc, *V_loc, *K_glob, *V_glob;
   void* o;
   int B, N, H, d_k, w;
+  // Chunk form (bf16 only): the queries are positions q0 .. N-1 (Q, o hold
+  // N - q0 rows), the global arrays hold positions 0 .. N-1 and the local
+  // arrays positions loc0 .. N-1.  A whole prefill has q0 = loc0 = 0.
+  int q0 = 0, loc0 = 0;
 };
 hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s);
 
@@ -184,6 +189,15 @@ struct DecodeProblem {
   void* ws;  // workspace after the rope tables
 };
 size_t decode_workspace_bytes(const DecodeProblem& p);
+// Pieces of the cache kernels (fp16 <-> bf16 conversions, positions relative to
+// array bases; see cache.hip).
+hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap, int row0,
+                              void* h_D_cache, hipStream_t s);
+hipError_t launch_ring_fill(const void* K, const void* Vt, int B, int heads, int d_k, int N,
+                            int base, int w, void* K_win, void* V_win, hipStream_t s);
+hipError_t launch_ring_to_local(const void* K_win, const void* V_win, int B, int heads, int d_k,
+                                int w, int base, int p0, int len, void* K, void* Vt,
+                                hipStream_t s);
 // Decode cache from prefill outputs (fp16 h_D, K_loc, V_loc^T -> bf16 cache).
 hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc,
                                      int B, int N, int heads, int d_k, int d_down, int w,

@@ -95,20 +95,22 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
     if (gcol >= width) return;
     const int head = gcol / D, t = gcol % D;
     const int grow0 = row0 + r0;
-    const int b0 = grow0 / Nq, n0 = grow0 % Nq;
+    const int ld = seg.ld_seq ? seg.ld_seq : Nq;
+    const int b0 = grow0 / Nq, n0 = grow0 % Nq, no0 = n0 + seg.seq_off;
     float v[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) v[i] = tile[(r0 + i) * EPI_P + c];
-    const bool fast = (grow0 + RPT <= M) && (n0 + RPT <= Nq) && ((n0 & 7) == 0) && ((Nq & 7) == 0);
+    const bool fast =
+        (grow0 + RPT <= M) && (n0 + RPT <= Nq) && ((no0 & 7) == 0) && ((ld & 7) == 0);
     if (fast) {
-      store_run<OutT, RPT>(out + (((size_t)b0 * H + head) * D + t) * Nq + n0, v);
+      store_run<OutT, RPT>(out + (((size_t)b0 * H + head) * D + t) * ld + no0, v);
     } else {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int grow = grow0 + i;
         if (grow >= M) break;
         const int b = grow / Nq, n = grow % Nq;
-        out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<OutT>(v[i]);
+        out[(((size_t)b * H + head) * D + t) * ld + n + seg.seq_off] = from_f32<OutT>(v[i]);
       }
     }
     return;
@@ -300,14 +302,15 @@ template <typename OutT, int D, int TP>
 __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, int col0,
                                            const GemmSeg& seg, const GemmProblem& p) {
   const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int ld = seg.ld_seq ? seg.ld_seq : Nq;  // output sequence stride
   OutT* out = (OutT*)seg.out;
   const int tc = tid & 7;  // chunk of 8 tokens within the 64-token run
 #pragma unroll
   for (int run = 0; run < 2; ++run) {
     const int grow0 = row0 + 128 * run + 64 * hf + 8 * tc;
     if (grow0 >= M) continue;
-    const int b0 = grow0 / Nq, n0 = grow0 % Nq;
-    const bool fast = (grow0 + 8 <= M) && (n0 + 8 <= Nq) && ((n0 & 7) == 0) && ((Nq & 7) == 0);
+    const int b0 = grow0 / Nq, n0 = grow0 % Nq, no0 = n0 + seg.seq_off;
+    const bool fast = (grow0 + 8 <= M) && (n0 + 8 <= Nq) && ((no0 & 7) == 0) && ((ld & 7) == 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = (tid >> 3) + 32 * k;
@@ -317,14 +320,14 @@ __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, 
       float v[8];
       read8(tile + c * TP + 64 * run + 8 * tc, v);
       if (fast) {
-        store_run<OutT, 8>(out + (((size_t)b0 * H + head) * D + t) * Nq + n0, v);
+        store_run<OutT, 8>(out + (((size_t)b0 * H + head) * D + t) * ld + no0, v);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int grow = grow0 + i;
           if (grow >= M) break;
           const int b = grow / Nq, n = grow % Nq;
-          out[(((size_t)b * H + head) * D + t) * Nq + n] = from_f32<OutT>(v[i]);
+          out[(((size_t)b * H + head) * D + t) * ld + n + seg.seq_off] = from_f32<OutT>(v[i]);
         }
       }
     }

@@ -152,6 +152,38 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
                              size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * dar_prefill_chunk -- prefill the next C tokens of every sequence over the
+ * mixed cache, and extend the cache.
+ *
+ * The chunk holds positions p0 .. p0+C-1 (N = p0 + C); its queries attend to
+ * every position j <= i as in Eqs. (3)-(4): the chunk's own keys/values from
+ * its projections, the prefix's through the cache the way decode reads it --
+ * local pairs (i - j < w) from the ring, global pairs from the latents,
+ * k_j = RoPE_j(h^D_j W_upK), v_j = h^D_j W_upV (Eqs. 2-3 with the fold).
+ * Splitting a prompt into chunks therefore gives the rows of the whole
+ * prefill (up to the bf16 rounding of the cache).
+ *   h       [B, C, d]                   the chunk's hidden states (bf16)
+ *   W_down, W_Q, W_K, W_V               column-major, as for dar_project
+ *   W_upK, W_upV [d_down x heads*d_k]   folded weights (dar_fold)
+ * Cache (bf16, updated in place; the layout of dar_cache_from_prefill):
+ *   h_D_cache [B, cap, d_down]   rows 0 .. p0-1 read, rows p0 .. N-1 written
+ *                                (cap >= N)
+ *   K_win, V_win [B, heads, w, d_k]  positions max(0,p0-w) .. p0-1 read; on
+ *                                return they hold positions max(0,N-w) .. N-1
+ *                                (slot = position mod w; NULL when w = 0)
+ *   o [B, C, heads*d_k]           the chunk's output rows (bf16)
+ * Start from an empty cache with p0 = 0.  The workspace (query with NULL)
+ * holds the chunk's projections and the prefix's rebuilt global keys and
+ * values (O(B heads d_k N) fp16).  DAR_BF16 only; limits as dar_project.
+ */
+dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q, const void* W_K,
+                             const void* W_V, const void* W_upK, const void* W_upV, int B, int C,
+                             int d, int d_down, int heads, int d_k, int p0, int w, int cap,
+                             float rope_base, dar_dtype dtype, void* h_D_cache, void* K_win,
+                             void* V_win, void* o, void* workspace, size_t* workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * dar_cache_from_prefill -- the decode cache of a prefilled prompt.
  *
  * After a prompt of N tokens is prefilled, generation keeps the latent h^D of

@@ -205,3 +205,33 @@ def cache(**kw):
 ])
 def test_cache_from_prefill_rejects(kw, code):
     assert cache(**kw) == code
+
+
+def chunk(**kw):
+    a = dict(B=2, C=100, d=256, d_down=64, heads=4, d_k=64, p0=300, w=64, cap=512, base=10000.0,
+             dtype=1, ring=True, o=F(10), ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    f = [F(i) for i in range(10)]
+    st = dar.lib().dar_prefill_chunk(*f[:7], a["B"], a["C"], a["d"], a["d_down"], a["heads"],
+                                     a["d_k"], a["p0"], a["w"], a["cap"], a["base"], a["dtype"],
+                                     f[7], f[8] if a["ring"] else None,
+                                     f[9] if a["ring"] else None, a["o"], a["ws"],
+                                     ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_chunk_size_query_and_rejects():
+    st, n = chunk()
+    assert st == OK and n > 0
+    assert chunk(p0=400)[0] == OK and chunk(p0=400)[1] > n   # longer prefix, more to rebuild
+    assert chunk(w=0, ring=False)[0] == OK                   # no window: no ring needed
+    assert chunk(p0=450)[0] == INVALID                       # p0 + C beyond the cache
+    assert chunk(p0=-1)[0] == INVALID
+    assert chunk(C=0)[0] == INVALID
+    assert chunk(ring=False)[0] == INVALID                   # w > 0 needs the ring
+    assert chunk(o=F(0))[0] == INVALID                       # output aliases an input
+    assert chunk(o=F(7))[0] == INVALID                       # output aliases the cache
+    assert chunk(dtype=0)[0] == UNSUP
+    assert chunk(d_k=96)[0] == UNSUP
+    assert chunk(ws=F(20), wsb=n - 1)[0] == WS

@@ -227,3 +227,43 @@ def test_prefill_cache_append_decode_matches_prefill_row(N, w, d_k, dd):
     err = max_err(host(o), ref[:, N])
     log("  prefill -> cache -> append -> decode vs prefill row %d: err %.3g" % (N, err))
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunks,w,d_k,dd,H", [
+    ((150, 200, 130), 100, 64, 64, 4),     # window shorter than a chunk
+    ((100, 64, 250), 300, 128, 128, 2),    # window longer than the prefix
+    ((60, 1, 70), 16, 64, 32, 4),          # a one-token chunk
+    ((128, 100), 0, 64, 64, 4),            # no window: every pair global
+])
+def test_chunked_prefill_matches_prefill_rows(chunks, w, d_k, dd, H):
+    """A prompt prefilled chunk by chunk over the mixed cache gives every row of
+    the oracle's prefill over the whole prompt; decoding the next token after
+    the last chunk gives the oracle's next row."""
+    B, d = 2, 256
+    N = sum(chunks)
+    inp = prefill_case(B, N + 1, d, H, d_k, dd, "bf16", seed=900 + N + w)
+    W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    h = dev(inp["h"], "bf16")
+    cap = N + 1
+    Lc = torch.zeros((B, cap, dd), dtype=torch.bfloat16, device="cuda")
+    Kw = torch.zeros((B, H, max(w, 1), d_k), dtype=torch.bfloat16, device="cuda") if w else None
+    Vw = torch.zeros((B, H, max(w, 1), d_k), dtype=torch.bfloat16, device="cuda") if w else None
+    ref, _, _ = oracle.prefill(inp, H, d_k, w)
+    p0 = 0
+    for C in chunks:
+        o = dar.dar_prefill_chunk(h[:, p0:p0 + C].contiguous(), W["W_down"], W["W_Q"], W["W_K"],
+                                  W["W_V"], Wk, Wv, H, d_k, p0, Lc, Kw, Vw, w)
+        torch.cuda.synchronize()
+        err = max_err(host(o), ref[:, p0:p0 + C])
+        log("  chunk p0=%d C=%d max err %.3g" % (p0, C, err))
+        assert err <= TOL["bf16"]
+        p0 += C
+    q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
+    dar.dar_decode_append(h[:, N].contiguous(), W["W_down"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                          N, q, Kw, Vw, Lc)
+    od = dar.dar_attn_decode(q, Kw, Vw, Lc, Wk, Wv, N + 1, w)
+    torch.cuda.synchronize()
+    err = max_err(host(od), ref[:, N])
+    log("  decode after the chunks: max err %.3g" % err)
+    assert err <= TOL["bf16"]
