@@ -183,6 +183,49 @@ def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
     return wall, ev, graph_launch_ms(torch, proj), graph_launch_ms(torch, attn)
 
 
+def chunk_flops(B, C, p0, d, d_down):
+    """Algorithmic FLOP of one prefill chunk of C tokens after p0 cached ones:
+    the chunk's projections, the prefix's global keys/values rebuilt from the
+    latents (2 d_down d per token per key and value), and the chunk's queries
+    against every key at or before them (4 d per pair)."""
+    pairs = C * p0 + C * (C + 1) // 2
+    return (2.0 * B * C * (3 * d * d + 3 * d * d_down) + 4.0 * B * p0 * d * d_down
+            + 4.0 * B * d * pairs)
+
+
+def time_chunked(torch, dar, di, cfg, chunk, reps):
+    """The prompt of cfg prefilled in chunks of `chunk` tokens over the mixed
+    cache (each chunk: dar_prefill_chunk), timed as a whole with HIP events."""
+    B, N, d, H, d_k, w, d_down = cfg
+    inp, s = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=3000)
+    W = s["W"]
+    cache = torch.zeros((B, N, d_down), dtype=torch.bfloat16, device="cuda")
+    Kw = torch.zeros((B, H, w, d_k), dtype=torch.bfloat16, device="cuda")
+    Vw = torch.zeros_like(Kw)
+    hs = [s["h"][:, p0:p0 + chunk].contiguous() for p0 in range(0, N, chunk)]
+    o = torch.empty((B, chunk, H * d_k), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(dar.chunk_workspace_bytes(B, chunk, d, d_down, H, d_k, N - chunk, w, N),
+                         256), dtype=torch.uint8, device="cuda")
+
+    def run():
+        for i, hc in enumerate(hs):
+            dar.dar_prefill_chunk(hc, W["W_down"], W["W_Q"], W["W_K"], W["W_V"], s["Wk"],
+                                  s["Wv"], H, d_k, i * chunk, cache, Kw, Vw, w, o=o, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = sum(chunk_flops(B, chunk, p0, d, d_down) for p0 in range(0, N, chunk))
+    del inp, s, cache, Kw, Vw, hs, o, ws
+    return {"ms": ms, "TFLOP/s": flops / ms / 1e9, "chunks": N // chunk, "chunk": chunk}
+
+
 def cpu_baseline(oracle, inp, H, d_k, w, d_down, budget_s=10.0):
     """The fp64 oracle on the step's own input (all sequences, all heads),
     repeated until about budget_s seconds of host time have passed."""
@@ -394,6 +437,11 @@ def main():
                 log("%s: %.3f ms, %.1f TFLOP/s" % (name, ms3, (pf + af) / ms3 / 1e9))
                 del s3
             res["sweep"] = sweep
+            cfg1b = (4, 8192, 2048, 16, 128, 512, 512)
+            ch = time_chunked(torch, dar, di, cfg1b, 2048, max(2, args.steps // 8))
+            ch["workload"] = "1b prompt B4 N8192 in chunks of 2048 over the mixed cache"
+            res["chunked_prefill"] = ch
+            log("chunked prefill: %.3f ms, %.1f TFLOP/s" % (ch["ms"], ch["TFLOP/s"]))
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         log("decode: building the 32k-context cache")
