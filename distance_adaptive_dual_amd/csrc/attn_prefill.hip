@@ -424,7 +424,9 @@ __device__ __forceinline__ WavePass wave_pass_info(int j0, int src, int qw0, int
   return r;
 }
 
-template <int D>
+// CHUNK: queries start at p.q0 and the local arrays at p.loc0 (a prefill
+// chunk); otherwise both are 0 and compiled in as constants.
+template <int D, bool CHUNK>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(PrefillProblem p, int nQT, int nPair,
                                                           int remap, int paired) {
   __shared__ PassSmem<D> sm;
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
   const int b = bh / H, h = bh % H;
   // Positions: queries q0 .. N-1 (Q and o hold those rows only), keys 0 .. N-1
   // in the global arrays, keys loc0 .. N-1 in the local arrays.
-  const int q0 = p.q0, loc0 = p.loc0, nqr = N - q0, nloc = N - loc0;
+  const int q0 = CHUNK ? p.q0 : 0, loc0 = CHUNK ? p.loc0 : 0, nqr = N - q0, nloc = N - loc0;
   const f16* Qp = (const f16*)p.Q + (size_t)bh * nqr * D;
   const f16* Kg = (const f16*)p.K_glob + (size_t)bh * N * D;
   const f16* Kl = (const f16*)p.K_loc + (size_t)bh * nloc * D;
@@ -662,11 +664,15 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
     const int nPair = paired ? (nQT + 1) / 2 : nQT;
     const int remap = (BH % kNumXcd) == 0 ? 1 : 0;
     const dim3 grid(nPair * BH);
-    if (p.d_k == 64)
-      hipLaunchKernelGGL(attn_prefill_f16<64>, grid, dim3(256), 0, s, p, nQT, nPair, remap, paired);
-    else
-      hipLaunchKernelGGL(attn_prefill_f16<128>, grid, dim3(256), 0, s, p, nQT, nPair, remap,
-                         paired);
+    const bool chunk = p.q0 != 0 || p.loc0 != 0;
+#define DAR_ATTN(DV, CV) \
+  hipLaunchKernelGGL((attn_prefill_f16<DV, CV>), grid, dim3(256), 0, s, p, nQT, nPair, remap, paired)
+    if (p.d_k == 64) {
+      if (chunk) DAR_ATTN(64, true); else DAR_ATTN(64, false);
+    } else {
+      if (chunk) DAR_ATTN(128, true); else DAR_ATTN(128, false);
+    }
+#undef DAR_ATTN
   } else {
     const dim3 grid((p.N + FQ - 1) / FQ, p.H, p.B);
     if (p.d_k == 64)
