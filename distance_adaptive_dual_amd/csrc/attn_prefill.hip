@@ -466,6 +466,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
   auto src_len = [&](int s) { return s ? nloc : N; };
   auto src_rel = [&](int s, int j0) { return s ? j0 - loc0 : j0; };
   auto src_vec = [&](int s, int j0) {
+    if constexpr (!CHUNK) return (N % 8) == 0 && j0 + KT <= N;  // tiles start at multiples of 64
     const int len = src_len(s), jr = src_rel(s, j0);
     return (len % 8) == 0 && (jr & 7) == 0 && jr >= 0 && jr + KT <= len;
   };
@@ -563,7 +564,11 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     if (qi < N) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const float inv = 1.f / l_tot;
-      bf16* out = (bf16*)p.o + ((size_t)b * nqr + (qi - q0)) * (size_t)(H * D) + (size_t)h * D;
+      // the row index is formed here (the empty asm keeps the compiler from
+      // computing the 64-bit address before the pass loop and holding it)
+      int qr = qi - q0;
+      __asm__ volatile("" : "+v"(qr));
+      bf16* out = (bf16*)p.o + ((size_t)b * nqr + qr) * (size_t)(H * D) + (size_t)h * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
