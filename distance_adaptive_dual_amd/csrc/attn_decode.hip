@@ -61,7 +61,7 @@ DecodeGeom geom(const DecodeProblem& p) {
   DecodeGeom g{};
   const long pp = (long)p.ctx - 1;
   g.n_glob = (int)(pp - p.w + 1 > 0 ? pp - p.w + 1 : 0);
-  g.heads_per_wg = NWAVE * 64 / p.d_k;
+  g.heads_per_wg = NWAVE * 64 / p.d_k / (p.d_down > 256 ? 2 : 1);
   g.n_hg = (p.H + g.heads_per_wg - 1) / g.heads_per_wg;
   const int blocks = (g.n_glob + TB - 1) / TB;
   int want = TARGET_WG / (p.B * g.n_hg);
@@ -191,7 +191,10 @@ template <int D, int KS>
 __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeGeom g,
                                                     float* part_win) {
   using S = LatentSmem<D, KS>;
-  constexpr int DD = S::DD, LP = S::LP, HPW = NWAVE * 64 / D, WPH = D / 64, HALF = D / 2;
+  // NS: slices of d_down per frequency block (a wave holds the folded rows of
+  // 32 frequencies over d_down / NS latent dims: at most 128 VGPRs).
+  constexpr int DD = S::DD, LP = S::LP, WPH = D / 64, HALF = D / 2;
+  constexpr int NS = KS > 16 ? 2 : 1, KSW = KS / NS, WPHS = WPH * NS, HPW = NWAVE / WPHS;
   union Smem {
     S lat;
     WindowSmem<D> win;
@@ -215,7 +218,8 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const int hl = wave / WPH, tb = wave % WPH;
+  // wave -> head hl of the group, frequency block tb, d_down slice sl
+  const int hl = wave / WPHS, wih = wave % WPHS, tb = wih / NS, sl = wih % NS;
   const int head = hg * HPW + hl;
   const bool head_ok = head < p.H;
 
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 
   // Query-folded weight rows (MFMA A operand): row t = 32 tb + lr of this
   // lane and its partner t + D/2; scores come out in base-2 logits.
-  bf16x8 gf[2][KS];
+  bf16x8 gf[2][KSW];
   {
     const bf16* Wk = (const bf16*)p.W_upK;
     const int hh = head_ok ? head : 0;
@@ -235,10 +239,10 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     const bf16* qp = (const bf16*)p.q + ((size_t)b * p.H + hh) * D;
     const float scl = kLog2e / sqrtf((float)D);
     const float qa = (float)qp[t] * scl, qb = (float)qp[t + HALF] * scl;
-    const bf16* r0 = Wk + (size_t)(hh * D + t) * DD + 8 * lg;
+    const bf16* r0 = Wk + (size_t)(hh * D + t) * DD + 16 * KSW * sl + 8 * lg;
     const bf16* r1 = r0 + (size_t)HALF * DD;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KSW; ++ks) {
       const bf16x8 w0 = *(const bf16x8*)(r0 + 16 * ks), w1 = *(const bf16x8*)(r1 + 16 * ks);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     }
   };
 
-  // softmax state, kept by the tb == 0 wave of each head (lanes 0..31 own tokens)
+  // softmax state, kept by the first wave of each head (lanes 0..31 own tokens)
   float m_ref = kNegBig, l_lane = 0.f;
   constexpr int NB = DD / 16;
   constexpr int NB_PER_WAVE = (NB + NWAVE - 1) / NWAVE;
@@ -309,14 +313,14 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     if (blk + 1 < nblk) load_blk(blk + 1);
 
     // h^D . [alpha | beta] for 32 tokens (lane column lr)
-    const bf16* lrow = &sm.lat[buf][lr * LP + 8 * lg];
+    const bf16* lrow = &sm.lat[buf][lr * LP + 16 * KSW * sl + 8 * lg];
     f32x16 kc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) kc[mb][r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KSW; ++ks) {
       const bf16x8 lf = *(const bf16x8*)(lrow + 16 * ks);
       kc[0] = mfma32x32x16(gf[0][ks], lf, kc[0]);
       kc[1] = mfma32x32x16(gf[1][ks], lf, kc[1]);
@@ -338,11 +342,12 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     __syncthreads();  // B1: partial scores visible; lat[buf ^ 1] free
 
     if (blk + 1 < nblk) store_blk(buf ^ 1);
-    if (tb == 0 && wave < NWAVE) {
-      // score of token j0 + lr for head hl (both lane halves hold it)
+    if (wih == 0) {
+      // score of token j0 + lr for head hl (both lane halves hold it): the
+      // partial sums of the head's WPHS waves
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < WPH; ++i) s += sm.sc[buf][wave + i][lr];
+      for (int i = 0; i < WPHS; ++i) s += sm.sc[buf][wave + i][lr];
       const bool ok = head_ok && (j0 + lr < j_end);
       s = ok ? s : -INFINITY;
       float al = 1.f;
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 
   // partials: part[((b*H + head)*n_chunks + chunk)] = {m, l, acc[d_down]}
   float* part = (float*)p.ws;
-  if (tb == 0) {
+  if (wih == 0) {
     float l = l_lane;
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) l += __shfl_xor(l, off);
@@ -510,10 +515,12 @@ hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
   DAR_LAT(64, 4)
   DAR_LAT(64, 8)
   DAR_LAT(64, 16)
+  DAR_LAT(64, 32)
   DAR_LAT(128, 2)
   DAR_LAT(128, 4)
   DAR_LAT(128, 8)
   DAR_LAT(128, 16)
+  DAR_LAT(128, 32)
 #undef DAR_LAT
   if (e != hipSuccess) return e;
   if (p.d_k == 64)
@@ -527,7 +534,8 @@ hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
 
 bool decode_supported(int d_k, int d_down) {
   const int KS = d_down / 16;
-  return (d_k == 64 || d_k == 128) && d_down % 16 == 0 && (KS == 2 || KS == 4 || KS == 8 || KS == 16);
+  return (d_k == 64 || d_k == 128) && d_down % 16 == 0 &&
+         (KS == 2 || KS == 4 || KS == 8 || KS == 16 || KS == 32);
 }
 
 }  // namespace dar

@@ -223,7 +223,8 @@ dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void
  *   o      [B, heads*d_k]
  * Global keys are rebuilt as RoPE_j(h^D_j W_upK); values are accumulated in
  * latent space and lifted once: sum_j p_j h^D_j W_upV = (sum_j p_j h^D_j) W_upV.
- * bf16 only (fp32 returns DAR_ERR_UNSUPPORTED).
+ * bf16 only (fp32 returns DAR_ERR_UNSUPPORTED); d_down in {32, 64, 128, 256, 512}
+ * (others return DAR_ERR_UNSUPPORTED).
  */
 dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
                            const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,

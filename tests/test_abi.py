@@ -120,6 +120,8 @@ def test_decode_size_query_and_rejects():
     assert decode(w=-1)[0] == INVALID
     assert decode(dtype=0)[0] == UNSUP          # fp32 decode is not provided
     assert decode(d_down=96)[0] == UNSUP
+    assert decode(d_down=512)[0] == OK          # two latent slices per frequency block
+    assert decode(d_down=1024)[0] == UNSUP
     assert decode(w=0, K_win=None, V_win=None)[0] == OK
     assert decode(ws=F(20), wsb=n - 1)[0] == WS
 

@@ -33,6 +33,8 @@ def run_decode(inp, ctx, w, H, d_k):
     (2, 1, 128, 2, 64, 64, 4),          # first token
     (1, 65, 512, 8, 64, 256, 64),       # exactly one latent token
     (2, 2000, 512, 16, 128, 256, 100),  # 16 heads (several head groups)
+    (2, 3000, 512, 4, 128, 512, 256),   # d_down 512: two latent slices per frequency block
+    (2, 1500, 256, 4, 64, 512, 64),     # d_down 512 with 64-wide heads
 ])
 def test_decode_small(B, ctx, d, H, d_k, dd, w):
     inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=10 * ctx + w)
