@@ -84,8 +84,10 @@ template <int D, int KS>
 struct LatentSmem {
   static constexpr int DD = KS * 16;   // d_down
   static constexpr int LP = DD + 8;    // bf16 per latent row (16 B pad)
-  bf16 lat[2][TB * LP];                // latent blocks (double buffer)
-  float2 step[D / 2];                  // (cos, sin)(32 theta_t): one block forward
+  static constexpr int NBUF = KS <= 16 ? 4 : 2;  // latent ring depth
+  static constexpr int CP = D / 2 + 2; // float2 per cos/sin row (16 B pad)
+  bf16 lat[NBUF][TB * LP];             // latent blocks
+  float2 cs[2][TB * CP];               // (cos, sin)(j theta_t) of a block, [token][t]
   float sc[2][NWAVE][TB];              // per-wave partial scores
   bf16 pm[2][16][TB + 8];              // probabilities, rows = heads of the group
   float alpha[2][16];                  // per-head rescale of this block
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   using S = LatentSmem<D, KS>;
   // NS: slices of d_down per frequency block (a wave holds the folded rows of
   // 32 frequencies over d_down / NS latent dims: at most 128 VGPRs).
-  constexpr int DD = S::DD, LP = S::LP, WPH = D / 64, HALF = D / 2;
+  constexpr int DD = S::DD, LP = S::LP, NBUF = S::NBUF, CP = S::CP, WPH = D / 64, HALF = D / 2;
   constexpr int NS = KS > 16 ? 2 : 1, KSW = KS / NS, WPHS = WPH * NS, HPW = NWAVE / WPHS;
   union Smem {
     S lat;
@@ -227,8 +229,6 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   const int j_end = min(g.n_glob, j_begin + g.chunk_len);
   const int nblk = j_end > j_begin ? (j_end - j_begin + TB - 1) / TB : 0;
 
-  for (int e = tid; e < HALF; e += 512) sm.step[e] = p.rope.lo[32 * HALF + e];
-
   // Query-folded weight rows (MFMA A operand): row t = 32 tb + lr of this
   // lane and its partner t + D/2; scores come out in base-2 logits.
   bf16x8 gf[2][KSW];
@@ -252,19 +252,26 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       }
     }
   }
-  // cos/sin(pos theta_t') of this lane's token for its 16 output frequencies
-  // t' = 32 tb + 8 (r/4) + 4 lg + r%4
-  float cs_c[16], cs_s[16];
-  {
-    const int pos = j_begin + lr;
+  // cos/sin(j theta_t) of the current block go through LDS, shared by every
+  // wave: thread tid carries frequency t = tid % (D/2) for NE tokens of the
+  // block and advances them by one complex multiply with (cos, sin)(32 theta_t)
+  // per block, starting from the fp64 tables at the chunk's first position.
+  constexpr int NE = TB * HALF / 512, TSTEP = 512 / HALF;
+  const int ct = tid % HALF, ctok = tid / HALF;
+  const float2 cstep = p.rope.lo[32 * HALF + ct];
+  float2 cst[NE];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * tb + 8 * (r >> 2) + 4 * lg + (r & 3);
-      const float2 v = rope_cs(p.rope, pos, t);
-      cs_c[r] = v.x;
-      cs_s[r] = v.y;
+  for (int i = 0; i < NE; ++i) cst[i] = rope_cs(p.rope, j_begin + ctok + TSTEP * i, ct);
+  // table of the next block into cs[buf]; the state moves one block on
+  auto put_cs = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      sm.cs[buf][(ctok + TSTEP * i) * CP + ct] = cst[i];
+      const float c = cst[i].x * cstep.x - cst[i].y * cstep.y;
+      cst[i].y = cst[i].x * cstep.y + cst[i].y * cstep.x;
+      cst[i].x = c;
     }
-  }
+  };
 
   const bf16* Lb = (const bf16*)p.h_D + (size_t)b * p.cap * DD;
   constexpr int NCH = TB * DD / 8;
@@ -302,18 +309,68 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 #pragma unroll
   for (int i = 0; i < NB_PER_WAVE; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nblk > 0) {
-    load_blk(0);
-    store_blk(0);
-  }
+  // acc[head, dims] = alpha * acc + P L for block `blk` (16x16x32 MFMA, K = the
+  // 32 tokens).  Contraction slot c of lane group kg is token 8*(c/2) + 2*kg +
+  // c%2: both operands use that order, and the four groups then read latent
+  // rows two apart, which fall in disjoint LDS banks.
+  auto accumulate = [&](int blk) {
+    const int pb = blk & 1;
+    const bf16* L = sm.lat[blk % NBUF];
+#pragma unroll
+    for (int i = 0; i < NB_PER_WAVE; ++i) {
+      const int nb = wave + NWAVE * i;
+      if (nb < NB) {
+        const int row = lane & 15, kg = lane >> 4;
+        bf16x8 af;
+        if (row < HPW) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t two = *(const uint32_t*)(&sm.pm[pb][row][8 * m + 2 * kg]);
+            af[2 * m] = __builtin_bit_cast(bf16, (uint16_t)(two & 0xffffu));
+            af[2 * m + 1] = __builtin_bit_cast(bf16, (uint16_t)(two >> 16));
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) af[c] = (bf16)0.f;
+        }
+        bf16x8 bfr;
+        const int n = nb * 16 + row;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bfr[c] = L[(8 * (c >> 1) + 2 * kg + (c & 1)) * LP + n];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hrow = 4 * kg + r;
+          acc[i][r] *= (hrow < HPW) ? sm.alpha[pb][hrow] : 1.f;
+        }
+        acc[i] = mfma16x16x32(af, bfr, acc[i]);
+      }
+    }
+  };
+
+  // Block k lives in lat[k % NBUF] and is loaded AHEAD blocks early.  With a
+  // ring of four, its scores are formed in iteration k, its probabilities in
+  // iteration k after the barrier and its value sum in iteration k + 1, and
+  // one barrier per block orders all of it: barrier k publishes the partial
+  // scores of block k, the probabilities of block k - 1 and the cos/sin table
+  // of block k + 1, and frees lat[(k + 2) % 4] (last read by the value sum of
+  // block k - 2 in iteration k - 1).  With a ring of two (the widest latents,
+  // for LDS room) a second barrier precedes the value sum of block k itself.
+  constexpr int AHEAD = NBUF / 2;
+#pragma unroll
+  for (int k = 0; k < AHEAD; ++k)
+    if (k < nblk) {
+      load_blk(k);
+      store_blk(k);
+    }
+  put_cs(0);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
-    const int buf = blk & 1;
+    const int pb = blk & 1;
     const int j0 = j_begin + blk * TB;
-    if (blk + 1 < nblk) load_blk(blk + 1);
+    if (blk + AHEAD < nblk) load_blk(blk + AHEAD);
 
     // h^D . [alpha | beta] for 32 tokens (lane column lr)
-    const bf16* lrow = &sm.lat[buf][lr * LP + 16 * KSW * sl + 8 * lg];
+    const bf16* lrow = &sm.lat[blk % NBUF][lr * LP + 16 * KSW * sl + 8 * lg];
     f32x16 kc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -325,29 +382,30 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       kc[0] = mfma32x32x16(gf[0][ks], lf, kc[0]);
       kc[1] = mfma32x32x16(gf[1][ks], lf, kc[1]);
     }
+    // output register r holds frequency t = 32 tb + 8 (r/4) + 4 lg + r%4 of
+    // token j0 + lr: four consecutive frequencies per r/4, 32 bytes of the table
     float sp = 0.f;
+    const float2* crow = &sm.cs[pb][lr * CP + 32 * tb + 4 * lg];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sp = fmaf(cs_c[r], kc[0][r], fmaf(cs_s[r], kc[1][r], sp));
-    sp += __shfl_xor(sp, 32);
-    if (lg == 0) sm.sc[buf][wave][lr] = sp;
-    // advance cos/sin by 32 positions
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * tb + 8 * (r >> 2) + 4 * lg + (r & 3);
-      const float2 st = sm.step[t];
-      const float c = cs_c[r] * st.x - cs_s[r] * st.y;
-      cs_s[r] = cs_c[r] * st.y + cs_s[r] * st.x;
-      cs_c[r] = c;
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *(const f32x4*)(crow + 8 * g), y = *(const f32x4*)(crow + 8 * g + 2);
+      sp = fmaf(x[0], kc[0][4 * g], fmaf(x[1], kc[1][4 * g], sp));
+      sp = fmaf(x[2], kc[0][4 * g + 1], fmaf(x[3], kc[1][4 * g + 1], sp));
+      sp = fmaf(y[0], kc[0][4 * g + 2], fmaf(y[1], kc[1][4 * g + 2], sp));
+      sp = fmaf(y[2], kc[0][4 * g + 3], fmaf(y[3], kc[1][4 * g + 3], sp));
     }
-    __syncthreads();  // B1: partial scores visible; lat[buf ^ 1] free
+    sp += __shfl_xor(sp, 32);
+    if (lg == 0) sm.sc[pb][wave][lr] = sp;
+    put_cs(pb ^ 1);
+    __syncthreads();
 
-    if (blk + 1 < nblk) store_blk(buf ^ 1);
+    if (blk + AHEAD < nblk) store_blk((blk + AHEAD) % NBUF);
     if (wih == 0) {
       // score of token j0 + lr for head hl (both lane halves hold it): the
       // partial sums of the head's WPHS waves
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < WPHS; ++i) s += sm.sc[buf][wave + i][lr];
+      for (int i = 0; i < WPHS; ++i) s += sm.sc[pb][wave + i][lr];
       const bool ok = head_ok && (j0 + lr < j_end);
       s = ok ? s : -INFINITY;
       float al = 1.f;
@@ -364,46 +422,20 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       const bf16 eb = (bf16)e;
       if (lg == 0) {
         l_lane += (float)eb;  // the sum of exactly the probabilities used below
-        sm.pm[buf][hl][lr] = eb;
+        sm.pm[pb][hl][lr] = eb;
       }
-      if (lane == 0) sm.alpha[buf][hl] = al;
+      if (lane == 0) sm.alpha[pb][hl] = al;
     }
-    __syncthreads();  // B2: probabilities, rescale factors and lat[buf ^ 1] visible
-
-    // acc[head, dims] = alpha * acc + P L  (16x16x32 MFMA, K = the 32 tokens).
-    // Contraction slot c of lane group kg is token 8*(c/2) + 2*kg + c%2: both
-    // operands use that order, and the four groups then read latent rows two
-    // apart, which fall in disjoint LDS banks.
-#pragma unroll
-    for (int i = 0; i < NB_PER_WAVE; ++i) {
-      const int nb = wave + NWAVE * i;
-      if (nb < NB) {
-        const int row = lane & 15, kg = lane >> 4;
-        bf16x8 af;
-        if (row < HPW) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t two = *(const uint32_t*)(&sm.pm[buf][row][8 * m + 2 * kg]);
-            af[2 * m] = __builtin_bit_cast(bf16, (uint16_t)(two & 0xffffu));
-            af[2 * m + 1] = __builtin_bit_cast(bf16, (uint16_t)(two >> 16));
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) af[c] = (bf16)0.f;
-        }
-        bf16x8 bfr;
-        const int n = nb * 16 + row;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          bfr[c] = sm.lat[buf][(8 * (c >> 1) + 2 * kg + (c & 1)) * LP + n];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int hrow = 4 * kg + r;
-          acc[i][r] *= (hrow < HPW) ? sm.alpha[buf][hrow] : 1.f;
-        }
-        acc[i] = mfma16x16x32(af, bfr, acc[i]);
-      }
+    if constexpr (NBUF == 4) {
+      if (blk > 0) accumulate(blk - 1);
+    } else {
+      __syncthreads();  // probabilities of block blk and lat[(blk + 1) % 2] visible
+      accumulate(blk);
     }
+  }
+  if constexpr (NBUF == 4) {
+    __syncthreads();  // probabilities of the last block
+    if (nblk > 0) accumulate(nblk - 1);
   }
 
   // partials: part[((b*H + head)*n_chunks + chunk)] = {m, l, acc[d_down]}
