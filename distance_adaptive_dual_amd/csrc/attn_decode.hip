@@ -83,10 +83,13 @@ constexpr float kNegBig = -1e30f;
 template <int D, int KS>
 struct LatentSmem {
   static constexpr int DD = KS * 16;   // d_down
-  static constexpr int LP = DD + 8;    // bf16 per latent row (16 B pad)
-  static constexpr int NBUF = KS <= 16 ? 4 : 2;  // latent ring depth
+  static constexpr int NBUF = KS <= 16 ? 4 : 3;  // latent ring depth
   static constexpr int CP = D / 2 + 2; // float2 per cos/sin row (16 B pad)
-  bf16 lat[NBUF][TB * LP];             // latent blocks
+  // latent blocks [token][d_down], unpadded: 16-byte chunk c of token row r
+  // sits in slot c ^ (r & SWM), so that eight consecutive rows read at one
+  // logical chunk hit eight different bank groups
+  static constexpr int SWM = (2 * KS < 8 ? 2 * KS : 8) - 1;
+  bf16 lat[NBUF][TB * DD];
   float2 cs[2][TB * CP];               // (cos, sin)(j theta_t) of a block, [token][t]
   float sc[2][NWAVE][TB];              // per-wave partial scores
   bf16 pm[2][16][TB + 8];              // probabilities, rows = heads of the group
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   using S = LatentSmem<D, KS>;
   // NS: slices of d_down per frequency block (a wave holds the folded rows of
   // 32 frequencies over d_down / NS latent dims: at most 128 VGPRs).
-  constexpr int DD = S::DD, LP = S::LP, NBUF = S::NBUF, CP = S::CP, WPH = D / 64, HALF = D / 2;
+  constexpr int DD = S::DD, SWM = S::SWM, NBUF = S::NBUF, CP = S::CP, WPH = D / 64, HALF = D / 2;
   constexpr int NS = KS > 16 ? 2 : 1, KSW = KS / NS, WPHS = WPH * NS, HPW = NWAVE / WPHS;
   union Smem {
     S lat;
@@ -273,30 +276,25 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     }
   };
 
-  const bf16* Lb = (const bf16*)p.h_D + (size_t)b * p.cap * DD;
-  constexpr int NCH = TB * DD / 8;
-  constexpr int CPT = (NCH + 511) / 512;
-  u32x4 stg[CPT];
-  auto load_blk = [&](int blk) {
-    const int j0 = j_begin + blk * TB;
+  // Latent blocks go from HBM straight into LDS (buffer loads with an LDS
+  // destination, no registers): one load of 64 x 16 bytes fills 1 KB of a
+  // block, KS loads per block spread over the waves.  The buffer covers this
+  // chunk's rows only, so rows past j_end read as zeros.
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)p.h_D + ((size_t)b * p.cap + j_begin) * DD), (short)0,
+      (int)((size_t)(j_end > j_begin ? j_end - j_begin : 0) * DD * sizeof(bf16)), 0x00020000);
+  constexpr int CPR = 2 * KS;  // 16-byte chunks per latent row
+  auto issue_blk = [&](int blk) {
+    bf16* dst = sm.lat[blk % NBUF];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 512 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < NCH) {
-        const int row = c / (DD / 8), col = (c % (DD / 8)) * 8;
-        if (j0 + row < j_end) v = *(const u32x4*)(Lb + (size_t)(j0 + row) * DD + col);
-      }
-      stg[i] = v;
-    }
-  };
-  auto store_blk = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 512 * i;
-      if (c < NCH) {
-        const int row = c / (DD / 8), col = (c % (DD / 8)) * 8;
-        *(u32x4*)(&sm.lat[buf][row * LP + col]) = stg[i];
+    for (int i0 = 0; i0 < KS; i0 += NWAVE) {
+      const int i = i0 + wave;
+      if (KS % NWAVE == 0 || i < KS) {
+        const int row = (64 * i + lane) / CPR, slot = lane % CPR;
+        const int c = slot ^ (row & SWM);
+        const unsigned off = (unsigned)(((blk * TB + row) * DD + 8 * c) * sizeof(bf16));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            lrs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, off, 0, 0, 0);
       }
     }
   };
@@ -336,7 +334,12 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         bf16x8 bfr;
         const int n = nb * 16 + row;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) bfr[c] = L[(8 * (c >> 1) + 2 * kg + (c & 1)) * LP + n];
+        for (int c = 0; c < 8; ++c) {
+          // row & SWM depends on (kg, c % 2) only
+          const int row = 8 * (c >> 1) + 2 * kg + (c & 1);
+          const int colp = 8 * ((n >> 3) ^ ((2 * kg + (c & 1)) & SWM)) + (n & 7);
+          bfr[c] = L[row * DD + colp];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int hrow = 4 * kg + r;
@@ -347,30 +350,34 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     }
   };
 
-  // Block k lives in lat[k % NBUF] and is loaded AHEAD blocks early.  With a
-  // ring of four, its scores are formed in iteration k, its probabilities in
-  // iteration k after the barrier and its value sum in iteration k + 1, and
-  // one barrier per block orders all of it: barrier k publishes the partial
-  // scores of block k, the probabilities of block k - 1 and the cos/sin table
-  // of block k + 1, and frees lat[(k + 2) % 4] (last read by the value sum of
-  // block k - 2 in iteration k - 1).  With a ring of two (the widest latents,
-  // for LDS room) a second barrier precedes the value sum of block k itself.
-  constexpr int AHEAD = NBUF / 2;
-#pragma unroll
-  for (int k = 0; k < AHEAD; ++k)
-    if (k < nblk) {
-      load_blk(k);
-      store_blk(k);
-    }
+  // Block k lives in lat[k % NBUF].  Its loads are issued after barrier k - 2
+  // and waited for (each wave its own) just before barrier k - 1, so they
+  // have a whole block's work to land in.  With a ring of four, its scores
+  // are formed in iteration k, its probabilities in iteration k after the
+  // barrier and its value sum in iteration k + 1, and one barrier per block
+  // orders all of it: barrier k publishes the partial scores of block k, the
+  // probabilities of block k - 1, the cos/sin table of block k + 1 and the
+  // latents of block k + 1, and frees lat[(k + 2) % 4] (last read by the value
+  // sum of block k - 2 in iteration k - 1).  With a ring of three (the widest
+  // latents, for LDS room) a second barrier precedes the value sum of block k
+  // itself, and lat[(k + 2) % 3] (block k - 1) is free after barrier k.
+  if (nblk > 0) issue_blk(0);
+  if (nblk > 1) issue_blk(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   put_cs(0);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int pb = blk & 1;
     const int j0 = j_begin + blk * TB;
-    if (blk + AHEAD < nblk) load_blk(blk + AHEAD);
 
-    // h^D . [alpha | beta] for 32 tokens (lane column lr)
-    const bf16* lrow = &sm.lat[blk % NBUF][lr * LP + 16 * KSW * sl + 8 * lg];
+    // h^D . [alpha | beta] for 32 tokens (lane column lr): logical chunk
+    // 2 KSW sl + 8 (ks / 4) + (2 (ks % 4) + lg) of row lr; the swizzle only
+    // touches the low three bits, so four base addresses serve every ks
+    constexpr int NR = KSW < 4 ? KSW : 4;
+    const bf16* lb[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      lb[r] = sm.lat[blk % NBUF] + lr * DD + 16 * KSW * sl + 8 * ((2 * r + lg) ^ (lr & SWM));
     f32x16 kc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       for (int r = 0; r < 16; ++r) kc[mb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
-      const bf16x8 lf = *(const bf16x8*)(lrow + 16 * ks);
+      const bf16x8 lf = *(const bf16x8*)(lb[ks % NR] + 64 * (ks / NR));
       kc[0] = mfma32x32x16(gf[0][ks], lf, kc[0]);
       kc[1] = mfma32x32x16(gf[1][ks], lf, kc[1]);
     }
@@ -397,9 +404,10 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     sp += __shfl_xor(sp, 32);
     if (lg == 0) sm.sc[pb][wave][lr] = sp;
     put_cs(pb ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk + 1
     __syncthreads();
 
-    if (blk + AHEAD < nblk) store_blk((blk + AHEAD) % NBUF);
+    if (blk + 2 < nblk) issue_blk(blk + 2);
     if (wih == 0) {
       // score of token j0 + lr for head hl (both lane halves hold it): the
       // partial sums of the head's WPHS waves
