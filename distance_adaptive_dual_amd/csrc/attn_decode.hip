@@ -352,13 +352,11 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 
   // Block k lives in lat[k % NBUF].  Its loads are issued after barrier k - 2
   // and waited for (each wave its own) just before barrier k - 1, so they
-  // have a whole block's work to land in.  With a ring of four, its scores
-  // are formed in iteration k, its probabilities in iteration k after the
-  // barrier and its value sum in iteration k + 1, and one barrier per block
-  // orders all of it: barrier k publishes the partial scores of block k, the
+  // have a whole block's work to land in.  With a ring of four there is one
+  // barrier per block: barrier k publishes the partial scores of block k, the
   // probabilities of block k - 1, the cos/sin table of block k + 1 and the
-  // latents of block k + 1, and frees lat[(k + 2) % 4] (last read by the value
-  // sum of block k - 2 in iteration k - 1).  With a ring of three (the widest
+  // latents of block k + 1, and frees lat[(k + 2) % 4] (block k - 2, whose
+  // value sum ran before barrier k).  With a ring of three (the widest
   // latents, for LDS room) a second barrier precedes the value sum of block k
   // itself, and lat[(k + 2) % 3] (block k - 1) is free after barrier k.
   if (nblk > 0) issue_blk(0);
@@ -366,10 +364,10 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   put_cs(0);
   __syncthreads();
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int pb = blk & 1;
-    const int j0 = j_begin + blk * TB;
 
+  // Scores of block blk into sc[blk % 2]; cos/sin table of block blk + 1.
+  auto scores = [&](int blk) {
+    const int pb = blk & 1;
     // h^D . [alpha | beta] for 32 tokens (lane column lr): logical chunk
     // 2 KSW sl + 8 (ks / 4) + (2 (ks % 4) + lg) of row lr; the swizzle only
     // touches the low three bits, so four base addresses serve every ks
@@ -404,10 +402,12 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
     sp += __shfl_xor(sp, 32);
     if (lg == 0) sm.sc[pb][wave][lr] = sp;
     put_cs(pb ^ 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk + 1
-    __syncthreads();
-
-    if (blk + 2 < nblk) issue_blk(blk + 2);
+  };
+  // Probabilities of block blk (sc[blk % 2] -> pm, alpha), kept by the first
+  // wave of each head.
+  auto softmax = [&](int blk) {
+    const int pb = blk & 1;
+    const int j0 = j_begin + blk * TB;
     if (wih == 0) {
       // score of token j0 + lr for head hl (both lane halves hold it): the
       // partial sums of the head's WPHS waves
@@ -434,16 +434,46 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       }
       if (lane == 0) sm.alpha[pb][hl] = al;
     }
-    if constexpr (NBUF == 4) {
-      if (blk > 0) accumulate(blk - 1);
-    } else {
-      __syncthreads();  // probabilities of block blk and lat[(blk + 1) % 2] visible
+  };
+
+  if constexpr (NBUF == 4) {
+    // Iteration blk runs between barriers blk - 1 and blk: the loads of block
+    // blk + 1, the scores of block blk, the probabilities of block blk - 1 and
+    // the value sum of block blk - 2, in either order (each reads only what
+    // barrier blk - 1 published).  The waves of the upper half take the
+    // probabilities and value sum first, so the two waves that share a SIMD
+    // are out of phase: one issues MFMAs while the other runs VALU work.
+    const bool post_first = wave >= NWAVE / 2;
+    for (int blk = 0; blk < nblk; ++blk) {
+      if (blk > 0 && blk + 1 < nblk) issue_blk(blk + 1);
+      if (post_first && blk > 0) {
+        softmax(blk - 1);
+        if (blk > 1) accumulate(blk - 2);
+      }
+      scores(blk);
+      if (!post_first && blk > 0) {
+        softmax(blk - 1);
+        if (blk > 1) accumulate(blk - 2);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk + 1
+      __syncthreads();
+    }
+    if (nblk > 0) {
+      softmax(nblk - 1);
+      if (nblk > 1) accumulate(nblk - 2);
+      __syncthreads();  // probabilities of the last block
+      accumulate(nblk - 1);
+    }
+  } else {
+    for (int blk = 0; blk < nblk; ++blk) {
+      scores(blk);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block blk + 1
+      __syncthreads();
+      if (blk + 2 < nblk) issue_blk(blk + 2);
+      softmax(blk);
+      __syncthreads();  // probabilities of block blk visible
       accumulate(blk);
     }
-  }
-  if constexpr (NBUF == 4) {
-    __syncthreads();  // probabilities of the last block
-    if (nblk > 0) accumulate(nblk - 1);
   }
 
   // partials: part[((b*H + head)*n_chunks + chunk)] = {m, l, acc[d_down]}
