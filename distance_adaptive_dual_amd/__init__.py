@@ -26,7 +26,8 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
            "dar_attn_prefill", "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
-           "dar_attn_decode")
+           "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
+           "dar_attn_decode_varlen")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -66,6 +67,14 @@ def lib() -> ctypes.CDLL:
             _SZ, _P]
         L.dar_attn_decode.restype = _I
         L.dar_attn_decode.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P, _SZ, _P]
+        L.dar_cache_from_prefill_varlen.restype = _I
+        L.dar_cache_from_prefill_varlen.argtypes = [_P] * 3 + [_I, _I, _P] + [_I] * 6 + [_P] * 4
+        L.dar_decode_append_varlen.restype = _I
+        L.dar_decode_append_varlen.argtypes = [_P] * 5 + [_I] * 5 + [_P, _I, _I, ctypes.c_float,
+                                                                   _I] + [_P] * 5 + [_SZ, _P]
+        L.dar_attn_decode_varlen.restype = _I
+        L.dar_attn_decode_varlen.argtypes = [_P] * 6 + [_I, _P] + [_I] * 6 + [
+            ctypes.c_float, _I, _P, _P, _SZ, _P]
         _lib = L
     return _lib
 
@@ -245,6 +254,71 @@ def dar_cache_from_prefill(h_D, K_loc, V_loc, w: int, cap: int = None, h_D_cache
                                       _ptr(V_win) if w > 0 else None, _stream(stream))
     _check("dar_cache_from_prefill", st)
     return h_D_cache, K_win, V_win
+
+
+def _lens(t, B: int):
+    """A device int32 vector of B per-sequence lengths or positions."""
+    torch = _torch()
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != B:
+        raise ValueError("per-sequence lengths/positions must be an int32 vector of %d" % B)
+    return _ptr(t)
+
+
+def dar_cache_from_prefill_varlen(h_D, K_loc, V_loc, lens, w: int, cap: int = None,
+                                  h_D_cache=None, K_win=None, V_win=None, stream=None):
+    """dar_cache_from_prefill for a padded batch whose sequence b has lens[b]
+    tokens (lens: device int32 [B]).  Returns (h_D_cache, K_win, V_win)."""
+    torch = _torch()
+    B, N, d_down = h_D.shape
+    _, H, _, d_k = K_loc.shape
+    cap = N if cap is None else cap
+    kw = dict(dtype=torch.bfloat16, device=h_D.device)
+    if h_D_cache is None:
+        h_D_cache = torch.zeros((B, cap, d_down), **kw)
+    if w > 0 and K_win is None:
+        K_win = torch.zeros((B, H, w, d_k), **kw)
+    if w > 0 and V_win is None:
+        V_win = torch.zeros((B, H, w, d_k), **kw)
+    st = lib().dar_cache_from_prefill_varlen(
+        _ptr(h_D), _ptr(K_loc) if w > 0 else None, _ptr(V_loc) if w > 0 else None, B, N,
+        _lens(lens, B), H, d_k, d_down, int(w), int(h_D_cache.shape[1]), _dtype_code(h_D),
+        _ptr(h_D_cache), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None,
+        _stream(stream))
+    _check("dar_cache_from_prefill_varlen", st)
+    return h_D_cache, K_win, V_win
+
+
+def dar_decode_append_varlen(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos, q, K_win,
+                             V_win, h_D, rope_base: float = 10000.0, workspace=None,
+                             stream=None):
+    """dar_decode_append with sequence b's token at position pos[b] (device
+    int32 [B]).  Returns q."""
+    B, d = h.shape
+    d_down = W_down.shape[0]
+    w = K_win.shape[2] if K_win is not None else 0
+    cap = h_D.shape[1]
+    args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), B, d, d_down, heads, d_k,
+            _lens(pos, B), int(w), cap, float(rope_base), _dtype_code(h), _ptr(q),
+            _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D)]
+    _call_ws("dar_decode_append_varlen", lib().dar_decode_append_varlen, args, workspace, h,
+             stream)
+    return q
+
+
+def dar_attn_decode_varlen(q, K_win, V_win, h_D, W_upK, W_upV, ctx_lens, max_ctx: int, w: int,
+                           rope_base: float = 10000.0, o=None, workspace=None, stream=None):
+    """dar_attn_decode with sequence b's query at position ctx_lens[b] - 1
+    (device int32 [B], each in [1, max_ctx]).  Returns o [B, heads*d_k]."""
+    torch = _torch()
+    B, H, d_k = q.shape
+    cap, d_down = h_D.shape[1], h_D.shape[2]
+    if o is None:
+        o = torch.empty((B, H * d_k), dtype=q.dtype, device=q.device)
+    args = [_ptr(q), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D),
+            _ptr(W_upK), _ptr(W_upV), B, _lens(ctx_lens, B), int(max_ctx), cap, H, d_k, d_down,
+            int(w), float(rope_base), _dtype_code(q), _ptr(o)]
+    _call_ws("dar_attn_decode_varlen", lib().dar_attn_decode_varlen, args, workspace, q, stream)
+    return o
 
 
 def chunk_workspace_bytes(B, C, d, d_down, heads, d_k, p0, w, cap):

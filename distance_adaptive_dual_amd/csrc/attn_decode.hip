@@ -76,6 +76,14 @@ DecodeGeom geom(const DecodeProblem& p) {
   return g;
 }
 
+// Context length of sequence b (ragged batches read it from the device,
+// clamped to [1, ctx]).
+__device__ __forceinline__ int seq_ctx(const DecodeProblem& p, int b) {
+  if (p.ctx_lens == nullptr) return p.ctx;
+  const int c = p.ctx_lens[b];
+  return c < 1 ? 1 : (c > p.ctx ? p.ctx : c);
+}
+
 // --------------------------------------------------------------------------
 constexpr float kTau = 8.f;        // move the reference max only past 2^8 growth
 constexpr float kNegBig = -1e30f;
@@ -126,8 +134,8 @@ template <int D>
 __device__ void window_part(const DecodeProblem& p, float* part_win, int bh, WindowSmem<D>& sm) {
   constexpr int CK = WindowSmem<D>::CK, KP = WindowSmem<D>::KP, NT = 512;
   const int tid = threadIdx.x;
-  const long pp = (long)p.ctx - 1;
-  const int nw = (int)(pp + 1 < p.w ? pp + 1 : p.w);
+  const int ctx_b = seq_ctx(p, bh / p.H);
+  const int nw = ctx_b < p.w ? ctx_b : p.w;
   const float scl = kLog2e / sqrtf((float)D);
   const bf16* qp = (const bf16*)p.q + (size_t)bh * D;
   const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
@@ -229,7 +237,8 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   const bool head_ok = head < p.H;
 
   const int j_begin = chunk * g.chunk_len;
-  const int j_end = min(g.n_glob, j_begin + g.chunk_len);
+  const int n_glob_b = p.ctx_lens ? max(seq_ctx(p, b) - p.w, 0) : g.n_glob;
+  const int j_end = min(n_glob_b, j_begin + g.chunk_len);
   const int nblk = j_end > j_begin ? (j_end - j_begin + TB - 1) / TB : 0;
 
   // Query-folded weight rows (MFMA A operand): row t = 32 tb + lr of this

@@ -45,18 +45,28 @@ __global__ __launch_bounds__(256) void latent_cast_kernel(const f16* __restrict_
 // from arrays holding positions base .. N-1 (len = N - base rows):
 // K_win[b, h, j mod w, :] = bf16(K[b, h, j - base, :]) and
 // V_win[b, h, j mod w, :] = bf16(Vt[b, h, :, j - base]).
+// Ragged batches (lens != null, base 0): sequence b ends at lens[b] (clamped
+// to [1, N]) and its last min(w, lens[b]) positions are written.
 template <int D>
 __global__ __launch_bounds__(256) void ring_fill_kernel(const f16* __restrict__ Kl,
                                                         const f16* __restrict__ Vl,
                                                         bf16* __restrict__ Kw,
                                                         bf16* __restrict__ Vw, int N, int w,
-                                                        int j_lo, int base) {
+                                                        int j_lo, int base, int heads,
+                                                        const int* __restrict__ lens) {
   constexpr int TJ = 64, TP = TJ + 2;  // positions per tile; LDS pitch (f16)
   __shared__ f16 vt[D * TP];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int len = N - base;
-  const int j0 = j_lo + TJ * blockIdx.y;
-  const int nj = min(TJ, N - j0);
+  int n_end = N, lo = j_lo;
+  if (lens != nullptr) {
+    const int l = lens[bh / heads];
+    n_end = l < 1 ? 1 : (l > N ? N : l);
+    lo = max(n_end - w, base);
+  }
+  const int j0 = lo + TJ * blockIdx.y;
+  const int nj = min(TJ, n_end - j0);
+  if (nj <= 0) return;
   const f16* K = Kl + (size_t)bh * len * D;
   const f16* V = Vl + (size_t)bh * D * len;
   bf16* KW = Kw + (size_t)bh * w * D;
@@ -130,16 +140,18 @@ hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap
 }
 
 hipError_t launch_ring_fill(const void* K, const void* Vt, int B, int heads, int d_k, int N,
-                            int base, int w, void* K_win, void* V_win, hipStream_t s) {
+                            int base, int w, void* K_win, void* V_win, hipStream_t s,
+                            const int* lens) {
   const int j_lo = max(N - w, base);
   if (w <= 0 || j_lo >= N) return hipSuccess;
+  // a ragged sequence writes at most min(w, N - base) positions as well
   const dim3 grid(B * heads, (N - j_lo + 63) / 64);
   if (d_k == 64)
     hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, (const f16*)K,
-                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base);
+                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base, heads, lens);
   else
     hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, (const f16*)K,
-                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base);
+                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base, heads, lens);
   return hipGetLastError();
 }
 
@@ -160,10 +172,10 @@ hipError_t launch_ring_to_local(const void* K_win, const void* V_win, int B, int
 hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc,
                                      int B, int N, int heads, int d_k, int d_down, int w,
                                      int cap, void* h_D_cache, void* K_win, void* V_win,
-                                     hipStream_t s) {
+                                     hipStream_t s, const int* lens) {
   hipError_t e = launch_latent_cast(h_D, B, N, d_down, cap, 0, h_D_cache, s);
   if (e == hipSuccess)
-    e = launch_ring_fill(K_loc, V_loc, B, heads, d_k, N, 0, w, K_win, V_win, s);
+    e = launch_ring_fill(K_loc, V_loc, B, heads, d_k, N, 0, w, K_win, V_win, s, lens);
   return e;
 }
 

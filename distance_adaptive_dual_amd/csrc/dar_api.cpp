@@ -202,34 +202,40 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
   return hip_status(launch_attn_prefill(p, dtype, stream));
 }
 
-dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q, const void* W_K,
-                             const void* W_V, int B, int d, int d_down, int heads, int d_k,
-                             int pos, int w, int cap, float rope_base, dar_dtype dtype, void* q,
-                             void* K_win, void* V_win, void* h_D, void* workspace,
-                             size_t* workspace_bytes, hipStream_t stream) {
+// Decode append, uniform (pos_arr == nullptr: every sequence at position pos)
+// or ragged (pos_arr: device int32[B], sequence b at pos_arr[b] < cap).
+static dar_status decode_append_impl(const void* h, const void* W_down, const void* W_Q,
+                                     const void* W_K, const void* W_V, int B, int d, int d_down,
+                                     int heads, int d_k, int pos, const int* pos_arr, int w,
+                                     int cap, float rope_base, dar_dtype dtype, void* q,
+                                     void* K_win, void* V_win, void* h_D, void* workspace,
+                                     size_t* workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
   if (B < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || pos < 0 || w < 0 ||
       cap < 1)
     return DAR_ERR_INVALID_ARG;
   if (pos >= cap || !(rope_base > 1.0f)) return DAR_ERR_INVALID_ARG;
+  if (pos_arr != nullptr && ((uintptr_t)pos_arr & 3u)) return DAR_ERR_INVALID_ARG;
   const void* need[] = {h, W_down, W_Q, W_K, W_V, q, h_D};
   for (const void* ptr : need)
     if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
   if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
   const int hd = heads * d_k;
   const size_t es = elem_size(dtype);
-  const Span ins[5] = {{h, es * B * (size_t)d}, {W_down, es * d * (size_t)d_down},
+  const Span ins[6] = {{h, es * B * (size_t)d}, {W_down, es * d * (size_t)d_down},
                        {W_Q, es * d * (size_t)hd}, {W_K, es * d * (size_t)hd},
-                       {W_V, es * d * (size_t)hd}};
+                       {W_V, es * d * (size_t)hd}, {pos_arr, sizeof(int) * (size_t)B}};
   const Span outs[4] = {{q, es * B * (size_t)hd},
                         {K_win, w > 0 ? es * B * (size_t)hd * w : 0},
                         {V_win, w > 0 ? es * B * (size_t)hd * w : 0},
                         {h_D, es * B * (size_t)cap * d_down}};
-  if (!disjoint(outs, 4, ins, 5)) return DAR_ERR_INVALID_ARG;
+  if (!disjoint(outs, 4, ins, 6)) return DAR_ERR_INVALID_ARG;
   if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
   if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
     return DAR_ERR_UNSUPPORTED;
-  const size_t need_bytes = rope_table_bytes(d_k, pos);
+  // ragged positions are only known on the device: tables cover the cache
+  const int max_pos = pos_arr != nullptr ? cap - 1 : pos;
+  const size_t need_bytes = rope_table_bytes(d_k, max_pos);
   if (workspace == nullptr) {
     *workspace_bytes = need_bytes;
     return DAR_OK;
@@ -245,10 +251,11 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
   }
   float2* lo = (float2*)workspace;
   float2* hi = lo + 64 * (d_k / 2);
-  hipError_t e = launch_rope_tables(lo, hi, d_k, pos, rope_base, stream);
+  hipError_t e = launch_rope_tables(lo, hi, d_k, max_pos, rope_base, stream);
   if (e != hipSuccess) return DAR_ERR_HIP;
-  // One GEMM over the B new tokens (one per sequence, all at position pos):
-  // q at [b, head, 0, t]; k, v into ring slot pos mod w; h^D into row pos.
+  // One GEMM over the B new tokens (one per sequence, at position pos or
+  // pos_arr[b]): q at [b, head, 0, t]; k, v into ring slot pos mod w; h^D into
+  // row pos.
   GemmProblem g{};
   g.A = h;
   g.M = B;
@@ -261,39 +268,84 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
   g.d_k = d_k;
   g.pos0 = pos;
   g.rope = RopeTab{lo, hi, d_k / 2};
+  g.row_pos = pos_arr;
+  g.pos_max = max_pos;
   int ns = 0;
-  g.seg[ns++] = GemmSeg{W_Q, q, hd, kHead, 1, 1, 0};
+  g.seg[ns++] = GemmSeg{W_Q, q, hd, kHead, 1, 1, 0, kPosFixed};
   if (w > 0) {
-    g.seg[ns++] = GemmSeg{W_K, K_win, hd, kHead, 1, w, pos % w};
-    g.seg[ns++] = GemmSeg{W_V, V_win, hd, kHead, 0, w, pos % w};
+    g.seg[ns++] = GemmSeg{W_K, K_win, hd, kHead, 1, w, pos % w, kPosRing};
+    g.seg[ns++] = GemmSeg{W_V, V_win, hd, kHead, 0, w, pos % w, kPosRing};
   }
-  g.seg[ns++] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos};
+  g.seg[ns++] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos, kPosRow};
   g.nseg = ns;
   return hip_status(launch_project_gemm(g, dtype, stream));
+}
+
+dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q, const void* W_K,
+                             const void* W_V, int B, int d, int d_down, int heads, int d_k,
+                             int pos, int w, int cap, float rope_base, dar_dtype dtype, void* q,
+                             void* K_win, void* V_win, void* h_D, void* workspace,
+                             size_t* workspace_bytes, hipStream_t stream) {
+  return decode_append_impl(h, W_down, W_Q, W_K, W_V, B, d, d_down, heads, d_k, pos, nullptr, w,
+                            cap, rope_base, dtype, q, K_win, V_win, h_D, workspace,
+                            workspace_bytes, stream);
+}
+
+dar_status dar_decode_append_varlen(const void* h, const void* W_down, const void* W_Q,
+                                    const void* W_K, const void* W_V, int B, int d, int d_down,
+                                    int heads, int d_k, const int* pos, int w, int cap,
+                                    float rope_base, dar_dtype dtype, void* q, void* K_win,
+                                    void* V_win, void* h_D, void* workspace,
+                                    size_t* workspace_bytes, hipStream_t stream) {
+  if (pos == nullptr) return DAR_ERR_INVALID_ARG;
+  return decode_append_impl(h, W_down, W_Q, W_K, W_V, B, d, d_down, heads, d_k, 0, pos, w, cap,
+                            rope_base, dtype, q, K_win, V_win, h_D, workspace, workspace_bytes,
+                            stream);
+}
+
+static dar_status cache_from_prefill_impl(const void* h_D, const void* K_loc, const void* V_loc,
+                                          int B, int N, const int* lens, int heads, int d_k,
+                                          int d_down, int w, int cap, dar_dtype dtype,
+                                          void* h_D_cache, void* K_win, void* V_win,
+                                          hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_down < 1 || w < 0 || cap < N)
+    return DAR_ERR_INVALID_ARG;
+  if (lens != nullptr && ((uintptr_t)lens & 3u)) return DAR_ERR_INVALID_ARG;
+  if (!aligned16(h_D) || !aligned16(h_D_cache)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_loc) || !aligned16(V_loc) || !aligned16(K_win) || !aligned16(V_win)))
+    return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k;
+  const Span ins[4] = {{h_D, 2 * (size_t)B * N * d_down},
+                       {w > 0 ? K_loc : nullptr, 2 * (size_t)B * N * hd},
+                       {w > 0 ? V_loc : nullptr, 2 * (size_t)B * N * hd},
+                       {lens, sizeof(int) * (size_t)B}};
+  const Span outs[3] = {{h_D_cache, 2 * (size_t)B * cap * d_down},
+                        {w > 0 ? K_win : nullptr, 2 * (size_t)B * w * hd},
+                        {w > 0 ? V_win : nullptr, 2 * (size_t)B * w * hd}};
+  if (!disjoint(outs, 3, ins, 4)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!head_supported(d_k) || d_down % 8) return DAR_ERR_UNSUPPORTED;
+  return hip_status(launch_cache_from_prefill(h_D, K_loc, V_loc, B, N, heads, d_k, d_down, w,
+                                              cap, h_D_cache, K_win, V_win, stream, lens));
 }
 
 dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc, int B,
                                   int N, int heads, int d_k, int d_down, int w, int cap,
                                   dar_dtype dtype, void* h_D_cache, void* K_win, void* V_win,
                                   hipStream_t stream) {
-  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
-  if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_down < 1 || w < 0 || cap < N)
-    return DAR_ERR_INVALID_ARG;
-  if (!aligned16(h_D) || !aligned16(h_D_cache)) return DAR_ERR_INVALID_ARG;
-  if (w > 0 && (!aligned16(K_loc) || !aligned16(V_loc) || !aligned16(K_win) || !aligned16(V_win)))
-    return DAR_ERR_INVALID_ARG;
-  const size_t hd = (size_t)heads * d_k;
-  const Span ins[3] = {{h_D, 2 * (size_t)B * N * d_down},
-                       {w > 0 ? K_loc : nullptr, 2 * (size_t)B * N * hd},
-                       {w > 0 ? V_loc : nullptr, 2 * (size_t)B * N * hd}};
-  const Span outs[3] = {{h_D_cache, 2 * (size_t)B * cap * d_down},
-                        {w > 0 ? K_win : nullptr, 2 * (size_t)B * w * hd},
-                        {w > 0 ? V_win : nullptr, 2 * (size_t)B * w * hd}};
-  if (!disjoint(outs, 3, ins, 3)) return DAR_ERR_INVALID_ARG;
-  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
-  if (!head_supported(d_k) || d_down % 8) return DAR_ERR_UNSUPPORTED;
-  return hip_status(launch_cache_from_prefill(h_D, K_loc, V_loc, B, N, heads, d_k, d_down, w,
-                                              cap, h_D_cache, K_win, V_win, stream));
+  return cache_from_prefill_impl(h_D, K_loc, V_loc, B, N, nullptr, heads, d_k, d_down, w, cap,
+                                 dtype, h_D_cache, K_win, V_win, stream);
+}
+
+dar_status dar_cache_from_prefill_varlen(const void* h_D, const void* K_loc, const void* V_loc,
+                                         int B, int N, const int* lens, int heads, int d_k,
+                                         int d_down, int w, int cap, dar_dtype dtype,
+                                         void* h_D_cache, void* K_win, void* V_win,
+                                         hipStream_t stream) {
+  if (lens == nullptr) return DAR_ERR_INVALID_ARG;
+  return cache_from_prefill_impl(h_D, K_loc, V_loc, B, N, lens, heads, d_k, d_down, w, cap,
+                                 dtype, h_D_cache, K_win, V_win, stream);
 }
 
 dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q, const void* W_K,
@@ -457,12 +509,13 @@ dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q,
   return hip_status(e);
 }
 
-dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
-                           const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
-                           int heads, int d_k, int d_down, int w, float rope_base,
-                           dar_dtype dtype, void* o, void* workspace, size_t* workspace_bytes,
-                           hipStream_t stream) {
+static dar_status attn_decode_impl(const void* q, const void* K_win, const void* V_win,
+                                   const void* h_D, const void* W_upK, const void* W_upV, int B,
+                                   int ctx_len, const int* ctx_lens, int cap, int heads, int d_k,
+                                   int d_down, int w, float rope_base, dar_dtype dtype, void* o,
+                                   void* workspace, size_t* workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (ctx_lens != nullptr && ((uintptr_t)ctx_lens & 3u)) return DAR_ERR_INVALID_ARG;
   if (B < 1 || ctx_len < 1 || cap < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_down < 1 ||
       w < 0)
     return DAR_ERR_INVALID_ARG;
@@ -476,14 +529,15 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
   if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
   const int hd = heads * d_k;
   const size_t es = elem_size(dtype);
-  const Span ins[6] = {{q, es * B * hd},
+  const Span ins[7] = {{q, es * B * hd},
                        {K_win, w > 0 ? es * B * hd * (size_t)w : 0},
                        {V_win, w > 0 ? es * B * hd * (size_t)w : 0},
                        {h_D, es * B * (size_t)cap * d_down},
                        {W_upK, es * d_down * hd},
-                       {W_upV, es * d_down * hd}};
+                       {W_upV, es * d_down * hd},
+                       {ctx_lens, sizeof(int) * (size_t)B}};
   const Span outs[1] = {{o, es * B * hd}};
-  if (!disjoint(outs, 1, ins, 6)) return DAR_ERR_INVALID_ARG;
+  if (!disjoint(outs, 1, ins, 7)) return DAR_ERR_INVALID_ARG;
   if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
   if (!decode_supported(d_k, d_down) || hd % 64) return DAR_ERR_UNSUPPORTED;
 
@@ -502,6 +556,7 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
   p.d_k = d_k;
   p.d_down = d_down;
   p.w = w;
+  p.ctx_lens = ctx_lens;
   const size_t rope_bytes = rope_table_bytes(d_k, std::max(0L, n_glob - 1));
   const size_t need_bytes = rope_bytes + decode_workspace_bytes(p);
   if (workspace == nullptr) {
@@ -524,6 +579,25 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
   p.rope = RopeTab{lo, hi, d_k / 2};
   p.ws = wsp + rope_bytes;
   return hip_status(launch_attn_decode(p, stream));
+}
+
+dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, const void* h_D,
+                           const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
+                           int heads, int d_k, int d_down, int w, float rope_base,
+                           dar_dtype dtype, void* o, void* workspace, size_t* workspace_bytes,
+                           hipStream_t stream) {
+  return attn_decode_impl(q, K_win, V_win, h_D, W_upK, W_upV, B, ctx_len, nullptr, cap, heads,
+                          d_k, d_down, w, rope_base, dtype, o, workspace, workspace_bytes, stream);
+}
+
+dar_status dar_attn_decode_varlen(const void* q, const void* K_win, const void* V_win,
+                                  const void* h_D, const void* W_upK, const void* W_upV, int B,
+                                  const int* ctx_lens, int max_ctx, int cap, int heads, int d_k,
+                                  int d_down, int w, float rope_base, dar_dtype dtype, void* o,
+                                  void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+  if (ctx_lens == nullptr) return DAR_ERR_INVALID_ARG;
+  return attn_decode_impl(q, K_win, V_win, h_D, W_upK, W_upV, B, max_ctx, ctx_lens, cap, heads,
+                          d_k, d_down, w, rope_base, dtype, o, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -148,7 +148,11 @@ struct GemmSeg {
   // write one token into a ring slot or a latent-cache row, and a prefill
   // chunk write its rows after the prefix's.
   int ld_seq = 0, seq_off = 0;
+  // With GemmProblem::row_pos (one token per sequence): where row b lands.
+  // kPosFixed: index seq_off; kPosRow: row_pos[b]; kPosRing: row_pos[b] mod ld_seq.
+  int pos_mode = 0;
 };
+enum PosMode : int { kPosFixed = 0, kPosRow = 1, kPosRing = 2 };
 
 // Element types of GEMM operands and outputs.
 enum ElemType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
@@ -162,6 +166,12 @@ struct GemmProblem {
   int n_seq;  // rows per sequence (row -> (b, n))
   int heads, d_k, pos0;
   RopeTab rope;
+  // Ragged append (n_seq == 1): row b is sequence b's token at position
+  // row_pos[b] (device, int32), clamped to [0, pos_max] (the last position the
+  // RoPE tables hold); an index past a segment's ld_seq is clamped to its last
+  // row.  Null: position pos0 + n.
+  const int* row_pos = nullptr;
+  int pos_max = 0;
 };
 
 hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s);
@@ -187,6 +197,9 @@ struct DecodeProblem {
   int B, ctx, cap, H, d_k, d_down, w;
   RopeTab rope;
   void* ws;  // workspace after the rope tables
+  // Ragged batch: ctx_lens[b] (device, int32) is sequence b's context length,
+  // clamped to [1, ctx]; ctx is then the largest.  Null: every sequence has ctx.
+  const int* ctx_lens = nullptr;
 };
 size_t decode_workspace_bytes(const DecodeProblem& p);
 // Pieces of the cache kernels (fp16 <-> bf16 conversions, positions relative to
@@ -194,7 +207,8 @@ size_t decode_workspace_bytes(const DecodeProblem& p);
 hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap, int row0,
                               void* h_D_cache, hipStream_t s);
 hipError_t launch_ring_fill(const void* K, const void* Vt, int B, int heads, int d_k, int N,
-                            int base, int w, void* K_win, void* V_win, hipStream_t s);
+                            int base, int w, void* K_win, void* V_win, hipStream_t s,
+                            const int* lens = nullptr);
 hipError_t launch_ring_to_local(const void* K_win, const void* V_win, int B, int heads, int d_k,
                                 int w, int base, int p0, int len, void* K, void* Vt,
                                 hipStream_t s);
@@ -202,7 +216,7 @@ hipError_t launch_ring_to_local(const void* K_win, const void* V_win, int B, int
 hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const void* V_loc,
                                      int B, int N, int heads, int d_k, int d_down, int w,
                                      int cap, void* h_D_cache, void* K_win, void* V_win,
-                                     hipStream_t s);
+                                     hipStream_t s, const int* lens = nullptr);
 bool decode_supported(int d_k, int d_down);  // d_k in {64,128}, d_down in {32,...,512}
 hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s);
 

@@ -178,6 +178,22 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
 // 64-token runs starting at 64 hf and 128 + 64 hf).  Work is cut into 16-byte
 // output chunks (8 values) so that eight consecutive lanes write 128
 // contiguous bytes, and the lane order keeps the LDS reads conflict-free.
+// RoPE position of token (b, n), and its index in the output sequence of
+// segment seg (stride ld): fixed offsets, or per-row positions of a ragged
+// append (one token per sequence).
+__device__ __forceinline__ int row_position(const GemmProblem& p, int b, int n) {
+  if (p.row_pos == nullptr) return p.pos0 + n;
+  const int q = p.row_pos[b];
+  return q < 0 ? 0 : (q > p.pos_max ? p.pos_max : q);
+}
+
+__device__ __forceinline__ int out_index(const GemmProblem& p, const GemmSeg& seg, int b, int n,
+                                         int ld) {
+  if (p.row_pos == nullptr || seg.pos_mode == kPosFixed) return n + seg.seq_off;
+  const int q = row_position(p, b, n);
+  return seg.pos_mode == kPosRing ? q % ld : min(q, ld - 1);
+}
+
 __device__ __forceinline__ int epi_row(int row0, int hf, int r) {
   return row0 + 128 * (r >> 6) + 64 * hf + (r & 63);
 }
@@ -214,7 +230,7 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
     const int r = ((tid >> 3) + 32 * k) & 127;
     const int grow = epi_row(row0, hf, r);
     if (grow >= M) continue;
-    const int b = grow / Nq, no = grow % Nq + seg.seq_off;
+    const int b = grow / Nq, no = out_index(p, seg, b, grow % Nq, ld);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int c = 8 * ((tid & 7) + 8 * h2);
@@ -256,7 +272,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
   const int b0 = grow0 / Nq, n0 = grow0 % Nq;
   const bool consec = grow0 + 3 < M && n0 + 3 < Nq;  // one sequence, consecutive positions
   float2 cs[8], step[8];
-  rope_cs8(p.rope, p.pos0 + n0, t0, cs);
+  rope_cs8(p.rope, row_position(p, b0, n0), t0, cs);
   if (consec) {
     const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
 #pragma unroll
@@ -280,7 +296,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
         if (grow >= M) break;
         b = grow / Nq;
         n = grow % Nq;
-        rope_cs8(p.rope, p.pos0 + n, t0, cs);
+        rope_cs8(p.rope, row_position(p, b, n), t0, cs);
       }
     }
     float x[8], y[8], a[8], bb[8];
@@ -291,7 +307,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
       a[i] = x[i] * cs[i].x - y[i] * cs[i].y;
       bb[i] = x[i] * cs[i].y + y[i] * cs[i].x;
     }
-    OutT* dst = out + (((size_t)b * H + head) * ld + n + seg.seq_off) * D + t0;
+    OutT* dst = out + (((size_t)b * H + head) * ld + out_index(p, seg, b, n, ld)) * D + t0;
     store_run<OutT, 8>(dst, a);
     store_run<OutT, 8>(dst + HALF, bb);
   }

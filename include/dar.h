@@ -208,6 +208,47 @@ dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void
                                   hipStream_t stream);
 
 /*
+ * Ragged batches: sequences of different lengths in one call.
+ *
+ * A batch of prompts of lengths N_b <= N is prefilled padded to N (dar_project
+ * and dar_attn_prefill as usual): attention is causal, so the rows n < N_b of
+ * sequence b do not depend on its padding and are exactly those of an
+ * unpadded prefill.  From there on each sequence moves at its own position.
+ * The per-sequence lengths and positions are device int32 arrays of B entries
+ * (caller-owned, 4-byte aligned, read by the kernels; they are never read on
+ * the host, so values are not validated: each is clamped into range, which
+ * keeps every access in bounds but gives meaningless results for bad values).
+ *
+ * dar_cache_from_prefill_varlen -- as dar_cache_from_prefill, with sequence b
+ *   ending at lens[b] (1 <= lens[b] <= N): its ring gets the positions
+ *   max(0, lens[b]-w) .. lens[b]-1.  Latent rows 0 .. N-1 are copied for every
+ *   sequence (rows past lens[b] are never read by decode).
+ * dar_decode_append_varlen -- as dar_decode_append, with sequence b's token at
+ *   position pos[b] (0 <= pos[b] < cap): RoPE at pos[b], ring slot pos[b] mod w,
+ *   latent row pos[b].  The workspace holds RoPE tables up to cap - 1.
+ * dar_attn_decode_varlen -- as dar_attn_decode, with sequence b's query at
+ *   position ctx_lens[b] - 1 (1 <= ctx_lens[b] <= max_ctx, max_ctx - w < cap
+ *   when max_ctx > w).  The work split and workspace follow max_ctx;
+ *   workgroups past a sequence's end return after writing empty partials.
+ */
+dar_status dar_cache_from_prefill_varlen(const void* h_D, const void* K_loc, const void* V_loc,
+                                         int B, int N, const int* lens, int heads, int d_k,
+                                         int d_down, int w, int cap, dar_dtype dtype,
+                                         void* h_D_cache, void* K_win, void* V_win,
+                                         hipStream_t stream);
+dar_status dar_decode_append_varlen(const void* h, const void* W_down, const void* W_Q,
+                                    const void* W_K, const void* W_V, int B, int d, int d_down,
+                                    int heads, int d_k, const int* pos, int w, int cap,
+                                    float rope_base, dar_dtype dtype, void* q, void* K_win,
+                                    void* V_win, void* h_D, void* workspace,
+                                    size_t* workspace_bytes, hipStream_t stream);
+dar_status dar_attn_decode_varlen(const void* q, const void* K_win, const void* V_win,
+                                  const void* h_D, const void* W_upK, const void* W_upV, int B,
+                                  const int* ctx_lens, int max_ctx, int cap, int heads, int d_k,
+                                  int d_down, int w, float rope_base, dar_dtype dtype, void* o,
+                                  void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * dar_attn_decode -- one new query per sequence over the mixed cache.
  *
  * The inference remarks of the paper note that each past token contributes

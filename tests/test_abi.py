@@ -237,3 +237,59 @@ def test_chunk_size_query_and_rejects():
     assert chunk(dtype=0)[0] == UNSUP
     assert chunk(d_k=96)[0] == UNSUP
     assert chunk(ws=F(20), wsb=n - 1)[0] == WS
+
+
+# Ragged-batch entry points: the per-sequence arrays are device int32 [B].
+def decode_varlen(**kw):
+    a = dict(lens=F(7), max_ctx=1000, cap=1000, w=128, d_down=256, ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    st = dar.lib().dar_attn_decode_varlen(F(0), F(1), F(2), F(3), F(4), F(5), 2, a["lens"],
+                                          a["max_ctx"], a["cap"], 4, 128, a["d_down"], a["w"],
+                                          10000.0, 1, F(6), a["ws"], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_decode_varlen_size_query_and_rejects():
+    st, n = decode_varlen()
+    assert st == OK and n == decode()[1]        # sized by the longest context
+    assert decode_varlen(lens=None)[0] == INVALID
+    assert decode_varlen(lens=F(7) + 2)[0] == INVALID   # misaligned lengths
+    assert decode_varlen(lens=F(6))[0] == INVALID        # lengths alias the output
+    assert decode_varlen(cap=800)[0] == INVALID
+    assert decode_varlen(d_down=96)[0] == UNSUP
+    assert decode_varlen(ws=F(20), wsb=n - 1)[0] == WS
+
+
+def append_varlen(**kw):
+    a = dict(pos=F(9), cap=200, w=16, ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    st = dar.lib().dar_decode_append_varlen(F(0), F(1), F(2), F(3), F(4), 2, 256, 64, 4, 64,
+                                            a["pos"], a["w"], a["cap"], 10000.0, 1, F(5), F(6),
+                                            F(7), F(8), a["ws"], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_append_varlen_size_query_and_rejects():
+    st, n = append_varlen()
+    assert st == OK and n == append(pos=199)[1]  # tables up to the last cache row
+    assert append_varlen(pos=None)[0] == INVALID
+    assert append_varlen(pos=F(9) + 1)[0] == INVALID
+    assert append_varlen(pos=F(5))[0] == INVALID         # positions alias the q output
+    assert append_varlen(ws=F(20), wsb=n - 1)[0] == WS
+
+
+def cache_varlen(**kw):
+    a = dict(lens=F(6), N=100, cap=128)
+    a.update(kw)
+    return dar.lib().dar_cache_from_prefill_varlen(F(0), F(1), F(2), 2, a["N"], a["lens"], 4, 64,
+                                                   64, 16, a["cap"], 1, F(3), F(4), F(5), None)
+
+
+def test_cache_varlen_rejects():
+    # (valid arguments would launch; the CPU suite checks rejections only)
+    assert cache_varlen(lens=None) == INVALID
+    assert cache_varlen(lens=F(6) + 2) == INVALID
+    assert cache_varlen(lens=F(3)) == INVALID           # lengths alias the cache
+    assert cache_varlen(cap=99) == INVALID
