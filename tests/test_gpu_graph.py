@@ -93,3 +93,29 @@ def test_decode_graph_replays_match_eager():
         o2 = dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx - 7, w)
         torch.cuda.synchronize()
         assert not torch.equal(o2, ref)
+
+
+def test_ragged_decode_graph_follows_device_lengths():
+    """A captured ragged decode reads the per-sequence lengths from device
+    memory at every replay: changing them in place between replays gives the
+    eager result for the new lengths."""
+    B, max_ctx, d, H, d_k, dd, w = 3, 2500, 512, 4, 128, 128, 256
+    inp = di.decode_inputs(B, max_ctx, d, H, d_k, dd, w, seed0=99)
+    W_up, W_K, W_V = (dev_w(inp[k], "bf16") for k in ("W_up", "W_K", "W_V"))
+    Wk, Wv = dar.dar_fold(W_up, W_K, W_V, H, d_k)
+    q, K_win, V_win, h_D = (dev(inp[k], "bf16") for k in ("q", "K_win", "V_win", "h_D"))
+    lens = torch.tensor([2500, 300, 1200], dtype=torch.int32, device="cuda")
+    ws = torch.empty(dar.decode_workspace_bytes(B, max_ctx, max_ctx, H, d_k, dd, w),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, H * d_k), dtype=torch.bfloat16, device="cuda")
+    g = capture(lambda: dar.dar_attn_decode_varlen(q, K_win, V_win, h_D, Wk, Wv, lens, max_ctx,
+                                                   w, o=o, workspace=ws))
+    for rep, new in enumerate(([2500, 300, 1200], [17, 2499, 256], [1, 257, 2000])):
+        lens.copy_(torch.tensor(new, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = dar.dar_attn_decode_varlen(q, K_win, V_win, h_D, Wk, Wv, lens, max_ctx, w)
+        torch.cuda.synchronize()
+        log("ragged decode graph replay %d lens %s" % (rep, new))
+        assert torch.equal(o, ref)
