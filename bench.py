@@ -245,7 +245,10 @@ def cpu_baseline(oracle, inp, H, d_k, w, d_down, budget_s=10.0):
                       "metric" % (B, N, H, reps)}
 
 
-def time_decode(torch, dar, di, steps, warmup, cfg):
+def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
+    """The mixed-cache decode step of cfg (B sequences at context ctx), or with
+    lens, a ragged batch: sequence b at context lens[b] <= ctx
+    (dar_attn_decode_varlen)."""
     B, ctx, d, H, d_k, d_down, w = cfg
     inp = di.decode_inputs(B, ctx, d, H, d_k, d_down, w, dtype="bf16", seed0=5000)
 
@@ -261,8 +264,13 @@ def time_decode(torch, dar, di, steps, warmup, cfg):
     ws = torch.empty(dar.decode_workspace_bytes(B, ctx, ctx, H, d_k, d_down, w),
                      dtype=torch.uint8, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # > Infinity Cache
-    g = capture(torch, lambda: dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o,
-                                                   workspace=ws))
+    if lens is None:
+        g = capture(torch, lambda: dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o,
+                                                       workspace=ws))
+    else:
+        lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        g = capture(torch, lambda: dar.dar_attn_decode_varlen(q, K_win, V_win, h_D, Wk, Wv, lens_d,
+                                                              ctx, w, o=o, workspace=ws))
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -277,8 +285,18 @@ def time_decode(torch, dar, di, steps, warmup, cfg):
         times.append(e0.elapsed_time(e1))
     del g
     ms = float(np.median(times))
-    byts, flops = decode_work(B, ctx, d, d_down, w, H)
-    return {"workload": "decode B%d ctx%d d%d H%d dk%d w%d d_down%d" % (B, ctx, d, H, d_k, w, d_down),
+    if lens is None:
+        byts, flops = decode_work(B, ctx, d, d_down, w, H)
+        name = "decode B%d ctx%d d%d H%d dk%d w%d d_down%d" % (B, ctx, d, H, d_k, w, d_down)
+    else:
+        n_lat = sum(max(0, c - w) for c in lens)
+        n_win = sum(min(w, c) for c in lens)
+        byts = 2.0 * (n_lat * d_down + n_win * 2 * d + 2 * d_down * d + 2 * B * d)
+        flops = (n_lat * (2.0 * d * d_down + 2.0 * d + 2.0 * H * d_down) + n_win * 4.0 * d
+                 + B * 2.0 * d_down * d)
+        name = ("ragged decode B%d ctx %d..%d (mean %d) d%d H%d dk%d w%d d_down%d"
+                % (B, min(lens), max(lens), sum(lens) // B, d, H, d_k, w, d_down))
+    return {"workload": name,
             "ms": ms, "GB/s": byts / ms / 1e6, "hbm_frac": byts / ms / 1e6 / PEAK_HBM_GBS,
             "TFLOP/s": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / PEAK_BF16_TFLOPS,
             "bytes": byts, "flops": flops}
@@ -451,6 +469,14 @@ def main():
         dec["hbm_frac_measured"] = dec["GB/s"] / cal["hbm_copy_gbs"]
         dec["mfma_frac_measured"] = dec["TFLOP/s"] / cal["mfma_f16_tflops"]
         res["decode"] = dec
+        if not args.no_sweep:
+            # a serving-like batch: 16 contexts spread over 1k .. 32k
+            lens = [int(x) for x in np.linspace(1024, 32768, 16)[::-1]]
+            rg = time_decode(torch, dar, di, max(3, args.steps // 2), 2,
+                             (16, 32768, 2048, 16, 128, 256, 512), lens=lens)
+            log("ragged decode: %.3f ms, %.0f GB/s, %.1f TFLOP/s" % (rg["ms"], rg["GB/s"],
+                                                                   rg["TFLOP/s"]))
+            res["decode_ragged"] = rg
         if res["value"] is None:
             res.update(value=dec["GB/s"], unit="GB/s", ms_per_step=dec["ms"])
             res["config"] = {"workload": dec["workload"], "global_batch": 16, "seq_len": 32768,

@@ -181,16 +181,20 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
 // RoPE position of token (b, n), and its index in the output sequence of
 // segment seg (stride ld): fixed offsets, or per-row positions of a ragged
 // append (one token per sequence).
+// RP (compile time): the problem carries row_pos.
+template <bool RP>
 __device__ __forceinline__ int row_position(const GemmProblem& p, int b, int n) {
-  if (p.row_pos == nullptr) return p.pos0 + n;
+  if constexpr (!RP) return p.pos0 + n;
   const int q = p.row_pos[b];
   return q < 0 ? 0 : (q > p.pos_max ? p.pos_max : q);
 }
 
+template <bool RP>
 __device__ __forceinline__ int out_index(const GemmProblem& p, const GemmSeg& seg, int b, int n,
                                          int ld) {
-  if (p.row_pos == nullptr || seg.pos_mode == kPosFixed) return n + seg.seq_off;
-  const int q = row_position(p, b, n);
+  if constexpr (!RP) return n + seg.seq_off;
+  if (seg.pos_mode == kPosFixed) return n + seg.seq_off;
+  const int q = row_position<RP>(p, b, n);
   return seg.pos_mode == kPosRing ? q % ld : min(q, ld - 1);
 }
 
@@ -217,7 +221,7 @@ __device__ __forceinline__ void rope_cs8(const RopeTab& t, int pos, int t0, floa
 }
 
 // Tile [128 tokens][EPI_P] -> kRowMajor, or kHead without rotation.
-template <typename OutT, int D>
+template <typename OutT, int D, bool RP>
 __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, int hf, int col0,
                                                  const GemmSeg& seg, const GemmProblem& p) {
   const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
@@ -230,7 +234,7 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
     const int r = ((tid >> 3) + 32 * k) & 127;
     const int grow = epi_row(row0, hf, r);
     if (grow >= M) continue;
-    const int b = grow / Nq, no = out_index(p, seg, b, grow % Nq, ld);
+    const int b = grow / Nq, no = out_index<RP>(p, seg, b, grow % Nq, ld);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int c = 8 * ((tid & 7) + 8 * h2);
@@ -255,7 +259,7 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
 // for 4 consecutive tokens: the angles of the first token come from the
 // tables, the next ones by one complex multiplication with (cos, sin)(theta_t)
 // each (the table row for position 1).
-template <typename OutT, int D>
+template <typename OutT, int D, bool RP>
 __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int hf, int col0,
                                                 const GemmSeg& seg, const GemmProblem& p) {
   constexpr int HALF = D / 2, PCH = D / 16;  // pair chunks of 8 per head
@@ -272,7 +276,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
   const int b0 = grow0 / Nq, n0 = grow0 % Nq;
   const bool consec = grow0 + 3 < M && n0 + 3 < Nq;  // one sequence, consecutive positions
   float2 cs[8], step[8];
-  rope_cs8(p.rope, row_position(p, b0, n0), t0, cs);
+  rope_cs8(p.rope, row_position<RP>(p, b0, n0), t0, cs);
   if (consec) {
     const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
 #pragma unroll
@@ -296,7 +300,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
         if (grow >= M) break;
         b = grow / Nq;
         n = grow % Nq;
-        rope_cs8(p.rope, row_position(p, b, n), t0, cs);
+        rope_cs8(p.rope, row_position<RP>(p, b, n), t0, cs);
       }
     }
     float x[8], y[8], a[8], bb[8];
@@ -307,7 +311,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
       a[i] = x[i] * cs[i].x - y[i] * cs[i].y;
       bb[i] = x[i] * cs[i].y + y[i] * cs[i].x;
     }
-    OutT* dst = out + (((size_t)b * H + head) * ld + out_index(p, seg, b, n, ld)) * D + t0;
+    OutT* dst = out + (((size_t)b * H + head) * ld + out_index<RP>(p, seg, b, n, ld)) * D + t0;
     store_run<OutT, 8>(dst, a);
     store_run<OutT, 8>(dst + HALF, bb);
   }
@@ -359,7 +363,7 @@ __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, 
 // accumulators hold one token and runs of 4 consecutive output columns, which
 // go to an LDS staging tile as 16-byte writes ([token][column] for Q, K and h^D,
 // [column][token] for the transposed V layout [b, head, t, n]).
-template <typename TM, typename TB, typename TO, int D>
+template <typename TM, typename TB, typename TO, int D, bool RP>
 __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTiles st, int nM,
                                                            int nC, int nCp, int order) {
   typedef typename Vec8<TM>::type TMx8;
@@ -528,9 +532,9 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
     if (seg.kind == kHeadT)
       store_cols<TO, D, BM + 4>(tile, row0, hf, col0, seg, p);
     else if (seg.kind == kHead && seg.rope)
-      store_rows_rope<TO, D>(tile, row0, hf, col0, seg, p);
+      store_rows_rope<TO, D, RP>(tile, row0, hf, col0, seg, p);
     else
-      store_rows_plain<TO, D>(tile, row0, hf, col0, seg, p);
+      store_rows_plain<TO, D, RP>(tile, row0, hf, col0, seg, p);
   }
 }
 
@@ -627,16 +631,19 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
     for (int i = 0; i < p.nseg; ++i) wbytes += (size_t)p.seg[i].width * p.K * 2;
     const int order = wbytes <= (size_t)(2 << 20) ? 1 : 0;
     const dim3 grid(order == 1 ? nMp * nC : nM * nCp);
-#define DAR_G(TA, TO, D)                                                                    \
-  hipLaunchKernelGGL((project_gemm_mfma<TA, bf16, TO, D>), grid, dim3(256), 0, s, p, st, nM, \
-                     nC, nCp, order)
+#define DAR_G(TA, TO, D, RP)                                                         \
+  hipLaunchKernelGGL((project_gemm_mfma<TA, bf16, TO, D, RP>), grid, dim3(256), 0, s, p, st, \
+                     nM, nC, nCp, order)
     if (p.b_type != kBF16) return hipErrorInvalidValue;
-    if (p.a_type == kBF16 && p.out_type == kF16) {
-      if (p.d_k == 64) DAR_G(bf16, f16, 64); else DAR_G(bf16, f16, 128);
+    if (p.row_pos != nullptr) {  // ragged append: bf16 in and out only
+      if (p.a_type != kBF16 || p.out_type != kBF16 || p.n_seq != 1) return hipErrorInvalidValue;
+      if (p.d_k == 64) DAR_G(bf16, bf16, 64, true); else DAR_G(bf16, bf16, 128, true);
+    } else if (p.a_type == kBF16 && p.out_type == kF16) {
+      if (p.d_k == 64) DAR_G(bf16, f16, 64, false); else DAR_G(bf16, f16, 128, false);
     } else if (p.a_type == kF16 && p.out_type == kF16) {
-      if (p.d_k == 64) DAR_G(f16, f16, 64); else DAR_G(f16, f16, 128);
+      if (p.d_k == 64) DAR_G(f16, f16, 64, false); else DAR_G(f16, f16, 128, false);
     } else if (p.a_type == kBF16 && p.out_type == kBF16) {
-      if (p.d_k == 64) DAR_G(bf16, bf16, 64); else DAR_G(bf16, bf16, 128);
+      if (p.d_k == 64) DAR_G(bf16, bf16, 64, false); else DAR_G(bf16, bf16, 128, false);
     } else {
       return hipErrorInvalidValue;
     }
