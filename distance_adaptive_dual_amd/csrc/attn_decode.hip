@@ -524,43 +524,55 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeo
   __shared__ float lat[1024];
   __shared__ float wsc[1024];
   __shared__ float red[2];
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int DD = p.d_down, nc = g.n_chunks;
-  const float* pl = part_lat + (size_t)bh * nc * g.part_lat_floats;
+  const size_t PF = g.part_lat_floats;
+  const float* pl = part_lat + (size_t)bh * nc * PF;
   const float* pw = part_win + (size_t)bh * (2 + D);
-  if (tid == 0) {
-    float M = pw[1] > 0.f ? pw[0] : -INFINITY;
-    for (int c = 0; c < nc; ++c)
-      if (pl[(size_t)c * g.part_lat_floats + 1] > 0.f)
-        M = fmaxf(M, pl[(size_t)c * g.part_lat_floats]);
+  if (wave == 0) {
+    // common maximum over the non-empty partials, their weights and the total
+    float M = (lane == 0 && pw[1] > 0.f) ? pw[0] : -INFINITY;
+    for (int c = lane; c < nc; c += 64)
+      if (pl[c * PF + 1] > 0.f) M = fmaxf(M, pl[c * PF]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float L = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const float* e = pl + (size_t)c * g.part_lat_floats;
+    for (int c = lane; c < nc; c += 64) {
+      const float* e = pl + c * PF;
       const float f = (e[1] > 0.f) ? exp2f(e[0] - M) : 0.f;
       wsc[c] = f;
       L += f * e[1];
     }
-    const float fw = (pw[1] > 0.f) ? exp2f(pw[0] - M) : 0.f;
-    L += fw * pw[1];
-    red[0] = fw;
-    red[1] = L;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (lane == 0) {
+      const float fw = (pw[1] > 0.f) ? exp2f(pw[0] - M) : 0.f;
+      red[0] = fw;
+      red[1] = L + fw * pw[1];
+    }
   }
   __syncthreads();
   for (int kk = tid; kk < DD; kk += 256) {
     float a = 0.f;
-    for (int c = 0; c < nc; ++c) a += wsc[c] * pl[(size_t)c * g.part_lat_floats + 2 + kk];
+    for (int c = 0; c < nc; ++c) a += wsc[c] * pl[c * PF + 2 + kk];
     lat[kk] = a;
   }
   __syncthreads();
+  // lift by W_upV: a wave per output row, 4 consecutive latent dims per lane
   const int h = bh % p.H;
   const bf16* Wv = (const bf16*)p.W_upV + (size_t)h * D * DD;
   const float inv = 1.f / red[1];
-  for (int t = tid; t < D; t += 256) {
+  for (int t = wave; t < D; t += 4) {
     const bf16* wr = Wv + (size_t)t * DD;
     float a = 0.f;
-    for (int kk = 0; kk < DD; ++kk) a += lat[kk] * (float)wr[kk];
-    a += red[0] * pw[2 + t];
-    ((bf16*)p.o)[(size_t)bh * D + t] = (bf16)(a * inv);
+    for (int kk = 4 * lane; kk < DD; kk += 256) {
+      const u32x2 v = *(const u32x2*)(wr + kk);
+      a += lat[kk] * __uint_as_float(v[0] << 16) + lat[kk + 1] * __uint_as_float(v[0] & 0xffff0000u) +
+           lat[kk + 2] * __uint_as_float(v[1] << 16) + lat[kk + 3] * __uint_as_float(v[1] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+    if (lane == 0) ((bf16*)p.o)[(size_t)bh * D + t] = (bf16)((a + red[0] * pw[2 + t]) * inv);
   }
 }
 
