@@ -93,11 +93,11 @@ struct LatentSmem {
   static constexpr int DD = KS * 16;   // d_down
   static constexpr int NBUF = KS <= 16 ? 4 : 3;  // latent ring depth
   static constexpr int CP = D / 2 + 2; // float2 per cos/sin row (16 B pad)
-  // latent blocks [token][d_down], unpadded: 16-byte chunk c of token row r
-  // sits in slot c ^ (r & SWM), so that eight consecutive rows read at one
-  // logical chunk hit eight different bank groups
-  static constexpr int SWM = (2 * KS < 8 ? 2 * KS : 8) - 1;
-  bf16 lat[NBUF][TB * DD];
+  // latent blocks [token][d_down] with rows LP = d_down + 8 apart: the
+  // 16-byte pad puts consecutive rows read at one column in different bank
+  // groups
+  static constexpr int LP = DD + 8;
+  bf16 lat[NBUF][TB * LP];
   float2 cs[2][TB * CP];               // (cos, sin)(j theta_t) of a block, [token][t]
   float sc[2][NWAVE][TB];              // per-wave partial scores
   bf16 pm[2][16][TB + 8];              // probabilities, rows = heads of the group
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   using S = LatentSmem<D, KS>;
   // NS: slices of d_down per frequency block (a wave holds the folded rows of
   // 32 frequencies over d_down / NS latent dims: at most 128 VGPRs).
-  constexpr int DD = S::DD, SWM = S::SWM, NBUF = S::NBUF, CP = S::CP, WPH = D / 64, HALF = D / 2;
+  constexpr int DD = S::DD, LP = S::LP, NBUF = S::NBUF, CP = S::CP, WPH = D / 64, HALF = D / 2;
   constexpr int NS = KS > 16 ? 2 : 1, KSW = KS / NS, WPHS = WPH * NS, HPW = NWAVE / WPHS;
   union Smem {
     S lat;
@@ -286,9 +286,10 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   };
 
   // Latent blocks go from HBM straight into LDS (buffer loads with an LDS
-  // destination, no registers): one load of 64 x 16 bytes fills 1 KB of a
-  // block, KS loads per block spread over the waves.  The buffer covers this
-  // chunk's rows only, so rows past j_end read as zeros.
+  // destination, no registers): one load per token row, its 2 KS lanes writing
+  // 16 bytes each from the row's start (the other lanes idle), wave w loading
+  // rows w, w + 8, ...  The buffer covers this chunk's rows only, so rows past
+  // j_end read as zeros.
   const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const bf16*)p.h_D + ((size_t)b * p.cap + j_begin) * DD), (short)0,
       (int)((size_t)(j_end > j_begin ? j_end - j_begin : 0) * DD * sizeof(bf16)), 0x00020000);
@@ -296,14 +297,12 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   auto issue_blk = [&](int blk) {
     bf16* dst = sm.lat[blk % NBUF];
 #pragma unroll
-    for (int i0 = 0; i0 < KS; i0 += NWAVE) {
-      const int i = i0 + wave;
-      if (KS % NWAVE == 0 || i < KS) {
-        const int row = (64 * i + lane) / CPR, slot = lane % CPR;
-        const int c = slot ^ (row & SWM);
-        const unsigned off = (unsigned)(((blk * TB + row) * DD + 8 * c) * sizeof(bf16));
+    for (int i = 0; i < TB / NWAVE; ++i) {
+      const int row = wave + NWAVE * i;
+      if (CPR == 64 || lane < CPR) {
+        const unsigned off = (unsigned)(((blk * TB + row) * DD + 8 * lane) * sizeof(bf16));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            lrs, (__attribute__((address_space(3))) void*)(dst + 512 * i), 16, off, 0, 0, 0);
+            lrs, (__attribute__((address_space(3))) void*)(dst + row * LP), 16, off, 0, 0, 0);
       }
     }
   };
@@ -344,10 +343,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
         const int n = nb * 16 + row;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          // row & SWM depends on (kg, c % 2) only
-          const int row = 8 * (c >> 1) + 2 * kg + (c & 1);
-          const int colp = 8 * ((n >> 3) ^ ((2 * kg + (c & 1)) & SWM)) + (n & 7);
-          bfr[c] = L[row * DD + colp];
+          bfr[c] = L[(8 * (c >> 1) + 2 * kg + (c & 1)) * LP + n];
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -377,14 +373,8 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
   // Scores of block blk into sc[blk % 2]; cos/sin table of block blk + 1.
   auto scores = [&](int blk) {
     const int pb = blk & 1;
-    // h^D . [alpha | beta] for 32 tokens (lane column lr): logical chunk
-    // 2 KSW sl + 8 (ks / 4) + (2 (ks % 4) + lg) of row lr; the swizzle only
-    // touches the low three bits, so four base addresses serve every ks
-    constexpr int NR = KSW < 4 ? KSW : 4;
-    const bf16* lb[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-      lb[r] = sm.lat[blk % NBUF] + lr * DD + 16 * KSW * sl + 8 * ((2 * r + lg) ^ (lr & SWM));
+    // h^D . [alpha | beta] for 32 tokens (lane column lr)
+    const bf16* lrow = sm.lat[blk % NBUF] + lr * LP + 16 * KSW * sl + 8 * lg;
     f32x16 kc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -392,7 +382,7 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
       for (int r = 0; r < 16; ++r) kc[mb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
-      const bf16x8 lf = *(const bf16x8*)(lb[ks % NR] + 64 * (ks / NR));
+      const bf16x8 lf = *(const bf16x8*)(lrow + 16 * ks);
       kc[0] = mfma32x32x16(gf[0][ks], lf, kc[0]);
       kc[1] = mfma32x32x16(gf[1][ks], lf, kc[1]);
     }
