@@ -136,6 +136,17 @@ def capture(torch, fn, copies=1):
     return g
 
 
+def settle(torch, g, seconds=1.0):
+    """Replays graph g for about `seconds` before anything is timed.  The GPU's
+    clocks ramp up under sustained load: the same step graph measured right
+    after set-up runs about 15% slower than a second later, so the timed
+    region should start from the settled state."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        g.replay()
+        torch.cuda.synchronize()
+
+
 def graph_launch_ms(torch, fn, copies=10, reps=3):
     """Average duration of one call of fn: a graph of `copies` back-to-back
     calls, replayed `reps` times between HIP events on the launch stream."""
@@ -161,6 +172,7 @@ def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
     step = lambda: prefill_step(dar, s, H, d_k, w)
     warm = capture(torch, step, max(warmup, 1))
     timed = capture(torch, step, steps)
+    settle(torch, warm)
     if warmup > 0:
         warm.replay()
     torch.cuda.synchronize()
@@ -271,6 +283,7 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
         lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
         g = capture(torch, lambda: dar.dar_attn_decode_varlen(q, K_win, V_win, h_D, Wk, Wv, lens_d,
                                                               ctx, w, o=o, workspace=ws))
+    settle(torch, g)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
