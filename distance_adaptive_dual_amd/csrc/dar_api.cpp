@@ -115,12 +115,8 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
     return DAR_ERR_UNSUPPORTED;
 
-  // bf16 mode forms RoPE angles in the GEMM epilogue from per-frequency
-  // revolutions passed with the launch; fp32 mode reads fp64-built tables.
-  const bool bf = dtype == DAR_BF16;
   const long max_pos = (long)pos0 + N - 1;
-  if (bf && max_pos >= (1L << 24)) return DAR_ERR_UNSUPPORTED;  // positions exact in fp32
-  const size_t rope_bytes = bf ? 0 : rope_table_bytes(d_k, max_pos);
+  const size_t rope_bytes = rope_table_bytes(d_k, max_pos);
   const size_t fold_bytes = have_fold ? 0 : 2 * round256(es * d_down * hd);
   const size_t need_bytes = rope_bytes + fold_bytes;
   if (workspace == nullptr) {
@@ -138,15 +134,10 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   }
 
   char* wsp = (char*)workspace;
-  float2* lo = nullptr;
-  float2* hi = nullptr;
-  hipError_t e = hipSuccess;
-  if (!bf) {
-    lo = (float2*)wsp;
-    hi = lo + 64 * (d_k / 2);
-    e = launch_rope_tables(lo, hi, d_k, max_pos, rope_base, stream);
-    if (e != hipSuccess) return DAR_ERR_HIP;
-  }
+  float2* lo = (float2*)wsp;
+  float2* hi = lo + 64 * (d_k / 2);
+  hipError_t e = launch_rope_tables(lo, hi, d_k, max_pos, rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
   const void* fK = W_upK;
   const void* fV = W_upV;
   if (!have_fold) {
@@ -161,6 +152,7 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   const RopeTab rope{lo, hi, d_k / 2};
 
   GemmProblem g1{};
+  const bool bf = dtype == DAR_BF16;
   g1.A = h;
   g1.M = (int)M;
   g1.K = d;
@@ -177,7 +169,6 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   g1.d_k = d_k;
   g1.pos0 = pos0;
   g1.rope = rope;
-  if (bf) rope_revolutions(d_k, rope_base, g1.rev);
   e = launch_project_gemm(g1, dtype, stream);
   if (e != hipSuccess) return DAR_ERR_HIP;
 

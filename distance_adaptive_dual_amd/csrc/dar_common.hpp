@@ -120,25 +120,6 @@ __device__ __forceinline__ float2 rope_cs(const RopeTab& t, int pos, int k) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
 
-// RoPE angles without tables: theta_t / (2 pi) in revolutions, held as an
-// fp32 pair phi = hi + lo computed on the host in fp64.  For an integer
-// position p < 2^24, p * hi is split exactly by one fma, the whole turns are
-// removed exactly, and v_cos_f32 / v_sin_f32 (which take revolutions) see an
-// argument in about [-1/2, 1/2].
-__device__ __forceinline__ float rope_rev(int pos, float2 phi) {
-  const float p = (float)pos;
-  const float a = p * phi.x;
-  const float e = fmaf(p, phi.x, -a);
-  return (a - rintf(a)) + fmaf(p, phi.y, e);
-}
-
-__device__ __forceinline__ float2 cos_sin_rev(float f) {
-  return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
-}
-
-// Host: phi_t = theta_t / (2 pi) with theta_t = base^(-2t/d_k), t < d_k/2.
-void rope_revolutions(int d_k, float base, float2* rev);
-
 // ----------------------------------------------------------------------------
 // Internal launchers (defined in the .hip files, called by the C ABI layer).
 // All return hipSuccess or the launch error.
@@ -184,10 +165,7 @@ struct GemmProblem {
   GemmSeg seg[4];
   int n_seq;  // rows per sequence (row -> (b, n))
   int heads, d_k, pos0;
-  // RoPE angles: from the tables when rope.lo is set, otherwise from rev
-  // (bf16 MFMA GEMM only; rev[t] = theta_t / (2 pi), see rope_rev)
   RopeTab rope;
-  float2 rev[64];
   // Ragged append (n_seq == 1): row b is sequence b's token at position
   // row_pos[b] (device, int32), clamped to [0, pos_max] (the last position the
   // RoPE tables hold); an index past a segment's ld_seq is clamped to its last

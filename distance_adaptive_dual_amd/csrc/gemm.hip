@@ -254,23 +254,11 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
   }
 }
 
-// cos/sin(pos * theta_t) for t = t0 .. t0+7: from the tables, or (rope.lo
-// null) from the revolutions p.rev.
-__device__ __forceinline__ void rope_first8(const GemmProblem& p, int pos, int t0,
-                                            float2 (&cs)[8]) {
-  if (p.rope.lo == nullptr) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cs[i] = cos_sin_rev(rope_rev(pos, p.rev[t0 + i]));
-  } else {
-    rope_cs8(p.rope, pos, t0, cs);
-  }
-}
-
 // Tile [128 tokens][EPI_P] -> kHead with RoPE at position pos0 + n on the
 // rotate-half pairs (t, t + D/2).  A lane takes 8 consecutive pairs of one head
 // for 4 consecutive tokens: the angles of the first token come from the
-// tables (or the revolutions), the next ones by one complex multiplication
-// with (cos, sin)(theta_t) each.
+// tables, the next ones by one complex multiplication with (cos, sin)(theta_t)
+// each (the table row for position 1).
 template <typename OutT, int D, bool RP>
 __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int hf, int col0,
                                                 const GemmSeg& seg, const GemmProblem& p) {
@@ -288,19 +276,14 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
   const int b0 = grow0 / Nq, n0 = grow0 % Nq;
   const bool consec = grow0 + 3 < M && n0 + 3 < Nq;  // one sequence, consecutive positions
   float2 cs[8], step[8];
-  rope_first8(p, row_position<RP>(p, b0, n0), t0, cs);
+  rope_cs8(p.rope, row_position<RP>(p, b0, n0), t0, cs);
   if (consec) {
-    if (p.rope.lo == nullptr) {
+    const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) step[i] = cos_sin_rev(p.rev[t0 + i].x);
-    } else {
-      const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 a = st[i];
-        step[2 * i] = make_float2(a.x, a.y);
-        step[2 * i + 1] = make_float2(a.z, a.w);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = st[i];
+      step[2 * i] = make_float2(a.x, a.y);
+      step[2 * i + 1] = make_float2(a.z, a.w);
     }
   }
 #pragma unroll
@@ -317,7 +300,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
         if (grow >= M) break;
         b = grow / Nq;
         n = grow % Nq;
-        rope_first8(p, row_position<RP>(p, b, n), t0, cs);
+        rope_cs8(p.rope, row_position<RP>(p, b, n), t0, cs);
       }
     }
     float x[8], y[8], a[8], bb[8];

@@ -45,17 +45,6 @@ __global__ void rope_tables_kernel(float2* __restrict__ lo, float2* __restrict__
   }
 }
 
-void rope_revolutions(int d_k, float base, float2* rev) {
-  const int half = d_k / 2;
-  const double l2b = std::log2((double)base);
-  const double two_pi = 6.283185307179586232;
-  for (int t = 0; t < half; ++t) {
-    const double phi = exp2(-(double)t / (double)half * l2b) / two_pi;
-    const float hi = (float)phi;
-    rev[t] = make_float2(hi, (float)(phi - (double)hi));
-  }
-}
-
 size_t rope_table_bytes(int d_k, long max_pos) {
   const long n_hi = (max_pos >> 6) + 1;
   const size_t b = sizeof(float2) * (size_t)(d_k / 2) * (size_t)(64 + n_hi);

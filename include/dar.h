@@ -105,11 +105,6 @@ dar_status dar_fold(const void* W_up, const void* W_K, const void* W_V, int d, i
  *   V_glob [B, heads, d_k, N]   h^D W_upV = h' W_V, transposed like V_loc
  * In bf16 mode h^D is rounded to fp16 before the global GEMM (it is the
  * stored latent).  Outputs must not alias inputs or each other.
- * Workspace: DAR_BF16 forms the RoPE angles in the GEMM epilogue (positions
- * must stay below 2^24, DAR_ERR_UNSUPPORTED otherwise) and needs none with
- * folded weights; DAR_FP32 holds fp64-built RoPE tables there.  Either adds
- * room for the folded weights when W_upK / W_upV are NULL.  A size of 0 still
- * takes a non-NULL workspace pointer (NULL asks for the size).
  */
 dar_status dar_project(const void* h, const void* W_down, const void* W_up, const void* W_Q,
                        const void* W_K, const void* W_V, const void* W_upK, const void* W_upV,

@@ -56,13 +56,11 @@ def project(**kw):
 
 def test_project_size_query():
     st, n = project()
-    assert st == OK and n == 0                 # bf16, folded: RoPE angles need no tables
+    assert st == OK and n > 0
     st2, n2 = project(W_upK=None, W_upV=None)  # fold into the workspace
     assert st2 == OK and n2 > n
-    st4, n4 = project(dtype=0)                 # fp32 mode reads RoPE tables
-    assert st4 == OK and n4 > 0
-    st3, n3 = project(dtype=0, N=4096)         # longer RoPE table
-    assert st3 == OK and n3 > n4
+    st3, n3 = project(N=4096)                  # longer RoPE table
+    assert st3 == OK and n3 > n
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -79,17 +77,9 @@ def test_project_rejects(kw, code):
 
 
 def test_project_small_workspace():
-    st, n = project(dtype=0)
-    assert project(dtype=0, ws=F(20), wsb=n - 1)[0] == WS
-    assert project(dtype=0, ws=F(20) + 16, wsb=n)[0] == INVALID  # workspace must be 256-B aligned
-    st, n = project(W_upK=None, W_upV=None)
-    assert project(W_upK=None, W_upV=None, ws=F(20), wsb=n - 1)[0] == WS
-
-
-def test_project_position_limit():
-    # bf16 angles take positions exact in fp32
-    assert project(pos0=(1 << 24) - 128)[0] == OK
-    assert project(pos0=(1 << 24) - 127)[0] == UNSUP
+    st, n = project()
+    assert project(ws=F(20), wsb=n - 1)[0] == WS
+    assert project(ws=F(20) + 16, wsb=n)[0] == INVALID  # workspace must be 256-B aligned
 
 
 def attn(**kw):

@@ -32,7 +32,7 @@ def test_prefill_graph_replays_match_eager():
     W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
     h = dev(inp["h"], "bf16")
     Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
-    ws = torch.empty(max(dar.project_workspace_bytes(B, N, d, dd, H, d_k), 256), dtype=torch.uint8,
+    ws = torch.empty(dar.project_workspace_bytes(B, N, d, dd, H, d_k), dtype=torch.uint8,
                      device="cuda")
     out = dar.dar_project(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
                           W_upK=Wk, W_upV=Wv, workspace=ws)
