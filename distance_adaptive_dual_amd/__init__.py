@@ -120,7 +120,7 @@ def _call_ws(fn: str, f, args, workspace, like, stream):
     """Calls entry point f with a workspace.  A caller-supplied workspace is
     tried first; when none is given (or it is too small) the size is queried
     and a fresh buffer allocated."""
-    if workspace is not None:
+    if workspace is not None and workspace.numel() > 0:  # an empty tensor's pointer is NULL
         n = ctypes.c_size_t(workspace.numel())
         st = f(*args, _ptr(workspace), ctypes.byref(n), _stream(stream))
         if st != 3:  # DAR_ERR_WORKSPACE

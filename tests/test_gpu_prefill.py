@@ -94,6 +94,27 @@ def test_fp32_ragged_and_pos0():
     assert max_err(host(o), ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("pos0,d_k", [(32768 - 40, 64), (2 ** 24 - 96, 128), (1234567, 64)])
+def test_bf16_rope_large_positions(pos0, d_k):
+    """bf16 projections at large positions: the rotation matches the fp64 one
+    to within the fp16 rounding of the output (relative to the magnitude of
+    each rotated pair)."""
+    B, N, d, H, dd, w = 1, 96, 128, 2, 32, 16
+    inp = prefill_case(B, N, d, H, d_k, dd, "bf16", seed=pos0 % 1000 + 5)
+    log("bf16 rope pos0 %d d_k %d" % (pos0, d_k))
+    o, out = run_prefill(inp, H, d_k, w, "bf16", pos0=pos0)
+    ref, _, P = oracle.prefill(inp, H, d_k, w, pos0=pos0)
+    half = d_k // 2
+    for name, r in (("Q", P["Q"]), ("K_loc", P["KL"])):
+        mag = np.sqrt(r[..., :half] ** 2 + r[..., half:] ** 2)
+        mag = np.concatenate([mag, mag], axis=-1)
+        err = np.abs(host(out[name]) - r)
+        worst = float((err / (mag + 1e-6)).max())
+        log("  %s worst err / pair magnitude %.3g" % (name, worst))
+        assert np.all(err <= 2.0 ** -10 * mag + 1e-5), name
+    assert max_err(host(o), ref) <= TOL["bf16"]
+
+
 def test_peaked_softmax_and_hot_rows():
     """W_Q x4 (sharp softmax) and rows of h scaled x8 (scores in the tens).
 
