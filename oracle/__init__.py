@@ -48,6 +48,9 @@ def _load():
         lib.dar_oracle_attend_rows.restype = ctypes.c_int
         lib.dar_oracle_attend_rows.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_long, ctypes.c_int, _I, _I, _I, _D, _D]
+        lib.dar_oracle_attend_backward.restype = ctypes.c_int
+        lib.dar_oracle_attend_backward.argtypes = [_D] * 6 + [ctypes.c_int] * 4 + [
+            ctypes.c_long] + [_D] * 5
         lib.dar_oracle_decode.restype = ctypes.c_int
         lib.dar_oracle_decode.argtypes = [_D] * 7 + [ctypes.c_int, ctypes.c_long, ctypes.c_long] + [
             ctypes.c_int] * 4 + [ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_int, _D]
@@ -120,6 +123,22 @@ def attend_rows(P, w, rows):
     if rc != 0:
         raise ValueError("dar_oracle_attend_rows rejected its arguments")
     return o, rs
+
+
+def attend_backward(P, w, dO):
+    """Gradients of the Eq. 3-4 attention for dL/do = dO [B,N,H*d_k].  Returns
+    dict dQ, dKL, dVL, dKG, dVG, each [B,H,N,d_k] (float64)."""
+    Q, KL, VL, KG, VG = (_f64(P[k]) for k in ("Q", "KL", "VL", "KG", "VG"))
+    dO = _f64(dO)
+    B, H, N, d_k = Q.shape
+    assert dO.shape == (B, N, H * d_k)
+    g = {k: np.zeros((B, H, N, d_k)) for k in ("dQ", "dKL", "dVL", "dKG", "dVG")}
+    rc = _load().dar_oracle_attend_backward(_p(Q), _p(KL), _p(VL), _p(KG), _p(VG), _p(dO), B, N,
+                                            H, d_k, int(w), _p(g["dQ"]), _p(g["dKL"]),
+                                            _p(g["dVL"]), _p(g["dKG"]), _p(g["dVG"]))
+    if rc != 0:
+        raise ValueError("dar_oracle_attend_backward rejected its arguments")
+    return g
 
 
 def prefill(inp, H, d_k, w, pos0=0, base=10000.0):

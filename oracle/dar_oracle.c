@@ -192,6 +192,88 @@ int dar_oracle_attend_rows(const double* Q, const double* KL, const double* VL,
 }
 
 /*
+ * Backward of the attention of Eqs. (3)-(4) for a loss L with dL/do = dO.
+ * The selection of Eq. (3) is a fixed choice per (i, j) pair, so each pair's
+ * gradient flows to the source it used: with p_j = softmax(s)_j over j <= i
+ * and s_j = q_i . k_j / sqrt(d_k),
+ *   dv_j    += p_j dO_i                       (o_i = sum_j p_j v_j)
+ *   dp_j     = dO_i . v_j
+ *   ds_j     = p_j (dp_j - sum_l p_l dp_l)    (derivative of the softmax)
+ *   dq_i    += ds_j k_j / sqrt(d_k),   dk_j += ds_j q_i / sqrt(d_k)
+ * where (k_j, v_j, dk_j, dv_j) belong to the local source when i - j < w and
+ * to the global one otherwise.  dO: [B, N, H*d_k] like o; every gradient is
+ * [B, H, N, d_k] and is overwritten.
+ */
+int dar_oracle_attend_backward(const double* Q, const double* KL, const double* VL,
+                               const double* KG, const double* VG, const double* dO, int B,
+                               int N, int H, int d_k, long w, double* dQ, double* dKL,
+                               double* dVL, double* dKG, double* dVG) {
+  if (B < 1 || N < 1 || H < 1 || d_k < 1 || w < 0) return -1;
+  const size_t n_all = (size_t)B * H * N * d_k;
+  memset(dQ, 0, sizeof(double) * n_all);
+  memset(dKL, 0, sizeof(double) * n_all);
+  memset(dVL, 0, sizeof(double) * n_all);
+  memset(dKG, 0, sizeof(double) * n_all);
+  memset(dVG, 0, sizeof(double) * n_all);
+  const double scale = 1.0 / sqrt((double)d_k);
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (long ba = 0; ba < (long)B * H; ++ba) {
+      const int b = (int)(ba / H), a = (int)(ba % H);
+      const size_t off = (size_t)ba * N;
+      for (int i = 0; i < N; ++i) {
+        const double* q = Q + (off + i) * d_k;
+        const double* g = dO + ((size_t)b * N + i) * H * d_k + (size_t)a * d_k;
+        double m = -INFINITY;
+        for (int j = 0; j <= i; ++j) {
+          const double* k = ((long)(i - j) < w ? KL : KG) + (off + j) * d_k;
+          double dot = 0.0;
+          for (int t = 0; t < d_k; ++t) dot += q[t] * k[t];
+          p[j] = dot * scale;
+          if (p[j] > m) m = p[j];
+        }
+        double Z = 0.0;
+        for (int j = 0; j <= i; ++j) {
+          p[j] = exp(p[j] - m);
+          Z += p[j];
+        }
+        double pdp = 0.0;
+        for (int j = 0; j <= i; ++j) {
+          p[j] /= Z;
+          const int local = (long)(i - j) < w;
+          const double* v = (local ? VL : VG) + (off + j) * d_k;
+          double* dv = (local ? dVL : dVG) + (off + j) * d_k;
+          double dot = 0.0;
+          for (int t = 0; t < d_k; ++t) {
+            dot += g[t] * v[t];
+            dv[t] += p[j] * g[t];
+          }
+          dp[j] = dot;
+          pdp += p[j] * dot;
+        }
+        double* dq = dQ + (off + i) * d_k;
+        for (int j = 0; j <= i; ++j) {
+          const int local = (long)(i - j) < w;
+          const double* k = (local ? KL : KG) + (off + j) * d_k;
+          double* dk = (local ? dKL : dKG) + (off + j) * d_k;
+          const double ds = p[j] * (dp[j] - pdp) * scale;
+          for (int t = 0; t < d_k; ++t) {
+            dq[t] += ds * k[t];
+            dk[t] += ds * q[t];
+          }
+        }
+      }
+    }
+    free(p);
+    free(dp);
+  }
+  return 0;
+}
+
+/*
  * Decode step over the mixed cache, one query per sequence at position
  * p = ctx - 1 (the latent-cache reading of the inference remarks: full keys
  * and values for the w most recent positions, the d_down latent beyond).
