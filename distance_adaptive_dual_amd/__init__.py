@@ -25,7 +25,7 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
-           "dar_attn_prefill", "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
+           "dar_attn_prefill", "dar_attn_prefill_backward", "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
            "dar_attn_decode_varlen")
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.dar_project.argtypes = [_P] * 8 + [_I] * 7 + [ctypes.c_float, _I] + [_P] * 7 + [_SZ, _P]
         L.dar_attn_prefill.restype = _I
         L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P]
+        L.dar_attn_prefill_backward.restype = _I
+        L.dar_attn_prefill_backward.argtypes = [_P] * 7 + [_I] * 6 + [_P] * 6 + [_SZ, _P]
         L.dar_decode_append.restype = _I
         L.dar_decode_append.argtypes = [_P] * 5 + [_I] * 8 + [ctypes.c_float, _I] + [_P] * 5 + [
             _SZ, _P]
@@ -197,6 +199,33 @@ def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None
             _ptr(W_upK), _ptr(W_upV), B, N, d, d_down, heads, d_k, pos0, float(rope_base), dt]
     args += [_ptr(out[k]) for k in ("Q", "K_loc", "V_loc", "h_D", "K_glob", "V_glob")]
     _call_ws("dar_project", lib().dar_project, args, workspace, h, stream)
+    return out
+
+
+def attn_backward_workspace_bytes(B, N, heads, d_k, dtype=DAR_BF16):
+    n = ctypes.c_size_t(0)
+    f = [_fake(i) for i in range(12)]
+    st = lib().dar_attn_prefill_backward(*f[:7], B, N, heads, d_k, 0, dtype, *f[7:], None,
+                                         ctypes.byref(n), None)
+    _check("dar_attn_prefill_backward", st)
+    return n.value
+
+
+def dar_attn_prefill_backward(Q, K_loc, V_loc, K_glob, V_glob, o, dO, w: int, out=None,
+                              workspace=None, stream=None):
+    """Gradients of dar_attn_prefill for dL/do = dO.  Returns dict dQ, dK_loc,
+    dV_loc, dK_glob, dV_glob (float32, [B, heads, N, d_k]; dV not transposed)."""
+    torch = _torch()
+    B, H, N, d_k = Q.shape
+    dt = _dtype_code(Q)
+    if out is None:
+        out = {k: torch.empty((B, H, N, d_k), dtype=torch.float32, device=Q.device)
+               for k in ("dQ", "dK_loc", "dV_loc", "dK_glob", "dV_glob")}
+    args = [_ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(K_glob), _ptr(V_glob), _ptr(o), _ptr(dO),
+            B, N, H, d_k, int(w), dt]
+    args += [_ptr(out[k]) for k in ("dQ", "dK_loc", "dV_loc", "dK_glob", "dV_glob")]
+    _call_ws("dar_attn_prefill_backward", lib().dar_attn_prefill_backward, args, workspace, Q,
+             stream)
     return out
 
 

@@ -14,8 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdar.so")
-SOURCES = ["dar_api.cpp", "rope.hip", "gemm.hip", "attn_prefill.hip", "attn_decode.hip",
-           "cache.hip"]
+SOURCES = ["dar_api.cpp", "rope.hip", "gemm.hip", "attn_prefill.hip", "attn_backward.hip",
+           "attn_decode.hip", "cache.hip"]
 CALIB_LIB = os.path.join(HERE, "libdar_calib.so")
 CALIB_SOURCES = ["calib.hip"]
 HEADERS = ["dar_common.hpp"]

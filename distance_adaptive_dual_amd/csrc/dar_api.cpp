@@ -202,6 +202,64 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
   return hip_status(launch_attn_prefill(p, dtype, stream));
 }
 
+dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const void* V_loc,
+                                     const void* K_glob, const void* V_glob, const void* o,
+                                     const void* dO, int B, int N, int heads, int d_k, int w,
+                                     dar_dtype dtype, float* dQ, float* dK_loc, float* dV_loc,
+                                     float* dK_glob, float* dV_glob, void* workspace,
+                                     size_t* workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || w < 0) return DAR_ERR_INVALID_ARG;
+  const void* need[] = {Q, K_loc, V_loc, K_glob, V_glob, o, dO, dQ, dK_loc, dV_loc, dK_glob,
+                        dV_glob};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  const size_t n_el = (size_t)B * N * heads * d_k;
+  const size_t sz = elem_size(dtype) * n_el, gz = sizeof(float) * n_el;
+  const Span ins[7] = {{Q, sz}, {K_loc, sz}, {V_loc, sz}, {K_glob, sz},
+                       {V_glob, sz}, {o, sz}, {dO, sz}};
+  const Span outs[5] = {{dQ, gz}, {dK_loc, gz}, {dV_loc, gz}, {dK_glob, gz}, {dV_glob, gz}};
+  if (!disjoint(outs, 5, ins, 7)) return DAR_ERR_INVALID_ARG;
+  if (!head_supported(d_k)) return DAR_ERR_UNSUPPORTED;
+  if (n_el > 0x7fffffffffffL || (size_t)B * heads > 0x7fffffff / ((size_t)N + 63))
+    return DAR_ERR_UNSUPPORTED;
+  const size_t need_bytes = attn_backward_workspace_bytes(B, N, heads);
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& x : ins)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+    for (const Span& x : outs)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+  }
+  BwdProblem p{};
+  p.Q = Q;
+  p.K_loc = K_loc;
+  p.V_loc = V_loc;
+  p.K_glob = K_glob;
+  p.V_glob = V_glob;
+  p.o = o;
+  p.dO = dO;
+  p.dQ = dQ;
+  p.dK_loc = dK_loc;
+  p.dV_loc = dV_loc;
+  p.dK_glob = dK_glob;
+  p.dV_glob = dV_glob;
+  p.lse = (float*)workspace;
+  p.Dd = (float*)((char*)workspace + need_bytes / 2);
+  p.B = B;
+  p.N = N;
+  p.H = heads;
+  p.d_k = d_k;
+  p.w = w;
+  return hip_status(launch_attn_backward(p, dtype, stream));
+}
+
 // Decode append, uniform (pos_arr == nullptr: every sequence at position pos)
 // or ragged (pos_arr: device int32[B], sequence b at pos_arr[b] < cap).
 static dar_status decode_append_impl(const void* h, const void* W_down, const void* W_Q,

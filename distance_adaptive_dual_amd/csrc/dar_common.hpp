@@ -191,6 +191,19 @@ struct PrefillProblem {
 };
 hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s);
 
+// Backward of the prefill attention: Q, K_*, V_* in the forward's layouts and
+// types (V transposed per head), o and dO [B, N, H*d_k] (bf16 in bf16 mode);
+// fp32 gradients [B, H, N, d_k] (dV not transposed); lse, Dd: [B, H, N] fp32
+// workspace (per-query log-sum-exp and dO . o).
+struct BwdProblem {
+  const void *Q, *K_loc, *V_loc, *K_glob, *V_glob, *o, *dO;
+  float *dQ, *dK_loc, *dV_loc, *dK_glob, *dV_glob;
+  float *lse, *Dd;
+  int B, N, H, d_k, w;
+};
+size_t attn_backward_workspace_bytes(int B, int N, int H);
+hipError_t launch_attn_backward(const BwdProblem& p, dar_dtype dt, hipStream_t s);
+
 struct DecodeProblem {
   const void *q, *K_win, *V_win, *h_D, *W_upK, *W_upV;
   void* o;

@@ -131,6 +131,33 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
                             int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream);
 
 /*
+ * dar_attn_prefill_backward -- gradients of dar_attn_prefill for dL/do = dO.
+ *
+ * Training remark after Eq. (4): each past token keeps both representations
+ * and each (i, j) pair is served by the one Eq. (3) selects, so its gradient
+ * reaches only that source (the bottleneck weights learn from global pairs).
+ * With s_ij = q_i . k_j / sqrt(d_k), p_ij = softmax over j <= i,
+ * dp_ij = dO_i . v_j, D_i = dO_i . o_i and ds_ij = p_ij (dp_ij - D_i):
+ *   dQ_i = sum_j ds_ij k_j / sqrt(d_k);  dK_j += ds_ij q_i / sqrt(d_k);
+ *   dV_j += p_ij dO_i   (K, V, dK, dV of the pair's source).
+ *   Q, K_loc, V_loc, K_glob, V_glob, w   exactly as given to dar_attn_prefill
+ *                                        (fp16 in DAR_BF16 mode; V transposed)
+ *   o, dO   [B, N, heads*d_k]            the forward output and its gradient
+ *                                        (bf16 in DAR_BF16 mode)
+ * Outputs, float32 in both modes, each written in full:
+ *   dQ, dK_loc, dK_glob, dV_loc, dV_glob [B, heads, N, d_k]  (dV NOT transposed)
+ * Workspace: 8*B*heads*N bytes (rounded) for the per-query log-sum-exp and D.
+ * Outputs must not alias inputs, each other or the workspace.  Supported:
+ * d_k in {64, 128}.  Arithmetic is fp32 on the VALU (no MFMA).
+ */
+dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const void* V_loc,
+                                     const void* K_glob, const void* V_glob, const void* o,
+                                     const void* dO, int B, int N, int heads, int d_k, int w,
+                                     dar_dtype dtype, float* dQ, float* dK_loc, float* dV_loc,
+                                     float* dK_glob, float* dV_glob, void* workspace,
+                                     size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * dar_decode_append -- project one new token per sequence into the mixed cache.
  *
  * The inference remark after Eq. (5) (each past token is used through exactly

@@ -99,6 +99,43 @@ def test_prefill_rejects(kw, code):
     assert attn(**kw) == code
 
 
+def attn_bwd(**kw):
+    a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), o=F(5), dO=F(6), B=1,
+             N=64, heads=2, d_k=64, w=8, dtype=1, dQ=F(7), dK_loc=F(8), dV_loc=F(9),
+             dK_glob=F(10), dV_glob=F(11), ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    st = dar.lib().dar_attn_prefill_backward(
+        a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"], a["o"], a["dO"], a["B"], a["N"],
+        a["heads"], a["d_k"], a["w"], a["dtype"], a["dQ"], a["dK_loc"], a["dV_loc"], a["dK_glob"],
+        a["dV_glob"], a["ws"], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_backward_size_query():
+    st, n = attn_bwd()
+    assert st == OK and n == 2 * 512  # lse and D: 4 bytes per (b, head, query), 256-B rounded
+    assert attn_bwd(N=1000, heads=4, B=3)[1] == 2 * ((4 * 3 * 4 * 1000 + 255) // 256 * 256)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=-1), INVALID), (dict(N=0), INVALID), (dict(dO=None), INVALID),
+    (dict(dQ=F(0)), INVALID),          # gradient aliases an input
+    (dict(dV_glob=F(7)), INVALID),     # two gradients alias
+    (dict(o=F(5) + 8), INVALID),       # misaligned
+    (dict(dtype=3), INVALID), (dict(d_k=96), UNSUP),
+])
+def test_backward_rejects(kw, code):
+    assert attn_bwd(**kw)[0] == code
+
+
+def test_backward_workspace_checks():
+    _, n = attn_bwd()
+    assert attn_bwd(ws=F(20), wsb=n - 1)[0] == WS
+    assert attn_bwd(ws=F(20) + 16, wsb=n)[0] == INVALID
+    assert attn_bwd(ws=F(7), wsb=n)[0] == INVALID  # workspace overlaps a gradient
+
+
 def decode(**kw):
     a = dict(q=F(0), K_win=F(1), V_win=F(2), h_D=F(3), W_upK=F(4), W_upV=F(5), B=2, ctx=1000,
              cap=1000, heads=4, d_k=128, d_down=256, w=128, base=10000.0, dtype=1, o=F(6),
