@@ -315,6 +315,41 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
             "bytes": byts, "flops": flops}
 
 
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
+
+
+def time_backward(torch, dar, di, cfg, reps):
+    """dar_attn_prefill_backward on seeded fp16 Q/K/V, the forward's o and a
+    seeded bf16 dO.  Algorithmic work: four products of 2 d_k FLOP per causal
+    pair (dV, dP, dQ, dK); the kernels also recompute the scores (twice) and
+    dP (twice), on the VALU in fp32."""
+    B, N, H, d_k, w = cfg
+
+    def g(i, shape, t):
+        x = torch.from_numpy(di.gaussian(7000 + i, shape, 1.0, t)).to(torch.float32)
+        return x.to(torch.float16 if t == "f16" else torch.bfloat16).cuda()
+
+    qk = (B, H, N, d_k)
+    vt = (B, H, d_k, N)
+    Q, KL, KG = g(0, qk, "f16"), g(1, qk, "f16"), g(2, qk, "f16")
+    VL, VG = g(3, vt, "f16"), g(4, vt, "f16")
+    dO = g(5, (B, N, H * d_k), "bf16")
+    o = dar.dar_attn_prefill(Q, KL, VL, KG, VG, w)
+    out = {k: torch.empty(qk, dtype=torch.float32, device="cuda")
+           for k in ("dQ", "dK_loc", "dV_loc", "dK_glob", "dV_glob")}
+    ws = torch.empty(max(dar.attn_backward_workspace_bytes(B, N, H, d_k), 256),
+                     dtype=torch.uint8, device="cuda")
+    fn = lambda: dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dO, w, out=out,
+                                               workspace=ws)
+    ms = graph_launch_ms(torch, fn, copies=3, reps=reps)
+    flops = 4.0 * B * H * d_k * N * (N + 1)
+    tf = flops / ms / 1e9
+    return {"workload": "attention backward B%d N%d H%d dk%d w%d (bf16 inputs, fp32 grads)"
+                        % (B, N, H, d_k, w),
+            "ms": ms, "TFLOP/s": tf, "flops": flops, "bound": "alu",
+            "peak": PEAK_FP32_VALU_TFLOPS, "frac": tf / PEAK_FP32_VALU_TFLOPS}
+
+
 def calibrate(torch):
     """Measured peaks on this device: dense fp16 MFMA rate and HBM copy
     bandwidth (libdar_calib.so), to read the kernels' rates against."""
@@ -375,7 +410,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline leg")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -473,6 +508,11 @@ def main():
             ch["workload"] = "1b prompt B4 N8192 in chunks of 2048 over the mixed cache"
             res["chunked_prefill"] = ch
             log("chunked prefill: %.3f ms, %.1f TFLOP/s" % (ch["ms"], ch["TFLOP/s"]))
+        torch.cuda.empty_cache()
+    if args.only in ("all", "backward") and not args.no_sweep:
+        bw = time_backward(torch, dar, di, (B, N, H, d_k, w), 2)
+        res["backward"] = bw
+        log("backward: %.3f ms, %.1f TFLOP/s" % (bw["ms"], bw["TFLOP/s"]))
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         log("decode: building the 32k-context cache")

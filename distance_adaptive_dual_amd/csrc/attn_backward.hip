@@ -251,6 +251,369 @@ __global__ __launch_bounds__(256) void bwd_dkv(BwdProblem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA kernels (bf16 mode, fp16 Q/K/V).  32x32x16 fp16 MFMAs with fp32
+// accumulation; softmax in base 2 (lse2_i = log2 sum_j 2^(s_ij log2(e)/sqrt(d_k))).
+// Operand layout of mfma32x32x16: lane l gives row / column l % 32 and
+// contraction elements 8 (l / 32) .. +8 of each 16-wide step; result
+// register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+// Feeding the rows of the first product in the order row_perm (bits 2 and 3
+// of the row index swapped) makes result registers 8u .. 8u+7 of lane l the
+// rows 16u + 8 (l / 32) .. +8: exactly the B operand of a later product that
+// contracts over those rows.
+constexpr int MQ = 128;  // queries (bwd_dq_mfma) or keys (bwd_dkv_mfma) per workgroup
+constexpr int MB = 32;   // keys or queries per staged block
+
+__device__ __forceinline__ int row_perm(int r) {  // swap bits 2 and 3
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Row offset (within a 32-row block fed through row_perm) of result register r.
+__device__ __forceinline__ constexpr int perm_row(int r, int lg) {
+  return 16 * (r >> 3) + 8 * lg + (r & 7);
+}
+
+// Pair classification of a 32 x 32 block for one source, from the distance
+// range of its pairs: any kept pair, and whether the element mask is needed.
+// Kept pairs: local 0 <= i - j < w, global i - j >= w, with i, j < N.
+struct BlockPass {
+  bool part, masked;
+};
+__device__ __forceinline__ BlockPass block_pass(int src, int q0, int k0, int N, int w) {
+  const int q_last = min(q0 + 31, N - 1), k_last = min(k0 + 31, N - 1);
+  const int dmax = q_last - k0, dmin = q0 - k_last;
+  BlockPass r{false, false};
+  if (q0 >= N || k0 >= N || dmax < 0) return r;
+  if (src == 0) {
+    r.part = w > 0 && max(dmin, 0) < w;
+    r.masked = dmin < 0 || dmax >= w;
+  } else {
+    r.part = dmax >= w;
+    r.masked = dmin < w;
+  }
+  r.masked = r.masked || q0 + 32 > N || k0 + 32 > N;
+  return r;
+}
+
+__device__ __forceinline__ bool keep_pair(int src, int dist, int w) {
+  return src == 0 ? (dist >= 0 && dist < w) : dist >= w;
+}
+
+// Stages 32 rows (positions r0 .. r0+31, zero past N) of a row-major fp16
+// [n][D] array as rows of pitch RP and, transposed, as [d][row] of pitch TP.
+template <int D, int RP, int TP>
+__device__ __forceinline__ void stage_rows(const f16* src, int r0, int N, f16* rows, f16* cols) {
+  for (int c = threadIdx.x; c < MB * D / 8; c += 256) {
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + row < N) v = *(const u32x4*)(src + (size_t)(r0 + row) * D + col);
+    *(u32x4*)(rows + row * RP + col) = v;
+    const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cols[(col + e) * TP + row] = h[e];
+  }
+}
+
+template <int D>
+struct DqSmem {
+  static constexpr int RP = D + 8;   // fp16 pitch of [key][d] rows
+  static constexpr int TP = MB + 8;  // fp16 pitch of [d][key] rows
+  f16 k[MB * RP];
+  f16 kt[D * TP];
+  f16 v[MB * RP];
+};
+
+// dq and the per-query statistics (lse2, D) for the key-stationary kernel.
+// Workgroup: 128 queries of one (batch, head), a wave per 32; key blocks of 32
+// staged per source.  S^T = K Q^T keeps a query per lane; dP^T = V dO^T;
+// dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
+  constexpr int NS = D / 16, NB = D / 32;
+  constexpr int RP = DqSmem<D>::RP, TP = DqSmem<D>::TP;
+  __shared__ DqSmem<D> sm;
+  const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
+  const int nQT = (N + MQ - 1) / MQ;
+  const int qt = nQT - 1 - (int)(blockIdx.x / BH);  // longest first
+  const int bh = (int)(blockIdx.x % BH), b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int q0 = qt * MQ, qw0 = q0 + 32 * wave, qi = qw0 + lr;
+  const int qc = qi < N ? qi : N - 1;
+  const f16* Qp = (const f16*)p.Q + (size_t)bh * N * D;
+  const f16* Kp[2] = {(const f16*)p.K_loc + (size_t)bh * N * D,
+                      (const f16*)p.K_glob + (size_t)bh * N * D};
+  const f16* Vp[2] = {(const f16*)p.V_loc + (size_t)bh * D * N,
+                      (const f16*)p.V_glob + (size_t)bh * D * N};
+  const float sc2 = kLog2e / sqrtf((float)D);
+
+  f16x8 qf[NS], gf[NS];
+  float Dd = 0.f;
+  {
+    const size_t orow = ((size_t)b * N + qc) * (size_t)(H * D) + (size_t)h * D;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int d0 = 16 * st + 8 * lg;
+      qf[st] = *(const f16x8*)(Qp + (size_t)qc * D + d0);
+      const u32x4 g = *(const u32x4*)((const bf16*)p.dO + orow + d0);
+      const u32x4 o = *(const u32x4*)((const bf16*)p.o + orow + d0);
+      gf[st] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(g));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Dd = fmaf(__uint_as_float(g[e] << 16), __uint_as_float(o[e] << 16), Dd);
+        Dd = fmaf(__uint_as_float(g[e] & 0xffff0000u), __uint_as_float(o[e] & 0xffff0000u), Dd);
+      }
+    }
+  }
+  Dd += __shfl_xor(Dd, 32);  // the other half of the dims
+
+  const int i_last = min(q0 + MQ, N) - 1;
+  const int wi_last = min(qw0 + 31, N - 1);
+  auto need = [&](int src, int j0) {  // does any wave of the workgroup have pairs here?
+    const int dmax = i_last - j0, dmin = q0 - min(j0 + 31, N - 1);
+    if (dmax < 0) return false;
+    return src == 0 ? (w > 0 && max(dmin, 0) < w) : dmax >= w;
+  };
+  auto scores = [&](f32x16& s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      s = mfma32x32x16(*(const f16x8*)(sm.k + row_perm(lr) * RP + 16 * st + 8 * lg), qf[st], s);
+  };
+  auto mask = [&](f32x16& s, int src, int j0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + perm_row(r, lg);
+      if (!(j < N && keep_pair(src, qi - j, w))) s[r] = -INFINITY;
+    }
+  };
+
+  // sweep 1: lse2 of each query (max and sum per lane half, then combined)
+  float m = -INFINITY, l = 0.f;
+  for (int j0 = 0; j0 <= i_last; j0 += MB) {
+    for (int src = 1; src >= 0; --src) {
+      if (!need(src, j0)) continue;
+      __syncthreads();
+      for (int c = tid; c < MB * D / 8; c += 256) {
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j0 + row < N) v = *(const u32x4*)(Kp[src] + (size_t)(j0 + row) * D + col);
+        *(u32x4*)(sm.k + row * RP + col) = v;
+      }
+      __syncthreads();
+      const BlockPass bp = block_pass(src, qw0, j0, N, w);
+      if (!bp.part) continue;
+      f32x16 s;
+      scores(s);
+      if (bp.masked) mask(s, src, j0);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      mt *= sc2;
+      const float m_new = fmaxf(m, mt);
+      if (m_new > -INFINITY) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -m_new));
+        l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
+        m = m_new;
+      }
+    }
+  }
+  {
+    const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+    const float mm = fmaxf(m, mo);
+    l = (m > -INFINITY ? l * __builtin_amdgcn_exp2f(m - mm) : 0.f) +
+        (mo > -INFINITY ? lo * __builtin_amdgcn_exp2f(mo - mm) : 0.f);
+    m = mm;
+  }
+  const float lse2 = m + __log2f(l);
+  if (qi < N && lg == 0) {
+    p.lse[(size_t)bh * N + qi] = lse2;
+    p.Dd[(size_t)bh * N + qi] = Dd;
+  }
+
+  // sweep 2: dQ^T += K^T (P^T (dP^T - D))
+  f32x16 dq[NB];
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+  for (int j0 = 0; j0 <= i_last; j0 += MB) {
+    for (int src = 1; src >= 0; --src) {
+      if (!need(src, j0)) continue;
+      __syncthreads();
+      stage_rows<D, RP, TP>(Kp[src], j0, N, sm.k, sm.kt);
+      for (int c = tid; c < MB * D / 8; c += 256) {  // V^T [d][n] -> rows [key][d]
+        const int d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
+        const f16* vsrc = Vp[src] + (size_t)d * N + j0 + kc;
+        if ((N & 7) == 0 && j0 + kc + 8 <= N) {
+          const f16x8 v = *(const f16x8*)vsrc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sm.v[(kc + e) * RP + d] = v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sm.v[(kc + e) * RP + d] = j0 + kc + e < N ? vsrc[e] : (f16)0.f;
+        }
+      }
+      __syncthreads();
+      const BlockPass bp = block_pass(src, qw0, j0, N, w);
+      if (!bp.part) continue;
+      f32x16 s, dp;
+      scores(s);
+      if (bp.masked) mask(s, src, j0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+        dp = mfma32x32x16(*(const f16x8*)(sm.v + row_perm(lr) * RP + 16 * st + 8 * lg), gf[st], dp);
+      f16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
+        dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - Dd));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+          dq[db] = mfma32x32x16(*(const f16x8*)(sm.kt + (32 * db + lr) * TP + 16 * u + 8 * lg),
+                                dsb[u], dq[db]);
+    }
+  }
+  if (qi < N) {
+    const float sc = 1.f / sqrtf((float)D);
+    float* out = p.dQ + ((size_t)bh * N + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = 32 * db + 8 * a + 4 * lg;
+        *(float4*)(out + d) = make_float4(dq[db][4 * a] * sc, dq[db][4 * a + 1] * sc,
+                                          dq[db][4 * a + 2] * sc, dq[db][4 * a + 3] * sc);
+      }
+  }
+}
+
+template <int D>
+struct DkvSmem {
+  static constexpr int RP = D + 8;   // fp16 pitch of [query][d] rows
+  static constexpr int TP = MB + 8;  // fp16 pitch of [d][query] rows
+  f16 q[MB * RP];
+  f16 qt[D * TP];
+  f16 g[MB * RP];
+  f16 gt[D * TP];
+  float lse[MB], Dd[MB];
+};
+
+// dK and dV of each source.  Workgroup: 128 keys of one (batch, head), a wave
+// per 32; query blocks of 32 (Q, dO, lse2, D) staged in LDS, one sweep per
+// source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
+// dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_mfma(BwdProblem p) {
+  constexpr int NS = D / 16, NB = D / 32;
+  constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP;
+  __shared__ DkvSmem<D> sm;
+  const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
+  const int kt = (int)(blockIdx.x / BH);  // small key tiles (most queries) first
+  const int bh = (int)(blockIdx.x % BH), b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int k0 = kt * MQ, kw0 = k0 + 32 * wave, kj = kw0 + lr;
+  const int kc = kj < N ? kj : N - 1;
+  const f16* Qp = (const f16*)p.Q + (size_t)bh * N * D;
+  const float sc2 = kLog2e / sqrtf((float)D), sc = 1.f / sqrtf((float)D);
+  const int k_last = min(k0 + MQ, N) - 1;
+
+  for (int src = 0; src < 2; ++src) {
+    const f16* Kp = (const f16*)(src ? p.K_glob : p.K_loc) + (size_t)bh * N * D;
+    const f16* Vp = (const f16*)(src ? p.V_glob : p.V_loc) + (size_t)bh * D * N;
+    f16x8 kf[NS], vf[NS];  // this lane's key, dims 16 st + 8 lg .. +8
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      kf[st] = *(const f16x8*)(Kp + (size_t)kc * D + 16 * st + 8 * lg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[st][e] = Vp[(size_t)(16 * st + 8 * lg + e) * N + kc];
+    }
+    f32x16 dvt[NB], dkt[NB];
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dvt[db][r] = dkt[db][r] = 0.f;
+    // queries with a pair of this source for some key of the workgroup
+    const int i_begin = src == 0 ? k0 : min(N, k0 + w) / MB * MB;
+    const int i_end = src == 0 ? min(N, k_last + w) : N;
+    for (int i0 = i_begin; i0 < i_end; i0 += MB) {
+      __syncthreads();
+      stage_rows<D, RP, TP>(Qp, i0, N, sm.q, sm.qt);
+      for (int c = tid; c < MB * D / 8; c += 256) {  // dO rows, bf16 -> fp16
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (i0 + row < N)
+          v = bf16x8_to_f16x8(*(const u32x4*)((const bf16*)p.dO +
+                                              ((size_t)b * N + i0 + row) * (size_t)(H * D) +
+                                              (size_t)h * D + col));
+        *(u32x4*)(sm.g + row * RP + col) = v;
+        const f16x8 hv = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.gt[(col + e) * TP + row] = hv[e];
+      }
+      if (tid < MB) {
+        const int i = i0 + tid;
+        sm.lse[tid] = i < N ? p.lse[(size_t)bh * N + i] : 0.f;
+        sm.Dd[tid] = i < N ? p.Dd[(size_t)bh * N + i] : 0.f;
+      }
+      __syncthreads();
+      const BlockPass bp = block_pass(src, i0, kw0, N, w);
+      if (!bp.part) continue;
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = mfma32x32x16(*(const f16x8*)(sm.q + row_perm(lr) * RP + 16 * st + 8 * lg), kf[st], s);
+        dp = mfma32x32x16(*(const f16x8*)(sm.g + row_perm(lr) * RP + 16 * st + 8 * lg), vf[st],
+                          dp);
+      }
+      f16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qo = perm_row(r, lg);
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -sm.lse[qo]));
+        if (bp.masked) {
+          const int i = i0 + qo;
+          if (!(i < N && kj < N && keep_pair(src, i - kj, w))) pr = 0.f;
+        }
+        pb[r >> 3][r & 7] = (f16)pr;
+        dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - sm.Dd[qo]));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt + (32 * db + lr) * TP + 16 * u + 8 * lg),
+                                 pb[u], dvt[db]);
+          dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt + (32 * db + lr) * TP + 16 * u + 8 * lg),
+                                 dsb[u], dkt[db]);
+        }
+    }
+    if (kj < N) {
+      float* dK = (src ? p.dK_glob : p.dK_loc) + ((size_t)bh * N + kj) * D;
+      float* dV = (src ? p.dV_glob : p.dV_loc) + ((size_t)bh * N + kj) * D;
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d = 32 * db + 8 * a + 4 * lg;
+          *(float4*)(dK + d) = make_float4(dkt[db][4 * a] * sc, dkt[db][4 * a + 1] * sc,
+                                           dkt[db][4 * a + 2] * sc, dkt[db][4 * a + 3] * sc);
+          *(float4*)(dV + d) = make_float4(dvt[db][4 * a], dvt[db][4 * a + 1],
+                                           dvt[db][4 * a + 2], dvt[db][4 * a + 3]);
+        }
+    }
+  }
+}
+
 }  // namespace
 
 size_t attn_backward_workspace_bytes(int B, int N, int H) {
@@ -272,8 +635,12 @@ hipError_t launch_attn_backward(const BwdProblem& p_in, dar_dtype dt, hipStream_
     hipLaunchKernelGGL((bwd_dkv<BFV, DV>), g2, dim3(256), 0, s, p);        \
   } while (0)
   const bool bf = dt == DAR_BF16;
-  if (p.d_k == 64) {
-    if (bf) DAR_BWD(true, 64); else DAR_BWD(false, 64);
+  if (p.d_k == 64 && bf) {
+    const int nT = (p.N + MQ - 1) / MQ;
+    hipLaunchKernelGGL((bwd_dq_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkv_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
+  } else if (p.d_k == 64) {
+    DAR_BWD(false, 64);
   } else {
     if (bf) DAR_BWD(true, 128); else DAR_BWD(false, 128);
   }
