@@ -315,14 +315,11 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
             "bytes": byts, "flops": flops}
 
 
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
-
-
 def time_backward(torch, dar, di, cfg, reps):
     """dar_attn_prefill_backward on seeded fp16 Q/K/V, the forward's o and a
     seeded bf16 dO.  Algorithmic work: four products of 2 d_k FLOP per causal
-    pair (dV, dP, dQ, dK); the kernels also recompute the scores (twice) and
-    dP (twice), on the VALU in fp32."""
+    pair (dV, dP, dQ, dK); the MFMA kernels also recompute the scores (three
+    times: the lse sweep, dq, dK/dV) and dP (twice)."""
     B, N, H, d_k, w = cfg
 
     def g(i, shape, t):
@@ -346,8 +343,8 @@ def time_backward(torch, dar, di, cfg, reps):
     tf = flops / ms / 1e9
     return {"workload": "attention backward B%d N%d H%d dk%d w%d (bf16 inputs, fp32 grads)"
                         % (B, N, H, d_k, w),
-            "ms": ms, "TFLOP/s": tf, "flops": flops, "bound": "alu",
-            "peak": PEAK_FP32_VALU_TFLOPS, "frac": tf / PEAK_FP32_VALU_TFLOPS}
+            "ms": ms, "TFLOP/s": tf, "flops": flops, "bound": "mfma",
+            "peak": PEAK_BF16_TFLOPS, "frac": tf / PEAK_BF16_TFLOPS}
 
 
 def calibrate(torch):

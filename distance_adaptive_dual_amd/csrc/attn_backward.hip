@@ -296,7 +296,7 @@ __device__ __forceinline__ BlockPass block_pass(int src, int q0, int k0, int N, 
 }
 
 __device__ __forceinline__ bool keep_pair(int src, int dist, int w) {
-  return src == 0 ? (dist >= 0 && dist < w) : dist >= w;
+  return src == 0 ? (unsigned)dist < (unsigned)w : dist >= w;
 }
 
 // Stages 32 rows (positions r0 .. r0+31, zero past N) of a row-major fp16
@@ -318,15 +318,16 @@ template <int D>
 struct DqSmem {
   static constexpr int RP = D + 8;   // fp16 pitch of [key][d] rows
   static constexpr int TP = MB + 8;  // fp16 pitch of [d][key] rows
-  f16 k[MB * RP];
-  f16 kt[D * TP];
-  f16 v[MB * RP];
+  f16 k[2][MB * RP];                 // [buffer]
+  f16 kt[2][D * TP];
+  f16 v[2][MB * RP];
 };
 
 // dq and the per-query statistics (lse2, D) for the key-stationary kernel.
 // Workgroup: 128 queries of one (batch, head), a wave per 32; key blocks of 32
-// staged per source.  S^T = K Q^T keeps a query per lane; dP^T = V dO^T;
-// dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
+// staged per source into a double LDS buffer (the next pass is staged while
+// the current one is computed, one barrier per pass).  S^T = K Q^T keeps a
+// query per lane; dP^T = V dO^T; dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
@@ -367,57 +368,95 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
   Dd += __shfl_xor(Dd, 32);  // the other half of the dims
 
   const int i_last = min(q0 + MQ, N) - 1;
-  const int wi_last = min(qw0 + 31, N - 1);
   auto need = [&](int src, int j0) {  // does any wave of the workgroup have pairs here?
     const int dmax = i_last - j0, dmin = q0 - min(j0 + 31, N - 1);
     if (dmax < 0) return false;
     return src == 0 ? (w > 0 && max(dmin, 0) < w) : dmax >= w;
   };
-  auto scores = [&](f32x16& s) {
+  // Passes: for each key block, the global source (if needed) then the local
+  // one; every block j0 <= i_last needs at least one.
+  auto next_pass = [&](int& j0, int& src) {
+    if (src == 1 && need(0, j0)) {
+      src = 0;
+    } else {
+      j0 += MB;
+      src = need(1, j0) ? 1 : 0;
+    }
+  };
+  auto stage_k = [&](int j0, int src, int bf) {
+    for (int c = tid; c < MB * D / 8; c += 256) {
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j0 + row < N) v = *(const u32x4*)(Kp[src] + (size_t)(j0 + row) * D + col);
+      *(u32x4*)(sm.k[bf] + row * RP + col) = v;
+    }
+  };
+  auto stage_all = [&](int j0, int src, int bf) {
+    stage_rows<D, RP, TP>(Kp[src], j0, N, sm.k[bf], sm.kt[bf]);
+    for (int c = tid; c < MB * D / 8; c += 256) {  // V^T [d][n] -> rows [key][d]
+      const int d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
+      const f16* vsrc = Vp[src] + (size_t)d * N + j0 + kc;
+      f16* vdst = sm.v[bf] + kc * RP + d;
+      if ((N & 7) == 0 && j0 + kc + 8 <= N) {
+        const f16x8 v = *(const f16x8*)vsrc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vdst[e * RP] = v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vdst[e * RP] = j0 + kc + e < N ? vsrc[e] : (f16)0.f;
+      }
+    }
+  };
+  auto scores = [&](f32x16& s, int bf) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      s = mfma32x32x16(*(const f16x8*)(sm.k + row_perm(lr) * RP + 16 * st + 8 * lg), qf[st], s);
+      s = mfma32x32x16(*(const f16x8*)(sm.k[bf] + row_perm(lr) * RP + 16 * st + 8 * lg), qf[st],
+                       s);
   };
   auto mask = [&](f32x16& s, int src, int j0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + perm_row(r, lg);
-      if (!(j < N && keep_pair(src, qi - j, w))) s[r] = -INFINITY;
+      s[r] = ((j < N) & keep_pair(src, qi - j, w)) ? s[r] : -INFINITY;
     }
   };
 
   // sweep 1: lse2 of each query (max and sum per lane half, then combined)
   float m = -INFINITY, l = 0.f;
-  for (int j0 = 0; j0 <= i_last; j0 += MB) {
-    for (int src = 1; src >= 0; --src) {
-      if (!need(src, j0)) continue;
-      __syncthreads();
-      for (int c = tid; c < MB * D / 8; c += 256) {
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (j0 + row < N) v = *(const u32x4*)(Kp[src] + (size_t)(j0 + row) * D + col);
-        *(u32x4*)(sm.k + row * RP + col) = v;
-      }
-      __syncthreads();
+  {
+    int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
+    stage_k(j0, src, bf);
+    __syncthreads();
+    while (true) {
+      int nj0 = j0, nsrc = src;
+      next_pass(nj0, nsrc);
+      const bool has_next = nj0 <= i_last;
+      if (has_next) stage_k(nj0, nsrc, bf ^ 1);
       const BlockPass bp = block_pass(src, qw0, j0, N, w);
-      if (!bp.part) continue;
-      f32x16 s;
-      scores(s);
-      if (bp.masked) mask(s, src, j0);
-      float mt = -INFINITY;
+      if (bp.part) {
+        f32x16 s;
+        scores(s, bf);
+        if (bp.masked) mask(s, src, j0);
+        float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
-      mt *= sc2;
-      const float m_new = fmaxf(m, mt);
-      if (m_new > -INFINITY) {
-        float acc = 0.f;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
+        mt *= sc2;
+        const float m_new = fmaxf(m, mt);
+        if (m_new > -INFINITY) {
+          float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -m_new));
-        l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
-        m = m_new;
+          for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -m_new));
+          l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
+          m = m_new;
+        }
       }
+      __syncthreads();
+      if (!has_next) break;
+      j0 = nj0;
+      src = nsrc;
+      bf ^= 1;
     }
   }
   {
@@ -439,46 +478,45 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
   for (int db = 0; db < NB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
-  for (int j0 = 0; j0 <= i_last; j0 += MB) {
-    for (int src = 1; src >= 0; --src) {
-      if (!need(src, j0)) continue;
-      __syncthreads();
-      stage_rows<D, RP, TP>(Kp[src], j0, N, sm.k, sm.kt);
-      for (int c = tid; c < MB * D / 8; c += 256) {  // V^T [d][n] -> rows [key][d]
-        const int d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
-        const f16* vsrc = Vp[src] + (size_t)d * N + j0 + kc;
-        if ((N & 7) == 0 && j0 + kc + 8 <= N) {
-          const f16x8 v = *(const f16x8*)vsrc;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sm.v[(kc + e) * RP + d] = v[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sm.v[(kc + e) * RP + d] = j0 + kc + e < N ? vsrc[e] : (f16)0.f;
-        }
-      }
-      __syncthreads();
+  {
+    int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
+    stage_all(j0, src, bf);
+    __syncthreads();
+    while (true) {
+      int nj0 = j0, nsrc = src;
+      next_pass(nj0, nsrc);
+      const bool has_next = nj0 <= i_last;
+      if (has_next) stage_all(nj0, nsrc, bf ^ 1);
       const BlockPass bp = block_pass(src, qw0, j0, N, w);
-      if (!bp.part) continue;
-      f32x16 s, dp;
-      scores(s);
-      if (bp.masked) mask(s, src, j0);
+      if (bp.part) {
+        f32x16 s, dp;
+        scores(s, bf);
+        if (bp.masked) mask(s, src, j0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
-        dp = mfma32x32x16(*(const f16x8*)(sm.v + row_perm(lr) * RP + 16 * st + 8 * lg), gf[st], dp);
-      f16x8 dsb[2];
+        for (int st = 0; st < NS; ++st)
+          dp = mfma32x32x16(*(const f16x8*)(sm.v[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
+                            gf[st], dp);
+        f16x8 dsb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
-        dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - Dd));
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
+          dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - Dd));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < NB; ++db)
+            dq[db] = mfma32x32x16(
+                *(const f16x8*)(sm.kt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), dsb[u],
+                dq[db]);
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < NB; ++db)
-          dq[db] = mfma32x32x16(*(const f16x8*)(sm.kt + (32 * db + lr) * TP + 16 * u + 8 * lg),
-                                dsb[u], dq[db]);
+      __syncthreads();
+      if (!has_next) break;
+      j0 = nj0;
+      src = nsrc;
+      bf ^= 1;
     }
   }
   if (qi < N) {
@@ -499,19 +537,19 @@ template <int D>
 struct DkvSmem {
   static constexpr int RP = D + 8;   // fp16 pitch of [query][d] rows
   static constexpr int TP = MB + 8;  // fp16 pitch of [d][query] rows
-  f16 q[MB * RP];
-  f16 qt[D * TP];
-  f16 g[MB * RP];
-  f16 gt[D * TP];
-  float lse[MB], Dd[MB];
+  f16 q[2][MB * RP];                 // [buffer]
+  f16 qt[2][D * TP];
+  f16 g[2][MB * RP];
+  f16 gt[2][D * TP];
+  float lse[2][MB], Dd[2][MB];
 };
 
 // dK and dV of each source.  Workgroup: 128 keys of one (batch, head), a wave
-// per 32; query blocks of 32 (Q, dO, lse2, D) staged in LDS, one sweep per
-// source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
+// per 32; query blocks of 32 (Q, dO, lse2, D) staged into a double LDS buffer,
+// one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
 // dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkv_mfma(BwdProblem p) {
+__global__ __launch_bounds__(256, 2) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP;
   __shared__ DkvSmem<D> sm;
@@ -525,6 +563,28 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma(BwdProblem p) {
   const float sc2 = kLog2e / sqrtf((float)D), sc = 1.f / sqrtf((float)D);
   const int k_last = min(k0 + MQ, N) - 1;
 
+  auto stage = [&](int i0, int bf) {
+    stage_rows<D, RP, TP>(Qp, i0, N, sm.q[bf], sm.qt[bf]);
+    for (int c = tid; c < MB * D / 8; c += 256) {  // dO rows, bf16 -> fp16
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (i0 + row < N)
+        v = bf16x8_to_f16x8(*(const u32x4*)((const bf16*)p.dO +
+                                            ((size_t)b * N + i0 + row) * (size_t)(H * D) +
+                                            (size_t)h * D + col));
+      *(u32x4*)(sm.g[bf] + row * RP + col) = v;
+      const f16x8 hv = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.gt[bf][(col + e) * TP + row] = hv[e];
+    }
+    if (tid < MB) {
+      const int i = i0 + tid;
+      sm.lse[bf][tid] = i < N ? p.lse[(size_t)bh * N + i] : 0.f;
+      sm.Dd[bf][tid] = i < N ? p.Dd[(size_t)bh * N + i] : 0.f;
+    }
+  };
+
+#pragma unroll 1
   for (int src = 0; src < 2; ++src) {
     const f16* Kp = (const f16*)(src ? p.K_glob : p.K_loc) + (size_t)bh * N * D;
     const f16* Vp = (const f16*)(src ? p.V_glob : p.V_loc) + (size_t)bh * D * N;
@@ -543,59 +603,54 @@ __global__ __launch_bounds__(256) void bwd_dkv_mfma(BwdProblem p) {
     // queries with a pair of this source for some key of the workgroup
     const int i_begin = src == 0 ? k0 : min(N, k0 + w) / MB * MB;
     const int i_end = src == 0 ? min(N, k_last + w) : N;
-    for (int i0 = i_begin; i0 < i_end; i0 += MB) {
+    if (i_begin < i_end) {
+      int i0 = i_begin, bf = 0;
+      stage(i0, bf);
       __syncthreads();
-      stage_rows<D, RP, TP>(Qp, i0, N, sm.q, sm.qt);
-      for (int c = tid; c < MB * D / 8; c += 256) {  // dO rows, bf16 -> fp16
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (i0 + row < N)
-          v = bf16x8_to_f16x8(*(const u32x4*)((const bf16*)p.dO +
-                                              ((size_t)b * N + i0 + row) * (size_t)(H * D) +
-                                              (size_t)h * D + col));
-        *(u32x4*)(sm.g + row * RP + col) = v;
-        const f16x8 hv = __builtin_bit_cast(f16x8, v);
+      while (true) {
+        const bool has_next = i0 + MB < i_end;
+        if (has_next) stage(i0 + MB, bf ^ 1);
+        const BlockPass bp = block_pass(src, i0, kw0, N, w);
+        if (bp.part) {
+          f32x16 s, dp;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.gt[(col + e) * TP + row] = hv[e];
-      }
-      if (tid < MB) {
-        const int i = i0 + tid;
-        sm.lse[tid] = i < N ? p.lse[(size_t)bh * N + i] : 0.f;
-        sm.Dd[tid] = i < N ? p.Dd[(size_t)bh * N + i] : 0.f;
-      }
-      __syncthreads();
-      const BlockPass bp = block_pass(src, i0, kw0, N, w);
-      if (!bp.part) continue;
-      f32x16 s, dp;
+          for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+          for (int st = 0; st < NS; ++st) {
+            s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
+                             kf[st], s);
+            dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
+                              vf[st], dp);
+          }
+          f16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = mfma32x32x16(*(const f16x8*)(sm.q + row_perm(lr) * RP + 16 * st + 8 * lg), kf[st], s);
-        dp = mfma32x32x16(*(const f16x8*)(sm.g + row_perm(lr) * RP + 16 * st + 8 * lg), vf[st],
-                          dp);
-      }
-      f16x8 pb[2], dsb[2];
+          for (int r = 0; r < 16; ++r) {
+            const int qo = perm_row(r, lg);
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -sm.lse[bf][qo]));
+            if (bp.masked) {
+              const int i = i0 + qo;
+              pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
+            }
+            pb[r >> 3][r & 7] = (f16)pr;
+            dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - sm.Dd[bf][qo]));
+          }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qo = perm_row(r, lg);
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -sm.lse[qo]));
-        if (bp.masked) {
-          const int i = i0 + qo;
-          if (!(i < N && kj < N && keep_pair(src, i - kj, w))) pr = 0.f;
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int db = 0; db < NB; ++db) {
+              dvt[db] = mfma32x32x16(
+                  *(const f16x8*)(sm.gt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), pb[u],
+                  dvt[db]);
+              dkt[db] = mfma32x32x16(
+                  *(const f16x8*)(sm.qt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), dsb[u],
+                  dkt[db]);
+            }
         }
-        pb[r >> 3][r & 7] = (f16)pr;
-        dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - sm.Dd[qo]));
+        __syncthreads();
+        if (!has_next) break;
+        i0 += MB;
+        bf ^= 1;
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt + (32 * db + lr) * TP + 16 * u + 8 * lg),
-                                 pb[u], dvt[db]);
-          dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt + (32 * db + lr) * TP + 16 * u + 8 * lg),
-                                 dsb[u], dkt[db]);
-        }
     }
     if (kj < N) {
       float* dK = (src ? p.dK_glob : p.dK_loc) + ((size_t)bh * N + kj) * D;
