@@ -299,18 +299,81 @@ __device__ __forceinline__ bool keep_pair(int src, int dist, int w) {
   return src == 0 ? (unsigned)dist < (unsigned)w : dist >= w;
 }
 
-// Stages 32 rows (positions r0 .. r0+31, zero past N) of a row-major fp16
-// [n][D] array as rows of pitch RP and, transposed, as [d][row] of pitch TP.
-template <int D, int RP, int TP>
-__device__ __forceinline__ void stage_rows(const f16* src, int r0, int N, f16* rows, f16* cols) {
-  for (int c = threadIdx.x; c < MB * D / 8; c += 256) {
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r0 + row < N) v = *(const u32x4*)(src + (size_t)(r0 + row) * D + col);
-    *(u32x4*)(rows + row * RP + col) = v;
-    const f16x8 h = __builtin_bit_cast(f16x8, v);
+// A 32-row block of a [n][D] fp16 array held in registers on its way to LDS:
+// chunk c = tid + 256 i is row c / (D/8), columns 8 (c % (D/8)) .. +8.
+template <int D>
+struct Rows {
+  static constexpr int NCH = MB * D / 8 / 256;
+  u32x4 v[NCH];
+};
+
+// Rows r0 .. r0+31 of a row-major fp16 [n][D] array (zero past N).
+template <int D>
+__device__ __forceinline__ void load_rows(Rows<D>& x, const f16* src, int r0, int N) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cols[(col + e) * TP + row] = h[e];
+  for (int i = 0; i < Rows<D>::NCH; ++i) {
+    const int c = threadIdx.x + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
+    x.v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + row < N) x.v[i] = *(const u32x4*)(src + (size_t)(r0 + row) * D + col);
+  }
+}
+
+// Rows r0 .. r0+31 of dO (bf16, [b][n][H*D] with head offset), as fp16.
+template <int D>
+__device__ __forceinline__ void load_grad_rows(Rows<D>& x, const bf16* src, size_t ld, int r0,
+                                               int N) {
+#pragma unroll
+  for (int i = 0; i < Rows<D>::NCH; ++i) {
+    const int c = threadIdx.x + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
+    x.v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + row < N) x.v[i] = bf16x8_to_f16x8(*(const u32x4*)(src + (size_t)(r0 + row) * ld + col));
+  }
+}
+
+// The block as rows of pitch RP and, if cols is set, transposed as [d][row]
+// of pitch TP.
+template <int D, int RP, int TP>
+__device__ __forceinline__ void store_rows(const Rows<D>& x, f16* rows, f16* cols) {
+#pragma unroll
+  for (int i = 0; i < Rows<D>::NCH; ++i) {
+    const int c = threadIdx.x + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
+    *(u32x4*)(rows + row * RP + col) = x.v[i];
+    if (cols != nullptr) {
+      const f16x8 h = __builtin_bit_cast(f16x8, x.v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cols[(col + e) * TP + row] = h[e];
+    }
+  }
+}
+
+// Keys j0 .. j0+31 of a transposed fp16 V^T [D][n] (zero past N): chunk c is
+// dim c / 4, keys 8 (c % 4) .. +8.
+template <int D>
+__device__ __forceinline__ void load_vt(Rows<D>& x, const f16* src, int j0, int N) {
+#pragma unroll
+  for (int i = 0; i < Rows<D>::NCH; ++i) {
+    const int c = threadIdx.x + 256 * i, d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
+    const f16* p = src + (size_t)d * N + j0 + kc;
+    if ((N & 7) == 0 && j0 + kc + 8 <= N) {
+      x.v[i] = *(const u32x4*)p;
+    } else {
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = j0 + kc + e < N ? p[e] : (f16)0.f;
+      x.v[i] = __builtin_bit_cast(u32x4, h);
+    }
+  }
+}
+
+// ... stored as rows [key][d] of pitch RP.
+template <int D, int RP>
+__device__ __forceinline__ void store_vt(const Rows<D>& x, f16* rows) {
+#pragma unroll
+  for (int i = 0; i < Rows<D>::NCH; ++i) {
+    const int c = threadIdx.x + 256 * i, d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
+    const f16x8 h = __builtin_bit_cast(f16x8, x.v[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rows[(kc + e) * RP + d] = h[e];
   }
 }
 
@@ -383,30 +446,6 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
       src = need(1, j0) ? 1 : 0;
     }
   };
-  auto stage_k = [&](int j0, int src, int bf) {
-    for (int c = tid; c < MB * D / 8; c += 256) {
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j0 + row < N) v = *(const u32x4*)(Kp[src] + (size_t)(j0 + row) * D + col);
-      *(u32x4*)(sm.k[bf] + row * RP + col) = v;
-    }
-  };
-  auto stage_all = [&](int j0, int src, int bf) {
-    stage_rows<D, RP, TP>(Kp[src], j0, N, sm.k[bf], sm.kt[bf]);
-    for (int c = tid; c < MB * D / 8; c += 256) {  // V^T [d][n] -> rows [key][d]
-      const int d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
-      const f16* vsrc = Vp[src] + (size_t)d * N + j0 + kc;
-      f16* vdst = sm.v[bf] + kc * RP + d;
-      if ((N & 7) == 0 && j0 + kc + 8 <= N) {
-        const f16x8 v = *(const f16x8*)vsrc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vdst[e * RP] = v[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vdst[e * RP] = j0 + kc + e < N ? vsrc[e] : (f16)0.f;
-      }
-    }
-  };
   auto scores = [&](f32x16& s, int bf) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -427,13 +466,15 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
   float m = -INFINITY, l = 0.f;
   {
     int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
-    stage_k(j0, src, bf);
+    Rows<D> kx;
+    load_rows<D>(kx, Kp[src], j0, N);
+    store_rows<D, RP, TP>(kx, sm.k[bf], nullptr);
     __syncthreads();
     while (true) {
       int nj0 = j0, nsrc = src;
       next_pass(nj0, nsrc);
       const bool has_next = nj0 <= i_last;
-      if (has_next) stage_k(nj0, nsrc, bf ^ 1);
+      if (has_next) load_rows<D>(kx, Kp[nsrc], nj0, N);  // in flight during the pass
       const BlockPass bp = block_pass(src, qw0, j0, N, w);
       if (bp.part) {
         f32x16 s;
@@ -452,6 +493,7 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
           m = m_new;
         }
       }
+      if (has_next) store_rows<D, RP, TP>(kx, sm.k[bf ^ 1], nullptr);
       __syncthreads();
       if (!has_next) break;
       j0 = nj0;
@@ -480,13 +522,20 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
   {
     int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
-    stage_all(j0, src, bf);
+    Rows<D> kx, vx;
+    load_rows<D>(kx, Kp[src], j0, N);
+    load_vt<D>(vx, Vp[src], j0, N);
+    store_rows<D, RP, TP>(kx, sm.k[bf], sm.kt[bf]);
+    store_vt<D, RP>(vx, sm.v[bf]);
     __syncthreads();
     while (true) {
       int nj0 = j0, nsrc = src;
       next_pass(nj0, nsrc);
       const bool has_next = nj0 <= i_last;
-      if (has_next) stage_all(nj0, nsrc, bf ^ 1);
+      if (has_next) {  // in flight during the pass
+        load_rows<D>(kx, Kp[nsrc], nj0, N);
+        load_vt<D>(vx, Vp[nsrc], nj0, N);
+      }
       const BlockPass bp = block_pass(src, qw0, j0, N, w);
       if (bp.part) {
         f32x16 s, dp;
@@ -511,6 +560,10 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
             dq[db] = mfma32x32x16(
                 *(const f16x8*)(sm.kt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), dsb[u],
                 dq[db]);
+      }
+      if (has_next) {
+        store_rows<D, RP, TP>(kx, sm.k[bf ^ 1], sm.kt[bf ^ 1]);
+        store_vt<D, RP>(vx, sm.v[bf ^ 1]);
       }
       __syncthreads();
       if (!has_next) break;
@@ -563,24 +616,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_mfma(BwdProblem p) {
   const float sc2 = kLog2e / sqrtf((float)D), sc = 1.f / sqrtf((float)D);
   const int k_last = min(k0 + MQ, N) - 1;
 
-  auto stage = [&](int i0, int bf) {
-    stage_rows<D, RP, TP>(Qp, i0, N, sm.q[bf], sm.qt[bf]);
-    for (int c = tid; c < MB * D / 8; c += 256) {  // dO rows, bf16 -> fp16
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (i0 + row < N)
-        v = bf16x8_to_f16x8(*(const u32x4*)((const bf16*)p.dO +
-                                            ((size_t)b * N + i0 + row) * (size_t)(H * D) +
-                                            (size_t)h * D + col));
-      *(u32x4*)(sm.g[bf] + row * RP + col) = v;
-      const f16x8 hv = __builtin_bit_cast(f16x8, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.gt[bf][(col + e) * TP + row] = hv[e];
-    }
+  const bf16* Gp = (const bf16*)p.dO + (size_t)b * N * (size_t)(H * D) + (size_t)h * D;
+  Rows<D> qx, gx;
+  float lx = 0.f, dx = 0.f;
+  auto load = [&](int i0) {
+    load_rows<D>(qx, Qp, i0, N);
+    load_grad_rows<D>(gx, Gp, (size_t)(H * D), i0, N);
     if (tid < MB) {
       const int i = i0 + tid;
-      sm.lse[bf][tid] = i < N ? p.lse[(size_t)bh * N + i] : 0.f;
-      sm.Dd[bf][tid] = i < N ? p.Dd[(size_t)bh * N + i] : 0.f;
+      lx = i < N ? p.lse[(size_t)bh * N + i] : 0.f;
+      dx = i < N ? p.Dd[(size_t)bh * N + i] : 0.f;
+    }
+  };
+  auto store = [&](int bf) {
+    store_rows<D, RP, TP>(qx, sm.q[bf], sm.qt[bf]);
+    store_rows<D, RP, TP>(gx, sm.g[bf], sm.gt[bf]);
+    if (tid < MB) {
+      sm.lse[bf][tid] = lx;
+      sm.Dd[bf][tid] = dx;
     }
   };
 
@@ -605,11 +658,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_mfma(BwdProblem p) {
     const int i_end = src == 0 ? min(N, k_last + w) : N;
     if (i_begin < i_end) {
       int i0 = i_begin, bf = 0;
-      stage(i0, bf);
+      load(i0);
+      store(bf);
       __syncthreads();
       while (true) {
         const bool has_next = i0 + MB < i_end;
-        if (has_next) stage(i0 + MB, bf ^ 1);
+        if (has_next) load(i0 + MB);  // in flight during the block
         const BlockPass bp = block_pass(src, i0, kw0, N, w);
         if (bp.part) {
           f32x16 s, dp;
@@ -646,6 +700,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_mfma(BwdProblem p) {
                   dkt[db]);
             }
         }
+        if (has_next) store(bf ^ 1);
         __syncthreads();
         if (!has_next) break;
         i0 += MB;
