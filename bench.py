@@ -317,9 +317,10 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
 
 def time_backward(torch, dar, di, cfg, reps):
     """dar_attn_prefill_backward on seeded fp16 Q/K/V, the forward's o and a
-    seeded bf16 dO.  Algorithmic work: four products of 2 d_k FLOP per causal
-    pair (dV, dP, dQ, dK); the MFMA kernels also recompute the scores (three
-    times: the lse sweep, dq, dK/dV) and dP (twice)."""
+    seeded bf16 dO, with the forward's lse (dar_attn_prefill_lse), as a training
+    step would run it.  Algorithmic work: four products of 2 d_k FLOP per causal
+    pair (dV, dP, dQ, dK); the MFMA kernels also recompute the scores (in dq
+    and in dK/dV) and dP (twice)."""
     B, N, H, d_k, w = cfg
 
     def g(i, shape, t):
@@ -331,12 +332,12 @@ def time_backward(torch, dar, di, cfg, reps):
     Q, KL, KG = g(0, qk, "f16"), g(1, qk, "f16"), g(2, qk, "f16")
     VL, VG = g(3, vt, "f16"), g(4, vt, "f16")
     dO = g(5, (B, N, H * d_k), "bf16")
-    o = dar.dar_attn_prefill(Q, KL, VL, KG, VG, w)
+    o, lse = dar.dar_attn_prefill_lse(Q, KL, VL, KG, VG, w)
     out = {k: torch.empty(qk, dtype=torch.float32, device="cuda")
            for k in ("dQ", "dK_loc", "dV_loc", "dK_glob", "dV_glob")}
     ws = torch.empty(max(dar.attn_backward_workspace_bytes(B, N, H, d_k), 256),
                      dtype=torch.uint8, device="cuda")
-    fn = lambda: dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dO, w, out=out,
+    fn = lambda: dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dO, w, lse=lse, out=out,
                                                workspace=ws)
     ms = graph_launch_ms(torch, fn, copies=3, reps=reps)
     flops = 4.0 * B * H * d_k * N * (N + 1)

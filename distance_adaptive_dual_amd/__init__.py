@@ -25,7 +25,8 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
-           "dar_attn_prefill", "dar_attn_prefill_backward", "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
+           "dar_attn_prefill", "dar_attn_prefill_lse", "dar_attn_prefill_backward",
+           "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
            "dar_attn_decode_varlen")
 
@@ -57,8 +58,10 @@ def lib() -> ctypes.CDLL:
         L.dar_project.argtypes = [_P] * 8 + [_I] * 7 + [ctypes.c_float, _I] + [_P] * 7 + [_SZ, _P]
         L.dar_attn_prefill.restype = _I
         L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P]
+        L.dar_attn_prefill_lse.restype = _I
+        L.dar_attn_prefill_lse.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
         L.dar_attn_prefill_backward.restype = _I
-        L.dar_attn_prefill_backward.argtypes = [_P] * 7 + [_I] * 6 + [_P] * 6 + [_SZ, _P]
+        L.dar_attn_prefill_backward.argtypes = [_P] * 8 + [_I] * 6 + [_P] * 6 + [_SZ, _P]
         L.dar_decode_append.restype = _I
         L.dar_decode_append.argtypes = [_P] * 5 + [_I] * 8 + [ctypes.c_float, _I] + [_P] * 5 + [
             _SZ, _P]
@@ -205,16 +208,17 @@ def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None
 def attn_backward_workspace_bytes(B, N, heads, d_k, dtype=DAR_BF16):
     n = ctypes.c_size_t(0)
     f = [_fake(i) for i in range(12)]
-    st = lib().dar_attn_prefill_backward(*f[:7], B, N, heads, d_k, 0, dtype, *f[7:], None,
+    st = lib().dar_attn_prefill_backward(*f[:7], None, B, N, heads, d_k, 0, dtype, *f[7:], None,
                                          ctypes.byref(n), None)
     _check("dar_attn_prefill_backward", st)
     return n.value
 
 
-def dar_attn_prefill_backward(Q, K_loc, V_loc, K_glob, V_glob, o, dO, w: int, out=None,
-                              workspace=None, stream=None):
+def dar_attn_prefill_backward(Q, K_loc, V_loc, K_glob, V_glob, o, dO, w: int, lse=None,
+                              out=None, workspace=None, stream=None):
     """Gradients of dar_attn_prefill for dL/do = dO.  Returns dict dQ, dK_loc,
-    dV_loc, dK_glob, dV_glob (float32, [B, heads, N, d_k]; dV not transposed)."""
+    dV_loc, dK_glob, dV_glob (float32, [B, heads, N, d_k]; dV not transposed).
+    lse: the forward's normaliser from dar_attn_prefill_lse, or None."""
     torch = _torch()
     B, H, N, d_k = Q.shape
     dt = _dtype_code(Q)
@@ -222,11 +226,28 @@ def dar_attn_prefill_backward(Q, K_loc, V_loc, K_glob, V_glob, o, dO, w: int, ou
         out = {k: torch.empty((B, H, N, d_k), dtype=torch.float32, device=Q.device)
                for k in ("dQ", "dK_loc", "dV_loc", "dK_glob", "dV_glob")}
     args = [_ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(K_glob), _ptr(V_glob), _ptr(o), _ptr(dO),
-            B, N, H, d_k, int(w), dt]
+            _ptr(lse), B, N, H, d_k, int(w), dt]
     args += [_ptr(out[k]) for k in ("dQ", "dK_loc", "dV_loc", "dK_glob", "dV_glob")]
     _call_ws("dar_attn_prefill_backward", lib().dar_attn_prefill_backward, args, workspace, Q,
              stream)
     return out
+
+
+def dar_attn_prefill_lse(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, lse=None,
+                         stream=None):
+    """dar_attn_prefill that also returns lse [B, heads, N] (float32, natural log)."""
+    torch = _torch()
+    B, H, N, d_k = Q.shape
+    dt = _dtype_code(Q)
+    if o is None:
+        o = torch.empty((B, N, H * d_k), dtype=torch.bfloat16 if dt == DAR_BF16 else torch.float32,
+                        device=Q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=Q.device)
+    st = lib().dar_attn_prefill_lse(_ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(K_glob), _ptr(V_glob),
+                                    B, N, H, d_k, int(w), dt, _ptr(o), _ptr(lse), _stream(stream))
+    _check("dar_attn_prefill_lse", st)
+    return o, lse
 
 
 def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=None):

@@ -84,9 +84,13 @@ __global__ __launch_bounds__(256) void bwd_dq(BwdProblem p) {
   const float sc = 1.f / sqrtf((float)D);
   const int i_last = min(N, qt * BQ + BQ) - 1;
 
-  // sweep 1: lse_i over j <= i
+  // lse_i: the forward's, or sweep 1 over j <= i
   float m = -INFINITY, l = 0.f;
-  for (int j0 = 0; j0 <= i_last; j0 += BK) {
+  if (p.lse_in != nullptr) {
+    m = p.lse_in[(size_t)bh * N + qc];
+    l = 1.f;
+  }
+  for (int j0 = 0; p.lse_in == nullptr && j0 <= i_last; j0 += BK) {
     __syncthreads();
     for (int e = tid; e < BK * D; e += 256) {
       const int kk = e / D, d = e % D, j = j0 + kk;
@@ -462,53 +466,59 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
     }
   };
 
-  // sweep 1: lse2 of each query (max and sum per lane half, then combined)
-  float m = -INFINITY, l = 0.f;
-  {
-    int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
-    Rows<D> kx;
-    load_rows<D>(kx, Kp[src], j0, N);
-    store_rows<D, RP, TP>(kx, sm.k[bf], nullptr);
-    __syncthreads();
-    while (true) {
-      int nj0 = j0, nsrc = src;
-      next_pass(nj0, nsrc);
-      const bool has_next = nj0 <= i_last;
-      if (has_next) load_rows<D>(kx, Kp[nsrc], nj0, N);  // in flight during the pass
-      const BlockPass bp = block_pass(src, qw0, j0, N, w);
-      if (bp.part) {
-        f32x16 s;
-        scores(s, bf);
-        if (bp.masked) mask(s, src, j0);
-        float mt = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
-        mt *= sc2;
-        const float m_new = fmaxf(m, mt);
-        if (m_new > -INFINITY) {
-          float acc = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -m_new));
-          l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
-          m = m_new;
-        }
-      }
-      if (has_next) store_rows<D, RP, TP>(kx, sm.k[bf ^ 1], nullptr);
+  // lse2 of each query: the forward's, or sweep 1 (maximum and sum per lane
+  // half, then combined)
+  float lse2;
+  if (p.lse_in != nullptr) {
+    lse2 = p.lse_in[(size_t)bh * N + qc] * kLog2e;
+  } else {
+    float m = -INFINITY, l = 0.f;
+    {
+      int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
+      Rows<D> kx;
+      load_rows<D>(kx, Kp[src], j0, N);
+      store_rows<D, RP, TP>(kx, sm.k[bf], nullptr);
       __syncthreads();
-      if (!has_next) break;
-      j0 = nj0;
-      src = nsrc;
-      bf ^= 1;
+      while (true) {
+        int nj0 = j0, nsrc = src;
+        next_pass(nj0, nsrc);
+        const bool has_next = nj0 <= i_last;
+        if (has_next) load_rows<D>(kx, Kp[nsrc], nj0, N);  // in flight during the pass
+        const BlockPass bp = block_pass(src, qw0, j0, N, w);
+        if (bp.part) {
+          f32x16 s;
+          scores(s, bf);
+          if (bp.masked) mask(s, src, j0);
+          float mt = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
+          mt *= sc2;
+          const float m_new = fmaxf(m, mt);
+          if (m_new > -INFINITY) {
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -m_new));
+            l = l * __builtin_amdgcn_exp2f(m - m_new) + acc;
+            m = m_new;
+          }
+        }
+        if (has_next) store_rows<D, RP, TP>(kx, sm.k[bf ^ 1], nullptr);
+        __syncthreads();
+        if (!has_next) break;
+        j0 = nj0;
+        src = nsrc;
+        bf ^= 1;
+      }
     }
+    {
+      const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+      const float mm = fmaxf(m, mo);
+      l = (m > -INFINITY ? l * __builtin_amdgcn_exp2f(m - mm) : 0.f) +
+          (mo > -INFINITY ? lo * __builtin_amdgcn_exp2f(mo - mm) : 0.f);
+      m = mm;
+    }
+    lse2 = m + __log2f(l);
   }
-  {
-    const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
-    const float mm = fmaxf(m, mo);
-    l = (m > -INFINITY ? l * __builtin_amdgcn_exp2f(m - mm) : 0.f) +
-        (mo > -INFINITY ? lo * __builtin_amdgcn_exp2f(mo - mm) : 0.f);
-    m = mm;
-  }
-  const float lse2 = m + __log2f(l);
   if (qi < N && lg == 0) {
     p.lse[(size_t)bh * N + qi] = lse2;
     p.Dd[(size_t)bh * N + qi] = Dd;

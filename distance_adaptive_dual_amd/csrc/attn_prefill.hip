@@ -564,6 +564,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     if (qi < N) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const float inv = 1.f / l_tot;
+      if (!CHUNK && p.lse != nullptr && lg == 0)  // m_ref and l are in base 2
+        p.lse[(size_t)bh * N + qi] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
       // the row index is formed here (the empty asm keeps the compiler from
       // computing the 64-bit address before the pass loop and holding it)
       int qr = qi - q0;
@@ -646,6 +648,7 @@ __global__ __launch_bounds__(256) void attn_prefill_f32(PrefillProblem p) {
     }
   }
   if (qi >= N) return;
+  if (p.lse != nullptr && pt == 0) p.lse[((size_t)b * H + h) * N + qi] = m + logf(l);
   float* out = (float*)p.o + ((size_t)b * N + qi) * (size_t)(H * D) + (size_t)h * D;
   const float inv = 1.f / l;
 #pragma unroll

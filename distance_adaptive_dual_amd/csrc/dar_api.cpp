@@ -183,9 +183,10 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   return hip_status(e);
 }
 
-dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
-                            const void* K_glob, const void* V_glob, int B, int N, int heads,
-                            int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream) {
+static dar_status attn_prefill_impl(const void* Q, const void* K_loc, const void* V_loc,
+                                    const void* K_glob, const void* V_glob, int B, int N,
+                                    int heads, int d_k, int w, dar_dtype dtype, void* o,
+                                    float* lse, hipStream_t stream) {
   if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || w < 0) return DAR_ERR_INVALID_ARG;
   const void* need[] = {Q, K_loc, V_loc, K_glob, V_glob, o};
@@ -194,18 +195,36 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
   const size_t es = elem_size(dtype);
   const size_t sz = es * (size_t)B * N * heads * d_k;
   const Span ins[5] = {{Q, sz}, {K_loc, sz}, {V_loc, sz}, {K_glob, sz}, {V_glob, sz}};
-  const Span outs[1] = {{o, sz}};
-  if (!disjoint(outs, 1, ins, 5)) return DAR_ERR_INVALID_ARG;
+  const Span outs[2] = {{o, sz}, {lse, sizeof(float) * (size_t)B * heads * N}};
+  if (!disjoint(outs, lse != nullptr ? 2 : 1, ins, 5)) return DAR_ERR_INVALID_ARG;
   if (!head_supported(d_k)) return DAR_ERR_UNSUPPORTED;
   if ((size_t)B * heads * N * d_k > 0x7fffffffffffL) return DAR_ERR_UNSUPPORTED;
   PrefillProblem p{Q, K_loc, V_loc, K_glob, V_glob, o, B, N, heads, d_k, w};
+  p.lse = lse;
   return hip_status(launch_attn_prefill(p, dtype, stream));
+}
+
+dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
+                            const void* K_glob, const void* V_glob, int B, int N, int heads,
+                            int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream) {
+  return attn_prefill_impl(Q, K_loc, V_loc, K_glob, V_glob, B, N, heads, d_k, w, dtype, o,
+                           nullptr, stream);
+}
+
+dar_status dar_attn_prefill_lse(const void* Q, const void* K_loc, const void* V_loc,
+                                const void* K_glob, const void* V_glob, int B, int N, int heads,
+                                int d_k, int w, dar_dtype dtype, void* o, float* lse,
+                                hipStream_t stream) {
+  if (!aligned16(lse)) return DAR_ERR_INVALID_ARG;
+  return attn_prefill_impl(Q, K_loc, V_loc, K_glob, V_glob, B, N, heads, d_k, w, dtype, o, lse,
+                           stream);
 }
 
 dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const void* V_loc,
                                      const void* K_glob, const void* V_glob, const void* o,
-                                     const void* dO, int B, int N, int heads, int d_k, int w,
-                                     dar_dtype dtype, float* dQ, float* dK_loc, float* dV_loc,
+                                     const void* dO, const float* lse, int B, int N, int heads,
+                                     int d_k, int w, dar_dtype dtype, float* dQ, float* dK_loc,
+                                     float* dV_loc,
                                      float* dK_glob, float* dV_glob, void* workspace,
                                      size_t* workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
@@ -216,10 +235,11 @@ dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const voi
     if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
   const size_t n_el = (size_t)B * N * heads * d_k;
   const size_t sz = elem_size(dtype) * n_el, gz = sizeof(float) * n_el;
-  const Span ins[7] = {{Q, sz}, {K_loc, sz}, {V_loc, sz}, {K_glob, sz},
-                       {V_glob, sz}, {o, sz}, {dO, sz}};
+  if (lse != nullptr && ((uintptr_t)lse & 3u)) return DAR_ERR_INVALID_ARG;
+  const Span ins[8] = {{Q, sz},      {K_loc, sz}, {V_loc, sz}, {K_glob, sz},
+                       {V_glob, sz}, {o, sz},     {dO, sz},    {lse, sizeof(float) * n_el / d_k}};
   const Span outs[5] = {{dQ, gz}, {dK_loc, gz}, {dV_loc, gz}, {dK_glob, gz}, {dV_glob, gz}};
-  if (!disjoint(outs, 5, ins, 7)) return DAR_ERR_INVALID_ARG;
+  if (!disjoint(outs, 5, ins, 8)) return DAR_ERR_INVALID_ARG;
   if (!head_supported(d_k)) return DAR_ERR_UNSUPPORTED;
   if (n_el > 0x7fffffffffffL || (size_t)B * heads > 0x7fffffff / ((size_t)N + 63))
     return DAR_ERR_UNSUPPORTED;
@@ -245,6 +265,7 @@ dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const voi
   p.V_glob = V_glob;
   p.o = o;
   p.dO = dO;
+  p.lse_in = lse;
   p.dQ = dQ;
   p.dK_loc = dK_loc;
   p.dV_loc = dV_loc;

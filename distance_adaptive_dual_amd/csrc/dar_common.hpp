@@ -188,6 +188,9 @@ struct PrefillProblem {
   // N - q0 rows), the global arrays hold positions 0 .. N-1 and the local
   // arrays positions loc0 .. N-1.  A whole prefill has q0 = loc0 = 0.
   int q0 = 0, loc0 = 0;
+  // Optional [B, H, N] fp32 output (whole prefill only): the natural-log
+  // log-sum-exp of each query's scaled scores, log sum_j exp(q_i . k_j / sqrt(d_k)).
+  float* lse = nullptr;
 };
 hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s);
 
@@ -197,6 +200,7 @@ hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_
 // workspace (per-query log-sum-exp and dO . o).
 struct BwdProblem {
   const void *Q, *K_loc, *V_loc, *K_glob, *V_glob, *o, *dO;
+  const float* lse_in;  // the forward's natural-log lse [B, H, N], or null
   float *dQ, *dK_loc, *dV_loc, *dK_glob, *dV_glob;
   float *lse, *Dd;
   int B, N, H, d_k, w;

@@ -131,6 +131,18 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
                             int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream);
 
 /*
+ * dar_attn_prefill_lse -- dar_attn_prefill that also stores, for training,
+ * each query's softmax normaliser of Eq. (4):
+ *   lse [B, heads, N] float32, lse_i = log sum_{j <= i} exp(q_i . k_j / sqrt(d_k))
+ * (natural log, keys chosen by Eq. (3)).  o is identical to dar_attn_prefill's.
+ * lse must be 16-byte aligned and must not alias an input or o.
+ */
+dar_status dar_attn_prefill_lse(const void* Q, const void* K_loc, const void* V_loc,
+                                const void* K_glob, const void* V_glob, int B, int N, int heads,
+                                int d_k, int w, dar_dtype dtype, void* o, float* lse,
+                                hipStream_t stream);
+
+/*
  * dar_attn_prefill_backward -- gradients of dar_attn_prefill for dL/do = dO.
  *
  * Training remark after Eq. (4): each past token keeps both representations
@@ -143,19 +155,25 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
  *   Q, K_loc, V_loc, K_glob, V_glob, w   exactly as given to dar_attn_prefill
  *                                        (fp16 in DAR_BF16 mode; V transposed)
  *   o, dO   [B, N, heads*d_k]            the forward output and its gradient
- *                                        (bf16 in DAR_BF16 mode)
+ *                                        (bf16 in DAR_BF16 mode; dO within the
+ *                                        fp16 range: it enters fp16 products)
+ *   lse     [B, heads, N] float32 or NULL  the forward's normaliser from
+ *                                        dar_attn_prefill_lse; NULL: recomputed
+ *                                        here (one more pass over the scores)
  * Outputs, float32 in both modes, each written in full:
  *   dQ, dK_loc, dK_glob, dV_loc, dV_glob [B, heads, N, d_k]  (dV NOT transposed)
  * Workspace: 8*B*heads*N bytes (rounded) for the per-query log-sum-exp and D.
  * Outputs must not alias inputs, each other or the workspace.  Supported:
- * d_k in {64, 128}.  Arithmetic is fp32 on the VALU (no MFMA).
+ * d_k in {64, 128}.  DAR_BF16 with d_k = 64 runs fp16 MFMAs with fp32
+ * accumulation (P and dS rounded to fp16); otherwise fp32 on the VALU.
  */
 dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const void* V_loc,
                                      const void* K_glob, const void* V_glob, const void* o,
-                                     const void* dO, int B, int N, int heads, int d_k, int w,
-                                     dar_dtype dtype, float* dQ, float* dK_loc, float* dV_loc,
-                                     float* dK_glob, float* dV_glob, void* workspace,
-                                     size_t* workspace_bytes, hipStream_t stream);
+                                     const void* dO, const float* lse, int B, int N, int heads,
+                                     int d_k, int w, dar_dtype dtype, float* dQ, float* dK_loc,
+                                     float* dV_loc, float* dK_glob, float* dV_glob,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream);
 
 /*
  * dar_decode_append -- project one new token per sequence into the mixed cache.

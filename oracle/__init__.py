@@ -48,6 +48,8 @@ def _load():
         lib.dar_oracle_attend_rows.restype = ctypes.c_int
         lib.dar_oracle_attend_rows.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_long, ctypes.c_int, _I, _I, _I, _D, _D]
+        lib.dar_oracle_attend_lse.restype = ctypes.c_int
+        lib.dar_oracle_attend_lse.argtypes = [_D] * 3 + [ctypes.c_int] * 4 + [ctypes.c_long, _D]
         lib.dar_oracle_attend_backward.restype = ctypes.c_int
         lib.dar_oracle_attend_backward.argtypes = [_D] * 6 + [ctypes.c_int] * 4 + [
             ctypes.c_long] + [_D] * 5
@@ -123,6 +125,17 @@ def attend_rows(P, w, rows):
     if rc != 0:
         raise ValueError("dar_oracle_attend_rows rejected its arguments")
     return o, rs
+
+
+def attend_lse(P, w):
+    """Row normalisers of Eq. 4: lse [B,H,N] = log sum_{j<=i} exp(q_i.k_j/sqrt(d_k))."""
+    Q, KL, KG = (_f64(P[k]) for k in ("Q", "KL", "KG"))
+    B, H, N, d_k = Q.shape
+    lse = np.zeros((B, H, N))
+    rc = _load().dar_oracle_attend_lse(_p(Q), _p(KL), _p(KG), B, N, H, d_k, int(w), _p(lse))
+    if rc != 0:
+        raise ValueError("dar_oracle_attend_lse rejected its arguments")
+    return lse
 
 
 def attend_backward(P, w, dO):

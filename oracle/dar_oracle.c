@@ -192,6 +192,39 @@ int dar_oracle_attend_rows(const double* Q, const double* KL, const double* VL,
 }
 
 /*
+ * Softmax normaliser of each row of Eq. (4): lse_i = log sum_{j <= i}
+ * exp(q_i . k_j / sqrt(d_k)), keys chosen by Eq. (3).  lse: [B, H, N].
+ */
+int dar_oracle_attend_lse(const double* Q, const double* KL, const double* KG, int B, int N,
+                          int H, int d_k, long w, double* lse) {
+  if (B < 1 || N < 1 || H < 1 || d_k < 1 || w < 0) return -1;
+  const double scale = 1.0 / sqrt((double)d_k);
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 8)
+    for (long r = 0; r < (long)B * H * N; ++r) {
+      const int i = (int)(r % N);
+      const size_t off = (size_t)(r / N) * N;
+      const double* q = Q + (off + i) * d_k;
+      double m = -INFINITY;
+      for (int j = 0; j <= i; ++j) {
+        const double* k = ((long)(i - j) < w ? KL : KG) + (off + j) * d_k;
+        double dot = 0.0;
+        for (int t = 0; t < d_k; ++t) dot += q[t] * k[t];
+        s[j] = dot * scale;
+        if (s[j] > m) m = s[j];
+      }
+      double Z = 0.0;
+      for (int j = 0; j <= i; ++j) Z += exp(s[j] - m);
+      lse[r] = m + log(Z);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/*
  * Backward of the attention of Eqs. (3)-(4) for a loss L with dL/do = dO.
  * The selection of Eq. (3) is a fixed choice per (i, j) pair, so each pair's
  * gradient flows to the source it used: with p_j = softmax(s)_j over j <= i

@@ -100,16 +100,33 @@ def test_prefill_rejects(kw, code):
 
 
 def attn_bwd(**kw):
-    a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), o=F(5), dO=F(6), B=1,
-             N=64, heads=2, d_k=64, w=8, dtype=1, dQ=F(7), dK_loc=F(8), dV_loc=F(9),
-             dK_glob=F(10), dV_glob=F(11), ws=None, wsb=0)
+    a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), o=F(5), dO=F(6),
+             lse=None, B=1, N=64, heads=2, d_k=64, w=8, dtype=1, dQ=F(7), dK_loc=F(8),
+             dV_loc=F(9), dK_glob=F(10), dV_glob=F(11), ws=None, wsb=0)
     a.update(kw)
     n = ctypes.c_size_t(a["wsb"])
     st = dar.lib().dar_attn_prefill_backward(
-        a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"], a["o"], a["dO"], a["B"], a["N"],
+        a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"], a["o"], a["dO"], a["lse"],
+        a["B"], a["N"],
         a["heads"], a["d_k"], a["w"], a["dtype"], a["dQ"], a["dK_loc"], a["dV_loc"], a["dK_glob"],
         a["dV_glob"], a["ws"], ctypes.byref(n), None)
     return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), INVALID), (dict(lse=F(6) + 4), INVALID),  # null or misaligned
+    (dict(lse=F(5)), INVALID),                                 # lse overlaps o
+    (dict(lse=F(0)), INVALID),                                 # lse overlaps Q
+    (dict(N=0), INVALID), (dict(d_k=32), UNSUP),
+])
+def test_prefill_lse_rejects(kw, code):
+    a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), B=1, N=64, heads=2,
+             d_k=64, w=8, dtype=1, o=F(5), lse=F(6))
+    a.update(kw)
+    st = dar.lib().dar_attn_prefill_lse(a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"],
+                                        a["B"], a["N"], a["heads"], a["d_k"], a["w"], a["dtype"],
+                                        a["o"], a["lse"], None)
+    assert st == code
 
 
 def test_backward_size_query():
@@ -123,6 +140,8 @@ def test_backward_size_query():
     (dict(dQ=F(0)), INVALID),          # gradient aliases an input
     (dict(dV_glob=F(7)), INVALID),     # two gradients alias
     (dict(o=F(5) + 8), INVALID),       # misaligned
+    (dict(lse=F(12) + 2), INVALID),    # misaligned lse
+    (dict(lse=F(7)), INVALID),         # lse overlaps a gradient
     (dict(dtype=3), INVALID), (dict(d_k=96), UNSUP),
 ])
 def test_backward_rejects(kw, code):

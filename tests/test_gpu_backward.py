@@ -36,14 +36,20 @@ def _inputs(B, H, N, d_k, seed, mode):
     return P, dO
 
 
-def _gpu(P, dO, w, mode):
+def _gpu(P, dO, w, mode, use_lse=False):
+    """Forward then backward on the GPU; with use_lse the backward takes the
+    forward's normaliser (dar_attn_prefill_lse) instead of recomputing it."""
     t = "f16" if mode == "bf16" else "f32"
     Q, KL, KG = (dev(P[k], t) for k in ("Q", "KL", "KG"))
     VL = dev(P["VL"].transpose(0, 1, 3, 2), t)
     VG = dev(P["VG"].transpose(0, 1, 3, 2), t)
-    o = dar.dar_attn_prefill(Q, KL, VL, KG, VG, w)
+    lse = None
+    if use_lse:
+        o, lse = dar.dar_attn_prefill_lse(Q, KL, VL, KG, VG, w)
+    else:
+        o = dar.dar_attn_prefill(Q, KL, VL, KG, VG, w)
     g = dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dev(dO, "bf16" if mode == "bf16"
-                                                                else "f32"), w)
+                                                                else "f32"), w, lse=lse)
     torch.cuda.synchronize()
     return {k: host(v) for k, v in g.items()}
 
@@ -106,3 +112,28 @@ def test_backward_pythia70m_sampled_heads():
         ref = oracle.attend_backward(Ps, w, dOs)
         sub = {k: v[b:b + 1, h:h + 1] for k, v in got.items()}
         _check(sub, ref, "bf16", "b%d h%d" % (b, h))
+
+
+@pytest.mark.parametrize("mode,N,d_k,w", [("bf16", 300, 64, 77), ("bf16", 257, 128, 129),
+                                          ("bf16", 200, 64, 0), ("f32", 150, 64, 1000)])
+def test_forward_lse_and_backward_from_it(mode, N, d_k, w):
+    """dar_attn_prefill_lse: o identical to dar_attn_prefill's, lse against the
+    oracle's row normalisers (the bf16 mode sums p rounded to fp16: |error| of
+    lse <= log(1 + 2^-11) plus fp32 score rounding, bound 2e-3; fp32 mode 1e-5);
+    then the backward fed that lse against the oracle."""
+    B, H = 1, 2
+    P, dO = _inputs(B, H, N, d_k, 700 + N + w, mode)
+    t = "f16" if mode == "bf16" else "f32"
+    Q, KL, KG = (dev(P[k], t) for k in ("Q", "KL", "KG"))
+    VL = dev(P["VL"].transpose(0, 1, 3, 2), t)
+    VG = dev(P["VG"].transpose(0, 1, 3, 2), t)
+    o1 = dar.dar_attn_prefill(Q, KL, VL, KG, VG, w)
+    o2, lse = dar.dar_attn_prefill_lse(Q, KL, VL, KG, VG, w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    ref = oracle.attend_lse(P, w)
+    err = float(np.abs(host(lse) - ref).max())
+    log("lse %s N%d dk%d w%d max err %.3g" % (mode, N, d_k, w, err))
+    assert err <= (2e-3 if mode == "bf16" else 1e-5)
+    got = _gpu(P, dO, w, mode, use_lse=True)
+    _check(got, oracle.attend_backward(P, w, dO), mode, "from lse")

@@ -117,3 +117,18 @@ def test_uniform_attention_value_gradient_closed_form(w):
                 wg[:, :, j] += G[:, :, i] / (i + 1)
     assert np.abs(g["dVL"] - wl).max() < 1e-12
     assert np.abs(g["dVG"] - wg).max() < 1e-12
+
+
+def test_lse_uniform_and_vanilla():
+    """Q = 0: every score is 0, so lse_i = log(i + 1).  w >= N: the causal
+    log-sum-exp of plain attention, from torch."""
+    B, H, N, d_k = 1, 2, 40, 8
+    P, _ = _rand(B, H, N, d_k, seed=11)
+    Z = dict(P)
+    Z["Q"] = np.zeros_like(P["Q"])
+    lse = oracle.attend_lse(Z, 7)
+    assert np.abs(lse - np.log(np.arange(1, N + 1))[None, None]).max() < 1e-13
+    s = torch.tensor(P["Q"]) @ torch.tensor(P["KL"]).transpose(-1, -2) / np.sqrt(d_k)
+    s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    want = torch.logsumexp(s, dim=-1).numpy()
+    assert np.abs(oracle.attend_lse(P, N) - want).max() < 1e-12
