@@ -425,8 +425,9 @@ __device__ __forceinline__ WavePass wave_pass_info(int j0, int src, int qw0, int
 }
 
 // CHUNK: queries start at p.q0 and the local arrays at p.loc0 (a prefill
-// chunk); otherwise both are 0 and compiled in as constants.
-template <int D, bool CHUNK>
+// chunk); otherwise both are 0 and compiled in as constants.  LSE: also store
+// each query's log-sum-exp in p.lse (whole prefills only).
+template <int D, bool CHUNK, bool LSE>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(PrefillProblem p, int nQT, int nPair,
                                                           int remap, int paired) {
   __shared__ PassSmem<D> sm;
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     if (qi < N) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const float inv = 1.f / l_tot;
-      if (!CHUNK && p.lse != nullptr && lg == 0)  // m_ref and l are in base 2
+      if (LSE && lg == 0)  // m_ref and l are in base 2
         p.lse[(size_t)bh * N + qi] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
       // the row index is formed here (the empty asm keeps the compiler from
       // computing the 64-bit address before the pass loop and holding it)
@@ -673,12 +674,19 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
     const int remap = (BH % kNumXcd) == 0 ? 1 : 0;
     const dim3 grid(nPair * BH);
     const bool chunk = p.q0 != 0 || p.loc0 != 0;
-#define DAR_ATTN(DV, CV) \
-  hipLaunchKernelGGL((attn_prefill_f16<DV, CV>), grid, dim3(256), 0, s, p, nQT, nPair, remap, paired)
+#define DAR_ATTN(DV, CV, LV) \
+  hipLaunchKernelGGL((attn_prefill_f16<DV, CV, LV>), grid, dim3(256), 0, s, p, nQT, nPair, remap, \
+                     paired)
+    if (chunk && p.lse != nullptr) return hipErrorInvalidValue;
+    const bool lse = p.lse != nullptr;
     if (p.d_k == 64) {
-      if (chunk) DAR_ATTN(64, true); else DAR_ATTN(64, false);
+      if (chunk) DAR_ATTN(64, true, false);
+      else if (lse) DAR_ATTN(64, false, true);
+      else DAR_ATTN(64, false, false);
     } else {
-      if (chunk) DAR_ATTN(128, true); else DAR_ATTN(128, false);
+      if (chunk) DAR_ATTN(128, true, false);
+      else if (lse) DAR_ATTN(128, false, true);
+      else DAR_ATTN(128, false, false);
     }
 #undef DAR_ATTN
   } else {
