@@ -511,6 +511,10 @@ def main():
         bw = time_backward(torch, dar, di, (B, N, H, d_k, w), 2)
         res["backward"] = bw
         log("backward: %.3f ms, %.1f TFLOP/s" % (bw["ms"], bw["TFLOP/s"]))
+        bw1 = time_backward(torch, dar, di, (4, 8192, 16, 128, 512), 1)
+        res["backward_1b"] = bw1
+        log("backward 1b: %.3f ms, %.1f TFLOP/s" % (bw1["ms"], bw1["TFLOP/s"]))
+        torch.cuda.empty_cache()
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
         log("decode: building the 32k-context cache")

@@ -612,7 +612,7 @@ struct DkvSmem {
 // one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
 // dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkv_mfma(BwdProblem p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP;
   __shared__ DkvSmem<D> sm;
@@ -755,10 +755,15 @@ hipError_t launch_attn_backward(const BwdProblem& p_in, dar_dtype dt, hipStream_
     hipLaunchKernelGGL((bwd_dkv<BFV, DV>), g2, dim3(256), 0, s, p);        \
   } while (0)
   const bool bf = dt == DAR_BF16;
-  if (p.d_k == 64 && bf) {
+  if (bf) {
     const int nT = (p.N + MQ - 1) / MQ;
-    hipLaunchKernelGGL((bwd_dq_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkv_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
+    if (p.d_k == 64) {
+      hipLaunchKernelGGL((bwd_dq_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkv_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_mfma<128>), dim3(nT * BH), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkv_mfma<128>), dim3(nT * BH), dim3(256), 0, s, p);
+    }
   } else if (p.d_k == 64) {
     DAR_BWD(false, 64);
   } else {

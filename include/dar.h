@@ -164,8 +164,8 @@ dar_status dar_attn_prefill_lse(const void* Q, const void* K_loc, const void* V_
  *   dQ, dK_loc, dK_glob, dV_loc, dV_glob [B, heads, N, d_k]  (dV NOT transposed)
  * Workspace: 8*B*heads*N bytes (rounded) for the per-query log-sum-exp and D.
  * Outputs must not alias inputs, each other or the workspace.  Supported:
- * d_k in {64, 128}.  DAR_BF16 with d_k = 64 runs fp16 MFMAs with fp32
- * accumulation (P and dS rounded to fp16); otherwise fp32 on the VALU.
+ * d_k in {64, 128}.  DAR_BF16 runs fp16 MFMAs with fp32 accumulation (P and
+ * dS rounded to fp16); DAR_FP32 runs fp32 on the VALU.
  */
 dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const void* V_loc,
                                      const void* K_glob, const void* V_glob, const void* o,
