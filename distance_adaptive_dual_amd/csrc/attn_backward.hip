@@ -13,8 +13,8 @@
 //   dk_j  = sum_i ds_ij q_i / sqrt(d_k)     (into the source of pair (i, j))
 //   dv_j  = sum_i p_ij dO_i                 (likewise)
 //
-// Two VALU kernels, fp32 arithmetic (the inputs are fp16 / bf16 in bf16 mode,
-// fp32 in fp32 mode; the gradients are fp32):
+// bf16 mode runs the MFMA kernels further below.  fp32 mode runs two VALU
+// kernels in fp32 (the gradients are fp32 in both modes):
 //   bwd_dq:  64 queries per workgroup, four lanes per query (lane part pt owns
 //            dims pt, pt + 4, ...).  Keys of both sources are staged 32 at a
 //            time.  A first sweep forms lse_i (online maximum and sum), then
@@ -767,7 +767,7 @@ hipError_t launch_attn_backward(const BwdProblem& p_in, dar_dtype dt, hipStream_
   } else if (p.d_k == 64) {
     DAR_BWD(false, 64);
   } else {
-    if (bf) DAR_BWD(true, 128); else DAR_BWD(false, 128);
+    DAR_BWD(false, 128);
   }
 #undef DAR_BWD
   return hipGetLastError();
