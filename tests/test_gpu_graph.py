@@ -119,3 +119,45 @@ def test_ragged_decode_graph_follows_device_lengths():
         torch.cuda.synchronize()
         log("ragged decode graph replay %d lens %s" % (rep, new))
         assert torch.equal(o, ref)
+
+
+def test_training_step_graph_replays_match_eager():
+    """Forward with lse and the backward captured together: every replay gives
+    the eager gradients exactly; the backward is also deterministic."""
+    B, H, N, d_k, w = 2, 2, 600, 64, 100
+    g_ = [dev(di.gaussian(900 + i, (B, H, N, d_k), 1.0, "f16"), "f16") for i in range(3)]
+    Q, KL, KG = g_
+    VL = dev(di.gaussian(905, (B, H, d_k, N), 1.0, "f16"), "f16")
+    VG = dev(di.gaussian(906, (B, H, d_k, N), 1.0, "f16"), "f16")
+    dO = dev(di.gaussian(907, (B, N, H * d_k), 1.0, "bf16"), "bf16")
+    o, lse = dar.dar_attn_prefill_lse(Q, KL, VL, KG, VG, w)
+    ws = torch.empty(max(dar.attn_backward_workspace_bytes(B, N, H, d_k), 256), dtype=torch.uint8,
+                     device="cuda")
+    grads = dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dO, w, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in grads.items()}
+    ref_o, ref_lse = o.clone(), lse.clone()
+    again = dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dO, w, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(again[k], ref[k]), k
+
+    def step():
+        dar.dar_attn_prefill_lse(Q, KL, VL, KG, VG, w, o=o, lse=lse)
+        dar.dar_attn_prefill_backward(Q, KL, VL, KG, VG, o, dO, w, lse=lse, out=grads,
+                                      workspace=ws)
+
+    g = capture(step)
+    for rep in range(3):
+        for v in list(grads.values()) + [o, lse]:
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log("training graph replay %d" % rep)
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+        for k in ref:
+            assert torch.equal(grads[k], ref[k]), k
+        # eager work of the program between replays
+        dar.dar_attn_prefill(Q, KG, VG, KL, VL, w)
+        torch.cuda.synchronize()
