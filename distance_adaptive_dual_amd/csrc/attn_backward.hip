@@ -632,10 +632,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   auto load = [&](int i0) {
     load_rows<D>(qx, Qp, i0, N);
     load_grad_rows<D>(gx, Gp, (size_t)(H * D), i0, N);
-    if (tid < MB) {
+    if (tid < MB) {  // staged as the initial values of the S and dP accumulators
       const int i = i0 + tid;
-      lx = i < N ? p.lse[(size_t)bh * N + i] : 0.f;
-      dx = i < N ? p.Dd[(size_t)bh * N + i] : 0.f;
+      lx = i < N ? -p.lse[(size_t)bh * N + i] / sc2 : 0.f;
+      dx = i < N ? -p.Dd[(size_t)bh * N + i] : 0.f;
     }
   };
   auto store = [&](int bf) {
@@ -676,9 +676,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
         if (has_next) load(i0 + MB);  // in flight during the block
         const BlockPass bp = block_pass(src, i0, kw0, N, w);
         if (bp.part) {
+          // S - lse2/sc2 and dP - D: the accumulators start from the staged
+          // per-query values, so P = 2^(S sc2) and dS = P dP afterwards
           f32x16 s, dp;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            s[r] = sm.lse[bf][perm_row(r, lg)];
+            dp[r] = sm.Dd[bf][perm_row(r, lg)];
+          }
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
             s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
@@ -689,14 +694,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
           f16x8 pb[2], dsb[2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int qo = perm_row(r, lg);
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -sm.lse[bf][qo]));
+            float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
             if (bp.masked) {
-              const int i = i0 + qo;
+              const int i = i0 + perm_row(r, lg);
               pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
             }
             pb[r >> 3][r & 7] = (f16)pr;
-            dsb[r >> 3][r & 7] = (f16)(pr * (dp[r] - sm.Dd[bf][qo]));
+            dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
           }
 #pragma unroll
           for (int u = 0; u < 2; ++u)
