@@ -408,10 +408,12 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
   const int q0 = qt * MQ, qw0 = q0 + 32 * wave, qi = qw0 + lr;
   const int qc = qi < N ? qi : N - 1;
   const f16* Qp = (const f16*)p.Q + (size_t)bh * N * D;
-  const f16* Kp[2] = {(const f16*)p.K_loc + (size_t)bh * N * D,
-                      (const f16*)p.K_glob + (size_t)bh * N * D};
-  const f16* Vp[2] = {(const f16*)p.V_loc + (size_t)bh * D * N,
-                      (const f16*)p.V_glob + (size_t)bh * D * N};
+  const f16* const Kl = (const f16*)p.K_loc + (size_t)bh * N * D;
+  const f16* const Kg = (const f16*)p.K_glob + (size_t)bh * N * D;
+  const f16* const Vl = (const f16*)p.V_loc + (size_t)bh * D * N;
+  const f16* const Vg = (const f16*)p.V_glob + (size_t)bh * D * N;
+  auto Kp = [&](int src) { return src ? Kg : Kl; };  // source 0 local, 1 global
+  auto Vp = [&](int src) { return src ? Vg : Vl; };
   const float sc2 = kLog2e / sqrtf((float)D);
 
   f16x8 qf[NS], gf[NS];
@@ -476,14 +478,14 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
     {
       int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
       Rows<D> kx;
-      load_rows<D>(kx, Kp[src], j0, N);
+      load_rows<D>(kx, Kp(src), j0, N);
       store_rows<D, RP, TP>(kx, sm.k[bf], nullptr);
       __syncthreads();
       while (true) {
         int nj0 = j0, nsrc = src;
         next_pass(nj0, nsrc);
         const bool has_next = nj0 <= i_last;
-        if (has_next) load_rows<D>(kx, Kp[nsrc], nj0, N);  // in flight during the pass
+        if (has_next) load_rows<D>(kx, Kp(nsrc), nj0, N);  // in flight during the pass
         const BlockPass bp = block_pass(src, qw0, j0, N, w);
         if (bp.part) {
           f32x16 s;
@@ -533,8 +535,8 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
   {
     int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
     Rows<D> kx, vx;
-    load_rows<D>(kx, Kp[src], j0, N);
-    load_vt<D>(vx, Vp[src], j0, N);
+    load_rows<D>(kx, Kp(src), j0, N);
+    load_vt<D>(vx, Vp(src), j0, N);
     store_rows<D, RP, TP>(kx, sm.k[bf], sm.kt[bf]);
     store_vt<D, RP>(vx, sm.v[bf]);
     __syncthreads();
@@ -543,8 +545,8 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
       next_pass(nj0, nsrc);
       const bool has_next = nj0 <= i_last;
       if (has_next) {  // in flight during the pass
-        load_rows<D>(kx, Kp[nsrc], nj0, N);
-        load_vt<D>(vx, Vp[nsrc], nj0, N);
+        load_rows<D>(kx, Kp(nsrc), nj0, N);
+        load_vt<D>(vx, Vp(nsrc), nj0, N);
       }
       const BlockPass bp = block_pass(src, qw0, j0, N, w);
       if (bp.part) {
