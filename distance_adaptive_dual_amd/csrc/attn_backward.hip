@@ -13,13 +13,14 @@
 //   dk_j  = sum_i ds_ij q_i / sqrt(d_k)     (into the source of pair (i, j))
 //   dv_j  = sum_i p_ij dO_i                 (likewise)
 //
-// bf16 mode runs the MFMA kernels further below.  fp32 mode runs two VALU
-// kernels in fp32 (the gradients are fp32 in both modes):
+// bf16 mode runs the MFMA kernels further below (bwd_dq_mfma, bwd_dkv_mfma).
+// fp32 mode runs two VALU kernels in fp32 (the gradients are fp32 in both
+// modes):
 //   bwd_dq:  64 queries per workgroup, four lanes per query (lane part pt owns
 //            dims pt, pt + 4, ...).  Keys of both sources are staged 32 at a
-//            time.  A first sweep forms lse_i (online maximum and sum), then
-//            D_i and lse_i are stored for the second kernel and a second sweep
-//            accumulates dq_i.
+//            time.  lse_i comes from the forward or from a first sweep (online
+//            maximum and sum); D_i and lse_i are stored for the second kernel
+//            and a second sweep accumulates dq_i.
 //   bwd_dkv: d_k / 16 lanes per key (16 dims each), 64 or 32 keys per
 //            workgroup, both sources' k, v and gradient accumulators in
 //            registers.  Queries i >= j stream through LDS 32 at a time with
