@@ -323,62 +323,101 @@ __device__ __forceinline__ void load_rows(Rows<D>& x, const f16* src, int r0, in
   }
 }
 
-// Rows r0 .. r0+31 of dO (bf16, [b][n][H*D] with head offset), as fp16.
-template <int D>
-__device__ __forceinline__ void load_grad_rows(Rows<D>& x, const bf16* src, size_t ld, int r0,
-                                               int N) {
-#pragma unroll
-  for (int i = 0; i < Rows<D>::NCH; ++i) {
-    const int c = threadIdx.x + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
-    x.v[i] = u32x4{0u, 0u, 0u, 0u};
-    if (r0 + row < N) x.v[i] = bf16x8_to_f16x8(*(const u32x4*)(src + (size_t)(r0 + row) * ld + col));
-  }
-}
-
-// The block as rows of pitch RP and, if cols is set, transposed as [d][row]
-// of pitch TP.
-template <int D, int RP, int TP>
-__device__ __forceinline__ void store_rows(const Rows<D>& x, f16* rows, f16* cols) {
+// ... stored as rows of pitch RP.
+template <int D, int RP>
+__device__ __forceinline__ void store_rows(const Rows<D>& x, f16* rows) {
 #pragma unroll
   for (int i = 0; i < Rows<D>::NCH; ++i) {
     const int c = threadIdx.x + 256 * i, row = c / (D / 8), col = (c % (D / 8)) * 8;
     *(u32x4*)(rows + row * RP + col) = x.v[i];
-    if (cols != nullptr) {
-      const f16x8 h = __builtin_bit_cast(f16x8, x.v[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) cols[(col + e) * TP + row] = h[e];
-    }
   }
 }
 
-// Keys j0 .. j0+31 of a transposed fp16 V^T [D][n] (zero past N): chunk c is
-// dim c / 4, keys 8 (c % 4) .. +8.
+// Paired staging for the blocks that LDS also needs transposed: 128 threads
+// (pi = 0 .. 127) each take two adjacent rows (or dims) of one 8-wide chunk,
+// so the transposed copy is written as 4-byte pairs.  Pair slot q = pi + 128 i
+// covers rows 2 (q % 16), +1 and columns 8 (q / 16) .. +8 (a wave's 4-byte
+// writes then spread over 32 banks).
 template <int D>
-__device__ __forceinline__ void load_vt(Rows<D>& x, const f16* src, int j0, int N) {
+struct Pairs {
+  static constexpr int NP = MB * D / 16 / 128;
+  u32x4 a[NP], b[NP];  // the two rows
+};
+
+__device__ __forceinline__ uint32_t pack2(f16 lo, f16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Rows r0 .. r0+31 of a row-major fp16 [n][D] array (zero past N); with
+// grad_ld > 0 the source is bf16 dO rows of stride grad_ld, turned into fp16.
+template <int D>
+__device__ __forceinline__ void load_pairs(Pairs<D>& x, const void* src, size_t grad_ld, int r0,
+                                           int N, int pi) {
 #pragma unroll
-  for (int i = 0; i < Rows<D>::NCH; ++i) {
-    const int c = threadIdx.x + 256 * i, d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
-    const f16* p = src + (size_t)d * N + j0 + kc;
-    if ((N & 7) == 0 && j0 + kc + 8 <= N) {
-      x.v[i] = *(const u32x4*)p;
+  for (int i = 0; i < Pairs<D>::NP; ++i) {
+    const int q = pi + 128 * i, row = 2 * (q % 16), col = (q / 16) * 8;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    x.a[i] = x.b[i] = z;
+    if (grad_ld == 0) {
+      const f16* s = (const f16*)src;
+      if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * D + col);
+      if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * D + col);
     } else {
-      f16x8 h;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = j0 + kc + e < N ? p[e] : (f16)0.f;
-      x.v[i] = __builtin_bit_cast(u32x4, h);
+      const bf16* s = (const bf16*)src;
+      if (r0 + row < N) x.a[i] = bf16x8_to_f16x8(*(const u32x4*)(s + (size_t)(r0 + row) * grad_ld + col));
+      if (r0 + row + 1 < N)
+        x.b[i] = bf16x8_to_f16x8(*(const u32x4*)(s + (size_t)(r0 + row + 1) * grad_ld + col));
     }
   }
 }
 
-// ... stored as rows [key][d] of pitch RP.
+// ... as rows of pitch RP and transposed as [d][row] of pitch TP.
+template <int D, int RP, int TP>
+__device__ __forceinline__ void store_pairs(const Pairs<D>& x, f16* rows, f16* cols, int pi) {
+#pragma unroll
+  for (int i = 0; i < Pairs<D>::NP; ++i) {
+    const int q = pi + 128 * i, row = 2 * (q % 16), col = (q / 16) * 8;
+    *(u32x4*)(rows + row * RP + col) = x.a[i];
+    *(u32x4*)(rows + (row + 1) * RP + col) = x.b[i];
+    const f16x8 ha = __builtin_bit_cast(f16x8, x.a[i]), hb = __builtin_bit_cast(f16x8, x.b[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *(uint32_t*)(cols + (col + e) * TP + row) = pack2(ha[e], hb[e]);
+  }
+}
+
+// Keys j0 .. j0+31 of V^T [D][n] (zero past N): pair slot q covers dims
+// 2 (q / 4), +1 and keys 8 (q % 4) .. +8; stored as rows [key][d].
+template <int D>
+__device__ __forceinline__ void load_vt_pairs(Pairs<D>& x, const f16* src, int j0, int N, int pi) {
+#pragma unroll
+  for (int i = 0; i < Pairs<D>::NP; ++i) {
+    const int q = pi + 128 * i, d = 2 * (q / (MB / 8)), kc = (q % (MB / 8)) * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f16* p = src + (size_t)(d + h) * N + j0 + kc;
+      u32x4 v;
+      if ((N & 7) == 0 && j0 + kc + 8 <= N) {
+        v = *(const u32x4*)p;
+      } else {
+        f16x8 t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = j0 + kc + e < N ? p[e] : (f16)0.f;
+        v = __builtin_bit_cast(u32x4, t);
+      }
+      (h ? x.b[i] : x.a[i]) = v;
+    }
+  }
+}
+
 template <int D, int RP>
-__device__ __forceinline__ void store_vt(const Rows<D>& x, f16* rows) {
+__device__ __forceinline__ void store_vt_pairs(const Pairs<D>& x, f16* rows, int pi) {
 #pragma unroll
-  for (int i = 0; i < Rows<D>::NCH; ++i) {
-    const int c = threadIdx.x + 256 * i, d = c / (MB / 8), kc = (c % (MB / 8)) * 8;
-    const f16x8 h = __builtin_bit_cast(f16x8, x.v[i]);
+  for (int i = 0; i < Pairs<D>::NP; ++i) {
+    const int q = pi + 128 * i, d = 2 * (q / (MB / 8)), kc = (q % (MB / 8)) * 8;
+    const f16x8 ha = __builtin_bit_cast(f16x8, x.a[i]), hb = __builtin_bit_cast(f16x8, x.b[i]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rows[(kc + e) * RP + d] = h[e];
+    for (int e = 0; e < 8; ++e) *(uint32_t*)(rows + (kc + e) * RP + d) = pack2(ha[e], hb[e]);
   }
 }
 
@@ -480,7 +519,7 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
       int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
       Rows<D> kx;
       load_rows<D>(kx, Kp(src), j0, N);
-      store_rows<D, RP, TP>(kx, sm.k[bf], nullptr);
+      store_rows<D, RP>(kx, sm.k[bf]);
       __syncthreads();
       while (true) {
         int nj0 = j0, nsrc = src;
@@ -505,7 +544,7 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
             m = m_new;
           }
         }
-        if (has_next) store_rows<D, RP, TP>(kx, sm.k[bf ^ 1], nullptr);
+        if (has_next) store_rows<D, RP>(kx, sm.k[bf ^ 1]);
         __syncthreads();
         if (!has_next) break;
         j0 = nj0;
@@ -535,20 +574,26 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
   {
     int j0 = 0, src = need(1, 0) ? 1 : 0, bf = 0;
-    Rows<D> kx, vx;
-    load_rows<D>(kx, Kp(src), j0, N);
-    load_vt<D>(vx, Vp(src), j0, N);
-    store_rows<D, RP, TP>(kx, sm.k[bf], sm.kt[bf]);
-    store_vt<D, RP>(vx, sm.v[bf]);
+    // threads 0 .. 127 stage K (rows and transposed), 128 .. 255 V (as rows)
+    const bool kside = tid < 128;
+    const int pi = tid & 127;
+    Pairs<D> px;
+    auto load2 = [&](int jj, int ss) {
+      if (kside) load_pairs<D>(px, Kp(ss), 0, jj, N, pi);
+      else load_vt_pairs<D>(px, Vp(ss), jj, N, pi);
+    };
+    auto store2 = [&](int bb) {
+      if (kside) store_pairs<D, RP, TP>(px, sm.k[bb], sm.kt[bb], pi);
+      else store_vt_pairs<D, RP>(px, sm.v[bb], pi);
+    };
+    load2(j0, src);
+    store2(bf);
     __syncthreads();
     while (true) {
       int nj0 = j0, nsrc = src;
       next_pass(nj0, nsrc);
       const bool has_next = nj0 <= i_last;
-      if (has_next) {  // in flight during the pass
-        load_rows<D>(kx, Kp(nsrc), nj0, N);
-        load_vt<D>(vx, Vp(nsrc), nj0, N);
-      }
+      if (has_next) load2(nj0, nsrc);  // in flight during the pass
       const BlockPass bp = block_pass(src, qw0, j0, N, w);
       if (bp.part) {
         f32x16 s, dp;
@@ -574,10 +619,7 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
                 *(const f16x8*)(sm.kt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), dsb[u],
                 dq[db]);
       }
-      if (has_next) {
-        store_rows<D, RP, TP>(kx, sm.k[bf ^ 1], sm.kt[bf ^ 1]);
-        store_vt<D, RP>(vx, sm.v[bf ^ 1]);
-      }
+      if (has_next) store2(bf ^ 1);
       __syncthreads();
       if (!has_next) break;
       j0 = nj0;
@@ -630,11 +672,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   const int k_last = min(k0 + MQ, N) - 1;
 
   const bf16* Gp = (const bf16*)p.dO + (size_t)b * N * (size_t)(H * D) + (size_t)h * D;
-  Rows<D> qx, gx;
+  // threads 0 .. 127 stage Q, 128 .. 255 dO (rows and transposed)
+  const bool qside = tid < 128;
+  const int pi = tid & 127;
+  Pairs<D> px;
   float lx = 0.f, dx = 0.f;
   auto load = [&](int i0) {
-    load_rows<D>(qx, Qp, i0, N);
-    load_grad_rows<D>(gx, Gp, (size_t)(H * D), i0, N);
+    if (qside) load_pairs<D>(px, Qp, 0, i0, N, pi);
+    else load_pairs<D>(px, Gp, (size_t)(H * D), i0, N, pi);
     if (tid < MB) {  // staged as the initial values of the S and dP accumulators
       const int i = i0 + tid;
       lx = i < N ? -p.lse[(size_t)bh * N + i] / sc2 : 0.f;
@@ -642,8 +687,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
     }
   };
   auto store = [&](int bf) {
-    store_rows<D, RP, TP>(qx, sm.q[bf], sm.qt[bf]);
-    store_rows<D, RP, TP>(gx, sm.g[bf], sm.gt[bf]);
+    if (qside) store_pairs<D, RP, TP>(px, sm.q[bf], sm.qt[bf], pi);
+    else store_pairs<D, RP, TP>(px, sm.g[bf], sm.gt[bf], pi);
     if (tid < MB) {
       sm.lse[bf][tid] = lx;
       sm.Dd[bf][tid] = dx;
