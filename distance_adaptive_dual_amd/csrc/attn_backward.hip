@@ -335,12 +335,12 @@ __device__ __forceinline__ void store_rows(const Rows<D>& x, f16* rows) {
 
 // Paired staging for the blocks that LDS also needs transposed: 128 threads
 // (pi = 0 .. 127) each take two adjacent rows (or dims) of one 8-wide chunk,
-// so the transposed copy is written as 4-byte pairs.  Pair slot q = pi + 128 i
-// covers rows 2 (q % 16), +1 and columns 8 (q / 16) .. +8 (a wave's 4-byte
-// writes then spread over 32 banks).
-template <int D>
+// so the transposed copy is written as 4-byte pairs.  For a block of ROWS rows,
+// pair slot q = pi + 128 i covers rows 2 (q % (ROWS/2)), +1 and columns
+// 8 (q / (ROWS/2)) .. +8 (a wave's 4-byte writes then spread over the banks).
+template <int D, int ROWS>
 struct Pairs {
-  static constexpr int NP = MB * D / 16 / 128;
+  static constexpr int NP = ROWS * D / 16 / 128;
   u32x4 a[NP], b[NP];  // the two rows
 };
 
@@ -351,12 +351,12 @@ __device__ __forceinline__ uint32_t pack2(f16 lo, f16 hi) {
 
 // Rows r0 .. r0+31 of a row-major fp16 [n][D] array (zero past N); with
 // grad_ld > 0 the source is bf16 dO rows of stride grad_ld, turned into fp16.
-template <int D>
-__device__ __forceinline__ void load_pairs(Pairs<D>& x, const void* src, size_t grad_ld, int r0,
-                                           int N, int pi) {
+template <int D, int ROWS>
+__device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, size_t grad_ld,
+                                           int r0, int N, int pi) {
 #pragma unroll
-  for (int i = 0; i < Pairs<D>::NP; ++i) {
-    const int q = pi + 128 * i, row = 2 * (q % 16), col = (q / 16) * 8;
+  for (int i = 0; i < Pairs<D, ROWS>::NP; ++i) {
+    const int q = pi + 128 * i, row = 2 * (q % (ROWS / 2)), col = (q / (ROWS / 2)) * 8;
     u32x4 z = {0u, 0u, 0u, 0u};
     x.a[i] = x.b[i] = z;
     if (grad_ld == 0) {
@@ -373,11 +373,12 @@ __device__ __forceinline__ void load_pairs(Pairs<D>& x, const void* src, size_t 
 }
 
 // ... as rows of pitch RP and transposed as [d][row] of pitch TP.
-template <int D, int RP, int TP>
-__device__ __forceinline__ void store_pairs(const Pairs<D>& x, f16* rows, f16* cols, int pi) {
+template <int D, int ROWS, int RP, int TP>
+__device__ __forceinline__ void store_pairs(const Pairs<D, ROWS>& x, f16* rows, f16* cols,
+                                            int pi) {
 #pragma unroll
-  for (int i = 0; i < Pairs<D>::NP; ++i) {
-    const int q = pi + 128 * i, row = 2 * (q % 16), col = (q / 16) * 8;
+  for (int i = 0; i < Pairs<D, ROWS>::NP; ++i) {
+    const int q = pi + 128 * i, row = 2 * (q % (ROWS / 2)), col = (q / (ROWS / 2)) * 8;
     *(u32x4*)(rows + row * RP + col) = x.a[i];
     *(u32x4*)(rows + (row + 1) * RP + col) = x.b[i];
     const f16x8 ha = __builtin_bit_cast(f16x8, x.a[i]), hb = __builtin_bit_cast(f16x8, x.b[i]);
@@ -389,9 +390,10 @@ __device__ __forceinline__ void store_pairs(const Pairs<D>& x, f16* rows, f16* c
 // Keys j0 .. j0+31 of V^T [D][n] (zero past N): pair slot q covers dims
 // 2 (q / 4), +1 and keys 8 (q % 4) .. +8; stored as rows [key][d].
 template <int D>
-__device__ __forceinline__ void load_vt_pairs(Pairs<D>& x, const f16* src, int j0, int N, int pi) {
+__device__ __forceinline__ void load_vt_pairs(Pairs<D, MB>& x, const f16* src, int j0, int N,
+                                              int pi) {
 #pragma unroll
-  for (int i = 0; i < Pairs<D>::NP; ++i) {
+  for (int i = 0; i < Pairs<D, MB>::NP; ++i) {
     const int q = pi + 128 * i, d = 2 * (q / (MB / 8)), kc = (q % (MB / 8)) * 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -411,9 +413,9 @@ __device__ __forceinline__ void load_vt_pairs(Pairs<D>& x, const f16* src, int j
 }
 
 template <int D, int RP>
-__device__ __forceinline__ void store_vt_pairs(const Pairs<D>& x, f16* rows, int pi) {
+__device__ __forceinline__ void store_vt_pairs(const Pairs<D, MB>& x, f16* rows, int pi) {
 #pragma unroll
-  for (int i = 0; i < Pairs<D>::NP; ++i) {
+  for (int i = 0; i < Pairs<D, MB>::NP; ++i) {
     const int q = pi + 128 * i, d = 2 * (q / (MB / 8)), kc = (q % (MB / 8)) * 8;
     const f16x8 ha = __builtin_bit_cast(f16x8, x.a[i]), hb = __builtin_bit_cast(f16x8, x.b[i]);
 #pragma unroll
@@ -577,13 +579,13 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
     // threads 0 .. 127 stage K (rows and transposed), 128 .. 255 V (as rows)
     const bool kside = tid < 128;
     const int pi = tid & 127;
-    Pairs<D> px;
+    Pairs<D, MB> px;
     auto load2 = [&](int jj, int ss) {
-      if (kside) load_pairs<D>(px, Kp(ss), 0, jj, N, pi);
+      if (kside) load_pairs<D, MB>(px, Kp(ss), 0, jj, N, pi);
       else load_vt_pairs<D>(px, Vp(ss), jj, N, pi);
     };
     auto store2 = [&](int bb) {
-      if (kside) store_pairs<D, RP, TP>(px, sm.k[bb], sm.kt[bb], pi);
+      if (kside) store_pairs<D, MB, RP, TP>(px, sm.k[bb], sm.kt[bb], pi);
       else store_vt_pairs<D, RP>(px, sm.v[bb], pi);
     };
     load2(j0, src);
@@ -643,23 +645,24 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
 
 template <int D>
 struct DkvSmem {
+  static constexpr int QB = 64;      // queries per staged block (two 32-row sub-blocks)
   static constexpr int RP = D + 8;   // fp16 pitch of [query][d] rows
-  static constexpr int TP = MB + 8;  // fp16 pitch of [d][query] rows
-  f16 q[2][MB * RP];                 // [buffer]
+  static constexpr int TP = QB + 8;  // fp16 pitch of [d][query] rows
+  f16 q[2][QB * RP];                 // [buffer]
   f16 qt[2][D * TP];
-  f16 g[2][MB * RP];
+  f16 g[2][QB * RP];
   f16 gt[2][D * TP];
-  float lse[2][MB], Dd[2][MB];
+  float lse[2][QB], Dd[2][QB];
 };
 
 // dK and dV of each source.  Workgroup: 128 keys of one (batch, head), a wave
-// per 32; query blocks of 32 (Q, dO, lse2, D) staged into a double LDS buffer,
-// one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
+// per 32; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
+// and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
 // dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
-  constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP;
+  constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP, QB = DkvSmem<D>::QB;
   __shared__ DkvSmem<D> sm;
   const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
   const int kt = (int)(blockIdx.x / BH);  // small key tiles (most queries) first
@@ -675,21 +678,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   // threads 0 .. 127 stage Q, 128 .. 255 dO (rows and transposed)
   const bool qside = tid < 128;
   const int pi = tid & 127;
-  Pairs<D> px;
+  Pairs<D, QB> px;
   float lx = 0.f, dx = 0.f;
   auto load = [&](int i0) {
-    if (qside) load_pairs<D>(px, Qp, 0, i0, N, pi);
-    else load_pairs<D>(px, Gp, (size_t)(H * D), i0, N, pi);
-    if (tid < MB) {  // staged as the initial values of the S and dP accumulators
+    if (qside) load_pairs<D, QB>(px, Qp, 0, i0, N, pi);
+    else load_pairs<D, QB>(px, Gp, (size_t)(H * D), i0, N, pi);
+    if (tid < QB) {  // staged as the initial values of the S and dP accumulators
       const int i = i0 + tid;
       lx = i < N ? -p.lse[(size_t)bh * N + i] / sc2 : 0.f;
       dx = i < N ? -p.Dd[(size_t)bh * N + i] : 0.f;
     }
   };
   auto store = [&](int bf) {
-    if (qside) store_pairs<D, RP, TP>(px, sm.q[bf], sm.qt[bf], pi);
-    else store_pairs<D, RP, TP>(px, sm.g[bf], sm.gt[bf], pi);
-    if (tid < MB) {
+    if (qside) store_pairs<D, QB, RP, TP>(px, sm.q[bf], sm.qt[bf], pi);
+    else store_pairs<D, QB, RP, TP>(px, sm.g[bf], sm.gt[bf], pi);
+    if (tid < QB) {
       sm.lse[bf][tid] = lx;
       sm.Dd[bf][tid] = dx;
     }
@@ -720,31 +723,33 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
       store(bf);
       __syncthreads();
       while (true) {
-        const bool has_next = i0 + MB < i_end;
-        if (has_next) load(i0 + MB);  // in flight during the block
-        const BlockPass bp = block_pass(src, i0, kw0, N, w);
-        if (bp.part) {
+        const bool has_next = i0 + QB < i_end;
+        if (has_next) load(i0 + QB);  // in flight during the block
+#pragma unroll 1
+        for (int sb = 0; sb < 2; ++sb) {
+          const int q0 = i0 + 32 * sb;  // first query of the sub-block
+          const BlockPass bp = block_pass(src, q0, kw0, N, w);
+          if (!bp.part) continue;
           // S - lse2/sc2 and dP - D: the accumulators start from the staged
           // per-query values, so P = 2^(S sc2) and dS = P dP afterwards
           f32x16 s, dp;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            s[r] = sm.lse[bf][perm_row(r, lg)];
-            dp[r] = sm.Dd[bf][perm_row(r, lg)];
+            s[r] = sm.lse[bf][32 * sb + perm_row(r, lg)];
+            dp[r] = sm.Dd[bf][32 * sb + perm_row(r, lg)];
           }
+          const int arow = (32 * sb + row_perm(lr)) * RP + 8 * lg;
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
-            s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
-                             kf[st], s);
-            dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
-                              vf[st], dp);
+            s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + arow + 16 * st), kf[st], s);
+            dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + arow + 16 * st), vf[st], dp);
           }
           f16x8 pb[2], dsb[2];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
             if (bp.masked) {
-              const int i = i0 + perm_row(r, lg);
+              const int i = q0 + perm_row(r, lg);
               pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
             }
             pb[r >> 3][r & 7] = (f16)pr;
@@ -754,18 +759,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
           for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              dvt[db] = mfma32x32x16(
-                  *(const f16x8*)(sm.gt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), pb[u],
-                  dvt[db]);
-              dkt[db] = mfma32x32x16(
-                  *(const f16x8*)(sm.qt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), dsb[u],
-                  dkt[db]);
+              const int t = (32 * db + lr) * TP + 32 * sb + 16 * u + 8 * lg;
+              dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt[bf] + t), pb[u], dvt[db]);
+              dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt[bf] + t), dsb[u], dkt[db]);
             }
         }
         if (has_next) store(bf ^ 1);
         __syncthreads();
         if (!has_next) break;
-        i0 += MB;
+        i0 += QB;
         bf ^= 1;
       }
     }
