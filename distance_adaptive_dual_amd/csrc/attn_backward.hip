@@ -438,7 +438,7 @@ struct DqSmem {
 // the current one is computed, one barrier per pass).  S^T = K Q^T keeps a
 // query per lane; dP^T = V dO^T; dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_mfma(BwdProblem p) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int RP = DqSmem<D>::RP, TP = DqSmem<D>::TP;
   __shared__ DqSmem<D> sm;
