@@ -350,7 +350,9 @@ __device__ __forceinline__ uint32_t pack2(f16 lo, f16 hi) {
 }
 
 // Rows r0 .. r0+31 of a row-major fp16 [n][D] array (zero past N); with
-// grad_ld > 0 the source is bf16 dO rows of stride grad_ld, turned into fp16.
+// grad_ld > 0 the source is bf16 dO rows of stride grad_ld, held as bf16 bits
+// (store_pairs<..., true> turns them into fp16), so that no instruction uses
+// the loaded registers before the store and the loads stay in flight.
 template <int D, int ROWS>
 __device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, size_t grad_ld,
                                            int r0, int N, int pi) {
@@ -365,23 +367,25 @@ __device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, s
       if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * D + col);
     } else {
       const bf16* s = (const bf16*)src;
-      if (r0 + row < N) x.a[i] = bf16x8_to_f16x8(*(const u32x4*)(s + (size_t)(r0 + row) * grad_ld + col));
-      if (r0 + row + 1 < N)
-        x.b[i] = bf16x8_to_f16x8(*(const u32x4*)(s + (size_t)(r0 + row + 1) * grad_ld + col));
+      if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * grad_ld + col);
+      if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * grad_ld + col);
     }
   }
 }
 
-// ... as rows of pitch RP and transposed as [d][row] of pitch TP.
-template <int D, int ROWS, int RP, int TP>
+// ... as rows of pitch RP and transposed as [d][row] of pitch TP (BF: the
+// registers hold bf16 bits, converted to fp16 here).
+template <int D, int ROWS, int RP, int TP, bool BF = false>
 __device__ __forceinline__ void store_pairs(const Pairs<D, ROWS>& x, f16* rows, f16* cols,
                                             int pi) {
 #pragma unroll
   for (int i = 0; i < Pairs<D, ROWS>::NP; ++i) {
     const int q = pi + 128 * i, row = 2 * (q % (ROWS / 2)), col = (q / (ROWS / 2)) * 8;
-    *(u32x4*)(rows + row * RP + col) = x.a[i];
-    *(u32x4*)(rows + (row + 1) * RP + col) = x.b[i];
-    const f16x8 ha = __builtin_bit_cast(f16x8, x.a[i]), hb = __builtin_bit_cast(f16x8, x.b[i]);
+    const u32x4 va = BF ? bf16x8_to_f16x8(x.a[i]) : x.a[i];
+    const u32x4 vb = BF ? bf16x8_to_f16x8(x.b[i]) : x.b[i];
+    *(u32x4*)(rows + row * RP + col) = va;
+    *(u32x4*)(rows + (row + 1) * RP + col) = vb;
+    const f16x8 ha = __builtin_bit_cast(f16x8, va), hb = __builtin_bit_cast(f16x8, vb);
 #pragma unroll
     for (int e = 0; e < 8; ++e) *(uint32_t*)(cols + (col + e) * TP + row) = pack2(ha[e], hb[e]);
   }
@@ -659,6 +663,9 @@ struct DkvSmem {
 // per 32; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
 // and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
 // dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
+// At d_k 128 (one wave per SIMD, nothing to hide latency behind) the next
+// block is staged in two 32-query halves, which frees registers for operand
+// reads issued ahead of their MFMAs; at d_k 64 those extra registers spill.
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
@@ -667,7 +674,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
   const int kt = (int)(blockIdx.x / BH);  // small key tiles (most queries) first
   const int bh = (int)(blockIdx.x % BH), b = bh / H, h = bh % H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  constexpr bool WIDE = D == 128;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int wave = WIDE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int k0 = kt * MQ, kw0 = k0 + 32 * wave, kj = kw0 + lr;
   const int kc = kj < N ? kj : N - 1;
   const f16* Qp = (const f16*)p.Q + (size_t)bh * N * D;
@@ -678,21 +687,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   // threads 0 .. 127 stage Q, 128 .. 255 dO (rows and transposed)
   const bool qside = tid < 128;
   const int pi = tid & 127;
-  Pairs<D, QB> px;
+  constexpr int SR = WIDE ? 32 : QB;  // queries per staged part of a block
+  Pairs<D, SR> px;
   float lx = 0.f, dx = 0.f;
-  auto load = [&](int i0) {
-    if (qside) load_pairs<D, QB>(px, Qp, 0, i0, N, pi);
-    else load_pairs<D, QB>(px, Gp, (size_t)(H * D), i0, N, pi);
-    if (tid < QB) {  // staged as the initial values of the S and dP accumulators
+  auto load = [&](int i0, int hf) {
+    if (qside) load_pairs<D, SR>(px, Qp, 0, i0 + SR * hf, N, pi);
+    else load_pairs<D, SR>(px, Gp, (size_t)(H * D), i0 + SR * hf, N, pi);
+    if (hf == 0 && tid < QB) {  // staged as the initial values of the S and dP accumulators
       const int i = i0 + tid;
       lx = i < N ? -p.lse[(size_t)bh * N + i] / sc2 : 0.f;
       dx = i < N ? -p.Dd[(size_t)bh * N + i] : 0.f;
     }
   };
-  auto store = [&](int bf) {
-    if (qside) store_pairs<D, QB, RP, TP>(px, sm.q[bf], sm.qt[bf], pi);
-    else store_pairs<D, QB, RP, TP>(px, sm.g[bf], sm.gt[bf], pi);
-    if (tid < QB) {
+  auto store = [&](int bf, int hf) {
+    if (qside) store_pairs<D, SR, RP, TP>(px, sm.q[bf] + SR * hf * RP, sm.qt[bf] + SR * hf, pi);
+    else store_pairs<D, SR, RP, TP, true>(px, sm.g[bf] + SR * hf * RP, sm.gt[bf] + SR * hf, pi);
+    if (hf == 0 && tid < QB) {
       sm.lse[bf][tid] = lx;
       sm.Dd[bf][tid] = dx;
     }
@@ -719,16 +729,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
     const int i_end = src == 0 ? min(N, k_last + w) : N;
     if (i_begin < i_end) {
       int i0 = i_begin, bf = 0;
-      load(i0);
-      store(bf);
+      load(i0, 0);
+      store(bf, 0);
+      if (WIDE) {
+        load(i0, 1);
+        store(bf, 1);
+      }
       __syncthreads();
       while (true) {
         const bool has_next = i0 + QB < i_end;
-        if (has_next) load(i0 + QB);  // in flight during the block
+        if (has_next) load(i0 + QB, 0);  // in flight during the (first) sub-block
 #pragma unroll 1
         for (int sb = 0; sb < 2; ++sb) {
           const int q0 = i0 + 32 * sb;  // first query of the sub-block
           const BlockPass bp = block_pass(src, q0, kw0, N, w);
+          if (WIDE && sb == 1 && has_next) {  // the other buffer is not read in this block
+            store(bf ^ 1, 0);
+            load(i0 + QB, 1);
+          }
           if (!bp.part) continue;
           // S - lse2/sc2 and dP - D: the accumulators start from the staged
           // per-query values, so P = 2^(S sc2) and dS = P dP afterwards
@@ -744,27 +762,83 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
             s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + arow + 16 * st), kf[st], s);
             dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + arow + 16 * st), vf[st], dp);
           }
-          f16x8 pb[2], dsb[2];
+          if constexpr (WIDE) {
+            // the 32 staged lse/D values and the first four operands are read
+            // before the MFMAs start, then one more after each MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 16 + 4, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
-            if (bp.masked) {
-              const int i = q0 + perm_row(r, lg);
-              pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
+            for (int k = 0; k < 2 * NS - 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            pb[r >> 3][r & 7] = (f16)pr;
-            dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            // dV/dK operands of the first 16 queries, read before the
+            // exponentials so that their LDS latency hides under them
+            const int tb = lr * TP + 32 * sb + 8 * lg;
+            f16x8 ga[NB], qa[NB];
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              const int t = (32 * db + lr) * TP + 32 * sb + 16 * u + 8 * lg;
-              dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt[bf] + t), pb[u], dvt[db]);
-              dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt[bf] + t), dsb[u], dkt[db]);
+              ga[db] = *(const f16x8*)(sm.gt[bf] + tb + 32 * db * TP);
+              qa[db] = *(const f16x8*)(sm.qt[bf] + tb + 32 * db * TP);
             }
+            f16x8 pb[2], dsb[2];
+            if (bp.masked) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int i = q0 + perm_row(r, lg);
+                float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
+                pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
+                pb[r >> 3][r & 7] = (f16)pr;
+                dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
+                pb[r >> 3][r & 7] = (f16)pr;
+                dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
+              }
+            }
+            // the second 16 queries' operands, read while the first ones' MFMAs run
+            f16x8 gb[NB], qb[NB];
+#pragma unroll
+            for (int db = 0; db < NB; ++db) {
+              gb[db] = *(const f16x8*)(sm.gt[bf] + tb + 32 * db * TP + 16);
+              qb[db] = *(const f16x8*)(sm.qt[bf] + tb + 32 * db * TP + 16);
+            }
+#pragma unroll
+            for (int db = 0; db < NB; ++db) {
+              dvt[db] = mfma32x32x16(ga[db], pb[0], dvt[db]);
+              dkt[db] = mfma32x32x16(qa[db], dsb[0], dkt[db]);
+            }
+#pragma unroll
+            for (int db = 0; db < NB; ++db) {
+              dvt[db] = mfma32x32x16(gb[db], pb[1], dvt[db]);
+              dkt[db] = mfma32x32x16(qb[db], dsb[1], dkt[db]);
+            }
+          } else {
+            f16x8 pb[2], dsb[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
+              if (bp.masked) {
+                const int i = q0 + perm_row(r, lg);
+                pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
+              }
+              pb[r >> 3][r & 7] = (f16)pr;
+              dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int db = 0; db < NB; ++db) {
+                const int t = (32 * db + lr) * TP + 32 * sb + 16 * u + 8 * lg;
+                dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt[bf] + t), pb[u], dvt[db]);
+                dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt[bf] + t), dsb[u], dkt[db]);
+              }
+          }
         }
-        if (has_next) store(bf ^ 1);
+        if (has_next) store(bf ^ 1, WIDE ? 1 : 0);
         __syncthreads();
         if (!has_next) break;
         i0 += QB;
