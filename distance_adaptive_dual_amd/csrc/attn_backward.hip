@@ -663,9 +663,10 @@ struct DkvSmem {
 // per 32; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
 // and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
 // dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
-// At d_k 128 (one wave per SIMD, nothing to hide latency behind) the next
-// block is staged in two 32-query halves, which frees registers for operand
-// reads issued ahead of their MFMAs; at d_k 64 those extra registers spill.
+// The next block is staged in two 32-query halves (half a block of registers
+// in flight).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
+// the MFMA operands are also read ahead of their MFMAs; at d_k 64 the
+// registers that takes spill.
 template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
@@ -676,7 +677,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   const int bh = (int)(blockIdx.x % BH), b = bh / H, h = bh % H;
   constexpr bool WIDE = D == 128;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-  const int wave = WIDE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // block tests are scalar
   const int k0 = kt * MQ, kw0 = k0 + 32 * wave, kj = kw0 + lr;
   const int kc = kj < N ? kj : N - 1;
   const f16* Qp = (const f16*)p.Q + (size_t)bh * N * D;
@@ -687,7 +688,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   // threads 0 .. 127 stage Q, 128 .. 255 dO (rows and transposed)
   const bool qside = tid < 128;
   const int pi = tid & 127;
-  constexpr int SR = WIDE ? 32 : QB;  // queries per staged part of a block
+  constexpr int SR = QB / 2;  // queries per staged half of a block
   Pairs<D, SR> px;
   float lx = 0.f, dx = 0.f;
   auto load = [&](int i0, int hf) {
@@ -731,19 +732,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
       int i0 = i_begin, bf = 0;
       load(i0, 0);
       store(bf, 0);
-      if (WIDE) {
-        load(i0, 1);
-        store(bf, 1);
-      }
+      load(i0, 1);
+      store(bf, 1);
       __syncthreads();
       while (true) {
         const bool has_next = i0 + QB < i_end;
-        if (has_next) load(i0 + QB, 0);  // in flight during the (first) sub-block
+        if (has_next) load(i0 + QB, 0);  // in flight during the first sub-block
 #pragma unroll 1
         for (int sb = 0; sb < 2; ++sb) {
           const int q0 = i0 + 32 * sb;  // first query of the sub-block
           const BlockPass bp = block_pass(src, q0, kw0, N, w);
-          if (WIDE && sb == 1 && has_next) {  // the other buffer is not read in this block
+          if (sb == 1 && has_next) {  // the other buffer is not read in this block
             store(bf ^ 1, 0);
             load(i0 + QB, 1);
           }
@@ -772,33 +771,37 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
               __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            // dV/dK operands of the first 16 queries, read before the
-            // exponentials so that their LDS latency hides under them
-            const int tb = lr * TP + 32 * sb + 8 * lg;
-            f16x8 ga[NB], qa[NB];
+          }
+          // dV/dK operands of the first 16 queries (d_k 128: read before the
+          // exponentials, so that their LDS latency hides under them)
+          const int tb = lr * TP + 32 * sb + 8 * lg;
+          f16x8 ga[NB], qa[NB];
+          if constexpr (WIDE) {
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
               ga[db] = *(const f16x8*)(sm.gt[bf] + tb + 32 * db * TP);
               qa[db] = *(const f16x8*)(sm.qt[bf] + tb + 32 * db * TP);
             }
-            f16x8 pb[2], dsb[2];
-            if (bp.masked) {
+          }
+          f16x8 pb[2], dsb[2];
+          if (bp.masked) {
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int i = q0 + perm_row(r, lg);
-                float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
-                pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
-                pb[r >> 3][r & 7] = (f16)pr;
-                dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
-              }
-            } else {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
-                pb[r >> 3][r & 7] = (f16)pr;
-                dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
-              }
+            for (int r = 0; r < 16; ++r) {
+              const int i = q0 + perm_row(r, lg);
+              float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
+              pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
+              pb[r >> 3][r & 7] = (f16)pr;
+              dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
             }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
+              pb[r >> 3][r & 7] = (f16)pr;
+              dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
+            }
+          }
+          if constexpr (WIDE) {
             // the second 16 queries' operands, read while the first ones' MFMAs run
             f16x8 gb[NB], qb[NB];
 #pragma unroll
@@ -817,28 +820,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
               dkt[db] = mfma32x32x16(qb[db], dsb[1], dkt[db]);
             }
           } else {
-            f16x8 pb[2], dsb[2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
-              if (bp.masked) {
-                const int i = q0 + perm_row(r, lg);
-                pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
-              }
-              pb[r >> 3][r & 7] = (f16)pr;
-              dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
-            }
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
               for (int db = 0; db < NB; ++db) {
-                const int t = (32 * db + lr) * TP + 32 * sb + 16 * u + 8 * lg;
+                const int t = tb + 32 * db * TP + 16 * u;
                 dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt[bf] + t), pb[u], dvt[db]);
                 dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt[bf] + t), dsb[u], dkt[db]);
               }
           }
         }
-        if (has_next) store(bf ^ 1, WIDE ? 1 : 0);
+        if (has_next) store(bf ^ 1, 1);
         __syncthreads();
         if (!has_next) break;
         i0 += QB;
