@@ -43,6 +43,9 @@ def _load():
         lib.dar_oracle_project.restype = ctypes.c_int
         lib.dar_oracle_project.argtypes = [_D] * 6 + [ctypes.c_int] * 6 + [
             ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [_D] * 7
+        lib.dar_oracle_project_act.restype = ctypes.c_int
+        lib.dar_oracle_project_act.argtypes = [_D] * 6 + [ctypes.c_int] * 6 + [
+            ctypes.c_long, ctypes.c_double] + [ctypes.c_int] * 4 + [_D] * 7
         lib.dar_oracle_attend.restype = ctypes.c_int
         lib.dar_oracle_attend.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [ctypes.c_long] + [_D] * 2
         lib.dar_oracle_attend_rows.restype = ctypes.c_int
@@ -73,12 +76,15 @@ def threads() -> int:
 
 
 def project(h, W_down, W_up, W_Q, W_K, W_V, H, d_k, pos0=0, base=10000.0, n_tok=None,
-            heads=None):
+            heads=None, act="linear"):
     """Eqs. 1-3 projections.  Returns dict hD, hp, Q, KL, VL, KG, VG (float64).
 
     h [B,N,d]; Q/KL/VL/KG/VG [B,H,N,d_k]; only tokens < n_tok and heads in the
-    ``heads`` range (lo, hi) are computed (the rest stay zero).
+    ``heads`` range (lo, hi) are computed (the rest stay zero).  act="sigmoid":
+    the variant with a sigmoid after the down-projection of Eq. 1.
     """
+    if act not in ("linear", "sigmoid"):
+        raise ValueError("act must be 'linear' or 'sigmoid'")
     h, W_down, W_up, W_Q, W_K, W_V = map(_f64, (h, W_down, W_up, W_Q, W_K, W_V))
     B, N, d = h.shape
     d_down = W_down.shape[1]
@@ -89,10 +95,11 @@ def project(h, W_down, W_up, W_Q, W_K, W_V, H, d_k, pos0=0, base=10000.0, n_tok=
     out = dict(hD=np.zeros((B, N, d_down)), hp=np.zeros((B, N, d)))
     for k in ("Q", "KL", "VL", "KG", "VG"):
         out[k] = np.zeros((B, H, N, d_k))
-    rc = _load().dar_oracle_project(
+    rc = _load().dar_oracle_project_act(
         _p(h), _p(W_down), _p(W_up), _p(W_Q), _p(W_K), _p(W_V), B, N, d, d_down, H, d_k,
-        int(pos0), float(base), n_tok, lo, hi, _p(out["hD"]), _p(out["hp"]), _p(out["Q"]),
-        _p(out["KL"]), _p(out["VL"]), _p(out["KG"]), _p(out["VG"]))
+        int(pos0), float(base), n_tok, lo, hi, 1 if act == "sigmoid" else 0, _p(out["hD"]),
+        _p(out["hp"]), _p(out["Q"]), _p(out["KL"]), _p(out["VL"]), _p(out["KG"]),
+        _p(out["VG"]))
     if rc != 0:
         raise ValueError("dar_oracle_project rejected its arguments")
     return out

@@ -66,6 +66,8 @@ static void rope(double* x, int d_k, double pos, double base) {
 /*
  * Projections of tokens n < n_tok of every sequence, heads [head_lo, head_hi):
  *   hD = h W_down                      (Eq. 1)      hD : [B, N, d_down]
+ *        act = 1: hD = sigmoid(h W_down), 1 / (1 + e^-x) per element (the
+ *        variant named in the paragraph after Eq. 1); act = 0: as written
  *   hp = hD W_up                       (Eq. 2)      hp : [B, N, d]
  *   Q  = RoPE_p(h  W_Q[:, S_a])        (q_i, Eq. 4 text)
  *   KL = RoPE_p(h  W_K[:, S_a]),  VL = h  W_V[:, S_a]   (Eq. 3, i - j <  w)
@@ -73,12 +75,13 @@ static void rope(double* x, int d_k, double pos, double base) {
  * Q, KL, VL, KG, VG : [B, H, N, d_k]; p = pos0 + n.
  * Returns 0, or -1 on a bad argument.
  */
-int dar_oracle_project(const double* h, const double* W_down, const double* W_up,
-                       const double* W_Q, const double* W_K, const double* W_V,
-                       int B, int N, int d, int d_down, int H, int d_k, long pos0,
-                       double base, int n_tok, int head_lo, int head_hi,
-                       double* hD, double* hp, double* Q, double* KL, double* VL,
-                       double* KG, double* VG) {
+int dar_oracle_project_act(const double* h, const double* W_down, const double* W_up,
+                           const double* W_Q, const double* W_K, const double* W_V,
+                           int B, int N, int d, int d_down, int H, int d_k, long pos0,
+                           double base, int n_tok, int head_lo, int head_hi, int act,
+                           double* hD, double* hp, double* Q, double* KL, double* VL,
+                           double* KG, double* VG) {
+  if (act != 0 && act != 1) return -1;
   if (B < 1 || N < 1 || d < 1 || d_down < 1 || H < 1 || d_k < 2 || (d_k & 1)) return -1;
   if (n_tok < 0 || n_tok > N || head_lo < 0 || head_hi > H || head_lo > head_hi) return -1;
   const int hd = H * d_k;
@@ -91,6 +94,8 @@ int dar_oracle_project(const double* h, const double* W_down, const double* W_up
     double* xD = hD + tok * d_down;
     double* xp = hp + tok * d;
     vec_mat(x, W_down, d, d_down, 0, d_down, xD);  /* Eq. 1 */
+    if (act == 1) /* the variant with a sigmoid after the down-projection */
+      for (int k = 0; k < d_down; ++k) xD[k] = 1.0 / (1.0 + exp(-xD[k]));
     vec_mat(xD, W_up, d_down, d, 0, d, xp);        /* Eq. 2 */
     const double pos = (double)(pos0 + n);
     for (int a = head_lo; a < head_hi; ++a) {
@@ -106,6 +111,16 @@ int dar_oracle_project(const double* h, const double* W_down, const double* W_up
     }
   }
   return 0;
+}
+
+int dar_oracle_project(const double* h, const double* W_down, const double* W_up,
+                       const double* W_Q, const double* W_K, const double* W_V,
+                       int B, int N, int d, int d_down, int H, int d_k, long pos0,
+                       double base, int n_tok, int head_lo, int head_hi,
+                       double* hD, double* hp, double* Q, double* KL, double* VL,
+                       double* KG, double* VG) {
+  return dar_oracle_project_act(h, W_down, W_up, W_Q, W_K, W_V, B, N, d, d_down, H, d_k, pos0,
+                                base, n_tok, head_lo, head_hi, 0, hD, hp, Q, KL, VL, KG, VG);
 }
 
 /*
