@@ -111,7 +111,8 @@ def make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed):
 def prefill_step(dar, s, H, d_k, w):
     W = s["W"]
     dar.dar_project(s["h"], W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
-                    W_upK=s["Wk"], W_upV=s["Wv"], out=s["out"], workspace=s["ws"])
+                    W_upK=s["Wk"], W_upV=s["Wv"], out=s["out"], workspace=s["ws"],
+                    sigmoid=s.get("sigmoid", False))
     out = s["out"]
     dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"], out["V_glob"], w,
                          o=s["o"])
@@ -189,7 +190,7 @@ def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
     out = s["out"]
     proj = lambda: dar.dar_project(s["h"], W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"],
                                    H, d_k, W_upK=s["Wk"], W_upV=s["Wv"], out=out,
-                                   workspace=s["ws"])
+                                   workspace=s["ws"], sigmoid=s.get("sigmoid", False))
     attn = lambda: dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"],
                                         out["V_glob"], w, o=s["o"])
     return wall, ev, graph_launch_ms(torch, proj), graph_launch_ms(torch, attn)
@@ -486,6 +487,15 @@ def main():
                 pf, af = prefill_flops(B, N, d, dd)
                 sweep["d_down%d" % dd] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9}
                 del s2
+            # the sigmoid-bottleneck variant on the same workload (the sigmoid is
+            # B N d_down exponentials in the projection epilogue; FLOP count as above)
+            _, s2 = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=2000 + d_down)
+            s2["sigmoid"] = True
+            ms2, _, p2, a2 = time_prefill(torch, dar, s2, H, d_k, w, args.steps, args.warmup)
+            pf, af = prefill_flops(B, N, d, d_down)
+            sweep["sigmoid d_down%d" % d_down] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9,
+                                                 "proj_ms": p2, "attn_ms": a2}
+            del s2
             for name, cfg in (("pythia410m B8 N2048 d1024 H16 dk64 w128 d_down256",
                                (8, 2048, 1024, 16, 64, 128, 256)),
                               ("1b B4 N8192 d2048 H16 dk128 w512 d_down512",

@@ -25,6 +25,7 @@ STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
 EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
+           "dar_project_sigmoid",
            "dar_attn_prefill", "dar_attn_prefill_lse", "dar_attn_prefill_backward",
            "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.dar_fold.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]
         L.dar_project.restype = _I
         L.dar_project.argtypes = [_P] * 8 + [_I] * 7 + [ctypes.c_float, _I] + [_P] * 7 + [_SZ, _P]
+        L.dar_project_sigmoid.restype = _I
+        L.dar_project_sigmoid.argtypes = L.dar_project.argtypes
         L.dar_attn_prefill.restype = _I
         L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P]
         L.dar_attn_prefill_lse.restype = _I
@@ -181,11 +184,12 @@ def project_workspace_bytes(B, N, d, d_down, heads, d_k, pos0=0, folded=True, dt
 
 def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None, W_upV=None,
                 pos0: int = 0, rope_base: float = 10000.0, out=None, workspace=None,
-                stream=None):
+                stream=None, sigmoid: bool = False):
     """Eqs. (1)-(3) projections.  Returns dict Q, K_loc, V_loc, h_D, K_glob, V_glob.
 
     h [B, N, d]; weights column-major ([out, in] tensors).  V_loc / V_glob come
-    back as [B, heads, d_k, N] (token innermost)."""
+    back as [B, heads, d_k, N] (token innermost).  sigmoid=True calls
+    dar_project_sigmoid (h^D = sigmoid(h W_down))."""
     torch = _torch()
     B, N, d = h.shape
     d_down = W_down.shape[0]
@@ -201,7 +205,8 @@ def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None
     args = [_ptr(h), _ptr(W_down), _ptr(W_up), _ptr(W_Q), _ptr(W_K), _ptr(W_V),
             _ptr(W_upK), _ptr(W_upV), B, N, d, d_down, heads, d_k, pos0, float(rope_base), dt]
     args += [_ptr(out[k]) for k in ("Q", "K_loc", "V_loc", "h_D", "K_glob", "V_glob")]
-    _call_ws("dar_project", lib().dar_project, args, workspace, h, stream)
+    name = "dar_project_sigmoid" if sigmoid else "dar_project"
+    _call_ws(name, getattr(lib(), name), args, workspace, h, stream)
     return out
 
 

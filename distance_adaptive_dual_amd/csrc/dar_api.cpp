@@ -85,12 +85,14 @@ dar_status dar_fold(const void* W_up, const void* W_K, const void* W_V, int d, i
   return hip_status(e);
 }
 
-dar_status dar_project(const void* h, const void* W_down, const void* W_up, const void* W_Q,
-                       const void* W_K, const void* W_V, const void* W_upK, const void* W_upV,
-                       int B, int N, int d, int d_down, int heads, int d_k, int pos0,
-                       float rope_base, dar_dtype dtype, void* Q, void* K_loc, void* V_loc,
-                       void* h_D, void* K_glob, void* V_glob, void* workspace,
-                       size_t* workspace_bytes, hipStream_t stream) {
+// act: 0 for Eq. (1) as written, 1 for the sigmoid after the down-projection.
+static dar_status project_impl(const void* h, const void* W_down, const void* W_up,
+                               const void* W_Q, const void* W_K, const void* W_V,
+                               const void* W_upK, const void* W_upV, int B, int N, int d,
+                               int d_down, int heads, int d_k, int pos0, float rope_base,
+                               dar_dtype dtype, void* Q, void* K_loc, void* V_loc, void* h_D,
+                               void* K_glob, void* V_glob, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream, int act) {
   if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || pos0 < 0)
     return DAR_ERR_INVALID_ARG;
@@ -164,6 +166,7 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   g1.seg[1] = GemmSeg{W_K, K_loc, hd, kHead, 1};
   g1.seg[2] = GemmSeg{W_V, V_loc, hd, kHeadT, 0};
   g1.seg[3] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0};
+  g1.seg[3].act = act;
   g1.n_seq = N;
   g1.heads = heads;
   g1.d_k = d_k;
@@ -181,6 +184,29 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
   g2.seg[1] = GemmSeg{fV, V_glob, hd, kHeadT, 0};
   e = launch_project_gemm(g2, dtype, stream);
   return hip_status(e);
+}
+
+dar_status dar_project(const void* h, const void* W_down, const void* W_up, const void* W_Q,
+                       const void* W_K, const void* W_V, const void* W_upK, const void* W_upV,
+                       int B, int N, int d, int d_down, int heads, int d_k, int pos0,
+                       float rope_base, dar_dtype dtype, void* Q, void* K_loc, void* V_loc,
+                       void* h_D, void* K_glob, void* V_glob, void* workspace,
+                       size_t* workspace_bytes, hipStream_t stream) {
+  return project_impl(h, W_down, W_up, W_Q, W_K, W_V, W_upK, W_upV, B, N, d, d_down, heads, d_k,
+                      pos0, rope_base, dtype, Q, K_loc, V_loc, h_D, K_glob, V_glob, workspace,
+                      workspace_bytes, stream, 0);
+}
+
+dar_status dar_project_sigmoid(const void* h, const void* W_down, const void* W_up,
+                               const void* W_Q, const void* W_K, const void* W_V,
+                               const void* W_upK, const void* W_upV, int B, int N, int d,
+                               int d_down, int heads, int d_k, int pos0, float rope_base,
+                               dar_dtype dtype, void* Q, void* K_loc, void* V_loc, void* h_D,
+                               void* K_glob, void* V_glob, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream) {
+  return project_impl(h, W_down, W_up, W_Q, W_K, W_V, W_upK, W_upV, B, N, d, d_down, heads, d_k,
+                      pos0, rope_base, dtype, Q, K_loc, V_loc, h_D, K_glob, V_glob, workspace,
+                      workspace_bytes, stream, 1);
 }
 
 static dar_status attn_prefill_impl(const void* Q, const void* K_loc, const void* V_loc,

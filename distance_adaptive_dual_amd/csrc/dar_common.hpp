@@ -151,6 +151,9 @@ struct GemmSeg {
   // With GemmProblem::row_pos (one token per sequence): where row b lands.
   // kPosFixed: index seq_off; kPosRow: row_pos[b]; kPosRing: row_pos[b] mod ld_seq.
   int pos_mode = 0;
+  // kRowMajor only: 1 applies the logistic sigmoid to the fp32 result before
+  // it is rounded and stored (the sigmoid-bottleneck variant of h^D)
+  int act = 0;
 };
 enum PosMode : int { kPosFixed = 0, kPosRow = 1, kPosRing = 2 };
 

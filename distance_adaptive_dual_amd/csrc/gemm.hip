@@ -79,6 +79,13 @@ __device__ __forceinline__ void store_run4(OutT* dst, const float* v) {
 // tile column c is segment column col0 + c.  Each thread owns one row and a
 // contiguous run of columns (kHeadT: one column and a run of rows), so the
 // (b, n) division happens once per thread and stores are 8-16 bytes wide.
+// Logistic sigmoid 1 / (1 + e^-x) in fp32, for the variant that applies it
+// after the down-projection of Eq. (1).
+__device__ __forceinline__ void sigmoid8(float* v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 1.f / (1.f + expf(-v[e]));
+}
+
 template <typename OutT, int D, int ROWS>
 __device__ void epilogue_store(const float* tile, int row0, int col0, const GemmSeg& seg,
                                const GemmProblem& p) {
@@ -133,6 +140,7 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = trow[c + i + e];
+      if (seg.act) sigmoid8(v);
       store_run<OutT, 8>(dst + i, v);
     }
     return;
@@ -245,6 +253,7 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
       OutT* dst;
       if (seg.kind == kRowMajor) {
         dst = out + ((size_t)b * ld + no) * width + gcol;
+        if (seg.act) sigmoid8(v);
       } else {
         const int head = gcol / D, t = gcol % D;
         dst = out + (((size_t)b * H + head) * ld + no) * D + t;

@@ -114,6 +114,27 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
                        size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * dar_project_sigmoid -- dar_project for the variant that applies a sigmoid
+ * after the down-projection of Eq. (1) ("Dual Dimensionality for Local and
+ * Global Attention", the paragraph after Eq. (1): evaluated by the authors,
+ * found comparable to the linear form, not adopted):
+ *   h_D    [B, N, d_down]       sigma(h W_down),  sigma(x) = 1 / (1 + e^-x)
+ *   K_glob, V_glob              from that h^D through the same folded weights
+ * elementwise, in fp32, before h^D is rounded to its storage type.  Q, K_loc
+ * and V_loc are those of dar_project.  Arguments, layouts, workspace and
+ * errors are those of dar_project.  The decode-side entry points compute the
+ * linear h^D; a model with this variant builds its cache from this call's
+ * h_D (dar_cache_from_prefill).
+ */
+dar_status dar_project_sigmoid(const void* h, const void* W_down, const void* W_up,
+                               const void* W_Q, const void* W_K, const void* W_V,
+                               const void* W_upK, const void* W_upV, int B, int N, int d,
+                               int d_down, int heads, int d_k, int pos0, float rope_base,
+                               dar_dtype dtype, void* Q, void* K_loc, void* V_loc, void* h_D,
+                               void* K_glob, void* V_glob, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * dar_attn_prefill -- Eq. (4) with the Eq. (3) distance selection, causal.
  *
  * For query i and key j <= i of the same sequence and head, the key/value

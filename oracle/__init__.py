@@ -161,10 +161,10 @@ def attend_backward(P, w, dO):
     return g
 
 
-def prefill(inp, H, d_k, w, pos0=0, base=10000.0):
+def prefill(inp, H, d_k, w, pos0=0, base=10000.0, act="linear"):
     """Whole forward pass: projections then attention.  Returns (o, rowsum, projections)."""
     P = project(inp["h"], inp["W_down"], inp["W_up"], inp["W_Q"], inp["W_K"], inp["W_V"],
-                H, d_k, pos0=pos0, base=base)
+                H, d_k, pos0=pos0, base=base, act=act)
     o, rs = attend(P, w)
     return o, rs, P
 
