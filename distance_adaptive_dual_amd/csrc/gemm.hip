@@ -80,10 +80,13 @@ __device__ __forceinline__ void store_run4(OutT* dst, const float* v) {
 // contiguous run of columns (kHeadT: one column and a run of rows), so the
 // (b, n) division happens once per thread and stores are 8-16 bytes wide.
 // Logistic sigmoid 1 / (1 + e^-x) in fp32, for the variant that applies it
-// after the down-projection of Eq. (1).
+// after the down-projection of Eq. (1): e^-x as 2^(-x log2 e) and the
+// hardware reciprocal (a few ulp; the latent is then rounded to 16 bits in
+// bf16 mode).  Large negative x gives 2^+inf = inf and 0, large positive 1.
 __device__ __forceinline__ void sigmoid8(float* v) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = 1.f / (1.f + expf(-v[e]));
+  for (int e = 0; e < 8; ++e)
+    v[e] = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-v[e] * kLog2e));
 }
 
 template <typename OutT, int D, int ROWS>
