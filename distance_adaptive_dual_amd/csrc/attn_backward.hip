@@ -349,11 +349,12 @@ __device__ __forceinline__ uint32_t pack2(f16 lo, f16 hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-// Rows r0 .. r0+31 of a row-major fp16 [n][D] array (zero past N); with
+// Rows r0 .. r0+ROWS-1, columns 0 .. D-1 of a row-major fp16 array of row
+// stride LDF (zero past N); with
 // grad_ld > 0 the source is bf16 dO rows of stride grad_ld, held as bf16 bits
 // (store_pairs<..., true> turns them into fp16), so that no instruction uses
 // the loaded registers before the store and the loads stay in flight.
-template <int D, int ROWS>
+template <int D, int ROWS, int LDF = D>
 __device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, size_t grad_ld,
                                            int r0, int N, int pi) {
 #pragma unroll
@@ -363,8 +364,8 @@ __device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, s
     x.a[i] = x.b[i] = z;
     if (grad_ld == 0) {
       const f16* s = (const f16*)src;
-      if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * D + col);
-      if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * D + col);
+      if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * LDF + col);
+      if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * LDF + col);
     } else {
       const bf16* s = (const bf16*)src;
       if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * grad_ld + col);
@@ -663,8 +664,9 @@ struct DkvSmem {
 // per 32; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
 // and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
 // dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
-// The next block is staged in two 32-query halves (half a block of registers
-// in flight).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
+// The next block is staged in two halves of its head dims (all 64 queries
+// each, half a block of registers in flight; a wave's transposed stores then
+// cover 32 row pairs in two column groups 32 banks apart, without conflicts).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
 // the MFMA operands are also read ahead of their MFMAs; at d_k 64 the
 // registers that takes spill.
 template <int D>
@@ -688,12 +690,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   // threads 0 .. 127 stage Q, 128 .. 255 dO (rows and transposed)
   const bool qside = tid < 128;
   const int pi = tid & 127;
-  constexpr int SR = QB / 2;  // queries per staged half of a block
-  Pairs<D, SR> px;
+  constexpr int DC = D / 2;  // head dims per staged half of a block (all its queries)
+  Pairs<DC, QB> px;
   float lx = 0.f, dx = 0.f;
   auto load = [&](int i0, int hf) {
-    if (qside) load_pairs<D, SR>(px, Qp, 0, i0 + SR * hf, N, pi);
-    else load_pairs<D, SR>(px, Gp, (size_t)(H * D), i0 + SR * hf, N, pi);
+    if (qside) load_pairs<DC, QB, D>(px, Qp + DC * hf, 0, i0, N, pi);
+    else load_pairs<DC, QB>(px, Gp + DC * hf, (size_t)(H * D), i0, N, pi);
     if (hf == 0 && tid < QB) {  // staged as the initial values of the S and dP accumulators
       const int i = i0 + tid;
       lx = i < N ? -p.lse[(size_t)bh * N + i] / sc2 : 0.f;
@@ -701,8 +703,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
     }
   };
   auto store = [&](int bf, int hf) {
-    if (qside) store_pairs<D, SR, RP, TP>(px, sm.q[bf] + SR * hf * RP, sm.qt[bf] + SR * hf, pi);
-    else store_pairs<D, SR, RP, TP, true>(px, sm.g[bf] + SR * hf * RP, sm.gt[bf] + SR * hf, pi);
+    if (qside) store_pairs<DC, QB, RP, TP>(px, sm.q[bf] + DC * hf, sm.qt[bf] + DC * hf * TP, pi);
+    else store_pairs<DC, QB, RP, TP, true>(px, sm.g[bf] + DC * hf, sm.gt[bf] + DC * hf * TP, pi);
     if (hf == 0 && tid < QB) {
       sm.lse[bf][tid] = lx;
       sm.Dd[bf][tid] = dx;
