@@ -66,6 +66,21 @@ struct Stage {
   u32x4 k[NCH], v[NCH];
 };
 
+// One 16-byte chunk of K row j (fp16 [N x D] rows, j may lie outside [0, N)):
+// through a buffer resource whose range check returns zeros past the rows,
+// no branch, while the slice is below 2 GiB; else a guarded load.
+template <int D>
+__device__ __forceinline__ u32x4 load_k_chunk(const f16* K, int N, int j, int col) {
+  if ((long)N * D * 2 < 0x7fffffffL) {
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)K, (short)0, N * D * 2, 0x00020000);
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rk, (j * D + col) * 2, 0, 0));
+  }
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return ((unsigned)j < (unsigned)N) ? *(const u32x4*)(K + (size_t)j * D + col) : z;
+}
+
 // K and Vt hold positions base .. base+N-1 of one (batch, head) (K [N x D],
 // Vt [D x N]); j0 = first position of the tile - base, which may be negative
 // for the local arrays of a chunk: rows outside [0, N) read as zeros.
@@ -78,7 +93,7 @@ __device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16*
   for (int i = 0; i < Stage<D>::NCH; ++i) {
     const int c = tid + 256 * i;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    st.k[i] = ((unsigned)(j0 + row) < (unsigned)N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
+    st.k[i] = load_k_chunk<D>(K, N, j0 + row, col);
     const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
     if (vec_ok) {
       st.v[i] = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
@@ -107,7 +122,7 @@ __device__ __forceinline__ void load_k(u32x4 (&k)[Stage<D>::NCH], const f16* K, 
   for (int i = 0; i < Stage<D>::NCH; ++i) {
     const int c = tid + 256 * i;
     const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    k[i] = ((unsigned)(j0 + row) < (unsigned)N) ? *(const u32x4*)(K + (size_t)(j0 + row) * D + col) : z;
+    k[i] = load_k_chunk<D>(K, N, j0 + row, col);
   }
 }
 
