@@ -349,28 +349,37 @@ __device__ __forceinline__ uint32_t pack2(f16 lo, f16 hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// 16 bytes at row r, column col of a row-major array of 2-byte elements with
+// n rows of stride ld; rows r >= n read as zeros.  BUF (the launcher's choice
+// when every staged array is under 2 GiB): through a buffer resource, whose
+// range check supplies the zeros without a branch; else a guarded load.
+template <bool BUF>
+__device__ __forceinline__ u32x4 load_row16(const void* base, int n, size_t ld, int r, int col) {
+  if constexpr (BUF) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(n * ld * 2), 0x00020000);
+    const unsigned off = ((unsigned)r * (unsigned)ld + (unsigned)col) * 2u;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    return r < n ? *(const u32x4*)((const uint16_t*)base + (size_t)r * ld + col) : z;
+  }
+}
+
 // Rows r0 .. r0+ROWS-1, columns 0 .. D-1 of a row-major fp16 array of row
 // stride LDF (zero past N); with
 // grad_ld > 0 the source is bf16 dO rows of stride grad_ld, held as bf16 bits
 // (store_pairs<..., true> turns them into fp16), so that no instruction uses
 // the loaded registers before the store and the loads stay in flight.
-template <int D, int ROWS, int LDF = D>
+template <int D, int ROWS, bool BUF, int LDF = D>
 __device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, size_t grad_ld,
                                            int r0, int N, int pi) {
+  const size_t ld = grad_ld == 0 ? (size_t)LDF : grad_ld;
 #pragma unroll
   for (int i = 0; i < Pairs<D, ROWS>::NP; ++i) {
     const int q = pi + 128 * i, row = 2 * (q % (ROWS / 2)), col = (q / (ROWS / 2)) * 8;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    x.a[i] = x.b[i] = z;
-    if (grad_ld == 0) {
-      const f16* s = (const f16*)src;
-      if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * LDF + col);
-      if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * LDF + col);
-    } else {
-      const bf16* s = (const bf16*)src;
-      if (r0 + row < N) x.a[i] = *(const u32x4*)(s + (size_t)(r0 + row) * grad_ld + col);
-      if (r0 + row + 1 < N) x.b[i] = *(const u32x4*)(s + (size_t)(r0 + row + 1) * grad_ld + col);
-    }
+    x.a[i] = load_row16<BUF>(src, N, ld, r0 + row, col);
+    x.b[i] = load_row16<BUF>(src, N, ld, r0 + row + 1, col);
   }
 }
 
@@ -442,7 +451,7 @@ struct DqSmem {
 // staged per source into a double LDS buffer (the next pass is staged while
 // the current one is computed, one barrier per pass).  S^T = K Q^T keeps a
 // query per lane; dP^T = V dO^T; dS^T = P^T (dP^T - D); dQ^T += K^T dS^T.
-template <int D>
+template <int D, bool BUF>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int RP = DqSmem<D>::RP, TP = DqSmem<D>::TP;
@@ -586,7 +595,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p
     const int pi = tid & 127;
     Pairs<D, MB> px;
     auto load2 = [&](int jj, int ss) {
-      if (kside) load_pairs<D, MB>(px, Kp(ss), 0, jj, N, pi);
+      if (kside) load_pairs<D, MB, BUF>(px, Kp(ss), 0, jj, N, pi);
       else load_vt_pairs<D>(px, Vp(ss), jj, N, pi);
     };
     auto store2 = [&](int bb) {
@@ -669,7 +678,7 @@ struct DkvSmem {
 // cover 32 row pairs in two column groups 32 banks apart, without conflicts).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
 // the MFMA operands are also read ahead of their MFMAs; at d_k 64 the
 // registers that takes spill.
-template <int D>
+template <int D, bool BUF>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP, QB = DkvSmem<D>::QB;
@@ -694,8 +703,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   Pairs<DC, QB> px;
   float lx = 0.f, dx = 0.f;
   auto load = [&](int i0, int hf) {
-    if (qside) load_pairs<DC, QB, D>(px, Qp + DC * hf, 0, i0, N, pi);
-    else load_pairs<DC, QB>(px, Gp + DC * hf, (size_t)(H * D), i0, N, pi);
+    if (qside) load_pairs<DC, QB, BUF, D>(px, Qp + DC * hf, 0, i0, N, pi);
+    else load_pairs<DC, QB, BUF>(px, Gp + DC * hf, (size_t)(H * D), i0, N, pi);
     if (hf == 0 && tid < QB) {  // staged as the initial values of the S and dP accumulators
       const int i = i0 + tid;
       lx = i < N ? -p.lse[(size_t)bh * N + i] / sc2 : 0.f;
@@ -879,13 +888,22 @@ hipError_t launch_attn_backward(const BwdProblem& p_in, dar_dtype dt, hipStream_
   const bool bf = dt == DAR_BF16;
   if (bf) {
     const int nT = (p.N + MQ - 1) / MQ;
+    // buffer-resource staging when the largest staged array (one batch's dO
+    // rows, stride heads * d_k) is under 2 GiB
+    const bool buf = (long)p.N * p.H * p.d_k * 2 < 0x7fffffffL;
+#define DAR_BWD_MFMA(DV, BUFV)                                                   \
+  do {                                                                           \
+    hipLaunchKernelGGL((bwd_dq_mfma<DV, BUFV>), dim3(nT * BH), dim3(256), 0, s, p);  \
+    hipLaunchKernelGGL((bwd_dkv_mfma<DV, BUFV>), dim3(nT * BH), dim3(256), 0, s, p); \
+  } while (0)
     if (p.d_k == 64) {
-      hipLaunchKernelGGL((bwd_dq_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
-      hipLaunchKernelGGL((bwd_dkv_mfma<64>), dim3(nT * BH), dim3(256), 0, s, p);
+      if (buf) DAR_BWD_MFMA(64, true);
+      else DAR_BWD_MFMA(64, false);
     } else {
-      hipLaunchKernelGGL((bwd_dq_mfma<128>), dim3(nT * BH), dim3(256), 0, s, p);
-      hipLaunchKernelGGL((bwd_dkv_mfma<128>), dim3(nT * BH), dim3(256), 0, s, p);
+      if (buf) DAR_BWD_MFMA(128, true);
+      else DAR_BWD_MFMA(128, false);
     }
+#undef DAR_BWD_MFMA
   } else if (p.d_k == 64) {
     DAR_BWD(false, 64);
   } else {
