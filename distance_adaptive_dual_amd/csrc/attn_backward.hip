@@ -786,12 +786,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
           // dV/dK operands of the first 16 queries (d_k 128: read before the
           // exponentials, so that their LDS latency hides under them)
           const int tb = lr * TP + 32 * sb + 8 * lg;
+          // (16-byte aligned: every term is a multiple of 8 halves; stated, or
+          // the reads below are split into 4-byte accesses that conflict)
+          const f16* gtb = (const f16*)__builtin_assume_aligned(sm.gt[bf] + tb, 16);
+          const f16* qtb = (const f16*)__builtin_assume_aligned(sm.qt[bf] + tb, 16);
           f16x8 ga[NB], qa[NB];
           if constexpr (WIDE) {
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              ga[db] = *(const f16x8*)(sm.gt[bf] + tb + 32 * db * TP);
-              qa[db] = *(const f16x8*)(sm.qt[bf] + tb + 32 * db * TP);
+              ga[db] = *(const f16x8*)(gtb + 32 * db * TP);
+              qa[db] = *(const f16x8*)(qtb + 32 * db * TP);
             }
           }
           f16x8 pb[2], dsb[2];
@@ -817,8 +821,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
             f16x8 gb[NB], qb[NB];
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              gb[db] = *(const f16x8*)(sm.gt[bf] + tb + 32 * db * TP + 16);
-              qb[db] = *(const f16x8*)(sm.qt[bf] + tb + 32 * db * TP + 16);
+              gb[db] = *(const f16x8*)(gtb + 32 * db * TP + 16);
+              qb[db] = *(const f16x8*)(qtb + 32 * db * TP + 16);
             }
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
