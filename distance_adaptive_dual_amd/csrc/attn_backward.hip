@@ -671,12 +671,14 @@ struct DkvSmem {
 
 // dK and dV of each source.  Workgroup: 128 keys of one (batch, head), a wave
 // per 32; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
-// and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps a key per lane; P = 2^(S sc2 - lse2);
-// dP = dO V^T; dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS.
+// and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps
+// a key per lane; P = 2^(S sc2 - lse2); dP = dO V^T; dS = P (dP - D);
+// dV^T += dO^T P; dK^T += Q^T dS.
 // The next block is staged in two halves of its head dims (all 64 queries
-// each, half a block of registers in flight; a wave's transposed stores then
-// cover 32 row pairs in two column groups 32 banks apart, without conflicts).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
-// the MFMA operands are also read ahead of their MFMAs; at d_k 64 the
+// each, so half a block of registers is in flight; a wave's transposed stores
+// then cover 32 row pairs in two column groups 32 banks apart, without
+// conflicts).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
+// the dV/dK operands are also read ahead of their MFMAs; at d_k 64 the
 // registers that takes spill.
 template <int D, bool BUF>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
