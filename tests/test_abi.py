@@ -39,14 +39,17 @@ def test_version_and_status_strings():
 F = dar._fake
 
 
-def project(**kw):
+PROJECT_ENTRIES = ("dar_project", "dar_project_sigmoid")  # same arguments and checks
+
+
+def project(entry="dar_project", **kw):
     a = dict(h=F(0), W_down=F(1), W_up=F(2), W_Q=F(3), W_K=F(4), W_V=F(5), W_upK=F(6),
              W_upV=F(7), B=2, N=128, d=256, d_down=64, heads=4, d_k=64, pos0=0, base=10000.0,
              dtype=1, Q=F(8), K_loc=F(9), V_loc=F(10), h_D=F(11), K_glob=F(12), V_glob=F(13),
              ws=None, wsb=0)
     a.update(kw)
     n = ctypes.c_size_t(a["wsb"])
-    st = dar.lib().dar_project(a["h"], a["W_down"], a["W_up"], a["W_Q"], a["W_K"], a["W_V"],
+    st = getattr(dar.lib(), entry)(a["h"], a["W_down"], a["W_up"], a["W_Q"], a["W_K"], a["W_V"],
                                a["W_upK"], a["W_upV"], a["B"], a["N"], a["d"], a["d_down"],
                                a["heads"], a["d_k"], a["pos0"], a["base"], a["dtype"], a["Q"],
                                a["K_loc"], a["V_loc"], a["h_D"], a["K_glob"], a["V_glob"],
@@ -54,13 +57,15 @@ def project(**kw):
     return st, n.value
 
 
-def test_project_size_query():
-    st, n = project()
+@pytest.mark.parametrize("entry", PROJECT_ENTRIES)
+def test_project_size_query(entry):
+    st, n = project(entry)
     assert st == OK and n > 0
-    st2, n2 = project(W_upK=None, W_upV=None)  # fold into the workspace
+    st2, n2 = project(entry, W_upK=None, W_upV=None)  # fold into the workspace
     assert st2 == OK and n2 > n
-    st3, n3 = project(N=4096)                  # longer RoPE table
+    st3, n3 = project(entry, N=4096)                  # longer RoPE table
     assert st3 == OK and n3 > n
+    assert (n, n2, n3) == (project()[1], project(W_upK=None, W_upV=None)[1], project(N=4096)[1])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -72,14 +77,16 @@ def test_project_size_query():
     (dict(W_upK=None, W_upV=None, W_up=None), INVALID),
     (dict(d_k=96), UNSUP), (dict(d=200), UNSUP), (dict(d_down=48), UNSUP),
 ])
-def test_project_rejects(kw, code):
-    assert project(**kw)[0] == code
+@pytest.mark.parametrize("entry", PROJECT_ENTRIES)
+def test_project_rejects(entry, kw, code):
+    assert project(entry, **kw)[0] == code
 
 
-def test_project_small_workspace():
-    st, n = project()
-    assert project(ws=F(20), wsb=n - 1)[0] == WS
-    assert project(ws=F(20) + 16, wsb=n)[0] == INVALID  # workspace must be 256-B aligned
+@pytest.mark.parametrize("entry", PROJECT_ENTRIES)
+def test_project_small_workspace(entry):
+    st, n = project(entry)
+    assert project(entry, ws=F(20), wsb=n - 1)[0] == WS
+    assert project(entry, ws=F(20) + 16, wsb=n)[0] == INVALID  # workspace must be 256-B aligned
 
 
 def attn(**kw):
