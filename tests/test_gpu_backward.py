@@ -82,6 +82,29 @@ def test_backward_bf16(B, H, N, d_k, w):
     _check(got, ref, "bf16", "bf16")
 
 
+def _sweep_cases(n=12, seed=4242):
+    """Seeded shapes around the staging boundaries of the MFMA kernels: N not a
+    multiple of the 32- or 64-row blocks or of the 128-key/query tiles,
+    windows 0, 1, random and >= N, both head widths, with and without lse."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for k in range(n):
+        N = int(g.integers(2, 600))
+        d_k = (64, 128)[k % 2]
+        w = (0, 1, int(g.integers(2, N + 10)), N + 100)[(k // 2) % 4]
+        out.append((int(g.integers(1, 3)), int(g.integers(1, 4)), N, d_k, w, bool(k % 3 == 0)))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d_k,w,use_lse", _sweep_cases())
+def test_backward_bf16_seeded_sweep(B, H, N, d_k, w, use_lse):
+    P, dO = _inputs(B, H, N, d_k, 7100 + N + w, "bf16")
+    log("backward sweep B%d H%d N%d dk%d w%d lse=%s" % (B, H, N, d_k, w, use_lse))
+    got = _gpu(P, dO, w, "bf16", use_lse=use_lse)
+    ref = oracle.attend_backward(P, w, dO)
+    _check(got, ref, "bf16", "sweep")
+
+
 @pytest.mark.parametrize("N,d_k,w", [(200, 64, 50), (150, 128, 40)])
 def test_backward_fp32(N, d_k, w):
     P, dO = _inputs(1, 2, N, d_k, 900 + N, "f32")

@@ -235,6 +235,29 @@ def test_attention_seeded(N, d_k, w):
     assert err <= TOL["bf16"]
 
 
+def _sweep_cases(n=12, seed=5151):
+    """Seeded shapes around the 64-key tiles and 128-query tiles (and the
+    zero rows the K staging reads past N): random N, windows 0, 1, random and
+    >= N, both head widths, 1-2 batches and 1-3 heads."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for k in range(n):
+        N = int(g.integers(1, 900))
+        w = (0, 1, int(g.integers(2, N + 10)), N + 50)[(k // 2) % 4]
+        out.append((int(g.integers(1, 3)), int(g.integers(1, 4)), N, (64, 128)[k % 2], w))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d_k,w", _sweep_cases())
+def test_attention_seeded_sweep(B, H, N, d_k, w):
+    P = _attn_inputs(B, H, N, d_k, seed=6100 + N + w)
+    got = _attn_gpu(P, w)
+    ref, _ = oracle.attend(P, w)
+    err = max_err(got, ref)
+    log("attn sweep B%d H%d N%d dk%d w%d max err %.3g" % (B, H, N, d_k, w, err))
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("N,d_k,w", [(700, 64, 100), (700, 128, 100), (300, 64, 0),
                                      (300, 128, 1), (2048, 128, 512), (513, 64, 700)])
 def test_selection_counts_exact(N, d_k, w):
