@@ -132,3 +132,22 @@ def test_lse_uniform_and_vanilla():
     s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
     want = torch.logsumexp(s, dim=-1).numpy()
     assert np.abs(oracle.attend_lse(P, N) - want).max() < 1e-12
+
+
+@pytest.mark.parametrize("w", [0, 1, 5, 39])
+def test_lse_window_edge_closed_form(w):
+    """Eq. 3's edge i - j < w in the normaliser.  q = e_0, local keys 0 (score
+    0), global keys with q.k = c sqrt(d_k) (score c): row i has min(i+1, w)
+    local pairs and max(0, i+1-w) global ones, so
+    lse_i = log(min(i+1, w) + max(0, i+1-w) e^c).  Taking i - j <= w instead
+    moves one pair per row from e^c to 1 and fails this."""
+    B, H, N, d_k, c = 1, 2, 40, 8, 1.5
+    Q = np.zeros((B, H, N, d_k))
+    Q[..., 0] = 1.0
+    KG = np.zeros((B, H, N, d_k))
+    KG[..., 0] = c * np.sqrt(d_k)
+    P = dict(Q=Q, KL=np.zeros((B, H, N, d_k)), KG=KG)
+    i = np.arange(N)
+    want = np.log(np.minimum(i + 1, w) + np.maximum(0, i + 1 - w) * np.exp(c))
+    got = oracle.attend_lse(P, w)
+    assert np.abs(got - want[None, None]).max() < 1e-13
