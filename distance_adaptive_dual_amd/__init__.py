@@ -15,6 +15,8 @@ equations' W in R^{in x out} transposed and made contiguous).
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +31,8 @@ EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
            "dar_attn_prefill", "dar_attn_prefill_lse", "dar_attn_prefill_backward",
            "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
-           "dar_attn_decode_varlen")
+           "dar_attn_decode_varlen", "dar_decode_append_sigmoid",
+           "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -80,6 +83,12 @@ def lib() -> ctypes.CDLL:
         L.dar_decode_append_varlen.restype = _I
         L.dar_decode_append_varlen.argtypes = [_P] * 5 + [_I] * 5 + [_P, _I, _I, ctypes.c_float,
                                                                    _I] + [_P] * 5 + [_SZ, _P]
+        L.dar_decode_append_sigmoid.restype = _I
+        L.dar_decode_append_sigmoid.argtypes = L.dar_decode_append.argtypes
+        L.dar_decode_append_varlen_sigmoid.restype = _I
+        L.dar_decode_append_varlen_sigmoid.argtypes = L.dar_decode_append_varlen.argtypes
+        L.dar_prefill_chunk_sigmoid.restype = _I
+        L.dar_prefill_chunk_sigmoid.argtypes = L.dar_prefill_chunk.argtypes
         L.dar_attn_decode_varlen.restype = _I
         L.dar_attn_decode_varlen.argtypes = [_P] * 6 + [_I, _P] + [_I] * 6 + [
             ctypes.c_float, _I, _P, _P, _SZ, _P]
@@ -119,6 +128,24 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
+def _on_stream(fn):
+    """Run a binding call on the caller's `stream`, if one is given: the
+    workspace and outputs it allocates, and the fills of fresh cache buffers,
+    then belong to the stream the library launches on, so the caching
+    allocator cannot hand their blocks out again while that stream still
+    uses them."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with _torch().cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return call
+
+
 def _check(fn: str, status: int):
     if status != 0:
         raise DarError(fn, status)
@@ -150,6 +177,7 @@ def _workspace(nbytes: int, like):
     return _torch().empty(max(nbytes, 256), dtype=torch_uint8(), device=like.device)
 
 
+@_on_stream
 def dar_fold(W_up, W_K, W_V, heads: int, d_k: int, W_upK=None, W_upV=None, stream=None):
     """W_upK = W_up W_K, W_upV = W_up W_V (column-major, [heads*d_k, d_down] tensors)."""
     torch = _torch()
@@ -182,6 +210,7 @@ def project_workspace_bytes(B, N, d, d_down, heads, d_k, pos0=0, folded=True, dt
     return n.value
 
 
+@_on_stream
 def dar_project(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, W_upK=None, W_upV=None,
                 pos0: int = 0, rope_base: float = 10000.0, out=None, workspace=None,
                 stream=None, sigmoid: bool = False):
@@ -219,6 +248,7 @@ def attn_backward_workspace_bytes(B, N, heads, d_k, dtype=DAR_BF16):
     return n.value
 
 
+@_on_stream
 def dar_attn_prefill_backward(Q, K_loc, V_loc, K_glob, V_glob, o, dO, w: int, lse=None,
                               out=None, workspace=None, stream=None):
     """Gradients of dar_attn_prefill for dL/do = dO.  Returns dict dQ, dK_loc,
@@ -238,6 +268,7 @@ def dar_attn_prefill_backward(Q, K_loc, V_loc, K_glob, V_glob, o, dO, w: int, ls
     return out
 
 
+@_on_stream
 def dar_attn_prefill_lse(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, lse=None,
                          stream=None):
     """dar_attn_prefill that also returns lse [B, heads, N] (float32, natural log)."""
@@ -255,6 +286,7 @@ def dar_attn_prefill_lse(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, lse=No
     return o, lse
 
 
+@_on_stream
 def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=None):
     """Eq. (4) with the Eq. (3) selection.  Returns o [B, N, heads*d_k]."""
     torch = _torch()
@@ -269,8 +301,10 @@ def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=Non
     return o
 
 
+@_on_stream
 def dar_decode_append(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos: int, q, K_win, V_win,
-                      h_D, rope_base: float = 10000.0, workspace=None, stream=None):
+                      h_D, rope_base: float = 10000.0, workspace=None, stream=None,
+                      sigmoid: bool = False):
     """Project the token at position `pos` of every sequence into the cache:
     q [B, heads, d_k] (RoPE'd), ring slot pos mod w of K_win / V_win, row pos
     of h_D.  h [B, d]; weights column-major.  Returns q."""
@@ -281,10 +315,12 @@ def dar_decode_append(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos: int, 
     args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), B, d, d_down, heads, d_k,
             int(pos), int(w), cap, float(rope_base), _dtype_code(h), _ptr(q),
             _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D)]
-    _call_ws("dar_decode_append", lib().dar_decode_append, args, workspace, h, stream)
+    name = "dar_decode_append_sigmoid" if sigmoid else "dar_decode_append"
+    _call_ws(name, getattr(lib(), name), args, workspace, h, stream)
     return q
 
 
+@_on_stream
 def dar_cache_from_prefill(h_D, K_loc, V_loc, w: int, cap: int = None, h_D_cache=None,
                            K_win=None, V_win=None, stream=None):
     """Decode cache of a prefilled prompt from dar_project's outputs (fp16):
@@ -319,6 +355,7 @@ def _lens(t, B: int):
     return _ptr(t)
 
 
+@_on_stream
 def dar_cache_from_prefill_varlen(h_D, K_loc, V_loc, lens, w: int, cap: int = None,
                                   h_D_cache=None, K_win=None, V_win=None, stream=None):
     """dar_cache_from_prefill for a padded batch whose sequence b has lens[b]
@@ -343,9 +380,10 @@ def dar_cache_from_prefill_varlen(h_D, K_loc, V_loc, lens, w: int, cap: int = No
     return h_D_cache, K_win, V_win
 
 
+@_on_stream
 def dar_decode_append_varlen(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos, q, K_win,
                              V_win, h_D, rope_base: float = 10000.0, workspace=None,
-                             stream=None):
+                             stream=None, sigmoid: bool = False):
     """dar_decode_append with sequence b's token at position pos[b] (device
     int32 [B]).  Returns q."""
     B, d = h.shape
@@ -355,11 +393,12 @@ def dar_decode_append_varlen(h, W_down, W_Q, W_K, W_V, heads: int, d_k: int, pos
     args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), B, d, d_down, heads, d_k,
             _lens(pos, B), int(w), cap, float(rope_base), _dtype_code(h), _ptr(q),
             _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D)]
-    _call_ws("dar_decode_append_varlen", lib().dar_decode_append_varlen, args, workspace, h,
-             stream)
+    name = "dar_decode_append_varlen_sigmoid" if sigmoid else "dar_decode_append_varlen"
+    _call_ws(name, getattr(lib(), name), args, workspace, h, stream)
     return q
 
 
+@_on_stream
 def dar_attn_decode_varlen(q, K_win, V_win, h_D, W_upK, W_upV, ctx_lens, max_ctx: int, w: int,
                            rope_base: float = 10000.0, o=None, workspace=None, stream=None):
     """dar_attn_decode with sequence b's query at position ctx_lens[b] - 1
@@ -386,9 +425,10 @@ def chunk_workspace_bytes(B, C, d, d_down, heads, d_k, p0, w, cap):
     return n.value
 
 
+@_on_stream
 def dar_prefill_chunk(h, W_down, W_Q, W_K, W_V, W_upK, W_upV, heads: int, d_k: int, p0: int,
                       h_D_cache, K_win, V_win, w: int, o=None, rope_base: float = 10000.0,
-                      workspace=None, stream=None):
+                      workspace=None, stream=None, sigmoid: bool = False):
     """Prefill the chunk h [B, C, d] at positions p0 .. p0+C-1 over the cache
     (h_D_cache [B, cap, d_down], ring K_win / V_win [B, heads, w, d_k], bf16;
     updated in place).  Returns o [B, C, heads*d_k]."""
@@ -402,7 +442,8 @@ def dar_prefill_chunk(h, W_down, W_Q, W_K, W_V, W_upK, W_upV, heads: int, d_k: i
             B, C, d, d_down, heads, d_k, int(p0), int(w), cap, float(rope_base), _dtype_code(h),
             _ptr(h_D_cache), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None,
             _ptr(o)]
-    _call_ws("dar_prefill_chunk", lib().dar_prefill_chunk, args, workspace, h, stream)
+    name = "dar_prefill_chunk_sigmoid" if sigmoid else "dar_prefill_chunk"
+    _call_ws(name, getattr(lib(), name), args, workspace, h, stream)
     return o
 
 
@@ -415,6 +456,7 @@ def decode_workspace_bytes(B, ctx_len, cap, heads, d_k, d_down, w, dtype=DAR_BF1
     return n.value
 
 
+@_on_stream
 def dar_attn_decode(q, K_win, V_win, h_D, W_upK, W_upV, ctx_len: int, w: int,
                     rope_base: float = 10000.0, o=None, workspace=None, stream=None):
     """One query per sequence at position ctx_len-1 over the mixed cache.  Returns o [B, heads*d_k]."""

@@ -161,3 +161,46 @@ def test_training_step_graph_replays_match_eager():
         # eager work of the program between replays
         dar.dar_attn_prefill(Q, KG, VG, KL, VL, w)
         torch.cuda.synchronize()
+
+
+def test_calls_on_a_side_stream_match_the_current_stream():
+    """Every binding call given `stream` allocates its outputs and workspace on
+    that stream and launches there: a prompt -> cache -> append -> decode
+    sequence issued on a side stream (while the current stream is kept busy)
+    gives exactly the bytes of the same sequence on the current stream."""
+    B, N, d, H, d_k, dd, w = 2, 300, 256, 4, 64, 64, 64
+    inp = prefill_case(B, N + 1, d, H, d_k, dd, "bf16", seed=808)
+    W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    h = dev(inp["h"], "bf16")
+
+    def sequence(stream):
+        Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k, stream=stream)
+        out = dar.dar_project(h[:, :N].contiguous(), W["W_down"], W["W_up"], W["W_Q"],
+                              W["W_K"], W["W_V"], H, d_k, W_upK=Wk, W_upV=Wv, stream=stream)
+        o = dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"],
+                                 out["V_glob"], w, stream=stream)
+        cache, K_win, V_win = dar.dar_cache_from_prefill(out["h_D"], out["K_loc"],
+                                                         out["V_loc"], w, cap=N + 1,
+                                                         stream=stream)
+        with torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(
+                torch.cuda.current_stream()):
+            q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
+        dar.dar_decode_append(h[:, N].contiguous(), W["W_down"], W["W_Q"], W["W_K"], W["W_V"],
+                              H, d_k, N, q, K_win, V_win, cache, stream=stream)
+        od = dar.dar_attn_decode(q, K_win, V_win, cache, Wk, Wv, N + 1, w, stream=stream)
+        return [o, od, cache, K_win, V_win]
+
+    ref = [t.clone() for t in sequence(None)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    busy = torch.randn(4096, 4096, device="cuda")
+    for _ in range(8):  # keep the current stream busy meanwhile
+        busy = busy @ busy
+        busy /= busy.norm()
+    got = sequence(side)
+    side.synchronize()
+    res = [t.clone() for t in got]
+    torch.cuda.synchronize()
+    for a, b in zip(ref, res):
+        assert torch.equal(a, b)
