@@ -1,8 +1,8 @@
 // Decode over the mixed cache.
 //
-// "Dual Dimensionality for Local and Global Attention": at inference every
-// past token contributes through exactly one path (the remark after Eq. (5)),
-// so the cache keeps full keys/values only for the w most recent positions and
+// "Dual Dimensionality for Local and Global Attention": at inference a past
+// token reaches a query through one source only, fixed by its distance (the
+// remark after Eq. (5)), so the cache keeps full keys/values only for the w most recent positions and
 // the d_down-wide latent h^D_j (Eq. 1) for every older position j.  For the
 // query at position p:
 //   j >  p - w : k_j, v_j read from the window ring (slot j mod w)

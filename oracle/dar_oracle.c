@@ -7,8 +7,8 @@
  * Source: "Dual Dimensionality for Local and Global Attention" (the DAR
  * paper), Eq. (1) bottleneck h^D = h W_down, Eq. (2) lift h' = h^D W_up,
  * Eq. (3) distance-selected keys and values, Eq. (4) softmax attention with
- * the 1/sqrt(d_k) scale.  Multi-head attention replicates the single-head
- * construction (same section of the paper, the paragraph after Eq. (1)).
+ * the 1/sqrt(d_k) scale.  The paper states one head; several heads apply
+ * that one-head form head by head (the paragraph before Eq. (2)).
  *
  * Readings taken where the paper is silent:
  *  - RoPE rotates both q_i (position i) and k_j (position j); rotate-half
