@@ -314,7 +314,7 @@ static dar_status decode_append_impl(const void* h, const void* W_down, const vo
                                      int heads, int d_k, int pos, const int* pos_arr, int w,
                                      int cap, float rope_base, dar_dtype dtype, void* q,
                                      void* K_win, void* V_win, void* h_D, void* workspace,
-                                     size_t* workspace_bytes, hipStream_t stream) {
+                                     size_t* workspace_bytes, hipStream_t stream, int act) {
   if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
   if (B < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || pos < 0 || w < 0 ||
       cap < 1)
@@ -381,7 +381,8 @@ static dar_status decode_append_impl(const void* h, const void* W_down, const vo
     g.seg[ns++] = GemmSeg{W_K, K_win, hd, kHead, 1, w, pos % w, kPosRing};
     g.seg[ns++] = GemmSeg{W_V, V_win, hd, kHead, 0, w, pos % w, kPosRing};
   }
-  g.seg[ns++] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos, kPosRow};
+  g.seg[ns] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos, kPosRow};
+  g.seg[ns++].act = act;
   g.nseg = ns;
   return hip_status(launch_project_gemm(g, dtype, stream));
 }
@@ -393,7 +394,18 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
                              size_t* workspace_bytes, hipStream_t stream) {
   return decode_append_impl(h, W_down, W_Q, W_K, W_V, B, d, d_down, heads, d_k, pos, nullptr, w,
                             cap, rope_base, dtype, q, K_win, V_win, h_D, workspace,
-                            workspace_bytes, stream);
+                            workspace_bytes, stream, 0);
+}
+
+dar_status dar_decode_append_sigmoid(const void* h, const void* W_down, const void* W_Q,
+                                     const void* W_K, const void* W_V, int B, int d, int d_down,
+                                     int heads, int d_k, int pos, int w, int cap, float rope_base,
+                                     dar_dtype dtype, void* q, void* K_win, void* V_win, void* h_D,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream) {
+  return decode_append_impl(h, W_down, W_Q, W_K, W_V, B, d, d_down, heads, d_k, pos, nullptr, w,
+                            cap, rope_base, dtype, q, K_win, V_win, h_D, workspace,
+                            workspace_bytes, stream, 1);
 }
 
 dar_status dar_decode_append_varlen(const void* h, const void* W_down, const void* W_Q,
@@ -405,7 +417,19 @@ dar_status dar_decode_append_varlen(const void* h, const void* W_down, const voi
   if (pos == nullptr) return DAR_ERR_INVALID_ARG;
   return decode_append_impl(h, W_down, W_Q, W_K, W_V, B, d, d_down, heads, d_k, 0, pos, w, cap,
                             rope_base, dtype, q, K_win, V_win, h_D, workspace, workspace_bytes,
-                            stream);
+                            stream, 0);
+}
+
+dar_status dar_decode_append_varlen_sigmoid(const void* h, const void* W_down, const void* W_Q,
+                                            const void* W_K, const void* W_V, int B, int d,
+                                            int d_down, int heads, int d_k, const int* pos, int w,
+                                            int cap, float rope_base, dar_dtype dtype, void* q,
+                                            void* K_win, void* V_win, void* h_D, void* workspace,
+                                            size_t* workspace_bytes, hipStream_t stream) {
+  if (pos == nullptr) return DAR_ERR_INVALID_ARG;
+  return decode_append_impl(h, W_down, W_Q, W_K, W_V, B, d, d_down, heads, d_k, 0, pos, w, cap,
+                            rope_base, dtype, q, K_win, V_win, h_D, workspace, workspace_bytes,
+                            stream, 1);
 }
 
 static dar_status cache_from_prefill_impl(const void* h_D, const void* K_loc, const void* V_loc,
@@ -453,12 +477,13 @@ dar_status dar_cache_from_prefill_varlen(const void* h_D, const void* K_loc, con
                                  dtype, h_D_cache, K_win, V_win, stream);
 }
 
-dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q, const void* W_K,
-                             const void* W_V, const void* W_upK, const void* W_upV, int B, int C,
-                             int d, int d_down, int heads, int d_k, int p0, int w, int cap,
-                             float rope_base, dar_dtype dtype, void* h_D_cache, void* K_win,
-                             void* V_win, void* o, void* workspace, size_t* workspace_bytes,
-                             hipStream_t stream) {
+static dar_status prefill_chunk_impl(const void* h, const void* W_down, const void* W_Q,
+                                     const void* W_K, const void* W_V, const void* W_upK,
+                                     const void* W_upV, int B, int C, int d, int d_down, int heads,
+                                     int d_k, int p0, int w, int cap, float rope_base,
+                                     dar_dtype dtype, void* h_D_cache, void* K_win, void* V_win,
+                                     void* o, void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream, int act) {
   if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
   if (B < 1 || C < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || p0 < 0 ||
       w < 0 || cap < 1 || (long)p0 + C > cap || !(rope_base > 1.f) || workspace_bytes == nullptr)
@@ -545,7 +570,8 @@ dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q,
     g1.seg[ns++] = GemmSeg{W_K, Kl, (int)hd, kHead, 1, nloc, p0 - loc0};
     g1.seg[ns++] = GemmSeg{W_V, Vl, (int)hd, kHeadT, 0, nloc, p0 - loc0};
   }
-  g1.seg[ns++] = GemmSeg{W_down, hDc, d_down, kRowMajor, 0};
+  g1.seg[ns] = GemmSeg{W_down, hDc, d_down, kRowMajor, 0};
+  g1.seg[ns++].act = act;
   g1.nseg = ns;
   e = launch_project_gemm(g1, dtype, stream);
   if (e == hipSuccess) e = launch_latent_cast(hDc, B, C, d_down, cap, p0, h_D_cache, stream);
@@ -612,6 +638,29 @@ dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q,
   if (e == hipSuccess)
     e = launch_ring_fill(Kl, Vl, B, heads, d_k, N, loc0, w, K_win, V_win, stream);
   return hip_status(e);
+}
+
+dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q, const void* W_K,
+                             const void* W_V, const void* W_upK, const void* W_upV, int B, int C,
+                             int d, int d_down, int heads, int d_k, int p0, int w, int cap,
+                             float rope_base, dar_dtype dtype, void* h_D_cache, void* K_win,
+                             void* V_win, void* o, void* workspace, size_t* workspace_bytes,
+                             hipStream_t stream) {
+  return prefill_chunk_impl(h, W_down, W_Q, W_K, W_V, W_upK, W_upV, B, C, d, d_down, heads, d_k,
+                            p0, w, cap, rope_base, dtype, h_D_cache, K_win, V_win, o, workspace,
+                            workspace_bytes, stream, 0);
+}
+
+dar_status dar_prefill_chunk_sigmoid(const void* h, const void* W_down, const void* W_Q,
+                                     const void* W_K, const void* W_V, const void* W_upK,
+                                     const void* W_upV, int B, int C, int d, int d_down, int heads,
+                                     int d_k, int p0, int w, int cap, float rope_base,
+                                     dar_dtype dtype, void* h_D_cache, void* K_win, void* V_win,
+                                     void* o, void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream) {
+  return prefill_chunk_impl(h, W_down, W_Q, W_K, W_V, W_upK, W_upV, B, C, d, d_down, heads, d_k,
+                            p0, w, cap, rope_base, dtype, h_D_cache, K_win, V_win, o, workspace,
+                            workspace_bytes, stream, 1);
 }
 
 static dar_status attn_decode_impl(const void* q, const void* K_win, const void* V_win,

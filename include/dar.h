@@ -8,8 +8,8 @@
  *   Eq. (3)  k_j = RoPE(h_j W_K), v_j = h_j W_V     if i - j <  w   (local path)
  *            k_j = RoPE(h'_j W_K), v_j = h'_j W_V   otherwise       (global path)
  *   Eq. (4)  o_i = softmax(q_i K_i^T / sqrt(d_k)) V_i, q_i = h_i W_Q, causal j <= i
- * Multi-head attention replicates the construction per head (the paragraph
- * after Eq. (1)); one W_down / W_up is shared by all heads.
+ * The paper writes one head; several heads apply the one-head form head by
+ * head (the paragraph before Eq. (2)); one W_down / W_up serves all heads.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -28,8 +28,12 @@
  *    bfloat16.  The six prefill intermediates that dar_project hands to
  *    dar_attn_prefill (Q, K_loc, V_loc, h_D, K_glob, V_glob) are IEEE fp16:
  *    same size and MFMA rate, 3 more mantissa bits, which keeps the
- *    end-to-end error several times inside 2e-2; their magnitude must stay
- *    below 65504 (not checked).  Arithmetic is MFMA with fp32 accumulation,
+ *    end-to-end error several times inside 2e-2.  Their range is fp16's:
+ *    an intermediate element of magnitude >= 65520 is stored as +-inf
+ *    (round to nearest even), and the attention rows that read it come out
+ *    inf or NaN; no status reports it, since the values exist only on the
+ *    device.  Magnitudes up to 65504 are exact to fp16 rounding.  (The
+ *    fp32 mode has no such limit.)  Arithmetic is MFMA with fp32 accumulation,
  *    softmax in fp32.  DAR_FP32: every float tensor is float32 and every
  *    step is computed in fp32 (no 16-bit rounding anywhere).
  *  - Positions are 0-based: token n of a prefill sits at position pos0 + n.
@@ -122,9 +126,11 @@ dar_status dar_project(const void* h, const void* W_down, const void* W_up, cons
  *   K_glob, V_glob              from that h^D through the same folded weights
  * elementwise, in fp32, before h^D is rounded to its storage type.  Q, K_loc
  * and V_loc are those of dar_project.  Arguments, layouts, workspace and
- * errors are those of dar_project.  The decode-side entry points compute the
- * linear h^D; a model with this variant builds its cache from this call's
- * h_D (dar_cache_from_prefill).
+ * errors are those of dar_project.  A model with this variant builds its
+ * decode cache from this call's h_D (dar_cache_from_prefill) and extends it
+ * with the *_sigmoid forms of dar_decode_append(_varlen) and
+ * dar_prefill_chunk, which store sigma(h W_down) as the latent row; the
+ * decode attention itself (dar_attn_decode) reads whatever latent is stored.
  */
 dar_status dar_project_sigmoid(const void* h, const void* W_down, const void* W_up,
                                const void* W_Q, const void* W_K, const void* W_V,
@@ -218,6 +224,20 @@ dar_status dar_decode_append(const void* h, const void* W_down, const void* W_Q,
                              size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * dar_decode_append_sigmoid -- dar_decode_append for the sigmoid-bottleneck
+ * variant (the paragraph after Eq. (1)): the latent row written at `pos` is
+ * sigma(h W_down), sigma(x) = 1 / (1 + e^-x), in fp32 before its bf16
+ * rounding.  q and the ring slot are those of dar_decode_append; arguments,
+ * workspace and errors likewise.
+ */
+dar_status dar_decode_append_sigmoid(const void* h, const void* W_down, const void* W_Q,
+                                     const void* W_K, const void* W_V, int B, int d, int d_down,
+                                     int heads, int d_k, int pos, int w, int cap, float rope_base,
+                                     dar_dtype dtype, void* q, void* K_win, void* V_win, void* h_D,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream);
+
+/*
  * dar_prefill_chunk -- prefill the next C tokens of every sequence over the
  * mixed cache, and extend the cache.
  *
@@ -248,6 +268,21 @@ dar_status dar_prefill_chunk(const void* h, const void* W_down, const void* W_Q,
                              float rope_base, dar_dtype dtype, void* h_D_cache, void* K_win,
                              void* V_win, void* o, void* workspace, size_t* workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * dar_prefill_chunk_sigmoid -- dar_prefill_chunk for the sigmoid-bottleneck
+ * variant (the paragraph after Eq. (1)): the chunk's latents are
+ * sigma(h W_down) (fp32, then stored), both in the latent cache and as the
+ * source of the chunk's global keys and values; the prefix's latents are read
+ * from the cache as stored.  Everything else is dar_prefill_chunk's.
+ */
+dar_status dar_prefill_chunk_sigmoid(const void* h, const void* W_down, const void* W_Q,
+                                     const void* W_K, const void* W_V, const void* W_upK,
+                                     const void* W_upV, int B, int C, int d, int d_down, int heads,
+                                     int d_k, int p0, int w, int cap, float rope_base,
+                                     dar_dtype dtype, void* h_D_cache, void* K_win, void* V_win,
+                                     void* o, void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream);
 
 /*
  * dar_cache_from_prefill -- the decode cache of a prefilled prompt.
@@ -308,6 +343,14 @@ dar_status dar_decode_append_varlen(const void* h, const void* W_down, const voi
                                     float rope_base, dar_dtype dtype, void* q, void* K_win,
                                     void* V_win, void* h_D, void* workspace,
                                     size_t* workspace_bytes, hipStream_t stream);
+/* dar_decode_append_varlen_sigmoid -- the ragged append of the sigmoid
+ * variant: latent row pos[b] <- sigma(h_b W_down) (as dar_decode_append_sigmoid). */
+dar_status dar_decode_append_varlen_sigmoid(const void* h, const void* W_down, const void* W_Q,
+                                            const void* W_K, const void* W_V, int B, int d,
+                                            int d_down, int heads, int d_k, const int* pos, int w,
+                                            int cap, float rope_base, dar_dtype dtype, void* q,
+                                            void* K_win, void* V_win, void* h_D, void* workspace,
+                                            size_t* workspace_bytes, hipStream_t stream);
 dar_status dar_attn_decode_varlen(const void* q, const void* K_win, const void* V_win,
                                   const void* h_D, const void* W_upK, const void* W_upV, int B,
                                   const int* ctx_lens, int max_ctx, int cap, int heads, int d_k,
@@ -317,9 +360,10 @@ dar_status dar_attn_decode_varlen(const void* q, const void* K_win, const void* 
 /*
  * dar_attn_decode -- one new query per sequence over the mixed cache.
  *
- * The inference remarks of the paper note that each past token contributes
- * through exactly one path, so a decode cache only needs full keys/values for
- * the w most recent positions and the d_down-wide latent h^D beyond them.
+ * At inference a past token is seen by a query through one source only,
+ * chosen by its distance (the remark after Eq. (5)), so a decode cache needs
+ * full keys/values for the w most recent positions and the d_down-wide latent
+ * h^D for older ones.
  * The query sits at position p = ctx_len - 1 (its own key/value already in
  * the window).
  *   q      [B, heads, d_k]          RoPE'd at p
