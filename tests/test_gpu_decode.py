@@ -78,21 +78,52 @@ def test_decode_matches_prefill_row():
     assert err <= TOL["bf16"]
 
 
-def test_long_context_decode_sampled():
-    """B16, ctx 32768, d2048, 16 heads of 128, w512, d_down 256: the full-size
-    launch, checked for two (batch, head) pairs (the oracle rebuilds every
-    global key of that batch and head in fp64)."""
-    B, ctx, d, H, d_k, dd, w = 16, 32768, 2048, 16, 128, 256, 512
-    inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=5000)
-    got = run_decode(inp, ctx, w, H, d_k)
-    for b, hh in [(0, 0), (13, 11)]:
+def _long_decode_check(inp, got, pairs, ctx, w, d_k, label):
+    for b, hh in pairs:
         ref = oracle.decode(inp["q"][b:b + 1], inp["K_win"][b:b + 1], inp["V_win"][b:b + 1],
                             inp["h_D"][b:b + 1], inp["W_up"], inp["W_K"], inp["W_V"], ctx, w,
                             heads=(hh, hh + 1))
         sl = slice(hh * d_k, (hh + 1) * d_k)
         err = max_err(got[b, sl], ref[0, sl])
-        log("  long decode b%d h%d max err %.3g" % (b, hh, err))
+        log("  %s b%d h%d max err %.3g (max |o| %.3g)" % (label, b, hh, err,
+                                                          np.abs(ref[0, sl]).max()))
         assert err <= TOL["bf16"]
+
+
+LONG = dict(B=16, ctx=32768, d=2048, H=16, d_k=128, dd=256, w=512)
+
+
+def test_long_context_decode_planted():
+    """B16, ctx 32768, d2048, 16 heads of 128, w512, d_down 256: the full-size
+    launch on a cache where, for one head of every even batch, latent rows
+    (at both sides of the 2016-token chunk edges, the first and the last
+    global position) and window slots (oldest, middle, the query's own) carry
+    keys aligned with the query, so o is of order 1 and depends on every
+    part of the cache (tests/test_planted_decode_bites.py shows the
+    mistakes this exposes on the CPU).  8 (batch, head) pairs, all heads
+    distinct."""
+    import planted
+    from test_planted_decode_bites import planted_positions
+    c = LONG
+    inp = di.decode_inputs(c["B"], c["ctx"], c["d"], c["H"], c["d_k"], c["dd"], c["w"],
+                           seed0=5000)
+    pairs = [(b, (5 * b + 3) % 16) for b in range(0, 16, 2)]
+    inp = planted.plant(inp, c["ctx"], c["w"], c["d_k"], pairs,
+                        *planted_positions(c["ctx"], c["w"]))
+    got = run_decode(inp, c["ctx"], c["w"], c["H"], c["d_k"])
+    _long_decode_check(inp, got, pairs, c["ctx"], c["w"], c["d_k"], "planted decode")
+
+
+def test_long_context_decode_gaussian():
+    """The same launch on the workload's Gaussian cache (softmax spread over
+    thousands of keys, |o| ~ 0.02): one head of every odd batch, so the two
+    tests together cover every batch and every head."""
+    c = LONG
+    inp = di.decode_inputs(c["B"], c["ctx"], c["d"], c["H"], c["d_k"], c["dd"], c["w"],
+                           seed0=5000)
+    got = run_decode(inp, c["ctx"], c["w"], c["H"], c["d_k"])
+    pairs = [(b, (5 * b + 3) % 16) for b in range(1, 16, 2)]
+    _long_decode_check(inp, got, pairs, c["ctx"], c["w"], c["d_k"], "gaussian decode")
 
 
 def test_decode_deterministic():
