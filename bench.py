@@ -2,11 +2,13 @@
 
 A step is one prefill pass of the layer (dar_project + dar_attn_prefill, the
 folded weights prepared once beforehand) over one batch of synthetic input
-already resident in HBM.  Default workload: the Pythia-70M-shaped layer
-(batch 8, N 2048, d 512, 8 heads of 64, w 128, d_down 128, bf16).  The same
-run also times the long-context decode step (batch 16, context 32768, d 2048,
-16 heads of 128, w 512, d_down 256) and the d_down sweep, and times the fp64
-oracle on a bounded sample on the host cores (a reported baseline).
+already resident in HBM.  Headline workload: the 1B-scale layer (batch 4,
+N 8192, d 2048, 16 heads of 128, w 512, d_down 512, bf16), the largest
+prefill configuration.  The same run also times the Pythia-70M- and
+410M-shaped layers, the d_down sweep, chunked prefill, the attention backward
+and the long-context decode step (batch 16, context 32768, d 2048, 16 heads
+of 128, w 512, d_down 256), and times the fp64 oracle on a bounded sample of
+the headline workload on the host cores (a reported baseline).
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -239,23 +241,51 @@ def time_chunked(torch, dar, di, cfg, chunk, reps):
     return {"ms": ms, "TFLOP/s": flops / ms / 1e9, "chunks": N // chunk, "chunk": chunk}
 
 
-def cpu_baseline(oracle, inp, H, d_k, w, d_down, budget_s=10.0):
-    """The fp64 oracle on the step's own input (all sequences, all heads),
-    repeated until about budget_s seconds of host time have passed."""
-    B, N, d = inp["h"].shape
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sample_flops(N, d, d_down, nh, d_k):
+    """Algorithmic FLOP of one sequence restricted to nh heads, counted as the
+    GPU metric counts a whole step: the shared latent h W_down, the nh heads'
+    columns of W_Q, W_K, W_V and of the folded W_upK, W_upV, and their causal
+    attention."""
+    hd = nh * d_k
+    return 2.0 * N * (d * d_down + 3 * d * hd + 2 * d_down * hd) + 2.0 * hd * N * (N + 1)
+
+
+def cpu_baseline(oracle, inp, H, d_k, w, budget_s=10.0, heads=2):
+    """The fp64 oracle on a bounded sample of the step's own input: sequence 0
+    in full (all N positions), its first `heads` heads (projections, then the
+    attention of Eqs. 3-4), repeated until about budget_s seconds of host
+    time have passed."""
+    h1 = inp["h"][:1]
+    _, N, d = h1.shape
+    d_down = inp["W_down"].shape[1]
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.prefill(inp, H, d_k, w)
+        P = oracle.project(h1, inp["W_down"], inp["W_up"], inp["W_Q"], inp["W_K"], inp["W_V"],
+                           H, d_k, heads=(0, heads))
+        S = {k: np.ascontiguousarray(P[k][:, :heads]) for k in ("Q", "KL", "VL", "KG", "VG")}
+        oracle.attend(S, w)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= budget_s:
             break
-    proj, attn = prefill_flops(B, N, d, d_down)
-    return {"value": reps * (proj + attn) / dt / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.threads(), "kind": "oracle", "seconds": dt,
-            "sample": "the whole step (%d sequences of N %d, %d heads, projections + "
-                      "attention) in fp64, %d times; same algorithmic FLOP count as the GPU "
-                      "metric" % (B, N, H, reps)}
+    f = sample_flops(N, d, d_down, heads, d_k)
+    return {"value": reps * f / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.threads(), "cpu_model": cpu_model(), "kind": "oracle",
+            "seconds": dt,
+            "sample": "sequence 0 of the headline batch (N %d, d %d), heads 0..%d of %d: "
+                      "projections (incl. the shared h W_down) and causal attention in fp64, "
+                      "%d times; algorithmic FLOP of that sample counted as the GPU metric "
+                      "counts a step" % (N, d, heads - 1, H, reps)}
 
 
 def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
@@ -443,41 +473,61 @@ def main():
            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
 
-    B, N, d, H, d_k, w, d_down = 8, 2048, 512, 8, 64, 128, 128
     if args.only in ("all", "prefill"):
-        log("prefill: building inputs")
-        inp, s = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=2000 + d_down)
+        # headline: the 1B-scale layer
+        B, N, d, H, d_k, w, d_down = 4, 8192, 2048, 16, 128, 512, 512
+        log("prefill 1b layer: building inputs")
+        inp, s = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=4000)
         ms, ev_ms, proj_ms, attn_ms = time_prefill(torch, dar, s, H, d_k, w, args.steps,
                                                    args.warmup)
         proj_f, attn_f = prefill_flops(B, N, d, d_down)
         tflops = (proj_f + attn_f) / ms / 1e9
-        log("prefill: %.3f ms/step, %.1f TFLOP/s (proj %.3f ms, attn %.3f ms)"
+        log("prefill 1b: %.3f ms/step, %.1f TFLOP/s (proj %.3f ms, attn %.3f ms)"
             % (ms, tflops, proj_ms, attn_ms))
         res.update(value=tflops, ms_per_step=ms)
         res["gpu_ms_per_step"] = ev_ms
-        res["config"] = {"workload": "pythia70m-layer prefill B%d N%d d%d H%d dk%d w%d d_down%d"
+        res["config"] = {"workload": "1b-layer prefill B%d N%d d%d H%d dk%d w%d d_down%d"
                          % (B, N, d, H, d_k, w, d_down), "global_batch": B, "seq_len": N,
                          "parallelism": "none (1 GPU)"}
         res["mfma_frac"] = tflops / PEAK_BF16_TFLOPS
         res["kernels"] = {"dar_project_ms": proj_ms, "dar_project_TFLOP/s": proj_f / proj_ms / 1e9,
                           "dar_attn_prefill_ms": attn_ms,
                           "dar_attn_prefill_TFLOP/s": attn_f / attn_ms / 1e9}
-        # The fused attention kernel is the only launch of dar_attn_prefill:
-        # events around a graph of back-to-back calls time that kernel.
+        # The fused attention kernel is the only launch of dar_attn_prefill and
+        # the largest kernel of the step: HIP events on its launch stream around
+        # a graph of back-to-back calls time that kernel.
         achieved = attn_f / attn_ms / 1e9
-        res["roofline"] = {"kernel": "attn_prefill_f16<64>", "bound": "mfma",
+        res["roofline"] = {"kernel": "attn_prefill_f16<128>", "bound": "mfma",
                            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,
-                           "traffic": recorded_traffic("attn_prefill_f16<64>@pythia70m",
+                           "traffic": recorded_traffic("attn_prefill_f16<128>@1b",
                                                        ["attn_prefill.hip", "dar_common.hpp"]),
                            "flops_per_launch": attn_f, "launch_ms": attn_ms,
                            "peak_measured": cal["mfma_f16_tflops"],
                            "frac_measured": achieved / cal["mfma_f16_tflops"]}
         if not args.no_cpu:
             import oracle
-            log("cpu baseline: oracle on one sequence")
-            res["cpu_baseline"] = cpu_baseline(oracle, inp, H, d_k, w, d_down)
+            log("cpu baseline: the oracle on sequence 0, two heads, of the headline input")
+            res["cpu_baseline"] = cpu_baseline(oracle, inp, H, d_k, w)
         del s, inp
+        torch.cuda.empty_cache()
+        # the Pythia-70M-shaped layer (d_down 128), with its own roofline line
+        B, N, d, H, d_k, w, d_down = 8, 2048, 512, 8, 64, 128, 128
+        _, s = make_prefill(torch, dar, di, B, N, d, H, d_k, d_down, seed=2000 + d_down)
+        ms2, _, p2, a2 = time_prefill(torch, dar, s, H, d_k, w, args.steps, args.warmup)
+        pf, af = prefill_flops(B, N, d, d_down)
+        res["pythia70m"] = {"workload": "pythia70m-layer prefill B8 N2048 d512 H8 dk64 w128 "
+                                        "d_down128", "ms": ms2,
+                            "TFLOP/s": (pf + af) / ms2 / 1e9, "proj_ms": p2, "attn_ms": a2,
+                            "roofline": {"kernel": "attn_prefill_f16<64>", "bound": "mfma",
+                                         "achieved": af / a2 / 1e9, "peak": PEAK_BF16_TFLOPS,
+                                         "unit": "TFLOP/s",
+                                         "frac": af / a2 / 1e9 / PEAK_BF16_TFLOPS,
+                                         "traffic": recorded_traffic(
+                                             "attn_prefill_f16<64>@pythia70m",
+                                             ["attn_prefill.hip", "dar_common.hpp"])}}
+        log("pythia70m: %.3f ms, %.1f TFLOP/s" % (ms2, (pf + af) / ms2 / 1e9))
+        del s
         if not args.no_sweep:
             sweep = {}
             for dd in (256, 64):
@@ -485,7 +535,7 @@ def main():
                 ms2, _, p2, a2 = time_prefill(torch, dar, s2, H, d_k, w, args.steps,
                                               args.warmup)
                 pf, af = prefill_flops(B, N, d, dd)
-                sweep["d_down%d" % dd] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9}
+                sweep["pythia70m d_down%d" % dd] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9}
                 del s2
             # the sigmoid-bottleneck variant on the same workload (the sigmoid is
             # B N d_down exponentials in the projection epilogue; FLOP count as above)
@@ -493,23 +543,20 @@ def main():
             s2["sigmoid"] = True
             ms2, _, p2, a2 = time_prefill(torch, dar, s2, H, d_k, w, args.steps, args.warmup)
             pf, af = prefill_flops(B, N, d, d_down)
-            sweep["sigmoid d_down%d" % d_down] = {"ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9,
-                                                 "proj_ms": p2, "attn_ms": a2}
+            sweep["pythia70m sigmoid d_down%d" % d_down] = {
+                "ms": ms2, "TFLOP/s": (pf + af) / ms2 / 1e9, "proj_ms": p2, "attn_ms": a2}
             del s2
-            for name, cfg in (("pythia410m B8 N2048 d1024 H16 dk64 w128 d_down256",
-                               (8, 2048, 1024, 16, 64, 128, 256)),
-                              ("1b B4 N8192 d2048 H16 dk128 w512 d_down512",
-                               (4, 8192, 2048, 16, 128, 512, 512))):
-                b_, n_, d_, h_, k_, w_, dd_ = cfg
-                _, s3 = make_prefill(torch, dar, di, b_, n_, d_, h_, k_, dd_, seed=3000)
-                ms3, _, p3, a3 = time_prefill(torch, dar, s3, h_, k_, w_,
-                                              max(3, args.steps // 4), 2)
-                pf, af = prefill_flops(b_, n_, d_, dd_)
-                sweep[name] = {"ms": ms3, "TFLOP/s": (pf + af) / ms3 / 1e9,
-                               "proj_ms": p3, "attn_ms": a3,
-                               "attn_TFLOP/s": af / a3 / 1e9, "proj_TFLOP/s": pf / p3 / 1e9}
-                log("%s: %.3f ms, %.1f TFLOP/s" % (name, ms3, (pf + af) / ms3 / 1e9))
-                del s3
+            name, cfg = ("pythia410m B8 N2048 d1024 H16 dk64 w128 d_down256",
+                         (8, 2048, 1024, 16, 64, 128, 256))
+            b_, n_, d_, h_, k_, w_, dd_ = cfg
+            _, s3 = make_prefill(torch, dar, di, b_, n_, d_, h_, k_, dd_, seed=3000)
+            ms3, _, p3, a3 = time_prefill(torch, dar, s3, h_, k_, w_, max(3, args.steps // 2), 2)
+            pf, af = prefill_flops(b_, n_, d_, dd_)
+            sweep[name] = {"ms": ms3, "TFLOP/s": (pf + af) / ms3 / 1e9,
+                           "proj_ms": p3, "attn_ms": a3,
+                           "attn_TFLOP/s": af / a3 / 1e9, "proj_TFLOP/s": pf / p3 / 1e9}
+            log("%s: %.3f ms, %.1f TFLOP/s" % (name, ms3, (pf + af) / ms3 / 1e9))
+            del s3
             res["sweep"] = sweep
             cfg1b = (4, 8192, 2048, 16, 128, 512, 512)
             ch = time_chunked(torch, dar, di, cfg1b, 2048, max(2, args.steps // 8))
@@ -518,7 +565,7 @@ def main():
             log("chunked prefill: %.3f ms, %.1f TFLOP/s" % (ch["ms"], ch["TFLOP/s"]))
         torch.cuda.empty_cache()
     if args.only in ("all", "backward") and not args.no_sweep:
-        bw = time_backward(torch, dar, di, (B, N, H, d_k, w), 2)
+        bw = time_backward(torch, dar, di, (8, 2048, 8, 64, 128), 2)
         res["backward"] = bw
         log("backward: %.3f ms, %.1f TFLOP/s" % (bw["ms"], bw["TFLOP/s"]))
         bw1 = time_backward(torch, dar, di, (4, 8192, 16, 128, 512), 1)
