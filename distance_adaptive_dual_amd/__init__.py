@@ -32,7 +32,8 @@ EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
            "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
            "dar_attn_decode_varlen", "dar_decode_append_sigmoid",
-           "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid")
+           "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid",
+           "dar_attn_decode_noalloc")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.dar_decode_append_varlen_sigmoid.argtypes = L.dar_decode_append_varlen.argtypes
         L.dar_prefill_chunk_sigmoid.restype = _I
         L.dar_prefill_chunk_sigmoid.argtypes = L.dar_prefill_chunk.argtypes
+        L.dar_attn_decode_noalloc.restype = _I
+        L.dar_attn_decode_noalloc.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P]
         L.dar_attn_decode_varlen.restype = _I
         L.dar_attn_decode_varlen.argtypes = [_P] * 6 + [_I, _P] + [_I] * 6 + [
             ctypes.c_float, _I, _P, _P, _SZ, _P]
@@ -469,4 +472,20 @@ def dar_attn_decode(q, K_win, V_win, h_D, W_upK, W_upV, ctx_len: int, w: int,
             _ptr(W_upK), _ptr(W_upV), B, int(ctx_len), cap, H, d_k, d_down, int(w),
             float(rope_base), _dtype_code(q), _ptr(o)]
     _call_ws("dar_attn_decode", lib().dar_attn_decode, args, workspace, q, stream)
+    return o
+
+
+@_on_stream
+def dar_attn_decode_noalloc(q, K_win, V_win, h_D, W_upK, W_upV, ctx_len: int, w: int, o,
+                            rope_base: float = 10000.0, stream=None):
+    """dar_attn_decode without a workspace: the library's static per-GPU
+    scratch array serves as one (calls on one GPU must not overlap).  The
+    output o [B, heads*d_k] must be given: nothing is allocated.  Returns o."""
+    B, H, d_k = q.shape
+    cap, d_down = h_D.shape[1], h_D.shape[2]
+    st = lib().dar_attn_decode_noalloc(
+        _ptr(q), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _ptr(h_D),
+        _ptr(W_upK), _ptr(W_upV), B, int(ctx_len), cap, H, d_k, d_down, int(w),
+        float(rope_base), _dtype_code(q), _ptr(o), _stream(stream))
+    _check("dar_attn_decode_noalloc", st)
     return o

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "dar_common.hpp"
 
@@ -742,6 +743,52 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
                            hipStream_t stream) {
   return attn_decode_impl(q, K_win, V_win, h_D, W_upK, W_upV, B, ctx_len, nullptr, cap, heads,
                           d_k, d_down, w, rope_base, dtype, o, workspace, workspace_bytes, stream);
+}
+
+// Allocation-free decode: the workspace of dar_attn_decode (RoPE tables and
+// per-chunk partials) lives in a file-scope device array, one per GPU, held
+// until the process ends.  The host never passes the array's name to a
+// kernel: its device address is looked up once per device with
+// hipGetSymbolAddress and kept here.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+static hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+dar_status dar_attn_decode_noalloc(const void* q, const void* K_win, const void* V_win,
+                                   const void* h_D, const void* W_upK, const void* W_upV, int B,
+                                   int ctx_len, int cap, int heads, int d_k, int d_down, int w,
+                                   float rope_base, dar_dtype dtype, void* o,
+                                   hipStream_t stream) {
+  // validation and the workspace size, without touching the device
+  size_t need = 0;
+  dar_status st = attn_decode_impl(q, K_win, V_win, h_D, W_upK, W_upV, B, ctx_len, nullptr, cap,
+                                   heads, d_k, d_down, w, rope_base, dtype, o, nullptr, &need,
+                                   stream);
+  if (st != DAR_OK) return st;
+  if (need > kNoAllocScratchBytes) return DAR_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return DAR_ERR_HIP;
+  size_t have = kNoAllocScratchBytes;
+  return attn_decode_impl(q, K_win, V_win, h_D, W_upK, W_upV, B, ctx_len, nullptr, cap, heads,
+                          d_k, d_down, w, rope_base, dtype, o, ws, &have, stream);
 }
 
 dar_status dar_attn_decode_varlen(const void* q, const void* K_win, const void* V_win,

@@ -383,6 +383,30 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
                            dar_dtype dtype, void* o, void* workspace, size_t* workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * dar_attn_decode_noalloc -- dar_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, layouts, results and errors are those of dar_attn_decode, minus
+ * the workspace: the call allocates nothing and takes its scratch memory (the
+ * RoPE tables and the per-chunk softmax partials) from a static device array
+ * of 32 MiB that the library holds on each GPU it runs on until the process
+ * ends.  A problem whose dar_attn_decode workspace exceeds 32 MiB returns
+ * DAR_ERR_WORKSPACE without launching (about 4.7 MiB at batch 16, context
+ * 32768, 16 heads of 128, d_down 256; the RoPE tables add 256 KiB per 64k
+ * positions of context).  Every call on one GPU shares that GPU's array and
+ * rewrites all of it that it reads, so nothing carries over between calls;
+ * calls that overlap in time on one GPU (several streams or threads) race on
+ * it and must be serialised by the caller.  DAR_ERR_HIP if the array's
+ * device address cannot be obtained.
+ */
+dar_status dar_attn_decode_noalloc(const void* q, const void* K_win, const void* V_win,
+                                   const void* h_D, const void* W_upK, const void* W_upV, int B,
+                                   int ctx_len, int cap, int heads, int d_k, int d_down, int w,
+                                   float rope_base, dar_dtype dtype, void* o,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

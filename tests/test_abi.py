@@ -189,6 +189,33 @@ def test_decode_size_query_and_rejects():
     assert decode(ws=F(20), wsb=n - 1)[0] == WS
 
 
+def decode_noalloc(**kw):
+    a = dict(q=F(0), K_win=F(1), V_win=F(2), h_D=F(3), W_upK=F(4), W_upV=F(5), B=2, ctx=1000,
+             cap=1000, heads=4, d_k=128, d_down=256, w=128, base=10000.0, dtype=1, o=F(6))
+    a.update(kw)
+    return dar.lib().dar_attn_decode_noalloc(a["q"], a["K_win"], a["V_win"], a["h_D"],
+                                             a["W_upK"], a["W_upV"], a["B"], a["ctx"], a["cap"],
+                                             a["heads"], a["d_k"], a["d_down"], a["w"], a["base"],
+                                             a["dtype"], a["o"], None)
+
+
+def test_decode_noalloc_rejects_before_touching_the_device():
+    """The allocation-free decode validates like dar_attn_decode, and a problem
+    whose workspace would exceed its 32 MiB static scratch returns
+    DAR_ERR_WORKSPACE; none of these reaches the device (fake addresses)."""
+    assert decode_noalloc(cap=800) == INVALID
+    assert decode_noalloc(w=-1) == INVALID
+    assert decode_noalloc(o=F(3)) == INVALID     # output aliases the latent cache
+    assert decode_noalloc(dtype=0) == UNSUP
+    assert decode_noalloc(d_down=96) == UNSUP
+    # 5M positions: the RoPE tables alone need ~40 MB
+    st, n = decode(ctx=5_000_000, cap=5_000_000)
+    assert st == OK and n > (32 << 20)
+    assert decode_noalloc(ctx=5_000_000, cap=5_000_000) == WS
+    st, n = decode(ctx=1_000_000, cap=1_000_000)
+    assert st == OK and n <= (32 << 20)          # a million positions fit
+
+
 def test_fold_rejects():
     L = dar.lib()
     assert L.dar_fold(F(0), F(1), F(2), 256, 64, 4, 64, 1, F(3), F(0), None) == INVALID
