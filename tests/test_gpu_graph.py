@@ -172,11 +172,14 @@ def test_calls_on_a_side_stream_match_the_current_stream():
     inp = prefill_case(B, N + 1, d, H, d_k, dd, "bf16", seed=808)
     W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
     h = dev(inp["h"], "bf16")
+    # inputs are made before the side stream is ordered after the current one:
+    # a caller's inputs must be ready on the stream it passes
+    h_prompt, h_next = h[:, :N].contiguous(), h[:, N].contiguous()
 
     def sequence(stream):
         Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k, stream=stream)
-        out = dar.dar_project(h[:, :N].contiguous(), W["W_down"], W["W_up"], W["W_Q"],
-                              W["W_K"], W["W_V"], H, d_k, W_upK=Wk, W_upV=Wv, stream=stream)
+        out = dar.dar_project(h_prompt, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"],
+                              H, d_k, W_upK=Wk, W_upV=Wv, stream=stream)
         o = dar.dar_attn_prefill(out["Q"], out["K_loc"], out["V_loc"], out["K_glob"],
                                  out["V_glob"], w, stream=stream)
         cache, K_win, V_win = dar.dar_cache_from_prefill(out["h_D"], out["K_loc"],
@@ -185,8 +188,8 @@ def test_calls_on_a_side_stream_match_the_current_stream():
         with torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(
                 torch.cuda.current_stream()):
             q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
-        dar.dar_decode_append(h[:, N].contiguous(), W["W_down"], W["W_Q"], W["W_K"], W["W_V"],
-                              H, d_k, N, q, K_win, V_win, cache, stream=stream)
+        dar.dar_decode_append(h_next, W["W_down"], W["W_Q"], W["W_K"], W["W_V"], H, d_k, N, q,
+                              K_win, V_win, cache, stream=stream)
         od = dar.dar_attn_decode(q, K_win, V_win, cache, Wk, Wv, N + 1, w, stream=stream)
         return [o, od, cache, K_win, V_win]
 
