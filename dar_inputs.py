@@ -132,3 +132,35 @@ def decode_inputs(B, ctx, d, H, d_k, d_down, w, cap=None, dtype="bf16", seed0=50
         W_down=gaussian(seed0 + 7, (d, d_down), d ** -0.5, dtype),
         W_Q=gaussian(seed0 + 8, (d, hd), d ** -0.5, dtype),
     )
+
+
+def drope_prefill_inputs(B, N, d, H, d_k, d_down, d_R, dtype="bf16", seed0=7000, q_scale=1.0):
+    """prefill_inputs plus the rotary weights of the decoupled-RoPE variant:
+    W_QR [d, H d_R] and W_KR [d, d_R], both ~ N(0, 1/d) (fan-in d)."""
+    out = prefill_inputs(B, N, d, H, d_k, d_down, dtype=dtype, seed0=seed0, q_scale=q_scale)
+    out["W_QR"] = gaussian(seed0 + 7, (d, H * d_R), d ** -0.5, dtype)
+    out["W_KR"] = gaussian(seed0 + 8, (d, d_R), d ** -0.5, dtype)
+    return out
+
+
+def drope_decode_inputs(B, ctx, d, H, d_k, d_down, d_R, w, cap=None, dtype="bf16",
+                        seed0=8000):
+    """Mixed cache of the decoupled-RoPE variant for one query per sequence at
+    p = ctx - 1 (every value drawn directly; rotated parts are drawn already
+    rotated):
+    qC [B,H,d_k], qR [B,H,d_R]; K_win, V_win [B,H,w,d_k] (content keys and
+    values, ring slot = position mod w); KR [B,cap,d_R] (rotary keys of every
+    position); h_D [B,cap,d_down]; W_up, W_K, W_V (pages' layout)."""
+    cap = ctx if cap is None else cap
+    hd = H * d_k
+    return dict(
+        qC=gaussian(seed0 + 0, (B, H, d_k), 1.0, dtype),
+        qR=gaussian(seed0 + 1, (B, H, d_R), 1.0, dtype),
+        K_win=gaussian(seed0 + 2, (B, H, w, d_k), 1.0, dtype),
+        V_win=gaussian(seed0 + 3, (B, H, w, d_k), 1.0, dtype),
+        KR=gaussian(seed0 + 4, (B, cap, d_R), 1.0, dtype),
+        h_D=gaussian(seed0 + 5, (B, cap, d_down), 1.0, dtype),
+        W_up=gaussian(seed0 + 6, (d_down, d), d_down ** -0.5, dtype),
+        W_K=gaussian(seed0 + 7, (d, hd), d ** -0.5, dtype),
+        W_V=gaussian(seed0 + 8, (d, hd), d ** -0.5, dtype),
+    )

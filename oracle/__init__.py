@@ -59,6 +59,16 @@ def _load():
         lib.dar_oracle_decode.restype = ctypes.c_int
         lib.dar_oracle_decode.argtypes = [_D] * 7 + [ctypes.c_int, ctypes.c_long, ctypes.c_long] + [
             ctypes.c_int] * 4 + [ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_int, _D]
+        lib.dar_oracle_project_drope.restype = ctypes.c_int
+        lib.dar_oracle_project_drope.argtypes = [_D] * 8 + [ctypes.c_int] * 7 + [
+            ctypes.c_long, ctypes.c_double] + [ctypes.c_int] * 3 + [_D] * 9
+        lib.dar_oracle_attend_drope.restype = ctypes.c_int
+        lib.dar_oracle_attend_drope.argtypes = [_D] * 7 + [ctypes.c_int] * 5 + [
+            ctypes.c_long, _D, _D]
+        lib.dar_oracle_decode_drope.restype = ctypes.c_int
+        lib.dar_oracle_decode_drope.argtypes = [_D] * 9 + [ctypes.c_int, ctypes.c_long,
+                                                           ctypes.c_long] + [ctypes.c_int] * 5 + [
+            ctypes.c_long, ctypes.c_int, ctypes.c_int, _D]
         _lib = lib
     return _lib
 
@@ -188,4 +198,89 @@ def decode(q, K_win, V_win, hD, W_up, W_K, W_V, ctx, w, base=10000.0, heads=None
                                    float(base), lo, hi, _p(o))
     if rc != 0:
         raise ValueError("dar_oracle_decode rejected its arguments (rc=%d)" % rc)
+    return o
+
+
+# ---------------------------------------------------------------- decoupled RoPE
+def project_drope(h, W_down, W_up, W_Q, W_K, W_V, W_QR, W_KR, H, d_k, d_R, pos0=0,
+                  base=10000.0, n_tok=None, heads=None):
+    """Projections of the decoupled-RoPE variant.  Returns dict hD, hp, QC, QR,
+    KL, VL, KG, VG, KR (float64): content parts and values [B,H,N,d_k], rotary
+    queries QR [B,H,N,d_R], rotary keys KR [B,N,d_R] (one per token)."""
+    h, W_down, W_up, W_Q, W_K, W_V = map(_f64, (h, W_down, W_up, W_Q, W_K, W_V))
+    B, N, d = h.shape
+    d_down = W_down.shape[1]
+    W_QR = _f64(W_QR) if d_R else np.zeros((d, 0))
+    W_KR = _f64(W_KR) if d_R else np.zeros((d, 0))
+    assert W_QR.shape == (d, H * d_R) and W_KR.shape == (d, d_R)
+    n_tok = N if n_tok is None else int(n_tok)
+    lo, hi = (0, H) if heads is None else heads
+    out = dict(hD=np.zeros((B, N, d_down)), hp=np.zeros((B, N, d)),
+               QR=np.zeros((B, H, N, d_R)), KR=np.zeros((B, N, d_R)))
+    for k in ("QC", "KL", "VL", "KG", "VG"):
+        out[k] = np.zeros((B, H, N, d_k))
+    z = np.zeros(1)
+    rc = _load().dar_oracle_project_drope(
+        _p(h), _p(W_down), _p(W_up), _p(W_Q), _p(W_K), _p(W_V),
+        _p(W_QR) if d_R else _p(z), _p(W_KR) if d_R else _p(z), B, N, d, d_down, H, d_k, d_R,
+        int(pos0), float(base), n_tok, lo, hi, _p(out["hD"]), _p(out["hp"]), _p(out["QC"]),
+        _p(out["QR"]) if d_R else _p(z), _p(out["KL"]), _p(out["VL"]), _p(out["KG"]),
+        _p(out["VG"]), _p(out["KR"]) if d_R else _p(z))
+    if rc != 0:
+        raise ValueError("dar_oracle_project_drope rejected its arguments")
+    return out
+
+
+def attend_drope(P, w):
+    """Attention of the decoupled-RoPE variant for every row.  P holds QC, QR,
+    KL, VL, KG, VG, KR.  Returns (o [B,N,H*d_k], rowsum [B,H,N])."""
+    QC, KL, VL, KG, VG = (_f64(P[k]) for k in ("QC", "KL", "VL", "KG", "VG"))
+    B, H, N, d_k = QC.shape
+    QR, KR = _f64(P["QR"]), _f64(P["KR"])
+    d_R = QR.shape[-1]
+    assert QR.shape == (B, H, N, d_R) and KR.shape == (B, N, d_R)
+    o = np.zeros((B, N, H * d_k))
+    rs = np.zeros((B, H, N))
+    z = np.zeros(1)
+    rc = _load().dar_oracle_attend_drope(_p(QC), _p(QR) if d_R else _p(z), _p(KL), _p(VL),
+                                         _p(KG), _p(VG), _p(KR) if d_R else _p(z), B, N, H, d_k,
+                                         d_R, int(w), _p(o), _p(rs))
+    if rc != 0:
+        raise ValueError("dar_oracle_attend_drope rejected its arguments")
+    return o, rs
+
+
+def prefill_drope(inp, H, d_k, d_R, w, pos0=0, base=10000.0):
+    """Whole forward pass of the variant.  Returns (o, rowsum, projections)."""
+    P = project_drope(inp["h"], inp["W_down"], inp["W_up"], inp["W_Q"], inp["W_K"], inp["W_V"],
+                      inp.get("W_QR"), inp.get("W_KR"), H, d_k, d_R, pos0=pos0, base=base)
+    o, rs = attend_drope(P, w)
+    return o, rs, P
+
+
+def decode_drope(qC, qR, K_win, V_win, KR, hD, W_up, W_K, W_V, ctx, w, heads=None):
+    """Decode step of the variant at position ctx-1 over its cache.  qC [B,H,d_k],
+    qR [B,H,d_R]; K_win/V_win [B,H,w,d_k] (content keys, values); KR [B,cap,d_R]
+    (rotary keys of every position); hD [B,cap,d_down].  Returns o [B, H*d_k]."""
+    qC, hD, W_up, W_K, W_V = map(_f64, (qC, hD, W_up, W_K, W_V))
+    B, H, d_k = qC.shape
+    qR, KR = _f64(qR), _f64(KR)
+    d_R = qR.shape[-1]
+    cap, d_down = hD.shape[1], hD.shape[2]
+    d = W_up.shape[1]
+    assert KR.shape == (B, cap, d_R)
+    if w > 0:
+        K_win, V_win = _f64(K_win), _f64(V_win)
+        assert K_win.shape == V_win.shape == (B, H, w, d_k)
+    else:
+        K_win = V_win = np.zeros(1)
+    lo, hi = (0, H) if heads is None else heads
+    o = np.zeros((B, H * d_k))
+    z = np.zeros(1)
+    rc = _load().dar_oracle_decode_drope(_p(qC), _p(qR) if d_R else _p(z), _p(K_win),
+                                         _p(V_win), _p(KR) if d_R else _p(z), _p(hD), _p(W_up),
+                                         _p(W_K), _p(W_V), B, int(ctx), cap, H, d_k, d_R, d_down,
+                                         d, int(w), lo, hi, _p(o))
+    if rc != 0:
+        raise ValueError("dar_oracle_decode_drope rejected its arguments (rc=%d)" % rc)
     return o

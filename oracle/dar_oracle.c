@@ -403,3 +403,212 @@ int dar_oracle_decode(const double* q, const double* K_win, const double* V_win,
   free(s);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Decoupled-RoPE variant.  The DAR paper names MLA's decoupled rotary
+ * embedding as the route to an efficient implementation (the paragraph after
+ * the inference remark) and calls its latent h^D the counterpart of MLA's
+ * compressed vector (the paragraph after Eq. (1)); the papernotes summary's
+ * efficiency analysis repeats the pairing.  The pages do not write the
+ * variant out; the reading taken is MLA's construction carried over to Eqs.
+ * (1)-(4):
+ *   - every head's query and key get a rotary part of width d_R beside the
+ *     content part of width d_k; only the rotary part is rotated;
+ *   - content:  qC_i = h_i W_Q[:, S_a];  kC_j = h_j W_K[:, S_a] (i - j < w)
+ *               or h'_j W_K[:, S_a] (otherwise), Eq. (3) without RoPE;
+ *   - rotary:   qR_i = RoPE_i(h_i W_QR[:, R_a]), R_a = [a d_R, (a+1) d_R);
+ *               kR_j = RoPE_j(h_j W_KR), one rotary key per token, from the
+ *               full hidden state, shared by every head and by both paths;
+ *   - values as Eq. (3); s_ij = (qC_i . kC_j + qR_i . kR_j) / sqrt(d_k + d_R);
+ *     o_i = sum_j softmax(s)_j v_j (Eq. (4)).
+ * d_R = 0 leaves the content part alone (no rotation anywhere, scale
+ * 1/sqrt(d_k)).  RoPE over the rotary part: pairs (t, t + d_R/2), theta_t =
+ * base^(-2t/d_R).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Projections of the variant for tokens n < n_tok, heads [head_lo, head_hi):
+ *   hD [B,N,d_down], hp [B,N,d]                 Eqs. (1)-(2)
+ *   QC, KL, VL, KG, VG [B,H,N,d_k]              content parts, values
+ *   QR [B,H,N,d_R]                              rotary queries
+ *   KR [B,N,d_R]                                rotary keys (every token)
+ * W_QR [d, H d_R], W_KR [d, d_R].
+ */
+int dar_oracle_project_drope(const double* h, const double* W_down, const double* W_up,
+                             const double* W_Q, const double* W_K, const double* W_V,
+                             const double* W_QR, const double* W_KR, int B, int N, int d,
+                             int d_down, int H, int d_k, int d_R, long pos0, double base,
+                             int n_tok, int head_lo, int head_hi, double* hD, double* hp,
+                             double* QC, double* QR, double* KL, double* VL, double* KG,
+                             double* VG, double* KR) {
+  if (B < 1 || N < 1 || d < 1 || d_down < 1 || H < 1 || d_k < 1 || d_R < 0 || (d_R & 1))
+    return -1;
+  if (n_tok < 0 || n_tok > N || head_lo < 0 || head_hi > H || head_lo > head_hi) return -1;
+  const int hd = H * d_k, hr = H * d_R;
+  const long total = (long)B * n_tok;
+#pragma omp parallel for schedule(dynamic, 4)
+  for (long bn = 0; bn < total; ++bn) {
+    const int b = (int)(bn / n_tok), n = (int)(bn % n_tok);
+    const size_t tok = (size_t)b * N + n;
+    const double* x = h + tok * d;
+    double* xD = hD + tok * d_down;
+    double* xp = hp + tok * d;
+    vec_mat(x, W_down, d, d_down, 0, d_down, xD); /* Eq. 1 */
+    vec_mat(xD, W_up, d_down, d, 0, d, xp);       /* Eq. 2 */
+    const double pos = (double)(pos0 + n);
+    if (d_R > 0) {
+      vec_mat(x, W_KR, d, d_R, 0, d_R, KR + tok * d_R);
+      rope(KR + tok * d_R, d_R, pos, base);
+    }
+    for (int a = head_lo; a < head_hi; ++a) {
+      const size_t off = (((size_t)b * H + a) * N + n) * d_k;
+      vec_mat(x, W_Q, d, hd, a * d_k, d_k, QC + off);
+      vec_mat(x, W_K, d, hd, a * d_k, d_k, KL + off);
+      vec_mat(x, W_V, d, hd, a * d_k, d_k, VL + off);
+      vec_mat(xp, W_K, d, hd, a * d_k, d_k, KG + off);
+      vec_mat(xp, W_V, d, hd, a * d_k, d_k, VG + off);
+      if (d_R > 0) {
+        const size_t offr = (((size_t)b * H + a) * N + n) * d_R;
+        vec_mat(x, W_QR, d, hr, a * d_R, d_R, QR + offr);
+        rope(QR + offr, d_R, pos, base);
+      }
+    }
+  }
+  return 0;
+}
+
+/* Attention of the variant, every row: o [B,N,H d_k], rowsum [B,H,N] (may be
+ * NULL).  Keys j <= i; the content key and the value come from the local
+ * arrays when i - j < w, else from the global ones; the rotary key KR_j is
+ * the token's own in both cases. */
+int dar_oracle_attend_drope(const double* QC, const double* QR, const double* KL,
+                            const double* VL, const double* KG, const double* VG,
+                            const double* KR, int B, int N, int H, int d_k, int d_R, long w,
+                            double* o, double* rowsum) {
+  if (B < 1 || N < 1 || H < 1 || d_k < 1 || d_R < 0 || w < 0) return -1;
+  const double scale = 1.0 / sqrt((double)(d_k + d_R));
+  const long total = (long)B * H * N;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 8)
+    for (long r = 0; r < total; ++r) {
+      const int i = (int)(r % N), a = (int)((r / N) % H), b = (int)(r / ((long)N * H));
+      const size_t row0 = ((size_t)b * H + a) * N;
+      const double* qc = QC + (row0 + i) * d_k;
+      const double* qr = QR + (row0 + i) * d_R;
+      double m = -INFINITY;
+      for (int j = 0; j <= i; ++j) {
+        const double* kc = (((long)(i - j) < w) ? KL : KG) + (row0 + j) * d_k;
+        const double* kr = KR + ((size_t)b * N + j) * d_R;
+        double dot = 0.0;
+        for (int t = 0; t < d_k; ++t) dot += qc[t] * kc[t];
+        for (int t = 0; t < d_R; ++t) dot += qr[t] * kr[t];
+        s[j] = dot * scale;
+        if (s[j] > m) m = s[j];
+      }
+      double Z = 0.0;
+      for (int j = 0; j <= i; ++j) {
+        s[j] = exp(s[j] - m);
+        Z += s[j];
+      }
+      double* orow = o + ((size_t)b * N + i) * H * d_k + (size_t)a * d_k;
+      for (int t = 0; t < d_k; ++t) orow[t] = 0.0;
+      double psum = 0.0;
+      for (int j = 0; j <= i; ++j) {
+        const double* v = (((long)(i - j) < w) ? VL : VG) + (row0 + j) * d_k;
+        const double p = s[j] / Z;
+        psum += p;
+        for (int t = 0; t < d_k; ++t) orow[t] += p * v[t];
+      }
+      if (rowsum) rowsum[r] = psum;
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/*
+ * Decode step of the variant over its mixed cache, one query per sequence at
+ * p = ctx - 1:
+ *   qC [B,H,d_k], qR [B,H,d_R]   the query's content part and rotary part
+ *                                 (rotated at p)
+ *   K_win, V_win [B,H,w,d_k]      content keys (not rotated) and values of
+ *                                 positions p-w+1 .. p, slot = position mod w
+ *   KR [B,cap,d_R]                rotary keys of every position (rotated)
+ *   hD [B,cap,d_down]             latents; rows j <= p - w are read
+ * Positions j <= p - w use kC_j = h^D_j W_up W_K[:, S_a] and v_j = h^D_j W_up
+ * W_V[:, S_a] (Eqs. 2-3, in fp64, unfolded).  o [B, H d_k]; heads outside
+ * [head_lo, head_hi) are left untouched.
+ */
+int dar_oracle_decode_drope(const double* qC, const double* qR, const double* K_win,
+                            const double* V_win, const double* KR, const double* hD,
+                            const double* W_up, const double* W_K, const double* W_V, int B,
+                            long ctx, long cap, int H, int d_k, int d_R, int d_down, int d,
+                            long w, int head_lo, int head_hi, double* o) {
+  if (B < 1 || ctx < 1 || cap < 1 || H < 1 || d_k < 1 || d_R < 0 || d_down < 1 || d < 1 ||
+      w < 0 || head_lo < 0 || head_hi > H || head_lo > head_hi)
+    return -1;
+  const long p = ctx - 1;
+  const long n_glob = p - w + 1 > 0 ? p - w + 1 : 0;
+  if (n_glob > cap || p >= cap) return -1;
+  const int hd = H * d_k, nh = head_hi - head_lo;
+  if (nh == 0) return 0;
+  const double scale = 1.0 / sqrt((double)(d_k + d_R));
+  double* KGb = (double*)malloc(sizeof(double) * (size_t)(n_glob > 0 ? n_glob : 1) * nh * d_k);
+  double* VGb = (double*)malloc(sizeof(double) * (size_t)(n_glob > 0 ? n_glob : 1) * nh * d_k);
+  double* s = (double*)malloc(sizeof(double) * (size_t)(p + 1));
+  if (!KGb || !VGb || !s) {
+    free(KGb); free(VGb); free(s);
+    return -2;
+  }
+  for (int b = 0; b < B; ++b) {
+#pragma omp parallel
+    {
+      double* xp = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+      for (long j = 0; j < n_glob; ++j) {
+        vec_mat(hD + ((size_t)b * cap + j) * d_down, W_up, d_down, d, 0, d, xp); /* Eq. 2 */
+        for (int a = head_lo; a < head_hi; ++a) {
+          vec_mat(xp, W_K, d, hd, a * d_k, d_k, KGb + ((size_t)j * nh + (a - head_lo)) * d_k);
+          vec_mat(xp, W_V, d, hd, a * d_k, d_k, VGb + ((size_t)j * nh + (a - head_lo)) * d_k);
+        }
+      }
+      free(xp);
+    }
+    for (int a = head_lo; a < head_hi; ++a) {
+      const double* qc = qC + ((size_t)b * H + a) * d_k;
+      const double* qr = qR + ((size_t)b * H + a) * d_R;
+      double m = -INFINITY;
+      for (long j = 0; j <= p; ++j) {
+        const double* kc = (p - j < w)
+                               ? K_win + (((size_t)b * H + a) * w + (size_t)(j % w)) * d_k
+                               : KGb + ((size_t)j * nh + (a - head_lo)) * d_k;
+        const double* kr = KR + ((size_t)b * cap + j) * d_R;
+        double dot = 0.0;
+        for (int t = 0; t < d_k; ++t) dot += qc[t] * kc[t];
+        for (int t = 0; t < d_R; ++t) dot += qr[t] * kr[t];
+        s[j] = dot * scale;
+        if (s[j] > m) m = s[j];
+      }
+      double Z = 0.0;
+      for (long j = 0; j <= p; ++j) {
+        s[j] = exp(s[j] - m);
+        Z += s[j];
+      }
+      double* oa = o + (size_t)b * hd + (size_t)a * d_k;
+      for (int t = 0; t < d_k; ++t) oa[t] = 0.0;
+      for (long j = 0; j <= p; ++j) {
+        const double* v = (p - j < w)
+                              ? V_win + (((size_t)b * H + a) * w + (size_t)(j % w)) * d_k
+                              : VGb + ((size_t)j * nh + (a - head_lo)) * d_k;
+        const double pj = s[j] / Z;
+        for (int t = 0; t < d_k; ++t) oa[t] += pj * v[t];
+      }
+    }
+  }
+  free(KGb);
+  free(VGb);
+  free(s);
+  return 0;
+}
