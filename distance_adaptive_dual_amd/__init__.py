@@ -33,7 +33,7 @@ EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
            "dar_attn_decode_varlen", "dar_decode_append_sigmoid",
            "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid",
-           "dar_attn_decode_noalloc")
+           "dar_attn_decode_noalloc", "dar_attn_decode_drope")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.dar_prefill_chunk_sigmoid.argtypes = L.dar_prefill_chunk.argtypes
         L.dar_attn_decode_noalloc.restype = _I
         L.dar_attn_decode_noalloc.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P]
+        L.dar_attn_decode_drope.restype = _I
+        L.dar_attn_decode_drope.argtypes = [_P] * 8 + [_I] * 8 + [_I, _P, _P, _SZ, _P]
         L.dar_attn_decode_varlen.restype = _I
         L.dar_attn_decode_varlen.argtypes = [_P] * 6 + [_I, _P] + [_I] * 6 + [
             ctypes.c_float, _I, _P, _P, _SZ, _P]
@@ -488,4 +490,34 @@ def dar_attn_decode_noalloc(q, K_win, V_win, h_D, W_upK, W_upV, ctx_len: int, w:
         _ptr(W_upK), _ptr(W_upV), B, int(ctx_len), cap, H, d_k, d_down, int(w),
         float(rope_base), _dtype_code(q), _ptr(o), _stream(stream))
     _check("dar_attn_decode_noalloc", st)
+    return o
+
+
+def decode_drope_workspace_bytes(B, ctx_len, cap, heads, d_k, d_R, d_down, w):
+    n = ctypes.c_size_t(0)
+    f = [_fake(i) for i in range(9)]
+    st = lib().dar_attn_decode_drope(*f[:8], B, ctx_len, cap, heads, d_k, d_R, d_down, w,
+                                     DAR_BF16, f[8], None, ctypes.byref(n), None)
+    _check("dar_attn_decode_drope", st)
+    return n.value
+
+
+@_on_stream
+def dar_attn_decode_drope(qC, qR, K_win, V_win, KR, h_D, W_upK, W_upV, ctx_len: int, w: int,
+                          o=None, workspace=None, stream=None):
+    """Decode step of the decoupled-RoPE variant at position ctx_len-1.
+    qC [B, heads, d_k], qR [B, heads, d_R] (rotated); K_win / V_win
+    [B, heads, w, d_k] (content keys, values); KR [B, cap, d_R] (rotary keys
+    of every position); h_D [B, cap, d_down]; W_upK / W_upV from dar_fold.
+    Returns o [B, heads*d_k]."""
+    torch = _torch()
+    B, H, d_k = qC.shape
+    d_R = qR.shape[2]
+    cap, d_down = h_D.shape[1], h_D.shape[2]
+    if o is None:
+        o = torch.empty((B, H * d_k), dtype=qC.dtype, device=qC.device)
+    args = [_ptr(qC), _ptr(qR), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None,
+            _ptr(KR), _ptr(h_D), _ptr(W_upK), _ptr(W_upV), B, int(ctx_len), cap, H, d_k, d_R,
+            d_down, int(w), _dtype_code(qC), _ptr(o)]
+    _call_ws("dar_attn_decode_drope", lib().dar_attn_decode_drope, args, workspace, qC, stream)
     return o

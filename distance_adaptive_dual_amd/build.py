@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdar.so")
 SOURCES = ["dar_api.cpp", "rope.hip", "gemm.hip", "attn_prefill.hip", "attn_backward.hip",
-           "attn_decode.hip", "cache.hip"]
+           "attn_decode.hip", "attn_decode_drope.hip", "cache.hip"]
 CALIB_LIB = os.path.join(HERE, "libdar_calib.so")
 CALIB_SOURCES = ["calib.hip"]
 HEADERS = ["dar_common.hpp"]

@@ -613,6 +613,20 @@ hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_decode_combine(const DecodeProblem& p, int n_chunks, const float* part_lat,
+                                 const float* part_win, hipStream_t s) {
+  DecodeGeom g{};
+  g.n_chunks = n_chunks;
+  g.part_lat_floats = 2 + (size_t)p.d_down;
+  if (p.d_k == 64)
+    hipLaunchKernelGGL(decode_combine<64>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
+                       part_win);
+  else
+    hipLaunchKernelGGL(decode_combine<128>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
+                       part_win);
+  return hipGetLastError();
+}
+
 bool decode_supported(int d_k, int d_down) {
   const int KS = d_down / 16;
   return (d_k == 64 || d_k == 128) && d_down % 16 == 0 &&

@@ -1,0 +1,499 @@
+// Decode of the decoupled-RoPE variant: one query per sequence, streaming the
+// latent cache.
+//
+// "Dual Dimensionality for Local and Global Attention" names MLA's decoupled
+// rotary embedding as the way to an efficient implementation (the paragraph
+// after the inference remark).  The variant, read as MLA's construction on
+// Eqs. (1)-(4): every head's query and key carry a content part (Eq. (3)
+// without rotation) and a rotary part of width d_R; the rotary key
+// kR_j = RoPE_j(h_j W_KR) is one per token, shared by the heads and by both
+// paths; s_ij = (qC_i . kC_j + qR_i . kR_j) / sqrt(d_k + d_R).
+//
+// No rotation sits between W_upK and the query any more, so the content score
+// of a distant token is qC_a . (h^D_j W_upK_a) = (W_upK_a^T qC_a) . h^D_j:
+// the fold is absorbed into the query once per step, and the cache stream
+// reads [h^D_j ; kR_j] (d_down + d_R values per token) once for all heads.
+//   absorb  -- qa[b, a] = scale [W_upK_a^T qC_a ; qR_a] in fp32, stored as two
+//              bf16 parts (hi + lo), so the score MFMAs lose nothing to the
+//              rounding of the query;
+//   stream  -- per (batch, group of 16 heads, chunk of positions), two waves
+//              each streaming half the chunk through their own LDS double
+//              buffer (buffer loads with an LDS destination):
+//              S^T = X Qa^T on 16x16x32 MFMAs (X rows = tokens), an online
+//              softmax per head, acc[head, d_down] += P X_lat on 16x16x32
+//              MFMAs.  The P operand is the score registers as they are; the
+//              X_lat operand (eight tokens of one latent column per lane) is
+//              read from the row-major block with ds_read_b64_tr_b16;
+//   window  -- per (batch, head): the positions p-w+1 .. p, content keys and
+//              values from the ring, rotary keys from the cache;
+//   combine -- the latent decode's log-sum-exp merge and single lift by
+//              W_upV (decode_combine).
+// Scores are base-2 logits: log2(e) / sqrt(d_k + d_R) is folded into qa.
+#include <math.h>
+
+#include "dar_common.hpp"
+
+namespace dar {
+
+namespace {
+
+constexpr int DT = 32;              // tokens per streamed block
+constexpr int DWAVES = 2;           // waves per stream workgroup
+constexpr int DTARGET_WG = 512;     // stream workgroups to aim for (two per CU)
+constexpr float kTauD = 8.f;        // move the reference max only past 2^8 growth
+constexpr float kNegBigD = -1e30f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Geometry of one decode step.
+struct DropeGeom {
+  int n_glob;     // latent positions 0 .. n_glob-1
+  int n_hg;       // groups of 16 heads
+  int n_chunks;   // chunks per (batch, head group)
+  int chunk_len;  // positions per chunk (a multiple of DWAVES * DT)
+  int qw;         // d_down + d_R: width of an absorbed query row
+};
+
+DropeGeom drope_geom(const DropeDecodeProblem& p) {
+  DropeGeom g{};
+  const long pp = (long)p.ctx - 1;
+  g.n_glob = (int)(pp - p.w + 1 > 0 ? pp - p.w + 1 : 0);
+  g.n_hg = (p.H + 15) / 16;
+  g.qw = p.d_down + p.d_R;
+  int want = DTARGET_WG / (p.B * g.n_hg);
+  if (want < 1) want = 1;
+  const int unit = DWAVES * DT;
+  int len = (g.n_glob + want - 1) / want;
+  len = (len + unit - 1) / unit * unit;
+  if (len < unit) len = unit;
+  g.chunk_len = len;
+  g.n_chunks = g.n_glob > 0 ? (g.n_glob + len - 1) / len : 1;
+  return g;
+}
+
+// qa = scale [W_upK_a^T qC_a ; qR_a] split into bf16 hi + lo.  Grid (H, ceil(qw / 64)):
+// thread (t, batch group) forms element t of the rows of batches bg, bg + 4, ...
+template <int D, int DR>
+__global__ __launch_bounds__(256) void drope_absorb(DropeDecodeProblem p, DropeGeom g, bf16* qa_hi,
+                                                     bf16* qa_lo) {
+  const int h = blockIdx.x, t = blockIdx.y * 64 + (threadIdx.x & 63), bg = threadIdx.x >> 6;
+  const int DD = p.d_down;
+  if (t >= g.qw) return;
+  const float scl = kLog2e / sqrtf((float)(D + DR));
+  const bf16* Wk = (const bf16*)p.W_upK + (size_t)h * D * DD;
+  for (int b = bg; b < p.B; b += 4) {
+    const size_t row = (size_t)b * p.H + h;
+    float a = 0.f;
+    if (t < DD) {
+      const bf16* qc = (const bf16*)p.qC + row * D;
+      for (int c = 0; c < D; ++c) a = fmaf((float)Wk[(size_t)c * DD + t], (float)qc[c], a);
+    } else {
+      a = (float)((const bf16*)p.qR)[row * DR + (t - DD)];
+    }
+    a *= scl;
+    const bf16 hi = (bf16)a;
+    qa_hi[row * g.qw + t] = hi;
+    qa_lo[row * g.qw + t] = (bf16)(a - (float)hi);
+  }
+}
+
+template <int DD, int DR>
+struct StreamSmem {
+  // [wave][buffer] blocks of DT tokens, rows of DD (latent) / DR (rotary)
+  // bf16 stored with 16-byte chunk c of row r at slot c ^ (r mod slots)
+  bf16 lat[DWAVES][2][DT * DD];
+  bf16 rot[DWAVES][2][DT * DR];
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(N), other counters free
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
+
+template <int D, int DD, int DR>
+__global__ __launch_bounds__(DWAVES * 64) void drope_stream(DropeDecodeProblem p, DropeGeom g,
+                                                            const bf16* qa_hi, const bf16* qa_lo,
+                                                            float* part) {
+  __shared__ StreamSmem<DD, DR> sm;
+  constexpr int KL = DD / 32, KR = DR / 32;       // 32-wide contraction steps
+  constexpr int SL = 2 * DD / 16, SR = 2 * DR / 16;  // 16-byte slots per row
+  constexpr int NL = DT * DD * 2 / 1024;          // 1 KB load instructions per block
+  constexpr int NR = DT * DR * 2 / 1024;
+  static_assert(SL >= 16 && (SL & (SL - 1)) == 0, "latent rows of 16+ slots");
+  static_assert(NR >= 1 && SR >= 4, "rotary block of at least one instruction");
+  constexpr int NCT = DD / 16;                    // 16-column tiles of the accumulator
+
+  const int wg = blockIdx.x;
+  const int chunk = wg % g.n_chunks, bhg = wg / g.n_chunks;
+  const int b = bhg / g.n_hg, hg = bhg % g.n_hg;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, gq = lane >> 4;
+  const int sub = g.chunk_len / DWAVES;
+  const int c0 = chunk * g.chunk_len;
+  const int w0 = min(g.n_glob, c0 + wave * sub), w1 = min(g.n_glob, c0 + (wave + 1) * sub);
+  const int nblk = (w1 - w0 + DT - 1) / DT;
+
+  // absorbed query of head hg*16 + n as the B operand (contraction k-group gq)
+  bf16x8 qh[KL + KR], ql[KL + KR];
+  {
+    const int head = hg * 16 + n;
+    if (head < p.H) {
+      const size_t off = ((size_t)b * p.H + head) * g.qw + 8 * gq;
+#pragma unroll
+      for (int ks = 0; ks < KL + KR; ++ks) {
+        qh[ks] = *(const bf16x8*)(qa_hi + off + 32 * ks);
+        ql[ks] = *(const bf16x8*)(qa_lo + off + 32 * ks);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KL + KR; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qh[ks][e] = ql[ks][e] = (bf16)0.f;
+    }
+  }
+
+  // Rows w0 .. w1-1 of this sequence; the resources' range returns zeros past w1.
+  const size_t row0 = (size_t)b * p.cap + (w0 < w1 ? w0 : 0);
+  const int nrows = w1 - w0;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)p.h_D + row0 * DD), (short)0, nrows * DD * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)p.KR + row0 * DR), (short)0, nrows * DR * 2, 0x00020000);
+  auto issue = [&](int blk, int buf) {
+    bf16* dl = sm.lat[wave][buf];
+    bf16* dr = sm.rot[wave][buf];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int byte = i * 1024 + 16 * lane;  // where this lane's 16 bytes land
+      const int r = byte / (2 * DD), s = (byte % (2 * DD)) / 16;
+      const int c = s ^ (r & 15);             // the row's chunk kept at slot s
+      const unsigned off = (unsigned)(((blk * DT + r) * DD) * 2 + 16 * c);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)(dl + i * 512), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int byte = i * 1024 + 16 * lane;
+      const int r = byte / (2 * DR), s = (byte % (2 * DR)) / 16;
+      const int c = s ^ (r & (SR - 1));
+      const unsigned off = (unsigned)(((blk * DT + r) * DR) * 2 + 16 * c);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rr, (__attribute__((address_space(3))) void*)(dr + i * 512), 16, off, 0, 0, 0);
+    }
+  };
+
+  float m_ref = kNegBigD, l_lane = 0.f;  // head n: reference max, this lane's share of the sum
+  f32x4 acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int blk, int buf) {
+    const bf16* L = sm.lat[wave][buf];
+    const bf16* R = sm.rot[wave][buf];
+    // scores: tile t holds tokens 16 t + 4 gq + i (register i) of head n
+    f32x4 sh[2], sl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sh[t] = sl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KL; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 16 * t + n, c = 4 * ks + gq;
+        const bf16x8 a = *(const bf16x8*)(L + row * DD + 8 * (c ^ (row & 15)));
+        sh[t] = mfma16(a, qh[ks], sh[t]);
+        sl[t] = mfma16(a, ql[ks], sl[t]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 16 * t + n, c = 4 * ks + gq;
+        const bf16x8 a = *(const bf16x8*)(R + row * DR + 8 * (c ^ (row & (SR - 1))));
+        sh[t] = mfma16(a, qh[KL + ks], sh[t]);
+        sl[t] = mfma16(a, ql[KL + ks], sl[t]);
+      }
+    }
+    const int j0 = w0 + blk * DT;
+    float s[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = j0 + 16 * t + 4 * gq + i < w1;
+        s[t][i] = ok ? sh[t][i] + sl[t][i] : -INFINITY;
+        mt = fmaxf(mt, s[t][i]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTauD) != 0) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float al = __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_lane *= al;
+      // accumulator rows are heads 4 gq + i, whose state sits in lane 4 gq + i
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(al, 4 * gq + i);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ct][i] *= ar[i];
+    }
+    // P (A operand: row = head n, contraction slots 8 gq .. 8 gq + 7 = tokens
+    // 4 gq + i of tile 0, then of tile 1) and its fp32 sum from the same bf16
+    bf16x8 pf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16 e = (bf16)__builtin_amdgcn_exp2f(s[t][i] - m_ref);
+        pf[4 * t + i] = e;
+        l_lane += (float)e;
+      }
+    // X_lat operand of column tile ct, read transposed: this lane addresses
+    // row 4 (lane >> 4) + ((lane >> 2) & 3) (+ 16 for the second read) at
+    // columns 16 ct + 4 (lane & 3) .. + 3 and receives tokens 4 gq .. 4 gq + 3
+    // (then 16 + ...) of column 16 ct + n.
+    const int r = lane & 3, k = (lane >> 2) & 3;
+    const int ra = 4 * gq + k, rb = 16 + 4 * gq + k;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 2 * ct + (r >> 1), half = r & 1;
+      const bf16* pa = L + ra * DD + 8 * (c ^ (ra & 15)) + 4 * half;
+      const bf16* pb = L + rb * DD + 8 * (c ^ (rb & 15)) + 4 * half;
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)pa);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)pb);
+      // whole dwords: tokens 4 gq .. 4 gq + 3 then 16 + 4 gq .. (element order kept)
+      const u32x2 ua = __builtin_bit_cast(u32x2, va), ub = __builtin_bit_cast(u32x2, vb);
+      const u32x4 uw = {ua[0], ua[1], ub[0], ub[1]};
+      acc[ct] = mfma16(pf, __builtin_bit_cast(bf16x8, uw), acc[ct]);
+    }
+  };
+
+  if (nblk > 0) issue(0, 0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    __asm__ volatile("" ::: "memory");
+    if (blk + 1 < nblk) {
+      issue(blk + 1, (blk + 1) & 1);
+      wait_vm<NL + NR>();  // block blk has landed; block blk + 1 may be in flight
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __asm__ volatile("" ::: "memory");
+    compute(blk, blk & 1);
+  }
+
+  // Merge the two waves' partials (wave 1 -> LDS -> wave 0), then write one
+  // (max, sum, accumulator) per head of the group.
+  float l_head = l_lane + __shfl_xor(l_lane, 16);
+  l_head += __shfl_xor(l_head, 32);
+  __asm__ volatile("" ::: "memory");
+  __syncthreads();  // every wave is done with its staging buffers
+  float* xacc = (float*)&sm.lat[1][0][0];  // [16 heads][DD]
+  float* xml = (float*)&sm.lat[1][1][0];   // [2][16]
+  if (wave == 1) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xacc[(4 * gq + i) * DD + 16 * ct + n] = acc[ct][i];
+    if (gq == 0) {
+      xml[n] = m_ref;
+      xml[16 + n] = l_head;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float m1 = xml[n], l1 = xml[16 + n];
+    const float M = fmaxf(l_head > 0.f ? m_ref : -INFINITY, l1 > 0.f ? m1 : -INFINITY);
+    const float f0 = l_head > 0.f ? __builtin_amdgcn_exp2f(m_ref - M) : 0.f;
+    const float f1 = l1 > 0.f ? __builtin_amdgcn_exp2f(m1 - M) : 0.f;
+    const float L = f0 * l_head + f1 * l1;
+    float g0[4], g1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g0[i] = __shfl(f0, 4 * gq + i);
+      g1[i] = __shfl(f1, 4 * gq + i);
+    }
+    const size_t PF = 2 + (size_t)DD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int head = hg * 16 + 4 * gq + i;
+      if (head < p.H) {
+        float* dst = part + (((size_t)b * p.H + head) * g.n_chunks + chunk) * PF + 2;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          dst[16 * ct + n] = g0[i] * acc[ct][i] + g1[i] * xacc[(4 * gq + i) * DD + 16 * ct + n];
+      }
+    }
+    const int head = hg * 16 + n;
+    if (gq == 0 && head < p.H) {
+      float* dst = part + (((size_t)b * p.H + head) * g.n_chunks + chunk) * PF;
+      dst[0] = L > 0.f ? M : kNegBigD;
+      dst[1] = L;
+    }
+  }
+}
+
+// Window part: the positions p-w+1 .. p of (batch, head) in tiles of 256
+// keys, a thread per key for the score (content key from the ring slot
+// j mod w, rotary key from the cache row j), then the value sum with two
+// threads per column (each over half the tile's keys).
+template <int D, int DR>
+__global__ __launch_bounds__(256) void drope_window(DropeDecodeProblem p, float* part_win) {
+  __shared__ float qs[D + DR];
+  __shared__ float pr[256];
+  __shared__ float red[8];
+  __shared__ float hacc[D];
+  const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long pp = (long)p.ctx - 1;
+  const long lo = pp - p.w + 1 > 0 ? pp - p.w + 1 : 0;
+  const int nw = p.w > 0 ? (int)(pp - lo + 1) : 0;
+  const float scl = kLog2e / sqrtf((float)(D + DR));
+  if (tid < D) qs[tid] = (float)((const bf16*)p.qC)[(size_t)bh * D + tid] * scl;
+  else if (tid < D + DR) qs[tid] = (float)((const bf16*)p.qR)[(size_t)bh * DR + tid - D] * scl;
+  __syncthreads();
+  const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
+  const bf16* Vw = (const bf16*)p.V_win + (size_t)bh * p.w * D;
+  const bf16* Kr = (const bf16*)p.KR + (size_t)b * p.cap * DR;
+  float m = kNegBigD, l = 0.f, acc = 0.f;
+  const int col = tid % D, part = tid / D;  // D = 64: four parts; D = 128: two
+  constexpr int NPART = 256 / D;
+  for (int k0 = 0; k0 < nw; k0 += 256) {
+    const int k = k0 + tid;
+    float s = -INFINITY;
+    if (k < nw) {
+      const long j = lo + k;
+      const bf16* kc = Kw + (size_t)(j % p.w) * D;
+      const bf16* kr = Kr + (size_t)j * DR;
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; c += 8) {
+        const bf16x8 v = *(const bf16x8*)(kc + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf((float)v[e], qs[c + e], a);
+      }
+#pragma unroll
+      for (int c = 0; c < DR; c += 8) {
+        const bf16x8 v = *(const bf16x8*)(kr + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf((float)v[e], qs[D + c + e], a);
+      }
+      s = a;
+    }
+    float mt = s;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+    if (lane == 0) red[wave] = mt;
+    __syncthreads();
+    mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float m_new = fmaxf(m, mt);
+    const float al = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    const float e = k < nw ? __builtin_amdgcn_exp2f(s - m) : 0.f;
+    pr[tid] = e;
+    float es = e;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) es += __shfl_xor(es, off);
+    __syncthreads();  // pr complete; red read by everyone
+    if (lane == 0) red[4 + wave] = es;
+    acc *= al;
+    const int kn = min(256, nw - k0);
+    for (int kk = part; kk < kn; kk += NPART) {
+      const long j = lo + k0 + kk;
+      acc = fmaf(pr[kk], (float)Vw[(size_t)(j % p.w) * D + col], acc);
+    }
+    __syncthreads();
+    l = l * al + (red[4] + red[5] + red[6] + red[7]);
+    __syncthreads();  // red and pr are rewritten by the next tile
+  }
+  if (part == 0) hacc[col] = acc;
+  __syncthreads();
+  for (int q = 1; q < NPART; ++q) {
+    if (part == q) hacc[col] += acc;
+    __syncthreads();
+  }
+  float* dst = part_win + (size_t)bh * (2 + D);
+  if (tid < D) dst[2 + tid] = hacc[tid];
+  if (tid == 0) {
+    dst[0] = nw > 0 ? m : -INFINITY;
+    dst[1] = l;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool drope_decode_supported(int d_k, int d_R, int d_down) {
+  return ((d_k == 64 && d_R == 32) || (d_k == 128 && d_R == 64)) &&
+         (d_down == 128 || d_down == 256 || d_down == 512);
+}
+
+size_t drope_decode_workspace_bytes(const DropeDecodeProblem& p) {
+  const DropeGeom g = drope_geom(p);
+  const size_t qa = align256(sizeof(bf16) * (size_t)p.B * p.H * g.qw);
+  const size_t lat = align256(sizeof(float) * (size_t)p.B * p.H * g.n_chunks * (2 + p.d_down));
+  const size_t win = align256(sizeof(float) * (size_t)p.B * p.H * (2 + p.d_k));
+  return 2 * qa + lat + win;
+}
+
+hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) {
+  const DropeGeom g = drope_geom(p);
+  char* ws = (char*)p.ws;
+  const size_t qa = align256(sizeof(bf16) * (size_t)p.B * p.H * g.qw);
+  const size_t lat = align256(sizeof(float) * (size_t)p.B * p.H * g.n_chunks * (2 + p.d_down));
+  bf16* qa_hi = (bf16*)ws;
+  bf16* qa_lo = (bf16*)(ws + qa);
+  float* part_lat = (float*)(ws + 2 * qa);
+  float* part_win = (float*)(ws + 2 * qa + lat);
+  const dim3 ga(p.H, (g.qw + 63) / 64);
+  const int n_stream = p.B * g.n_hg * g.n_chunks;
+  if (p.d_k == 64) {
+    hipLaunchKernelGGL((drope_absorb<64, 32>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
+    if (p.d_down == 128)
+      hipLaunchKernelGGL((drope_stream<64, 128, 32>), dim3(n_stream), dim3(DWAVES * 64), 0, s, p,
+                         g, qa_hi, qa_lo, part_lat);
+    else if (p.d_down == 256)
+      hipLaunchKernelGGL((drope_stream<64, 256, 32>), dim3(n_stream), dim3(DWAVES * 64), 0, s, p,
+                         g, qa_hi, qa_lo, part_lat);
+    else
+      hipLaunchKernelGGL((drope_stream<64, 512, 32>), dim3(n_stream), dim3(DWAVES * 64), 0, s, p,
+                         g, qa_hi, qa_lo, part_lat);
+    hipLaunchKernelGGL((drope_window<64, 32>), dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+  } else {
+    hipLaunchKernelGGL((drope_absorb<128, 64>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
+    if (p.d_down == 128)
+      hipLaunchKernelGGL((drope_stream<128, 128, 64>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
+                         p, g, qa_hi, qa_lo, part_lat);
+    else if (p.d_down == 256)
+      hipLaunchKernelGGL((drope_stream<128, 256, 64>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
+                         p, g, qa_hi, qa_lo, part_lat);
+    else
+      hipLaunchKernelGGL((drope_stream<128, 512, 64>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
+                         p, g, qa_hi, qa_lo, part_lat);
+    hipLaunchKernelGGL((drope_window<128, 64>), dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DecodeProblem c{};
+  c.W_upV = p.W_upV;
+  c.o = p.o;
+  c.B = p.B;
+  c.H = p.H;
+  c.d_k = p.d_k;
+  c.d_down = p.d_down;
+  return launch_decode_combine(c, g.n_chunks, part_lat, part_win, s);
+}
+
+}  // namespace dar

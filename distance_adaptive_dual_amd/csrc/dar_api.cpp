@@ -745,6 +745,70 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
                           d_k, d_down, w, rope_base, dtype, o, workspace, workspace_bytes, stream);
 }
 
+dar_status dar_attn_decode_drope(const void* qC, const void* qR, const void* K_win,
+                                 const void* V_win, const void* KR, const void* h_D,
+                                 const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
+                                 int heads, int d_k, int d_R, int d_down, int w, dar_dtype dtype,
+                                 void* o, void* workspace, size_t* workspace_bytes,
+                                 hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || ctx_len < 1 || cap < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_R < 0 ||
+      (d_R & 1) || d_down < 1 || w < 0)
+    return DAR_ERR_INVALID_ARG;
+  if (ctx_len > cap) return DAR_ERR_INVALID_ARG;  // rotary keys of every position <= p are read
+  const void* need[] = {qC, qR, KR, h_D, W_upK, W_upV, o};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k, es = elem_size(dtype);
+  const Span ins[8] = {{qC, es * B * hd},
+                       {qR, es * B * (size_t)heads * d_R},
+                       {K_win, w > 0 ? es * B * hd * (size_t)w : 0},
+                       {V_win, w > 0 ? es * B * hd * (size_t)w : 0},
+                       {KR, es * B * (size_t)cap * d_R},
+                       {h_D, es * B * (size_t)cap * d_down},
+                       {W_upK, es * d_down * hd},
+                       {W_upV, es * d_down * hd}};
+  const Span outs[1] = {{o, es * B * hd}};
+  if (!disjoint(outs, 1, ins, 8)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!drope_decode_supported(d_k, d_R, d_down)) return DAR_ERR_UNSUPPORTED;
+  if ((size_t)cap * d_down * 2 > 0x7fffffffu) return DAR_ERR_UNSUPPORTED;  // 32-bit offsets
+  DropeDecodeProblem p{};
+  p.qC = qC;
+  p.qR = qR;
+  p.K_win = K_win;
+  p.V_win = V_win;
+  p.KR = KR;
+  p.h_D = h_D;
+  p.W_upK = W_upK;
+  p.W_upV = W_upV;
+  p.o = o;
+  p.B = B;
+  p.ctx = ctx_len;
+  p.cap = cap;
+  p.H = heads;
+  p.d_k = d_k;
+  p.d_R = d_R;
+  p.d_down = d_down;
+  p.w = w;
+  const size_t need_bytes = drope_decode_workspace_bytes(p);
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& x : ins)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+    if (overlap(ws, outs[0])) return DAR_ERR_INVALID_ARG;
+  }
+  p.ws = workspace;
+  return hip_status(launch_attn_decode_drope(p, stream));
+}
+
 // Allocation-free decode: the workspace of dar_attn_decode (RoPE tables and
 // per-chunk partials) lives in a file-scope device array, one per GPU, held
 // until the process ends.  The host never passes the array's name to a

@@ -222,6 +222,22 @@ struct DecodeProblem {
   const int* ctx_lens = nullptr;
 };
 size_t decode_workspace_bytes(const DecodeProblem& p);
+// The latent decode's log-sum-exp merge and lift by W_upV over n_chunks latent
+// partials (max, sum, acc[d_down]) per (batch, head) and one window partial
+// (max, sum, acc[d_k]); reads p.W_upV, p.B, p.H, p.d_k, p.d_down, writes p.o.
+hipError_t launch_decode_combine(const DecodeProblem& p, int n_chunks, const float* part_lat,
+                                 const float* part_win, hipStream_t s);
+
+// Decode of the decoupled-RoPE variant (attn_decode_drope.hip).
+struct DropeDecodeProblem {
+  const void *qC, *qR, *K_win, *V_win, *KR, *h_D, *W_upK, *W_upV;
+  void* o;
+  int B, ctx, cap, H, d_k, d_R, d_down, w;
+  void* ws;
+};
+bool drope_decode_supported(int d_k, int d_R, int d_down);
+size_t drope_decode_workspace_bytes(const DropeDecodeProblem& p);
+hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s);
 // Pieces of the cache kernels (fp16 <-> bf16 conversions, positions relative to
 // array bases; see cache.hip).
 hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap, int row0,

@@ -384,6 +384,44 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
                            hipStream_t stream);
 
 /*
+ * Decoupled-RoPE variant.  "Dual Dimensionality for Local and Global
+ * Attention" names MLA's decoupled rotary embedding as the route to an
+ * efficient implementation (the paragraph after the inference remark)
+ * without writing it out.  Reading taken (MLA's construction on Eqs. 1-4):
+ * every head's query and key carry a content part and a rotary part of width
+ * d_R; only the rotary part is rotated;
+ *   qC_i = h_i W_Q[:, S_a],  qR_i = RoPE_i(h_i W_QR[:, R_a])   (R_a: d_R columns of head a)
+ *   kC_j = h_j W_K[:, S_a] if i - j < w, else h'_j W_K[:, S_a] (Eq. 3 without RoPE)
+ *   kR_j = RoPE_j(h_j W_KR)   one rotary key per token, from the full hidden
+ *                             state, shared by every head and both paths
+ *   v_j as Eq. 3;  s_ij = (qC_i . kC_j + qR_i . kR_j) / sqrt(d_k + d_R).
+ * RoPE over the rotary part: pairs (t, t + d_R/2), theta_t = base^(-2t/d_R).
+ * Supported: d_R = d_k / 2 (d_k 64 or 128).
+ *
+ * dar_attn_decode_drope -- one query per sequence at p = ctx_len - 1 over the
+ * variant's cache.  With no rotation between W_upK and the query, the content
+ * score of an old position is (W_upK_a^T qC_a) . h^D_j: the fold is absorbed
+ * into the query once per step and the cache is streamed as [h^D_j ; kR_j]
+ * for all heads at once (latent-space value sum, one lift by W_upV).
+ *   qC     [B, heads, d_k]        content query
+ *   qR     [B, heads, d_R]        rotary query, rotated at p
+ *   K_win  [B, heads, w, d_k]     content keys (not rotated) of positions
+ *   V_win  [B, heads, w, d_k]     p-w+1 .. p and their values, slot = pos mod w
+ *   KR     [B, cap, d_R]          rotary keys of every position (rows 0 .. p read)
+ *   h_D    [B, cap, d_down]       latents (rows 0 .. p-w read); cap >= ctx_len
+ *   W_upK, W_upV                  folded weights from dar_fold
+ *   o      [B, heads*d_k]
+ * bf16 only; d_down in {128, 256, 512}.  Workspace (query with NULL): the
+ * absorbed queries and the softmax partials.
+ */
+dar_status dar_attn_decode_drope(const void* qC, const void* qR, const void* K_win,
+                                 const void* V_win, const void* KR, const void* h_D,
+                                 const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,
+                                 int heads, int d_k, int d_R, int d_down, int w, dar_dtype dtype,
+                                 void* o, void* workspace, size_t* workspace_bytes,
+                                 hipStream_t stream);
+
+/*
  * dar_attn_decode_noalloc -- dar_attn_decode for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).
