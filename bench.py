@@ -288,6 +288,80 @@ def cpu_baseline(oracle, inp, H, d_k, w, budget_s=10.0, heads=2):
                       "counts a step" % (N, d, heads - 1, H, reps)}
 
 
+def cache_flusher(torch):
+    """A 1 GiB device read (libdar_calib.so) run before each timed decode call:
+    it replaces the 256 MB Infinity Cache's contents with clean lines of an
+    unrelated buffer, so the call reads its cache from HBM.  (A write-based
+    flush would leave dirty lines whose write-back then lands inside the
+    timed call.)"""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "distance_adaptive_dual_amd", "libdar_calib.so"))
+    L.dar_calib_read.restype = ctypes.c_int
+    L.dar_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+
+    def flush():
+        st = L.dar_calib_read(buf.data_ptr(), buf.numel(), sink.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError("dar_calib_read failed")
+    flush.keep = (buf, sink)
+    return flush
+
+
+def time_decode_drope(torch, dar, di, steps, warmup, cfg):
+    """The decoupled-RoPE variant's decode step (dar_attn_decode_drope) at the
+    long-context shape, timed like time_decode.  Bytes: the latent and rotary
+    caches (d_down + d_R per position), the window's content keys and values
+    and its rotary keys, the folded weights, q and o."""
+    B, ctx, d, H, d_k, d_down, w, d_R = cfg
+    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, d_down, d_R, w, seed0=8000)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(
+            torch.bfloat16).cuda()
+
+    W_up, W_K, W_V = (dev(inp[k].T) for k in ("W_up", "W_K", "W_V"))
+    Wk, Wv = dar.dar_fold(W_up, W_K, W_V, H, d_k)
+    t = {k: dev(inp[k]) for k in ("qC", "qR", "K_win", "V_win", "KR", "h_D")}
+    del inp
+    o = torch.empty((B, H * d_k), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dar.decode_drope_workspace_bytes(B, ctx, ctx, H, d_k, d_R, d_down, w),
+                     dtype=torch.uint8, device="cuda")
+    flush = cache_flusher(torch)
+    g = capture(torch, lambda: dar.dar_attn_decode_drope(t["qC"], t["qR"], t["K_win"], t["V_win"],
+                                                         t["KR"], t["h_D"], Wk, Wv, ctx, w, o=o,
+                                                         workspace=ws))
+    settle(torch, g)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del g
+    ms = float(np.median(times))
+    n_lat = ctx - w
+    byts = 2.0 * (B * n_lat * (d_down + d_R) + B * w * (2 * H * d_k + d_R) + 2 * d_down * H * d_k
+                  + B * H * (d_k + d_R) + B * H * d_k)
+    flops = (B * n_lat * H * (2.0 * (d_down + d_R) + 2.0 * d_down) + B * w * H * (4.0 * d_k + 2.0 * d_R)
+             + 2.0 * B * H * d_k * d_down * 2)
+    return {"workload": "decoupled-RoPE decode B%d ctx%d d%d H%d dk%d dR%d w%d d_down%d"
+                        % (B, ctx, d, H, d_k, d_R, w, d_down),
+            "ms": ms, "GB/s": byts / ms / 1e6, "TFLOP/s": flops / ms / 1e9,
+            "bytes": byts, "flops": flops,
+            "roofline": {"bound": "hbm", "achieved": byts / ms / 1e6, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": byts / ms / 1e6 / PEAK_HBM_GBS}}
+
+
 def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
     """The mixed-cache decode step of cfg (B sequences at context ctx), or with
     lens, a ragged batch: sequence b at context lens[b] <= ctx
@@ -306,7 +380,7 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
     o = torch.empty((B, H * d_k), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(dar.decode_workspace_bytes(B, ctx, ctx, H, d_k, d_down, w),
                      dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # > Infinity Cache
+    flush = cache_flusher(torch)
     if lens is None:
         g = capture(torch, lambda: dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o,
                                                        workspace=ws))
@@ -320,7 +394,7 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
     torch.cuda.synchronize()
     times = []
     for _ in range(steps):
-        flush.zero_()
+        flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         g.replay()
@@ -424,14 +498,24 @@ def calibrate(torch):
             raise RuntimeError("dar_calib_copy failed")
 
     ms_c = timed(copy)
-    del src, dst, sink
+    L.dar_calib_read.restype = ctypes.c_int
+    L.dar_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    rsink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+
+    def read():
+        if L.dar_calib_read(src.data_ptr(), nbytes, rsink.data_ptr(), stream) != 0:
+            raise RuntimeError("dar_calib_read failed")
+
+    ms_r = timed(read)
+    del src, dst, sink, rsink
     torch.cuda.empty_cache()
     return {"mfma_f16_tflops": tflops, "mfma_f16_tflops_by_shape": rates,
-            "hbm_copy_gbs": 2 * nbytes / ms_c / 1e6,
+            "hbm_copy_gbs": 2 * nbytes / ms_c / 1e6, "hbm_read_gbs": nbytes / ms_r / 1e6,
             "vendor_mfma_tflops": PEAK_BF16_TFLOPS, "vendor_hbm_gbs": PEAK_HBM_GBS,
             "how": "fp16 MFMA loops from registers (the faster of 32x32x16 and 16x16x32), "
                    "2048 workgroups; 1 GiB device copy with 16-byte loads/stores (read + "
-                   "write bytes)"}
+                   "write bytes); 1 GiB device read with 16-byte loads"}
 
 
 def main():
@@ -578,9 +662,16 @@ def main():
         dec = time_decode(torch, dar, di, max(3, args.steps // 2), 2,
                           (16, 32768, 2048, 16, 128, 256, 512))
         log("decode: %.3f ms, %.0f GB/s, %.1f TFLOP/s" % (dec["ms"], dec["GB/s"], dec["TFLOP/s"]))
-        dec["hbm_frac_measured"] = dec["GB/s"] / cal["hbm_copy_gbs"]
+        dec["hbm_frac_measured"] = dec["GB/s"] / cal["hbm_read_gbs"]
         dec["mfma_frac_measured"] = dec["TFLOP/s"] / cal["mfma_f16_tflops"]
         res["decode"] = dec
+        dd = time_decode_drope(torch, dar, di, max(3, args.steps // 2), 2,
+                               (16, 32768, 2048, 16, 128, 256, 512, 64))
+        dd["roofline"]["frac_measured"] = dd["GB/s"] / cal["hbm_read_gbs"]
+        dd["roofline"]["peak_measured"] = cal["hbm_read_gbs"]
+        res["decode_drope"] = dd
+        log("decode (decoupled RoPE): %.3f ms, %.0f GB/s (%.1f%% of HBM)"
+            % (dd["ms"], dd["GB/s"], 100 * dd["roofline"]["frac"]))
         if not args.no_sweep:
             # a serving-like batch: 16 contexts spread over 1k .. 32k
             lens = [int(x) for x in np.linspace(1024, 32768, 16)[::-1]]

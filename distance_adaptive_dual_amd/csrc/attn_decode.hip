@@ -510,18 +510,38 @@ __global__ __launch_bounds__(512, 1) void decode_latent(DecodeProblem p, DecodeG
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeom g,
                                                       const float* part_lat,
-                                                      const float* part_win) {
+                                                      const float* part_win, int n_win) {
   __shared__ float lat[1024];
   __shared__ float wsc[1024];
+  __shared__ float wwf[64];
+  __shared__ float wacc[D];
   __shared__ float red[2];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int DD = p.d_down, nc = g.n_chunks;
   const size_t PF = g.part_lat_floats;
   const float* pl = part_lat + (size_t)bh * nc * PF;
-  const float* pw = part_win + (size_t)bh * (2 + D);
+  // window partials (max, sum, acc[D]) of this (batch, head): n_win in a row
+  const float* pw = part_win + (size_t)bh * n_win * (2 + D);
+  // The loads that do not depend on the merge weights go out first, so their
+  // latency overlaps the weights': the lift's W_upV row piece (TPR threads
+  // per output row t, DD / TPR columns each, 16-byte chunks) and this
+  // thread's latent column of the first CPF partials.
+  constexpr int TPR = 256 / D, WPF = 16, CPF = 32;
+  const int h = bh % p.H;
+  const bf16* Wv = (const bf16*)p.W_upV + (size_t)h * D * DD;
+  const int t = tid / TPR, part = tid % TPR;
+  const int per = DD / TPR;  // a multiple of 8 for every supported d_down
+  const bf16* wr = Wv + (size_t)t * DD + part * per;
+  bf16x8_t wv[WPF];
+#pragma unroll
+  for (int i = 0; i < WPF; ++i)
+    if (8 * i < per) wv[i] = *(const bf16x8_t*)(wr + 8 * i);
+  float pv[CPF];
+#pragma unroll
+  for (int c = 0; c < CPF; ++c) pv[c] = (tid < DD && c < nc) ? pl[c * PF + 2 + tid] : 0.f;
   if (wave == 0) {
     // common maximum over the non-empty partials, their weights and the total
-    float M = (lane == 0 && pw[1] > 0.f) ? pw[0] : -INFINITY;
+    float M = (lane < n_win && pw[lane * (2 + D) + 1] > 0.f) ? pw[lane * (2 + D)] : -INFINITY;
     for (int c = lane; c < nc; c += 64)
       if (pl[c * PF + 1] > 0.f) M = fmaxf(M, pl[c * PF]);
 #pragma unroll
@@ -533,37 +553,57 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeo
       wsc[c] = f;
       L += f * e[1];
     }
+    if (lane < n_win) {
+      const float* e = pw + lane * (2 + D);
+      const float f = (e[1] > 0.f) ? exp2f(e[0] - M) : 0.f;
+      wwf[lane] = f;
+      L += f * e[1];
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-    if (lane == 0) {
-      const float fw = (pw[1] > 0.f) ? exp2f(pw[0] - M) : 0.f;
-      red[0] = fw;
-      red[1] = L + fw * pw[1];
-    }
+    if (lane == 0) red[1] = L;
   }
   __syncthreads();
-  for (int kk = tid; kk < DD; kk += 256) {
+  // the window's value sum in d_k space
+  if (tid < D) {
     float a = 0.f;
-    for (int c = 0; c < nc; ++c) a += wsc[c] * pl[c * PF + 2 + kk];
-    lat[kk] = a;
+    for (int k = 0; k < n_win; ++k) a = fmaf(wwf[k], pw[k * (2 + D) + 2 + tid], a);
+    wacc[tid] = a;
   }
-  __syncthreads();
-  // lift by W_upV: a wave per output row, 4 consecutive latent dims per lane
-  const int h = bh % p.H;
-  const bf16* Wv = (const bf16*)p.W_upV + (size_t)h * D * DD;
-  const float inv = 1.f / red[1];
-  for (int t = wave; t < D; t += 4) {
-    const bf16* wr = Wv + (size_t)t * DD;
-    float a = 0.f;
-    for (int kk = 4 * lane; kk < DD; kk += 256) {
-      const u32x2 v = *(const u32x2*)(wr + kk);
-      a += lat[kk] * __uint_as_float(v[0] << 16) + lat[kk + 1] * __uint_as_float(v[0] & 0xffff0000u) +
-           lat[kk + 2] * __uint_as_float(v[1] << 16) + lat[kk + 3] * __uint_as_float(v[1] & 0xffff0000u);
-    }
+  // latent sum: a thread per latent column (the first CPF partials from the
+  // prefetched values)
+  if (tid < DD) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off);
-    if (lane == 0) ((bf16*)p.o)[(size_t)bh * D + t] = (bf16)((a + red[0] * pw[2 + t]) * inv);
+    for (int c = 0; c < CPF; ++c)
+      if (c < nc) a[c & 3] = fmaf(wsc[c], pv[c], a[c & 3]);
+    for (int c = CPF; c < nc; ++c) a[c & 3] = fmaf(wsc[c], pl[c * PF + 2 + tid], a[c & 3]);
+    lat[tid] = (a[0] + a[1]) + (a[2] + a[3]);
   }
+  for (int kk = tid + 256; kk < DD; kk += 256) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nc; ++c) a[c & 3] = fmaf(wsc[c], pl[c * PF + 2 + kk], a[c & 3]);
+    lat[kk] = (a[0] + a[1]) + (a[2] + a[3]);
+  }
+  __syncthreads();
+  // lift by W_upV, partial sums of a row met by shuffles
+  const float inv = 1.f / red[1];
+  const float* lp = lat + part * per;
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < WPF; ++i)
+    if (8 * i < per) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaf(lp[8 * i + e], (float)wv[i][e], a);
+    }
+  for (int kk = 8 * WPF; kk < per; kk += 8) {
+    const bf16x8_t v = *(const bf16x8_t*)(wr + kk);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaf(lp[kk + e], (float)v[e], a);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+  if (part == 0) ((bf16*)p.o)[(size_t)bh * D + t] = (bf16)((a + wacc[t]) * inv);
 }
 
 template <int D, int KS>
@@ -606,24 +646,24 @@ hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (p.d_k == 64)
     hipLaunchKernelGGL(decode_combine<64>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
-                       part_win);
+                       part_win, 1);
   else
     hipLaunchKernelGGL(decode_combine<128>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
-                       part_win);
+                       part_win, 1);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const DecodeProblem& p, int n_chunks, const float* part_lat,
-                                 const float* part_win, hipStream_t s) {
+                                 const float* part_win, int n_win, hipStream_t s) {
   DecodeGeom g{};
   g.n_chunks = n_chunks;
   g.part_lat_floats = 2 + (size_t)p.d_down;
   if (p.d_k == 64)
     hipLaunchKernelGGL(decode_combine<64>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
-                       part_win);
+                       part_win, n_win);
   else
     hipLaunchKernelGGL(decode_combine<128>, dim3(p.B * p.H), dim3(256), 0, s, p, g, part_lat,
-                       part_win);
+                       part_win, n_win);
   return hipGetLastError();
 }
 

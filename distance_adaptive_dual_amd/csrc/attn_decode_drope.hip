@@ -31,15 +31,24 @@
 // Scores are base-2 logits: log2(e) / sqrt(d_k + d_R) is folded into qa.
 #include <math.h>
 
+#include <algorithm>
+
 #include "dar_common.hpp"
 
 namespace dar {
 
 namespace {
 
+#ifndef DAR_STREAM_NB
+#define DAR_STREAM_NB 2
+#endif
+#ifndef DAR_STREAM_TARGET
+#define DAR_STREAM_TARGET 512
+#endif
+constexpr int kStreamNB = DAR_STREAM_NB;  // buffers per wave (d_down <= 256)
 constexpr int DT = 32;              // tokens per streamed block
-constexpr int DWAVES = 2;           // waves per stream workgroup
-constexpr int DTARGET_WG = 512;     // stream workgroups to aim for (two per CU)
+constexpr int DWAVES = 2;           // waves per stream workgroup (chunk split)
+constexpr int DTARGET_WG = DAR_STREAM_TARGET;  // stream workgroups to aim for
 constexpr float kTauD = 8.f;        // move the reference max only past 2^8 growth
 constexpr float kNegBigD = -1e30f;
 
@@ -56,6 +65,8 @@ struct DropeGeom {
   int n_chunks;   // chunks per (batch, head group)
   int chunk_len;  // positions per chunk (a multiple of DWAVES * DT)
   int qw;         // d_down + d_R: width of an absorbed query row
+  int n_win;      // window pieces per (batch, head), each <= win_len positions
+  int win_len;
 };
 
 DropeGeom drope_geom(const DropeDecodeProblem& p) {
@@ -72,41 +83,73 @@ DropeGeom drope_geom(const DropeDecodeProblem& p) {
   if (len < unit) len = unit;
   g.chunk_len = len;
   g.n_chunks = g.n_glob > 0 ? (g.n_glob + len - 1) / len : 1;
+  const long nw = p.w > 0 ? pp - (pp - p.w + 1 > 0 ? pp - p.w + 1 : 0) + 1 : 0;
+  g.n_win = nw > 0 ? (int)std::min<long>(64, (nw + 127) / 128) : 1;
+  g.win_len = nw > 0 ? (int)((nw + g.n_win - 1) / g.n_win) : 1;
   return g;
 }
 
-// qa = scale [W_upK_a^T qC_a ; qR_a] split into bf16 hi + lo.  Grid (H, ceil(qw / 64)):
-// thread (t, batch group) forms element t of the rows of batches bg, bg + 4, ...
+// qa = scale [W_upK_a^T qC_a ; qR_a] split into bf16 hi + lo.  Grid
+// (H, ceil(qw / 64), ceil(B / 4)), four waves: column t = 64 blockIdx.y + lane
+// of the absorbed rows of four batches, the contraction over the head's d_k
+// split between the waves (each a quarter, its loads all in flight) and
+// summed through LDS.
 template <int D, int DR>
 __global__ __launch_bounds__(256) void drope_absorb(DropeDecodeProblem p, DropeGeom g, bf16* qa_hi,
                                                      bf16* qa_lo) {
-  const int h = blockIdx.x, t = blockIdx.y * 64 + (threadIdx.x & 63), bg = threadIdx.x >> 6;
+  constexpr int NBT = 4, CQ = D / 4;
+  __shared__ float qcs[NBT][D];
+  __shared__ float red[4][NBT][64];
+  const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.y * 64 + lane;
   const int DD = p.d_down;
-  if (t >= g.qw) return;
   const float scl = kLog2e / sqrtf((float)(D + DR));
   const bf16* Wk = (const bf16*)p.W_upK + (size_t)h * D * DD;
-  for (int b = bg; b < p.B; b += 4) {
-    const size_t row = (size_t)b * p.H + h;
-    float a = 0.f;
-    if (t < DD) {
-      const bf16* qc = (const bf16*)p.qC + row * D;
-      for (int c = 0; c < D; ++c) a = fmaf((float)Wk[(size_t)c * DD + t], (float)qc[c], a);
-    } else {
-      a = (float)((const bf16*)p.qR)[row * DR + (t - DD)];
+  {
+    const int b0 = blockIdx.z * NBT;
+    const int nb = min(NBT, p.B - b0);
+    for (int e = threadIdx.x; e < NBT * D; e += 256) {
+      const int bi = e / D, c = e % D;
+      qcs[bi][c] = bi < nb ? (float)((const bf16*)p.qC)[((size_t)(b0 + bi) * p.H + h) * D + c]
+                           : 0.f;
     }
-    a *= scl;
-    const bf16 hi = (bf16)a;
-    qa_hi[row * g.qw + t] = hi;
-    qa_lo[row * g.qw + t] = (bf16)(a - (float)hi);
+    __syncthreads();
+    float acc[NBT];
+#pragma unroll
+    for (int bi = 0; bi < NBT; ++bi) acc[bi] = 0.f;
+    if (t < DD) {
+      float wv[CQ];
+#pragma unroll
+      for (int i = 0; i < CQ; ++i) wv[i] = (float)Wk[(size_t)(wave * CQ + i) * DD + t];
+#pragma unroll
+      for (int i = 0; i < CQ; ++i)
+#pragma unroll
+        for (int bi = 0; bi < NBT; ++bi) acc[bi] = fmaf(wv[i], qcs[bi][wave * CQ + i], acc[bi]);
+    }
+#pragma unroll
+    for (int bi = 0; bi < NBT; ++bi) red[wave][bi][lane] = acc[bi];
+    __syncthreads();
+    for (int bi = wave; bi < nb; bi += 4) {
+      if (t < g.qw) {
+        const size_t row = (size_t)(b0 + bi) * p.H + h;
+        float a = t < DD ? red[0][bi][lane] + red[1][bi][lane] + red[2][bi][lane] + red[3][bi][lane]
+                         : (float)((const bf16*)p.qR)[row * DR + (t - DD)];
+        a *= scl;
+        const bf16 hi = (bf16)a;
+        qa_hi[row * g.qw + t] = hi;
+        qa_lo[row * g.qw + t] = (bf16)(a - (float)hi);
+      }
+    }
+    __syncthreads();  // qcs and red are rewritten for the next batches
   }
 }
 
-template <int DD, int DR>
+template <int DD, int DR, int NB>
 struct StreamSmem {
   // [wave][buffer] blocks of DT tokens, rows of DD (latent) / DR (rotary)
   // bf16 stored with 16-byte chunk c of row r at slot c ^ (r mod slots)
-  bf16 lat[DWAVES][2][DT * DD];
-  bf16 rot[DWAVES][2][DT * DR];
+  bf16 lat[DWAVES][NB][DT * DD];
+  bf16 rot[DWAVES][NB][DT * DR];
 };
 
 template <int N>
@@ -115,11 +158,12 @@ __device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(N), other counte
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 
-template <int D, int DD, int DR>
+template <int D, int DD, int DR, int NB>
 __global__ __launch_bounds__(DWAVES * 64) void drope_stream(DropeDecodeProblem p, DropeGeom g,
                                                             const bf16* qa_hi, const bf16* qa_lo,
                                                             float* part) {
-  __shared__ StreamSmem<DD, DR> sm;
+  static_assert(NB == 2 || NB == 3, "two or three buffers per wave");
+  __shared__ StreamSmem<DD, DR, NB> sm;
   constexpr int KL = DD / 32, KR = DR / 32;       // 32-wide contraction steps
   constexpr int SL = 2 * DD / 16, SR = 2 * DR / 16;  // 16-byte slots per row
   constexpr int NL = DT * DD * 2 / 1024;          // 1 KB load instructions per block
@@ -279,18 +323,25 @@ __global__ __launch_bounds__(DWAVES * 64) void drope_stream(DropeDecodeProblem p
     }
   };
 
-  if (nblk > 0) issue(0, 0);
+  // Block k lives in buffer k % NB; loads run NB - 1 blocks ahead.  Before
+  // block blk is read, every load but those of the (up to NB - 2) blocks
+  // issued after it must have landed.
+  for (int k = 0; k < NB - 1 && k < nblk; ++k) issue(k, k);
   for (int blk = 0; blk < nblk; ++blk) {
     __asm__ volatile("" ::: "memory");
-    if (blk + 1 < nblk) {
-      issue(blk + 1, (blk + 1) & 1);
-      wait_vm<NL + NR>();  // block blk has landed; block blk + 1 may be in flight
+    if (blk + NB - 1 < nblk) issue(blk + NB - 1, (blk + NB - 1) % NB);
+    const int ahead = min(nblk - 1 - blk, NB - 1);
+    if constexpr (NB >= 3) {
+      if (ahead >= 2) wait_vm<2 * (NL + NR)>();
+      else if (ahead == 1) wait_vm<NL + NR>();
+      else wait_vm<0>();
     } else {
-      wait_vm<0>();
+      if (ahead == 1) wait_vm<NL + NR>();
+      else wait_vm<0>();
     }
     __builtin_amdgcn_sched_barrier(0);
     __asm__ volatile("" ::: "memory");
-    compute(blk, blk & 1);
+    compute(blk, blk % NB);
   }
 
   // Merge the two waves' partials (wave 1 -> LDS -> wave 0), then write one
@@ -344,87 +395,120 @@ __global__ __launch_bounds__(DWAVES * 64) void drope_stream(DropeDecodeProblem p
   }
 }
 
-// Window part: the positions p-w+1 .. p of (batch, head) in tiles of 256
-// keys, a thread per key for the score (content key from the ring slot
-// j mod w, rotary key from the cache row j), then the value sum with two
-// threads per column (each over half the tile's keys).
+// Window part: the positions p-w+1 .. p of (batch, head).  A key's content
+// row (2 d_k bytes) is read by d_k/8 lanes, 16 bytes each, its rotary row by
+// the first d_R/8 of them; the lanes' partial dot products meet by shuffles.
+// Keys go in tiles of up to WT: scores into LDS, the tile's maximum and
+// exponentials, then the values read the same way, each lane accumulating
+// its 8 columns; the key groups' accumulators are summed through LDS at the end.
 template <int D, int DR>
-__global__ __launch_bounds__(256) void drope_window(DropeDecodeProblem p, float* part_win) {
-  __shared__ float qs[D + DR];
-  __shared__ float pr[256];
-  __shared__ float red[8];
-  __shared__ float hacc[D];
-  const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+__global__ __launch_bounds__(256) void drope_window(DropeDecodeProblem p, DropeGeom g,
+                                                     float* part_win) {
+  constexpr int LPK = D / 8, KPI = 256 / LPK, RL = DR / 8, WT = 1024;
+  __shared__ float sc[WT];
+  __shared__ float red[2][4];
+  __shared__ float accs[KPI][D];
+  const int bh = blockIdx.x / g.n_win, piece = blockIdx.x % g.n_win, b = bh / p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = tid % LPK, kg = tid / LPK;
   const long pp = (long)p.ctx - 1;
-  const long lo = pp - p.w + 1 > 0 ? pp - p.w + 1 : 0;
-  const int nw = p.w > 0 ? (int)(pp - lo + 1) : 0;
+  const long lw = pp - p.w + 1 > 0 ? pp - p.w + 1 : 0;  // first window position
+  const int nw_all = p.w > 0 ? (int)(pp - lw + 1) : 0;
+  // this piece: window positions lo .. lo + nw - 1
+  const int k_begin = min(nw_all, piece * g.win_len);
+  const long lo = lw + k_begin;
+  const int nw = min(nw_all, k_begin + g.win_len) - k_begin;
   const float scl = kLog2e / sqrtf((float)(D + DR));
-  if (tid < D) qs[tid] = (float)((const bf16*)p.qC)[(size_t)bh * D + tid] * scl;
-  else if (tid < D + DR) qs[tid] = (float)((const bf16*)p.qR)[(size_t)bh * DR + tid - D] * scl;
-  __syncthreads();
+  float qc[8], qr[8];
+  {
+    const bf16x8 v = *(const bf16x8*)((const bf16*)p.qC + (size_t)bh * D + 8 * lr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qc[e] = (float)v[e] * scl;
+    if (lr < RL) {
+      const bf16x8 u = *(const bf16x8*)((const bf16*)p.qR + (size_t)bh * DR + 8 * lr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qr[e] = (float)u[e] * scl;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qr[e] = 0.f;
+    }
+  }
   const bf16* Kw = (const bf16*)p.K_win + (size_t)bh * p.w * D;
   const bf16* Vw = (const bf16*)p.V_win + (size_t)bh * p.w * D;
   const bf16* Kr = (const bf16*)p.KR + (size_t)b * p.cap * DR;
-  float m = kNegBigD, l = 0.f, acc = 0.f;
-  const int col = tid % D, part = tid / D;  // D = 64: four parts; D = 128: two
-  constexpr int NPART = 256 / D;
-  for (int k0 = 0; k0 < nw; k0 += 256) {
-    const int k = k0 + tid;
-    float s = -INFINITY;
-    if (k < nw) {
-      const long j = lo + k;
-      const bf16* kc = Kw + (size_t)(j % p.w) * D;
-      const bf16* kr = Kr + (size_t)j * DR;
+  auto block_max = [&](float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    if (lane == 0) red[0][wave] = x;
+    __syncthreads();
+    x = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    return x;
+  };
+  auto block_sum = [&](float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if (lane == 0) red[1][wave] = x;
+    __syncthreads();
+    return red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  };
+  float m = kNegBigD, l = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < nw; k0 += WT) {
+    const int nt = min(WT, nw - k0);
+#pragma unroll 8
+    for (int kk = kg; kk < nt; kk += KPI) {
+      const long j = lo + k0 + kk;
+      const bf16x8 v = *(const bf16x8*)(Kw + (size_t)(j % p.w) * D + 8 * lr);
       float a = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; c += 8) {
-        const bf16x8 v = *(const bf16x8*)(kc + c);
+      for (int e = 0; e < 8; ++e) a = fmaf((float)v[e], qc[e], a);
+      if (lr < RL) {
+        const bf16x8 u = *(const bf16x8*)(Kr + (size_t)j * DR + 8 * lr);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaf((float)v[e], qs[c + e], a);
+        for (int e = 0; e < 8; ++e) a = fmaf((float)u[e], qr[e], a);
       }
 #pragma unroll
-      for (int c = 0; c < DR; c += 8) {
-        const bf16x8 v = *(const bf16x8*)(kr + c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaf((float)v[e], qs[D + c + e], a);
-      }
-      s = a;
+      for (int off = LPK / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+      if (lr == 0) sc[kk] = a;
     }
-    float mt = s;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-    if (lane == 0) red[wave] = mt;
     __syncthreads();
-    mt = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float mt = -INFINITY;
+    for (int kk = tid; kk < nt; kk += 256) mt = fmaxf(mt, sc[kk]);
+    mt = block_max(mt);
     const float m_new = fmaxf(m, mt);
     const float al = __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
-    const float e = k < nw ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-    pr[tid] = e;
-    float es = e;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) es += __shfl_xor(es, off);
-    __syncthreads();  // pr complete; red read by everyone
-    if (lane == 0) red[4 + wave] = es;
-    acc *= al;
-    const int kn = min(256, nw - k0);
-    for (int kk = part; kk < kn; kk += NPART) {
-      const long j = lo + k0 + kk;
-      acc = fmaf(pr[kk], (float)Vw[(size_t)(j % p.w) * D + col], acc);
+    float ls = 0.f;
+    for (int kk = tid; kk < nt; kk += 256) {
+      const float e = __builtin_amdgcn_exp2f(sc[kk] - m);
+      sc[kk] = e;
+      ls += e;
     }
-    __syncthreads();
-    l = l * al + (red[4] + red[5] + red[6] + red[7]);
-    __syncthreads();  // red and pr are rewritten by the next tile
+    ls = block_sum(ls);  // its barrier also publishes the exponentials
+    l = l * al + ls;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= al;
+#pragma unroll 8
+    for (int kk = kg; kk < nt; kk += KPI) {
+      const long j = lo + k0 + kk;
+      const bf16x8 v = *(const bf16x8*)(Vw + (size_t)(j % p.w) * D + 8 * lr);
+      const float pk = sc[kk];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pk, (float)v[e], acc[e]);
+    }
+    __syncthreads();  // sc and red are rewritten by the next tile
   }
-  if (part == 0) hacc[col] = acc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) accs[kg][8 * lr + e] = acc[e];
   __syncthreads();
-  for (int q = 1; q < NPART; ++q) {
-    if (part == q) hacc[col] += acc;
-    __syncthreads();
+  float* dst = part_win + ((size_t)bh * g.n_win + piece) * (2 + D);
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < KPI; ++k) a += accs[k][tid];
+    dst[2 + tid] = a;
   }
-  float* dst = part_win + (size_t)bh * (2 + D);
-  if (tid < D) dst[2 + tid] = hacc[tid];
   if (tid == 0) {
     dst[0] = nw > 0 ? m : -INFINITY;
     dst[1] = l;
@@ -444,7 +528,7 @@ size_t drope_decode_workspace_bytes(const DropeDecodeProblem& p) {
   const DropeGeom g = drope_geom(p);
   const size_t qa = align256(sizeof(bf16) * (size_t)p.B * p.H * g.qw);
   const size_t lat = align256(sizeof(float) * (size_t)p.B * p.H * g.n_chunks * (2 + p.d_down));
-  const size_t win = align256(sizeof(float) * (size_t)p.B * p.H * (2 + p.d_k));
+  const size_t win = align256(sizeof(float) * (size_t)p.B * p.H * g.n_win * (2 + p.d_k));
   return 2 * qa + lat + win;
 }
 
@@ -457,32 +541,34 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) 
   bf16* qa_lo = (bf16*)(ws + qa);
   float* part_lat = (float*)(ws + 2 * qa);
   float* part_win = (float*)(ws + 2 * qa + lat);
-  const dim3 ga(p.H, (g.qw + 63) / 64);
+  const dim3 ga(p.H, (g.qw + 63) / 64, (p.B + 3) / 4);
   const int n_stream = p.B * g.n_hg * g.n_chunks;
   if (p.d_k == 64) {
     hipLaunchKernelGGL((drope_absorb<64, 32>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
     if (p.d_down == 128)
-      hipLaunchKernelGGL((drope_stream<64, 128, 32>), dim3(n_stream), dim3(DWAVES * 64), 0, s, p,
-                         g, qa_hi, qa_lo, part_lat);
+      hipLaunchKernelGGL((drope_stream<64, 128, 32, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
+                         0, s, p, g, qa_hi, qa_lo, part_lat);
     else if (p.d_down == 256)
-      hipLaunchKernelGGL((drope_stream<64, 256, 32>), dim3(n_stream), dim3(DWAVES * 64), 0, s, p,
-                         g, qa_hi, qa_lo, part_lat);
+      hipLaunchKernelGGL((drope_stream<64, 256, 32, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
+                         0, s, p, g, qa_hi, qa_lo, part_lat);
     else
-      hipLaunchKernelGGL((drope_stream<64, 512, 32>), dim3(n_stream), dim3(DWAVES * 64), 0, s, p,
-                         g, qa_hi, qa_lo, part_lat);
-    hipLaunchKernelGGL((drope_window<64, 32>), dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+      hipLaunchKernelGGL((drope_stream<64, 512, 32, 2>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
+                         p, g, qa_hi, qa_lo, part_lat);
+    hipLaunchKernelGGL((drope_window<64, 32>), dim3(p.B * p.H * g.n_win), dim3(256), 0, s, p, g,
+                       part_win);
   } else {
     hipLaunchKernelGGL((drope_absorb<128, 64>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
     if (p.d_down == 128)
-      hipLaunchKernelGGL((drope_stream<128, 128, 64>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
-                         p, g, qa_hi, qa_lo, part_lat);
+      hipLaunchKernelGGL((drope_stream<128, 128, 64, kStreamNB>), dim3(n_stream),
+                         dim3(DWAVES * 64), 0, s, p, g, qa_hi, qa_lo, part_lat);
     else if (p.d_down == 256)
-      hipLaunchKernelGGL((drope_stream<128, 256, 64>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
-                         p, g, qa_hi, qa_lo, part_lat);
+      hipLaunchKernelGGL((drope_stream<128, 256, 64, kStreamNB>), dim3(n_stream),
+                         dim3(DWAVES * 64), 0, s, p, g, qa_hi, qa_lo, part_lat);
     else
-      hipLaunchKernelGGL((drope_stream<128, 512, 64>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
+      hipLaunchKernelGGL((drope_stream<128, 512, 64, 2>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
                          p, g, qa_hi, qa_lo, part_lat);
-    hipLaunchKernelGGL((drope_window<128, 64>), dim3(p.B * p.H), dim3(256), 0, s, p, part_win);
+    hipLaunchKernelGGL((drope_window<128, 64>), dim3(p.B * p.H * g.n_win), dim3(256), 0, s, p,
+                       g, part_win);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -493,7 +579,7 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) 
   c.H = p.H;
   c.d_k = p.d_k;
   c.d_down = p.d_down;
-  return launch_decode_combine(c, g.n_chunks, part_lat, part_win, s);
+  return launch_decode_combine(c, g.n_chunks, part_lat, part_win, g.n_win, s);
 }
 
 }  // namespace dar

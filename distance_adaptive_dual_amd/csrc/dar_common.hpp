@@ -223,10 +223,11 @@ struct DecodeProblem {
 };
 size_t decode_workspace_bytes(const DecodeProblem& p);
 // The latent decode's log-sum-exp merge and lift by W_upV over n_chunks latent
-// partials (max, sum, acc[d_down]) per (batch, head) and one window partial
-// (max, sum, acc[d_k]); reads p.W_upV, p.B, p.H, p.d_k, p.d_down, writes p.o.
+// partials (max, sum, acc[d_down]) per (batch, head) and n_win (<= 64) window
+// partials (max, sum, acc[d_k]); reads p.W_upV, p.B, p.H, p.d_k, p.d_down,
+// writes p.o.
 hipError_t launch_decode_combine(const DecodeProblem& p, int n_chunks, const float* part_lat,
-                                 const float* part_win, hipStream_t s);
+                                 const float* part_win, int n_win, hipStream_t s);
 
 // Decode of the decoupled-RoPE variant (attn_decode_drope.hip).
 struct DropeDecodeProblem {

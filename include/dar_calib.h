@@ -30,6 +30,11 @@ int dar_calib_mfma(float* sink, int workgroups, int iters, int shape, hipStream_
  * with 16-byte loads and stores. */
 int dar_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
+/* Device read of `bytes` (multiple of 16; 16-byte aligned) with 16-byte
+ * loads, eight in flight per thread.  sink: device buffer of >= 8192
+ * unsigned (written only in an impossible case). */
+int dar_calib_read(const void* src, size_t bytes, unsigned* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -257,7 +257,7 @@ def test_calib_library_exports_and_rejects():
     include/dar_calib.h declares and rejects bad arguments before launching."""
     text = open(CALIB_HEADER).read()
     names = set(re.findall(r"^\s*(?:int|double)\s+(dar_\w+)\s*\(", text, re.M))
-    assert names == {"dar_calib_mfma_flops", "dar_calib_mfma", "dar_calib_copy"}
+    assert names == {"dar_calib_mfma_flops", "dar_calib_mfma", "dar_calib_copy", "dar_calib_read"}
     L = ctypes.CDLL(os.path.join(ROOT, "distance_adaptive_dual_amd", "libdar_calib.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -274,6 +274,10 @@ def test_calib_library_exports_and_rejects():
     assert L.dar_calib_mfma(F(0), 4, 10, 2, None) != 0       # unknown shape
     assert L.dar_calib_copy(F(0), F(1), 100, None) != 0      # not a multiple of 16
     assert L.dar_calib_copy(F(0) + 8, F(1), 64, None) != 0   # misaligned source
+    L.dar_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    assert L.dar_calib_read(F(0), 100, F(1), None) != 0      # not a multiple of 16
+    assert L.dar_calib_read(F(0), 64, None, None) != 0       # no sink
 
 
 def cache(**kw):
