@@ -33,7 +33,8 @@ EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
            "dar_attn_decode", "dar_cache_from_prefill_varlen", "dar_decode_append_varlen",
            "dar_attn_decode_varlen", "dar_decode_append_sigmoid",
            "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid",
-           "dar_attn_decode_noalloc", "dar_attn_decode_drope")
+           "dar_attn_decode_noalloc", "dar_attn_decode_drope", "dar_project_drope",
+           "dar_attn_prefill_drope", "dar_cache_from_prefill_drope", "dar_decode_append_drope")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -55,6 +56,7 @@ def lib() -> ctypes.CDLL:
             raise ImportError("libdar.so is not built; run python -m distance_adaptive_dual_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         L.dar_abi_version.restype = _I
+        L.dar_abi_version.argtypes = []
         L.dar_status_string.restype = ctypes.c_char_p
         L.dar_status_string.argtypes = [_I]
         L.dar_fold.restype = _I
@@ -92,6 +94,16 @@ def lib() -> ctypes.CDLL:
         L.dar_prefill_chunk_sigmoid.argtypes = L.dar_prefill_chunk.argtypes
         L.dar_attn_decode_noalloc.restype = _I
         L.dar_attn_decode_noalloc.argtypes = [_P] * 6 + [_I] * 7 + [ctypes.c_float, _I, _P, _P]
+        L.dar_project_drope.restype = _I
+        L.dar_project_drope.argtypes = [_P] * 10 + [_I] * 8 + [ctypes.c_float, _I] + [_P] * 9 + [
+            _SZ, _P]
+        L.dar_attn_prefill_drope.restype = _I
+        L.dar_attn_prefill_drope.argtypes = [_P] * 7 + [_I] * 7 + [_P, _P]
+        L.dar_cache_from_prefill_drope.restype = _I
+        L.dar_cache_from_prefill_drope.argtypes = [_P] * 4 + [_I] * 9 + [_P] * 5
+        L.dar_decode_append_drope.restype = _I
+        L.dar_decode_append_drope.argtypes = [_P] * 7 + [_I] * 9 + [ctypes.c_float, _I] + [
+            _P] * 7 + [_SZ, _P]
         L.dar_attn_decode_drope.restype = _I
         L.dar_attn_decode_drope.argtypes = [_P] * 8 + [_I] * 8 + [_I, _P, _P, _SZ, _P]
         L.dar_attn_decode_varlen.restype = _I
@@ -521,3 +533,91 @@ def dar_attn_decode_drope(qC, qR, K_win, V_win, KR, h_D, W_upK, W_upV, ctx_len: 
             d_down, int(w), _dtype_code(qC), _ptr(o)]
     _call_ws("dar_attn_decode_drope", lib().dar_attn_decode_drope, args, workspace, qC, stream)
     return o
+
+
+@_on_stream
+def dar_project_drope(h, W_down, W_up, W_Q, W_K, W_V, W_QR, W_KR, heads: int, d_k: int,
+                      W_upK=None, W_upV=None, pos0: int = 0, rope_base: float = 10000.0,
+                      out=None, workspace=None, stream=None):
+    """Projections of the decoupled-RoPE variant.  Returns dict QC, QR, K_loc,
+    V_loc, h_D, K_glob, V_glob, KR (fp16).  Weights column-major ([out, in]):
+    W_QR [heads*d_R, d], W_KR [d_R, d]."""
+    torch = _torch()
+    B, N, d = h.shape
+    d_down = W_down.shape[0]
+    d_R = W_KR.shape[0]
+    if out is None:
+        kw = dict(dtype=torch.float16, device=h.device)
+        out = dict(QC=torch.empty((B, heads, N, d_k), **kw),
+                   QR=torch.empty((B, heads, N, d_R), **kw),
+                   K_loc=torch.empty((B, heads, N, d_k), **kw),
+                   V_loc=torch.empty((B, heads, d_k, N), **kw),
+                   h_D=torch.empty((B, N, d_down), **kw),
+                   K_glob=torch.empty((B, heads, N, d_k), **kw),
+                   V_glob=torch.empty((B, heads, d_k, N), **kw),
+                   KR=torch.empty((B, N, d_R), **kw))
+    args = [_ptr(h), _ptr(W_down), _ptr(W_up), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_QR),
+            _ptr(W_KR), _ptr(W_upK), _ptr(W_upV), B, N, d, d_down, heads, d_k, d_R, int(pos0),
+            float(rope_base), _dtype_code(h)]
+    args += [_ptr(out[k]) for k in ("QC", "QR", "K_loc", "V_loc", "h_D", "K_glob", "V_glob", "KR")]
+    _call_ws("dar_project_drope", lib().dar_project_drope, args, workspace, h, stream)
+    return out
+
+
+@_on_stream
+def dar_attn_prefill_drope(P, w: int, o=None, stream=None):
+    """Attention of the variant from dar_project_drope's outputs P.  Returns
+    o [B, N, heads*d_k] (bf16)."""
+    torch = _torch()
+    B, H, N, d_k = P["QC"].shape
+    d_R = P["KR"].shape[2]
+    if o is None:
+        o = torch.empty((B, N, H * d_k), dtype=torch.bfloat16, device=P["QC"].device)
+    st = lib().dar_attn_prefill_drope(_ptr(P["QC"]), _ptr(P["QR"]), _ptr(P["K_loc"]),
+                                      _ptr(P["V_loc"]), _ptr(P["K_glob"]), _ptr(P["V_glob"]),
+                                      _ptr(P["KR"]), B, N, H, d_k, d_R, int(w),
+                                      _dtype_code(P["QC"]), _ptr(o), _stream(stream))
+    _check("dar_attn_prefill_drope", st)
+    return o
+
+
+@_on_stream
+def dar_cache_from_prefill_drope(P, w: int, cap: int = None, stream=None):
+    """The variant's decode cache from dar_project_drope's outputs P: returns
+    (h_D_cache [B, cap, d_down], K_win, V_win [B, heads, w, d_k] or None,
+    KR_cache [B, cap, d_R]), bf16."""
+    torch = _torch()
+    B, N, d_down = P["h_D"].shape
+    _, H, _, d_k = P["K_loc"].shape
+    d_R = P["KR"].shape[2]
+    cap = N if cap is None else cap
+    kw = dict(dtype=torch.bfloat16, device=P["h_D"].device)
+    L = torch.zeros((B, cap, d_down), **kw)
+    KRc = torch.zeros((B, cap, d_R), **kw)
+    Kw = torch.zeros((B, H, w, d_k), **kw) if w > 0 else None
+    Vw = torch.zeros((B, H, w, d_k), **kw) if w > 0 else None
+    st = lib().dar_cache_from_prefill_drope(
+        _ptr(P["h_D"]), _ptr(P["K_loc"]) if w > 0 else None, _ptr(P["V_loc"]) if w > 0 else None,
+        _ptr(P["KR"]), B, N, H, d_k, d_down, d_R, int(w), cap, DAR_BF16, _ptr(L),
+        _ptr(Kw) if w > 0 else None, _ptr(Vw) if w > 0 else None, _ptr(KRc), _stream(stream))
+    _check("dar_cache_from_prefill_drope", st)
+    return L, Kw, Vw, KRc
+
+
+@_on_stream
+def dar_decode_append_drope(h, W_down, W_Q, W_K, W_V, W_QR, W_KR, heads: int, d_k: int,
+                            pos: int, qC, qR, K_win, V_win, h_D, KR, rope_base: float = 10000.0,
+                            workspace=None, stream=None):
+    """The variant's token at position `pos` of every sequence into its cache.
+    h [B, d]; weights column-major.  Returns (qC, qR)."""
+    B, d = h.shape
+    d_down = W_down.shape[0]
+    d_R = W_KR.shape[0]
+    w = K_win.shape[2] if K_win is not None else 0
+    cap = h_D.shape[1]
+    args = [_ptr(h), _ptr(W_down), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_QR), _ptr(W_KR), B, d,
+            d_down, heads, d_k, d_R, int(pos), int(w), cap, float(rope_base), _dtype_code(h),
+            _ptr(qC), _ptr(qR), _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None,
+            _ptr(h_D), _ptr(KR)]
+    _call_ws("dar_decode_append_drope", lib().dar_decode_append_drope, args, workspace, h, stream)
+    return qC, qR

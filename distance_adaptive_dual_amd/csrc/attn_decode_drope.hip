@@ -520,7 +520,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool drope_decode_supported(int d_k, int d_R, int d_down) {
-  return ((d_k == 64 && d_R == 32) || (d_k == 128 && d_R == 64)) &&
+  return (d_k == 64 || d_k == 128) && d_R == 64 &&
          (d_down == 128 || d_down == 256 || d_down == 512);
 }
 
@@ -544,17 +544,17 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) 
   const dim3 ga(p.H, (g.qw + 63) / 64, (p.B + 3) / 4);
   const int n_stream = p.B * g.n_hg * g.n_chunks;
   if (p.d_k == 64) {
-    hipLaunchKernelGGL((drope_absorb<64, 32>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
+    hipLaunchKernelGGL((drope_absorb<64, 64>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
     if (p.d_down == 128)
-      hipLaunchKernelGGL((drope_stream<64, 128, 32, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
+      hipLaunchKernelGGL((drope_stream<64, 128, 64, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
                          0, s, p, g, qa_hi, qa_lo, part_lat);
     else if (p.d_down == 256)
-      hipLaunchKernelGGL((drope_stream<64, 256, 32, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
+      hipLaunchKernelGGL((drope_stream<64, 256, 64, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
                          0, s, p, g, qa_hi, qa_lo, part_lat);
     else
-      hipLaunchKernelGGL((drope_stream<64, 512, 32, 2>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
+      hipLaunchKernelGGL((drope_stream<64, 512, 64, 2>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
                          p, g, qa_hi, qa_lo, part_lat);
-    hipLaunchKernelGGL((drope_window<64, 32>), dim3(p.B * p.H * g.n_win), dim3(256), 0, s, p, g,
+    hipLaunchKernelGGL((drope_window<64, 64>), dim3(p.B * p.H * g.n_win), dim3(256), 0, s, p, g,
                        part_win);
   } else {
     hipLaunchKernelGGL((drope_absorb<128, 64>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);

@@ -50,20 +50,27 @@ __device__ __forceinline__ constexpr int key_off(int kb, int r) {
   return 32 * kb + 16 * (r >> 3) + (r & 7);
 }
 
-template <int D>
+// DR > 0 (the decoupled-RoPE variant): a key row holds the content part
+// (D) followed by the shared rotary key (DR); values stay D wide.
+template <int D, int DR = 0>
 struct PassSmem {
-  static constexpr int KP = D + 8;   // fp16 per K row (16 B pad: 4-bank shift per row)
+  static constexpr int DQ = D + DR;
+  static constexpr int KP = DQ + 8;  // fp16 per K row (16 B pad: 4-bank shift per row)
   static constexpr int VP = KT + 8;  // fp16 per V^T row
   f16 k[2][KT * KP];                 // [buffer][key][d]
   f16 v[2][D * VP];                  // [buffer][d][key]
 };
 
-// Register staging of one pass: a key tile of one source (K [KT x D] and
-// V^T [D x KT]), 16-byte chunks spread over the 256 threads.
-template <int D>
+// Register staging of one pass: a key tile of one source (K [KT x (D + DR)]
+// and V^T [D x KT]), 16-byte chunks spread over the 256 threads.
+template <int D, int DR = 0>
 struct Stage {
-  static constexpr int NCH = KT * D / 8 / 256;
-  u32x4 k[NCH], v[NCH];
+  static constexpr int NCH = KT * D / 8 / 256;         // V chunks per thread
+  static constexpr int NCK = KT * (D + DR) / 8 / 256;  // K chunks per thread
+  typedef u32x4 KArr[NCK];
+  typedef u32x4 VArr[NCH];
+  KArr k;
+  VArr v;
 };
 
 // One 16-byte chunk of K row j (fp16 [N x D] rows, j may lie outside [0, N)):
@@ -84,16 +91,32 @@ __device__ __forceinline__ u32x4 load_k_chunk(const f16* K, int N, int j, int co
 // K and Vt hold positions base .. base+N-1 of one (batch, head) (K [N x D],
 // Vt [D x N]); j0 = first position of the tile - base, which may be negative
 // for the local arrays of a chunk: rows outside [0, N) read as zeros.
-template <int D>
-__device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16* Vt, int N, int j0,
-                                          bool vec_ok) {
+// One 16-byte chunk of a staged key row: the content part from K, the
+// rotary part (DR > 0) from KR, the rows of the same positions.
+template <int D, int DR>
+__device__ __forceinline__ u32x4 load_key_chunk(const f16* K, const f16* KR, int N, int j,
+                                                int col) {
+  if constexpr (DR > 0) {
+    if (col >= D) return load_k_chunk<DR>(KR, N, j, col - D);
+  }
+  return load_k_chunk<D>(K, N, j, col);
+}
+
+template <int D, int DR = 0>
+__device__ __forceinline__ void load_pass(Stage<D, DR>& st, const f16* K, const f16* Vt, int N,
+                                          int j0, bool vec_ok, const f16* KR = nullptr) {
+  constexpr int DQ = D + DR;
   const int tid = threadIdx.x;
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
+  for (int i = 0; i < Stage<D, DR>::NCK; ++i) {
     const int c = tid + 256 * i;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    st.k[i] = load_k_chunk<D>(K, N, j0 + row, col);
+    const int row = c / (DQ / 8), col = (c % (DQ / 8)) * 8;
+    st.k[i] = load_key_chunk<D, DR>(K, KR, N, j0 + row, col);
+  }
+#pragma unroll
+  for (int i = 0; i < Stage<D, DR>::NCH; ++i) {
+    const int c = tid + 256 * i;
     const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
     if (vec_ok) {
       st.v[i] = *(const u32x4*)(Vt + (size_t)d * N + j0 + kc);
@@ -114,24 +137,25 @@ __device__ __forceinline__ void load_pass(Stage<D>& st, const f16* K, const f16*
 
 // The two halves of load_pass / store_pass, for staging K and V at different
 // times of a pass.
-template <int D>
-__device__ __forceinline__ void load_k(u32x4 (&k)[Stage<D>::NCH], const f16* K, int N, int j0) {
+template <int D, int DR = 0>
+__device__ __forceinline__ void load_k(typename Stage<D, DR>::KArr& k, const f16* K, int N,
+                                       int j0, const f16* KR = nullptr) {
+  constexpr int DQ = D + DR;
   const int tid = threadIdx.x;
-  const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
+  for (int i = 0; i < Stage<D, DR>::NCK; ++i) {
     const int c = tid + 256 * i;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    k[i] = load_k_chunk<D>(K, N, j0 + row, col);
+    const int row = c / (DQ / 8), col = (c % (DQ / 8)) * 8;
+    k[i] = load_key_chunk<D, DR>(K, KR, N, j0 + row, col);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void load_v(u32x4 (&v)[Stage<D>::NCH], const f16* Vt, int N, int j0,
-                                       bool vec_ok) {
+template <int D, int DR = 0>
+__device__ __forceinline__ void load_v(typename Stage<D, DR>::VArr& v, const f16* Vt, int N,
+                                       int j0, bool vec_ok) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
+  for (int i = 0; i < Stage<D, DR>::NCH; ++i) {
     const int c = tid + 256 * i;
     const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
     if (vec_ok) {
@@ -151,69 +175,62 @@ __device__ __forceinline__ void load_v(u32x4 (&v)[Stage<D>::NCH], const f16* Vt,
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_k(const u32x4 (&k)[Stage<D>::NCH], f16* sk) {
-  constexpr int KP = PassSmem<D>::KP;
+template <int D, int DR = 0>
+__device__ __forceinline__ void store_k(const typename Stage<D, DR>::KArr& k, f16* sk) {
+  constexpr int KP = PassSmem<D, DR>::KP, DQ = D + DR;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
+  for (int i = 0; i < Stage<D, DR>::NCK; ++i) {
     const int c = tid + 256 * i;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    const int row = c / (DQ / 8), col = (c % (DQ / 8)) * 8;
     *(u32x4*)(sk + row * KP + col) = k[i];
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_v(const u32x4 (&v)[Stage<D>::NCH], f16* sv) {
-  constexpr int VP = PassSmem<D>::VP;
+template <int D, int DR = 0>
+__device__ __forceinline__ void store_v(const typename Stage<D, DR>::VArr& v, f16* sv) {
+  constexpr int VP = PassSmem<D, DR>::VP;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
+  for (int i = 0; i < Stage<D, DR>::NCH; ++i) {
     const int c = tid + 256 * i;
     const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
     *(u32x4*)(sv + d * VP + kc) = v[i];
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_pass(const Stage<D>& st, f16* sk, f16* sv) {
-  constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    *(u32x4*)(sk + row * KP + col) = st.k[i];
-    const int d = c / (KT / 8), kc = (c % (KT / 8)) * 8;
-    *(u32x4*)(sv + d * VP + kc) = st.v[i];
-  }
+template <int D, int DR = 0>
+__device__ __forceinline__ void store_pass(const Stage<D, DR>& st, f16* sk, f16* sv) {
+  store_k<D, DR>(st.k, sk);
+  store_v<D, DR>(st.v, sv);
 }
 
 // K fragments of a staged key tile for S^T = K Q^T: kf[kb][st] holds rows
 // 32 kb + key_perm(lr) (keys j0 + ...) and dims 16 st + 8 lg .. +8.
-template <int D>
-__device__ __forceinline__ void read_kfrags(const f16* sk, f16x8 (&kf)[2][D / 16], int lr, int lg) {
-  constexpr int KP = PassSmem<D>::KP;
+template <int D, int DR = 0>
+__device__ __forceinline__ void read_kfrags(const f16* sk, f16x8 (&kf)[2][(D + DR) / 16], int lr,
+                                            int lg) {
+  constexpr int KP = PassSmem<D, DR>::KP;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) kf[kb][st] = *(const f16x8*)(base + 16 * st);
+    for (int st = 0; st < (D + DR) / 16; ++st) kf[kb][st] = *(const f16x8*)(base + 16 * st);
   }
 }
 
 // S^T = K Q^T: s[kb][r] is key j0 + 8 lg + key_off(kb, r) of this lane's
 // query.  The two 32-key blocks' accumulation chains are interleaved so that
 // no MFMA waits on the result of the one just issued.
-template <int D>
-__device__ __forceinline__ void mfma_scores(const f16x8 (&kf)[2][D / 16], const f16x8 (&qf)[D / 16],
-                                            f32x16 (&s)[2]) {
+template <int D, int DR = 0>
+__device__ __forceinline__ void mfma_scores(const f16x8 (&kf)[2][(D + DR) / 16],
+                                            const f16x8 (&qf)[(D + DR) / 16], f32x16 (&s)[2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st)
+  for (int st = 0; st < (D + DR) / 16; ++st)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[kb][st], qf[st], s[kb]);
 }
@@ -311,15 +328,15 @@ __device__ __forceinline__ void exp_and_pv(const f16* sv, const f32x16 (&s)[2],
 
 // One whole pass of one wave: scores against the staged tile, the keep mask,
 // online softmax, and O^T += V^T P^T.
-template <int D>
-__device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv, const f16x8 (&qf)[D / 16],
-                                          f32x16 (&o)[D / 32], float& m_ref, float& l_run,
-                                          bool masked, int keep_lo, int keep_hi, float sc,
-                                          int lr, int lg) {
-  f16x8 kf[2][D / 16];
-  read_kfrags<D>(sk, kf, lr, lg);
+template <int D, int DR = 0>
+__device__ __forceinline__ void wave_pass(const f16* sk, const f16* sv,
+                                          const f16x8 (&qf)[(D + DR) / 16], f32x16 (&o)[D / 32],
+                                          float& m_ref, float& l_run, bool masked, int keep_lo,
+                                          int keep_hi, float sc, int lr, int lg) {
+  f16x8 kf[2][(D + DR) / 16];
+  read_kfrags<D, DR>(sk, kf, lr, lg);
   f32x16 s[2];
-  mfma_scores<D>(kf, qf, s);
+  mfma_scores<D, DR>(kf, qf, s);
   mask_and_max<D>(s, o, m_ref, l_run, masked, keep_lo, keep_hi, sc);
   exp_and_pv<D>(sv, s, o, m_ref, l_run, sc, lr, lg);
 }
@@ -350,24 +367,24 @@ __device__ __forceinline__ void exp_half(const f32x16& s, float sc, float m, f16
 // keeps only half the score, K and V fragment registers live at a time, which
 // fits four waves per SIMD; the reference maximum may move between the halves
 // (same rule as a whole pass).
-template <int D>
+template <int D, int DR = 0>
 __device__ __forceinline__ void wave_half(int kb, const f16* sk, const f16* sv,
-                                          const f16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+                                          const f16x8 (&qf)[(D + DR) / 16], f32x16 (&o)[D / 32],
                                           float& m_ref, float& l_run, bool masked, int keep_lo,
                                           int keep_hi, float sc, int lr, int lg) {
-  constexpr int KP = PassSmem<D>::KP, VP = PassSmem<D>::VP;
+  constexpr int KP = PassSmem<D, DR>::KP, VP = PassSmem<D, DR>::VP, NQ = (D + DR) / 16;
   {
-    f16x8 kf[D / 16];
+    f16x8 kf[NQ];
     {
       const f16* base = sk + (32 * kb + key_perm(lr)) * KP + 8 * lg;
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
+      for (int st = 0; st < NQ; ++st) kf[st] = *(const f16x8*)(base + 16 * st);
     }
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) s = mfma32x32x16(kf[st], qf[st], s);
+    for (int st = 0; st < NQ; ++st) s = mfma32x32x16(kf[st], qf[st], s);
     if (masked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -442,10 +459,15 @@ __device__ __forceinline__ WavePass wave_pass_info(int j0, int src, int qw0, int
 // CHUNK: queries start at p.q0 and the local arrays at p.loc0 (a prefill
 // chunk); otherwise both are 0 and compiled in as constants.  LSE: also store
 // each query's log-sum-exp in p.lse (whole prefills only).
-template <int D, bool CHUNK, bool LSE>
-__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(PrefillProblem p, int nQT, int nPair,
-                                                          int remap, int paired) {
-  __shared__ PassSmem<D> sm;
+// DR > 0: the decoupled-RoPE variant (whole prefill only): every key row is
+// [content ; shared rotary key] and every query [content ; rotary], so the
+// score MFMA chain runs over D + DR; values and the output stay D wide.
+template <int D, bool CHUNK, bool LSE, int DR = 0>
+__global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefill_f16(
+    PrefillProblem p, int nQT, int nPair, int remap, int paired) {
+  static_assert(DR == 0 || !CHUNK, "the rotary part covers whole prefills");
+  constexpr int NQ = (D + DR) / 16;  // 16-wide steps of the score contraction
+  __shared__ PassSmem<D, DR> sm;
   const int N = p.N, H = p.H, BH = p.B * p.H, w = p.w;
   // paired: a workgroup takes query tile nQT-1-pr and then tile pr, so every
   // workgroup streams about the same number of key tiles.  Unpaired: one
@@ -478,6 +500,9 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
   const f16* Kl = (const f16*)p.K_loc + (size_t)bh * nloc * D;
   const f16* Vg = (const f16*)p.V_glob + (size_t)bh * N * D;
   const f16* Vl = (const f16*)p.V_loc + (size_t)bh * nloc * D;
+  // rotary keys of sequence b (positions 0 .. N-1, every head) and queries
+  const f16* KRb = DR > 0 ? (const f16*)p.KR + (size_t)b * N * DR : nullptr;
+  const f16* QRp = DR > 0 ? (const f16*)p.QR + (size_t)bh * N * DR : nullptr;
   // array, length, relative tile start and 16-byte V loads for source s at j0
   auto src_len = [&](int s) { return s ? nloc : N; };
   auto src_rel = [&](int s, int j0) { return s ? j0 - loc0 : j0; };
@@ -489,7 +514,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lg = lane >> 5;
-  const float sc = kLog2e / sqrtf((float)D);
+  const float sc = kLog2e / sqrtf((float)(D + DR));
   const int q_hi = nQT - 1 - pr;
   const int nq = (!paired || q_hi == pr) ? 1 : 2;
 
@@ -501,12 +526,18 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     const int i_last = min(i0 + QT - 1, N - 1);
     const int wi_last = min(qw0 + 31, N - 1);
 
-    f16x8 qf[D / 16];
+    f16x8 qf[NQ];
     {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
         u32x4 v = (qi < N) ? *(const u32x4*)(Qp + (size_t)(qi - q0) * D + 16 * st + 8 * lg) : z;
+        qf[st] = __builtin_bit_cast(f16x8, v);
+      }
+#pragma unroll
+      for (int st = D / 16; st < NQ; ++st) {
+        u32x4 v = (qi < N) ? *(const u32x4*)(QRp + (size_t)qi * DR + 16 * (st - D / 16) + 8 * lg)
+                           : z;
         qf[st] = __builtin_bit_cast(f16x8, v);
       }
     }
@@ -523,10 +554,10 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
     auto need_glob = [&](int j0) { return i_last - j0 >= w; };
     auto need_loc = [&](int j0) { return w > 0 && max(i0 - (j0 + KT - 1), 0) < w; };
     int j0 = 0, src = need_glob(0) ? 0 : 1;  // src 0 = global, 1 = local
-    Stage<D> stg;
-    load_pass<D>(stg, src ? Kl : Kg, src ? Vl : Vg, src_len(src), src_rel(src, j0),
-                 src_vec(src, j0));
-    store_pass<D>(stg, sm.k[0], sm.v[0]);
+    Stage<D, DR> stg;
+    load_pass<D, DR>(stg, src ? Kl : Kg, src ? Vl : Vg, src_len(src), src_rel(src, j0),
+                     src_vec(src, j0), KRb);
+    store_pass<D, DR>(stg, sm.k[0], sm.v[0]);
     __syncthreads();
     int buf = 0;
     while (true) {
@@ -543,33 +574,34 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void attn_prefill_f16(Prefill
         // K is fetched then and stored at the end (its LDS buffer is free
         // for the whole pass), so only one of the two is held in registers.
         if (has_next)
-          load_v<D>(stg.v, nsrc ? Vl : Vg, src_len(nsrc), src_rel(nsrc, nj0), src_vec(nsrc, nj0));
+          load_v<D, DR>(stg.v, nsrc ? Vl : Vg, src_len(nsrc), src_rel(nsrc, nj0),
+                        src_vec(nsrc, nj0));
       } else {
         if (has_next)
-          load_pass<D>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, src_len(nsrc), src_rel(nsrc, nj0),
-                       src_vec(nsrc, nj0));
+          load_pass<D, DR>(stg, nsrc ? Kl : Kg, nsrc ? Vl : Vg, src_len(nsrc), src_rel(nsrc, nj0),
+                           src_vec(nsrc, nj0), KRb);
       }
 
       const WavePass wp = wave_pass_info(j0, src, qw0, wi_last, qi, lg, N, w);
       if constexpr (D == 64) {
         if (wp.part)
-          wave_half<D>(0, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
-                       wp.keep_hi, sc, lr, lg);
+          wave_half<D, DR>(0, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
+                           wp.keep_hi, sc, lr, lg);
         if (has_next) {
-          store_v<D>(stg.v, sm.v[buf ^ 1]);
-          load_k<D>(stg.k, nsrc ? Kl : Kg, src_len(nsrc), src_rel(nsrc, nj0));
+          store_v<D, DR>(stg.v, sm.v[buf ^ 1]);
+          load_k<D, DR>(stg.k, nsrc ? Kl : Kg, src_len(nsrc), src_rel(nsrc, nj0), KRb);
         }
         if (wp.part)
-          wave_half<D>(1, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
-                       wp.keep_hi, sc, lr, lg);
+          wave_half<D, DR>(1, sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
+                           wp.keep_hi, sc, lr, lg);
         if (!has_next) break;
-        store_k<D>(stg.k, sm.k[buf ^ 1]);
+        store_k<D, DR>(stg.k, sm.k[buf ^ 1]);
       } else {
         if (wp.part)
-          wave_pass<D>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
-                       wp.keep_hi, sc, lr, lg);
+          wave_pass<D, DR>(sm.k[buf], sm.v[buf], qf, o, m_ref, l_run, wp.masked, wp.keep_lo,
+                           wp.keep_hi, sc, lr, lg);
         if (!has_next) break;
-        store_pass<D>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
+        store_pass<D, DR>(stg, sm.k[buf ^ 1], sm.v[buf ^ 1]);
       }
       __syncthreads();
       buf ^= 1;
@@ -694,6 +726,16 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
                      paired)
     if (chunk && p.lse != nullptr) return hipErrorInvalidValue;
     const bool lse = p.lse != nullptr;
+    if (p.d_R > 0) {  // decoupled-RoPE variant: whole prefill, d_R = 64
+      if (chunk || lse || p.d_R != 64) return hipErrorInvalidValue;
+      if (p.d_k == 64)
+        hipLaunchKernelGGL((attn_prefill_f16<64, false, false, 64>), grid, dim3(256), 0, s, p, nQT,
+                           nPair, remap, paired);
+      else
+        hipLaunchKernelGGL((attn_prefill_f16<128, false, false, 64>), grid, dim3(256), 0, s, p,
+                           nQT, nPair, remap, paired);
+      return hipGetLastError();
+    }
     if (p.d_k == 64) {
       if (chunk) DAR_ATTN(64, true, false);
       else if (lse) DAR_ATTN(64, false, true);

@@ -745,6 +745,249 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
                           d_k, d_down, w, rope_base, dtype, o, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- decoupled RoPE
+static bool drope_shape_ok(int d_k, int d_R) { return (d_k == 64 || d_k == 128) && d_R == 64; }
+
+dar_status dar_project_drope(const void* h, const void* W_down, const void* W_up, const void* W_Q,
+                             const void* W_K, const void* W_V, const void* W_QR, const void* W_KR,
+                             const void* W_upK, const void* W_upV, int B, int N, int d,
+                             int d_down, int heads, int d_k, int d_R, int pos0, float rope_base,
+                             dar_dtype dtype, void* QC, void* QR, void* K_loc, void* V_loc,
+                             void* h_D, void* K_glob, void* V_glob, void* KR, void* workspace,
+                             size_t* workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_R < 2 ||
+      (d_R & 1) || pos0 < 0 || !(rope_base > 1.0f) || (long)pos0 + N - 1 > 0x7fffffffL)
+    return DAR_ERR_INVALID_ARG;
+  const bool have_fold = (W_upK != nullptr) || (W_upV != nullptr);
+  if (have_fold && (!aligned16(W_upK) || !aligned16(W_upV))) return DAR_ERR_INVALID_ARG;
+  if (!have_fold && !aligned16(W_up)) return DAR_ERR_INVALID_ARG;
+  const void* need[] = {h, W_down, W_Q, W_K, W_V, W_QR, W_KR, QC, QR, K_loc, V_loc, h_D,
+                        K_glob, V_glob, KR};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k, hr = (size_t)heads * d_R, M = (size_t)B * N;
+  const size_t es = elem_size(dtype);
+  const Span ins[10] = {{h, es * M * d},         {W_down, es * d * d_down},
+                        {W_Q, es * d * hd},      {W_K, es * d * hd},
+                        {W_V, es * d * hd},      {W_QR, es * d * hr},
+                        {W_KR, es * d * d_R},    {have_fold ? nullptr : W_up, es * d_down * d},
+                        {W_upK, es * d_down * hd}, {W_upV, es * d_down * hd}};
+  const Span outs[8] = {{QC, es * M * hd},     {QR, es * M * hr},     {K_loc, es * M * hd},
+                        {V_loc, es * M * hd},  {h_D, es * M * d_down}, {K_glob, es * M * hd},
+                        {V_glob, es * M * hd}, {KR, es * M * d_R}};
+  if (!disjoint(outs, 8, ins, 10)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!drope_shape_ok(d_k, d_R) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
+    return DAR_ERR_UNSUPPORTED;
+  const long max_pos = (long)pos0 + N - 1;
+  const size_t rope_bytes = rope_table_bytes(d_R, max_pos);
+  const size_t fold_bytes = have_fold ? 0 : 2 * round256(es * d_down * hd);
+  const size_t need_bytes = rope_bytes + fold_bytes;
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& x : ins)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+    for (const Span& x : outs)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+  }
+  char* wsp = (char*)workspace;
+  float2* lo = (float2*)wsp;
+  float2* hi = lo + 64 * (d_R / 2);
+  hipError_t e = launch_rope_tables(lo, hi, d_R, max_pos, rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  const void* fK = W_upK;
+  const void* fV = W_upV;
+  if (!have_fold) {
+    void* k_out = wsp + rope_bytes;
+    void* v_out = wsp + rope_bytes + round256(es * d_down * hd);
+    e = launch_fold(W_up, W_K, k_out, d, d_down, (int)hd, dtype, stream);
+    if (e == hipSuccess) e = launch_fold(W_up, W_V, v_out, d, d_down, (int)hd, dtype, stream);
+    if (e != hipSuccess) return DAR_ERR_HIP;
+    fK = k_out;
+    fV = v_out;
+  }
+  const RopeTab rope{lo, hi, d_R / 2};
+  // content parts, values and the latent (no rotation)
+  GemmProblem g1{};
+  g1.A = h;
+  g1.M = (int)M;
+  g1.K = d;
+  g1.a_type = kBF16;
+  g1.b_type = kBF16;
+  g1.out_type = kF16;
+  g1.nseg = 4;
+  g1.seg[0] = GemmSeg{W_Q, QC, (int)hd, kHead, 0};
+  g1.seg[1] = GemmSeg{W_K, K_loc, (int)hd, kHead, 0};
+  g1.seg[2] = GemmSeg{W_V, V_loc, (int)hd, kHeadT, 0};
+  g1.seg[3] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0};
+  g1.n_seq = N;
+  g1.heads = heads;
+  g1.d_k = d_k;
+  g1.pos0 = pos0;
+  g1.rope = rope;
+  e = launch_project_gemm(g1, dtype, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  // rotary parts: the heads' queries and the one shared key
+  GemmProblem gr = g1;
+  gr.nseg = 2;
+  gr.d_k = d_R;
+  gr.seg[0] = GemmSeg{W_QR, QR, (int)hr, kHead, 1};
+  gr.seg[1] = GemmSeg{W_KR, KR, d_R, kHead, 1};
+  gr.seg[1].heads = 1;
+  e = launch_project_gemm(gr, dtype, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  // global content keys and values from h^D through the folded weights
+  GemmProblem g2 = g1;
+  g2.A = h_D;
+  g2.K = d_down;
+  g2.a_type = kF16;
+  g2.nseg = 2;
+  g2.seg[0] = GemmSeg{fK, K_glob, (int)hd, kHead, 0};
+  g2.seg[1] = GemmSeg{fV, V_glob, (int)hd, kHeadT, 0};
+  return hip_status(launch_project_gemm(g2, dtype, stream));
+}
+
+dar_status dar_attn_prefill_drope(const void* QC, const void* QR, const void* K_loc,
+                                  const void* V_loc, const void* K_glob, const void* V_glob,
+                                  const void* KR, int B, int N, int heads, int d_k, int d_R, int w,
+                                  dar_dtype dtype, void* o, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_R < 2 || (d_R & 1) || w < 0)
+    return DAR_ERR_INVALID_ARG;
+  const void* need[] = {QC, QR, K_loc, V_loc, K_glob, V_glob, KR, o};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype), n = (size_t)B * N * heads;
+  const Span ins[7] = {{QC, es * n * d_k},     {QR, es * n * d_R},     {K_loc, es * n * d_k},
+                       {V_loc, es * n * d_k},  {K_glob, es * n * d_k}, {V_glob, es * n * d_k},
+                       {KR, es * (size_t)B * N * d_R}};
+  const Span outs[1] = {{o, es * n * d_k}};
+  if (!disjoint(outs, 1, ins, 7)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!drope_shape_ok(d_k, d_R)) return DAR_ERR_UNSUPPORTED;
+  if (n * (d_k + d_R) > 0x7fffffffffffL) return DAR_ERR_UNSUPPORTED;
+  PrefillProblem p{QC, K_loc, V_loc, K_glob, V_glob, o, B, N, heads, d_k, w};
+  p.QR = QR;
+  p.KR = KR;
+  p.d_R = d_R;
+  return hip_status(launch_attn_prefill(p, dtype, stream));
+}
+
+dar_status dar_decode_append_drope(const void* h, const void* W_down, const void* W_Q,
+                                   const void* W_K, const void* W_V, const void* W_QR,
+                                   const void* W_KR, int B, int d, int d_down, int heads, int d_k,
+                                   int d_R, int pos, int w, int cap, float rope_base,
+                                   dar_dtype dtype, void* qC, void* qR, void* K_win, void* V_win,
+                                   void* h_D, void* KR, void* workspace, size_t* workspace_bytes,
+                                   hipStream_t stream) {
+  if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || d_R < 2 || (d_R & 1) ||
+      pos < 0 || w < 0 || cap < 1 || pos >= cap || !(rope_base > 1.0f))
+    return DAR_ERR_INVALID_ARG;
+  const void* need[] = {h, W_down, W_Q, W_K, W_V, W_QR, W_KR, qC, qR, h_D, KR};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_win) || !aligned16(V_win))) return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k, hr = (size_t)heads * d_R, es = elem_size(dtype);
+  const Span ins[7] = {{h, es * B * (size_t)d},  {W_down, es * d * (size_t)d_down},
+                       {W_Q, es * d * hd},       {W_K, es * d * hd},
+                       {W_V, es * d * hd},       {W_QR, es * d * hr},
+                       {W_KR, es * d * (size_t)d_R}};
+  const Span outs[6] = {{qC, es * B * hd},
+                        {qR, es * B * hr},
+                        {K_win, w > 0 ? es * B * hd * w : 0},
+                        {V_win, w > 0 ? es * B * hd * w : 0},
+                        {h_D, es * B * (size_t)cap * d_down},
+                        {KR, es * B * (size_t)cap * d_R}};
+  if (!disjoint(outs, 6, ins, 7)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!drope_shape_ok(d_k, d_R) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
+    return DAR_ERR_UNSUPPORTED;
+  const size_t need_bytes = rope_table_bytes(d_R, pos);
+  if (workspace == nullptr) {
+    *workspace_bytes = need_bytes;
+    return DAR_OK;
+  }
+  if (((uintptr_t)workspace & 255u) != 0) return DAR_ERR_INVALID_ARG;
+  if (*workspace_bytes < need_bytes) return DAR_ERR_WORKSPACE;
+  {
+    const Span ws{workspace, need_bytes};
+    for (const Span& x : ins)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+    for (const Span& x : outs)
+      if (overlap(ws, x)) return DAR_ERR_INVALID_ARG;
+  }
+  float2* lo = (float2*)workspace;
+  float2* hi = lo + 64 * (d_R / 2);
+  hipError_t e = launch_rope_tables(lo, hi, d_R, pos, rope_base, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  GemmProblem g{};
+  g.A = h;
+  g.M = B;
+  g.K = d;
+  g.a_type = kBF16;
+  g.b_type = kBF16;
+  g.out_type = kBF16;
+  g.n_seq = 1;
+  g.heads = heads;
+  g.d_k = d_k;
+  g.pos0 = pos;
+  g.rope = RopeTab{lo, hi, d_R / 2};
+  g.pos_max = pos;
+  int ns = 0;
+  g.seg[ns++] = GemmSeg{W_Q, qC, (int)hd, kHead, 0, 1, 0, kPosFixed};
+  if (w > 0) {
+    g.seg[ns++] = GemmSeg{W_K, K_win, (int)hd, kHead, 0, w, pos % w, kPosRing};
+    g.seg[ns++] = GemmSeg{W_V, V_win, (int)hd, kHead, 0, w, pos % w, kPosRing};
+  }
+  g.seg[ns++] = GemmSeg{W_down, h_D, d_down, kRowMajor, 0, cap, pos, kPosRow};
+  g.nseg = ns;
+  e = launch_project_gemm(g, dtype, stream);
+  if (e != hipSuccess) return DAR_ERR_HIP;
+  GemmProblem gr = g;
+  gr.d_k = d_R;
+  gr.nseg = 2;
+  gr.seg[0] = GemmSeg{W_QR, qR, (int)hr, kHead, 1, 1, 0, kPosFixed};
+  gr.seg[1] = GemmSeg{W_KR, KR, d_R, kHead, 1, cap, pos, kPosRow};
+  gr.seg[1].heads = 1;
+  return hip_status(launch_project_gemm(gr, dtype, stream));
+}
+
+dar_status dar_cache_from_prefill_drope(const void* h_D, const void* K_loc, const void* V_loc,
+                                        const void* KR, int B, int N, int heads, int d_k,
+                                        int d_down, int d_R, int w, int cap, dar_dtype dtype,
+                                        void* h_D_cache, void* K_win, void* V_win, void* KR_cache,
+                                        hipStream_t stream) {
+  if (!dtype_ok(dtype) || B < 1 || N < 1 || cap < N || d_R < 2 || (d_R & 1))
+    return DAR_ERR_INVALID_ARG;
+  if (!aligned16(KR) || !aligned16(KR_cache)) return DAR_ERR_INVALID_ARG;
+  const Span kr_in{KR, 2 * (size_t)B * N * d_R}, kr_out{KR_cache, 2 * (size_t)B * cap * d_R};
+  const Span others[5] = {{h_D, 2 * (size_t)B * N * d_down},
+                          {h_D_cache, 2 * (size_t)B * cap * d_down},
+                          {w > 0 ? K_win : nullptr, 2 * (size_t)B * w * heads * d_k},
+                          {w > 0 ? V_win : nullptr, 2 * (size_t)B * w * heads * d_k},
+                          {w > 0 ? K_loc : nullptr, 2 * (size_t)B * N * heads * d_k}};
+  if (overlap(kr_in, kr_out)) return DAR_ERR_INVALID_ARG;
+  for (const Span& x : others)
+    if (overlap(kr_out, x) || overlap(kr_in, x)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!drope_shape_ok(d_k, d_R)) return DAR_ERR_UNSUPPORTED;
+  // the latent rows and the ring: as for the exact method (content keys)
+  const dar_status st = cache_from_prefill_impl(h_D, K_loc, V_loc, B, N, nullptr, heads, d_k,
+                                                d_down, w, cap, dtype, h_D_cache, K_win, V_win,
+                                                stream);
+  if (st != DAR_OK) return st;
+  // rotary keys of every position, like the latent rows
+  return hip_status(launch_latent_cast(KR, B, N, d_R, cap, 0, KR_cache, stream));
+}
+
 dar_status dar_attn_decode_drope(const void* qC, const void* qR, const void* K_win,
                                  const void* V_win, const void* KR, const void* h_D,
                                  const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,

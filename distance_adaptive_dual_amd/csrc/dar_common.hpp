@@ -154,6 +154,10 @@ struct GemmSeg {
   // kRowMajor only: 1 applies the logistic sigmoid to the fp32 result before
   // it is rounded and stored (the sigmoid-bottleneck variant of h^D)
   int act = 0;
+  // kHead / kHeadT: heads of this segment's output ([B, heads, ...]); 0 means
+  // GemmProblem::heads.  A one-head segment writes [B, ld, d] (the shared
+  // rotary key of the decoupled-RoPE variant).
+  int heads = 0;
 };
 enum PosMode : int { kPosFixed = 0, kPosRow = 1, kPosRing = 2 };
 
@@ -194,6 +198,12 @@ struct PrefillProblem {
   // Optional [B, H, N] fp32 output (whole prefill only): the natural-log
   // log-sum-exp of each query's scaled scores, log sum_j exp(q_i . k_j / sqrt(d_k)).
   float* lse = nullptr;
+  // Decoupled-RoPE variant (whole prefill, bf16): rotary queries QR
+  // [B, H, N, d_R] and the shared rotary keys KR [B, N, d_R] extend every
+  // score, s = (q . k + qR . kR) / sqrt(d_k + d_R); d_R = 0 otherwise.
+  const void* QR = nullptr;
+  const void* KR = nullptr;
+  int d_R = 0;
 };
 hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s);
 

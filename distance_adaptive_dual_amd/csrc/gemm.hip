@@ -95,7 +95,7 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
   constexpr int TPR = 256 / ROWS;  // threads per tile row
   constexpr int CPT = BN / TPR;    // columns per thread
   const int tid = threadIdx.x;
-  const int M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
   OutT* out = (OutT*)seg.out;
   if (seg.kind == kHeadT) {
     // out[b, head, t, n]: thread = (column c, run of ROWS/2 rows)
@@ -235,7 +235,7 @@ __device__ __forceinline__ void rope_cs8(const RopeTab& t, int pos, int t0, floa
 template <typename OutT, int D, bool RP>
 __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, int hf, int col0,
                                                  const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
   const int ld = seg.ld_seq ? seg.ld_seq : Nq;
   OutT* out = (OutT*)seg.out;
   // chunk q = tid + 256 k: column chunk (q & 7) + 8 (q >> 10), tile row (q >> 3) & 127;
@@ -275,7 +275,7 @@ template <typename OutT, int D, bool RP>
 __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int hf, int col0,
                                                 const GemmSeg& seg, const GemmProblem& p) {
   constexpr int HALF = D / 2, PCH = D / 16;  // pair chunks of 8 per head
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
   const int ld = seg.ld_seq ? seg.ld_seq : Nq;
   OutT* out = (OutT*)seg.out;
   const int w8 = tid & 7, r0 = 4 * (tid >> 3);
@@ -333,7 +333,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
 template <typename OutT, int D, int TP>
 __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, int col0,
                                            const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = p.heads, Nq = p.n_seq;
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
   const int ld = seg.ld_seq ? seg.ld_seq : Nq;  // output sequence stride
   OutT* out = (OutT*)seg.out;
   const int tc = tid & 7;  // chunk of 8 tokens within the 64-token run

@@ -396,7 +396,7 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
  *                             state, shared by every head and both paths
  *   v_j as Eq. 3;  s_ij = (qC_i . kC_j + qR_i . kR_j) / sqrt(d_k + d_R).
  * RoPE over the rotary part: pairs (t, t + d_R/2), theta_t = base^(-2t/d_R).
- * Supported: d_R = d_k / 2 (d_k 64 or 128).
+ * Supported: d_R = 64 with d_k 64 or 128, bf16 mode.
  *
  * dar_attn_decode_drope -- one query per sequence at p = ctx_len - 1 over the
  * variant's cache.  With no rotation between W_upK and the query, the content
@@ -414,6 +414,69 @@ dar_status dar_attn_decode(const void* q, const void* K_win, const void* V_win, 
  * bf16 only; d_down in {128, 256, 512}.  Workspace (query with NULL): the
  * absorbed queries and the softmax partials.
  */
+/*
+ * dar_project_drope -- the variant's projections (bf16 mode; outputs fp16
+ * like dar_project's):
+ *   QC     [B, heads, N, d_k]   h W_Q (not rotated)
+ *   QR     [B, heads, N, d_R]   RoPE(h W_QR) at the token's position
+ *   K_loc  [B, heads, N, d_k]   h W_K (not rotated)
+ *   V_loc  [B, heads, d_k, N]   h W_V, token innermost
+ *   h_D    [B, N, d_down]       h W_down
+ *   K_glob [B, heads, N, d_k]   h^D W_upK (not rotated)
+ *   V_glob [B, heads, d_k, N]   h^D W_upV, token innermost
+ *   KR     [B, N, d_R]          RoPE(h W_KR), one per token
+ * Weights column-major as for dar_project: W_QR [d x heads*d_R], W_KR
+ * [d x d_R]; W_upK / W_upV from dar_fold, or both NULL (folded into the
+ * workspace, with W_up given).  Workspace (query with NULL): RoPE tables of
+ * width d_R (and the fold).
+ */
+dar_status dar_project_drope(const void* h, const void* W_down, const void* W_up, const void* W_Q,
+                             const void* W_K, const void* W_V, const void* W_QR, const void* W_KR,
+                             const void* W_upK, const void* W_upV, int B, int N, int d,
+                             int d_down, int heads, int d_k, int d_R, int pos0, float rope_base,
+                             dar_dtype dtype, void* QC, void* QR, void* K_loc, void* V_loc,
+                             void* h_D, void* K_glob, void* V_glob, void* KR, void* workspace,
+                             size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * dar_attn_prefill_drope -- Eq. (4) of the variant, causal, with the Eq. (3)
+ * selection on the content part: query i and key j <= i score
+ * (QC_i . K_src,j + QR_i . KR_j) / sqrt(d_k + d_R), K_src / V_src the local
+ * arrays when i - j < w and the global ones otherwise; o [B, N, heads*d_k]
+ * (bf16).  Inputs in dar_project_drope's layouts (fp16).  No workspace.
+ */
+dar_status dar_attn_prefill_drope(const void* QC, const void* QR, const void* K_loc,
+                                  const void* V_loc, const void* K_glob, const void* V_glob,
+                                  const void* KR, int B, int N, int heads, int d_k, int d_R, int w,
+                                  dar_dtype dtype, void* o, hipStream_t stream);
+
+/*
+ * dar_cache_from_prefill_drope -- the variant's decode cache of a prefilled
+ * prompt: latent rows and ring slots as dar_cache_from_prefill (the ring holds
+ * the content keys K_loc), plus KR_cache[b, n, :] <- KR[b, n, :] for n < N
+ * (fp16 -> bf16).  KR_cache [B, cap, d_R].
+ */
+dar_status dar_cache_from_prefill_drope(const void* h_D, const void* K_loc, const void* V_loc,
+                                        const void* KR, int B, int N, int heads, int d_k,
+                                        int d_down, int d_R, int w, int cap, dar_dtype dtype,
+                                        void* h_D_cache, void* K_win, void* V_win, void* KR_cache,
+                                        hipStream_t stream);
+
+/*
+ * dar_decode_append_drope -- the variant's new token at position `pos` of
+ * every sequence: qC <- h W_Q, qR <- RoPE_pos(h W_QR) ([B, heads, d_R]), the
+ * ring slot pos mod w of K_win / V_win <- h W_K, h W_V (content keys, not
+ * rotated), h_D[b, pos] <- h W_down, KR[b, pos] <- RoPE_pos(h W_KR).  bf16;
+ * workspace: RoPE tables of width d_R.
+ */
+dar_status dar_decode_append_drope(const void* h, const void* W_down, const void* W_Q,
+                                   const void* W_K, const void* W_V, const void* W_QR,
+                                   const void* W_KR, int B, int d, int d_down, int heads, int d_k,
+                                   int d_R, int pos, int w, int cap, float rope_base,
+                                   dar_dtype dtype, void* qC, void* qR, void* K_win, void* V_win,
+                                   void* h_D, void* KR, void* workspace, size_t* workspace_bytes,
+                                   hipStream_t stream);
+
 dar_status dar_attn_decode_drope(const void* qC, const void* qR, const void* K_win,
                                  const void* V_win, const void* KR, const void* h_D,
                                  const void* W_upK, const void* W_upV, int B, int ctx_len, int cap,

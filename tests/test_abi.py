@@ -29,6 +29,28 @@ def test_exports_match_header():
         assert hasattr(L, n), n
 
 
+def _param_counts(text):
+    """Number of parameters of every dar_* declaration in a header."""
+    out = {}
+    for m in re.finditer(r"^\s*(?:dar_status|int|const char\*)\s+(dar_\w+)\s*\(([^)]*)\)\s*;",
+                         text, re.M):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argtypes_match_header():
+    """Every entry point the binding types has as many arguments as the
+    header declares (a miscount would shift every later argument)."""
+    counts = _param_counts(open(HEADER).read())
+    assert set(counts) == set(declared())
+    L = dar.lib()
+    for n, c in counts.items():
+        at = getattr(L, n).argtypes
+        assert at is not None, n
+        assert len(at) == c, "%s: binding %d, header %d" % (n, len(at), c)
+
+
 def test_version_and_status_strings():
     L = dar.lib()
     assert L.dar_abi_version() == 1
@@ -387,3 +409,93 @@ def test_cache_varlen_rejects():
     assert cache_varlen(lens=F(6) + 2) == INVALID
     assert cache_varlen(lens=F(3)) == INVALID           # lengths alias the cache
     assert cache_varlen(cap=99) == INVALID
+
+
+# ------------------------------------------------------------------ decoupled-RoPE variant
+def project_drope(**kw):
+    a = dict(h=F(0), W_down=F(1), W_up=F(2), W_Q=F(3), W_K=F(4), W_V=F(5), W_QR=F(6),
+             W_KR=F(7), W_upK=None, W_upV=None, B=2, N=128, d=256, d_down=64, heads=4, d_k=64,
+             d_R=64, pos0=0, base=10000.0, dtype=1, QC=F(10), QR=F(11), K_loc=F(12),
+             V_loc=F(13), h_D=F(14), K_glob=F(15), V_glob=F(16), KR=F(17), ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    keys = ("h", "W_down", "W_up", "W_Q", "W_K", "W_V", "W_QR", "W_KR", "W_upK", "W_upV", "B",
+            "N", "d", "d_down", "heads", "d_k", "d_R", "pos0", "base", "dtype", "QC", "QR",
+            "K_loc", "V_loc", "h_D", "K_glob", "V_glob", "KR", "ws")
+    st = dar.lib().dar_project_drope(*[a[k] for k in keys], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_project_drope_size_query_and_rejects():
+    st, n = project_drope()
+    assert st == OK and n > 0                     # RoPE tables and the fold
+    st2, n2 = project_drope(W_upK=F(8), W_upV=F(9))
+    assert st2 == OK and n2 < n                   # folded weights given: tables only
+    assert project_drope(W_upK=F(8))[0] == INVALID  # one folded weight without the other
+    assert project_drope(d_R=63)[0] == INVALID
+    assert project_drope(d_R=32)[0] == UNSUP      # rotary width 64 only
+    assert project_drope(d_k=96)[0] == UNSUP
+    assert project_drope(dtype=0)[0] == UNSUP
+    assert project_drope(KR=F(0))[0] == INVALID   # output aliases h
+    assert project_drope(ws=F(30), wsb=n - 1)[0] == WS
+
+
+def prefill_drope(**kw):
+    a = dict(QC=F(0), QR=F(1), K_loc=F(2), V_loc=F(3), K_glob=F(4), V_glob=F(5), KR=F(6), B=2,
+             N=128, heads=4, d_k=128, d_R=64, w=32, dtype=1, o=F(7))
+    a.update(kw)
+    keys = ("QC", "QR", "K_loc", "V_loc", "K_glob", "V_glob", "KR", "B", "N", "heads", "d_k",
+            "d_R", "w", "dtype", "o")
+    return dar.lib().dar_attn_prefill_drope(*[a[k] for k in keys], None)
+
+
+def test_prefill_drope_rejects():
+    assert prefill_drope(w=-1) == INVALID
+    assert prefill_drope(N=0) == INVALID
+    assert prefill_drope(o=F(6)) == INVALID      # output aliases the rotary keys
+    assert prefill_drope(QR=F(1) + 8) == INVALID  # misaligned
+    assert prefill_drope(dtype=0) == UNSUP
+    assert prefill_drope(d_R=128) == UNSUP
+    assert prefill_drope(d_k=256) == UNSUP
+
+
+def append_drope(**kw):
+    a = dict(h=F(0), W_down=F(1), W_Q=F(2), W_K=F(3), W_V=F(4), W_QR=F(5), W_KR=F(6), B=2,
+             d=256, d_down=64, heads=4, d_k=64, d_R=64, pos=100, w=16, cap=200, base=10000.0,
+             dtype=1, qC=F(7), qR=F(8), K_win=F(9), V_win=F(10), h_D=F(11), KR=F(12), ws=None,
+             wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    keys = ("h", "W_down", "W_Q", "W_K", "W_V", "W_QR", "W_KR", "B", "d", "d_down", "heads",
+            "d_k", "d_R", "pos", "w", "cap", "base", "dtype", "qC", "qR", "K_win", "V_win", "h_D",
+            "KR", "ws")
+    st = dar.lib().dar_decode_append_drope(*[a[k] for k in keys], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_append_drope_size_query_and_rejects():
+    st, n = append_drope()
+    assert st == OK and n > 0
+    assert append_drope(pos=200)[0] == INVALID    # position past the cache
+    assert append_drope(w=0, K_win=None, V_win=None)[0] == OK
+    assert append_drope(KR=F(11))[0] == INVALID   # rotary keys alias the latent cache
+    assert append_drope(d_R=32)[0] == UNSUP
+    assert append_drope(dtype=0)[0] == UNSUP
+    assert append_drope(ws=F(30), wsb=n - 1)[0] == WS
+
+
+def cache_drope(**kw):
+    a = dict(h_D=F(0), K_loc=F(1), V_loc=F(2), KR=F(3), B=2, N=100, heads=4, d_k=64, d_down=64,
+             d_R=64, w=16, cap=128, dtype=1, L=F(4), K_win=F(5), V_win=F(6), KRc=F(7))
+    a.update(kw)
+    keys = ("h_D", "K_loc", "V_loc", "KR", "B", "N", "heads", "d_k", "d_down", "d_R", "w", "cap",
+            "dtype", "L", "K_win", "V_win", "KRc")
+    return dar.lib().dar_cache_from_prefill_drope(*[a[k] for k in keys], None)
+
+
+def test_cache_from_prefill_drope_rejects():
+    assert cache_drope(cap=99) == INVALID         # cache shorter than the prompt
+    assert cache_drope(KRc=F(3)) == INVALID       # output aliases the input rotary keys
+    assert cache_drope(KRc=F(4)) == INVALID       # rotary cache aliases the latent cache
+    assert cache_drope(dtype=0) == UNSUP
+    assert cache_drope(d_R=32) == UNSUP

@@ -45,7 +45,7 @@ def ref_drope_decode(inp, ctx, w, heads=None, b=None):
     (2, 3000, 512, 4, 128, 512, 256),   # d_down 512
 ])
 def test_drope_decode_small(B, ctx, d, H, d_k, dd, w):
-    d_R = d_k // 2
+    d_R = 64
     inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, d_R, w, seed0=20 * ctx + w)
     log("drope decode B%d ctx%d d%d H%d dk%d dR%d dd%d w%d" % (B, ctx, d, H, d_k, d_R, dd, w))
     got = run_drope_decode(inp, ctx, w, H, d_k)
@@ -57,7 +57,7 @@ def test_drope_decode_small(B, ctx, d, H, d_k, dd, w):
 
 def test_drope_decode_cap_larger_than_context():
     B, ctx, d, H, d_k, dd, w = 2, 700, 256, 4, 64, 128, 64
-    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, d_k // 2, w, cap=1024, seed0=99)
+    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, 64, w, cap=1024, seed0=99)
     err = max_err(run_drope_decode(inp, ctx, w, H, d_k), ref_drope_decode(inp, ctx, w))
     assert err <= TOL["bf16"]
 
@@ -67,7 +67,7 @@ def test_drope_decode_matches_prefill_row():
     decode at position p reproduces row p of the oracle's prefill of the
     variant."""
     B, N, d, H, d_k, dd, w = 2, 600, 256, 4, 64, 128, 100
-    d_R = d_k // 2
+    d_R = 64
     inp = di.drope_prefill_inputs(B, N, d, H, d_k, dd, d_R, seed0=606)
     o_ref, _, P = oracle.prefill_drope(inp, H, d_k, d_R, w)
     p = N - 1
@@ -90,7 +90,7 @@ def test_drope_long_context_decode():
     """B16, ctx 32768, d2048, 16 heads of 128 (d_R 64), w512, d_down 256: the
     full-size launch, one head of every batch against the oracle."""
     B, ctx, d, H, d_k, dd, w = 16, 32768, 2048, 16, 128, 256, 512
-    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, d_k // 2, w, seed0=8000)
+    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, 64, w, seed0=8000)
     got = run_drope_decode(inp, ctx, w, H, d_k)
     for b in range(B):
         hh = (5 * b + 3) % H
@@ -103,6 +103,6 @@ def test_drope_long_context_decode():
 
 def test_drope_decode_deterministic():
     B, ctx, d, H, d_k, dd, w = 2, 3000, 256, 4, 128, 256, 256
-    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, d_k // 2, w, seed0=77)
+    inp = di.drope_decode_inputs(B, ctx, d, H, d_k, dd, 64, w, seed0=77)
     assert np.array_equal(run_drope_decode(inp, ctx, w, H, d_k),
                           run_drope_decode(inp, ctx, w, H, d_k))
