@@ -26,7 +26,8 @@ DAR_FP32, DAR_BF16 = 0, 1
 STATUS = {0: "DAR_OK", 1: "DAR_ERR_INVALID_ARG", 2: "DAR_ERR_UNSUPPORTED",
           3: "DAR_ERR_WORKSPACE", 4: "DAR_ERR_HIP"}
 # Every entry point include/dar.h declares.
-EXPORTS = ("dar_abi_version", "dar_status_string", "dar_fold", "dar_project",
+EXPORTS = ("dar_abi_version", "dar_status_string", "dar_pack_weight", "dar_fold",
+           "dar_project",
            "dar_project_sigmoid",
            "dar_attn_prefill", "dar_attn_prefill_lse", "dar_attn_prefill_backward",
            "dar_decode_append", "dar_cache_from_prefill", "dar_prefill_chunk",
@@ -66,7 +67,9 @@ def lib() -> ctypes.CDLL:
         L.dar_project_sigmoid.restype = _I
         L.dar_project_sigmoid.argtypes = L.dar_project.argtypes
         L.dar_attn_prefill.restype = _I
-        L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P]
+        L.dar_attn_prefill.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _SZ, _P]
+        L.dar_pack_weight.restype = _I
+        L.dar_pack_weight.argtypes = [_P, _I, _I, _I, _P, _P]
         L.dar_attn_prefill_lse.restype = _I
         L.dar_attn_prefill_lse.argtypes = [_P] * 5 + [_I] * 6 + [_P, _P, _P]
         L.dar_attn_prefill_backward.restype = _I
@@ -313,9 +316,24 @@ def dar_attn_prefill(Q, K_loc, V_loc, K_glob, V_glob, w: int, o=None, stream=Non
         o = torch.empty((B, N, H * d_k), dtype=torch.bfloat16 if dt == DAR_BF16 else torch.float32,
                         device=Q.device)
     st = lib().dar_attn_prefill(_ptr(Q), _ptr(K_loc), _ptr(V_loc), _ptr(K_glob), _ptr(V_glob),
-                                B, N, H, d_k, int(w), dt, _ptr(o), _stream(stream))
+                                B, N, H, d_k, int(w), dt, _ptr(o), None, None, _stream(stream))
     _check("dar_attn_prefill", st)
     return o
+
+
+@_on_stream
+def dar_pack_weight(W, out=None, stream=None):
+    """The equations' matrix W in R^{rows x cols}, given row-major as a
+    [rows, cols] tensor, in the library's column-major layout: returns a
+    [cols, rows] tensor holding the same matrix (a bit-exact transpose run by
+    the library)."""
+    torch = _torch()
+    rows, cols = W.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=W.dtype, device=W.device)
+    st = lib().dar_pack_weight(_ptr(W), rows, cols, _dtype_code(W), _ptr(out), _stream(stream))
+    _check("dar_pack_weight", st)
+    return out
 
 
 @_on_stream

@@ -179,4 +179,41 @@ hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const v
   return e;
 }
 
+// Weight packing: the equations' W in R^{rows x cols}, stored row-major
+// (element (k, n) at k * cols + n, the row-vector convention of Eqs. 1-4), into
+// the library's column-major layout (element (k, n) at n * rows + k).  A plain
+// transpose through a 64 x 64 LDS tile: reads run along n, writes along k, both
+// coalesced.  The padded pitch (65 elements) spreads a column of the tile over
+// the banks.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_transpose_kernel(const T* __restrict__ src,
+                                                             T* __restrict__ dst, int rows,
+                                                             int cols) {
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = src[(size_t)r * cols + c];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) dst[(size_t)c * rows + r] = tile[tx][i];
+  }
+}
+
+hipError_t launch_pack_weight(const void* W, int rows, int cols, int elem_bytes, void* out,
+                              hipStream_t s) {
+  const dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  if (elem_bytes == 2)
+    pack_transpose_kernel<unsigned short>
+        <<<grid, 256, 0, s>>>((const unsigned short*)W, (unsigned short*)out, rows, cols);
+  else
+    pack_transpose_kernel<float><<<grid, 256, 0, s>>>((const float*)W, (float*)out, rows, cols);
+  return hipGetLastError();
+}
+
 }  // namespace dar

@@ -14,7 +14,7 @@ using namespace dar;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 size_t elem_size(dar_dtype dt) { return dt == DAR_BF16 ? 2 : 4; }
 bool dtype_ok(dar_dtype dt) { return dt == DAR_BF16 || dt == DAR_FP32; }
@@ -213,7 +213,7 @@ dar_status dar_project_sigmoid(const void* h, const void* W_down, const void* W_
 static dar_status attn_prefill_impl(const void* Q, const void* K_loc, const void* V_loc,
                                     const void* K_glob, const void* V_glob, int B, int N,
                                     int heads, int d_k, int w, dar_dtype dtype, void* o,
-                                    float* lse, hipStream_t stream) {
+                                    float* lse, hipStream_t stream, bool launch = true) {
   if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || heads < 1 || d_k < 2 || (d_k & 1) || w < 0) return DAR_ERR_INVALID_ARG;
   const void* need[] = {Q, K_loc, V_loc, K_glob, V_glob, o};
@@ -226,6 +226,7 @@ static dar_status attn_prefill_impl(const void* Q, const void* K_loc, const void
   if (!disjoint(outs, lse != nullptr ? 2 : 1, ins, 5)) return DAR_ERR_INVALID_ARG;
   if (!head_supported(d_k)) return DAR_ERR_UNSUPPORTED;
   if ((size_t)B * heads * N * d_k > 0x7fffffffffffL) return DAR_ERR_UNSUPPORTED;
+  if (!launch) return DAR_OK;
   PrefillProblem p{Q, K_loc, V_loc, K_glob, V_glob, o, B, N, heads, d_k, w};
   p.lse = lse;
   return hip_status(launch_attn_prefill(p, dtype, stream));
@@ -233,9 +234,27 @@ static dar_status attn_prefill_impl(const void* Q, const void* K_loc, const void
 
 dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
                             const void* K_glob, const void* V_glob, int B, int N, int heads,
-                            int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream) {
+                            int d_k, int w, dar_dtype dtype, void* o, void* workspace,
+                            size_t* workspace_bytes, hipStream_t stream) {
+  if (workspace == nullptr && workspace_bytes != nullptr) {
+    // size query: validate, then report that no workspace is needed
+    const dar_status st = attn_prefill_impl(Q, K_loc, V_loc, K_glob, V_glob, B, N, heads, d_k,
+                                            w, dtype, o, nullptr, stream, /*launch=*/false);
+    if (st == DAR_OK) *workspace_bytes = 0;
+    return st;
+  }
   return attn_prefill_impl(Q, K_loc, V_loc, K_glob, V_glob, B, N, heads, d_k, w, dtype, o,
                            nullptr, stream);
+}
+
+dar_status dar_pack_weight(const void* W, int rows, int cols, dar_dtype dtype, void* W_packed,
+                           hipStream_t stream) {
+  if (!dtype_ok(dtype) || rows < 1 || cols < 1 || !aligned16(W) || !aligned16(W_packed))
+    return DAR_ERR_INVALID_ARG;
+  const size_t bytes = elem_size(dtype) * (size_t)rows * cols;
+  if (overlap(Span{W, bytes}, Span{W_packed, bytes})) return DAR_ERR_INVALID_ARG;
+  if (rows > 64 * 65535 || cols > 64 * 65535) return DAR_ERR_UNSUPPORTED;
+  return hip_status(launch_pack_weight(W, rows, cols, (int)elem_size(dtype), W_packed, stream));
 }
 
 dar_status dar_attn_prefill_lse(const void* Q, const void* K_loc, const void* V_loc,

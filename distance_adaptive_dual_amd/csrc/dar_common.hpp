@@ -264,6 +264,9 @@ hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const v
                                      int B, int N, int heads, int d_k, int d_down, int w,
                                      int cap, void* h_D_cache, void* K_win, void* V_win,
                                      hipStream_t s, const int* lens = nullptr);
+// Row-major [rows, cols] -> column-major (cache.hip); grid limit rows, cols <= 64 * 65535.
+hipError_t launch_pack_weight(const void* W, int rows, int cols, int elem_bytes, void* out,
+                              hipStream_t s);
 bool decode_supported(int d_k, int d_down);  // d_k in {64,128}, d_down in {32,...,512}
 hipError_t launch_attn_decode(const DecodeProblem& p, hipStream_t s);
 

@@ -23,6 +23,14 @@
  *    output column is contiguous.  These are the same bytes as a row-major
  *    [c, r] array (the layout of a torch.nn.Linear weight).  The MFMA GEMMs
  *    read both operands along the contraction index, so no transpose runs.
+ *    A caller holding the equations' matrices row-major (W in R^{in x out}
+ *    with each row contiguous, right-multiplied by row vectors h) packs each
+ *    one once with dar_pack_weight.
+ *  - Internal formats: the prefill intermediates dar_project writes and
+ *    dar_attn_prefill reads are the library's own format, not the
+ *    equations' layout: V_loc and V_glob are stored transposed per head
+ *    ([B, heads, d_k, N], token innermost, the operand order of the
+ *    attention's value product) and, in DAR_BF16 mode, all six are fp16.
  *  - dtype DAR_BF16: the layer's inputs and outputs (h, the weights, the
  *    folded weights, o, and the decode cache q / K_win / V_win / h_D) are
  *    bfloat16.  The six prefill intermediates that dar_project hands to
@@ -77,6 +85,18 @@ int dar_abi_version(void);
 const char* dar_status_string(dar_status s);
 
 /*
+ * dar_pack_weight -- one of the equations' weight matrices in the library's
+ * layout.  W is W in R^{rows x cols} row-major (element (k, n) at
+ * k*cols + n: W_down [d x d_down], W_up [d_down x d], W_Q / W_K / W_V
+ * [d x heads*d_k] as Eqs. (1)-(4) write them); W_packed receives the same
+ * matrix column-major (element (k, n) at n*rows + k), the layout every other
+ * entry point reads.  A transpose, bit-exact, in dtype (bf16 or fp32).
+ * W_packed must not overlap W.  No workspace.
+ */
+dar_status dar_pack_weight(const void* W, int rows, int cols, dar_dtype dtype, void* W_packed,
+                           hipStream_t stream);
+
+/*
  * dar_fold -- fold the up-projection into the shared key/value weights.
  *
  * Eqs. (2)-(3): the global path applies W_K and W_V to h'_j = h^D_j W_up, so
@@ -85,7 +105,7 @@ const char* dar_status_string(dar_status s);
  * in fp32 and stores them in `dtype`, column-major like every weight (i.e.
  * as row-major [heads*d_k, d_down]).  Run once per weight set.
  *   W_up [d_down x d], W_K, W_V [d x heads*d_k]      (column-major, dtype)
- * No workspace is needed; pass workspace = NULL only to query (writes 0).
+ * No workspace.
  */
 dar_status dar_fold(const void* W_up, const void* W_K, const void* W_V, int d, int d_down,
                     int heads, int d_k, dar_dtype dtype, void* W_upK, void* W_upV,
@@ -151,11 +171,15 @@ dar_status dar_project_sigmoid(const void* h, const void* W_down, const void* W_
  *   V_loc, V_glob      [B, heads, d_k, N]   (token innermost, as dar_project writes)
  *   o                  [B, N, heads*d_k]    heads concatenated, before W_O
  *                                           (bf16 in DAR_BF16 mode)
- * No workspace is used (query returns 0).
+ * The kernel needs no workspace: with workspace NULL and workspace_bytes
+ * non-NULL the call validates, writes 0 and launches nothing (the size
+ * query of the protocol); otherwise it launches, and workspace_bytes may be
+ * NULL.
  */
 dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
                             const void* K_glob, const void* V_glob, int B, int N, int heads,
-                            int d_k, int w, dar_dtype dtype, void* o, hipStream_t stream);
+                            int d_k, int w, dar_dtype dtype, void* o, void* workspace,
+                            size_t* workspace_bytes, hipStream_t stream);
 
 /*
  * dar_attn_prefill_lse -- dar_attn_prefill that also stores, for training,

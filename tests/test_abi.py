@@ -53,7 +53,7 @@ def test_binding_argtypes_match_header():
 
 def test_version_and_status_strings():
     L = dar.lib()
-    assert L.dar_abi_version() == 1
+    assert L.dar_abi_version() == 2
     for code, name in dar.STATUS.items():
         assert L.dar_status_string(code).decode() == name
 
@@ -115,9 +115,19 @@ def attn(**kw):
     a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), B=1, N=64, heads=2,
              d_k=64, w=8, dtype=1, o=F(5))
     a.update(kw)
-    return dar.lib().dar_attn_prefill(a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"],
-                                      a["B"], a["N"], a["heads"], a["d_k"], a["w"], a["dtype"],
-                                      a["o"], None)
+    n = ctypes.c_size_t(12345)
+    # workspace NULL with a size pointer: the size query, which validates and
+    # launches nothing even for a valid problem
+    st = dar.lib().dar_attn_prefill(a["Q"], a["K_loc"], a["V_loc"], a["K_glob"], a["V_glob"],
+                                    a["B"], a["N"], a["heads"], a["d_k"], a["w"], a["dtype"],
+                                    a["o"], None, ctypes.byref(n), None)
+    assert st != OK or n.value == 0
+    return st
+
+
+def test_prefill_size_query():
+    assert attn() == OK
+    assert attn(dtype=0) == OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -499,3 +509,13 @@ def test_cache_from_prefill_drope_rejects():
     assert cache_drope(KRc=F(4)) == INVALID       # rotary cache aliases the latent cache
     assert cache_drope(dtype=0) == UNSUP
     assert cache_drope(d_R=32) == UNSUP
+
+
+def test_pack_weight_rejects():
+    L = dar.lib()
+    assert L.dar_pack_weight(F(0), 0, 64, 1, F(1), None) == INVALID
+    assert L.dar_pack_weight(F(0), 64, 64, 1, F(0) + 4096, None) == INVALID  # overlap
+    assert L.dar_pack_weight(F(0) + 8, 64, 64, 1, F(1), None) == INVALID    # misaligned
+    assert L.dar_pack_weight(None, 64, 64, 1, F(1), None) == INVALID
+    assert L.dar_pack_weight(F(0), 64, 64, 7, F(1), None) == INVALID       # unknown dtype
+    assert L.dar_pack_weight(F(0), 64 * 65536, 1, 1, F(1), None) == UNSUP
