@@ -27,6 +27,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Workgroups are handed to the 8 XCDs of an MI355X round-robin by linear id.
 constexpr int kNumXcd = 8;
 
+// Workgroup barrier for LDS pipelines: this wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it carries no release fence, which
+// would make the wave wait for every outstanding global load too (vmcnt(0)),
+// including the direct-to-LDS loads of k-tiles prefetched further ahead.
+// Callers wait on vmcnt themselves for the loads the next step reads.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

@@ -20,6 +20,8 @@
 // the same size and MFMA rate); the second GEMM therefore runs on fp16 MFMAs,
 // converting the bf16 folded weights to fp16 as they are staged into LDS.
 // fp32 path: an LDS-tiled VALU GEMM with the same epilogue (no bf16 anywhere).
+#include <type_traits>
+
 #include "dar_common.hpp"
 
 namespace dar {
@@ -29,6 +31,26 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDA_S = BK + 8;  // bf16 per LDS row: 144 B, rows land 4 banks apart
 constexpr int EPI_P = BN + 4;  // fp32 per epilogue row
+#ifndef DAR_WIDE_MIN_TILES
+#define DAR_WIDE_MIN_TILES 1024
+#endif
+constexpr long kWideMinTiles = DAR_WIDE_MIN_TILES;  // wide-tile GEMM from this many tiles
+#ifndef DAR_WIDE_BAND_BYTES
+#define DAR_WIDE_BAND_BYTES (4 << 20)
+#endif
+constexpr long kWideBandBytes = DAR_WIDE_BAND_BYTES;  // weight bytes of one band
+// The wide kernel serves long contractions only: its one workgroup per CU
+// cannot overlap the epilogue with another tile's main loop, which only a
+// long main loop amortizes (measured on the 1B-scale layer: K = 2048 gains 4%,
+// K = 512 loses 19% against the 256 x 128 kernel).
+constexpr int kWideMinK = 1024;
+
+// Slot of k-chunk c (of 4 per 64-byte row) in row r of a staged k-tile:
+// c ^ kswz(r).  Any 16 consecutive rows read at one chunk index then cover
+// all 64 banks once, which is what the 16-byte fragment reads need (measured:
+// a swizzle built for 8-lane groups over 32 banks raised the bank-conflict
+// cycles of the GEMM from 2% to 12% of its run time).
+__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
 
 struct SegTiles {
   int tile0[5];  // first column tile of each segment, tile0[nseg] = total
@@ -231,8 +253,8 @@ __device__ __forceinline__ void rope_cs8(const RopeTab& t, int pos, int t0, floa
   }
 }
 
-// Tile [128 tokens][EPI_P] -> kRowMajor, or kHead without rotation.
-template <typename OutT, int D, bool RP>
+// Tile [128 tokens][PITCH] (128 columns used) -> kRowMajor, or kHead without rotation.
+template <typename OutT, int D, bool RP, int PITCH = EPI_P>
 __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, int hf, int col0,
                                                  const GemmSeg& seg, const GemmProblem& p) {
   const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
@@ -252,7 +274,7 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
       const int gcol = col0 + c;  // width is a multiple of 32: chunks are whole
       if (gcol >= width) continue;
       float v[8];
-      read8(tile + r * EPI_P + c, v);
+      read8(tile + r * PITCH + c, v);
       OutT* dst;
       if (seg.kind == kRowMajor) {
         dst = out + ((size_t)b * ld + no) * width + gcol;
@@ -266,14 +288,39 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
   }
 }
 
-// Tile [128 tokens][EPI_P] -> kHead with RoPE at position pos0 + n on the
+// Tile [128 tokens][PITCH] (128 columns used) -> kHead with RoPE at position pos0 + n on the
 // rotate-half pairs (t, t + D/2).  A lane takes 8 consecutive pairs of one head
 // for 4 consecutive tokens: the angles of the first token come from the
 // tables, the next ones by one complex multiplication with (cos, sin)(theta_t)
 // each (the table row for position 1).
-template <typename OutT, int D, bool RP>
+// cos/sin of the first of the 4 tokens a thread of store_rows_rope takes in
+// epilogue pass hf, for its 8 pairs, and the one-position step; loaded ahead
+// (at kernel start) so their latency hides under the main loop.
+struct RopePre {
+  float2 cs[8], step[8];
+};
+
+template <int D>
+__device__ __forceinline__ void rope_prefetch(const GemmProblem& p, int row0, int hf,
+                                              RopePre& r) {
+  constexpr int PCH = D / 16;
+  const int tid = threadIdx.x, w8 = tid & 7, t0 = 8 * (w8 % PCH);
+  const int grow0 = epi_row(row0, hf, 4 * (tid >> 3));
+  const int n0 = (grow0 < p.M ? grow0 : 0) % p.n_seq;
+  rope_cs8(p.rope, p.pos0 + n0, t0, r.cs);
+  const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 a = st[i];
+    r.step[2 * i] = make_float2(a.x, a.y);
+    r.step[2 * i + 1] = make_float2(a.z, a.w);
+  }
+}
+
+template <typename OutT, int D, bool RP, int PITCH = EPI_P>
 __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int hf, int col0,
-                                                const GemmSeg& seg, const GemmProblem& p) {
+                                                const GemmSeg& seg, const GemmProblem& p,
+                                                const RopePre* pre = nullptr) {
   constexpr int HALF = D / 2, PCH = D / 16;  // pair chunks of 8 per head
   const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
   const int ld = seg.ld_seq ? seg.ld_seq : Nq;
@@ -288,14 +335,22 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
   const int b0 = grow0 / Nq, n0 = grow0 % Nq;
   const bool consec = grow0 + 3 < M && n0 + 3 < Nq;  // one sequence, consecutive positions
   float2 cs[8], step[8];
-  rope_cs8(p.rope, row_position<RP>(p, b0, n0), t0, cs);
-  if (consec) {
-    const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
+  if (!RP && pre != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 a = st[i];
-      step[2 * i] = make_float2(a.x, a.y);
-      step[2 * i + 1] = make_float2(a.z, a.w);
+    for (int i = 0; i < 8; ++i) {
+      cs[i] = pre->cs[i];
+      step[i] = pre->step[i];
+    }
+  } else {
+    rope_cs8(p.rope, row_position<RP>(p, b0, n0), t0, cs);
+    if (consec) {
+      const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = st[i];
+        step[2 * i] = make_float2(a.x, a.y);
+        step[2 * i + 1] = make_float2(a.z, a.w);
+      }
     }
   }
 #pragma unroll
@@ -316,8 +371,8 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
       }
     }
     float x[8], y[8], a[8], bb[8];
-    read8(tile + (r0 + kk) * EPI_P + c, x);
-    read8(tile + (r0 + kk) * EPI_P + c + HALF, y);
+    read8(tile + (r0 + kk) * PITCH + c, x);
+    read8(tile + (r0 + kk) * PITCH + c + HALF, y);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       a[i] = x[i] * cs[i].x - y[i] * cs[i].y;
@@ -387,8 +442,8 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   // buffer loads (global -> LDS, no staging registers; lanes past the matrix
   // edge read zeros), prefetching two k-tiles ahead, one barrier per k-tile.
   // Rows of a k-tile are 64 B = 4 chunks of 16 B; chunk c of row r sits in
-  // slot c ^ ((r >> 2) & 3), which makes the 16-byte MFMA fragment reads of 32
-  // consecutive rows conflict-free.
+  // slot c ^ kswz(r), which keeps the 16-byte MFMA fragment reads free of
+  // bank conflicts.
   constexpr int TBM = 2 * BM;  // tokens per workgroup tile
   constexpr int GBK = 32, NST = 3;
   constexpr int TOK = TBM * GBK, STAGE = TOK + BN * GBK;  // elements per stage
@@ -417,7 +472,9 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   const int row0 = mt * TBM;
   const int K = p.K, M = p.M;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keep it in a scalar register so the LDS
+  // destinations of the direct-to-LDS loads (M0) need no per-lane handling
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
   // wave -> (partner pair of 32-column blocks, 128-token half)
   const int wp = wave & 1, wt = wave >> 1;
@@ -436,32 +493,38 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
       (int)(b_ext < 0x7ffffff0u ? b_ext : 0x7ffffff0u), 0x00020000);
   TM* const lds = (TM*)smem;
   // One 16-byte chunk per lane per load: slot P of the k-tile holds chunk
-  // (P & 3) ^ ((row >> 2) & 3) of row P >> 2.
-  auto issue = [&](int kt, int stg) {
-    const int k0 = kt * GBK;
+  // (P & 3) ^ kswz(row) of row P >> 2.  K is a multiple of GBK, so
+  // only rows can fall off the matrix; a lane's byte offset within a k-tile
+  // is fixed (or past the buffer's extent, which reads zeros), and the
+  // k-tile's offset goes in the scalar operand.
+  unsigned va[4], vb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // token rows: 1024 chunks
-      const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
-      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 2) & 3));
-      const unsigned oa =
-          (row0 + r < M && kk < K) ? (unsigned)((r * K + kk) * sizeof(TM)) : 0x80000000u;
+  for (int i = 0; i < 4; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
+    const int kc = 8 * ((P & 3) ^ kswz(r));
+    va[i] = row0 + r < M ? (unsigned)((r * K + kc) * sizeof(TM)) : 0x80000000u;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
+    const int kc = 8 * ((P & 3) ^ kswz(r));
+    vb[i] = col0 + r < seg.width ? (unsigned)((r * K + kc) * sizeof(TB)) : 0x80000000u;
+  }
+  auto issue = [&](int kt, int stg) {
+    const int ka = kt * GBK * (int)sizeof(TM), kb = kt * GBK * (int)sizeof(TB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // token rows: 1024 chunks
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void*)(lds + stg * STAGE + (i * 4 + wave) * 512),
-          16, oa, 0, 0, 0);
-    }
+          16, va[i], ka, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // weight rows: 512 chunks
-      const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
-      const int kk = k0 + 8 * ((P & 3) ^ ((r >> 2) & 3));
-      const unsigned ob =
-          (col0 + r < seg.width && kk < K) ? (unsigned)((r * K + kk) * sizeof(TB)) : 0x80000000u;
+    for (int i = 0; i < 2; ++i)  // weight rows: 512 chunks
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb,
           (__attribute__((address_space(3))) void*)(lds + stg * STAGE + TOK + (i * 4 + wave) * 512),
-          16, ob, 0, 0, 0);
-    }
+          16, vb[i], kb, 0, 0);
   };
-  auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ ((row >> 2) & 3)); };
+  auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ kswz(row)); };
 
   // acc[i][j]: column block (cb0, cb1)[i] x token block j of this wave
   f32x16 acc[2][4];
@@ -481,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
       __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();  // k-tile kt is in LDS; everyone is done with k-tile kt-1
+    lds_barrier();  // k-tile kt is in LDS; everyone is done with k-tile kt-1
     if (kt + 2 < nk) issue(kt + 2, (kt + 2) % NST);
     const TM* sa = lds + (kt % NST) * STAGE;
     const TB* sb = (const TB*)(lds + (kt % NST) * STAGE + TOK);
@@ -548,6 +611,241 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
     else
       store_rows_plain<TO, D, RP>(tile, row0, hf, col0, seg, p);
   }
+}
+
+// --------------------------------------------------------------------------
+// Wide MFMA GEMM for large problems: workgroup tiles of 256 tokens x 256
+// output columns, 4 waves in a 2 x 2 grid, each wave 128 tokens x 128 columns
+// (16 accumulator blocks of 32 x 32).  A 16-wide k-step reads 8 fragments
+// from LDS for 16 MFMAs, and each k-tile staged in LDS feeds two waves per
+// row on either operand: per MFMA the LDS moves 0.75 KB (fragment reads plus
+// the direct-to-LDS fills) instead of the 1.125 KB of the 256 x 128 tile,
+// which keeps the LDS port below its limit when the matrix cores are busy.
+// One workgroup per CU (the accumulators take 256 registers per lane).
+//
+// Tile order ("bands"): the column tiles are cut into bands of WB; a band's
+// tiles are walked row tile by row tile, columns innermost, and the whole
+// sequence (band after band) is cut into 8 equal contiguous parts, one per XCD
+// (workgroup b runs on XCD b mod 8).  An XCD thus works on at most two bands
+// at a time: their weights stay in its L2 while the activation rows stream,
+// each read once per band; and every XCD gets the same number of tiles.
+constexpr int WBN = 256;  // columns per wide tile
+
+template <typename TM, typename TB, typename TO, int D, int GBK>
+__global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTiles st, int nM,
+                                                           int nC, int band, int per_xcd) {
+  typedef typename Vec8<TM>::type TMx8;
+  typedef typename Vec8<TB>::type TBx8;
+  constexpr int TBM = 256;
+  // k-tiles of GBK (32 or 64) in an LDS ring of NST stages (4 x 32 KB or 2 x 64 KB)
+  constexpr int NST = GBK == 64 ? 2 : 4;
+  constexpr int CPR = GBK / 8;   // 16-byte chunks per staged row
+  constexpr int KS = GBK / 16;   // MFMA k-steps per k-tile
+  constexpr int LPT = 2 * CPR;   // direct-to-LDS loads per lane per k-tile
+  static_assert(GBK == 32 || GBK == 64, "k-tile depth");
+  constexpr int TOK = TBM * GBK, STAGE = TOK + WBN * GBK;  // elements per stage
+  constexpr int RP_ = WBN + 4, CP_ = TBM / 2 + 4;           // epilogue pitches (fp32)
+  constexpr int MAIN_BYTES = NST * STAGE * 2;
+  constexpr int EPI_ROWS = 128 * RP_ * 4, EPI_COLS = WBN * CP_ * 4;
+  constexpr int EPI_BYTES = EPI_ROWS > EPI_COLS ? EPI_ROWS : EPI_COLS;
+  __shared__ __attribute__((aligned(16))) char smem[MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES];
+
+  const int bid = blockIdx.x;
+  const int seq = (bid % kNumXcd) * per_xcd + bid / kNumXcd;
+  const int nfull = nC / band;  // bands of exactly `band` columns
+  int mt, ct;
+  if (seq < nfull * band * nM) {
+    const int bd = seq / (band * nM), rem = seq % (band * nM);
+    mt = rem / band;
+    ct = bd * band + rem % band;
+  } else {
+    const int bw = nC - nfull * band, rem = seq - nfull * band * nM;
+    if (bw == 0) return;
+    mt = rem / bw;
+    ct = nfull * band + rem % bw;
+  }
+  if (ct >= nC || mt >= nM) return;
+  const int s = find_seg(st, p.nseg, ct);
+  const GemmSeg seg = p.seg[s];
+  const int col0 = (ct - st.tile0[s]) * WBN;
+  const int row0 = mt * TBM;
+  const int K = p.K, M = p.M;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int wc = wave & 1, wt = wave >> 1;  // column half, token half
+
+  const size_t a_ext = (size_t)(M - row0) * K * sizeof(TM);
+  const size_t b_ext = (size_t)(seg.width - col0) * K * sizeof(TB);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const TM*)p.A + (size_t)row0 * K), (short)0,
+      (int)(a_ext < 0x7ffffff0u ? a_ext : 0x7ffffff0u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const TB*)seg.Bt + (size_t)col0 * K), (short)0,
+      (int)(b_ext < 0x7ffffff0u ? b_ext : 0x7ffffff0u), 0x00020000);
+  TM* const lds = (TM*)smem;
+  // 16-byte chunk P of a k-tile region: row P / CPR, slot P % CPR holding
+  // k-chunk slot ^ swz(row) (32: kswz; 64: (row >> 1) & 7, which keeps 16
+  // consecutive 128-byte rows read at one chunk on distinct banks).  As in
+  // the 256 x 128 kernel, a lane's offset within a k-tile is fixed (rows past
+  // the edge read zeros) and the k-tile's offset is the scalar operand.
+  auto swz = [](int r) { return GBK == 64 ? (r >> 1) & 7 : kswz(r); };
+  // (fixed bound: a bound that depends on GBK drops the host-side launch stub)
+  unsigned va[8], vb[8];
+#pragma unroll
+  for (int i = 0; i < CPR; ++i) {
+    const int P = (i * 4 + wave) * 64 + lane, r = P / CPR;
+    const int kc = 8 * ((P % CPR) ^ swz(r));
+    va[i] = row0 + r < M ? (unsigned)((r * K + kc) * sizeof(TM)) : 0x80000000u;
+    vb[i] = col0 + r < seg.width ? (unsigned)((r * K + kc) * sizeof(TB)) : 0x80000000u;
+  }
+  auto issue = [&](int kt, int stg) {
+    const int ka = kt * GBK * (int)sizeof(TM), kb = kt * GBK * (int)sizeof(TB);
+#pragma unroll
+    for (int i = 0; i < CPR; ++i)  // token rows
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(lds + stg * STAGE + (i * 4 + wave) * 512),
+          16, va[i], ka, 0, 0);
+#pragma unroll
+    for (int i = 0; i < CPR; ++i)  // weight rows
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb,
+          (__attribute__((address_space(3))) void*)(lds + stg * STAGE + TOK + (i * 4 + wave) * 512),
+          16, vb[i], kb, 0, 0);
+  };
+  auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ swz(row)); };
+
+  // acc[i][j]: column block i (32 columns at 128 wc + 32 i) x token block j
+  // (32 tokens at 128 wt + 32 j)
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Software pipeline: the fragments of the next k-step are read from LDS
+  // while the MFMAs of the current one run.  k-tile kt+1 is waited for and
+  // published by the barrier between the two k-steps of tile kt (its second
+  // k-step's fragments are already in registers by then), and the loads of
+  // tile kt+3 go into the stage tile kt has just released.
+  auto read_frags = [&](int stg, int ks, TMx8 (&a)[4], TMx8 (&b)[4]) {
+    const TM* sa = lds + stg * STAGE;
+    const TB* sb = (const TB*)(lds + stg * STAGE + TOK);
+    const int ch = 2 * ks + lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const TBx8 w = *(const TBx8*)(sb + frag_off(128 * wc + 32 * i + lr, ch));
+      if constexpr (__is_same(TM, TB))
+        a[i] = w;
+      else
+        a[i] = __builtin_bit_cast(TMx8, bf16x8_to_f16x8(__builtin_bit_cast(u32x4, w)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *(const TMx8*)(sa + frag_off(128 * wt + 32 * j + lr, ch));
+  };
+  auto mfmas = [&](const TMx8 (&a)[4], const TMx8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+  };
+  // RoPE angles of the epilogue, fetched now so their latency hides under the
+  // main loop (the loads are older than every tile load, so the loop's vmcnt
+  // waits cover them)
+  RopePre rp[2];
+  const bool pre = seg.kind == kHead && seg.rope;
+  if (pre) {
+    rope_prefetch<D>(p, row0, 0, rp[0]);
+    rope_prefetch<D>(p, row0, 1, rp[1]);
+  }
+  // Each issue() is LPT loads per lane.  Wait until at most `n` later k-tiles
+  // are still in flight (vmcnt(LPT n); NST - 2 >= n, so at most 16).
+  // s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone: N's low 4 bits in
+  // [3:0], its high 2 bits in [15:14]
+  constexpr int W1 = (((1 * LPT) >> 4) << 14) | 0x0F70 | ((1 * LPT) & 15);
+  constexpr int W2 = (((2 * LPT) >> 4) << 14) | 0x0F70 | ((2 * LPT) & 15);
+  static_assert(2 * LPT < 64, "vmcnt holds 6 bits");
+  auto wait_tiles = [](int n) {
+    if (n >= 2)
+      __builtin_amdgcn_s_waitcnt(W2);
+    else if (n == 1)
+      __builtin_amdgcn_s_waitcnt(W1);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+  const int nk = (K + GBK - 1) / GBK;
+  for (int t = 0; t < NST - 1 && t < nk; ++t) issue(t, t);
+  wait_tiles(min(nk - 1, NST - 2));  // tile 0 landed
+  lds_barrier();
+  if (NST - 1 < nk) issue(NST - 1, NST - 1);
+  TMx8 fa[2][4], fb[2][4];
+  read_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;  // KS is even: the parity carries over
+      if (ks + 1 < KS) {
+        read_frags(kt % NST, ks + 1, fa[nxt], fb[nxt]);
+      } else if (kt + 1 < nk) {
+        // tile kt+1 is complete for this lane once only tiles kt+2 .. kt+NST-1 remain
+        wait_tiles(min(nk - 2 - kt, NST - 2));
+        lds_barrier();  // tile kt+1 visible; every read of tile kt done
+        if (kt + NST < nk) issue(kt + NST, (kt + NST) % NST);
+        read_frags((kt + 1) % NST, 0, fa[nxt], fb[nxt]);
+      }
+      mfmas(fa[cur], fb[cur]);
+    }
+  }
+
+  // Epilogue in two passes of 128 tokens (pass hf: token blocks 2hf, 2hf+1 of
+  // both token halves, tile row 64 wt + 32 jj + lr), each written out as two
+  // 128-column halves by the stores of the 256 x 128 kernel.  Register r of
+  // acc[i][j] is tile column 128 wc + 32 i + 8 (r/4) + 4 lg + r%4.
+  float* tile = (float*)smem;
+  // hf is a compile-time constant, so acc is only ever indexed statically
+  auto pass = [&](auto HF) {
+    constexpr int hf = decltype(HF)::value;
+    __syncthreads();  // LDS free (main loop, or the previous pass's stores)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * hf + jj;
+      const int trow = 64 * wt + 32 * jj + lr;
+      if (seg.kind == kHeadT) {  // tile [column][token]
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 128 * wc + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+            tile[c * CP_ + trow] = acc[i][j][r];
+          }
+      } else {  // tile [token][column], float4 runs
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int c = 128 * wc + 32 * i + 8 * a + 4 * lg;
+            *(float4*)(tile + trow * RP_ + c) =
+                make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2],
+                            acc[i][j][4 * a + 3]);
+          }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int chh = 0; chh < 2; ++chh) {
+      if (seg.kind == kHeadT)
+        store_cols<TO, D, CP_>(tile + 128 * chh * CP_, row0, hf, col0 + 128 * chh, seg, p);
+      else if (seg.kind == kHead && seg.rope)
+        store_rows_rope<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p,
+                                           &rp[hf]);
+      else
+        store_rows_plain<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p);
+    }
+  };
+  pass(std::integral_constant<int, 0>{});
+  pass(std::integral_constant<int, 1>{});
 }
 
 // --------------------------------------------------------------------------
@@ -618,12 +916,12 @@ __global__ __launch_bounds__(256) void gemm_simt(GemmProblem p, SegTiles st, lon
   epilogue_store<OutT, D, SM>(tile, row0, col0, seg, p);
 }
 
-SegTiles seg_tiles(const GemmProblem& p) {
+SegTiles seg_tiles(const GemmProblem& p, int tn = BN) {
   SegTiles st{};
   int t = 0;
   for (int s = 0; s < p.nseg; ++s) {
     st.tile0[s] = t;
-    t += (p.seg[s].width + BN - 1) / BN;
+    t += (p.seg[s].width + tn - 1) / tn;
   }
   for (int s = p.nseg; s < 5; ++s) st.tile0[s] = t;
   return st;
@@ -632,8 +930,35 @@ SegTiles seg_tiles(const GemmProblem& p) {
 }  // namespace
 
 hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s) {
+  // the MFMA kernels stage whole k-tiles of 32 (d % 64 == 0, d_down % 32 == 0)
+  if (dt == DAR_BF16 && p.K % 32 != 0) return hipErrorInvalidValue;
   const SegTiles st = seg_tiles(p);
   const int nC = st.tile0[p.nseg];
+  if (dt == DAR_BF16 && p.row_pos == nullptr && p.b_type == kBF16) {
+    // wide tiles once there are enough of them to fill every CU several times
+    const SegTiles sw = seg_tiles(p, WBN);
+    const int nCw = sw.tile0[p.nseg], nMw = (p.M + 255) / 256;
+    if ((long)nCw * nMw >= kWideMinTiles && p.K >= kWideMinK && p.K % 64 == 0 &&
+        p.a_type == kBF16) {
+      size_t wbytes = 0;
+      for (int i = 0; i < p.nseg; ++i) wbytes += (size_t)p.seg[i].width * p.K * 2;
+      // a band's weights about fill one XCD's L2 (4 MB)
+      const size_t tile_w = (size_t)WBN * p.K * 2;
+      int band = (int)((size_t)kWideBandBytes / tile_w);
+      band = band < 1 ? 1 : (band > nCw ? nCw : band);
+      if (wbytes <= (size_t)(2 << 20)) band = nCw;
+      const int total = nCw * nMw, per_xcd = (total + kNumXcd - 1) / kNumXcd;
+      const dim3 grid(per_xcd * kNumXcd);
+#define DAR_W(TA, TO, D)                                                                    \
+  hipLaunchKernelGGL((project_gemm_wide<TA, bf16, TO, D, 64>), grid, dim3(256), 0, s, p, sw, nMw, \
+                     nCw, band, per_xcd)
+      if (p.a_type == kBF16 && p.out_type == kF16) {
+        if (p.d_k == 64) DAR_W(bf16, f16, 64); else DAR_W(bf16, f16, 128);
+        return hipGetLastError();
+      }
+#undef DAR_W
+    }
+  }
   if (dt == DAR_BF16) {
     const int nM = (p.M + 2 * BM - 1) / (2 * BM);  // 256-token workgroup tiles
     const int nCp = (nC + kNumXcd - 1) / kNumXcd * kNumXcd;
