@@ -311,6 +311,34 @@ def cache_flusher(torch):
     return flush
 
 
+def timed_after_flush(torch, call, flush, steps, warmup):
+    """GPU time of one decode step read from a cold cache: each timed step is
+    the cache flush, then HIP events on the launch stream around the step's
+    kernels.  The step's launches are enqueued while the flush (a 1 GiB read)
+    still runs, so the events bracket the kernels back to back, with no host
+    launch time inside (a graph replay behind the flush added about 6 us of
+    start-up per step on this ROCm).  Sustained replays first settle the
+    clocks."""
+    t0 = time.time()
+    while time.time() - t0 < 1.0:
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return times
+
+
 def time_decode_drope(torch, dar, di, steps, warmup, cfg):
     """The decoupled-RoPE variant's decode step (dar_attn_decode_drope) at the
     long-context shape, timed like time_decode.  Bytes: the latent and rotary
@@ -331,23 +359,11 @@ def time_decode_drope(torch, dar, di, steps, warmup, cfg):
     ws = torch.empty(dar.decode_drope_workspace_bytes(B, ctx, ctx, H, d_k, d_R, d_down, w),
                      dtype=torch.uint8, device="cuda")
     flush = cache_flusher(torch)
-    g = capture(torch, lambda: dar.dar_attn_decode_drope(t["qC"], t["qR"], t["K_win"], t["V_win"],
-                                                         t["KR"], t["h_D"], Wk, Wv, ctx, w, o=o,
-                                                         workspace=ws))
-    settle(torch, g)
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        flush()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    del g
+
+    def call():
+        dar.dar_attn_decode_drope(t["qC"], t["qR"], t["K_win"], t["V_win"], t["KR"], t["h_D"], Wk,
+                                  Wv, ctx, w, o=o, workspace=ws)
+    times = timed_after_flush(torch, call, flush, steps, warmup)
     ms = float(np.median(times))
     n_lat = ctx - w
     byts = 2.0 * (B * n_lat * (d_down + d_R) + B * w * (2 * H * d_k + d_R) + 2 * d_down * H * d_k
@@ -382,26 +398,15 @@ def time_decode(torch, dar, di, steps, warmup, cfg, lens=None):
                      dtype=torch.uint8, device="cuda")
     flush = cache_flusher(torch)
     if lens is None:
-        g = capture(torch, lambda: dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o,
-                                                       workspace=ws))
+        def call():
+            dar.dar_attn_decode(q, K_win, V_win, h_D, Wk, Wv, ctx, w, o=o, workspace=ws)
     else:
         lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
-        g = capture(torch, lambda: dar.dar_attn_decode_varlen(q, K_win, V_win, h_D, Wk, Wv, lens_d,
-                                                              ctx, w, o=o, workspace=ws))
-    settle(torch, g)
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        flush()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    del g
+
+        def call():
+            dar.dar_attn_decode_varlen(q, K_win, V_win, h_D, Wk, Wv, lens_d, ctx, w, o=o,
+                                       workspace=ws)
+    times = timed_after_flush(torch, call, flush, steps, warmup)
     ms = float(np.median(times))
     if lens is None:
         byts, flops = decode_work(B, ctx, d, d_down, w, H)
