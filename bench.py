@@ -198,6 +198,57 @@ def time_prefill(torch, dar, s, H, d_k, w, steps, warmup):
     return wall, ev, graph_launch_ms(torch, proj), graph_launch_ms(torch, attn)
 
 
+def time_prefill_drope(torch, dar, di, cfg, d_R, steps, warmup):
+    """One prefill pass of the decoupled-RoPE variant (dar_project_drope +
+    dar_attn_prefill_drope) at cfg, timed like the headline step (a graph of
+    the timed steps).  Algorithmic FLOP: the projections (content, values and
+    latent; the rotary queries and the shared rotary key; the folded global
+    content keys and values) and, per causal pair and head, 2 (d_k + d_R) for
+    the score and 2 d_k for the value sum."""
+    B, N, d, H, d_k, w, d_down = cfg
+    inp = di.drope_prefill_inputs(B, N, d, H, d_k, d_down, d_R, seed0=4100)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(
+            torch.bfloat16).cuda()
+
+    W = {k: dev(inp[k].T) for k in ("W_down", "W_up", "W_Q", "W_K", "W_V", "W_QR", "W_KR")}
+    h = dev(inp["h"])
+    del inp
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    out = dar.dar_project_drope(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"],
+                                W["W_QR"], W["W_KR"], H, d_k, W_upK=Wk, W_upV=Wv)
+    o = torch.empty((B, N, H * d_k), dtype=torch.bfloat16, device="cuda")
+    # RoPE tables of width d_R: (64 + N/64) rows of d_R/2 (cos, sin) pairs, well under 1 MiB
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+
+    def step():
+        dar.dar_project_drope(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"],
+                              W["W_QR"], W["W_KR"], H, d_k, W_upK=Wk, W_upV=Wv, out=out,
+                              workspace=ws)
+        dar.dar_attn_prefill_drope(out, w, o=o)
+    warm = capture(torch, step, max(warmup, 1))
+    timed = capture(torch, step, steps)
+    settle(torch, warm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    timed.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del warm, timed
+    attn_ms = graph_launch_ms(torch, lambda: dar.dar_attn_prefill_drope(out, w, o=o))
+    proj_f = (2.0 * B * N * d * (3 * H * d_k + d_down + H * d_R + d_R)
+              + 4.0 * B * N * d_down * H * d_k)
+    attn_f = B * H * N * (N + 1) / 2.0 * (4.0 * d_k + 2.0 * d_R)
+    return {"workload": "decoupled-RoPE prefill B%d N%d d%d H%d dk%d dR%d w%d d_down%d"
+                        % (B, N, d, H, d_k, d_R, w, d_down),
+            "ms": ms, "TFLOP/s": (proj_f + attn_f) / ms / 1e9, "attn_ms": attn_ms,
+            "attn_TFLOP/s": attn_f / attn_ms / 1e9,
+            "attn_mfma_frac": attn_f / attn_ms / 1e9 / PEAK_BF16_TFLOPS}
+
+
 def chunk_flops(B, C, p0, d, d_down):
     """Algorithmic FLOP of one prefill chunk of C tokens after p0 cached ones:
     the chunk's projections, the prefix's global keys/values rebuilt from the
@@ -648,6 +699,11 @@ def main():
             del s3
             res["sweep"] = sweep
             cfg1b = (4, 8192, 2048, 16, 128, 512, 512)
+            pd = time_prefill_drope(torch, dar, di, cfg1b, 64, max(3, args.steps // 2), 2)
+            res["prefill_drope"] = pd
+            log("prefill (decoupled RoPE): %.3f ms, %.1f TFLOP/s (attention %.3f ms, %.1f%% of "
+                "MFMA peak)" % (pd["ms"], pd["TFLOP/s"], pd["attn_ms"], 100 * pd["attn_mfma_frac"]))
+            torch.cuda.empty_cache()
             ch = time_chunked(torch, dar, di, cfg1b, 2048, max(2, args.steps // 8))
             ch["workload"] = "1b prompt B4 N8192 in chunks of 2048 over the mixed cache"
             res["chunked_prefill"] = ch
