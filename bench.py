@@ -249,6 +249,63 @@ def time_prefill_drope(torch, dar, di, cfg, d_R, steps, warmup):
             "attn_mfma_frac": attn_f / attn_ms / 1e9 / PEAK_BF16_TFLOPS}
 
 
+def time_ragged_prefill(torch, dar, di, lens, d, H, d_k, w, d_down, reps):
+    """A batch of prompts of different lengths prefilled without padding
+    (dar_project_varlen + dar_attn_prefill_varlen) and, for comparison, padded
+    to the longest (dar_project + dar_attn_prefill).  Both report the
+    algorithmic FLOPs of the real tokens only."""
+    B, N, T = len(lens), max(lens), sum(lens)
+    inp = di.prefill_inputs(1, 1, d, H, d_k, d_down, dtype="bf16", seed0=6000)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(
+            torch.bfloat16).cuda()
+
+    W = {k: dev(inp[k].T) for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    h = torch.randn((T, d), device="cuda").to(torch.bfloat16)
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = torch.from_numpy(starts).cuda()
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    P = dar.dar_project_varlen(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                               cu, N, W_upK=Wk, W_upV=Wv, workspace=ws)
+    o = dar.dar_attn_prefill_varlen(P, cu, N, H, d_k, w)
+
+    def ragged():
+        dar.dar_project_varlen(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                               cu, N, W_upK=Wk, W_upV=Wv, out=P, workspace=ws)
+        dar.dar_attn_prefill_varlen(P, cu, N, H, d_k, w, o=o)
+    hp = torch.zeros((B, N, d), dtype=torch.bfloat16, device="cuda")
+    for b, n in enumerate(lens):
+        hp[b, :n] = h[starts[b]:starts[b + 1]]
+    outp = dar.dar_project(hp, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                           W_upK=Wk, W_upV=Wv)
+    op = torch.empty((B, N, H * d_k), dtype=torch.bfloat16, device="cuda")
+    wsp = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+
+    def padded():
+        dar.dar_project(hp, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                        W_upK=Wk, W_upV=Wv, out=outp, workspace=wsp)
+        dar.dar_attn_prefill(outp["Q"], outp["K_loc"], outp["V_loc"], outp["K_glob"],
+                             outp["V_glob"], w, o=op)
+    flops = sum(2.0 * n * (3 * d * d + 3 * d * d_down) + 2.0 * d * n * (n + 1) for n in lens)
+    res = {"workload": "ragged prefill of %d prompts, %d..%d tokens (%d in all), d%d H%d dk%d "
+                       "w%d d_down%d" % (B, min(lens), N, T, d, H, d_k, w, d_down)}
+    for name, fn in (("ragged", ragged), ("padded", padded)):
+        g = capture(torch, fn, reps)
+        settle(torch, g, 0.5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name + "_ms"] = ms
+        res[name + "_TFLOP/s"] = flops / ms / 1e9
+        del g
+    return res
+
+
 def chunk_flops(B, C, p0, d, d_down):
     """Algorithmic FLOP of one prefill chunk of C tokens after p0 cached ones:
     the chunk's projections, the prefix's global keys/values rebuilt from the
@@ -703,6 +760,15 @@ def main():
             res["prefill_drope"] = pd
             log("prefill (decoupled RoPE): %.3f ms, %.1f TFLOP/s (attention %.3f ms, %.1f%% of "
                 "MFMA peak)" % (pd["ms"], pd["TFLOP/s"], pd["attn_ms"], 100 * pd["attn_mfma_frac"]))
+            torch.cuda.empty_cache()
+            # a serving-like batch: 16 prompts spread over the 332 .. 1394-token
+            # contexts of the pages' downstream evaluations, at the 1B width
+            lens = [int(x) for x in np.linspace(332, 1394, 16)]
+            rp = time_ragged_prefill(torch, dar, di, lens, 2048, 16, 128, 512, 512,
+                                     max(3, args.steps // 2))
+            res["prefill_ragged"] = rp
+            log("ragged prefill: %.3f ms (%.1f TFLOP/s of real tokens) vs padded %.3f ms"
+                % (rp["ragged_ms"], rp["ragged_TFLOP/s"], rp["padded_ms"]))
             torch.cuda.empty_cache()
             ch = time_chunked(torch, dar, di, cfg1b, 2048, max(2, args.steps // 8))
             ch["workload"] = "1b prompt B4 N8192 in chunks of 2048 over the mixed cache"

@@ -35,7 +35,8 @@ EXPORTS = ("dar_abi_version", "dar_status_string", "dar_pack_weight", "dar_fold"
            "dar_attn_decode_varlen", "dar_decode_append_sigmoid",
            "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid",
            "dar_attn_decode_noalloc", "dar_attn_decode_drope", "dar_project_drope",
-           "dar_attn_prefill_drope", "dar_cache_from_prefill_drope", "dar_decode_append_drope")
+           "dar_attn_prefill_drope", "dar_cache_from_prefill_drope", "dar_decode_append_drope",
+           "dar_project_varlen", "dar_attn_prefill_varlen")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -109,6 +110,11 @@ def lib() -> ctypes.CDLL:
             _P] * 7 + [_SZ, _P]
         L.dar_attn_decode_drope.restype = _I
         L.dar_attn_decode_drope.argtypes = [_P] * 8 + [_I] * 8 + [_I, _P, _P, _SZ, _P]
+        L.dar_project_varlen.restype = _I
+        L.dar_project_varlen.argtypes = [_P] * 9 + [_I] * 7 + [ctypes.c_float, _I] + [_P] * 7 + [
+            _SZ, _P]
+        L.dar_attn_prefill_varlen.restype = _I
+        L.dar_attn_prefill_varlen.argtypes = [_P] * 6 + [_I] * 7 + [_P, _P]
         L.dar_attn_decode_varlen.restype = _I
         L.dar_attn_decode_varlen.argtypes = [_P] * 6 + [_I, _P] + [_I] * 6 + [
             ctypes.c_float, _I, _P, _P, _SZ, _P]
@@ -639,3 +645,58 @@ def dar_decode_append_drope(h, W_down, W_Q, W_K, W_V, W_QR, W_KR, heads: int, d_
             _ptr(h_D), _ptr(KR)]
     _call_ws("dar_decode_append_drope", lib().dar_decode_append_drope, args, workspace, h, stream)
     return qC, qR
+
+
+@_on_stream
+def dar_project_varlen(h, W_down, W_up, W_Q, W_K, W_V, heads: int, d_k: int, cu_seqlens,
+                       max_len: int, W_upK=None, W_upV=None, rope_base: float = 10000.0, out=None,
+                       workspace=None, stream=None):
+    """Projections of a ragged batch without padding: h [T, d] packs the
+    prompts, cu_seqlens (int32 device tensor, B + 1 entries) their starts.
+    Returns dict Q, K_loc, V_loc, K_glob, V_glob (flat fp16 tensors of
+    T*heads*d_k elements, one block per prompt; see varlen_block) and h_D
+    [T, d_down]."""
+    torch = _torch()
+    T, d = h.shape
+    d_down = W_down.shape[0]
+    B = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if out is None:
+        kw = dict(dtype=torch.float16, device=h.device)
+        n = T * heads * d_k
+        out = {k: torch.empty(n, **kw) for k in ("Q", "K_loc", "V_loc", "K_glob", "V_glob")}
+        out["h_D"] = torch.empty((T, d_down), **kw)
+    args = [_ptr(h), _ptr(W_down), _ptr(W_up), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_upK),
+            _ptr(W_upV), _ptr(cu_seqlens), B, T, int(max_len), d, d_down, heads, d_k,
+            float(rope_base), _dtype_code(h)]
+    args += [_ptr(out[k]) for k in ("Q", "K_loc", "V_loc", "h_D", "K_glob", "V_glob")]
+    _call_ws("dar_project_varlen", lib().dar_project_varlen, args, workspace, h, stream)
+    return out
+
+
+def varlen_block(x, starts, b: int, heads: int, d_k: int, transposed: bool = False):
+    """Prompt b's block of a packed head-major array from dar_project_varlen:
+    a view [heads, len_b, d_k] ([heads, d_k, len_b] for V).  starts: the
+    prompts' start rows as host integers (cu_seqlens on the host)."""
+    lo, hi = int(starts[b]), int(starts[b + 1])
+    blk = x[lo * heads * d_k:hi * heads * d_k]
+    return blk.view(heads, d_k, hi - lo) if transposed else blk.view(heads, hi - lo, d_k)
+
+
+@_on_stream
+def dar_attn_prefill_varlen(P, cu_seqlens, max_len: int, heads: int, d_k: int, w: int, o=None,
+                            stream=None):
+    """Attention of a ragged batch from dar_project_varlen's outputs P.
+    Returns o [T, heads*d_k] (bf16)."""
+    torch = _torch()
+    T = P["h_D"].shape[0]
+    B = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((T, heads * d_k), dtype=torch.bfloat16, device=P["Q"].device)
+    st = lib().dar_attn_prefill_varlen(_ptr(P["Q"]), _ptr(P["K_loc"]), _ptr(P["V_loc"]),
+                                       _ptr(P["K_glob"]), _ptr(P["V_glob"]), _ptr(cu_seqlens), B,
+                                       T, int(max_len), heads, d_k, int(w),
+                                       _dtype_code(P["Q"]), _ptr(o), _stream(stream))
+    _check("dar_attn_prefill_varlen", st)
+    return o

@@ -468,7 +468,7 @@ __global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefil
   static_assert(DR == 0 || !CHUNK, "the rotary part covers whole prefills");
   constexpr int NQ = (D + DR) / 16;  // 16-wide steps of the score contraction
   __shared__ PassSmem<D, DR> sm;
-  const int N = p.N, H = p.H, BH = p.B * p.H, w = p.w;
+  const int H = p.H, BH = p.B * p.H, w = p.w;
   // paired: a workgroup takes query tile nQT-1-pr and then tile pr, so every
   // workgroup streams about the same number of key tiles.  Unpaired: one
   // tile per workgroup, longest first (nPair = nQT).  With remap, all tiles
@@ -492,14 +492,29 @@ __global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefil
     }
   }
   const int b = bh / H, h = bh % H;
+  // Sequence b: N tokens.  Ragged batches (cu, whole prefills only): its rows
+  // cu[b] .. cu[b+1]-1 of the packed arrays, clamped into [0, T], each array
+  // holding one [H, N, D] block (V: [H, D, N]) per sequence from row cu[b].
+  int N = p.N;
+  size_t seq0 = 0;
+  if (!CHUNK && p.cu != nullptr) {
+    const int c0 = min(max(p.cu[b], 0), p.T), c1 = min(max(p.cu[b + 1], c0), p.T);
+    N = c1 - c0;
+    seq0 = (size_t)c0;
+  }
   // Positions: queries q0 .. N-1 (Q and o hold those rows only), keys 0 .. N-1
   // in the global arrays, keys loc0 .. N-1 in the local arrays.
   const int q0 = CHUNK ? p.q0 : 0, loc0 = CHUNK ? p.loc0 : 0, nqr = N - q0, nloc = N - loc0;
-  const f16* Qp = (const f16*)p.Q + (size_t)bh * nqr * D;
-  const f16* Kg = (const f16*)p.K_glob + (size_t)bh * N * D;
-  const f16* Kl = (const f16*)p.K_loc + (size_t)bh * nloc * D;
-  const f16* Vg = (const f16*)p.V_glob + (size_t)bh * N * D;
-  const f16* Vl = (const f16*)p.V_loc + (size_t)bh * nloc * D;
+  // first element of (batch, head)'s slice of an array of `rows` rows per sequence
+  auto slice = [&](int rows) {
+    return p.cu != nullptr && !CHUNK ? (seq0 * H + (size_t)h * N) * D : (size_t)bh * rows * D;
+  };
+  const f16* Qp = (const f16*)p.Q + slice(nqr);
+  const f16* Kg = (const f16*)p.K_glob + slice(N);
+  const f16* Kl = (const f16*)p.K_loc + slice(nloc);
+  const f16* Vg = (const f16*)p.V_glob + slice(N);
+  const f16* Vl = (const f16*)p.V_loc + slice(nloc);
+  const size_t orow0 = p.cu != nullptr && !CHUNK ? seq0 : (size_t)b * nqr;  // o's first row
   // rotary keys of sequence b (positions 0 .. N-1, every head) and queries
   const f16* KRb = DR > 0 ? (const f16*)p.KR + (size_t)b * N * DR : nullptr;
   const f16* QRp = DR > 0 ? (const f16*)p.QR + (size_t)bh * N * DR : nullptr;
@@ -522,6 +537,7 @@ __global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefil
     const int qt = qn == 0 ? q_hi : pr;
     if (qn > 0) __syncthreads();  // the LDS buffers are reused
     const int i0 = q0 + qt * QT, qw0 = i0 + 32 * wave;
+    if (i0 >= N) continue;  // past a short sequence of a ragged batch (uniform per workgroup)
     const int qi = qw0 + lr;  // this lane's query
     const int i_last = min(i0 + QT - 1, N - 1);
     const int wi_last = min(qw0 + 31, N - 1);
@@ -618,7 +634,7 @@ __global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefil
       // computing the 64-bit address before the pass loop and holding it)
       int qr = qi - q0;
       __asm__ volatile("" : "+v"(qr));
-      bf16* out = (bf16*)p.o + ((size_t)b * nqr + qr) * (size_t)(H * D) + (size_t)h * D;
+      bf16* out = (bf16*)p.o + (orow0 + qr) * (size_t)(H * D) + (size_t)h * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -726,6 +742,7 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
                      paired)
     if (chunk && p.lse != nullptr) return hipErrorInvalidValue;
     const bool lse = p.lse != nullptr;
+    if (p.cu != nullptr && (chunk || lse || p.d_R > 0 || p.T < 1)) return hipErrorInvalidValue;
     if (p.d_R > 0) {  // decoupled-RoPE variant: whole prefill, d_R = 64
       if (chunk || lse || p.d_R != 64) return hipErrorInvalidValue;
       if (p.d_k == 64)
@@ -747,6 +764,7 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
     }
 #undef DAR_ATTN
   } else {
+    if (p.cu != nullptr) return hipErrorInvalidValue;  // ragged batches: bf16 mode
     const dim3 grid((p.N + FQ - 1) / FQ, p.H, p.B);
     if (p.d_k == 64)
       hipLaunchKernelGGL(attn_prefill_f32<64>, grid, dim3(256), 0, s, p);

@@ -93,7 +93,8 @@ static dar_status project_impl(const void* h, const void* W_down, const void* W_
                                int d_down, int heads, int d_k, int pos0, float rope_base,
                                dar_dtype dtype, void* Q, void* K_loc, void* V_loc, void* h_D,
                                void* K_glob, void* V_glob, void* workspace,
-                               size_t* workspace_bytes, hipStream_t stream, int act) {
+                               size_t* workspace_bytes, hipStream_t stream, int act,
+                               const int* cu = nullptr, int n_cu = 0, int max_len = 0) {
   if (!dtype_ok(dtype) || workspace_bytes == nullptr) return DAR_ERR_INVALID_ARG;
   if (B < 1 || N < 1 || d < 1 || d_down < 1 || heads < 1 || d_k < 2 || (d_k & 1) || pos0 < 0)
     return DAR_ERR_INVALID_ARG;
@@ -118,7 +119,8 @@ static dar_status project_impl(const void* h, const void* W_down, const void* W_
   if (!head_supported(d_k) || d % 64 || d_down % 32 || d_down > 1024 || hd % 64)
     return DAR_ERR_UNSUPPORTED;
 
-  const long max_pos = (long)pos0 + N - 1;
+  // ragged rows: positions 0 .. max_len - 1 within each sequence
+  const long max_pos = cu != nullptr ? (long)max_len - 1 : (long)pos0 + N - 1;
   const size_t rope_bytes = rope_table_bytes(d_k, max_pos);
   const size_t fold_bytes = have_fold ? 0 : 2 * round256(es * d_down * hd);
   const size_t need_bytes = rope_bytes + fold_bytes;
@@ -173,6 +175,11 @@ static dar_status project_impl(const void* h, const void* W_down, const void* W_
   g1.d_k = d_k;
   g1.pos0 = pos0;
   g1.rope = rope;
+  if (cu != nullptr) {
+    g1.cu = cu;
+    g1.n_cu = n_cu;
+    g1.pos_max = (int)max_pos;
+  }
   e = launch_project_gemm(g1, dtype, stream);
   if (e != hipSuccess) return DAR_ERR_HIP;
 
@@ -264,6 +271,52 @@ dar_status dar_attn_prefill_lse(const void* Q, const void* K_loc, const void* V_
   if (!aligned16(lse)) return DAR_ERR_INVALID_ARG;
   return attn_prefill_impl(Q, K_loc, V_loc, K_glob, V_glob, B, N, heads, d_k, w, dtype, o, lse,
                            stream);
+}
+
+dar_status dar_project_varlen(const void* h, const void* W_down, const void* W_up,
+                              const void* W_Q, const void* W_K, const void* W_V,
+                              const void* W_upK, const void* W_upV, const int* cu_seqlens, int B,
+                              int T, int max_len, int d, int d_down, int heads, int d_k,
+                              float rope_base, dar_dtype dtype, void* Q, void* K_loc,
+                              void* V_loc, void* h_D, void* K_glob, void* V_glob,
+                              void* workspace, size_t* workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || B < 1 || T < 1 || max_len < 1 || max_len > T ||
+      ((uintptr_t)cu_seqlens & 3u) != 0 || cu_seqlens == nullptr)
+    return DAR_ERR_INVALID_ARG;
+  const Span cs{cu_seqlens, sizeof(int) * ((size_t)B + 1)};
+  const Span outs[6] = {{Q, 2 * (size_t)T * heads * d_k},     {K_loc, 2 * (size_t)T * heads * d_k},
+                        {V_loc, 2 * (size_t)T * heads * d_k}, {h_D, 2 * (size_t)T * d_down},
+                        {K_glob, 2 * (size_t)T * heads * d_k}, {V_glob, 2 * (size_t)T * heads * d_k}};
+  for (const Span& x : outs)
+    if (overlap(cs, x)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  return project_impl(h, W_down, W_up, W_Q, W_K, W_V, W_upK, W_upV, 1, T, d, d_down, heads, d_k, 0,
+                      rope_base, dtype, Q, K_loc, V_loc, h_D, K_glob, V_glob, workspace,
+                      workspace_bytes, stream, 0, cu_seqlens, B, max_len);
+}
+
+dar_status dar_attn_prefill_varlen(const void* Q, const void* K_loc, const void* V_loc,
+                                   const void* K_glob, const void* V_glob, const int* cu_seqlens,
+                                   int B, int T, int max_len, int heads, int d_k, int w,
+                                   dar_dtype dtype, void* o, hipStream_t stream) {
+  if (!dtype_ok(dtype) || B < 1 || T < 1 || max_len < 1 || max_len > T || heads < 1 || d_k < 2 ||
+      (d_k & 1) || w < 0 || cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u) != 0)
+    return DAR_ERR_INVALID_ARG;
+  const void* need[] = {Q, K_loc, V_loc, K_glob, V_glob, o};
+  for (const void* ptr : need)
+    if (!aligned16(ptr)) return DAR_ERR_INVALID_ARG;
+  const size_t sz = 2 * (size_t)T * heads * d_k;
+  const Span ins[6] = {{Q, sz},      {K_loc, sz}, {V_loc, sz},
+                       {K_glob, sz}, {V_glob, sz}, {cu_seqlens, sizeof(int) * ((size_t)B + 1)}};
+  const Span outs[1] = {{o, sz}};
+  if (!disjoint(outs, 1, ins, 6)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!head_supported(d_k)) return DAR_ERR_UNSUPPORTED;
+  if ((size_t)T * heads * d_k > 0x7fffffffffffL) return DAR_ERR_UNSUPPORTED;
+  PrefillProblem p{Q, K_loc, V_loc, K_glob, V_glob, o, B, max_len, heads, d_k, w};
+  p.cu = cu_seqlens;
+  p.T = T;
+  return hip_status(launch_attn_prefill(p, dtype, stream));
 }
 
 dar_status dar_attn_prefill_backward(const void* Q, const void* K_loc, const void* V_loc,

@@ -189,6 +189,14 @@ struct GemmProblem {
   // row.  Null: position pos0 + n.
   const int* row_pos = nullptr;
   int pos_max = 0;
+  // Ragged prefill: rows cu[b] .. cu[b+1]-1 (device, int32, n_cu + 1 entries)
+  // are sequence b's tokens at positions pos0 + 0, 1, ... (clamped to
+  // pos_max); each head-major output holds one [H, len_b, d_k] (V: [H, d_k,
+  // len_b]) block per sequence starting at row cu[b] (seg.ld_seq must be 0).
+  // Rows outside their sequence (inconsistent cu) are not written.  Null:
+  // n_seq rows per sequence.
+  const int* cu = nullptr;
+  int n_cu = 0;
 };
 
 hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s);
@@ -214,6 +222,12 @@ struct PrefillProblem {
   const void* QR = nullptr;
   const void* KR = nullptr;
   int d_R = 0;
+  // Ragged prefill (bf16, whole prefills, no lse / rotary part): B sequences,
+  // sequence b the rows cu[b] .. cu[b+1]-1 (device, int32) of the packed
+  // arrays, each source held as one [H, len_b, d_k] (V: [H, d_k, len_b])
+  // block per sequence from row cu[b]; o [T, H d_k]; N is the longest length.
+  const int* cu = nullptr;
+  int T = 0;
 };
 hipError_t launch_attn_prefill(const PrefillProblem& p, dar_dtype dt, hipStream_t s);
 

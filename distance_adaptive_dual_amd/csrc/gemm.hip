@@ -217,7 +217,10 @@ __device__ void epilogue_store(const float* tile, int row0, int col0, const Gemm
 // RP (compile time): the problem carries row_pos.
 template <bool RP>
 __device__ __forceinline__ int row_position(const GemmProblem& p, int b, int n) {
-  if constexpr (!RP) return p.pos0 + n;
+  if constexpr (!RP) {
+    const int q = p.pos0 + n;  // ragged rows: clamped into the tables
+    return p.cu != nullptr ? min(max(q, 0), p.pos_max) : q;
+  }
   const int q = p.row_pos[b];
   return q < 0 ? 0 : (q > p.pos_max ? p.pos_max : q);
 }
@@ -229,6 +232,52 @@ __device__ __forceinline__ int out_index(const GemmProblem& p, const GemmSeg& se
   if (seg.pos_mode == kPosFixed) return n + seg.seq_off;
   const int q = row_position<RP>(p, b, n);
   return seg.pos_mode == kPosRing ? q % ld : min(q, ld - 1);
+}
+
+// Where GEMM row `grow` goes: its sequence b, its index n and the sequence's
+// length, and the output's row base and sequence stride.  Head-major outputs
+// put token n of head `head` at row base * H + head * ld + n (V: column
+// base * H * D + (head * D + t) * ld + n); row-major ones at row base + n.
+// Uniform sequences: base = b * ld.  Ragged (cu): one block per sequence at
+// its first row, the sequence's row range clamped into [0, M]; `ok` is false
+// for a row outside the range found (inconsistent cu), which is not written.
+struct RowLoc {
+  int b, n, len, ld;
+  size_t base;
+  bool ok;
+};
+
+__device__ __forceinline__ RowLoc row_loc(const GemmProblem& p, const GemmSeg& seg, int grow) {
+  RowLoc r;
+  if (p.cu != nullptr) {
+    int lo = 0, hi = p.n_cu;  // the last b with cu[b] <= grow
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.cu[mid] <= grow) lo = mid; else hi = mid;
+    }
+    const int c0 = min(max(p.cu[lo], 0), p.M), c1 = min(max(p.cu[lo + 1], c0), p.M);
+    r.b = lo;
+    r.n = grow - c0;
+    r.len = c1 - c0;
+    r.ld = r.len;
+    r.base = (size_t)c0;
+    r.ok = r.n >= 0 && r.n < r.len;
+  } else {
+    const int Nq = p.n_seq;
+    r.b = grow / Nq;
+    r.n = grow % Nq;
+    r.len = Nq;
+    r.ld = seg.ld_seq ? seg.ld_seq : Nq;
+    r.base = (size_t)r.b * r.ld;
+    r.ok = true;
+  }
+  return r;
+}
+
+// RoPE position of row n of a sequence (ragged rows clamped into the tables).
+__device__ __forceinline__ int seq_position(const GemmProblem& p, int n) {
+  const int q = p.pos0 + n;
+  return p.cu != nullptr ? min(max(q, 0), p.pos_max) : q;
 }
 
 __device__ __forceinline__ int epi_row(int row0, int hf, int r) {
@@ -257,8 +306,7 @@ __device__ __forceinline__ void rope_cs8(const RopeTab& t, int pos, int t0, floa
 template <typename OutT, int D, bool RP, int PITCH = EPI_P>
 __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, int hf, int col0,
                                                  const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
-  const int ld = seg.ld_seq ? seg.ld_seq : Nq;
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
   OutT* out = (OutT*)seg.out;
   // chunk q = tid + 256 k: column chunk (q & 7) + 8 (q >> 10), tile row (q >> 3) & 127;
   // chunks k and k + 4 share the row
@@ -267,7 +315,9 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
     const int r = ((tid >> 3) + 32 * k) & 127;
     const int grow = epi_row(row0, hf, r);
     if (grow >= M) continue;
-    const int b = grow / Nq, no = out_index<RP>(p, seg, b, grow % Nq, ld);
+    const RowLoc L = row_loc(p, seg, grow);
+    if (!L.ok) continue;
+    const int no = out_index<RP>(p, seg, L.b, L.n, L.ld);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int c = 8 * ((tid & 7) + 8 * h2);
@@ -277,11 +327,11 @@ __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, in
       read8(tile + r * PITCH + c, v);
       OutT* dst;
       if (seg.kind == kRowMajor) {
-        dst = out + ((size_t)b * ld + no) * width + gcol;
+        dst = out + (L.base + no) * width + gcol;
         if (seg.act) sigmoid8(v);
       } else {
         const int head = gcol / D, t = gcol % D;
-        dst = out + (((size_t)b * H + head) * ld + no) * D + t;
+        dst = out + (L.base * H + (size_t)head * L.ld + no) * D + t;
       }
       store_run<OutT, 8>(dst, v);
     }
@@ -306,8 +356,9 @@ __device__ __forceinline__ void rope_prefetch(const GemmProblem& p, int row0, in
   constexpr int PCH = D / 16;
   const int tid = threadIdx.x, w8 = tid & 7, t0 = 8 * (w8 % PCH);
   const int grow0 = epi_row(row0, hf, 4 * (tid >> 3));
-  const int n0 = (grow0 < p.M ? grow0 : 0) % p.n_seq;
-  rope_cs8(p.rope, p.pos0 + n0, t0, r.cs);
+  GemmSeg none{};
+  const RowLoc L = row_loc(p, none, grow0 < p.M ? grow0 : 0);
+  rope_cs8(p.rope, seq_position(p, L.ok ? L.n : 0), t0, r.cs);
   const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -322,8 +373,7 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
                                                 const GemmSeg& seg, const GemmProblem& p,
                                                 const RopePre* pre = nullptr) {
   constexpr int HALF = D / 2, PCH = D / 16;  // pair chunks of 8 per head
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
-  const int ld = seg.ld_seq ? seg.ld_seq : Nq;
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
   OutT* out = (OutT*)seg.out;
   const int w8 = tid & 7, r0 = 4 * (tid >> 3);
   const int hl = w8 / PCH, t0 = 8 * (w8 % PCH);
@@ -332,17 +382,18 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
   const int grow0 = epi_row(row0, hf, r0);
   if (gcol >= width || grow0 >= M) return;
   const int head = gcol / D;
-  const int b0 = grow0 / Nq, n0 = grow0 % Nq;
-  const bool consec = grow0 + 3 < M && n0 + 3 < Nq;  // one sequence, consecutive positions
+  const RowLoc L0 = row_loc(p, seg, grow0);
+  // one sequence, consecutive positions
+  const bool consec = L0.ok && grow0 + 3 < M && L0.n + 3 < L0.len;
   float2 cs[8], step[8];
-  if (!RP && pre != nullptr) {
+  if (!RP && pre != nullptr && consec) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       cs[i] = pre->cs[i];
       step[i] = pre->step[i];
     }
   } else {
-    rope_cs8(p.rope, row_position<RP>(p, b0, n0), t0, cs);
+    rope_cs8(p.rope, row_position<RP>(p, L0.b, L0.n), t0, cs);
     if (consec) {
       const float4* st = (const float4*)(p.rope.lo + p.rope.half + t0);
 #pragma unroll
@@ -355,7 +406,8 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
   }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    int b = b0, n = n0 + kk;
+    RowLoc L = L0;
+    L.n += kk;
     if (kk > 0) {
       if (consec) {
 #pragma unroll
@@ -365,11 +417,11 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
       } else {
         const int grow = grow0 + kk;
         if (grow >= M) break;
-        b = grow / Nq;
-        n = grow % Nq;
-        rope_cs8(p.rope, row_position<RP>(p, b, n), t0, cs);
+        L = row_loc(p, seg, grow);
+        rope_cs8(p.rope, row_position<RP>(p, L.b, L.n), t0, cs);
       }
     }
+    if (!L.ok) continue;
     float x[8], y[8], a[8], bb[8];
     read8(tile + (r0 + kk) * PITCH + c, x);
     read8(tile + (r0 + kk) * PITCH + c + HALF, y);
@@ -378,7 +430,8 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
       a[i] = x[i] * cs[i].x - y[i] * cs[i].y;
       bb[i] = x[i] * cs[i].y + y[i] * cs[i].x;
     }
-    OutT* dst = out + (((size_t)b * H + head) * ld + out_index<RP>(p, seg, b, n, ld)) * D + t0;
+    OutT* dst =
+        out + (L.base * H + (size_t)head * L.ld + out_index<RP>(p, seg, L.b, L.n, L.ld)) * D + t0;
     store_run<OutT, 8>(dst, a);
     store_run<OutT, 8>(dst + HALF, bb);
   }
@@ -388,16 +441,17 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
 template <typename OutT, int D, int TP>
 __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, int col0,
                                            const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads, Nq = p.n_seq;
-  const int ld = seg.ld_seq ? seg.ld_seq : Nq;  // output sequence stride
+  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
   OutT* out = (OutT*)seg.out;
   const int tc = tid & 7;  // chunk of 8 tokens within the 64-token run
 #pragma unroll
   for (int run = 0; run < 2; ++run) {
     const int grow0 = row0 + 128 * run + 64 * hf + 8 * tc;
     if (grow0 >= M) continue;
-    const int b0 = grow0 / Nq, n0 = grow0 % Nq, no0 = n0 + seg.seq_off;
-    const bool fast = (grow0 + 8 <= M) && (n0 + 8 <= Nq) && ((no0 & 7) == 0) && ((ld & 7) == 0);
+    const RowLoc L0 = row_loc(p, seg, grow0);
+    const int no0 = L0.n + seg.seq_off;
+    const bool fast = L0.ok && (grow0 + 8 <= M) && (L0.n + 8 <= L0.len) && ((no0 & 7) == 0) &&
+                      ((L0.ld & 7) == 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = (tid >> 3) + 32 * k;
@@ -407,14 +461,16 @@ __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, 
       float v[8];
       read8(tile + c * TP + 64 * run + 8 * tc, v);
       if (fast) {
-        store_run<OutT, 8>(out + (((size_t)b0 * H + head) * D + t) * ld + no0, v);
+        store_run<OutT, 8>(out + L0.base * H * D + ((size_t)head * D + t) * L0.ld + no0, v);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int grow = grow0 + i;
           if (grow >= M) break;
-          const int b = grow / Nq, n = grow % Nq;
-          out[(((size_t)b * H + head) * D + t) * ld + n + seg.seq_off] = from_f32<OutT>(v[i]);
+          const RowLoc L = row_loc(p, seg, grow);
+          if (!L.ok) continue;
+          out[L.base * H * D + ((size_t)head * D + t) * L.ld + L.n + seg.seq_off] =
+              from_f32<OutT>(v[i]);
         }
       }
     }
@@ -576,8 +632,9 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   // Register r of acc[i][j] is column 32*cb_i + 8*(r/4) + 4*lg + r%4, token
   // 128*wt + 32*j + lr of the workgroup tile.
   float* tile = (float*)smem;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  // hf is a compile-time constant, so acc is only ever indexed statically
+  auto pass = [&](auto HF) {
+    constexpr int hf = decltype(HF)::value;
     __syncthreads();  // LDS free (main loop, or the previous pass's stores)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -610,7 +667,9 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
       store_rows_rope<TO, D, RP>(tile, row0, hf, col0, seg, p);
     else
       store_rows_plain<TO, D, RP>(tile, row0, hf, col0, seg, p);
-  }
+  };
+  pass(std::integral_constant<int, 0>{});
+  pass(std::integral_constant<int, 1>{});
 }
 
 // --------------------------------------------------------------------------
@@ -932,6 +991,9 @@ SegTiles seg_tiles(const GemmProblem& p, int tn = BN) {
 hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s) {
   // the MFMA kernels stage whole k-tiles of 32 (d % 64 == 0, d_down % 32 == 0)
   if (dt == DAR_BF16 && p.K % 32 != 0) return hipErrorInvalidValue;
+  // ragged rows: bf16 MFMA kernels, positions from the sequence starts only
+  if (p.cu != nullptr && (dt != DAR_BF16 || p.row_pos != nullptr || p.n_cu < 1))
+    return hipErrorInvalidValue;
   const SegTiles st = seg_tiles(p);
   const int nC = st.tile0[p.nseg];
   if (dt == DAR_BF16 && p.row_pos == nullptr && p.b_type == kBF16) {

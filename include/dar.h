@@ -182,6 +182,42 @@ dar_status dar_attn_prefill(const void* Q, const void* K_loc, const void* V_loc,
                             size_t* workspace_bytes, hipStream_t stream);
 
 /*
+ * Ragged prefill: a batch of B prompts of different lengths without padding
+ * (the inference remark after Eq. (5): a serving batch holds prompts of
+ * several lengths).  cu_seqlens (device, int32, B + 1 entries, nondecreasing,
+ * cu_seqlens[0] = 0, cu_seqlens[B] = T) puts prompt b at rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of the packed input; its tokens sit at
+ * positions 0, 1, ... of their own prompt; max_len bounds every length (the
+ * RoPE tables' reach).  The packed intermediates hold one block per prompt,
+ * at element offset cu_seqlens[b] * heads * d_k, laid out as a one-prompt
+ * dar_project would (Q, K_loc, K_glob [heads, len_b, d_k]; V_loc, V_glob
+ * [heads, d_k, len_b]); h_D is [T, d_down].  bf16 mode only.  The lengths are
+ * read on the device only: inconsistent values are clamped so that every
+ * access stays in bounds, and the rows they describe are not computed.
+ *
+ * dar_project_varlen -- Eqs. (1)-(3) and q = h W_Q over h [T, d]; weights,
+ * folded weights and workspace as for dar_project (the query covers max_len
+ * positions).
+ */
+dar_status dar_project_varlen(const void* h, const void* W_down, const void* W_up,
+                              const void* W_Q, const void* W_K, const void* W_V,
+                              const void* W_upK, const void* W_upV, const int* cu_seqlens, int B,
+                              int T, int max_len, int d, int d_down, int heads, int d_k,
+                              float rope_base, dar_dtype dtype, void* Q, void* K_loc,
+                              void* V_loc, void* h_D, void* K_glob, void* V_glob,
+                              void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * dar_attn_prefill_varlen -- Eq. (4) with the Eq. (3) selection for every
+ * prompt of a ragged batch, from dar_project_varlen's packed outputs;
+ * o [T, heads*d_k] (bf16), row t the query at packed row t.  No workspace.
+ */
+dar_status dar_attn_prefill_varlen(const void* Q, const void* K_loc, const void* V_loc,
+                                   const void* K_glob, const void* V_glob, const int* cu_seqlens,
+                                   int B, int T, int max_len, int heads, int d_k, int w,
+                                   dar_dtype dtype, void* o, hipStream_t stream);
+
+/*
  * dar_attn_prefill_lse -- dar_attn_prefill that also stores, for training,
  * each query's softmax normaliser of Eq. (4):
  *   lse [B, heads, N] float32, lse_i = log sum_{j <= i} exp(q_i . k_j / sqrt(d_k))

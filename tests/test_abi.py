@@ -519,3 +519,49 @@ def test_pack_weight_rejects():
     assert L.dar_pack_weight(None, 64, 64, 1, F(1), None) == INVALID
     assert L.dar_pack_weight(F(0), 64, 64, 7, F(1), None) == INVALID       # unknown dtype
     assert L.dar_pack_weight(F(0), 64 * 65536, 1, 1, F(1), None) == UNSUP
+
+
+def project_varlen(**kw):
+    a = dict(h=F(0), W_down=F(1), W_up=F(2), W_Q=F(3), W_K=F(4), W_V=F(5), W_upK=F(6), W_upV=F(7),
+             cu=F(8), B=3, T=500, max_len=300, d=256, d_down=64, heads=4, d_k=64, base=10000.0,
+             dtype=1, Q=F(10), K_loc=F(11), V_loc=F(12), h_D=F(13), K_glob=F(14), V_glob=F(15),
+             ws=None, wsb=0)
+    a.update(kw)
+    n = ctypes.c_size_t(a["wsb"])
+    keys = ("h", "W_down", "W_up", "W_Q", "W_K", "W_V", "W_upK", "W_upV", "cu", "B", "T",
+            "max_len", "d", "d_down", "heads", "d_k", "base", "dtype", "Q", "K_loc", "V_loc",
+            "h_D", "K_glob", "V_glob", "ws")
+    st = dar.lib().dar_project_varlen(*[a[k] for k in keys], ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_project_varlen_size_query_and_rejects():
+    st, n = project_varlen()
+    assert st == OK and n > 0
+    assert project_varlen(max_len=501)[0] == INVALID   # longer than the packed batch
+    assert project_varlen(max_len=0)[0] == INVALID
+    assert project_varlen(cu=None)[0] == INVALID
+    assert project_varlen(cu=F(8) + 2)[0] == INVALID   # int32 alignment
+    assert project_varlen(cu=F(10))[0] == INVALID      # lengths alias an output
+    assert project_varlen(dtype=0)[0] == UNSUP
+    assert project_varlen(d_k=96)[0] == UNSUP
+    assert project_varlen(ws=F(30), wsb=n - 1)[0] == WS
+
+
+def attn_varlen(**kw):
+    a = dict(Q=F(0), K_loc=F(1), V_loc=F(2), K_glob=F(3), V_glob=F(4), cu=F(5), B=3, T=500,
+             max_len=300, heads=4, d_k=64, w=16, dtype=1, o=F(6))
+    a.update(kw)
+    keys = ("Q", "K_loc", "V_loc", "K_glob", "V_glob", "cu", "B", "T", "max_len", "heads", "d_k",
+            "w", "dtype", "o")
+    return dar.lib().dar_attn_prefill_varlen(*[a[k] for k in keys], None)
+
+
+def test_attn_prefill_varlen_rejects():
+    assert attn_varlen(w=-1) == INVALID
+    assert attn_varlen(max_len=501) == INVALID
+    assert attn_varlen(o=F(5)) == INVALID       # output aliases the lengths
+    assert attn_varlen(o=F(0)) == INVALID       # output aliases Q
+    assert attn_varlen(cu=None) == INVALID
+    assert attn_varlen(dtype=0) == UNSUP
+    assert attn_varlen(d_k=32) == UNSUP

@@ -15,6 +15,11 @@ The signature of that miscompile in the assembly is an `s_and_saveexec_b64
 sX, ...` followed directly by `s_or_b64 exec, exec, sX`: a divergent block
 whose body was lost.  This test compiles every HIP source of the library to
 gfx950 assembly and requires that no kernel contains one.
+
+The same compilation reports each kernel's resources: no kernel may use
+scratch (register spills) apart from the ones listed in KNOWN_SPILLS.  A
+change that makes the compiler index an accumulator array dynamically (an
+epilogue loop it stops unrolling) shows up here as hundreds of bytes per lane.
 """
 import concurrent.futures as cf
 import os
@@ -58,24 +63,56 @@ def test_detector_finds_an_empty_block():
     assert empty_exec_blocks(asm) == [("_Zkernel", 2)]
 
 
+# Kernels whose spills are known (and measured): the attention backward's
+# dK/dV kernel (one wave per SIMD at d_k 128, 512 registers) and the d_k 64
+# forward that also stores the log-sum-exp (training only).
+KNOWN_SPILLS = ("bwd_dkv_mfma", "attn_prefill_f16ILi64ELb0ELb1E")
+
+
 def _compile(src, out_dir):
     out = os.path.join(out_dir, os.path.basename(src) + ".s")
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
            "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-S",
-           "--cuda-device-only", src, "-o", out]
+           "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage", src, "-o", out]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert r.returncode == 0, r.stdout[-2000:]
     with open(out) as fh:
-        return os.path.basename(src), fh.read()
+        return os.path.basename(src), fh.read(), r.stdout
 
 
-def test_no_kernel_has_an_empty_exec_block():
+@pytest.fixture(scope="module")
+def compiled():
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     tmp = tempfile.mkdtemp(prefix="dar_asm_")
     try:
         with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-            results = list(ex.map(lambda s: _compile(s, tmp), srcs))
+            return list(ex.map(lambda s: _compile(s, tmp), srcs))
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    bad = {name: empty_exec_blocks(asm)[:3] for name, asm in results if empty_exec_blocks(asm)}
+
+
+def scratch_by_kernel(remarks: str):
+    """{kernel: scratch bytes per lane} from the resource-usage remarks."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name:
+            out[name] = int(m.group(1))
+    return out
+
+
+def test_no_kernel_has_an_empty_exec_block(compiled):
+    bad = {name: empty_exec_blocks(asm)[:3] for name, asm, _ in compiled if empty_exec_blocks(asm)}
+    assert not bad, bad
+
+
+def test_no_unexpected_register_spills(compiled):
+    sizes = {}
+    for _, _, remarks in compiled:
+        sizes.update(scratch_by_kernel(remarks))
+    assert len(sizes) > 20  # the remarks were parsed
+    bad = {k: v for k, v in sizes.items() if v > 0 and not any(s in k for s in KNOWN_SPILLS)}
     assert not bad, bad
