@@ -36,7 +36,7 @@ EXPORTS = ("dar_abi_version", "dar_status_string", "dar_pack_weight", "dar_fold"
            "dar_decode_append_varlen_sigmoid", "dar_prefill_chunk_sigmoid",
            "dar_attn_decode_noalloc", "dar_attn_decode_drope", "dar_project_drope",
            "dar_attn_prefill_drope", "dar_cache_from_prefill_drope", "dar_decode_append_drope",
-           "dar_project_varlen", "dar_attn_prefill_varlen")
+           "dar_project_varlen", "dar_attn_prefill_varlen", "dar_cache_from_prefill_packed")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -115,6 +115,8 @@ def lib() -> ctypes.CDLL:
             _SZ, _P]
         L.dar_attn_prefill_varlen.restype = _I
         L.dar_attn_prefill_varlen.argtypes = [_P] * 6 + [_I] * 7 + [_P, _P]
+        L.dar_cache_from_prefill_packed.restype = _I
+        L.dar_cache_from_prefill_packed.argtypes = [_P] * 4 + [_I] * 9 + [_P] * 4
         L.dar_attn_decode_varlen.restype = _I
         L.dar_attn_decode_varlen.argtypes = [_P] * 6 + [_I, _P] + [_I] * 6 + [
             ctypes.c_float, _I, _P, _P, _SZ, _P]
@@ -700,3 +702,30 @@ def dar_attn_prefill_varlen(P, cu_seqlens, max_len: int, heads: int, d_k: int, w
                                        _dtype_code(P["Q"]), _ptr(o), _stream(stream))
     _check("dar_attn_prefill_varlen", st)
     return o
+
+
+@_on_stream
+def dar_cache_from_prefill_packed(P, cu_seqlens, max_len: int, heads: int, d_k: int, w: int,
+                                  cap: int = None, h_D_cache=None, K_win=None, V_win=None,
+                                  stream=None):
+    """The decode cache of a ragged batch from dar_project_varlen's outputs P:
+    prompt b's latent rows and its last min(w, len_b) ring slots.  Returns
+    (h_D_cache [B, cap, d_down], K_win, V_win [B, heads, w, d_k]) (bf16)."""
+    torch = _torch()
+    T, d_down = P["h_D"].shape
+    B = cu_seqlens.numel() - 1
+    cap = int(max_len) if cap is None else cap
+    kw = dict(dtype=torch.bfloat16, device=P["h_D"].device)
+    if h_D_cache is None:
+        h_D_cache = torch.zeros((B, cap, d_down), **kw)
+    if w > 0 and K_win is None:
+        K_win = torch.zeros((B, heads, w, d_k), **kw)
+    if w > 0 and V_win is None:
+        V_win = torch.zeros((B, heads, w, d_k), **kw)
+    st = lib().dar_cache_from_prefill_packed(
+        _ptr(P["h_D"]), _ptr(P["K_loc"]) if w > 0 else None,
+        _ptr(P["V_loc"]) if w > 0 else None, _ptr(cu_seqlens), B, T, int(max_len), heads, d_k,
+        d_down, int(w), int(h_D_cache.shape[1]), _dtype_code(P["h_D"]), _ptr(h_D_cache),
+        _ptr(K_win) if w > 0 else None, _ptr(V_win) if w > 0 else None, _stream(stream))
+    _check("dar_cache_from_prefill_packed", st)
+    return h_D_cache, K_win, V_win

@@ -25,17 +25,41 @@ __device__ __forceinline__ u32x4 f16x8_to_bf16x8(const u32x4& v) {
   return r;
 }
 
+// Packed prompts: the prompt b holding packed row r (the last b < nb with
+// cu[b] <= r) and the row's position r - cu[b] in it.  The starts are read on
+// the device only; for inconsistent values the result stays in [0, nb) and
+// `ok` is false unless the row lies inside its prompt's [cu[b], cu[b+1]).
+struct PackedRow { int b, n; bool ok; };
+__device__ __forceinline__ PackedRow packed_row(const int* __restrict__ cu, int nb, int r) {
+  int lo = 0, hi = nb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int start = cu[lo], end = cu[lo + 1];
+  return {lo, r - start, r >= start && r < end};
+}
+
 // h_D_cache[b, row0 + n, :] = bf16(h_D[b, n, :]) for n < N; 8 values per thread.
+// Packed prompts (cu != null, B = 1, N = T rows): packed row r of prompt b at
+// position n goes to h_D_cache[b, n, :] (n < cap), for b < nb.
 __global__ __launch_bounds__(256) void latent_cast_kernel(const f16* __restrict__ hD,
                                                           bf16* __restrict__ cache, int B, int N,
-                                                          int d_down, int cap, int row0) {
+                                                          int d_down, int cap, int row0,
+                                                          const int* __restrict__ cu, int nb) {
   const int cpr = d_down / 8;  // 16-byte chunks per row
   const size_t total = (size_t)B * N * cpr;
   for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
        c += (size_t)gridDim.x * blockDim.x) {
     const size_t row = c / cpr;
     const int col = (int)(c % cpr) * 8;
-    const size_t b = row / N, n = row % N;
+    size_t b = row / N, n = row % N;
+    if (cu != nullptr) {
+      const PackedRow L = packed_row(cu, nb, (int)row);
+      if (!L.ok || L.n >= cap) continue;
+      b = L.b;
+      n = L.n;
+    }
     const u32x4 v = *(const u32x4*)(hD + row * d_down + col);
     *(u32x4*)(cache + (b * cap + row0 + n) * d_down + col) = f16x8_to_bf16x8(v);
   }
@@ -47,28 +71,44 @@ __global__ __launch_bounds__(256) void latent_cast_kernel(const f16* __restrict_
 // V_win[b, h, j mod w, :] = bf16(Vt[b, h, :, j - base]).
 // Ragged batches (lens != null, base 0): sequence b ends at lens[b] (clamped
 // to [1, N]) and its last min(w, lens[b]) positions are written.
+// Packed prompts (cu != null, base 0, N = T packed rows): prompt b's block of
+// head-major rows starts at element cu[b] * heads * D ([heads, len_b, D] for K,
+// [heads, D, len_b] for V), len_b = cu[b+1] - cu[b] (clamped into the T rows).
 template <int D>
 __global__ __launch_bounds__(256) void ring_fill_kernel(const f16* __restrict__ Kl,
                                                         const f16* __restrict__ Vl,
                                                         bf16* __restrict__ Kw,
                                                         bf16* __restrict__ Vw, int N, int w,
                                                         int j_lo, int base, int heads,
-                                                        const int* __restrict__ lens) {
+                                                        const int* __restrict__ lens,
+                                                        const int* __restrict__ cu) {
   constexpr int TJ = 64, TP = TJ + 2;  // positions per tile; LDS pitch (f16)
   __shared__ f16 vt[D * TP];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const int len = N - base;
+  int len = N - base;
   int n_end = N, lo = j_lo;
-  if (lens != nullptr) {
-    const int l = lens[bh / heads];
-    n_end = l < 1 ? 1 : (l > N ? N : l);
-    lo = max(n_end - w, base);
+  const f16* K;
+  const f16* V;
+  if (cu != nullptr) {
+    const int b = bh / heads, hh = bh % heads;
+    const int s = min(max(cu[b], 0), N);
+    len = min(max(cu[b + 1], s), N) - s;
+    n_end = len;
+    lo = max(len - w, 0);
+    K = Kl + ((size_t)s * heads + (size_t)hh * len) * D;
+    V = Vl + ((size_t)s * heads + (size_t)hh * len) * D;
+  } else {
+    if (lens != nullptr) {
+      const int l = lens[bh / heads];
+      n_end = l < 1 ? 1 : (l > N ? N : l);
+      lo = max(n_end - w, base);
+    }
+    K = Kl + (size_t)bh * len * D;
+    V = Vl + (size_t)bh * D * len;
   }
   const int j0 = lo + TJ * blockIdx.y;
   const int nj = min(TJ, n_end - j0);
   if (nj <= 0) return;
-  const f16* K = Kl + (size_t)bh * len * D;
-  const f16* V = Vl + (size_t)bh * D * len;
   bf16* KW = Kw + (size_t)bh * w * D;
   bf16* VW = Vw + (size_t)bh * w * D;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
@@ -130,12 +170,12 @@ __global__ __launch_bounds__(256) void ring_to_local_kernel(const bf16* __restri
 }  // namespace
 
 hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap, int row0,
-                              void* h_D_cache, hipStream_t s) {
+                              void* h_D_cache, hipStream_t s, const int* cu, int nb) {
   const size_t chunks = (size_t)B * N * (d_down / 8);
   size_t blocks = (chunks + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(latent_cast_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const f16*)h_D, (bf16*)h_D_cache, B, N, d_down, cap, row0);
+                     (const f16*)h_D, (bf16*)h_D_cache, B, N, d_down, cap, row0, cu, nb);
   return hipGetLastError();
 }
 
@@ -148,10 +188,12 @@ hipError_t launch_ring_fill(const void* K, const void* Vt, int B, int heads, int
   const dim3 grid(B * heads, (N - j_lo + 63) / 64);
   if (d_k == 64)
     hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, (const f16*)K,
-                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base, heads, lens);
+                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base, heads, lens,
+                       nullptr);
   else
     hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, (const f16*)K,
-                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base, heads, lens);
+                       (const f16*)Vt, (bf16*)K_win, (bf16*)V_win, N, w, j_lo, base, heads, lens,
+                       nullptr);
   return hipGetLastError();
 }
 
@@ -177,6 +219,25 @@ hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const v
   if (e == hipSuccess)
     e = launch_ring_fill(K_loc, V_loc, B, heads, d_k, N, 0, w, K_win, V_win, s, lens);
   return e;
+}
+
+hipError_t launch_cache_from_packed(const void* h_D, const void* K_loc, const void* V_loc,
+                                    const int* cu, int B, int T, int max_len, int heads, int d_k,
+                                    int d_down, int w, int cap, void* h_D_cache, void* K_win,
+                                    void* V_win, hipStream_t s) {
+  hipError_t e = launch_latent_cast(h_D, 1, T, d_down, cap, 0, h_D_cache, s, cu, B);
+  if (e != hipSuccess || w <= 0) return e;
+  // each prompt writes its last min(w, len_b) <= min(w, max_len) positions
+  const dim3 grid(B * heads, (min(w, max_len) + 63) / 64);
+  if (d_k == 64)
+    hipLaunchKernelGGL(ring_fill_kernel<64>, grid, dim3(256), 0, s, (const f16*)K_loc,
+                       (const f16*)V_loc, (bf16*)K_win, (bf16*)V_win, T, w, 0, 0, heads, nullptr,
+                       cu);
+  else
+    hipLaunchKernelGGL(ring_fill_kernel<128>, grid, dim3(256), 0, s, (const f16*)K_loc,
+                       (const f16*)V_loc, (bf16*)K_win, (bf16*)V_win, T, w, 0, 0, heads, nullptr,
+                       cu);
+  return hipGetLastError();
 }
 
 // Weight packing: the equations' W in R^{rows x cols}, stored row-major

@@ -550,6 +550,36 @@ dar_status dar_cache_from_prefill_varlen(const void* h_D, const void* K_loc, con
                                  dtype, h_D_cache, K_win, V_win, stream);
 }
 
+dar_status dar_cache_from_prefill_packed(const void* h_D, const void* K_loc, const void* V_loc,
+                                         const int* cu_seqlens, int B, int T, int max_len,
+                                         int heads, int d_k, int d_down, int w, int cap,
+                                         dar_dtype dtype, void* h_D_cache, void* K_win,
+                                         void* V_win, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return DAR_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || max_len < 1 || max_len > T || heads < 1 || d_k < 2 || (d_k & 1) ||
+      d_down < 1 || w < 0 || cap < max_len || cu_seqlens == nullptr ||
+      ((uintptr_t)cu_seqlens & 3u) != 0)
+    return DAR_ERR_INVALID_ARG;
+  if (!aligned16(h_D) || !aligned16(h_D_cache)) return DAR_ERR_INVALID_ARG;
+  if (w > 0 && (!aligned16(K_loc) || !aligned16(V_loc) || !aligned16(K_win) || !aligned16(V_win)))
+    return DAR_ERR_INVALID_ARG;
+  const size_t hd = (size_t)heads * d_k;
+  const Span ins[4] = {{h_D, 2 * (size_t)T * d_down},
+                       {w > 0 ? K_loc : nullptr, 2 * (size_t)T * hd},
+                       {w > 0 ? V_loc : nullptr, 2 * (size_t)T * hd},
+                       {cu_seqlens, sizeof(int) * ((size_t)B + 1)}};
+  const Span outs[3] = {{h_D_cache, 2 * (size_t)B * cap * d_down},
+                        {w > 0 ? K_win : nullptr, 2 * (size_t)B * w * hd},
+                        {w > 0 ? V_win : nullptr, 2 * (size_t)B * w * hd}};
+  if (!disjoint(outs, 3, ins, 4)) return DAR_ERR_INVALID_ARG;
+  if (dtype != DAR_BF16) return DAR_ERR_UNSUPPORTED;
+  if (!head_supported(d_k) || d_down % 8 || (long)B * heads > 0x7fffffffL)
+    return DAR_ERR_UNSUPPORTED;
+  return hip_status(launch_cache_from_packed(h_D, K_loc, V_loc, cu_seqlens, B, T, max_len, heads,
+                                             d_k, d_down, w, cap, h_D_cache, K_win, V_win,
+                                             stream));
+}
+
 static dar_status prefill_chunk_impl(const void* h, const void* W_down, const void* W_Q,
                                      const void* W_K, const void* W_V, const void* W_upK,
                                      const void* W_upV, int B, int C, int d, int d_down, int heads,

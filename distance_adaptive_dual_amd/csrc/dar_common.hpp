@@ -276,7 +276,8 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s);
 // Pieces of the cache kernels (fp16 <-> bf16 conversions, positions relative to
 // array bases; see cache.hip).
 hipError_t launch_latent_cast(const void* h_D, int B, int N, int d_down, int cap, int row0,
-                              void* h_D_cache, hipStream_t s);
+                              void* h_D_cache, hipStream_t s, const int* cu = nullptr,
+                              int nb = 0);
 hipError_t launch_ring_fill(const void* K, const void* Vt, int B, int heads, int d_k, int N,
                             int base, int w, void* K_win, void* V_win, hipStream_t s,
                             const int* lens = nullptr);
@@ -288,6 +289,11 @@ hipError_t launch_cache_from_prefill(const void* h_D, const void* K_loc, const v
                                      int B, int N, int heads, int d_k, int d_down, int w,
                                      int cap, void* h_D_cache, void* K_win, void* V_win,
                                      hipStream_t s, const int* lens = nullptr);
+// The same from packed prompts (dar_project_varlen's layout; prompt starts cu).
+hipError_t launch_cache_from_packed(const void* h_D, const void* K_loc, const void* V_loc,
+                                    const int* cu, int B, int T, int max_len, int heads, int d_k,
+                                    int d_down, int w, int cap, void* h_D_cache, void* K_win,
+                                    void* V_win, hipStream_t s);
 // Row-major [rows, cols] -> column-major (cache.hip); grid limit rows, cols <= 64 * 65535.
 hipError_t launch_pack_weight(const void* W, int rows, int cols, int elem_bytes, void* out,
                               hipStream_t s);

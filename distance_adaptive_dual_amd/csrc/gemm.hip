@@ -450,8 +450,9 @@ __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, 
     if (grow0 >= M) continue;
     const RowLoc L0 = row_loc(p, seg, grow0);
     const int no0 = L0.n + seg.seq_off;
-    const bool fast = L0.ok && (grow0 + 8 <= M) && (L0.n + 8 <= L0.len) && ((no0 & 7) == 0) &&
-                      ((L0.ld & 7) == 0);
+    // the 8 tokens in one sequence: one address; 16-byte aligned runs store whole
+    const bool same = L0.ok && (grow0 + 8 <= M) && (L0.n + 8 <= L0.len);
+    const bool fast = same && ((no0 & 7) == 0) && ((L0.ld & 7) == 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = (tid >> 3) + 32 * k;
@@ -460,8 +461,12 @@ __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, 
       const int head = gcol / D, t = gcol % D;
       float v[8];
       read8(tile + c * TP + 64 * run + 8 * tc, v);
+      OutT* dst = out + L0.base * H * D + ((size_t)head * D + t) * L0.ld + no0;
       if (fast) {
-        store_run<OutT, 8>(out + L0.base * H * D + ((size_t)head * D + t) * L0.ld + no0, v);
+        store_run<OutT, 8>(dst, v);
+      } else if (same) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = from_f32<OutT>(v[i]);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {

@@ -218,6 +218,28 @@ dar_status dar_attn_prefill_varlen(const void* Q, const void* K_loc, const void*
                                    dar_dtype dtype, void* o, hipStream_t stream);
 
 /*
+ * dar_cache_from_prefill_packed -- the decode cache of a ragged batch
+ * prefilled without padding (the inference remark after Eq. (5)): from
+ * dar_project_varlen's packed h_D [T, d_down], K_loc and V_loc (fp16, one
+ * block per prompt as above), for every prompt b of length
+ * len_b = cu_seqlens[b+1] - cu_seqlens[b]:
+ *   h_D_cache[b, n, :]       <- h_D[cu_seqlens[b] + n, :]   for n < len_b
+ *   K_win[b, :, j mod w, :]  <- prompt b's K_loc[:, j, :]   for max(0, len_b-w) <= j < len_b
+ *   V_win[b, :, j mod w, :]  <- prompt b's V_loc[:, :, j]
+ * leaving every other row and slot untouched; h_D_cache [B, cap, d_down]
+ * with cap >= max_len, K_win and V_win [B, heads, w, d_k] (bf16; ignored, may
+ * be NULL, when w = 0).  Values are rounded fp16 -> bf16 (nearest even).  The
+ * next token of prompt b sits at position len_b (dar_decode_append_varlen with
+ * pos[b] = len_b, then dar_attn_decode_varlen with ctx_lens[b] = len_b + 1).
+ * DAR_BF16 only; d_down a multiple of 8.  No workspace.
+ */
+dar_status dar_cache_from_prefill_packed(const void* h_D, const void* K_loc, const void* V_loc,
+                                         const int* cu_seqlens, int B, int T, int max_len,
+                                         int heads, int d_k, int d_down, int w, int cap,
+                                         dar_dtype dtype, void* h_D_cache, void* K_win,
+                                         void* V_win, hipStream_t stream);
+
+/*
  * dar_attn_prefill_lse -- dar_attn_prefill that also stores, for training,
  * each query's softmax normaliser of Eq. (4):
  *   lse [B, heads, N] float32, lse_i = log sum_{j <= i} exp(q_i . k_j / sqrt(d_k))
@@ -371,10 +393,13 @@ dar_status dar_cache_from_prefill(const void* h_D, const void* K_loc, const void
 /*
  * Ragged batches: sequences of different lengths in one call.
  *
- * A batch of prompts of lengths N_b <= N is prefilled padded to N (dar_project
- * and dar_attn_prefill as usual): attention is causal, so the rows n < N_b of
- * sequence b do not depend on its padding and are exactly those of an
- * unpadded prefill.  From there on each sequence moves at its own position.
+ * A batch of prompts of lengths N_b <= N is prefilled either packed without
+ * padding (dar_project_varlen, dar_attn_prefill_varlen,
+ * dar_cache_from_prefill_packed) or padded to N (dar_project and
+ * dar_attn_prefill as usual): attention is causal, so the rows n < N_b of
+ * sequence b do not depend on its padding and equal those of an unpadded
+ * prefill up to rounding.  From there on each sequence moves at its own
+ * position.
  * The per-sequence lengths and positions are device int32 arrays of B entries
  * (caller-owned, 4-byte aligned, read by the kernels; they are never read on
  * the host, so values are not validated: each is clamped into range, which

@@ -565,3 +565,25 @@ def test_attn_prefill_varlen_rejects():
     assert attn_varlen(cu=None) == INVALID
     assert attn_varlen(dtype=0) == UNSUP
     assert attn_varlen(d_k=32) == UNSUP
+
+
+def cache_packed(**kw):
+    a = dict(h_D=F(0), K_loc=F(1), V_loc=F(2), cu=F(3), B=3, T=500, max_len=300, heads=4, d_k=64,
+             d_down=64, w=16, cap=320, dtype=1, cache=F(4), K_win=F(5), V_win=F(6))
+    a.update(kw)
+    keys = ("h_D", "K_loc", "V_loc", "cu", "B", "T", "max_len", "heads", "d_k", "d_down", "w",
+            "cap", "dtype", "cache", "K_win", "V_win")
+    return dar.lib().dar_cache_from_prefill_packed(*[a[k] for k in keys], None)
+
+
+def test_cache_from_prefill_packed_rejects():
+    assert cache_packed(cap=299) == INVALID        # a prompt of max_len rows would not fit
+    assert cache_packed(max_len=501) == INVALID
+    assert cache_packed(cu=None) == INVALID
+    assert cache_packed(cu=F(3) + 2) == INVALID    # int32 alignment
+    assert cache_packed(K_win=F(1)) == INVALID     # ring aliases K_loc
+    assert cache_packed(cache=F(3)) == INVALID     # cache aliases the starts
+    assert cache_packed(h_D=F(0) + 8) == INVALID   # 16-byte alignment
+    assert cache_packed(dtype=0) == UNSUP
+    assert cache_packed(d_down=12) == UNSUP
+    assert cache_packed(d_k=96) == UNSUP

@@ -1,7 +1,9 @@
 """GPU parity of the ragged (unpadded) prefill: dar_project_varlen and
 dar_attn_prefill_varlen over prompts of different lengths packed without
 padding, each prompt against the fp64 oracle's prefill of that prompt alone
-(its own positions from 0), through the C ABI.  bf16 I/O, max-abs 2e-2."""
+(its own positions from 0), through the C ABI.  bf16 I/O, max-abs 2e-2.
+dar_cache_from_prefill_packed is checked bit-exact (index moves and one
+fp16 -> bf16 rounding) and through the whole loop to the next token's decode."""
 import numpy as np
 import pytest
 import torch
@@ -124,3 +126,81 @@ def test_ragged_prefill_1b_width():
             blk = host(dar.varlen_block(P[k], starts, b, H, d_k, transposed=tr))[hh]
             refb = S[rk][0, 0].T if tr else S[rk][0, 0]
             check_block(k, blk, refb)
+
+
+@pytest.mark.parametrize("lens,w,d_k,dd", [([300, 17, 1, 150], 64, 64, 64),
+                                           ([90, 200], 128, 128, 128),
+                                           ([5, 40], 0, 64, 32)])
+def test_packed_cache_exact(lens, w, d_k, dd):
+    """dar_cache_from_prefill_packed on seeded fp16 packed blocks: every latent
+    row and ring slot is the fp16 value rounded to bf16, and every row and slot
+    it must not write keeps its earlier contents."""
+    log("packed cache lens %s w%d dk%d dd%d" % (lens, w, d_k, dd))
+    H, B, T, N = 3, len(lens), sum(lens), max(lens)
+    cap = N + 7
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    g = torch.Generator().manual_seed(97 + T + w)
+    P = {k: torch.randn(T * H * d_k, generator=g).to(torch.float16) for k in ("K_loc", "V_loc")}
+    P["h_D"] = torch.randn((T, dd), generator=g).to(torch.float16)
+    Lc0 = torch.randn((B, cap, dd), generator=g).to(torch.bfloat16)
+    Kw0 = torch.randn((B, H, max(w, 1), d_k), generator=g).to(torch.bfloat16)
+    Vw0 = torch.randn((B, H, max(w, 1), d_k), generator=g).to(torch.bfloat16)
+    Pd = {k: v.cuda() for k, v in P.items()}
+    Lc, Kw, Vw = Lc0.cuda(), Kw0.cuda(), Vw0.cuda()
+    dar.dar_cache_from_prefill_packed(Pd, torch.from_numpy(starts).cuda(), N, H, d_k, w, cap=cap,
+                                      h_D_cache=Lc, K_win=Kw if w else None,
+                                      V_win=Vw if w else None)
+    torch.cuda.synchronize()
+    eL, eK, eV = Lc0.clone(), Kw0.clone(), Vw0.clone()
+    for b, n in enumerate(lens):
+        eL[b, :n] = P["h_D"][starts[b]:starts[b + 1]].to(torch.bfloat16)
+        if w == 0:
+            continue
+        K = varlen_cpu(P["K_loc"], starts, b, H, d_k, False)
+        V = varlen_cpu(P["V_loc"], starts, b, H, d_k, True)
+        for j in range(max(0, n - w), n):
+            eK[b, :, j % w] = K[:, j].to(torch.bfloat16)
+            eV[b, :, j % w] = V[:, :, j].to(torch.bfloat16)
+    assert torch.equal(Lc.cpu(), eL)
+    if w:
+        assert torch.equal(Kw.cpu(), eK) and torch.equal(Vw.cpu(), eV)
+
+
+def varlen_cpu(x, starts, b, H, d_k, transposed):
+    lo, hi = int(starts[b]), int(starts[b + 1])
+    blk = x[lo * H * d_k:hi * H * d_k]
+    return blk.view(H, d_k, hi - lo) if transposed else blk.view(H, hi - lo, d_k)
+
+
+@pytest.mark.parametrize("lens,w,d_k,dd", [([300, 41, 1, 177], 64, 64, 128),
+                                           ([129, 400], 128, 128, 64)])
+def test_packed_prefill_inference_loop(lens, w, d_k, dd):
+    """Prompts prefilled packed, their decode cache from the packed outputs, one
+    appended token per prompt at position len_b and the ragged decode give row
+    len_b of each prompt's own prefill (oracle, len_b + 1 tokens)."""
+    log("packed prefill -> cache -> append -> decode lens %s w%d dk%d dd%d" % (lens, w, d_k, dd))
+    d, H, B = 256, 4, len(lens)
+    N = max(lens)
+    base, hs = ragged_case([n + 1 for n in lens], d, H, d_k, dd, seed=808 + N)
+    W = {k: dev_w(base[k], "bf16") for k in WNAMES}
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    h = dev(np.concatenate([x[0, :n] for x, n in zip(hs, lens)], axis=0), "bf16")
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = torch.from_numpy(starts).cuda()
+    P = dar.dar_project_varlen(h, W["W_down"], W["W_up"], W["W_Q"], W["W_K"], W["W_V"], H, d_k,
+                               cu, N, W_upK=Wk, W_upV=Wv)
+    Lc, Kw, Vw = dar.dar_cache_from_prefill_packed(P, cu, N, H, d_k, w, cap=N + 1)
+    nxt = dev(np.stack([x[0, n] for x, n in zip(hs, lens)]), "bf16")
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    q = torch.empty((B, H, d_k), dtype=torch.bfloat16, device="cuda")
+    dar.dar_decode_append_varlen(nxt, W["W_down"], W["W_Q"], W["W_K"], W["W_V"], H, d_k, pos, q,
+                                 Kw, Vw, Lc)
+    ctx = torch.tensor([n + 1 for n in lens], dtype=torch.int32, device="cuda")
+    o = dar.dar_attn_decode_varlen(q, Kw, Vw, Lc, Wk, Wv, ctx, N + 1, w)
+    torch.cuda.synchronize()
+    got = host(o)
+    for b, n in enumerate(lens):
+        ref, _, _ = oracle.prefill(dict(base, h=hs[b]), H, d_k, w)
+        err = max_err(got[b:b + 1], ref[0:1, n])
+        log("  prompt %d: decode at position %d vs prefill row: err %.3g" % (b, n, err))
+        assert err <= TOL["bf16"]
