@@ -26,6 +26,10 @@
 // 16-byte LDS load per step.  Softmax runs in base 2 with log2(e)/sqrt(d_k)
 // folded into the score scale, in fp32.
 //
+// At d_k = 128, whole prefills whose N is a multiple of 64 run attn_prefill_ring
+// instead: eight waves share each key/value tile, which arrives by direct
+// loads into a four-stage LDS ring (see there).
+//
 // fp32 kernel: VALU only, four lanes per query, per-key online softmax; it
 // exists for the fp32 mode (1e-4 parity), never rounds to bf16.
 #include <math.h>
@@ -652,6 +656,235 @@ __global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefil
 }
 
 // ---------------------------------------------------------------------------
+// d_k = 128 whole prefills with N a multiple of 64 (every key tile complete):
+// eight waves of 32 queries (256 per workgroup, two waves per SIMD) share each
+// key/value tile.  Tiles arrive by direct buffer loads into a four-stage LDS
+// ring three passes ahead, so no staging registers, LDS stores or their
+// address arithmetic are needed, and each tile is fetched once per 256
+// queries.  The rows are unpadded, with an XOR chunk swizzle that keeps the
+// fragment reads of 16 consecutive rows on distinct banks.  Per wave a pass is
+// the one of attn_prefill_f16 (scores, keep mask and running maximum,
+// exponentials, P.V).
+constexpr int WQT = 256;  // queries per workgroup
+constexpr int WNS = 4;    // stages of the LDS ring
+constexpr int WD = 128;   // d_k
+
+struct RingStage {
+  f16 k[KT * WD];  // [key][d], chunk c of row r at slot c ^ (r & 15)
+  f16 v[WD * KT];  // [d][key], chunk c of row r at slot c ^ ((r >> 1) & 7)
+};
+static_assert(sizeof(RingStage) == 32768, "two 16 KB tiles");
+
+__device__ __forceinline__ int wk_off(int row, int ch) { return row * WD + 8 * (ch ^ (row & 15)); }
+__device__ __forceinline__ int wv_off(int row, int ch) {
+  return row * KT + 8 * (ch ^ ((row >> 1) & 7));
+}
+
+// exp_and_pv on the ring's swizzled V^T tile.
+__device__ __forceinline__ void ring_exp_pv(const f16* sv, const f32x16 (&s)[2],
+                                            f32x16 (&o)[WD / 32], float m_ref, float& l_run,
+                                            float sc, int lr, int lg) {
+  constexpr int VPRE = 2;  // column blocks of 32 whose V^T fragments are requested first
+  f16x8 vf[VPRE][4];
+#pragma unroll
+  for (int db = 0; db < VPRE; ++db)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vf[db][u] = *(const f16x8*)(sv + wv_off(32 * db + lr, lg + 2 * u));
+  f16x8 pf[4];
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one2 = {(f16)1.f, (f16)1.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + c], sc, -m_ref));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + c + 1], sc, -m_ref));
+      const h2 ph = __builtin_bit_cast(h2, pack_f16x2(e0, e1));
+      l_run = __builtin_amdgcn_fdot2(ph, one2, l_run, false);
+      pf[u][c] = ph[0];
+      pf[u][c + 1] = ph[1];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int db = 0; db < VPRE; ++db) o[db] = mfma32x32x16(vf[db][u], pf[u], o[db]);
+  f16x8 vx[WD / 32 - VPRE][4];
+#pragma unroll
+  for (int db = VPRE; db < WD / 32; ++db)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vx[db - VPRE][u] = *(const f16x8*)(sv + wv_off(32 * db + lr, lg + 2 * u));
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int db = VPRE; db < WD / 32; ++db) o[db] = mfma32x32x16(vx[db - VPRE][u], pf[u], o[db]);
+}
+
+// LSE: also store each query's log-sum-exp in p.lse.
+template <bool LSE>
+__global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, int nQT, int nPair,
+                                                            int remap) {
+  __shared__ RingStage sm[WNS];
+  const int H = p.H, BH = p.B * p.H, w = p.w;
+  int pr, bh;
+  {
+    const int bid = blockIdx.x;
+    if (remap) {  // every tile of one (batch, head) on one XCD
+      const int x = bid % kNumXcd, k = bid / kNumXcd;
+      pr = k % nPair;
+      bh = (k / nPair) * kNumXcd + x;
+    } else {
+      pr = bid / BH;
+      bh = bid % BH;
+    }
+  }
+  const int b = bh / H, h = bh % H;
+  const int N = p.N;
+  const size_t slice = (size_t)bh * N * WD;
+  const f16* Qp = (const f16*)p.Q + slice;
+  const size_t orow0 = (size_t)b * N;
+  const int bytes = N * WD * 2;  // < 2 GiB (checked by the launcher)
+  // (four scalars, not arrays: an array indexed by the source would be
+  // placed in memory)
+  const __amdgpu_buffer_rsrc_t rKg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const f16*)p.K_glob + slice), (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rKl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const f16*)p.K_loc + slice), (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rVg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const f16*)p.V_glob + slice), (short)0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rVl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const f16*)p.V_loc + slice), (short)0, bytes, 0x00020000);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lg = lane >> 5;
+  const float sc = kLog2e / sqrtf((float)WD);
+  // This lane's fixed byte offsets within a tile: LDS slot P = (8 i + wave) 64
+  // + lane of the K tile (row P / 16, slot P % 16) and of the V^T tile (row
+  // P / 8, slot P % 8), loaded from the chunk the swizzle puts there.
+  unsigned vk[2], vv[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int P = (8 * i + wave) * 64 + lane;
+    const int kr = P >> 4, kc = (P & 15) ^ (kr & 15);
+    vk[i] = (unsigned)((kr * WD + 8 * kc) * 2);
+    const int vr = P >> 3, vc = (P & 7) ^ ((vr >> 1) & 7);
+    vv[i] = (unsigned)((vr * N + 8 * vc) * 2);
+  }
+  auto issue = [&](int j0, int src, int stg) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src ? rKl : rKg, (__attribute__((address_space(3))) void*)(sm[stg].k + (8 * i + wave) * 512), 16,
+          vk[i], j0 * WD * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src ? rVl : rVg, (__attribute__((address_space(3))) void*)(sm[stg].v + (8 * i + wave) * 512), 16,
+          vv[i], j0 * 2, 0, 0);
+  };
+  // s_waitcnt vmcnt(4 n): at most n later passes (4 loads each) in flight
+  auto wait_passes = [](int n) {
+    if (n >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else if (n == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+
+  const int q_hi = nQT - 1 - pr;
+  const int nq = q_hi == pr ? 1 : 2;
+  for (int qn = 0; qn < nq; ++qn) {
+    const int qt = qn == 0 ? q_hi : pr;
+    if (qn > 0) __syncthreads();  // every wave is done with the ring
+    const int i0 = qt * WQT, qw0 = i0 + 32 * wave, qi = qw0 + lr;
+    const int i_last = min(i0 + WQT - 1, N - 1), wi_last = min(qw0 + 31, N - 1);
+    f16x8 qf[WD / 16];
+    {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int st = 0; st < WD / 16; ++st) {
+        const u32x4 v = qi < N ? *(const u32x4*)(Qp + (size_t)qi * WD + 16 * st + 8 * lg) : z;
+        qf[st] = __builtin_bit_cast(f16x8, v);
+      }
+    }
+    f32x16 o[WD / 32];
+#pragma unroll
+    for (int db = 0; db < WD / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_ref = kNegBig, l_run = 0.f;
+
+    const int j_end = min(N, i0 + WQT);
+    auto need_glob = [&](int j0) { return i_last - j0 >= w; };
+    auto need_loc = [&](int j0) { return w > 0 && max(i0 - (j0 + KT - 1), 0) < w; };
+    auto next = [&](int& j0, int& src) {
+      if (src == 0 && need_loc(j0)) {
+        src = 1;
+      } else {
+        j0 += KT;
+        src = need_glob(j0) ? 0 : 1;
+      }
+    };
+    int cj = 0, cs = need_glob(0) ? 0 : 1;  // the pass computed now
+    int aj = cj, as = cs;                   // the next pass to load
+    int issued = 0;
+#pragma unroll
+    for (int k = 0; k < WNS - 1; ++k)
+      if (aj < j_end) {
+        issue(aj, as, k);
+        next(aj, as);
+        ++issued;
+      }
+    for (int t = 0; cj < j_end; ++t) {
+      wait_passes(issued - t - 1);  // this lane's loads of pass t have landed
+      lds_barrier();                // everyone's have; everyone is done with pass t-1
+      if (aj < j_end) {
+        issue(aj, as, (t + WNS - 1) % WNS);
+        next(aj, as);
+        ++issued;
+      }
+      const RingStage& S = sm[t % WNS];
+      const WavePass wp = wave_pass_info(cj, cs, qw0, wi_last, qi, lg, N, w);
+      if (wp.part) {
+        f16x8 kf[2][WD / 16];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int st = 0; st < WD / 16; ++st)
+            kf[kb][st] = *(const f16x8*)(S.k + wk_off(32 * kb + key_perm(lr), 2 * st + lg));
+        f32x16 s[2];
+        mfma_scores<WD>(kf, qf, s);
+        mask_and_max<WD>(s, o, m_ref, l_run, wp.masked, wp.keep_lo, wp.keep_hi, sc);
+        ring_exp_pv(S.v, s, o, m_ref, l_run, sc, lr, lg);
+      }
+      next(cj, cs);
+    }
+
+    if (qi < N) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const float inv = 1.f / l_tot;
+      if (LSE && lg == 0)  // m_ref and l are in base 2
+        p.lse[(size_t)bh * N + qi] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
+      bf16* out = (bf16*)p.o + (orow0 + qi) * (size_t)(H * WD) + (size_t)h * WD;
+#pragma unroll
+      for (int db = 0; db < WD / 32; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d = 32 * db + 8 * rq + 4 * lg;
+          u32x2 v;
+          v[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
+          v[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+          *(u32x2*)(out + d) = v;
+        }
+    } else {
+      (void)__shfl_xor(l_run, 32);  // keep the exchange wave-uniform
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU kernel: 64 queries per workgroup, four lanes per query (lane part
 // `pt` owns dims pt, pt+4, ...), keys staged 32 at a time.
 constexpr int FQ = 64, FK = 32;
@@ -751,6 +984,18 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
       else
         hipLaunchKernelGGL((attn_prefill_f16<128, false, false, 64>), grid, dim3(256), 0, s, p,
                            nQT, nPair, remap, paired);
+      return hipGetLastError();
+    }
+    if (p.d_k == 128 && !chunk && p.cu == nullptr && p.N % KT == 0 &&
+        (long)p.N * WD * 2 < 0x7fffffffL) {
+      // whole prefill, complete key tiles: the ring kernel (pairs of query tiles)
+      const int nQW = (p.N + WQT - 1) / WQT, nPW = (nQW + 1) / 2;
+      if (lse)
+        hipLaunchKernelGGL(attn_prefill_ring<true>, dim3(nPW * BH), dim3(512), 0, s, p, nQW, nPW,
+                           remap);
+      else
+        hipLaunchKernelGGL(attn_prefill_ring<false>, dim3(nPW * BH), dim3(512), 0, s, p, nQW, nPW,
+                           remap);
       return hipGetLastError();
     }
     if (p.d_k == 64) {
