@@ -669,11 +669,22 @@ constexpr int WQT = 256;  // queries per workgroup
 constexpr int WNS = 4;    // stages of the LDS ring
 constexpr int WD = 128;   // d_k
 
+// DR = 64 (the decoupled-RoPE variant): the shared rotary keys of the tile's
+// positions in a region of their own ([key][d_R], 128-byte rows swizzled as
+// V^T's), since one buffer load reads one array.
+template <int DR>
 struct RingStage {
-  f16 k[KT * WD];  // [key][d], chunk c of row r at slot c ^ (r & 15)
-  f16 v[WD * KT];  // [d][key], chunk c of row r at slot c ^ ((r >> 1) & 7)
+  f16 k[KT * WD];   // [key][d], chunk c of row r at slot c ^ (r & 15)
+  f16 kr[KT * DR];  // [key][d_R], chunk c of row r at slot c ^ ((r >> 1) & 7)
+  f16 v[WD * KT];   // [d][key], chunk c of row r at slot c ^ ((r >> 1) & 7)
 };
-static_assert(sizeof(RingStage) == 32768, "two 16 KB tiles");
+template <>
+struct RingStage<0> {
+  f16 k[KT * WD];
+  f16 v[WD * KT];
+};
+static_assert(sizeof(RingStage<0>) == 32768, "two 16 KB tiles");
+static_assert(sizeof(RingStage<64>) == 40960, "16 + 8 + 16 KB");
 
 __device__ __forceinline__ int wk_off(int row, int ch) { return row * WD + 8 * (ch ^ (row & 15)); }
 __device__ __forceinline__ int wv_off(int row, int ch) {
@@ -721,11 +732,16 @@ __device__ __forceinline__ void ring_exp_pv(const f16* sv, const f32x16 (&s)[2],
     for (int db = VPRE; db < WD / 32; ++db) o[db] = mfma32x32x16(vx[db - VPRE][u], pf[u], o[db]);
 }
 
-// LSE: also store each query's log-sum-exp in p.lse.
-template <bool LSE>
+// LSE: also store each query's log-sum-exp in p.lse.  DR = 64: the
+// decoupled-RoPE variant (whole prefill; three stages fit in LDS).
+template <bool LSE, int DR = 0>
 __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, int nQT, int nPair,
                                                             int remap) {
-  __shared__ RingStage sm[WNS];
+  static_assert(DR == 0 || !LSE, "the variant's prefill stores no log-sum-exp");
+  constexpr int NS = DR > 0 ? 3 : WNS;  // stages
+  constexpr int LPP = DR > 0 ? 5 : 4;   // loads per lane and pass
+  constexpr int NQ = (WD + DR) / 16;    // 16-wide steps of the score contraction
+  __shared__ RingStage<DR> sm[NS];
   const int H = p.H, BH = p.B * p.H, w = p.w;
   int pr, bh;
   {
@@ -755,10 +771,15 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
       (void*)((const f16*)p.V_glob + slice), (short)0, bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rVl = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const f16*)p.V_loc + slice), (short)0, bytes, 0x00020000);
+  // rotary keys of sequence b (positions 0 .. N-1, every head) and queries
+  const __amdgpu_buffer_rsrc_t rKR = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(DR > 0 ? (const f16*)p.KR + (size_t)b * N * DR : (const f16*)p.Q), (short)0,
+      N * DR * 2, 0x00020000);
+  const f16* QRp = DR > 0 ? (const f16*)p.QR + (size_t)bh * N * DR : nullptr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
-  const float sc = kLog2e / sqrtf((float)WD);
+  const float sc = kLog2e / sqrtf((float)(WD + DR));
   // This lane's fixed byte offsets within a tile: LDS slot P = (8 i + wave) 64
   // + lane of the K tile (row P / 16, slot P % 16) and of the V^T tile (row
   // P / 8, slot P % 8), loaded from the chunk the swizzle puts there.
@@ -771,7 +792,17 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     const int vr = P >> 3, vc = (P & 7) ^ ((vr >> 1) & 7);
     vv[i] = (unsigned)((vr * N + 8 * vc) * 2);
   }
+  // rotary region: slot P = wave 64 + lane (row P / 8, slot P % 8)
+  unsigned vkr = 0;
+  if constexpr (DR > 0) {
+    const int P = wave * 64 + lane, rr = P >> 3, rc = (P & 7) ^ ((rr >> 1) & 7);
+    vkr = (unsigned)((rr * DR + 8 * rc) * 2);
+  }
   auto issue = [&](int j0, int src, int stg) {
+    if constexpr (DR > 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rKR, (__attribute__((address_space(3))) void*)(sm[stg].kr + wave * 512), 16, vkr,
+          j0 * DR * 2, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -783,12 +814,15 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
           src ? rVl : rVg, (__attribute__((address_space(3))) void*)(sm[stg].v + (8 * i + wave) * 512), 16,
           vv[i], j0 * 2, 0, 0);
   };
-  // s_waitcnt vmcnt(4 n): at most n later passes (4 loads each) in flight
+  // s_waitcnt vmcnt(LPP n) (lgkmcnt and expcnt left alone): at most n later
+  // passes in flight; N's low 4 bits in [3:0], its high 2 bits in [15:14]
+  constexpr int W1 = ((LPP >> 4) << 14) | 0x0F70 | (LPP & 15);
+  constexpr int W2 = (((2 * LPP) >> 4) << 14) | 0x0F70 | ((2 * LPP) & 15);
   auto wait_passes = [](int n) {
     if (n >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+      __builtin_amdgcn_s_waitcnt(W2);
     else if (n == 1)
-      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      __builtin_amdgcn_s_waitcnt(W1);
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
@@ -800,12 +834,18 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     if (qn > 0) __syncthreads();  // every wave is done with the ring
     const int i0 = qt * WQT, qw0 = i0 + 32 * wave, qi = qw0 + lr;
     const int i_last = min(i0 + WQT - 1, N - 1), wi_last = min(qw0 + 31, N - 1);
-    f16x8 qf[WD / 16];
+    f16x8 qf[NQ];
     {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int st = 0; st < WD / 16; ++st) {
         const u32x4 v = qi < N ? *(const u32x4*)(Qp + (size_t)qi * WD + 16 * st + 8 * lg) : z;
+        qf[st] = __builtin_bit_cast(f16x8, v);
+      }
+#pragma unroll
+      for (int st = WD / 16; st < NQ; ++st) {
+        const u32x4 v =
+            qi < N ? *(const u32x4*)(QRp + (size_t)qi * DR + 16 * (st - WD / 16) + 8 * lg) : z;
         qf[st] = __builtin_bit_cast(f16x8, v);
       }
     }
@@ -831,7 +871,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     int aj = cj, as = cs;                   // the next pass to load
     int issued = 0;
 #pragma unroll
-    for (int k = 0; k < WNS - 1; ++k)
+    for (int k = 0; k < NS - 1; ++k)
       if (aj < j_end) {
         issue(aj, as, k);
         next(aj, as);
@@ -841,21 +881,29 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
       wait_passes(issued - t - 1);  // this lane's loads of pass t have landed
       lds_barrier();                // everyone's have; everyone is done with pass t-1
       if (aj < j_end) {
-        issue(aj, as, (t + WNS - 1) % WNS);
+        issue(aj, as, (t + NS - 1) % NS);
         next(aj, as);
         ++issued;
       }
-      const RingStage& S = sm[t % WNS];
+      const RingStage<DR>& S = sm[t % NS];
       const WavePass wp = wave_pass_info(cj, cs, qw0, wi_last, qi, lg, N, w);
       if (wp.part) {
-        f16x8 kf[2][WD / 16];
+        f16x8 kf[2][NQ];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = 32 * kb + key_perm(lr);
 #pragma unroll
           for (int st = 0; st < WD / 16; ++st)
-            kf[kb][st] = *(const f16x8*)(S.k + wk_off(32 * kb + key_perm(lr), 2 * st + lg));
+            kf[kb][st] = *(const f16x8*)(S.k + wk_off(row, 2 * st + lg));
+          if constexpr (DR > 0) {
+#pragma unroll
+            for (int st = WD / 16; st < NQ; ++st)
+              kf[kb][st] = *(const f16x8*)(S.kr + row * DR +
+                                           8 * ((2 * (st - WD / 16) + lg) ^ ((row >> 1) & 7)));
+          }
+        }
         f32x16 s[2];
-        mfma_scores<WD>(kf, qf, s);
+        mfma_scores<WD, DR>(kf, qf, s);
         mask_and_max<WD>(s, o, m_ref, l_run, wp.masked, wp.keep_lo, wp.keep_hi, sc);
         ring_exp_pv(S.v, s, o, m_ref, l_run, sc, lr, lg);
       }
@@ -978,6 +1026,12 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
     if (p.cu != nullptr && (chunk || lse || p.d_R > 0 || p.T < 1)) return hipErrorInvalidValue;
     if (p.d_R > 0) {  // decoupled-RoPE variant: whole prefill, d_R = 64
       if (chunk || lse || p.d_R != 64) return hipErrorInvalidValue;
+      if (p.d_k == 128 && p.N % KT == 0 && (long)p.N * WD * 2 < 0x7fffffffL) {
+        const int nQW = (p.N + WQT - 1) / WQT, nPW = (nQW + 1) / 2;
+        hipLaunchKernelGGL((attn_prefill_ring<false, 64>), dim3(nPW * BH), dim3(512), 0, s, p, nQW,
+                           nPW, remap);
+        return hipGetLastError();
+      }
       if (p.d_k == 64)
         hipLaunchKernelGGL((attn_prefill_f16<64, false, false, 64>), grid, dim3(256), 0, s, p, nQT,
                            nPair, remap, paired);
