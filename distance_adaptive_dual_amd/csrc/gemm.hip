@@ -640,7 +640,9 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   // hf is a compile-time constant, so acc is only ever indexed statically
   auto pass = [&](auto HF) {
     constexpr int hf = decltype(HF)::value;
-    __syncthreads();  // LDS free (main loop, or the previous pass's stores)
+    // LDS free (main loop, or the previous pass's stores).  LDS order only: a
+    // __syncthreads() would also wait for this wave's global stores.
+    lds_barrier();
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = 2 * hf + jj;
@@ -665,7 +667,7 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
           }
       }
     }
-    __syncthreads();
+    lds_barrier();  // the tile is in LDS
     if (seg.kind == kHeadT)
       store_cols<TO, D, BM + 4>(tile, row0, hf, col0, seg, p);
     else if (seg.kind == kHead && seg.rope)
@@ -871,7 +873,9 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
   // hf is a compile-time constant, so acc is only ever indexed statically
   auto pass = [&](auto HF) {
     constexpr int hf = decltype(HF)::value;
-    __syncthreads();  // LDS free (main loop, or the previous pass's stores)
+    // LDS free (main loop, or the previous pass's stores).  LDS order only: a
+    // __syncthreads() would also wait for this wave's global stores.
+    lds_barrier();
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = 2 * hf + jj;
@@ -896,7 +900,7 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
           }
       }
     }
-    __syncthreads();
+    lds_barrier();  // the tile is in LDS
 #pragma unroll
     for (int chh = 0; chh < 2; ++chh) {
       if (seg.kind == kHeadT)
