@@ -694,10 +694,10 @@ def main():
         # the largest kernel of the step: HIP events on its launch stream around
         # a graph of back-to-back calls time that kernel.
         achieved = attn_f / attn_ms / 1e9
-        res["roofline"] = {"kernel": "attn_prefill_f16<128>", "bound": "mfma",
+        res["roofline"] = {"kernel": "attn_prefill_ring<128>", "bound": "mfma",
                            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,
-                           "traffic": recorded_traffic("attn_prefill_f16<128>@1b",
+                           "traffic": recorded_traffic("attn_prefill_ring<128>@1b",
                                                        ["attn_prefill.hip", "dar_common.hpp"]),
                            "flops_per_launch": attn_f, "launch_ms": attn_ms,
                            "peak_measured": cal["mfma_f16_tflops"],
