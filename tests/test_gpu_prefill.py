@@ -343,8 +343,36 @@ def test_attention_seeded_sweep(B, H, N, d_k, w):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("N,w", [(64, 4), (128, 0), (320, 1), (320, 63), (512, 64), (512, 65),
+                                 (448, 1000), (1216, 257), (1216, 1216)])
+def test_attention_ring_tiles(N, w):
+    """d_k 128 whole prefills whose N is a multiple of 64 run the ring kernel
+    (eight waves, 256 queries per workgroup, key tiles by direct loads into a
+    four-stage LDS ring): one key tile, partial 256-query tiles (N = 320, 448,
+    1216, so the pairs of query tiles include a short last one), windows on
+    both sides of the 64-key tile edge, w = 0 and w >= N.  o against the
+    oracle at 2e-2, and the log-sum-exp variant's lse against the oracle's row
+    normalisers at 2e-3 (its o bit-identical to dar_attn_prefill's)."""
+    B, H, d_k = 2, 3, 128
+    P = _attn_inputs(B, H, N, d_k, seed=8800 + N + w)
+    got = _attn_gpu(P, w)
+    ref, _ = oracle.attend(P, w)
+    err = max_err(got, ref)
+    Q, KL, KG = (dev(P[k], "f16") for k in ("Q", "KL", "KG"))
+    VL = dev(P["VL"].transpose(0, 1, 3, 2), "f16")
+    VG = dev(P["VG"].transpose(0, 1, 3, 2), "f16")
+    o2, lse = dar.dar_attn_prefill_lse(Q, KL, VL, KG, VG, w)
+    torch.cuda.synchronize()
+    lse_err = np.abs(host(lse) - oracle.attend_lse(P, w)).max()
+    log("ring N%d w%d: max err %.3g, lse err %.3g" % (N, w, err, lse_err))
+    assert err <= TOL["bf16"]
+    assert np.array_equal(host(o2), got)
+    assert lse_err <= 2e-3
+
+
 @pytest.mark.parametrize("N,d_k,w", [(700, 64, 100), (700, 128, 100), (300, 64, 0),
-                                     (300, 128, 1), (2048, 128, 512), (513, 64, 700)])
+                                     (300, 128, 1), (2048, 128, 512), (513, 64, 700),
+                                     (1216, 128, 100), (320, 128, 0)])
 def test_selection_counts_exact(N, d_k, w):
     """Closed form of Eq. 3's selection.  Q = 0 makes the softmax uniform over
     j <= i.  Value dims [0, d_k/2) carry an indicator of j mod (d_k/2) on the
@@ -375,7 +403,8 @@ def test_selection_counts_exact(N, d_k, w):
         assert np.max(np.abs(scaled[:, hh, :] - cnt)) < 0.25
 
 
-@pytest.mark.parametrize("N,d_k,w", [(600, 64, 100), (600, 128, 257), (300, 64, 1)])
+@pytest.mark.parametrize("N,d_k,w", [(600, 64, 100), (600, 128, 257), (300, 64, 1),
+                                     (1216, 128, 257), (320, 128, 1)])
 def test_key_source_selection(N, d_k, w):
     """Keys follow the same rule as values: q = e_0, local keys -1024 e_0 (their
     softmax weight underflows to 0 wherever a global pair exists), global keys
