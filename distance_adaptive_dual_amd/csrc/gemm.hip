@@ -74,12 +74,17 @@ __device__ __forceinline__ void store_run(OutT* dst, const float* v) {
       for (int e = 0; e < 4; ++e)
         w[e] = __is_same(OutT, f16) ? pack_f16x2(v[i + 2 * e], v[i + 2 * e + 1])
                                     : pack_bf16x2(v[i + 2 * e], v[i + 2 * e + 1]);
-      *(u32x4*)(dst + i) = w;
+      // streaming stores: the outputs are read by the next kernels, not
+      // here, so they should not push the tiles this kernel reuses out of L2
+      __builtin_nontemporal_store(w, (u32x4*)(dst + i));
     }
   } else {
     static_assert(NV % 4 == 0, "fp32 runs are stored 4 at a time");
 #pragma unroll
-    for (int i = 0; i < NV; i += 4) *(float4*)(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    for (int i = 0; i < NV; i += 4) {
+      const f32x4 x = {v[i], v[i + 1], v[i + 2], v[i + 3]};
+      __builtin_nontemporal_store(x, (f32x4*)(dst + i));
+    }
   }
 }
 
