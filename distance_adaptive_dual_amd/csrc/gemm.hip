@@ -686,13 +686,13 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
 
 // --------------------------------------------------------------------------
 // Wide MFMA GEMM for large problems: workgroup tiles of 256 tokens x 256
-// output columns, 4 waves in a 2 x 2 grid, each wave 128 tokens x 128 columns
-// (16 accumulator blocks of 32 x 32).  A 16-wide k-step reads 8 fragments
-// from LDS for 16 MFMAs, and each k-tile staged in LDS feeds two waves per
-// row on either operand: per MFMA the LDS moves 0.75 KB (fragment reads plus
-// the direct-to-LDS fills) instead of the 1.125 KB of the 256 x 128 tile,
-// which keeps the LDS port below its limit when the matrix cores are busy.
-// One workgroup per CU (the accumulators take 256 registers per lane).
+// output columns, one workgroup per CU.  Launched with 8 waves in a 4 x 2
+// grid, each 128 tokens x 64 columns (8 accumulator blocks of 32 x 32), two
+// waves per SIMD, so one wave's MFMAs cover the other's barrier and LDS
+// waits; a 16-wide k-step reads 6 fragments from LDS for 8 MFMAs.  (With 4
+// waves of 128 x 128, one per SIMD and 16 blocks each, a k-step reads 8
+// fragments for 16 MFMAs but nothing covers a wave's stalls: 3% slower on
+// the 1B-scale layer.)
 //
 // Tile order ("bands"): the column tiles are cut into bands of WB; a band's
 // tiles are walked row tile by row tile, columns innermost, and the whole
@@ -702,9 +702,10 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
 // each read once per band; and every XCD gets the same number of tiles.
 constexpr int WBN = 256;  // columns per wide tile
 
-template <typename TM, typename TB, typename TO, int D, int GBK>
-__global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTiles st, int nM,
-                                                           int nC, int band, int per_xcd) {
+template <typename TM, typename TB, typename TO, int D, int GBK, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void project_gemm_wide(GemmProblem p, SegTiles st,
+                                                                int nM, int nC, int band,
+                                                                int per_xcd) {
   typedef typename Vec8<TM>::type TMx8;
   typedef typename Vec8<TB>::type TBx8;
   constexpr int TBM = 256;
@@ -712,7 +713,12 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
   constexpr int NST = GBK == 64 ? 2 : 4;
   constexpr int CPR = GBK / 8;   // 16-byte chunks per staged row
   constexpr int KS = GBK / 16;   // MFMA k-steps per k-tile
-  constexpr int LPT = 2 * CPR;   // direct-to-LDS loads per lane per k-tile
+  // NW = 4: a wave per SIMD, each 128 tokens x 128 columns; NW = 8: two per
+  // SIMD, each 128 tokens x 64 columns (the other covers its stalls)
+  static_assert(NW == 4 || NW == 8, "waves");
+  constexpr int WCOLS = NW / 2, CW = WBN / WCOLS, NI = CW / 32;  // column groups, width, blocks
+  constexpr int NLD = CPR * 4 / NW;  // loads per lane per operand per k-tile
+  constexpr int LPT = 2 * NLD;   // direct-to-LDS loads per lane per k-tile
   static_assert(GBK == 32 || GBK == 64, "k-tile depth");
   constexpr int TOK = TBM * GBK, STAGE = TOK + WBN * GBK;  // elements per stage
   constexpr int RP_ = WBN + 4, CP_ = TBM / 2 + 4;           // epilogue pitches (fp32)
@@ -744,7 +750,7 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
-  const int wc = wave & 1, wt = wave >> 1;  // column half, token half
+  const int wc = wave % WCOLS, wt = wave / WCOLS;  // column group, token half
 
   const size_t a_ext = (size_t)(M - row0) * K * sizeof(TM);
   const size_t b_ext = (size_t)(seg.width - col0) * K * sizeof(TB);
@@ -764,8 +770,8 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
   // (fixed bound: a bound that depends on GBK drops the host-side launch stub)
   unsigned va[8], vb[8];
 #pragma unroll
-  for (int i = 0; i < CPR; ++i) {
-    const int P = (i * 4 + wave) * 64 + lane, r = P / CPR;
+  for (int i = 0; i < NLD; ++i) {
+    const int P = (i * NW + wave) * 64 + lane, r = P / CPR;
     const int kc = 8 * ((P % CPR) ^ swz(r));
     va[i] = row0 + r < M ? (unsigned)((r * K + kc) * sizeof(TM)) : 0x80000000u;
     vb[i] = col0 + r < seg.width ? (unsigned)((r * K + kc) * sizeof(TB)) : 0x80000000u;
@@ -773,21 +779,21 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
   auto issue = [&](int kt, int stg) {
     const int ka = kt * GBK * (int)sizeof(TM), kb = kt * GBK * (int)sizeof(TB);
 #pragma unroll
-    for (int i = 0; i < CPR; ++i)  // token rows
+    for (int i = 0; i < NLD; ++i)  // token rows
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(lds + stg * STAGE + (i * 4 + wave) * 512),
+          ra, (__attribute__((address_space(3))) void*)(lds + stg * STAGE + (i * NW + wave) * 512),
           16, va[i], ka, 0, 0);
 #pragma unroll
-    for (int i = 0; i < CPR; ++i)  // weight rows
+    for (int i = 0; i < NLD; ++i)  // weight rows
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb,
-          (__attribute__((address_space(3))) void*)(lds + stg * STAGE + TOK + (i * 4 + wave) * 512),
+          (__attribute__((address_space(3))) void*)(lds + stg * STAGE + TOK + (i * NW + wave) * 512),
           16, vb[i], kb, 0, 0);
   };
   auto frag_off = [&](int row, int chunk) { return row * GBK + 8 * (chunk ^ swz(row)); };
 
-  // acc[i][j]: column block i (32 columns at 128 wc + 32 i) x token block j
-  // (32 tokens at 128 wt + 32 j)
+  // acc[i][j]: column block i (32 columns at CW wc + 32 i, i < NI) x token
+  // block j (32 tokens at 128 wt + 32 j); fixed bounds, blocks i >= NI unused
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -806,8 +812,8 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
     const TB* sb = (const TB*)(lds + stg * STAGE + TOK);
     const int ch = 2 * ks + lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const TBx8 w = *(const TBx8*)(sb + frag_off(128 * wc + 32 * i + lr, ch));
+    for (int i = 0; i < NI; ++i) {
+      const TBx8 w = *(const TBx8*)(sb + frag_off(CW * wc + 32 * i + lr, ch));
       if constexpr (__is_same(TM, TB))
         a[i] = w;
       else
@@ -818,15 +824,16 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
   };
   auto mfmas = [&](const TMx8 (&a)[4], const TMx8 (&b)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
   };
   // RoPE angles of the epilogue, fetched now so their latency hides under the
   // main loop (the loads are older than every tile load, so the loop's vmcnt
   // waits cover them)
+  // (eight waves: no room for them in 256 registers)
   RopePre rp[2];
-  const bool pre = seg.kind == kHead && seg.rope;
+  const bool pre = NW == 4 && seg.kind == kHead && seg.rope;
   if (pre) {
     rope_prefetch<D>(p, row0, 0, rp[0]);
     rope_prefetch<D>(p, row0, 1, rp[1]);
@@ -887,18 +894,18 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
       const int trow = 64 * wt + 32 * jj + lr;
       if (seg.kind == kHeadT) {  // tile [column][token]
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int c = 128 * wc + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+            const int c = CW * wc + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
             tile[c * CP_ + trow] = acc[i][j][r];
           }
       } else {  // tile [token][column], float4 runs
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            const int c = 128 * wc + 32 * i + 8 * a + 4 * lg;
+            const int c = CW * wc + 32 * i + 8 * a + 4 * lg;
             *(float4*)(tile + trow * RP_ + c) =
                 make_float4(acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2],
                             acc[i][j][4 * a + 3]);
@@ -906,13 +913,14 @@ __global__ __launch_bounds__(256, 1) void project_gemm_wide(GemmProblem p, SegTi
       }
     }
     lds_barrier();  // the tile is in LDS
+    if (NW == 8 && tid >= 256) return;  // the stores are laid out for 256 threads
 #pragma unroll
     for (int chh = 0; chh < 2; ++chh) {
       if (seg.kind == kHeadT)
         store_cols<TO, D, CP_>(tile + 128 * chh * CP_, row0, hf, col0 + 128 * chh, seg, p);
       else if (seg.kind == kHead && seg.rope)
         store_rows_rope<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p,
-                                           &rp[hf]);
+                                           pre ? &rp[hf] : nullptr);
       else
         store_rows_plain<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p);
     }
@@ -1026,8 +1034,8 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
       const int total = nCw * nMw, per_xcd = (total + kNumXcd - 1) / kNumXcd;
       const dim3 grid(per_xcd * kNumXcd);
 #define DAR_W(TA, TO, D)                                                                    \
-  hipLaunchKernelGGL((project_gemm_wide<TA, bf16, TO, D, 64>), grid, dim3(256), 0, s, p, sw, nMw, \
-                     nCw, band, per_xcd)
+  hipLaunchKernelGGL((project_gemm_wide<TA, bf16, TO, D, 64, 8>), grid, dim3(512), 0, s, p, sw, \
+                     nMw, nCw, band, per_xcd)
       if (p.a_type == kBF16 && p.out_type == kF16) {
         if (p.d_k == 64) DAR_W(bf16, f16, 64); else DAR_W(bf16, f16, 128);
         return hipGetLastError();
