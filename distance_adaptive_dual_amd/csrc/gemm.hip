@@ -310,8 +310,9 @@ __device__ __forceinline__ void rope_cs8(const RopeTab& t, int pos, int t0, floa
 // Tile [128 tokens][PITCH] (128 columns used) -> kRowMajor, or kHead without rotation.
 template <typename OutT, int D, bool RP, int PITCH = EPI_P>
 __device__ __forceinline__ void store_rows_plain(const float* tile, int row0, int hf, int col0,
-                                                 const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
+                                                 const GemmSeg& seg, const GemmProblem& p,
+                                                 int tid = threadIdx.x) {
+  const int M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
   OutT* out = (OutT*)seg.out;
   // chunk q = tid + 256 k: column chunk (q & 7) + 8 (q >> 10), tile row (q >> 3) & 127;
   // chunks k and k + 4 share the row
@@ -376,9 +377,10 @@ __device__ __forceinline__ void rope_prefetch(const GemmProblem& p, int row0, in
 template <typename OutT, int D, bool RP, int PITCH = EPI_P>
 __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int hf, int col0,
                                                 const GemmSeg& seg, const GemmProblem& p,
-                                                const RopePre* pre = nullptr) {
+                                                const RopePre* pre = nullptr,
+                                                int tid = threadIdx.x) {
   constexpr int HALF = D / 2, PCH = D / 16;  // pair chunks of 8 per head
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
+  const int M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
   OutT* out = (OutT*)seg.out;
   const int w8 = tid & 7, r0 = 4 * (tid >> 3);
   const int hl = w8 / PCH, t0 = 8 * (w8 % PCH);
@@ -445,8 +447,9 @@ __device__ __forceinline__ void store_rows_rope(const float* tile, int row0, int
 // Tile [128 columns][TP] (token innermost) -> kHeadT, out[b, head, t, n].
 template <typename OutT, int D, int TP>
 __device__ __forceinline__ void store_cols(const float* tile, int row0, int hf, int col0,
-                                           const GemmSeg& seg, const GemmProblem& p) {
-  const int tid = threadIdx.x, M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
+                                           const GemmSeg& seg, const GemmProblem& p,
+                                           int tid = threadIdx.x) {
+  const int M = p.M, width = seg.width, H = seg.heads ? seg.heads : p.heads;
   OutT* out = (OutT*)seg.out;
   const int tc = tid & 7;  // chunk of 8 tokens within the 64-token run
 #pragma unroll
@@ -913,16 +916,23 @@ __global__ __launch_bounds__(64 * NW, 1) void project_gemm_wide(GemmProblem p, S
       }
     }
     lds_barrier();  // the tile is in LDS
-    if (NW == 8 && tid >= 256) return;  // the stores are laid out for 256 threads
-#pragma unroll
-    for (int chh = 0; chh < 2; ++chh) {
+    // The stores are laid out for 256 threads and 128 columns: with 8 waves
+    // each half of the workgroup writes one 128-column half of the tile.
+    auto store_half = [&](int chh, int t) {
       if (seg.kind == kHeadT)
-        store_cols<TO, D, CP_>(tile + 128 * chh * CP_, row0, hf, col0 + 128 * chh, seg, p);
+        store_cols<TO, D, CP_>(tile + 128 * chh * CP_, row0, hf, col0 + 128 * chh, seg, p, t);
       else if (seg.kind == kHead && seg.rope)
         store_rows_rope<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p,
-                                           pre ? &rp[hf] : nullptr);
+                                           pre ? &rp[hf] : nullptr, t);
       else
-        store_rows_plain<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p);
+        store_rows_plain<TO, D, false, RP_>(tile + 128 * chh, row0, hf, col0 + 128 * chh, seg, p,
+                                            t);
+    };
+    if constexpr (NW == 8) {
+      store_half(wave >> 2, tid & 255);
+    } else {
+      store_half(0, tid);
+      store_half(1, tid);
     }
   };
   pass(std::integral_constant<int, 0>{});
