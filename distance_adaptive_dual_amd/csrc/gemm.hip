@@ -39,10 +39,11 @@ constexpr long kWideMinTiles = DAR_WIDE_MIN_TILES;  // wide-tile GEMM from this 
 #define DAR_WIDE_BAND_BYTES (4 << 20)
 #endif
 constexpr long kWideBandBytes = DAR_WIDE_BAND_BYTES;  // weight bytes of one band
-// The wide kernel serves long contractions only: its one workgroup per CU
-// cannot overlap the epilogue with another tile's main loop, which only a
-// long main loop amortizes (measured on the 1B-scale layer: K = 2048 gains 4%,
-// K = 512 loses 19% against the 256 x 128 kernel).
+// The wide kernel's one workgroup per CU cannot overlap the epilogue with
+// another tile's main loop, which a long main loop amortizes: bf16
+// activations need K >= 1024 (the first projection GEMM).  The fp16 global
+// GEMM (K = d_down = 512 at the 1B scale) gains 1.4% of the projection with
+// the eight-wave kernel and its split stores.
 constexpr int kWideMinK = 1024;
 
 // Slot of k-chunk c (of 4 per 64-byte row) in row r of a staged k-tile:
@@ -1032,8 +1033,10 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
     // wide tiles once there are enough of them to fill every CU several times
     const SegTiles sw = seg_tiles(p, WBN);
     const int nCw = sw.tile0[p.nseg], nMw = (p.M + 255) / 256;
-    if ((long)nCw * nMw >= kWideMinTiles && p.K >= kWideMinK && p.K % 64 == 0 &&
-        p.a_type == kBF16) {
+    // (bf16 activations: the first GEMM, long contractions; fp16: the global
+    // GEMM of h^D, whose K = d_down is shorter but whose epilogue is half its time)
+    if ((long)nCw * nMw >= kWideMinTiles && p.K % 64 == 0 &&
+        ((p.K >= kWideMinK && p.a_type == kBF16) || (p.K >= 512 && p.a_type == kF16))) {
       size_t wbytes = 0;
       for (int i = 0; i < p.nseg; ++i) wbytes += (size_t)p.seg[i].width * p.K * 2;
       // a band's weights about fill one XCD's L2 (4 MB)
@@ -1048,6 +1051,10 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
                      nMw, nCw, band, per_xcd)
       if (p.a_type == kBF16 && p.out_type == kF16) {
         if (p.d_k == 64) DAR_W(bf16, f16, 64); else DAR_W(bf16, f16, 128);
+        return hipGetLastError();
+      }
+      if (p.a_type == kF16 && p.out_type == kF16) {
+        if (p.d_k == 64) DAR_W(f16, f16, 64); else DAR_W(f16, f16, 128);
         return hipGetLastError();
       }
 #undef DAR_W
