@@ -656,10 +656,20 @@ def main():
         sys.exit(1)
     dar.lib()
     if args.calib_copy:
+        # known traffic for the counter runs: a 256 MiB copy, and a 256 MiB
+        # read by direct-to-LDS loads (the DAR kernels' staging path)
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
+        torch.cuda.synchronize()
+        import ctypes
+        CL = ctypes.CDLL(os.path.join(ROOT, "distance_adaptive_dual_amd", "libdar_calib.so"))
+        CL.dar_calib_read_lds.restype = ctypes.c_int
+        CL.dar_calib_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        if CL.dar_calib_read_lds(src.data_ptr(), src.numel(),
+                                 torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("dar_calib_read_lds failed")
         torch.cuda.synchronize()
         del src, dst
 

@@ -84,6 +84,25 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   if ((x[0] ^ x[1] ^ x[2] ^ x[3]) == 0x9e3779b9u) sink[blockIdx.x] = x[0];
 }
 
+// Grid-stride read of 16 KB chunks by direct buffer loads into LDS (the
+// path the DAR kernels stage their tiles with), so traffic counters can be
+// scaled for that kind of load too.  The LDS copy is overwritten unread.
+__global__ __launch_bounds__(256) void read_lds_kernel(const char* __restrict__ src,
+                                                       size_t nchunks) {
+  __shared__ u32x4 buf[1024];  // 16 KB: 4 loads of 1 KB per wave
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + c * 16384), (short)0, 16384, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(buf + (4 * i + wave) * 64), 16,
+          (unsigned)(((4 * i + wave) * 64 + lane) * 16), 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,6 +146,16 @@ int dar_calib_read(const void* src, size_t bytes, unsigned* sink, hipStream_t st
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_kernel, dim3(8192), dim3(256), 0, stream, (const u32x4*)src,
                      bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// Reads `bytes` (a multiple of 16384, 16-byte aligned) from src on the device
+// by direct-to-LDS buffer loads.  Returns the hipError_t of the launch.
+int dar_calib_read_lds(const void* src, size_t bytes, hipStream_t stream) {
+  if (src == nullptr || (bytes % 16384) || ((uintptr_t)src & 15))
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_lds_kernel, dim3(2048), dim3(256), 0, stream, (const char*)src,
+                     bytes / 16384);
   return (int)hipGetLastError();
 }
 

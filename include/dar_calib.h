@@ -35,6 +35,11 @@ int dar_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream)
  * unsigned (written only in an impossible case). */
 int dar_calib_read(const void* src, size_t bytes, unsigned* sink, hipStream_t stream);
 
+/* Device read of `bytes` (multiple of 16384; 16-byte aligned) by direct
+ * buffer loads into LDS, 16 KB per workgroup step: the load path of the DAR
+ * kernels' tile staging, for scaling traffic counters. */
+int dar_calib_read_lds(const void* src, size_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

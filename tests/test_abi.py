@@ -289,7 +289,8 @@ def test_calib_library_exports_and_rejects():
     include/dar_calib.h declares and rejects bad arguments before launching."""
     text = open(CALIB_HEADER).read()
     names = set(re.findall(r"^\s*(?:int|double)\s+(dar_\w+)\s*\(", text, re.M))
-    assert names == {"dar_calib_mfma_flops", "dar_calib_mfma", "dar_calib_copy", "dar_calib_read"}
+    assert names == {"dar_calib_mfma_flops", "dar_calib_mfma", "dar_calib_copy", "dar_calib_read",
+                     "dar_calib_read_lds"}
     L = ctypes.CDLL(os.path.join(ROOT, "distance_adaptive_dual_amd", "libdar_calib.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -310,6 +311,10 @@ def test_calib_library_exports_and_rejects():
                                  ctypes.c_void_p]
     assert L.dar_calib_read(F(0), 100, F(1), None) != 0      # not a multiple of 16
     assert L.dar_calib_read(F(0), 64, None, None) != 0       # no sink
+    L.dar_calib_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert L.dar_calib_read_lds(F(0), 16000, None) != 0      # not a multiple of 16 KB
+    assert L.dar_calib_read_lds(F(0) + 8, 16384, None) != 0  # misaligned source
+    assert L.dar_calib_read_lds(None, 16384, None) != 0      # no source
 
 
 def cache(**kw):
