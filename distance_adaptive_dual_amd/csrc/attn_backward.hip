@@ -677,9 +677,8 @@ struct DkvSmem {
 // The next block is staged in two halves of its head dims (all 64 queries
 // each, so half a block of registers is in flight; a wave's transposed stores
 // then cover 32 row pairs in two column groups 32 banks apart, without
-// conflicts).  At d_k 128 (one wave per SIMD, nothing to hide latency behind)
-// the dV/dK operands are also read ahead of their MFMAs; at d_k 64 the
-// registers that takes spill.
+// conflicts).  The dV/dK operands are read ahead of their MFMAs (at d_k 128,
+// one wave per SIMD, there is nothing else to hide their latency behind).
 template <int D, bool BUF>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
@@ -688,7 +687,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
   const int kt = (int)(blockIdx.x / BH);  // small key tiles (most queries) first
   const int bh = (int)(blockIdx.x % BH), b = bh / H, h = bh % H;
-  constexpr bool WIDE = D == 128;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // block tests are scalar
   const int k0 = kt * MQ, kw0 = k0 + 32 * wave, kj = kw0 + lr;
@@ -728,10 +726,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
     const f16* Vp = (const f16*)(src ? p.V_glob : p.V_loc) + (size_t)bh * D * N;
     f16x8 kf[NS], vf[NS];  // this lane's key, dims 16 st + 8 lg .. +8
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
+    for (int st = 0; st < NS; ++st)
       kf[st] = *(const f16x8*)(Kp + (size_t)kc * D + 16 * st + 8 * lg);
+    {
+      // V is [d][n] per (batch, head), the key a column of it: a per-lane base
+      // and wave-uniform row offsets.  Indexed as (16 st + 8 lg + e) N + kc
+      // instead, the compiler hoists one 64-bit offset per element out of the
+      // source loop, NS * 8 register pairs held through the whole kernel.
+      const f16* vcol = Vp + (size_t)(8 * lg) * N + kc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vf[st][e] = Vp[(size_t)(16 * st + 8 * lg + e) * N + kc];
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vf[st][e] = vcol[(size_t)(16 * st + e) * N];
     }
     f32x16 dvt[NB], dkt[NB];
 #pragma unroll
@@ -774,31 +780,27 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
             s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + arow + 16 * st), kf[st], s);
             dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + arow + 16 * st), vf[st], dp);
           }
-          if constexpr (WIDE) {
-            // the 32 staged lse/D values and the first four operands are read
-            // before the MFMAs start, then one more after each MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 16 + 4, 0);
+          // the 32 staged lse/D values and the first four operands are read
+          // before the MFMAs start, then one more after each MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 16 + 4, 0);
 #pragma unroll
-            for (int k = 0; k < 2 * NS - 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          for (int k = 0; k < 2 * NS - 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          // dV/dK operands of the first 16 queries (d_k 128: read before the
-          // exponentials, so that their LDS latency hides under them)
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          // dV/dK operands of the first 16 queries, read before the
+          // exponentials so that their LDS latency hides under them
           const int tb = lr * TP + 32 * sb + 8 * lg;
           // (16-byte aligned: every term is a multiple of 8 halves; stated, or
           // the reads below are split into 4-byte accesses that conflict)
           const f16* gtb = (const f16*)__builtin_assume_aligned(sm.gt[bf] + tb, 16);
           const f16* qtb = (const f16*)__builtin_assume_aligned(sm.qt[bf] + tb, 16);
           f16x8 ga[NB], qa[NB];
-          if constexpr (WIDE) {
 #pragma unroll
-            for (int db = 0; db < NB; ++db) {
-              ga[db] = *(const f16x8*)(gtb + 32 * db * TP);
-              qa[db] = *(const f16x8*)(qtb + 32 * db * TP);
-            }
+          for (int db = 0; db < NB; ++db) {
+            ga[db] = *(const f16x8*)(gtb + 32 * db * TP);
+            qa[db] = *(const f16x8*)(qtb + 32 * db * TP);
           }
           f16x8 pb[2], dsb[2];
           if (bp.masked) {
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
               dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
             }
           }
-          if constexpr (WIDE) {
+          {
             // the second 16 queries' operands, read while the first ones' MFMAs run
             f16x8 gb[NB], qb[NB];
 #pragma unroll
@@ -836,15 +838,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
               dvt[db] = mfma32x32x16(gb[db], pb[1], dvt[db]);
               dkt[db] = mfma32x32x16(qb[db], dsb[1], dkt[db]);
             }
-          } else {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int db = 0; db < NB; ++db) {
-                const int t = tb + 32 * db * TP + 16 * u;
-                dvt[db] = mfma32x32x16(*(const f16x8*)(sm.gt[bf] + t), pb[u], dvt[db]);
-                dkt[db] = mfma32x32x16(*(const f16x8*)(sm.qt[bf] + t), dsb[u], dkt[db]);
-              }
           }
         }
         if (has_next) store(bf ^ 1, 1);

@@ -634,16 +634,17 @@ __global__ __launch_bounds__(256, (D == 64 && DR == 0) ? 4 : 2) void attn_prefil
       const float inv = 1.f / l_tot;
       if (LSE && lg == 0)  // m_ref and l are in base 2
         p.lse[(size_t)bh * N + qi] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
-      // the row index is formed here (the empty asm keeps the compiler from
-      // computing the 64-bit address before the pass loop and holding it)
-      int qr = qi - q0;
-      __asm__ volatile("" : "+v"(qr));
+      // the row index and the lane's column offset are formed here (the empty
+      // asm keeps the compiler from computing the 64-bit address before the
+      // pass loop and holding it)
+      int qr = qi - q0, dl = 4 * lg;
+      __asm__ volatile("" : "+v"(qr), "+v"(dl));
       bf16* out = (bf16*)p.o + (orow0 + qr) * (size_t)(H * D) + (size_t)h * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const int d = 32 * db + 8 * rq + 4 * lg;
+          const int d = 32 * db + 8 * rq + dl;
           u32x2 v;
           v[0] = pack_bf16x2(o[db][4 * rq + 0] * inv, o[db][4 * rq + 1] * inv);
           v[1] = pack_bf16x2(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
