@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeo
   // latency overlaps the weights': the lift's W_upV row piece (TPR threads
   // per output row t, DD / TPR columns each, 16-byte chunks) and this
   // thread's latent column of the first CPF partials.
-  constexpr int TPR = 256 / D, WPF = 16, CPF = 32;
+  constexpr int TPR = 256 / D, WPF = 16, CPF = 32, NWP = 4;
   const int h = bh % p.H;
   const bf16* Wv = (const bf16*)p.W_upV + (size_t)h * D * DD;
   const int t = tid / TPR, part = tid % TPR;
@@ -539,6 +539,10 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeo
   float pv[CPF];
 #pragma unroll
   for (int c = 0; c < CPF; ++c) pv[c] = (tid < DD && c < nc) ? pl[c * PF + 2 + tid] : 0.f;
+  // and this thread's column of the first NWP window partials
+  float wp[NWP];
+#pragma unroll
+  for (int k = 0; k < NWP; ++k) wp[k] = (tid < D && k < n_win) ? pw[k * (2 + D) + 2 + tid] : 0.f;
   if (wave == 0) {
     // common maximum over the non-empty partials, their weights and the total
     float M = (lane < n_win && pw[lane * (2 + D) + 1] > 0.f) ? pw[lane * (2 + D)] : -INFINITY;
@@ -567,7 +571,10 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeProblem p, DecodeGeo
   // the window's value sum in d_k space
   if (tid < D) {
     float a = 0.f;
-    for (int k = 0; k < n_win; ++k) a = fmaf(wwf[k], pw[k * (2 + D) + 2 + tid], a);
+#pragma unroll
+    for (int k = 0; k < NWP; ++k)
+      if (k < n_win) a = fmaf(wwf[k], wp[k], a);
+    for (int k = NWP; k < n_win; ++k) a = fmaf(wwf[k], pw[k * (2 + D) + 2 + tid], a);
     wacc[tid] = a;
   }
   // latent sum: a thread per latent column (the first CPF partials from the

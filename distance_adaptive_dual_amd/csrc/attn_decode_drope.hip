@@ -25,7 +25,8 @@
 //              X_lat operand (eight tokens of one latent column per lane) is
 //              read from the row-major block with ds_read_b64_tr_b16;
 //   window  -- per (batch, head): the positions p-w+1 .. p, content keys and
-//              values from the ring, rotary keys from the cache;
+//              values from the ring, rotary keys from the cache (in the same
+//              launch as the absorb, which it does not need);
 //   combine -- the latent decode's log-sum-exp merge and single lift by
 //              W_upV (decode_combine).
 // Scores are base-2 logits: log2(e) / sqrt(d_k + d_R) is folded into qa.
@@ -89,24 +90,24 @@ DropeGeom drope_geom(const DropeDecodeProblem& p) {
   return g;
 }
 
-// qa = scale [W_upK_a^T qC_a ; qR_a] split into bf16 hi + lo.  Grid
-// (H, ceil(qw / 64), ceil(B / 4)), four waves: column t = 64 blockIdx.y + lane
-// of the absorbed rows of four batches, the contraction over the head's d_k
-// split between the waves (each a quarter, its loads all in flight) and
-// summed through LDS.
+// qa = scale [W_upK_a^T qC_a ; qR_a] split into bf16 hi + lo.  Blocks
+// (h, by, bz) over (H, ceil(qw / 64), ceil(B / 4)), four waves: column
+// t = 64 by + lane of the absorbed rows of four batches, the contraction over
+// the head's d_k split between the waves (each a quarter, its loads all in
+// flight) and summed through LDS.
 template <int D, int DR>
-__global__ __launch_bounds__(256) void drope_absorb(DropeDecodeProblem p, DropeGeom g, bf16* qa_hi,
-                                                     bf16* qa_lo) {
+__device__ __forceinline__ void absorb_block(const DropeDecodeProblem& p, const DropeGeom& g,
+                                             bf16* qa_hi, bf16* qa_lo, int h, int by, int bz) {
   constexpr int NBT = 4, CQ = D / 4;
   __shared__ float qcs[NBT][D];
   __shared__ float red[4][NBT][64];
-  const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.y * 64 + lane;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = by * 64 + lane;
   const int DD = p.d_down;
   const float scl = kLog2e / sqrtf((float)(D + DR));
   const bf16* Wk = (const bf16*)p.W_upK + (size_t)h * D * DD;
   {
-    const int b0 = blockIdx.z * NBT;
+    const int b0 = bz * NBT;
     const int nb = min(NBT, p.B - b0);
     for (int e = threadIdx.x; e < NBT * D; e += 256) {
       const int bi = e / D, c = e % D;
@@ -402,13 +403,13 @@ __global__ __launch_bounds__(DWAVES * 64) void drope_stream(DropeDecodeProblem p
 // exponentials, then the values read the same way, each lane accumulating
 // its 8 columns; the key groups' accumulators are summed through LDS at the end.
 template <int D, int DR>
-__global__ __launch_bounds__(256) void drope_window(DropeDecodeProblem p, DropeGeom g,
-                                                     float* part_win) {
+__device__ __forceinline__ void window_block(const DropeDecodeProblem& p, const DropeGeom& g,
+                                             float* part_win, int blk) {
   constexpr int LPK = D / 8, KPI = 256 / LPK, RL = DR / 8, WT = 1024;
   __shared__ float sc[WT];
   __shared__ float red[2][4];
   __shared__ float accs[KPI][D];
-  const int bh = blockIdx.x / g.n_win, piece = blockIdx.x % g.n_win, b = bh / p.H;
+  const int bh = blk / g.n_win, piece = blk % g.n_win, b = bh / p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = tid % LPK, kg = tid / LPK;
   const long pp = (long)p.ctx - 1;
@@ -515,6 +516,22 @@ __global__ __launch_bounds__(256) void drope_window(DropeDecodeProblem p, DropeG
   }
 }
 
+// One launch for both: the window needs no absorbed query, so the absorb
+// blocks (dispatched first) finish under the window pieces' loads instead of
+// as a latency-bound launch of their own.
+template <int D, int DR>
+__global__ __launch_bounds__(256) void drope_absorb_window(DropeDecodeProblem p, DropeGeom g,
+                                                           bf16* qa_hi, bf16* qa_lo,
+                                                           float* part_win, int n_abs) {
+  const int bid = blockIdx.x;
+  if (bid < n_abs) {
+    const int ny = (g.qw + 63) / 64;
+    absorb_block<D, DR>(p, g, qa_hi, qa_lo, bid % p.H, (bid / p.H) % ny, bid / (p.H * ny));
+  } else {
+    window_block<D, DR>(p, g, part_win, bid - n_abs);
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -541,10 +558,12 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) 
   bf16* qa_lo = (bf16*)(ws + qa);
   float* part_lat = (float*)(ws + 2 * qa);
   float* part_win = (float*)(ws + 2 * qa + lat);
-  const dim3 ga(p.H, (g.qw + 63) / 64, (p.B + 3) / 4);
+  const int n_abs = p.H * ((g.qw + 63) / 64) * ((p.B + 3) / 4);
+  const dim3 gaw(n_abs + p.B * p.H * g.n_win);
   const int n_stream = p.B * g.n_hg * g.n_chunks;
   if (p.d_k == 64) {
-    hipLaunchKernelGGL((drope_absorb<64, 64>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
+    hipLaunchKernelGGL((drope_absorb_window<64, 64>), gaw, dim3(256), 0, s, p, g, qa_hi, qa_lo,
+                       part_win, n_abs);
     if (p.d_down == 128)
       hipLaunchKernelGGL((drope_stream<64, 128, 64, kStreamNB>), dim3(n_stream), dim3(DWAVES * 64),
                          0, s, p, g, qa_hi, qa_lo, part_lat);
@@ -554,10 +573,9 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) 
     else
       hipLaunchKernelGGL((drope_stream<64, 512, 64, 2>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
                          p, g, qa_hi, qa_lo, part_lat);
-    hipLaunchKernelGGL((drope_window<64, 64>), dim3(p.B * p.H * g.n_win), dim3(256), 0, s, p, g,
-                       part_win);
   } else {
-    hipLaunchKernelGGL((drope_absorb<128, 64>), ga, dim3(256), 0, s, p, g, qa_hi, qa_lo);
+    hipLaunchKernelGGL((drope_absorb_window<128, 64>), gaw, dim3(256), 0, s, p, g, qa_hi, qa_lo,
+                       part_win, n_abs);
     if (p.d_down == 128)
       hipLaunchKernelGGL((drope_stream<128, 128, 64, kStreamNB>), dim3(n_stream),
                          dim3(DWAVES * 64), 0, s, p, g, qa_hi, qa_lo, part_lat);
@@ -567,8 +585,6 @@ hipError_t launch_attn_decode_drope(const DropeDecodeProblem& p, hipStream_t s) 
     else
       hipLaunchKernelGGL((drope_stream<128, 512, 64, 2>), dim3(n_stream), dim3(DWAVES * 64), 0, s,
                          p, g, qa_hi, qa_lo, part_lat);
-    hipLaunchKernelGGL((drope_window<128, 64>), dim3(p.B * p.H * g.n_win), dim3(256), 0, s, p,
-                       g, part_win);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
