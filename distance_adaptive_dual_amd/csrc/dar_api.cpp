@@ -681,12 +681,16 @@ static dar_status prefill_chunk_impl(const void* h, const void* W_down, const vo
   // 2. the prefix's ring rows into the local arrays
   if (e == hipSuccess)
     e = launch_ring_to_local(K_win, V_win, B, heads, d_k, w, loc0, p0, nloc, Kl, Vl, stream);
-  // 3. global keys / values of the prefix from the latent cache (per sequence:
-  //    the cache rows are cap apart), then of the chunk from its fp16 h^D
-  for (int b = 0; b < B && p0 > 0 && e == hipSuccess; ++b) {
+  // 3. global keys / values of the prefix from the latent cache, then of the
+  //    chunk from its fp16 h^D.  The prefix is one GEMM over every sequence
+  //    (cache rows cap apart) while the cache is under 2 GiB, else one per
+  //    sequence.
+  const bool one = 2 * (size_t)B * cap * d_down <= (size_t)0x7ffffff0;
+  for (int b = 0; b < (one ? 1 : B) && p0 > 0 && e == hipSuccess; ++b) {
     GemmProblem g2{};
     g2.A = (const char*)h_D_cache + 2 * (size_t)b * cap * d_down;
-    g2.M = p0;
+    g2.M = one ? B * p0 : p0;
+    g2.a_ld_seq = one ? cap : 0;
     g2.K = d_down;
     g2.a_type = kBF16;
     g2.b_type = kBF16;

@@ -197,6 +197,10 @@ struct GemmProblem {
   // n_seq rows per sequence.
   const int* cu = nullptr;
   int n_cu = 0;
+  // Rows of A between the first rows of consecutive sequences (0: n_seq, the
+  // rows packed): GEMM row b n_seq + n reads A row b a_ld_seq + n, e.g. the
+  // prefixes of B sequences in a latent cache of a_ld_seq rows each.
+  int a_ld_seq = 0;
 };
 
 hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s);

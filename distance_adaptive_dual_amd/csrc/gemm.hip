@@ -249,6 +249,12 @@ __device__ __forceinline__ int out_index(const GemmProblem& p, const GemmSeg& se
 // Uniform sequences: base = b * ld.  Ragged (cu): one block per sequence at
 // its first row, the sequence's row range clamped into [0, M]; `ok` is false
 // for a row outside the range found (inconsistent cu), which is not written.
+// Row of A read by GEMM row g: g itself, or with a_ld_seq set, row n of
+// sequence b = g / n_seq at b a_ld_seq + n.
+__device__ __forceinline__ int a_row(const GemmProblem& p, int g) {
+  return p.a_ld_seq > 0 ? (g / p.n_seq) * p.a_ld_seq + g % p.n_seq : g;
+}
+
 struct RowLoc {
   int b, n, len, ld;
   size_t base;
@@ -555,10 +561,11 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
 
   // Buffer resources over this tile's rows (byte extents; invalid lanes use an
   // offset past the extent and read zeros).
-  const size_t a_ext = (size_t)(M - row0) * K * sizeof(TM);
+  const int ar0 = a_row(p, row0);
+  const size_t a_ext = (size_t)(a_row(p, M - 1) + 1 - ar0) * K * sizeof(TM);
   const size_t b_ext = (size_t)(seg.width - col0) * K * sizeof(TB);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const TM*)p.A + (size_t)row0 * K), (short)0,
+      (void*)((const TM*)p.A + (size_t)ar0 * K), (short)0,
       (int)(a_ext < 0x7ffffff0u ? a_ext : 0x7ffffff0u), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const TB*)seg.Bt + (size_t)col0 * K), (short)0,
@@ -574,7 +581,8 @@ __global__ __launch_bounds__(256, 2) void project_gemm_mfma(GemmProblem p, SegTi
   for (int i = 0; i < 4; ++i) {
     const int P = (i * 4 + wave) * 64 + lane, r = P >> 2;
     const int kc = 8 * ((P & 3) ^ kswz(r));
-    va[i] = row0 + r < M ? (unsigned)((r * K + kc) * sizeof(TM)) : 0x80000000u;
+    va[i] = row0 + r < M ? (unsigned)(((a_row(p, row0 + r) - ar0) * K + kc) * sizeof(TM))
+                         : 0x80000000u;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -758,10 +766,11 @@ __global__ __launch_bounds__(64 * NW, 1) void project_gemm_wide(GemmProblem p, S
   const int lr = lane & 31, lg = lane >> 5;
   const int wc = wave % WCOLS, wt = wave / WCOLS;  // column group, token half
 
-  const size_t a_ext = (size_t)(M - row0) * K * sizeof(TM);
+  const int ar0 = a_row(p, row0);
+  const size_t a_ext = (size_t)(a_row(p, M - 1) + 1 - ar0) * K * sizeof(TM);
   const size_t b_ext = (size_t)(seg.width - col0) * K * sizeof(TB);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const TM*)p.A + (size_t)row0 * K), (short)0,
+      (void*)((const TM*)p.A + (size_t)ar0 * K), (short)0,
       (int)(a_ext < 0x7ffffff0u ? a_ext : 0x7ffffff0u), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const TB*)seg.Bt + (size_t)col0 * K), (short)0,
@@ -779,7 +788,8 @@ __global__ __launch_bounds__(64 * NW, 1) void project_gemm_wide(GemmProblem p, S
   for (int i = 0; i < NLD; ++i) {
     const int P = (i * NW + wave) * 64 + lane, r = P / CPR;
     const int kc = 8 * ((P % CPR) ^ swz(r));
-    va[i] = row0 + r < M ? (unsigned)((r * K + kc) * sizeof(TM)) : 0x80000000u;
+    va[i] = row0 + r < M ? (unsigned)(((a_row(p, row0 + r) - ar0) * K + kc) * sizeof(TM))
+                         : 0x80000000u;
     vb[i] = col0 + r < seg.width ? (unsigned)((r * K + kc) * sizeof(TB)) : 0x80000000u;
   }
   auto issue = [&](int kt, int stg) {
@@ -970,7 +980,7 @@ __global__ __launch_bounds__(256) void gemm_simt(GemmProblem p, SegTiles st, lon
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 256 * i, r = e / SK, kk = e % SK;
       const int gr = row0 + r, gk = k0 + kk;
-      sAs[kk][r] = (gr < M && gk < K) ? to_f32(A[(size_t)gr * K + gk]) : 0.f;
+      sAs[kk][r] = (gr < M && gk < K) ? to_f32(A[(size_t)a_row(p, gr) * K + gk]) : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -1029,6 +1039,14 @@ hipError_t launch_project_gemm(const GemmProblem& p, dar_dtype dt, hipStream_t s
   // ragged rows: bf16 MFMA kernels, positions from the sequence starts only
   if (p.cu != nullptr && (dt != DAR_BF16 || p.row_pos != nullptr || p.n_cu < 1))
     return hipErrorInvalidValue;
+  // sequences spread in A: whole sequences of n_seq rows, every A row under
+  // 2 GiB of the start (the buffer resources' 32-bit offsets)
+  if (p.a_ld_seq > 0) {
+    const long last = (long)((p.M - 1) / p.n_seq) * p.a_ld_seq + (p.M - 1) % p.n_seq;
+    if (p.a_ld_seq < p.n_seq || p.cu != nullptr || p.row_pos != nullptr ||
+        (last + 1) * p.K * 2 > 0x7ffffff0L)
+      return hipErrorInvalidValue;
+  }
   const SegTiles st = seg_tiles(p);
   const int nC = st.tile0[p.nseg];
   if (dt == DAR_BF16 && p.row_pos == nullptr && p.b_type == kBF16) {
