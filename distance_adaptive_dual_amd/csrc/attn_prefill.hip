@@ -757,26 +757,31 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     }
   }
   const int b = bh / H, h = bh % H;
-  const int N = p.N;
-  const size_t slice = (size_t)bh * N * WD;
-  const f16* Qp = (const f16*)p.Q + slice;
-  const size_t orow0 = (size_t)b * N;
-  const int bytes = N * WD * 2;  // < 2 GiB (checked by the launcher)
+  // Chunk form: the queries are positions q0 .. N-1 (Q and o hold N - q0
+  // rows), the local arrays hold positions loc0 .. N-1 (loc0 a multiple of
+  // the key tile), the global arrays 0 .. N-1.  A whole prefill has
+  // q0 = loc0 = 0.
+  const int N = p.N, q0 = p.q0, loc0 = p.loc0;
+  const int nqr = N - q0, nloc = N - loc0;
+  const size_t slice = (size_t)bh * N * WD, lslice = (size_t)bh * nloc * WD;
+  const f16* Qp = (const f16*)p.Q + (size_t)bh * nqr * WD;
+  const size_t orow0 = (size_t)b * nqr;
+  const int bytes = N * WD * 2, lbytes = nloc * WD * 2;  // < 2 GiB (checked by the launcher)
   // (four scalars, not arrays: an array indexed by the source would be
   // placed in memory)
   const __amdgpu_buffer_rsrc_t rKg = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const f16*)p.K_glob + slice), (short)0, bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rKl = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const f16*)p.K_loc + slice), (short)0, bytes, 0x00020000);
+      (void*)((const f16*)p.K_loc + lslice), (short)0, lbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rVg = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const f16*)p.V_glob + slice), (short)0, bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rVl = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const f16*)p.V_loc + slice), (short)0, bytes, 0x00020000);
+      (void*)((const f16*)p.V_loc + lslice), (short)0, lbytes, 0x00020000);
   // rotary keys of sequence b (positions 0 .. N-1, every head) and queries
   const __amdgpu_buffer_rsrc_t rKR = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(DR > 0 ? (const f16*)p.KR + (size_t)b * N * DR : (const f16*)p.Q), (short)0,
       N * DR * 2, 0x00020000);
-  const f16* QRp = DR > 0 ? (const f16*)p.QR + (size_t)bh * N * DR : nullptr;
+  const f16* QRp = DR > 0 ? (const f16*)p.QR + (size_t)bh * nqr * DR : nullptr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
@@ -784,7 +789,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
   // This lane's fixed byte offsets within a tile: LDS slot P = (8 i + wave) 64
   // + lane of the K tile (row P / 16, slot P % 16) and of the V^T tile (row
   // P / 8, slot P % 8), loaded from the chunk the swizzle puts there.
-  unsigned vk[2], vv[2];
+  unsigned vk[2], vv[2], vl[2];  // V^T rows: N (global) or nloc (local) keys apart
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int P = (8 * i + wave) * 64 + lane;
@@ -792,6 +797,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     vk[i] = (unsigned)((kr * WD + 8 * kc) * 2);
     const int vr = P >> 3, vc = (P & 7) ^ ((vr >> 1) & 7);
     vv[i] = (unsigned)((vr * N + 8 * vc) * 2);
+    vl[i] = (unsigned)((vr * nloc + 8 * vc) * 2);
   }
   // rotary region: slot P = wave 64 + lane (row P / 8, slot P % 8)
   unsigned vkr = 0;
@@ -800,6 +806,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     vkr = (unsigned)((rr * DR + 8 * rc) * 2);
   }
   auto issue = [&](int j0, int src, int stg) {
+    const int jr = src ? j0 - loc0 : j0;  // first row of the tile in its source's arrays
     if constexpr (DR > 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rKR, (__attribute__((address_space(3))) void*)(sm[stg].kr + wave * 512), 16, vkr,
@@ -808,12 +815,12 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           src ? rKl : rKg, (__attribute__((address_space(3))) void*)(sm[stg].k + (8 * i + wave) * 512), 16,
-          vk[i], j0 * WD * 2, 0, 0);
+          vk[i], jr * WD * 2, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           src ? rVl : rVg, (__attribute__((address_space(3))) void*)(sm[stg].v + (8 * i + wave) * 512), 16,
-          vv[i], j0 * 2, 0, 0);
+          src ? vl[i] : vv[i], jr * 2, 0, 0);
   };
   // s_waitcnt vmcnt(LPP n) (lgkmcnt and expcnt left alone): at most n later
   // passes in flight; N's low 4 bits in [3:0], its high 2 bits in [15:14]
@@ -833,20 +840,22 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
   for (int qn = 0; qn < nq; ++qn) {
     const int qt = qn == 0 ? q_hi : pr;
     if (qn > 0) __syncthreads();  // every wave is done with the ring
-    const int i0 = qt * WQT, qw0 = i0 + 32 * wave, qi = qw0 + lr;
+    const int i0 = q0 + qt * WQT, qw0 = i0 + 32 * wave, qi = qw0 + lr;
     const int i_last = min(i0 + WQT - 1, N - 1), wi_last = min(qw0 + 31, N - 1);
     f16x8 qf[NQ];
     {
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int st = 0; st < WD / 16; ++st) {
-        const u32x4 v = qi < N ? *(const u32x4*)(Qp + (size_t)qi * WD + 16 * st + 8 * lg) : z;
+        const u32x4 v =
+            qi < N ? *(const u32x4*)(Qp + (size_t)(qi - q0) * WD + 16 * st + 8 * lg) : z;
         qf[st] = __builtin_bit_cast(f16x8, v);
       }
 #pragma unroll
       for (int st = WD / 16; st < NQ; ++st) {
-        const u32x4 v =
-            qi < N ? *(const u32x4*)(QRp + (size_t)qi * DR + 16 * (st - WD / 16) + 8 * lg) : z;
+        const u32x4 v = qi < N ? *(const u32x4*)(QRp + (size_t)(qi - q0) * DR +
+                                                 16 * (st - WD / 16) + 8 * lg)
+                               : z;
         qf[st] = __builtin_bit_cast(f16x8, v);
       }
     }
@@ -916,7 +925,7 @@ __global__ __launch_bounds__(512, 1) void attn_prefill_ring(PrefillProblem p, in
       const float inv = 1.f / l_tot;
       if (LSE && lg == 0)  // m_ref and l are in base 2
         p.lse[(size_t)bh * N + qi] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
-      bf16* out = (bf16*)p.o + (orow0 + qi) * (size_t)(H * WD) + (size_t)h * WD;
+      bf16* out = (bf16*)p.o + (orow0 + (qi - q0)) * (size_t)(H * WD) + (size_t)h * WD;
 #pragma unroll
       for (int db = 0; db < WD / 32; ++db)
 #pragma unroll
@@ -1041,10 +1050,11 @@ hipError_t launch_attn_prefill(const PrefillProblem& p_in, dar_dtype dt, hipStre
                            nQT, nPair, remap, paired);
       return hipGetLastError();
     }
-    if (p.d_k == 128 && !chunk && p.cu == nullptr && p.N % KT == 0 &&
+    if (p.d_k == 128 && p.cu == nullptr && p.N % KT == 0 && p.loc0 % KT == 0 &&
         (long)p.N * WD * 2 < 0x7fffffffL) {
-      // whole prefill, complete key tiles: the ring kernel (pairs of query tiles)
-      const int nQW = (p.N + WQT - 1) / WQT, nPW = (nQW + 1) / 2;
+      // complete key tiles (a whole prefill, or a chunk whose local arrays
+      // start on a tile): the ring kernel (pairs of query tiles)
+      const int nQW = (p.N - p.q0 + WQT - 1) / WQT, nPW = (nQW + 1) / 2;
       if (lse)
         hipLaunchKernelGGL(attn_prefill_ring<true>, dim3(nPW * BH), dim3(512), 0, s, p, nQW, nPW,
                            remap);

@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void ring_fill_kernel(const f16* __restrict__ 
 // The other direction, for a prefill chunk: positions j0 .. j0+63 (clipped to
 // [base, p0)) of the ring into the local arrays of positions base .. base+len-1
 // (fp16; Vt token-innermost):  K[b, h, j - base, :] = K_win[b, h, j mod w, :],
-// Vt[b, h, :, j - base] = V_win[b, h, j mod w, :].
+// Vt[b, h, :, j - base] = V_win[b, h, j mod w, :] for the positions the ring
+// holds (j > p0 - w), zeros below them (base may be rounded down to a tile).
 template <int D>
 __global__ __launch_bounds__(256) void ring_to_local_kernel(const bf16* __restrict__ Kw,
                                                             const bf16* __restrict__ Vw,
@@ -157,8 +158,10 @@ __global__ __launch_bounds__(256) void ring_to_local_kernel(const bf16* __restri
   for (int e = tid; e < nj * D; e += 256) {
     const int r = e / D, t = e % D;
     const int j = j0 + r;
-    K[(size_t)(j - base) * D + t] = (f16)(float)KW[(size_t)(j % w) * D + t];
-    vt[r * (D + 2) + t] = (f16)(float)VW[(size_t)(j % w) * D + t];
+    // positions the ring no longer holds (j <= p0 - w) are written as zeros
+    const bool held = j > p0 - w;
+    K[(size_t)(j - base) * D + t] = held ? (f16)(float)KW[(size_t)(j % w) * D + t] : (f16)0.f;
+    vt[r * (D + 2) + t] = held ? (f16)(float)VW[(size_t)(j % w) * D + t] : (f16)0.f;
   }
   __syncthreads();
   for (int e = tid; e < nj * D; e += 256) {

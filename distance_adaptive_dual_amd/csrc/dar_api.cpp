@@ -610,10 +610,12 @@ static dar_status prefill_chunk_impl(const void* h, const void* W_down, const vo
     return DAR_ERR_UNSUPPORTED;
 
   // Positions: the chunk is p0 .. N-1.  Global keys 0 .. N-1 are rebuilt from
-  // the latents; local keys that a chunk query can use are loc0 .. N-1
-  // (the ring's p0-w+1 .. p0-1, then the chunk's own).
+  // the latents; local keys that a chunk query can use are p0-w+1 .. N-1
+  // (the ring's, then the chunk's own).  The local arrays start at loc0, that
+  // position rounded down to a multiple of 64 (rows below p0-w+1 hold zeros
+  // and are never kept), so that their key tiles are whole.
   const int N = p0 + C;
-  const int loc0 = w > 0 ? std::max(0, p0 - (w - 1)) : N;
+  const int loc0 = w > 0 ? std::max(0, p0 - (w - 1)) / 64 * 64 : N;
   const int nloc = N - loc0;
   const size_t rope_bytes = rope_table_bytes(d_k, N - 1);
   const size_t q_bytes = round256(2 * (size_t)B * hd * C);

@@ -272,6 +272,23 @@ def test_chunked_prefill_matches_prefill_rows(chunks, w, d_k, dd, H):
     """A prompt prefilled chunk by chunk over the mixed cache gives every row of
     the oracle's prefill over the whole prompt; decoding the next token after
     the last chunk gives the oracle's next row."""
+    run_chunks(chunks, w, d_k, dd, H)
+
+
+@pytest.mark.parametrize("chunks,w,d_k,dd,H", [
+    ((128, 192, 256), 100, 128, 128, 2),   # local arrays rounded down to a key tile
+    ((64, 320, 64), 300, 128, 64, 2),      # window longer than the first prefixes
+    ((192, 256), 0, 128, 64, 2),           # every pair global
+    ((256, 64, 128), 1, 128, 64, 2),       # only the diagonal local
+])
+def test_chunked_prefill_ring_tiles(chunks, w, d_k, dd, H):
+    """Chunks whose ends are multiples of 64 at d_k 128 run the ring kernel
+    (whole key tiles, the local arrays starting at p0 - w + 1 rounded down to
+    a tile, the rows below it zero): every row matches the oracle's prefill."""
+    run_chunks(chunks, w, d_k, dd, H)
+
+
+def run_chunks(chunks, w, d_k, dd, H):
     B, d = 2, 256
     N = sum(chunks)
     inp = prefill_case(B, N + 1, d, H, d_k, dd, "bf16", seed=900 + N + w)
