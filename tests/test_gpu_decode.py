@@ -288,6 +288,39 @@ def test_chunked_prefill_ring_tiles(chunks, w, d_k, dd, H):
     run_chunks(chunks, w, d_k, dd, H)
 
 
+def test_1b_prompt_in_chunks_slice():
+    """The 1B-width prompt (N 8192, d 2048, 16 heads of 128, w 512, d_down 512)
+    in four chunks of 2048 at full size (the ring kernel on every chunk, with
+    many query-tile pairs per (batch, head) and the local arrays rounded down
+    to a key tile): every row of one (batch, head) slice of the second
+    sequence, chunk by chunk, against the oracle's whole prefill of that
+    slice."""
+    B, N, d, H, d_k, dd, w, C = 2, 8192, 2048, 16, 128, 512, 512, 2048
+    b, hh = 1, 11
+    inp = prefill_case(B, N, d, H, d_k, dd, "bf16", seed=4100)
+    W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    h = dev(inp["h"], "bf16")
+    Lc = torch.zeros((B, N, dd), dtype=torch.bfloat16, device="cuda")
+    Kw = torch.zeros((B, H, w, d_k), dtype=torch.bfloat16, device="cuda")
+    Vw = torch.zeros((B, H, w, d_k), dtype=torch.bfloat16, device="cuda")
+    outs = []
+    for p0 in range(0, N, C):
+        o = dar.dar_prefill_chunk(h[:, p0:p0 + C].contiguous(), W["W_down"], W["W_Q"], W["W_K"],
+                                  W["W_V"], Wk, Wv, H, d_k, p0, Lc, Kw, Vw, w)
+        outs.append(host(o[b:b + 1, :, hh * d_k:(hh + 1) * d_k]))
+    torch.cuda.synchronize()
+    one = dict(inp, h=inp["h"][b:b + 1])
+    P = oracle.project(one["h"], one["W_down"], one["W_up"], one["W_Q"], one["W_K"], one["W_V"],
+                       H, d_k, heads=(hh, hh + 1))
+    S = {k: np.ascontiguousarray(P[k][:, hh:hh + 1]) for k in ("Q", "KL", "VL", "KG", "VG")}
+    ref, _ = oracle.attend(S, w)
+    for c, got in enumerate(outs):
+        err = max_err(got, ref[:, c * C:(c + 1) * C])
+        log("  1b chunk %d (b%d h%d) every row: max err %.3g" % (c, b, hh, err))
+        assert err <= TOL["bf16"]
+
+
 def run_chunks(chunks, w, d_k, dd, H):
     B, d = 2, 256
     N = sum(chunks)
