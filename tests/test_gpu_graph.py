@@ -69,6 +69,50 @@ def test_prefill_graph_replays_match_eager():
         del o2, p2
 
 
+@pytest.mark.parametrize("C", [192, 150])  # chunk end on a key tile (ring kernel), and not
+def test_chunked_prefill_graph_replays_match_eager(C):
+    """One prefill chunk after a cached prefix, captured: every replay, from
+    the same cache state (restored by eager copies between replays, with other
+    eager work), writes the eager output, latent rows and window ring."""
+    B, d, H, d_k, dd, w, C0 = 2, 256, 2, 128, 64, 100, 128
+    N = C0 + C
+    inp = prefill_case(B, N, d, H, d_k, dd, "bf16", seed=950 + C)
+    W = {k: dev_w(inp[k], "bf16") for k in ("W_down", "W_up", "W_Q", "W_K", "W_V")}
+    Wk, Wv = dar.dar_fold(W["W_up"], W["W_K"], W["W_V"], H, d_k)
+    h = dev(inp["h"], "bf16")
+    h1 = h[:, C0:].contiguous()
+    Lc = torch.zeros((B, N, dd), dtype=torch.bfloat16, device="cuda")
+    Kw = torch.zeros((B, H, w, d_k), dtype=torch.bfloat16, device="cuda")
+    Vw = torch.zeros((B, H, w, d_k), dtype=torch.bfloat16, device="cuda")
+    args = (W["W_down"], W["W_Q"], W["W_K"], W["W_V"], Wk, Wv, H, d_k)
+    dar.dar_prefill_chunk(h[:, :C0].contiguous(), *args, 0, Lc, Kw, Vw, w)
+    state = [t.clone() for t in (Lc, Kw, Vw)]
+    ws = torch.empty(dar.chunk_workspace_bytes(B, C, d, dd, H, d_k, C0, w, N), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((B, C, H * d_k), dtype=torch.bfloat16, device="cuda")
+
+    def restore():
+        for t, s0 in zip((Lc, Kw, Vw), state):
+            t.copy_(s0)
+
+    dar.dar_prefill_chunk(h1, *args, C0, Lc, Kw, Vw, w, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, Lc, Kw, Vw)]
+    restore()
+    g = capture(lambda: dar.dar_prefill_chunk(h1, *args, C0, Lc, Kw, Vw, w, o=o, workspace=ws))
+    for rep in range(3):
+        restore()
+        o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("o", "latents", "K ring", "V ring"), (o, Lc, Kw, Vw), ref):
+            assert torch.equal(got, want), "replay %d: %s differs" % (rep, name)
+        # other eager work between replays
+        dar.dar_prefill_chunk(h[:, :C0].contiguous(), *args, 0, Lc, Kw, Vw, w)
+    log("  chunk C=%d: 3 replays equal the eager call" % C)
+
+
 def test_decode_graph_replays_match_eager():
     B, ctx, d, H, d_k, dd, w = 2, 3000, 512, 4, 128, 128, 256
     inp = di.decode_inputs(B, ctx, d, H, d_k, dd, w, seed0=88)
