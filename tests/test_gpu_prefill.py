@@ -372,7 +372,8 @@ def test_attention_ring_tiles(N, w):
 
 @pytest.mark.parametrize("N,d_k,w", [(700, 64, 100), (700, 128, 100), (300, 64, 0),
                                      (300, 128, 1), (2048, 128, 512), (513, 64, 700),
-                                     (1216, 128, 100), (320, 128, 0)])
+                                     (1216, 128, 100), (320, 128, 0), (1216, 64, 100),
+                                     (320, 64, 0)])
 def test_selection_counts_exact(N, d_k, w):
     """Closed form of Eq. 3's selection.  Q = 0 makes the softmax uniform over
     j <= i.  Value dims [0, d_k/2) carry an indicator of j mod (d_k/2) on the
@@ -404,7 +405,8 @@ def test_selection_counts_exact(N, d_k, w):
 
 
 @pytest.mark.parametrize("N,d_k,w", [(600, 64, 100), (600, 128, 257), (300, 64, 1),
-                                     (1216, 128, 257), (320, 128, 1)])
+                                     (1216, 128, 257), (320, 128, 1), (1216, 64, 257),
+                                     (320, 64, 1)])
 def test_key_source_selection(N, d_k, w):
     """Keys follow the same rule as values: q = e_0, local keys -1024 e_0 (their
     softmax weight underflows to 0 wherever a global pair exists), global keys
