@@ -284,9 +284,9 @@ __device__ __forceinline__ void exp_and_pv(const f16* sv, const f32x16 (&s)[2],
                                            f32x16 (&o)[D / 32], float m_ref, float& l_run,
                                            float sc, int lr, int lg) {
   constexpr int VP = PassSmem<D>::VP;
-  // V^T fragments of the first column blocks are requested first and arrive
-  // while the exponentials run.
-  constexpr int VPRE = 2;  // column blocks of 32 preloaded
+  // Every V^T fragment of the pass is requested first and arrives while the
+  // exponentials run.
+  constexpr int VPRE = D / 32;  // column blocks of 32
   f16x8 vf[VPRE][4];
 #pragma unroll
   for (int db = 0; db < VPRE; ++db) {
@@ -314,20 +314,6 @@ __device__ __forceinline__ void exp_and_pv(const f16* sv, const f32x16 (&s)[2],
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int db = 0; db < VPRE; ++db) o[db] = mfma32x32x16(vf[db][u], pf[u], o[db]);
-  if constexpr (D / 32 > VPRE) {
-    f16x8 vx[D / 32 - VPRE][4];
-#pragma unroll
-    for (int db = VPRE; db < D / 32; ++db) {
-      const f16* vb = sv + (32 * db + lr) * VP + 8 * lg;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) vx[db - VPRE][u] = *(const f16x8*)(vb + 16 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int db = VPRE; db < D / 32; ++db)
-        o[db] = mfma32x32x16(vx[db - VPRE][u], pf[u], o[db]);
-  }
 }
 
 // One whole pass of one wave: scores against the staged tile, the keep mask,
