@@ -288,6 +288,31 @@ def test_chunked_prefill_ring_tiles(chunks, w, d_k, dd, H):
     run_chunks(chunks, w, d_k, dd, H)
 
 
+def _chunk_sweep_cases(n=8, seed=4242):
+    """Seeded chunk splits: d_k 128 or 64, 1-4 heads, windows from 0 to past
+    the prompt, chunk ends mostly on multiples of 64 (the ring kernel at d_k
+    128) and sometimes not."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d_k = int(rng.choice([128, 64]))
+        H = int(rng.integers(1, 5))
+        chunks = []
+        for _ in range(int(rng.integers(2, 5))):
+            c = 64 * int(rng.integers(1, 6))
+            if rng.random() < 0.25:
+                c += int(rng.integers(1, 64))
+            chunks.append(c)
+        w = int(rng.choice([0, 1, int(rng.integers(2, 200)), int(rng.integers(200, 900))]))
+        cases.append((tuple(chunks), w, d_k, int(rng.choice([64, 128])), H))
+    return cases
+
+
+@pytest.mark.parametrize("chunks,w,d_k,dd,H", _chunk_sweep_cases())
+def test_chunked_prefill_seeded_sweep(chunks, w, d_k, dd, H):
+    run_chunks(chunks, w, d_k, dd, H)
+
+
 def test_1b_prompt_in_chunks_slice():
     """The 1B-width prompt (N 8192, d 2048, 16 heads of 128, w 512, d_down 512)
     in four chunks of 2048 at full size (the ring kernel on every chunk, with
