@@ -669,26 +669,32 @@ struct DkvSmem {
   float lse[2][QB], Dd[2][QB];
 };
 
-// dK and dV of each source.  Workgroup: 128 keys of one (batch, head), a wave
-// per 32; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
+// dK and dV of each source.  Workgroup: 128 keys of one (batch, head), 32 per
+// wave; query blocks of 64 (Q, dO, lse2, D) staged into a double LDS buffer
 // and taken as two 32-query sub-blocks, one sweep per source.  S = Q K^T keeps
 // a key per lane; P = 2^(S sc2 - lse2); dP = dO V^T; dS = P (dP - D);
 // dV^T += dO^T P; dK^T += Q^T dS.
 // The next block is staged in two halves of its head dims (all 64 queries
 // each, so half a block of registers is in flight; a wave's transposed stores
 // then cover 32 row pairs in two column groups 32 banks apart, without
-// conflicts).  The dV/dK operands are read ahead of their MFMAs (at d_k 128,
-// one wave per SIMD, there is nothing else to hide their latency behind).
-template <int D, bool BUF>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
+// conflicts).  The dV/dK operands are read ahead of their MFMAs.
+// ROLE 0: a wave computes both dV and dK of its 32 keys (4 waves).  ROLE 1 and
+// 2 split them over two waves that share the staged blocks: ROLE 1 stages the
+// blocks and forms S, P and dV; ROLE 2 forms S, dP, dS and dK.  S is then
+// computed twice, but each wave holds one accumulator instead of two, which
+// at d_k 128 is the difference between one and two waves per SIMD.
+constexpr int kDkvBoth = 0, kDkvV = 1, kDkvK = 2;
+
+template <int D, bool BUF, int ROLE>
+__device__ __forceinline__ void dkv_role(const BwdProblem& p, DkvSmem<D>& sm, int wave) {
   constexpr int NS = D / 16, NB = D / 32;
   constexpr int RP = DkvSmem<D>::RP, TP = DkvSmem<D>::TP, QB = DkvSmem<D>::QB;
-  __shared__ DkvSmem<D> sm;
+  constexpr bool DOV = ROLE != kDkvK, DOK = ROLE != kDkvV;  // this wave's accumulators
+  constexpr bool STAGE = ROLE != kDkvK;                     // this wave stages blocks
   const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
   const int kt = (int)(blockIdx.x / BH);  // small key tiles (most queries) first
   const int bh = (int)(blockIdx.x % BH), b = bh / H, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // block tests are scalar
   const int k0 = kt * MQ, kw0 = k0 + 32 * wave, kj = kw0 + lr;
   const int kc = kj < N ? kj : N - 1;
   const f16* Qp = (const f16*)p.Q + (size_t)bh * N * D;
@@ -703,6 +709,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   Pairs<DC, QB> px;
   float lx = 0.f, dx = 0.f;
   auto load = [&](int i0, int hf) {
+    if constexpr (!STAGE) return;
     if (qside) load_pairs<DC, QB, BUF, D>(px, Qp + DC * hf, 0, i0, N, pi);
     else load_pairs<DC, QB, BUF>(px, Gp + DC * hf, (size_t)(H * D), i0, N, pi);
     if (hf == 0 && tid < QB) {  // staged as the initial values of the S and dP accumulators
@@ -712,6 +719,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
     }
   };
   auto store = [&](int bf, int hf) {
+    if constexpr (!STAGE) return;
     if (qside) store_pairs<DC, QB, RP, TP>(px, sm.q[bf] + DC * hf, sm.qt[bf] + DC * hf * TP, pi);
     else store_pairs<DC, QB, RP, TP, true>(px, sm.g[bf] + DC * hf, sm.gt[bf] + DC * hf * TP, pi);
     if (hf == 0 && tid < QB) {
@@ -724,11 +732,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
   for (int src = 0; src < 2; ++src) {
     const f16* Kp = (const f16*)(src ? p.K_glob : p.K_loc) + (size_t)bh * N * D;
     const f16* Vp = (const f16*)(src ? p.V_glob : p.V_loc) + (size_t)bh * D * N;
-    f16x8 kf[NS], vf[NS];  // this lane's key, dims 16 st + 8 lg .. +8
+    f16x8 kf[NS], vf[DOK ? NS : 1];  // this lane's key, dims 16 st + 8 lg .. +8
 #pragma unroll
     for (int st = 0; st < NS; ++st)
       kf[st] = *(const f16x8*)(Kp + (size_t)kc * D + 16 * st + 8 * lg);
-    {
+    if constexpr (DOK) {
       // V is [d][n] per (batch, head), the key a column of it: a per-lane base
       // and wave-uniform row offsets.  Indexed as (16 st + 8 lg + e) N + kc
       // instead, the compiler hoists one 64-bit offset per element out of the
@@ -739,11 +747,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
 #pragma unroll
         for (int e = 0; e < 8; ++e) vf[st][e] = vcol[(size_t)(16 * st + e) * N];
     }
-    f32x16 dvt[NB], dkt[NB];
+    f32x16 dvt[DOV ? NB : 1], dkt[DOK ? NB : 1];
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dvt[db][r] = dkt[db][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (DOV) dvt[db][r] = 0.f;
+        if constexpr (DOK) dkt[db][r] = 0.f;
+      }
     // queries with a pair of this source for some key of the workgroup
     const int i_begin = src == 0 ? k0 : min(N, k0 + w) / MB * MB;
     const int i_end = src == 0 ? min(N, k_last + w) : N;
@@ -772,19 +783,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             s[r] = sm.lse[bf][32 * sb + perm_row(r, lg)];
-            dp[r] = sm.Dd[bf][32 * sb + perm_row(r, lg)];
+            if constexpr (DOK) dp[r] = sm.Dd[bf][32 * sb + perm_row(r, lg)];
           }
           const int arow = (32 * sb + row_perm(lr)) * RP + 8 * lg;
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
             s = mfma32x32x16(*(const f16x8*)(sm.q[bf] + arow + 16 * st), kf[st], s);
-            dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + arow + 16 * st), vf[st], dp);
+            if constexpr (DOK)
+              dp = mfma32x32x16(*(const f16x8*)(sm.g[bf] + arow + 16 * st), vf[st], dp);
           }
-          // the 32 staged lse/D values and the first four operands are read
+          // the staged lse/D values and the first four operands are read
           // before the MFMAs start, then one more after each MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 16 + 4, 0);
+          constexpr int NM = DOK ? 2 * NS : NS;  // MFMAs of the scores (and dP)
+          __builtin_amdgcn_sched_group_barrier(0x100, (DOK ? 16 : 8) + 4, 0);
 #pragma unroll
-          for (int k = 0; k < 2 * NS - 4; ++k) {
+          for (int k = 0; k < NM - 4; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
@@ -796,11 +809,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
           // the reads below are split into 4-byte accesses that conflict)
           const f16* gtb = (const f16*)__builtin_assume_aligned(sm.gt[bf] + tb, 16);
           const f16* qtb = (const f16*)__builtin_assume_aligned(sm.qt[bf] + tb, 16);
-          f16x8 ga[NB], qa[NB];
+          f16x8 ga[DOV ? NB : 1], qa[DOK ? NB : 1];
 #pragma unroll
           for (int db = 0; db < NB; ++db) {
-            ga[db] = *(const f16x8*)(gtb + 32 * db * TP);
-            qa[db] = *(const f16x8*)(qtb + 32 * db * TP);
+            if constexpr (DOV) ga[db] = *(const f16x8*)(gtb + 32 * db * TP);
+            if constexpr (DOK) qa[db] = *(const f16x8*)(qtb + 32 * db * TP);
           }
           f16x8 pb[2], dsb[2];
           if (bp.masked) {
@@ -809,34 +822,34 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
               const int i = q0 + perm_row(r, lg);
               float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
               pr = ((i < N) & (kj < N) & keep_pair(src, i - kj, w)) ? pr : 0.f;
-              pb[r >> 3][r & 7] = (f16)pr;
-              dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
+              if constexpr (DOV) pb[r >> 3][r & 7] = (f16)pr;
+              if constexpr (DOK) dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
             }
           } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float pr = __builtin_amdgcn_exp2f(s[r] * sc2);
-              pb[r >> 3][r & 7] = (f16)pr;
-              dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
+              if constexpr (DOV) pb[r >> 3][r & 7] = (f16)pr;
+              if constexpr (DOK) dsb[r >> 3][r & 7] = (f16)(pr * dp[r]);
             }
           }
           {
             // the second 16 queries' operands, read while the first ones' MFMAs run
-            f16x8 gb[NB], qb[NB];
+            f16x8 gb[DOV ? NB : 1], qb[DOK ? NB : 1];
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              gb[db] = *(const f16x8*)(gtb + 32 * db * TP + 16);
-              qb[db] = *(const f16x8*)(qtb + 32 * db * TP + 16);
+              if constexpr (DOV) gb[db] = *(const f16x8*)(gtb + 32 * db * TP + 16);
+              if constexpr (DOK) qb[db] = *(const f16x8*)(qtb + 32 * db * TP + 16);
             }
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              dvt[db] = mfma32x32x16(ga[db], pb[0], dvt[db]);
-              dkt[db] = mfma32x32x16(qa[db], dsb[0], dkt[db]);
+              if constexpr (DOV) dvt[db] = mfma32x32x16(ga[db], pb[0], dvt[db]);
+              if constexpr (DOK) dkt[db] = mfma32x32x16(qa[db], dsb[0], dkt[db]);
             }
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-              dvt[db] = mfma32x32x16(gb[db], pb[1], dvt[db]);
-              dkt[db] = mfma32x32x16(qb[db], dsb[1], dkt[db]);
+              if constexpr (DOV) dvt[db] = mfma32x32x16(gb[db], pb[1], dvt[db]);
+              if constexpr (DOK) dkt[db] = mfma32x32x16(qb[db], dsb[1], dkt[db]);
             }
           }
         }
@@ -855,13 +868,33 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem 
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int d = 32 * db + 8 * a + 4 * lg;
-          *(float4*)(dK + d) = make_float4(dkt[db][4 * a] * sc, dkt[db][4 * a + 1] * sc,
-                                           dkt[db][4 * a + 2] * sc, dkt[db][4 * a + 3] * sc);
-          *(float4*)(dV + d) = make_float4(dvt[db][4 * a], dvt[db][4 * a + 1],
-                                           dvt[db][4 * a + 2], dvt[db][4 * a + 3]);
+          if constexpr (DOK)
+            *(float4*)(dK + d) = make_float4(dkt[db][4 * a] * sc, dkt[db][4 * a + 1] * sc,
+                                             dkt[db][4 * a + 2] * sc, dkt[db][4 * a + 3] * sc);
+          if constexpr (DOV)
+            *(float4*)(dV + d) = make_float4(dvt[db][4 * a], dvt[db][4 * a + 1],
+                                             dvt[db][4 * a + 2], dvt[db][4 * a + 3]);
         }
     }
   }
+}
+
+template <int D, bool BUF>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_mfma(BwdProblem p) {
+  __shared__ DkvSmem<D> sm;
+  dkv_role<D, BUF, kDkvBoth>(p, sm, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+}
+
+// The same work on 8 waves: waves 0-3 stage and accumulate dV, waves 4-7
+// accumulate dK of the same keys (two waves per SIMD, one of each role).
+template <int D, bool BUF>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_split(BwdProblem p) {
+  __shared__ DkvSmem<D> sm;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // block tests are scalar
+  if (wave < 4)
+    dkv_role<D, BUF, kDkvV>(p, sm, wave);
+  else
+    dkv_role<D, BUF, kDkvK>(p, sm, wave - 4);
 }
 
 }  // namespace
@@ -890,17 +923,19 @@ hipError_t launch_attn_backward(const BwdProblem& p_in, dar_dtype dt, hipStream_
     // buffer-resource staging when the largest staged array (one batch's dO
     // rows, stride heads * d_k) is under 2 GiB
     const bool buf = (long)p.N * p.H * p.d_k * 2 < 0x7fffffffL;
-#define DAR_BWD_MFMA(DV, BUFV)                                                   \
-  do {                                                                           \
-    hipLaunchKernelGGL((bwd_dq_mfma<DV, BUFV>), dim3(nT * BH), dim3(256), 0, s, p);  \
-    hipLaunchKernelGGL((bwd_dkv_mfma<DV, BUFV>), dim3(nT * BH), dim3(256), 0, s, p); \
+    // d_k 64: one wave per 32 keys holds both accumulators at two waves per
+    // SIMD; d_k 128: the split kernel (dV and dK on separate waves)
+#define DAR_BWD_MFMA(DV, BUFV, KV, NT)                                                \
+  do {                                                                            \
+    hipLaunchKernelGGL((bwd_dq_mfma<DV, BUFV>), dim3(nT * BH), dim3(256), 0, s, p); \
+    hipLaunchKernelGGL((KV<DV, BUFV>), dim3(nT * BH), dim3(NT), 0, s, p);           \
   } while (0)
     if (p.d_k == 64) {
-      if (buf) DAR_BWD_MFMA(64, true);
-      else DAR_BWD_MFMA(64, false);
+      if (buf) DAR_BWD_MFMA(64, true, bwd_dkv_mfma, 256);
+      else DAR_BWD_MFMA(64, false, bwd_dkv_mfma, 256);
     } else {
-      if (buf) DAR_BWD_MFMA(128, true);
-      else DAR_BWD_MFMA(128, false);
+      if (buf) DAR_BWD_MFMA(128, true, bwd_dkv_split, 512);
+      else DAR_BWD_MFMA(128, false, bwd_dkv_split, 512);
     }
 #undef DAR_BWD_MFMA
   } else if (p.d_k == 64) {
