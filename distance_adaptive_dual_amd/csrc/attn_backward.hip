@@ -13,7 +13,8 @@
 //   dk_j  = sum_i ds_ij q_i / sqrt(d_k)     (into the source of pair (i, j))
 //   dv_j  = sum_i p_ij dO_i                 (likewise)
 //
-// bf16 mode runs the MFMA kernels further below (bwd_dq_mfma, bwd_dkv_mfma).
+// bf16 mode runs the MFMA kernels further below (bwd_dq_mfma, and bwd_dkv_mfma
+// at d_k 64 or bwd_dkv_split at d_k 128).
 // fp32 mode runs two VALU kernels in fp32 (the gradients are fp32 in both
 // modes):
 //   bwd_dq:  64 queries per workgroup, four lanes per query (lane part pt owns
