@@ -385,8 +385,9 @@ __device__ __forceinline__ void load_pairs(Pairs<D, ROWS>& x, const void* src, s
 }
 
 // ... as rows of pitch RP and transposed as [d][row] of pitch TP (BF: the
-// registers hold bf16 bits, converted to fp16 here).
-template <int D, int ROWS, int RP, int TP, bool BF = false>
+// registers hold bf16 bits, converted to fp16 here).  GP: extra halves after
+// every 16 transposed rows (see DqSmem).
+template <int D, int ROWS, int RP, int TP, bool BF = false, int GP = 0>
 __device__ __forceinline__ void store_pairs(const Pairs<D, ROWS>& x, f16* rows, f16* cols,
                                             int pi) {
 #pragma unroll
@@ -398,7 +399,8 @@ __device__ __forceinline__ void store_pairs(const Pairs<D, ROWS>& x, f16* rows, 
     *(u32x4*)(rows + (row + 1) * RP + col) = vb;
     const f16x8 ha = __builtin_bit_cast(f16x8, va), hb = __builtin_bit_cast(f16x8, vb);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *(uint32_t*)(cols + (col + e) * TP + row) = pack2(ha[e], hb[e]);
+    for (int e = 0; e < 8; ++e)
+      *(uint32_t*)(cols + (col + e) * TP + GP * ((col + e) >> 4) + row) = pack2(ha[e], hb[e]);
   }
 }
 
@@ -427,24 +429,32 @@ __device__ __forceinline__ void load_vt_pairs(Pairs<D, MB>& x, const f16* src, i
   }
 }
 
-template <int D, int RP>
+template <int D, int RP, int GP = 0>
 __device__ __forceinline__ void store_vt_pairs(const Pairs<D, MB>& x, f16* rows, int pi) {
 #pragma unroll
   for (int i = 0; i < Pairs<D, MB>::NP; ++i) {
     const int q = pi + 128 * i, d = 2 * (q / (MB / 8)), kc = (q % (MB / 8)) * 8;
     const f16x8 ha = __builtin_bit_cast(f16x8, x.a[i]), hb = __builtin_bit_cast(f16x8, x.b[i]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) *(uint32_t*)(rows + (kc + e) * RP + d) = pack2(ha[e], hb[e]);
+    for (int e = 0; e < 8; ++e)
+      *(uint32_t*)(rows + (kc + e) * RP + GP * ((kc + e) >> 4) + d) = pack2(ha[e], hb[e]);
   }
 }
 
+// kt and v take 4-byte pair writes whose 64 lanes fall into 4 groups of 16,
+// each group covering one row's 32 keys (kt) or 32 dims (v).  With 16-byte
+// aligned pitches the group starts land 0, 32, 0, 32 banks apart; GP extra
+// halves after every 16 rows move them to 0, 32, 16, 48 and keep every row
+// 16-byte aligned for the operand reads.  Kept at d_k 128 only, where it
+// measured faster (d_k 64: slightly slower).
 template <int D>
 struct DqSmem {
   static constexpr int RP = D + 8;   // fp16 pitch of [key][d] rows
   static constexpr int TP = MB + 8;  // fp16 pitch of [d][key] rows
+  static constexpr int GP = D == 128 ? 32 : 0;  // halves after every 16 rows of kt and v
   f16 k[2][MB * RP];                 // [buffer]
-  f16 kt[2][D * TP];
-  f16 v[2][MB * RP];
+  f16 kt[2][D * TP + GP * (D / 16)];
+  f16 v[2][MB * RP + GP * (MB / 16)];
 };
 
 // dq and the per-query statistics (lse2, D) for the key-stationary kernel.
@@ -455,7 +465,7 @@ struct DqSmem {
 template <int D, bool BUF>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p) {
   constexpr int NS = D / 16, NB = D / 32;
-  constexpr int RP = DqSmem<D>::RP, TP = DqSmem<D>::TP;
+  constexpr int RP = DqSmem<D>::RP, TP = DqSmem<D>::TP, GP = DqSmem<D>::GP;
   __shared__ DqSmem<D> sm;
   const int N = p.N, H = p.H, w = p.w, BH = p.B * p.H;
   const int nQT = (N + MQ - 1) / MQ;
@@ -600,8 +610,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p
       else load_vt_pairs<D>(px, Vp(ss), jj, N, pi);
     };
     auto store2 = [&](int bb) {
-      if (kside) store_pairs<D, MB, RP, TP>(px, sm.k[bb], sm.kt[bb], pi);
-      else store_vt_pairs<D, RP>(px, sm.v[bb], pi);
+      if (kside) store_pairs<D, MB, RP, TP, false, GP>(px, sm.k[bb], sm.kt[bb], pi);
+      else store_vt_pairs<D, RP, GP>(px, sm.v[bb], pi);
     };
     load2(j0, src);
     store2(bf);
@@ -620,7 +630,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p
         for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
         for (int st = 0; st < NS; ++st)
-          dp = mfma32x32x16(*(const f16x8*)(sm.v[bf] + row_perm(lr) * RP + 16 * st + 8 * lg),
+          dp = mfma32x32x16(*(const f16x8*)(sm.v[bf] + row_perm(lr) * RP +
+                                            GP * (row_perm(lr) >> 4) + 16 * st + 8 * lg),
                             gf[st], dp);
         f16x8 dsb[2];
 #pragma unroll
@@ -633,7 +644,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void bwd_dq_mfma(BwdProblem p
 #pragma unroll
           for (int db = 0; db < NB; ++db)
             dq[db] = mfma32x32x16(
-                *(const f16x8*)(sm.kt[bf] + (32 * db + lr) * TP + 16 * u + 8 * lg), dsb[u],
+                *(const f16x8*)(sm.kt[bf] + (32 * db + lr) * TP + GP * (2 * db + (lr >> 4)) +
+                                16 * u + 8 * lg),
+                dsb[u],
                 dq[db]);
       }
       if (has_next) store2(bf ^ 1);
